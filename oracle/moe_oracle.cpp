@@ -1,0 +1,392 @@
+// CPU oracle for the MoE expert-layer path.  TEST INFRASTRUCTURE ONLY: the
+// product path never links, loads or calls this file; only the tests, the
+// smoke check and the benchmark's CPU-baseline leg use it.
+//
+// Plain, slow, obviously correct: fp64 arithmetic, straight loops, no
+// blocking or fusion.  It shares no code with the GPU library.  Each function
+// names the passage of the pages it follows:
+//   [WideEP-Premise]  "Wide-EPとは?" explainer (scholia-notes), section
+//                     "前提:MoE(Mixture of Experts)とは": a router picks a few
+//                     experts per token, only they compute, and their results
+//                     are added up.
+//   [WideEP-Problem]  same page, "MoEの課題": which experts are chosen is not
+//                     known in advance (so per-expert row counts are data).
+//   [WideEP-Comm]     same page, "前提条件:GPU間の高速通信": tokens are sent to
+//                     their expert (dispatch) and results returned (combine).
+//   [TE-Grouped]      BioNeMo MoE article, "GroupedLinear Optimizes Expert
+//                     Computation in MoE Models": per-expert matrices kept,
+//                     all experts submitted as one operation; ScaledSwiGLU
+//                     folds the routing probabilities into the expert FFN.
+//   [TE-MXFP8]        same article, "MXFP8 Precision Reduces Memory Footprint
+//                     for Biological Models": 8-bit values with one scale per
+//                     block of 32 consecutive values.
+// Where the pages leave a step open, the reading taken is stated at the
+// function.  Parity pins for every function live in the CPU test suite.
+//
+// Data type codes for tensors passed as void*: 0 = fp32, 1 = bf16 (raw
+// uint16 bits), 2 = fp64.
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <vector>
+
+namespace {
+
+inline double load(const void *p, int dt, int64_t i) {
+  if (dt == 0) return (double)((const float *)p)[i];
+  if (dt == 1) {
+    uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    std::memcpy(&f, &u, 4);
+    return (double)f;
+  }
+  return ((const double *)p)[i];
+}
+
+inline size_t elem_size(int dt) { return dt == 0 ? 4 : (dt == 1 ? 2 : 8); }
+
+// SiLU(z) = z * sigmoid(z) (Elfwing et al. 2018; the Swish of Ramachandran
+// et al. 2017 with beta = 1).
+inline double silu(double z) { return z / (1.0 + std::exp(-z)); }
+
+inline double sigmoid(double z) { return 1.0 / (1.0 + std::exp(-z)); }
+
+}  // namespace
+
+extern "C" {
+
+// ---------------------------------------------------------------------------
+// Router.  [WideEP-Premise]: the router scores every expert for each token.
+// logits[t, e] = sum_h x[t, h] * w_r[e, h] + bias[e]   (bias may be NULL)
+// x [T, H], w_r [E, H] (K-contiguous), both of type dt; logits [T, E] fp64.
+void orc_router_logits(const void *x, const void *w_r, int dt,
+                       const float *bias, int64_t T, int64_t H, int64_t E,
+                       double *logits) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t e = 0; e < E; ++e) {
+      double acc = 0.0;
+      for (int64_t h = 0; h < H; ++h)
+        acc += load(x, dt, t * H + h) * load(w_r, dt, e * H + h);
+      logits[t * E + e] = acc + (bias ? (double)bias[e] : 0.0);
+    }
+}
+
+// Softmax over all E experts, keep the k most probable, renormalise the kept
+// probabilities to sum to one.  [WideEP-Premise] gives "the router picks k of
+// E"; the softmax / top-k / renormalise form is the workload definition.
+// Reading for ties (the pages are silent): equal probabilities are ordered by
+// lower expert index first; kept experts are listed by descending
+// probability.  logits [T, E] fp32 in; idx [T, k] int32, w [T, k] fp64 out.
+void orc_topk_softmax(const float *logits, int64_t T, int64_t E, int64_t k,
+                      int32_t *idx, double *w) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    const float *l = logits + t * E;
+    std::vector<double> p(E);
+    double mx = -INFINITY;
+    for (int64_t e = 0; e < E; ++e) mx = std::fmax(mx, (double)l[e]);
+    double z = 0.0;
+    for (int64_t e = 0; e < E; ++e) {
+      p[e] = std::exp((double)l[e] - mx);
+      z += p[e];
+    }
+    for (int64_t e = 0; e < E; ++e) p[e] /= z;
+    std::vector<char> taken(E, 0);
+    double kept = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      int64_t best = -1;
+      for (int64_t e = 0; e < E; ++e)
+        if (!taken[e] && (best < 0 || p[e] > p[best])) best = e;
+      taken[best] = 1;
+      idx[t * k + j] = (int32_t)best;
+      w[t * k + j] = p[best];
+      kept += p[best];
+    }
+    for (int64_t j = 0; j < k; ++j) w[t * k + j] /= kept;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch on one GPU.  [WideEP-Comm] sends every (token, chosen expert) slot
+// to its expert; [WideEP-Problem] makes the per-expert counts data.  Here the
+// slots routed to this GPU's experts [e_begin, e_begin + n_local) are laid
+// out expert by expert; inside an expert, slots keep their flat order
+// f = t*k + j (a stable counting sort; reading of "stable permute").  Slots
+// of other experts are dropped (inv = -1).
+//   counts[e]   = number of slots with idx == e_begin + e
+//   offsets[e]  = sum of counts before e; offsets[n_local] = R
+//   row_src[r]  = flat slot f placed at row r, for r < R
+//   inv[f]      = row of slot f, or -1
+void orc_permute(const int32_t *idx, int64_t T, int64_t k, int64_t e_begin,
+                 int64_t n_local, int32_t *counts, int32_t *offsets,
+                 int32_t *row_src, int32_t *inv) {
+  const int64_t F = T * k;
+  for (int64_t f = 0; f < F; ++f) inv[f] = -1;
+  for (int64_t e = 0; e < n_local; ++e) {
+    int32_t c = 0;
+    for (int64_t f = 0; f < F; ++f)
+      if (idx[f] == e_begin + e) ++c;
+    counts[e] = c;
+  }
+  offsets[0] = 0;
+  for (int64_t e = 0; e < n_local; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  for (int64_t e = 0; e < n_local; ++e) {
+    int32_t r = offsets[e];
+    for (int64_t f = 0; f < F; ++f)
+      if (idx[f] == e_begin + e) {
+        row_src[r] = (int32_t)f;
+        inv[f] = r;
+        ++r;
+      }
+  }
+}
+
+// x_perm[r, :] = x[row_src[r] / k, :]  (a byte copy of the token's row)
+void orc_gather_rows(const void *x, int dt, int64_t H, int64_t k,
+                     const int32_t *row_src, int64_t R, void *x_perm) {
+  const size_t rb = (size_t)H * elem_size(dt);
+  for (int64_t r = 0; r < R; ++r)
+    std::memcpy((char *)x_perm + (size_t)r * rb,
+                (const char *)x + (size_t)(row_src[r] / k) * rb, rb);
+}
+
+// ---------------------------------------------------------------------------
+// Expert FFN on listed rows.  [TE-Grouped]: each expert keeps its own
+// matrices; ScaledSwiGLU multiplies the routing probability ("scale") into
+// the expert FFN.  SwiGLU (Shazeer 2020) with SiLU, no biases:
+//   g = W_gate[e] x,  u = W_up[e] x,  a = s * SiLU(g) (.) u,  y = W_down[e] a
+// Row n uses activations xs[n, :] (type xdt), local expert ex[n] and scale
+// sc[n] (sc may be NULL: scale 1).  W_gate, W_up [n_local, I, H];
+// W_down [n_local, H, I] (type wdt).  a_out [n, I] and y_out [n, H] (fp64)
+// may each be NULL.
+void orc_expert_ffn_rows(const void *xs, int xdt, const int32_t *ex,
+                         const double *sc, const void *w_gate,
+                         const void *w_up, const void *w_down, int wdt,
+                         int64_t nrows, int64_t H, int64_t I, double *a_out,
+                         double *y_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < nrows; ++n) {
+    const int64_t e = ex[n];
+    const double s = sc ? sc[n] : 1.0;
+    std::vector<double> x(H), a(I);
+    for (int64_t h = 0; h < H; ++h) x[h] = load(xs, xdt, n * H + h);
+    for (int64_t i = 0; i < I; ++i) {
+      double g = 0.0, u = 0.0;
+      const int64_t base = (e * I + i) * H;
+      for (int64_t h = 0; h < H; ++h) {
+        g += load(w_gate, wdt, base + h) * x[h];
+        u += load(w_up, wdt, base + h) * x[h];
+      }
+      a[i] = s * silu(g) * u;
+    }
+    if (a_out)
+      for (int64_t i = 0; i < I; ++i) a_out[n * I + i] = a[i];
+    if (y_out)
+      for (int64_t h = 0; h < H; ++h) {
+        double acc = 0.0;
+        const int64_t base = (e * H + h) * I;
+        for (int64_t i = 0; i < I; ++i) acc += load(w_down, wdt, base + i) * a[i];
+        y_out[n * H + h] = acc;
+      }
+  }
+}
+
+// Gate and up pre-activations of listed rows (fp64): g, u [n, I].
+void orc_gate_up_rows(const void *xs, int xdt, const int32_t *ex,
+                      const void *w_gate, const void *w_up, int wdt,
+                      int64_t nrows, int64_t H, int64_t I, double *g_out,
+                      double *u_out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < nrows; ++n) {
+    const int64_t e = ex[n];
+    for (int64_t i = 0; i < I; ++i) {
+      double g = 0.0, u = 0.0;
+      const int64_t base = (e * I + i) * H;
+      for (int64_t h = 0; h < H; ++h) {
+        const double xv = load(xs, xdt, n * H + h);
+        g += load(w_gate, wdt, base + h) * xv;
+        u += load(w_up, wdt, base + h) * xv;
+      }
+      g_out[n * I + i] = g;
+      u_out[n * I + i] = u;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine.  [WideEP-Premise]/[WideEP-Comm]: the chosen experts' results come
+// back to the token and are added up.
+//   out[t, :] = sum_{j ascending, inv[t,j] >= 0} c_tj * y[inv[t,j], :]
+// with c_tj = w[t, j] when w is given, else 1 (the scale already went into
+// the expert FFN).  Tokens with no local slot get a zero row.
+void orc_combine(const double *y, const int32_t *inv, const double *w,
+                 int64_t T, int64_t k, int64_t H, double *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t t = 0; t < T; ++t) {
+    for (int64_t h = 0; h < H; ++h) out[t * H + h] = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      const int32_t r = inv[t * k + j];
+      if (r < 0) continue;
+      const double c = w ? w[t * k + j] : 1.0;
+      for (int64_t h = 0; h < H; ++h) out[t * H + h] += c * y[(int64_t)r * H + h];
+    }
+  }
+}
+
+// The whole layer by its definition for listed tokens, without any
+// permutation ([WideEP-Premise]):
+//   out[t] = sum_{j : e_begin <= idx[t,j] < e_begin+n_local}
+//            w[t,j] * W_down[e] ( SiLU(W_gate[e] x_t) (.) W_up[e] x_t )
+// tokens [ntok] lists token ids; out [ntok, H] fp64.
+void orc_moe_tokens(const void *x, int xdt, const int32_t *idx,
+                    const double *w, int64_t k, const int32_t *tokens,
+                    int64_t ntok, int64_t e_begin, int64_t n_local,
+                    const void *w_gate, const void *w_up, const void *w_down,
+                    int wdt, int64_t H, int64_t I, double *out) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t n = 0; n < ntok; ++n) {
+    const int64_t t = tokens[n];
+    std::vector<double> xv(H), a(I);
+    for (int64_t h = 0; h < H; ++h) xv[h] = load(x, xdt, t * H + h);
+    for (int64_t h = 0; h < H; ++h) out[n * H + h] = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      const int64_t e = (int64_t)idx[t * k + j] - e_begin;
+      if (e < 0 || e >= n_local) continue;
+      for (int64_t i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        const int64_t base = (e * I + i) * H;
+        for (int64_t h = 0; h < H; ++h) {
+          g += load(w_gate, wdt, base + h) * xv[h];
+          u += load(w_up, wdt, base + h) * xv[h];
+        }
+        a[i] = silu(g) * u;
+      }
+      const double c = w[t * k + j];
+      for (int64_t h = 0; h < H; ++h) {
+        double acc = 0.0;
+        const int64_t base = (e * H + h) * I;
+        for (int64_t i = 0; i < I; ++i) acc += load(w_down, wdt, base + i) * a[i];
+        out[n * H + h] += c * acc;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8.  [TE-MXFP8]: 8-bit values, one scale per 32 consecutive values.  The
+// pages fix no encoding or rounding; the reading taken is the OCP
+// Microscaling Formats specification v1.0: elements in FP8 E4M3 (the OCP "FN"
+// variant: bias 7, no infinities, 0x7F / 0xFF are NaN, largest finite 448),
+// the shared scale in E8M0 (2^(byte-127)), shared exponent
+// X = floor(log2(max|v|)) - 8 (8 being E4M3's largest normal exponent),
+// elements v / 2^X rounded to nearest, ties to even, saturating at +-448.
+// A block whose values are all zero gets scale byte 0 (its codes encode +-0).
+
+// Value of an E4M3 code, by the format's definition.
+double orc_e4m3_value(uint8_t code) {
+  const int s = code >> 7, ex = (code >> 3) & 15, m = code & 7;
+  if (ex == 15 && m == 7) return NAN;
+  double mag = ex == 0 ? std::ldexp((double)m / 8.0, -6)
+                       : std::ldexp(1.0 + (double)m / 8.0, ex - 7);
+  return s ? -mag : mag;
+}
+
+// Code of the E4M3 value nearest to v (ties: even code), saturating.
+uint8_t orc_e4m3_encode(double v) {
+  const double a = std::fabs(v);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7E; ++c) {  // every finite non-negative code
+    const double err = std::fabs(orc_e4m3_value((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1))) {
+      best = c;
+      best_err = err;
+    }
+  }
+  if (a > 448.0) best = 0x7E;  // saturate
+  // The sign is kept, also when the magnitude rounds to zero (code 0x80).
+  return (uint8_t)(best | (std::signbit(v) ? 0x80 : 0));
+}
+
+// Shared E8M0 scale byte of a block with largest magnitude amax.
+uint8_t orc_mx_scale_byte(double amax) {
+  if (amax == 0.0) return 0;
+  int e2;
+  std::frexp(amax, &e2);  // amax = m * 2^e2, m in [0.5, 1)
+  int X = (e2 - 1) - 8;
+  if (X < -127) X = -127;
+  if (X > 127) X = 127;
+  return (uint8_t)(X + 127);
+}
+
+// Quantise each row of v [rows, cols] in blocks of 32 along the row (the last
+// block of a row may be shorter: it behaves as if zero-padded).
+// codes [rows, cols]; scales [rows, ceil(cols/32)].
+void orc_mx_quantize_rows(const double *v, int64_t rows, int64_t cols,
+                          uint8_t *codes, uint8_t *scales) {
+  const int64_t nb = (cols + 31) / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < nb; ++b) {
+      const int64_t c0 = b * 32, c1 = std::min<int64_t>(cols, c0 + 32);
+      double amax = 0.0;
+      for (int64_t c = c0; c < c1; ++c) amax = std::fmax(amax, std::fabs(v[r * cols + c]));
+      const uint8_t sb = orc_mx_scale_byte(amax);
+      scales[r * nb + b] = sb;
+      const double inv_scale = std::ldexp(1.0, -((int)sb - 127));
+      for (int64_t c = c0; c < c1; ++c)
+        codes[r * cols + c] = orc_e4m3_encode(v[r * cols + c] * inv_scale);
+    }
+}
+
+// v[r, c] = value(codes[r, c]) * 2^(scales[r, c/32] - 127), exactly, in fp64.
+void orc_mx_dequantize_rows(const uint8_t *codes, const uint8_t *scales,
+                            int64_t rows, int64_t cols, double *v) {
+  const int64_t nb = (cols + 31) / 32;
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t c = 0; c < cols; ++c)
+      v[r * cols + c] = std::ldexp(orc_e4m3_value(codes[r * cols + c]),
+                                   (int)scales[r * nb + c / 32] - 127);
+}
+
+// ---------------------------------------------------------------------------
+// Plain fp64 products used by the MXFP8 training step (the GEMMs of the
+// backward pass follow the chain rule on the forward above).
+// C[m, n] = sum_k A[m, k] * B[n, k]    (A [M, K], B [N, K], C [M, N])
+void orc_matmul_nt(const double *A, const double *B, int64_t M, int64_t N,
+                   int64_t K, double *C) {
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int64_t kk = 0; kk < K; ++kk) acc += A[m * K + kk] * B[n * K + kk];
+      C[m * N + n] = acc;
+    }
+}
+
+// SwiGLU-with-scale backward, by the chain rule on a = s * SiLU(g) * u:
+//   dg = da * s * u * SiLU'(g),  du = da * s * SiLU(g),
+//   ds = sum_i da * SiLU(g) * u,
+// with SiLU'(z) = sigmoid(z) * (1 + z * (1 - sigmoid(z))).
+void orc_swiglu_bwd_rows(const double *da, const double *g, const double *u,
+                         const double *s, int64_t rows, int64_t I, double *dg,
+                         double *du, double *ds) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < I; ++i) {
+      const int64_t o = r * I + i;
+      const double z = g[o], sg = sigmoid(z);
+      const double sl = z * sg;
+      const double dsl = sg * (1.0 + z * (1.0 - sg));
+      dg[o] = da[o] * s[r] * u[o] * dsl;
+      du[o] = da[o] * s[r] * sl;
+      acc += da[o] * sl * u[o];
+    }
+    ds[r] = acc;
+  }
+}
+
+}  // extern "C"
