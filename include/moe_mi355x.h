@@ -1,0 +1,200 @@
+/*
+ * moe_mi355x.h - C ABI of the MoE expert-layer library for MI355X (gfx950).
+ *
+ * One GPU's share of a Mixture-of-Experts expert layer:
+ *   route (router GEMM, softmax, top-k, renormalise)
+ *   -> permute (per-expert counts, offsets, stable dispatch of token rows)
+ *   -> grouped gate/up GEMM with the SwiGLU x routing-scale epilogue
+ *   -> grouped down GEMM
+ *   -> unpermute / combine (weighted sum back to token order)
+ * plus an MXFP8 variant of the grouped MLP (E4M3 values, one E8M0 scale per
+ * 32 values along the reduction axis).
+ *
+ * Passages of the pages that define the operations (cited by page title and
+ * section):
+ *   "Wide-EPとは?" explainer (scholia-notes), sections
+ *     前提:MoE(Mixture of Experts)とは - a router chooses a few experts per
+ *       token; only those compute; their results are summed.
+ *     MoEの課題 - which expert is chosen when is not known beforehand.
+ *     効果2:演算強度が上がる - grouping many tokens per expert (GroupGEMM)
+ *       reuses each weight byte read from HBM.
+ *     前提条件:GPU間の高速通信 - tokens go to their expert (dispatch) and the
+ *       results come back (combine).
+ *   BioNeMo MoE article (quantumzeitgeist), sections
+ *     GroupedLinear Optimizes Expert Computation in MoE Models - expert
+ *       matrices stay separate but are submitted as one operation; the
+ *       ScaledSwiGLU step folds the routing probabilities ("scales") into the
+ *       expert FFN; the fused MLP avoids materialising intermediates.
+ *     MXFP8 Precision Reduces Memory Footprint for Biological Models - 8-bit
+ *       values, a scale per block of 32 consecutive values; quantisation,
+ *       SwiGLU and routing-weight scaling fused into one kernel.
+ *   NVL72 Wide-EP news item (mexc.fm), "Kernel Optimization and Load
+ *     Balancing" - expert routing moves data whose sizes are not static.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless stated otherwise; the caller owns
+ *     every buffer and the stream.  The library never allocates or frees
+ *     device memory and never synchronises the stream (except
+ *     moe_debug_sync, which exists for tests).
+ *   - Work is enqueued on `stream` (NULL = the default stream).
+ *   - Return value: MOE_OK, or an MOE_E_* code.  Arguments are validated on
+ *     the host before anything is enqueued; on a validation error nothing is
+ *     enqueued.  A failed launch returns MOE_E_HIP.  No exception crosses the
+ *     ABI and the library never aborts.
+ *   - Per-expert row counts exist only on the device (they are data); every
+ *     consumer reads them from `offsets`, so no host round trip happens.
+ *   - Matrices are row-major.  Weights are stored K-contiguous like
+ *     nn.Linear: W_router [E, H], W_gate and W_up [n_local, I, H],
+ *     W_down [n_local, H, I].
+ *   - dtype MOE_DT_BF16: activations, weights and outputs bf16 (raw 16-bit),
+ *     fp32 accumulation, outputs rounded to nearest even.  MOE_DT_F32: all
+ *     fp32.  Routing weights, logits and scales are always fp32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+  MOE_OK = 0,
+  MOE_E_ARG = 1,          /* NULL where a buffer is required, bad enum    */
+  MOE_E_SHAPE = 2,        /* sizes out of range or inconsistent           */
+  MOE_E_ALIGN = 3,        /* pointer not 16-byte aligned                  */
+  MOE_E_WORKSPACE = 4,    /* workspace missing or too small               */
+  MOE_E_UNSUPPORTED = 5,  /* valid but not implemented combination        */
+  MOE_E_HIP = 6           /* a HIP launch or runtime call failed          */
+};
+
+enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
+
+/* Human-readable name of a status code (static string, host). */
+const char *moe_status_string(int status);
+
+/* Library version as 10000*major + 100*minor + patch (host). */
+int moe_version(void);
+
+/*
+ * moe_route_topk - router scores, softmax over all E experts, the k most
+ * probable experts per token, their probabilities renormalised to sum to 1.
+ * (Wide-EP explainer, 前提:MoEとは: the router picks k of E per token.)
+ *
+ * Two modes:
+ *   x != NULL and w_router != NULL:  logits[t, e] = sum_h x[t,h] w_router[e,h]
+ *       (+ bias[e] when bias != NULL), written to `logits` (fp32), then top-k.
+ *   x == NULL and w_router == NULL:  `logits` is an input; only top-k runs
+ *       (bias must be NULL).
+ * x [T, H], w_router [E, H] of `dtype`; bias [E] fp32; logits [T, E] fp32.
+ * Outputs: topk_idx [T, k] int32 (descending probability; equal logits go to
+ * the lower expert index first) and topk_w [T, k] fp32.
+ * The top-k decision is taken on the fp32 logits.  The weights are
+ * exp(l_j - l_max) / sum over the kept experts of exp(l - l_max).
+ * Limits: 1 <= k <= min(E, 32), 1 <= E <= 1024, T >= 0 (T == 0 enqueues
+ * nothing), H >= 1; in GEMM mode with bf16, H % 8 == 0.
+ */
+int moe_route_topk(const void *x, const void *w_router, const float *bias,
+                   float *logits, int64_t T, int64_t H, int64_t E, int64_t k,
+                   int dtype, int32_t *topk_idx, float *topk_w,
+                   hipStream_t stream);
+
+/*
+ * moe_permute - local dispatch: lay the (token, slot) pairs routed to this
+ * GPU's experts [e_begin, e_begin + n_local) out expert by expert.
+ * (Wide-EP explainer, 前提条件:GPU間の高速通信 - dispatch; MoEの課題 and the
+ * NVL72 news item - counts are data, not static sizes.)
+ *
+ * Flat slot f = t*k + j.  Inside an expert, slots keep ascending f (a stable
+ * counting sort), so the result is unique and deterministic.
+ * Inputs:  topk_idx [T, k] int32; topk_w [T, k] fp32 or NULL;
+ *          x [T, H] of dtype or NULL (then x_perm is not written).
+ * Outputs: counts [n_local], offsets [n_local + 1] (exclusive scan,
+ *          offsets[n_local] = R, the rows this GPU computes),
+ *          row_src [T*k] (rows < R: the flat slot placed there),
+ *          inv [T, k] (row of slot f, or -1 when its expert is not local),
+ *          x_perm [T*k, H] (rows < R: x_perm[r] = x[row_src[r] / k]),
+ *          s_perm [T*k] fp32 (rows < R: topk_w of that slot; skipped when
+ *          topk_w is NULL or s_perm is NULL).
+ * Rows >= R of the capacity-sized outputs are left untouched.
+ * Indices outside [e_begin, e_begin + n_local) are non-local: dropped.
+ * workspace: moe_permute_workspace_bytes(T, k, n_local) bytes, 16-aligned.
+ * Limits: 1 <= k <= 32, T*k < 2^31, 1 <= n_local <= 4096, H % 8 == 0 when
+ * x is given (bf16) or H % 4 == 0 (fp32).
+ */
+size_t moe_permute_workspace_bytes(int64_t T, int64_t k, int64_t n_local);
+int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
+                int64_t T, int64_t k, int64_t H, int dtype, int64_t e_begin,
+                int64_t n_local, void *x_perm, float *s_perm,
+                int32_t *row_src, int32_t *inv, int32_t *counts,
+                int32_t *offsets, void *workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/*
+ * moe_grouped_gate_up - for every local expert e and its rows
+ * [offsets[e], offsets[e+1]) of x_perm, in one launch for all experts
+ * (BioNeMo article, GroupedLinear section):
+ *   g = x_perm . W_gate[e]^T,  u = x_perm . W_up[e]^T   (fp32 accumulation)
+ *   a = s_perm[r] * SiLU(g) * u   (ScaledSwiGLU; s_perm NULL -> scale 1)
+ * g and u never leave the chip; only `a` [R_cap, I] (dtype) is written, rows
+ * < R.  SiLU(z) = z * sigmoid(z).
+ * workspace: moe_grouped_ffn_workspace_bytes(...) bytes, 16-aligned.
+ * Limits (bf16): H % 64 == 0, I % 64 == 0, 1 <= n_local <= 4096,
+ * R_cap < 2^31.  (fp32): H % 4 == 0, I % 4 == 0.
+ */
+size_t moe_grouped_ffn_workspace_bytes(int64_t R_cap, int64_t n_local,
+                                       int64_t H, int64_t I, int dtype);
+int moe_grouped_gate_up(const void *x_perm, const int32_t *offsets,
+                        const float *s_perm, int64_t n_local, int64_t R_cap,
+                        int64_t H, int64_t I, const void *w_gate,
+                        const void *w_up, int dtype, void *a, void *workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_down - y[r] = a[r] . W_down[e]^T for every local expert's rows
+ * (fp32 accumulation, dtype output), rows < R of y [R_cap, H].
+ * Same limits and workspace as moe_grouped_gate_up.
+ */
+int moe_grouped_down(const void *a, const int32_t *offsets, int64_t n_local,
+                     int64_t R_cap, int64_t H, int64_t I, const void *w_down,
+                     int dtype, void *y, void *workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_ffn - moe_grouped_gate_up followed by moe_grouped_down; `a`
+ * [R_cap, I] (dtype) is the one intermediate handed between them.
+ */
+int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
+                    const float *s_perm, int64_t n_local, int64_t R_cap,
+                    int64_t H, int64_t I, const void *w_gate,
+                    const void *w_up, const void *w_down, int dtype, void *a,
+                    void *y, void *workspace, size_t workspace_bytes,
+                    hipStream_t stream);
+
+/*
+ * moe_unpermute_combine - bring expert outputs back to token order and add
+ * them up (Wide-EP explainer, 前提:MoEとは and 前提条件:GPU間の高速通信):
+ *   out[t] = sum over j ascending with inv[t,j] >= 0 of c_tj * y[inv[t,j]]
+ * with c_tj = topk_w[t,j] when topk_w != NULL, else 1 (use NULL when the
+ * routing scale already went into the gate/up epilogue).  fp32 accumulation,
+ * one rounding to dtype at the end; tokens with no local slot get a zero
+ * row.  No atomics: the result is bitwise reproducible.
+ * y [>= max(inv)+1, H], inv [T, k] int32, out [T, H] (dtype).
+ * Limits: 1 <= k <= 32, H % 8 == 0 (bf16) or H % 4 == 0 (fp32).
+ */
+int moe_unpermute_combine(const void *y, const int32_t *inv,
+                          const float *topk_w, int64_t T, int64_t k,
+                          int64_t H, int dtype, void *out, hipStream_t stream);
+
+/* Waits for `stream` and reports a pending HIP error as MOE_E_HIP (tests). */
+int moe_debug_sync(hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

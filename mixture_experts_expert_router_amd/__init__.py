@@ -1,0 +1,234 @@
+"""MI355X (gfx950) MoE expert layer: thin Python binding of libmoe_mi355x.so.
+
+Every function here marshals torch tensors (device memory) into the C ABI
+declared in ``include/moe_mi355x.h`` and calls it on the current HIP stream;
+all arithmetic runs in the library's HIP kernels.  There is no fallback: if
+the library is missing the import of a compute function raises.
+
+Functions keep the C names without the ``moe_`` prefix.  Outputs not passed
+in are allocated with torch (device memory is the only thing torch provides
+here).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+HEADER = os.path.join(os.path.dirname(_HERE), "include", "moe_mi355x.h")
+
+MOE_OK = 0
+DT_F32, DT_BF16 = 0, 1
+_DT = {torch.float32: DT_F32, torch.bfloat16: DT_BF16}
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (ctypes); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m mixture_experts_expert_router_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                            ctypes.c_size_t)
+        L.moe_status_string.argtypes = [i32]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_version.restype = i32
+        L.moe_route_topk.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                     vp, vp, vp]
+        L.moe_permute_workspace_bytes.argtypes = [i64, i64, i64]
+        L.moe_permute_workspace_bytes.restype = sz
+        L.moe_permute.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i64,
+                                  vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_grouped_ffn_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
+        L.moe_grouped_ffn_workspace_bytes.restype = sz
+        L.moe_grouped_gate_up.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp,
+                                          vp, i32, vp, vp, sz, vp]
+        L.moe_grouped_down.argtypes = [vp, vp, i64, i64, i64, i64, vp, i32,
+                                       vp, vp, sz, vp]
+        L.moe_grouped_ffn.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp, vp,
+                                      vp, i32, vp, vp, vp, sz, vp]
+        L.moe_unpermute_combine.argtypes = [vp, vp, vp, i64, i64, i64, i32,
+                                            vp, vp]
+        L.moe_debug_sync.argtypes = [vp]
+        for name in declared_functions():
+            getattr(L, name).restype = getattr(L, name).restype or i32
+        _lib = L
+    return _lib
+
+
+def declared_functions(header: str = HEADER):
+    """Names of the functions include/moe_mi355x.h declares."""
+    text = open(header, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def version() -> int:
+    return lib().moe_version()
+
+
+def _p(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _call(name, *args):
+    st = getattr(lib(), name)(*args)
+    if st != MOE_OK:
+        raise MoEError(name, st)
+
+
+def _dt(t):
+    try:
+        return _DT[t.dtype]
+    except KeyError:
+        raise TypeError(f"unsupported dtype {t.dtype}") from None
+
+
+def route_topk(k, logits=None, x=None, w_router=None, bias=None,
+               topk_idx=None, topk_w=None, stream=None, T=None, E=None):
+    """Router GEMM (when x and w_router are given) + softmax/top-k.
+
+    Returns (topk_idx [T,k] int32, topk_w [T,k] fp32, logits [T,E] fp32).
+    """
+    if x is not None:
+        T, H = x.shape
+        E = w_router.shape[0]
+        dtype = _dt(x)
+        if logits is None:
+            logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    else:
+        T, E = logits.shape
+        H = 0
+        dtype = DT_F32
+    dev = logits.device
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    _call("moe_route_topk", _p(x), _p(w_router), _p(bias), _p(logits), T, H,
+          E, k, dtype, _p(topk_idx), _p(topk_w), _stream(stream))
+    return topk_idx, topk_w, logits
+
+
+class PermuteOut:
+    """Outputs of permute (capacity-sized; rows < offsets[n_local] valid)."""
+
+    def __init__(self, T, k, H, n_local, dtype, device, with_x=True):
+        F = T * k
+        self.x_perm = (torch.empty((F, H), dtype=dtype, device=device)
+                       if with_x else None)
+        self.s_perm = torch.empty(F, dtype=torch.float32, device=device)
+        self.row_src = torch.empty(F, dtype=torch.int32, device=device)
+        self.inv = torch.empty((T, k), dtype=torch.int32, device=device)
+        self.counts = torch.empty(n_local, dtype=torch.int32, device=device)
+        self.offsets = torch.empty(n_local + 1, dtype=torch.int32,
+                                   device=device)
+        ws = lib().moe_permute_workspace_bytes(T, k, n_local)
+        self.workspace = torch.empty(max(ws, 16), dtype=torch.uint8,
+                                     device=device)
+
+
+def permute(topk_idx, x, e_begin, n_local, topk_w=None, out=None,
+            stream=None):
+    T, k = topk_idx.shape
+    H = x.shape[1] if x is not None else 0
+    dtype = x.dtype if x is not None else torch.bfloat16
+    if out is None:
+        out = PermuteOut(T, k, max(H, 1), n_local, dtype, topk_idx.device,
+                         with_x=x is not None)
+    _call("moe_permute", _p(topk_idx), _p(topk_w), _p(x), T, k, H,
+          _DT[dtype], e_begin, n_local, _p(out.x_perm),
+          _p(out.s_perm) if topk_w is not None else None, _p(out.row_src),
+          _p(out.inv), _p(out.counts), _p(out.offsets), _p(out.workspace),
+          out.workspace.numel(), _stream(stream))
+    return out
+
+
+def ffn_workspace(R_cap, n_local, H, I, dtype, device):
+    n = lib().moe_grouped_ffn_workspace_bytes(R_cap, n_local, H, I,
+                                              _DT[dtype])
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def grouped_gate_up(x_perm, offsets, s_perm, w_gate, w_up, a=None,
+                    workspace=None, stream=None):
+    R_cap, H = x_perm.shape
+    n_local, I, _ = w_gate.shape
+    if a is None:
+        a = torch.empty((R_cap, I), dtype=x_perm.dtype, device=x_perm.device)
+    if workspace is None:
+        workspace = ffn_workspace(R_cap, n_local, H, I, x_perm.dtype,
+                                  x_perm.device)
+    _call("moe_grouped_gate_up", _p(x_perm), _p(offsets), _p(s_perm),
+          n_local, R_cap, H, I, _p(w_gate), _p(w_up), _dt(x_perm), _p(a),
+          _p(workspace), workspace.numel(), _stream(stream))
+    return a
+
+
+def grouped_down(a, offsets, w_down, y=None, workspace=None, stream=None):
+    R_cap, I = a.shape
+    n_local, H, _ = w_down.shape
+    if y is None:
+        y = torch.empty((R_cap, H), dtype=a.dtype, device=a.device)
+    if workspace is None:
+        workspace = ffn_workspace(R_cap, n_local, H, I, a.dtype, a.device)
+    _call("moe_grouped_down", _p(a), _p(offsets), n_local, R_cap, H, I,
+          _p(w_down), _dt(a), _p(y), _p(workspace), workspace.numel(),
+          _stream(stream))
+    return y
+
+
+def grouped_ffn(x_perm, offsets, s_perm, w_gate, w_up, w_down, a=None,
+                y=None, workspace=None, stream=None):
+    R_cap, H = x_perm.shape
+    n_local, I, _ = w_gate.shape
+    if a is None:
+        a = torch.empty((R_cap, I), dtype=x_perm.dtype, device=x_perm.device)
+    if y is None:
+        y = torch.empty((R_cap, H), dtype=x_perm.dtype, device=x_perm.device)
+    if workspace is None:
+        workspace = ffn_workspace(R_cap, n_local, H, I, x_perm.dtype,
+                                  x_perm.device)
+    _call("moe_grouped_ffn", _p(x_perm), _p(offsets), _p(s_perm), n_local,
+          R_cap, H, I, _p(w_gate), _p(w_up), _p(w_down), _dt(x_perm), _p(a),
+          _p(y), _p(workspace), workspace.numel(), _stream(stream))
+    return a, y
+
+
+def unpermute_combine(y, inv, topk_w=None, out=None, stream=None):
+    T, k = inv.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=y.dtype, device=y.device)
+    _call("moe_unpermute_combine", _p(y), _p(inv), _p(topk_w), T, k, H,
+          _dt(y), _p(out), _stream(stream))
+    return out
+
+
+def debug_sync(stream=None):
+    _call("moe_debug_sync", _stream(stream))

@@ -1,0 +1,177 @@
+// Local dispatch: per-expert counts and offsets, a stable placement of every
+// (token, slot) pair routed to this GPU's experts, and the row copy.
+// Wide-EP explainer, 前提条件:GPU間の高速通信 (dispatch to the expert) and
+// MoEの課題 (counts are only known once the router has run).
+//
+// Four launches, all on the caller's stream, none needing the host to know a
+// count:
+//   1. hist:    each block counts its chunk of flat slots per local expert
+//               (LDS histogram) -> hist[e][blk]
+//   2. scan:    one block turns hist (expert-major) into exclusive prefixes:
+//               base[e][blk] = offsets[e] + slots of e in earlier chunks;
+//               writes counts and offsets
+//   3. scatter: one wavefront per chunk walks its slots in order, 64 at a
+//               time; a slot's rank among equal experts inside the 64 comes
+//               from ballots over the expert id bits (a wave-level match),
+//               plus a running per-expert count in LDS -> stable rows
+//   4. gather:  copies x[row_src[r] / k] into x_perm[r] with 16-byte vectors
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+
+__global__ __launch_bounds__(256) void permute_hist_kernel(
+    const int32_t *__restrict__ idx, int64_t F, int e_begin, int n_local,
+    int chunk, int nblk, int32_t *__restrict__ hist) {
+  extern __shared__ int32_t bins[];
+  for (int e = threadIdx.x; e < n_local; e += blockDim.x) bins[e] = 0;
+  __syncthreads();
+  const int64_t f0 = (int64_t)blockIdx.x * chunk;
+  const int64_t f1 = min(F, f0 + chunk);
+  for (int64_t f = f0 + threadIdx.x; f < f1; f += blockDim.x) {
+    const uint32_t e = (uint32_t)(idx[f] - e_begin);
+    if (e < (uint32_t)n_local) atomicAdd(&bins[e], 1);
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < n_local; e += blockDim.x)
+    hist[(int64_t)e * nblk + blockIdx.x] = bins[e];
+}
+
+// Exclusive scan of hist[n_local * nblk] (expert-major), in place, one block
+// of 1024 threads.  Also writes offsets[0..n_local] and counts[0..n_local).
+__global__ __launch_bounds__(1024) void permute_scan_kernel(
+    int32_t *__restrict__ hist, int n_local, int nblk,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
+  __shared__ int32_t part[1024];
+  __shared__ int32_t offs[4097];
+  const int64_t total = (int64_t)n_local * nblk;
+  const int tid = threadIdx.x;
+  const int64_t per = (total + 1023) / 1024;
+  const int64_t i0 = min(total, tid * per), i1 = min(total, i0 + per);
+  int32_t s = 0;
+  for (int64_t i = i0; i < i1; ++i) s += hist[i];
+  part[tid] = s;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the 1024 partial sums
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int32_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - s;  // exclusive prefix of this thread's run
+  for (int64_t i = i0; i < i1; ++i) {
+    const int32_t c = hist[i];
+    hist[i] = run;
+    if (i % nblk == 0) offs[i / nblk] = run;
+    run += c;
+  }
+  if (tid == 1023) offs[n_local] = part[1023];
+  __syncthreads();
+  for (int e = tid; e <= n_local; e += 1024) {
+    offsets[e] = offs[e];
+    if (e < n_local) counts[e] = offs[e + 1] - offs[e];
+  }
+}
+
+// One wavefront per chunk of flat slots.
+__global__ __launch_bounds__(64) void permute_scatter_kernel(
+    const int32_t *__restrict__ idx, const float *__restrict__ w, int64_t F,
+    int e_begin, int n_local, int nbits, int chunk, int nblk,
+    const int32_t *__restrict__ base, int32_t *__restrict__ row_src,
+    int32_t *__restrict__ inv, float *__restrict__ s_perm) {
+  extern __shared__ int32_t running[];
+  const int lane = threadIdx.x;
+  for (int e = lane; e < n_local; e += 64) running[e] = 0;
+  __syncthreads();
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int64_t f0 = (int64_t)blockIdx.x * chunk;
+  for (int step = 0; step < chunk; step += 64) {
+    const int64_t f = f0 + step + lane;
+    const bool valid = f < F;
+    const uint32_t e = valid ? (uint32_t)(idx[f] - e_begin) : 0xffffffffu;
+    const bool local = e < (uint32_t)n_local;
+    uint64_t match = __ballot(local);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1u;
+      const uint64_t bb = __ballot(local && bit);
+      match &= bit ? bb : ~bb;
+    }
+    int32_t r = -1;
+    if (local) {
+      const int rank = __popcll(match & lt_mask);
+      r = base[(int64_t)e * nblk + blockIdx.x] + running[e] + rank;
+    }
+    // every lane has read running[] above before any leader updates it
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    if (local && (match & lt_mask) == 0) running[e] += __popcll(match);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) inv[f] = r;
+    if (local) {
+      row_src[r] = (int32_t)f;
+      if (s_perm) s_perm[r] = w[f];
+    }
+  }
+}
+
+// x_perm[r] = x[row_src[r] / k] for r < offsets[n_local]; rows are `vecs`
+// 16-byte vectors long.
+__global__ __launch_bounds__(256) void permute_gather_kernel(
+    const uint4 *__restrict__ x, int64_t vecs, int k,
+    const int32_t *__restrict__ row_src, const int32_t *__restrict__ R_ptr,
+    uint4 *__restrict__ x_perm) {
+  const int R = *R_ptr;
+  for (int r = blockIdx.x; r < R; r += gridDim.x) {
+    const int64_t t = row_src[r] / k;
+    const uint4 *src = x + t * vecs;
+    uint4 *dst = x_perm + (int64_t)r * vecs;
+    for (int64_t c = threadIdx.x; c < vecs; c += blockDim.x) dst[c] = src[c];
+  }
+}
+
+int permute_chunk(int64_t F, int64_t n_local) {
+  (void)F;
+  return n_local <= 64 ? 256 : 1024;
+}
+
+size_t permute_workspace_bytes(int64_t T, int64_t k, int64_t n_local) {
+  const int64_t F = T * k;
+  const int chunk = permute_chunk(F, n_local);
+  const int64_t nblk = F > 0 ? (F + chunk - 1) / chunk : 1;
+  return (size_t)(((nblk * n_local * 4) + 255) / 256 * 256);
+}
+
+hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
+                          int64_t T, int64_t k, int64_t row_bytes,
+                          int64_t e_begin, int64_t n_local, void *x_perm,
+                          float *s_perm, int32_t *row_src, int32_t *inv,
+                          int32_t *counts, int32_t *offsets, void *ws,
+                          int num_cus, hipStream_t s) {
+  const int64_t F = T * k;
+  const int chunk = permute_chunk(F, n_local);
+  const int nblk = (int)((F + chunk - 1) / chunk);
+  int32_t *hist = (int32_t *)ws;
+  int nbits = 0;
+  while ((1ll << nbits) < n_local) ++nbits;
+  const size_t lds = (size_t)n_local * 4;
+  permute_hist_kernel<<<nblk, 256, lds, s>>>(idx, F, (int)e_begin,
+                                              (int)n_local, chunk, nblk, hist);
+  permute_scan_kernel<<<1, 1024, 0, s>>>(hist, (int)n_local, nblk, counts,
+                                         offsets);
+  permute_scatter_kernel<<<nblk, 64, lds, s>>>(
+      idx, w, F, (int)e_begin, (int)n_local, nbits, chunk, nblk, hist,
+      row_src, inv, (w ? s_perm : nullptr));
+  if (x && x_perm) {
+    const int64_t vecs = row_bytes / 16;
+    int64_t grid = F < (int64_t)num_cus * 8 ? F : (int64_t)num_cus * 8;
+    if (grid < 1) grid = 1;
+    permute_gather_kernel<<<(unsigned)grid, 256, 0, s>>>(
+        (const uint4 *)x, vecs, (int)k, row_src, offsets + n_local,
+        (uint4 *)x_perm);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

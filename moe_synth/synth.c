@@ -58,23 +58,45 @@ static inline uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+static inline void normal_pair(uint64_t key, uint64_t p, double *z0,
+                               double *z1) {
+  uint64_t h1 = draw(key, 2 * p), h2 = draw(key, 2 * p + 1);
+  double u1 = (double)((h1 >> 11) + 1) * 0x1.0p-53;
+  double u2 = (double)(h2 >> 11) * 0x1.0p-53;
+  double r = sqrt(-2.0 * log(u1));
+  double th = 6.283185307179586476925286766559 * u2;
+  *z0 = r * cos(th);
+  *z1 = r * sin(th);
+}
+
+/* Elements [offset, offset + n) of a stream, both Box-Muller outputs of each
+ * pair used; identical values to normal_at(). */
+#define SYNTH_FILL(CONVERT)                                                  \
+  uint64_t key = synth_stream_key(seed, stream);                             \
+  uint64_t p0 = offset >> 1, p1 = (offset + n + 1) >> 1;                     \
+  _Pragma("omp parallel for schedule(static, 32768)")                        \
+  for (int64_t p = (int64_t)p0; p < (int64_t)p1; ++p) {                      \
+    double z[2];                                                             \
+    normal_pair(key, (uint64_t)p, &z[0], &z[1]);                             \
+    for (int q = 0; q < 2; ++q) {                                            \
+      uint64_t i = 2 * (uint64_t)p + (uint64_t)q;                            \
+      if (i < offset || i >= offset + n) continue;                           \
+      out[i - offset] = CONVERT((float)(mean + std * z[q]));                 \
+    }                                                                        \
+  }
+
+#define SYNTH_ID(v) (v)
+
 /* out[j] = fp32(mean + std * z(offset + j)), j < n */
 void synth_normal_f32(uint64_t seed, uint64_t stream, uint64_t offset,
                       uint64_t n, double mean, double std, float *out) {
-  uint64_t key = synth_stream_key(seed, stream);
-#pragma omp parallel for schedule(static, 65536)
-  for (int64_t j = 0; j < (int64_t)n; ++j)
-    out[j] = (float)(mean + std * normal_at(key, offset + (uint64_t)j));
+  SYNTH_FILL(SYNTH_ID)
 }
 
 /* out[j] = bf16(fp32(mean + std * z(offset + j))) as raw bits, j < n */
 void synth_normal_bf16(uint64_t seed, uint64_t stream, uint64_t offset,
                        uint64_t n, double mean, double std, uint16_t *out) {
-  uint64_t key = synth_stream_key(seed, stream);
-#pragma omp parallel for schedule(static, 65536)
-  for (int64_t j = 0; j < (int64_t)n; ++j)
-    out[j] = f32_to_bf16_rne(
-        (float)(mean + std * normal_at(key, offset + (uint64_t)j)));
+  SYNTH_FILL(f32_to_bf16_rne)
 }
 
 /* A seeded permutation of 0..n-1 (Fisher-Yates, draw j picks among i+1). */

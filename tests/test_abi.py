@@ -1,0 +1,136 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects bad arguments before anything is enqueued.  None of
+these calls reaches a GPU (validation returns first), so they run on CPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixture_experts_expert_router_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+E_ARG, E_SHAPE, E_ALIGN, E_WS = 1, 2, 3, 4
+F32, BF16 = 0, 1
+P = 4096        # a fake, 16-byte aligned "device pointer" (never dereferenced)
+P_ODD = 4098    # misaligned
+
+
+@pytest.fixture(scope="module")
+def L():
+    return moe.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = moe.declared_functions()
+    assert {"moe_route_topk", "moe_permute", "moe_grouped_ffn",
+            "moe_unpermute_combine"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_version(L):
+    assert moe.status_string(0) == "ok"
+    for s in range(1, 7):
+        assert moe.status_string(s) not in ("ok", "unknown status")
+    assert moe.status_string(99) == "unknown status"
+    assert moe.version() >= 100
+
+
+def test_workspace_queries_are_pure(L):
+    a = L.moe_permute_workspace_bytes(8192, 8, 256)
+    assert a > 0 and a % 256 == 0
+    assert L.moe_permute_workspace_bytes(8192, 8, 256) == a
+    assert L.moe_permute_workspace_bytes(-1, 8, 256) == 0
+    b = L.moe_grouped_ffn_workspace_bytes(65536, 256, 7168, 2048, BF16)
+    assert b >= 257 * 4 and b % 256 == 0
+    assert L.moe_grouped_ffn_workspace_bytes(10, 0, 64, 64, BF16) == 0
+
+
+def test_route_topk_validation(L):
+    f = L.moe_route_topk
+    # bad dtype, k > E, E too large, k too large
+    assert f(None, None, None, P, 4, 0, 8, 2, 7, P, P, None) == E_ARG
+    assert f(None, None, None, P, 4, 0, 8, 9, F32, P, P, None) == E_SHAPE
+    assert f(None, None, None, P, 4, 0, 2048, 2, F32, P, P, None) == E_SHAPE
+    assert f(None, None, None, P, 4, 0, 64, 33, F32, P, P, None) == E_SHAPE
+    # x without w_router; bias in logits mode; missing outputs
+    assert f(P, None, None, P, 4, 64, 8, 2, BF16, P, P, None) == E_ARG
+    assert f(None, None, P, P, 4, 0, 8, 2, F32, P, P, None) == E_ARG
+    assert f(None, None, None, None, 4, 0, 8, 2, F32, P, P, None) == E_ARG
+    # bf16 router GEMM needs H % 64 == 0 and aligned operands
+    assert f(P, P, None, P, 4, 96, 8, 2, BF16, P, P, None) == E_SHAPE
+    assert f(P_ODD, P, None, P, 4, 128, 8, 2, BF16, P, P, None) == E_ALIGN
+    # nothing to do
+    assert f(None, None, None, None, 0, 0, 8, 2, F32, None, None, None) == 0
+
+
+def test_permute_validation(L):
+    f = L.moe_permute
+    ws = L.moe_permute_workspace_bytes(16, 2, 4)
+    ok = dict(idx=P, w=P, x=P, T=16, k=2, H=64, dt=BF16, eb=0, nl=4, xp=P,
+              sp=P, rs=P, inv=P, cnt=P, off=P, ws=P, wsb=ws)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["idx"], a["w"], a["x"], a["T"], a["k"], a["H"], a["dt"],
+                 a["eb"], a["nl"], a["xp"], a["sp"], a["rs"], a["inv"],
+                 a["cnt"], a["off"], a["ws"], a["wsb"], None)
+
+    assert call(dt=5) == E_ARG
+    assert call(k=0) == E_SHAPE and call(k=33) == E_SHAPE
+    assert call(nl=0) == E_SHAPE and call(nl=5000) == E_SHAPE
+    assert call(eb=-1) == E_SHAPE
+    assert call(cnt=None) == E_ARG and call(off=None) == E_ARG
+    assert call(rs=None) == E_ARG and call(inv=None) == E_ARG
+    assert call(xp=None) == E_ARG
+    assert call(H=60) == E_SHAPE
+    assert call(x=P_ODD) == E_ALIGN
+    assert call(ws=None) == E_WS and call(wsb=ws - 1) == E_WS
+    assert call(ws=P_ODD) == E_ALIGN
+
+
+def test_ffn_validation(L):
+    g = L.moe_grouped_gate_up
+    ws = L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)
+
+    def call(R=64, H=128, I=128, nl=4, dt=BF16, wsp=P, wsb=ws, x=P, off=P):
+        return g(x, off, None, nl, R, H, I, P, P, dt, P, wsp, wsb, None)
+
+    assert call(dt=3) == E_ARG
+    assert call(H=96) == E_SHAPE and call(I=100) == E_SHAPE
+    assert call(nl=0) == E_SHAPE and call(R=-1) == E_SHAPE
+    assert call(off=None) == E_ARG
+    assert call(wsp=None) == E_WS and call(wsb=16) == E_WS
+    assert call(x=None) == E_ARG
+    assert call(x=P_ODD) == E_ALIGN
+    assert call(R=0) == 0  # no rows: nothing enqueued
+    d = L.moe_grouped_down
+    assert d(P, P, 4, 64, 100, 128, P, BF16, P, P, ws, None) == E_SHAPE
+    assert d(P, P, 4, 64, 128, 128, None, BF16, P, P, ws, None) == E_ARG
+
+
+def test_combine_validation(L):
+    c = L.moe_unpermute_combine
+    assert c(P, P, None, 8, 2, 12, BF16, P, None) == E_SHAPE
+    assert c(P, P, None, 8, 0, 16, BF16, P, None) == E_SHAPE
+    assert c(P, P, None, 8, 2, 16, 9, P, None) == E_ARG
+    assert c(P_ODD, P, None, 8, 2, 16, BF16, P, None) == E_ALIGN
+    assert c(None, P, None, 8, 2, 16, BF16, P, None) == E_ARG
+    assert c(None, None, None, 0, 2, 16, BF16, None, None) == 0
+
+
+def _py_sources(d):
+    for root, _, files in os.walk(os.path.join(ROOT, d)):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".hpp", ".cpp", ".h", ".c")):
+                yield os.path.join(root, fn)
+
+
+def test_product_and_oracle_share_nothing():
+    pat_oracle = re.compile(r"^\s*(import|from)\s+oracle\b|moe_oracle|libmoe_oracle", re.M)
+    for path in _py_sources("mixture_experts_expert_router_amd"):
+        assert not pat_oracle.search(open(path, encoding="utf-8").read()), path
+    pat_pkg = re.compile(r"mixture_experts_expert_router_amd|moe_mi355x|csrc/")
+    for path in _py_sources("oracle"):
+        assert not pat_pkg.search(open(path, encoding="utf-8").read()), path

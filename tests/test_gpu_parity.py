@@ -1,0 +1,225 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer outputs (top-k indices, counts, offsets, row_src, inv, x_perm bits)
+must match bit for bit; floats must satisfy max|err| <= tau * RMS(ref) with
+tau = 2e-2 for bf16 and 1e-4 for fp32 (router logits: 1e-4 in both, as they
+accumulate in fp32 from exact inputs).
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_expert_router_amd as moe
+import moe_synth as synth
+import oracle as orc
+from gpu_util import assert_close, print_case, rel_err, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+SMALL = ["tiny_f32", "c1_tiny_f32", "tiny_bf16", "small_bf16",
+         "small_ep_bf16", "mid_bf16"]
+
+
+def bits(a):
+    """Raw bits of a bf16/fp32 tensor or array, for exact comparison."""
+    if isinstance(a, torch.Tensor):
+        a = a.cpu()
+        return (a.view(torch.int16) if a.dtype == torch.bfloat16
+                else a.view(torch.int32)).numpy()
+    return a.view(np.int16) if a.dtype == np.uint16 else a.view(np.int32)
+
+
+def _dt(wl):
+    return "f32" if wl.dtype == "f32" else "bf16"
+
+
+def gpu_chain(wl, d, logits=None):
+    if wl.router == "gemm":
+        idx, w, lg = moe.route_topk(wl.k, x=d["x"], w_router=d["w_router"],
+                                    bias=d.get("bias"))
+    else:
+        idx, w, lg = moe.route_topk(wl.k, logits=d["logits"].clone())
+    p = moe.permute(idx, d["x"], wl.e_begin, wl.n_local, topk_w=w)
+    a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
+                           d["w_up"], d["w_down"])
+    out = moe.unpermute_combine(y, p.inv)
+    moe.debug_sync()
+    return dict(idx=idx, w=w, logits=lg, p=p, a=a, y=y, out=out)
+
+
+@pytest.mark.parametrize("name", SMALL)
+def test_small_workload_stepwise(name):
+    wl = synth.WORKLOADS[name]
+    print_case(name)
+    inp = synth.make_inputs(wl)
+    ref = orc.moe_layer(wl, inp)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    g = gpu_chain(wl, d)
+    dt = _dt(wl)
+    if wl.router == "gemm":
+        assert rel_err(to_f64(g["logits"]), ref["logits"]) <= 1e-4
+    idx = g["idx"].cpu().numpy()
+    np.testing.assert_array_equal(idx, ref["idx"])
+    np.testing.assert_allclose(g["w"].cpu().numpy(), ref["topk_w"], atol=2e-6)
+    p = g["p"]
+    R = ref["R"]
+    np.testing.assert_array_equal(p.counts.cpu().numpy(), ref["counts"])
+    np.testing.assert_array_equal(p.offsets.cpu().numpy(), ref["offsets"])
+    np.testing.assert_array_equal(p.row_src.cpu().numpy()[:R], ref["row_src"])
+    np.testing.assert_array_equal(p.inv.cpu().numpy(), ref["inv"])
+    np.testing.assert_array_equal(bits(p.x_perm[:R]), bits(ref["x_perm"]))
+    np.testing.assert_allclose(p.s_perm[:R].cpu().numpy(), ref["s_perm"], atol=2e-6)
+    print_case(name, "plain err/RMS a %.2e y %.2e out %.2e" % (
+        rel_err(to_f64(g["a"][:R]), ref["a"]), rel_err(to_f64(g["y"][:R]), ref["y"]),
+        rel_err(to_f64(g["out"]), ref["out"])))
+    assert_close(to_f64(g["a"][:R]), ref["a"], dt, f"{name} a")
+    assert_close(to_f64(g["y"][:R]), ref["y"], dt, f"{name} y")
+    assert_close(to_f64(g["out"]), ref["out"], dt, f"{name} out")
+
+
+def test_topk_bit_exact_on_generated_logits():
+    wl = synth.WORKLOADS["c2_ep64_bf16"]
+    print_case("topk", wl.name)
+    l = synth.make_inputs(wl, with_weights=False)["logits"]
+    ridx, rw = orc.topk_softmax(l, wl.k)
+    idx, w, _ = moe.route_topk(wl.k, logits=to_dev(l))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, atol=2e-6)
+    np.testing.assert_allclose(w.sum(1).cpu().numpy(), 1.0, atol=2e-6)
+
+
+@pytest.mark.parametrize("E,k", [(8, 2), (64, 6), (100, 7), (256, 8),
+                                 (300, 3), (1024, 32)])
+def test_topk_ties_and_sizes(E, k):
+    print_case("topk sizes", E, k)
+    rng = np.random.default_rng(E * 31 + k)
+    l = rng.standard_normal((257, E)).astype(np.float32)
+    l[0, :] = 0.5                                   # all equal
+    l[1, ::3] = l[1].max() + 1.0                    # many equal maxima
+    l = np.round(l * 4) / 4                         # plenty of ties
+    ridx, rw = orc.topk_softmax(l, k)
+    idx, w, _ = moe.route_topk(k, logits=to_dev(l))
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, atol=2e-6)
+
+
+def _edge_inputs(counts, n_local, e_begin, E, k, H, I, seed=7):
+    """A routing that gives local experts exactly `counts` slots."""
+    rng = np.random.default_rng(seed)
+    T = max(max(counts), int(np.ceil(sum(counts) / k))) + 5
+    idx = np.full((T, k), -1, dtype=np.int32)
+    slots = []
+    for e, c in enumerate(counts):
+        slots += [e_begin + e] * c
+    rng.shuffle(slots)
+    # fill token by token, never the same expert twice in a token
+    pool = list(slots)
+    t = 0
+    while pool:
+        assert t < T
+        row = []
+        rest = []
+        for s in pool:
+            (rest if s in row or len(row) == k else row).append(s)
+        idx[t, :len(row)] = row
+        pool = rest
+        t += 1
+    nonlocal_experts = [e for e in range(E) if not (e_begin <= e < e_begin + n_local)]
+    for tt in range(T):
+        for j in range(k):
+            if idx[tt, j] < 0:
+                used = set(idx[tt].tolist())
+                cand = [e for e in nonlocal_experts if e not in used]
+                idx[tt, j] = cand[rng.integers(len(cand))]
+    w = rng.random((T, k)); w /= w.sum(1, keepdims=True)
+    x = synth.normal_bf16(seed, 1, 0, T * H, 0.0, 1.0).reshape(T, H)
+    wg = synth.normal_bf16(seed, 10, 0, n_local * I * H, 0.0, 0.05).reshape(n_local, I, H)
+    wu = synth.normal_bf16(seed, 11, 0, n_local * I * H, 0.0, 0.05).reshape(n_local, I, H)
+    wd = synth.normal_bf16(seed, 12, 0, n_local * H * I, 0.0, 0.05).reshape(n_local, H, I)
+    return idx, w, x, wg, wu, wd
+
+
+@pytest.mark.parametrize("counts,e_begin,H,I", [
+    ([0, 1, 129, 256], 0, 320, 192),     # empty expert, tile straddles, N tails
+    ([31, 32, 33, 0, 0, 97], 5, 256, 320),
+    ([300], 2, 128, 64),                 # one expert, three m-tiles
+])
+def test_ffn_edge_segments(counts, e_begin, H, I):
+    print_case("edge", counts, e_begin, H, I)
+    n_local, E, k = len(counts), 16, 4
+    idx, w, x, wg, wu, wd = _edge_inputs(counts, n_local, e_begin, E, k, H, I)
+    p_ref = orc.permute(idx, e_begin, n_local)
+    np.testing.assert_array_equal(p_ref["counts"], counts)
+    xp = orc.gather_rows(x, p_ref["row_src"], k)
+    s = w.reshape(-1)[p_ref["row_src"]]
+    ex = np.repeat(np.arange(n_local, dtype=np.int32), p_ref["counts"])
+    a_ref, y_ref = orc.expert_ffn_rows(xp, ex, s, wg, wu, wd)
+    out_ref = orc.combine(y_ref, p_ref["inv"])
+
+    wt = to_dev(w.astype(np.float32))
+    p = moe.permute(to_dev(idx), to_dev(x), e_begin, n_local, topk_w=wt)
+    a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, to_dev(wg),
+                           to_dev(wu), to_dev(wd))
+    out = moe.unpermute_combine(y, p.inv)
+    moe.debug_sync()
+    R = p_ref["R"]
+    np.testing.assert_array_equal(p.offsets.cpu().numpy(), p_ref["offsets"])
+    np.testing.assert_array_equal(p.row_src.cpu().numpy()[:R], p_ref["row_src"])
+    np.testing.assert_array_equal(p.inv.cpu().numpy(), p_ref["inv"])
+    assert_close(to_f64(a[:R]), a_ref, "bf16", "a")
+    assert_close(to_f64(y[:R]), y_ref, "bf16", "y")
+    o = to_f64(out)
+    assert_close(o, out_ref, "bf16", "out")
+    no_local = (p_ref["inv"] < 0).all(axis=1)
+    assert no_local.any() and not o[no_local].any()
+
+
+def test_scale_in_combine_matches_scale_in_ffn():
+    wl = synth.WORKLOADS["small_bf16"]
+    print_case("scale placement")
+    inp = synth.make_inputs(wl)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    idx, w, _ = moe.route_topk(wl.k, x=d["x"], w_router=d["w_router"],
+                               bias=d["bias"])
+    p = moe.permute(idx, d["x"], 0, wl.n_local, topk_w=w)
+    _, y1 = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
+                            d["w_up"], d["w_down"])
+    o1 = moe.unpermute_combine(y1, p.inv)
+    _, y2 = moe.grouped_ffn(p.x_perm, p.offsets, None, d["w_gate"],
+                            d["w_up"], d["w_down"])
+    o2 = moe.unpermute_combine(y2, p.inv, topk_w=w)
+    moe.debug_sync()
+    ref = orc.moe_layer(wl, inp, scale_in_ffn=False)["out"]
+    assert_close(to_f64(o1), ref, "bf16", "scale in ffn")
+    assert_close(to_f64(o2), ref, "bf16", "scale in combine")
+
+
+def test_empty_token_batch():
+    print_case("T=0")
+    dev = "cuda"
+    l = torch.empty((0, 8), dtype=torch.float32, device=dev)
+    idx, w, _ = moe.route_topk(2, logits=l)
+    assert idx.shape == (0, 2)
+    x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    p = moe.permute(idx, x, 0, 4, topk_w=w)
+    moe.debug_sync()
+    assert p.offsets.cpu().tolist() == [0] * 5
+    assert p.counts.cpu().tolist() == [0] * 4
+    out = moe.unpermute_combine(torch.empty((1, 64), dtype=torch.bfloat16,
+                                            device=dev), p.inv)
+    assert out.shape == (0, 64)
+
+
+def test_bitwise_deterministic():
+    wl = synth.WORKLOADS["mid_bf16"]
+    print_case("determinism")
+    inp = synth.make_inputs(wl)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    g1 = gpu_chain(wl, d)
+    g2 = gpu_chain(wl, d)
+    R = int(g1["p"].offsets[-1])
+    for key in ("idx", "w", "logits", "out"):
+        assert torch.equal(g1[key], g2[key]), key
+    for key in ("a", "y"):
+        assert torch.equal(g1[key][:R], g2[key][:R]), key
+    assert torch.equal(g1["p"].row_src[:R], g2["p"].row_src[:R])
