@@ -1,0 +1,254 @@
+"""Benchmark of the MoE expert-layer path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+router GEMM + softmax/top-k, permute, grouped gate/up with the SwiGLU x
+routing-scale epilogue, grouped down, combine (default workload: the full
+layer, 8192 tokens, hidden 7168, 256 experts, top-8, intermediate 2048).
+The EP-share workloads (--workload c2_ep64_bf16 | c3_ep8_bf16) route before
+the timed region and time permute + FFN + combine.
+
+Prints one JSON line.  `value` is the grouped-FFN (+ router) TFLOP/s of the
+whole step with inputs resident in HBM; `roofline` is for the dominant kernel
+(the grouped gate/up GEMM), timed with HIP events on its stream; `cpu_baseline`
+is the CPU oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mixture_experts_expert_router_amd as moe  # noqa: E402
+import moe_synth as synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+
+
+def to_dev(a, dev):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def make_device_workload(wl, dev, weight_copies):
+    """Inputs on the device; host copies kept for the CPU-baseline leg."""
+    inp = synth.make_inputs(wl, with_weights=False)
+    d = {k: to_dev(v, dev) for k, v in inp.items()}
+    host_w = {"w_gate": [], "w_up": [], "w_down": []}
+    copies = []
+    for c in range(weight_copies):
+        wg = torch.empty((wl.n_local, wl.I, wl.H), dtype=torch.bfloat16, device=dev)
+        wu = torch.empty_like(wg)
+        wd = torch.empty((wl.n_local, wl.H, wl.I), dtype=torch.bfloat16, device=dev)
+        copies.append((wg, wu, wd))
+    step = 32
+    for e0 in range(0, wl.n_local, step):
+        e1 = min(wl.n_local, e0 + step)
+        part = synth.make_weights(wl, range(wl.e_begin + e0, wl.e_begin + e1))
+        for c in copies:
+            for dst, key in zip(c, ("w_gate", "w_up", "w_down")):
+                dst[e0:e1].copy_(to_dev(part[key], dev))
+        for key in host_w:
+            host_w[key].append(part[key])
+    for key in host_w:
+        inp[key] = np.concatenate(host_w[key])
+    return inp, d, copies
+
+
+def algorithmic(wl, R, n_touched):
+    """FLOPs and HBM bytes of one step (see the design doc for the accounting)."""
+    H, I, T, E, k = wl.H, wl.I, wl.T, wl.E, wl.k
+    flop_ffn = 6.0 * R * H * I
+    flop_router = 2.0 * T * H * E if wl.router == "gemm" else 0.0
+    w_bytes = 3.0 * n_touched * H * I * 2
+    act = 2.0
+    gate_up_bytes = 2.0 * n_touched * H * I * 2 + R * H * act + R * I * act
+    step_bytes = (w_bytes + T * H * act            # x read by the permute
+                  + 2 * R * H * act                # x_perm write + read
+                  + 2 * R * I * act                # a write + read
+                  + 2 * R * H * act                # y write + read
+                  + T * H * act)                   # out write
+    if wl.router == "gemm":
+        step_bytes += T * H * act + E * H * act + 2 * T * E * 4
+    return dict(flop_ffn=flop_ffn, flop_router=flop_router,
+                gate_up_flop=4.0 * R * H * I, gate_up_bytes=gate_up_bytes,
+                step_bytes=step_bytes)
+
+
+def cpu_baseline(wl, inp, tokens):
+    """The oracle as it stands, on the first `tokens` tokens of the batch."""
+    import oracle
+    T = tokens
+    x = np.ascontiguousarray(inp["x"][:T])
+    t0 = time.perf_counter()
+    if wl.router == "gemm":
+        l64 = oracle.router_logits(x, inp["w_router"], inp.get("bias"))
+        l32 = l64.astype(np.float32)
+    else:
+        l32 = np.ascontiguousarray(inp["logits"][:T])
+    idx, w = oracle.topk_softmax(l32, wl.k)
+    oracle.moe_tokens(x, idx, w, np.arange(T), wl.e_begin, wl.n_local,
+                      inp["w_gate"], inp["w_up"], inp["w_down"])
+    dt = time.perf_counter() - t0
+    local = (idx >= wl.e_begin) & (idx < wl.e_begin + wl.n_local)
+    rows = int(local.sum())
+    flop = 6.0 * rows * wl.H * wl.I
+    if wl.router == "gemm":
+        flop += 2.0 * T * wl.H * wl.E
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"first {T} tokens of the batch ({rows} token-expert rows): "
+                      f"fp64 router logits + top-k + per-token SwiGLU FFN of the "
+                      f"chosen local experts + weighted sum; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4_full_bf16",
+                    choices=["c4_full_bf16", "c2_ep64_bf16", "c3_ep8_bf16",
+                             "mid_bf16"])
+    ap.add_argument("--cpu-tokens", type=int, default=1536)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU's share of the expert layer; runs on "
+              "more than one GPU are not part of this build (use --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    wl = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    # Weight copies rotate across steps when the weights are small enough for
+    # the 256 MB last-level cache to hold them between steps.
+    wbytes = 3 * wl.n_local * wl.H * wl.I * 2
+    copies = 1 if wbytes > 1.5e9 else 3
+    log(f"workload {wl.name}: generating inputs ({wbytes / 1e9:.2f} GB of "
+        f"weights x {copies})")
+    t0 = time.time()
+    inp, d, wcopies = make_device_workload(wl, dev, copies)
+    log(f"inputs ready in {time.time() - t0:.1f} s")
+
+    stream = torch.cuda.current_stream()
+    T, k, H, I = wl.T, wl.k, wl.H, wl.I
+    F = T * k
+    # Buffers (capacity-sized), allocated once.
+    logits = torch.empty((T, wl.E), dtype=torch.float32, device=dev)
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    pout = moe.PermuteOut(T, k, H, wl.n_local, torch.bfloat16, dev)
+    a = torch.empty((F, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((F, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = moe.ffn_workspace(F, wl.n_local, H, I, torch.bfloat16, dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def route():
+        if wl.router == "gemm":
+            moe.route_topk(k, logits=logits, x=d["x"], w_router=d["w_router"],
+                           bias=d.get("bias"), topk_idx=topk_idx, topk_w=topk_w)
+        else:
+            logits.copy_(d["logits"])
+            moe.route_topk(k, logits=logits, topk_idx=topk_idx, topk_w=topk_w)
+
+    def step(i, timed_ev=None):
+        wg, wu, wd = wcopies[i % len(wcopies)]
+        if wl.router == "gemm":
+            route()
+        moe.permute(topk_idx, d["x"], wl.e_begin, wl.n_local, topk_w=topk_w,
+                    out=pout)
+        if timed_ev is not None:
+            timed_ev[0].record(stream)
+        moe.grouped_gate_up(pout.x_perm, pout.offsets, pout.s_perm, wg, wu,
+                            a=a, workspace=ws)
+        if timed_ev is not None:
+            timed_ev[1].record(stream)
+        moe.grouped_down(a, pout.offsets, wd, y=y, workspace=ws)
+        moe.unpermute_combine(y, pout.inv, out=out)
+
+    if wl.router != "gemm":
+        route()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    R = int(pout.offsets[-1].item())
+    n_touched = int((pout.counts > 0).sum().item())
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_step = elapsed * 1e3 / args.steps
+    gate_up_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+
+    alg = algorithmic(wl, R, n_touched)
+    flop = alg["flop_ffn"] + alg["flop_router"]
+    tflops = flop / (ms_step * 1e-3) / 1e12
+    gu_gbs = alg["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
+    gu_tflops = alg["gate_up_flop"] / (gate_up_ms * 1e-3) / 1e12
+    res = {
+        "metric": "grouped MoE FFN TFLOP/s + rows/s per layer; % MFMA peak or % HBM BW",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded generator; random-init weights)",
+        "config": {
+            "workload": f"{wl.name}: T={T} hidden={H} intermediate={I} "
+                        f"E={wl.E} top-{k}, local experts "
+                        f"[{wl.e_begin},{wl.e_begin + wl.n_local})",
+            "rows": R, "experts_touched": n_touched,
+            "router": "router GEMM + softmax/top-k in the step"
+                      if wl.router == "gemm" else "routed before timing",
+        },
+        "rows_per_s": round(R / (ms_step * 1e-3), 1),
+        "step_hbm_gbs": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9, 1),
+        "step_hbm_frac": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "step_mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "roofline": {
+            "kernel": "grouped gate/up GEMM + SwiGLU x scale",
+            "bound": "hbm",
+            "achieved": round(gu_gbs, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "avg_ms": round(gate_up_ms, 4),
+            "tflops": round(gu_tflops, 2),
+            "mfma_frac": round(gu_tflops / BF16_PEAK_TFLOPS, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
+        res["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_tokens, T))
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
