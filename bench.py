@@ -125,6 +125,9 @@ def main():
                              "mid_bf16"])
     ap.add_argument("--cpu-tokens", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after timing, run one elementwise copy of this many "
+                         "MiB (read + write) to calibrate HBM byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -200,6 +203,16 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
     gate_up_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n * 2} bytes read, {n * 2} bytes written")
+        del src, dst
 
     alg = algorithmic(wl, R, n_touched)
     flop = alg["flop_ffn"] + alg["flop_router"]

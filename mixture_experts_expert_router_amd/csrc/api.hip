@@ -33,7 +33,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
 
 size_t tile_ws_bytes(int64_t n_local) {
-  return (size_t)(((n_local + 1) * 4 + 255) / 256 * 256);
+  return moe::gemm_workspace_bytes(n_local);
 }
 
 }  // namespace

@@ -8,30 +8,35 @@
 // Wide-EP explainer (効果2:演算強度が上がる) gives why: gathering all of an
 // expert's tokens into one GEMM reuses each weight byte read from HBM.
 //
-// Design (one launch per GEMM, all experts):
+// Design (one launch per expert-size class, all experts of that class):
 //   * C[r, n] = sum_k A[r, k] * B_e[n, k] for the rows r of expert e's
 //     segment [offsets[e], offsets[e+1]); A and B are K-contiguous bf16.
-//   * Work unit = tile of BM rows x BN B-rows of one expert.  A small plan
-//     kernel turns the device-side offsets into a tile prefix, so the host
-//     never needs the per-expert counts.
-//   * Persistent grid: every workgroup walks the tile list with stride
-//     gridDim.x.  Workgroups are renumbered so that consecutive logical
-//     workgroups sit on the same XCD (hardware places workgroup b on XCD
-//     b % 8), and tiles are ordered (expert, n-tile, m-tile): the m-tiles of
-//     one weight strip, and the n-tiles next to them, run at the same time on
-//     one XCD and share its L2.
+//   * Work unit = tile of BM rows x BN B-rows of one expert.  A plan kernel
+//     turns the device-side offsets into tile prefixes for two classes of
+//     experts: those with at most kSmallRows rows (decode-like shares, run
+//     with 64-row tiles) and the rest (128- or 256-row tiles).  Each class has its
+//     own persistent launch; a launch whose class is empty exits at once.
+//     The host never needs the per-expert counts.
+//   * Persistent grid: every workgroup walks its tile list with stride
+//     gridDim.x.  Workgroups are renumbered so consecutive logical workgroups
+//     sit on the same XCD (hardware places workgroup b on XCD b % 8); tiles
+//     are ordered (expert, n-tile, m-tile), so the m-tiles of one weight strip
+//     and the neighbouring n-tiles run together on one XCD and share its L2.
 //   * 256 threads = 4 wavefronts in a WM x WN grid; each wavefront owns a
-//     (BM/WM) x (BN/WN) sub-tile made of 32x32 blocks computed with
-//     v_mfma_f32_32x32x16_bf16 (fp32 accumulators in registers).
-//   * K is walked in steps of 64: global -> registers -> LDS (double buffer),
-//     the next step's global loads in flight while the current one computes.
-//     LDS rows are 128 B; 16-byte chunks are XOR-swizzled by (row & 7) so the
-//     fragment reads of 8 consecutive rows hit distinct banks.
-//   * 32-row sub-tiles past the end of an expert's segment are skipped (the
-//     branch is uniform per wavefront), so a tile with 16 rows costs one
-//     32-row MFMA pass, not BM/32.
+//     (BM/WM) x (BN/WN) sub-tile of 32x32 blocks, v_mfma_f32_32x32x16_bf16
+//     with fp32 accumulators.
+//   * K advances BK (32 or 64) at a time through a STAGES-deep ring of LDS
+//     buffers filled by direct global->LDS loads (global_load_lds_dwordx4, no
+//     register staging).  The loads are issued from inline assembly, so the
+//     compiler does not serialise them against LDS reads; the kernel waits
+//     for them itself: `s_waitcnt vmcnt(n)` for its own loads of the stage
+//     about to be used, then a workgroup barrier.  Each lane's global address
+//     is chosen so that 16-byte chunks land XOR-swizzled in LDS (conflict-free
+//     fragment reads) while every 8 lanes still read one contiguous row piece.
+//   * 32-row sub-tiles past the end of an expert's segment are skipped
+//     (uniform per wavefront).
 //   * Epilogues: SWIGLU (B rows interleaved as 16 gate + 16 up per 32-row
-//     block, so one lane swap pairs g and u of the same output; writes
+//     block, one lane swap pairs g and u of the same output; writes
 //     a = s * SiLU(g) * u in bf16), BF16 (plain store) and F32_BIAS (router
 //     logits + bias).
 #include "common.hpp"
@@ -49,7 +54,7 @@ struct GemmArgs {
   const float *row_scale;   // SWIGLU: per-row routing scale, may be null
   const float *bias;        // F32_BIAS: [N] or null
   const int32_t *offsets;   // [G + 1] row offsets, or null: one group
-  const int32_t *tile_prefix;  // [G + 1] tile prefix (grouped mode)
+  const int32_t *tile_prefix;  // [G + 1] tile prefix of this launch's class
   int single_rows;          // rows of the single group (offsets == null)
   int G;                    // groups
   int N;                    // output columns (a-columns for SWIGLU)
@@ -57,59 +62,185 @@ struct GemmArgs {
   int NT;                   // n-tiles per m-tile
 };
 
-constexpr int BK = 64;
+// Experts with at most this many rows run on the 64-row-tile kernel.
+constexpr int kSmallRows = 64;
 
-// tile_prefix[e+1] = tile_prefix[e] + ceil(rows_e / BM) * NT, one block.
+// Per class c (0 = small, 1 = large): prefix_c[e+1] = prefix_c[e] +
+// ceil(rows_e / BM_c) * NT_c when expert e belongs to class c.  One block.
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(
-    const int32_t *__restrict__ offsets, int G, int BM, int NT,
-    int32_t *__restrict__ tile_prefix) {
-  __shared__ int32_t part[1024];
+    const int32_t *__restrict__ offsets, int G, int bm_small, int nt_small,
+    int bm_large, int nt_large, int32_t *__restrict__ prefix_small,
+    int32_t *__restrict__ prefix_large) {
+  __shared__ int32_t part[2][1024];
   const int tid = threadIdx.x;
   const int per = (G + 1023) / 1024;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
-  int32_t s = 0;
-  for (int e = e0; e < e1; ++e)
-    s += (offsets[e + 1] - offsets[e] + BM - 1) / BM * NT;
-  part[tid] = s;
+  int32_t s0 = 0, s1 = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int n = offsets[e + 1] - offsets[e];
+    if (n <= kSmallRows) s0 += (n + bm_small - 1) / bm_small * nt_small;
+    else s1 += (n + bm_large - 1) / bm_large * nt_large;
+  }
+  part[0][tid] = s0;
+  part[1][tid] = s1;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = tid >= off ? part[tid - off] : 0;
+    const int32_t v0 = tid >= off ? part[0][tid - off] : 0;
+    const int32_t v1 = tid >= off ? part[1][tid - off] : 0;
     __syncthreads();
-    part[tid] += v;
+    part[0][tid] += v0;
+    part[1][tid] += v1;
     __syncthreads();
   }
-  int32_t run = part[tid] - s;
+  int32_t r0 = part[0][tid] - s0, r1 = part[1][tid] - s1;
   for (int e = e0; e < e1; ++e) {
-    tile_prefix[e] = run;
-    run += (offsets[e + 1] - offsets[e] + BM - 1) / BM * NT;
+    prefix_small[e] = r0;
+    prefix_large[e] = r1;
+    const int n = offsets[e + 1] - offsets[e];
+    if (n <= kSmallRows) r0 += (n + bm_small - 1) / bm_small * nt_small;
+    else r1 += (n + bm_large - 1) / bm_large * nt_large;
   }
-  if (tid == 1023) tile_prefix[G] = part[1023];
+  if (tid == 1023) {
+    prefix_small[G] = part[0][1023];
+    prefix_large[G] = part[1][1023];
+  }
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+// Wait until at most N of this wavefront's vector-memory loads are in flight
+// and its LDS reads are done, then join the workgroup barrier.  The "memory"
+// clobber keeps the compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void wait_loads_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_waitcnt lgkmcnt(0)\n\ts_barrier"
+               :: "i"(N) : "memory");
+}
+
+// Direct global -> LDS load of 16 bytes per lane: lane l's data goes to LDS
+// byte address lds_base + 16 * l (lds_base uniform over the wavefront).
+__device__ __forceinline__ void load_lds16(uint32_t lds_base, const void *g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(g) : "memory");
+}
+
+// Physical 16-byte chunk of logical chunk c of LDS row `row` (CPR chunks per
+// row).  A ds_read_b128 serves 16 lanes (256 bytes of banks) at a time, and
+// the fragment reads put 16 consecutive rows at one logical chunk in such a
+// group: with 128-byte rows, rows of equal parity must get distinct chunks
+// (c ^ (row/2 % 8)); with 64-byte rows, rows equal mod 4 must
+// (c ^ (row/4 % 4)).  Either way the 16 reads cover all 16 bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz(int row, int c) {
+  return CPR == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
+}
+
+// Load the A and B fragments of k-substep kk (16 values of K) from one LDS
+// stage: lane holds row (lane & 31) of each 32-row block, K chunk
+// 2*kk + lane/32.
+template <int CPR, int MV, int NB>
+__device__ __forceinline__ void load_frags(const uint4 *As, const uint4 *Bs,
+                                           int kk, int lane, int arow0,
+                                           int brow0, bf16x8 (&af)[MV],
+                                           bf16x8 (&bf)[NB]) {
+  const int ch = 2 * kk + (lane >> 5);
+#pragma unroll
+  for (int m = 0; m < MV; ++m) {
+    const int row = arow0 + m * 32 + (lane & 31);
+    const uint4 v = As[row * CPR + swz<CPR>(row, ch)];
+    af[m] = *(const bf16x8 *)&v;
+  }
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
+    const int row = brow0 + n * 32 + (lane & 31);
+    const uint4 v = Bs[row * CPR + swz<CPR>(row, ch)];
+    bf[n] = *(const bf16x8 *)&v;
+  }
+}
+
+// The K loop of one tile for a wavefront with MV valid 32-row blocks.
+// Stages 0 .. STAGES-2 have been issued by the caller.  Fragment reads of
+// k-substep kk+1 are issued before the MFMAs of kk so LDS latency overlaps
+// matrix work; the loop body has no data-dependent branches.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MV>
+__device__ __forceinline__ void gemm_kloop(
+    f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
+    const char *const (&gsrc)[(BM + BN) * (BK / 8) / 256], const uint4 *smem,
+    uint32_t lds0, uint32_t wave_off, int KT, int lane, int arow0,
+    int brow0) {
+  constexpr int CPR = BK / 8, NB = BN / WN / 32, KK = BK / 16;
+  constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
+  constexpr int L = STAGE_CHUNKS / 256;
+  for (int kt = 0; kt < KT; ++kt) {
+    // Stage kt has landed once at most min(STAGES-2, KT-1-kt) later stages
+    // of this wavefront are still in flight; the barrier then also says
+    // every wavefront is done with the buffer refilled just below.
+    const int after = min(STAGES - 2, KT - 1 - kt);
+    if (after >= 4) wait_loads_barrier<(STAGES >= 6 ? 4 : 0) * L>();
+    else if (after == 3) wait_loads_barrier<(STAGES >= 5 ? 3 : 0) * L>();
+    else if (after == 2) wait_loads_barrier<(STAGES >= 4 ? 2 : 0) * L>();
+    else if (after == 1) wait_loads_barrier<L>();
+    else wait_loads_barrier<0>();
+    if (kt + STAGES - 1 < KT) {
+      const int st = (kt + STAGES - 1) % STAGES;
+      const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
+      const int64_t koff = (int64_t)(kt + STAGES - 1) * (BK * 2);
+#pragma unroll
+      for (int i = 0; i < L; ++i)
+        load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
+    }
+    if constexpr (MV > 0) {
+      const uint4 *As = smem + (kt % STAGES) * STAGE_CHUNKS;
+      const uint4 *Bs = As + BM * CPR;
+      bf16x8 a0[MV], b0[NB], a1[MV], b1[NB];
+      load_frags<CPR, MV, NB>(As, Bs, 0, lane, arow0, brow0, a0, b0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        if (kk + 1 < KK) {
+          if (kk & 1) load_frags<CPR, MV, NB>(As, Bs, kk + 1, lane, arow0, brow0, a0, b0);
+          else load_frags<CPR, MV, NB>(As, Bs, kk + 1, lane, arow0, brow0, a1, b1);
+        }
+#pragma unroll
+        for (int m = 0; m < MV; ++m)
+#pragma unroll
+          for (int n = 0; n < NB; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                (kk & 1) ? a1[m] : a0[m], (kk & 1) ? b1[n] : b0[n], acc[m][n],
+                0, 0, 0);
+      }
+    }
+  }
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
+  constexpr int CPR = BK / 8;                  // 16-byte chunks per row
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
-  constexpr int CPR = BK / 8;  // 16-byte chunks per LDS row
-  constexpr int A_PER_T = BM * CPR / 256, B_PER_T = BN * CPR / 256;
+  constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
+  constexpr int L = STAGE_CHUNKS / 256;        // loads per thread per stage
+  constexpr int LA = BM * CPR / 256;           // of which A rows
   static_assert(WM * WN == 4, "four wavefronts");
   static_assert(MB >= 1 && NB >= 1, "wave tile is a multiple of 32x32");
-  static_assert(A_PER_T >= 1 && B_PER_T >= 1, "tile too small");
-  __shared__ uint4 smem[2][(BM + BN) * CPR];
+  static_assert(BM * CPR % 256 == 0 && BN * CPR % 256 == 0, "load split");
+  static_assert(BK == 32 || BK == 64, "BK");
+  static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 2) * L <= 63,
+                "vmcnt range");
+  __shared__ uint4 smem[STAGES * STAGE_CHUNKS];
 
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int wm = wid / WN, wn = wid % WN;
   const int K = p.K;
   const int KT = K / BK;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
   int total;
   if (p.offsets) total = p.tile_prefix[p.G];
   else total = (p.single_rows + BM - 1) / BM * p.NT;
 
   const int nwg = gridDim.x, bid = blockIdx.x;
-  const int L = (bid & 7) * (nwg >> 3) + (bid >> 3);
+  const int Lg = (bid & 7) * (nwg >> 3) + (bid >> 3);
 
-  for (int t = L; t < total; t += nwg) {
+  for (int t = Lg; t < total; t += nwg) {
     int e, r_begin, r_end, local;
     if (p.offsets) {
       e = upper_bound_minus1(p.tile_prefix, p.G, t);
@@ -124,30 +255,38 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     const int row0 = r_begin + mt * BM;
     const int rows = min(BM, r_end - row0);
 
-    // Per-thread global source pointers for the A and B chunks it loads.
-    const uint16_t *a_src[A_PER_T];
-    const uint16_t *b_src[B_PER_T];
+    // Global source of each of this thread's L loads per stage.  The stage
+    // is cut into groups of 64 chunks (one load instruction each); wavefront
+    // w issues groups [w*L, w*L + L), so with BM == BN two wavefronts load
+    // only A rows (mostly L2 hits) and two only B rows (weight stream): a
+    // wavefront's loads return in order, and this keeps the quick hits out
+    // of the queue behind slow misses.  Chunk q = (w*L + i)*64 + lane.
+    const char *gsrc[L];
 #pragma unroll
-    for (int i = 0; i < A_PER_T; ++i) {
-      const int c = tid + i * 256, row = c / CPR, kc = c % CPR;
-      a_src[i] = p.A + (int64_t)(row0 + min(row, rows - 1)) * K + kc * 8;
-    }
-#pragma unroll
-    for (int i = 0; i < B_PER_T; ++i) {
-      const int c = tid + i * 256, j = c / CPR, kc = c % CPR;
-      const uint16_t *base;
-      int col;
-      if (EPI == EPI_SWIGLU) {
-        const int w = j & 31;
-        col = nt * (BN / 2) + (j >> 5) * 16 + (w & 15);
-        base = w < 16 ? p.B0 : p.B1;
+    for (int i = 0; i < L; ++i) {
+      const int q = (wid * L + i) * 64 + lane;
+      const int row = q / CPR;
+      if (row < BM) {
+        const int kc = swz<CPR>(row, q % CPR);
+        gsrc[i] = (const char *)(p.A + (int64_t)(row0 + min(row, rows - 1)) * K + kc * 8);
       } else {
-        col = nt * BN + j;
-        base = p.B0;
+        const int j = row - BM;
+        const int kc = swz<CPR>(j, q % CPR);
+        const uint16_t *base;
+        int col;
+        if (EPI == EPI_SWIGLU) {
+          const int w = j & 31;
+          col = nt * (BN / 2) + (j >> 5) * 16 + (w & 15);
+          base = w < 16 ? p.B0 : p.B1;
+        } else {
+          col = nt * BN + j;
+          base = p.B0;
+        }
+        col = min(col, p.N - 1);
+        gsrc[i] = (const char *)(base + (int64_t)e * p.b_stride + (int64_t)col * K + kc * 8);
       }
-      col = min(col, p.N - 1);
-      b_src[i] = base + (int64_t)e * p.b_stride + (int64_t)col * K + kc * 8;
     }
+    const uint32_t wave_off = (uint32_t)(wid * L * 64 * 16);
 
     f32x16 acc[MB][NB];
 #pragma unroll
@@ -157,71 +296,40 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
 
-    uint4 ra[A_PER_T], rb[B_PER_T];
-#define MOE_GLOAD(kt_)                                                    \
-  {                                                                       \
-    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) ra[i] =           \
-        *(const uint4 *)(a_src[i] + (kt_) * BK);                          \
-    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) rb[i] =           \
-        *(const uint4 *)(b_src[i] + (kt_) * BK);                          \
-  }
-#define MOE_SSTORE(buf_)                                                  \
-  {                                                                       \
-    _Pragma("unroll") for (int i = 0; i < A_PER_T; ++i) {                 \
-      const int c = tid + i * 256, row = c / CPR, kc = c % CPR;           \
-      smem[buf_][row * CPR + (kc ^ (row & 7))] = ra[i];                   \
-    }                                                                     \
-    _Pragma("unroll") for (int i = 0; i < B_PER_T; ++i) {                 \
-      const int c = tid + i * 256, row = c / CPR, kc = c % CPR;           \
-      smem[buf_][(BM + row) * CPR + (kc ^ (row & 7))] = rb[i];            \
-    }                                                                     \
-  }
-
-    // number of valid 32-row blocks of this wavefront
     const int wrow0 = wm * WTM;
     const int mvalid = rows > wrow0 ? min(MB, (rows - wrow0 + 31) / 32) : 0;
 
-    MOE_GLOAD(0);
-    MOE_SSTORE(0);
-    __syncthreads();
-    for (int kt = 0; kt < KT; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < KT) MOE_GLOAD(kt + 1);
-      if (mvalid > 0) {
-        const uint4 *As = smem[buf];
-        const uint4 *Bs = smem[buf] + BM * CPR;
+    const int brow0 = wn * WTN;
+    // prologue: stages 0 .. STAGES-2
 #pragma unroll
-        for (int kk = 0; kk < BK / 16; ++kk) {
-          const int ch = 2 * kk + (lane >> 5);
-          bf16x8 af[MB], bfr[NB];
+    for (int st = 0; st < STAGES - 1; ++st) {
+      if (st < KT) {
+        const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
 #pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            const int row = wrow0 + m * 32 + (lane & 31);
-            const uint4 v = As[row * CPR + (ch ^ (row & 7))];
-            af[m] = *(const bf16x8 *)&v;
-          }
-#pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            const int row = wn * WTN + n * 32 + (lane & 31);
-            const uint4 v = Bs[row * CPR + (ch ^ (row & 7))];
-            bfr[n] = *(const bf16x8 *)&v;
-          }
-#pragma unroll
-          for (int m = 0; m < MB; ++m) {
-            if (m < mvalid) {
-#pragma unroll
-              for (int n = 0; n < NB; ++n)
-                acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                    af[m], bfr[n], acc[m][n], 0, 0, 0);
-            }
-          }
-        }
+        for (int i = 0; i < L; ++i)
+          load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + (int64_t)st * (BK * 2));
       }
-      if (kt + 1 < KT) MOE_SSTORE(buf ^ 1);
-      __syncthreads();
     }
-#undef MOE_GLOAD
-#undef MOE_SSTORE
+    // the K loop, specialised for this wavefront's number of valid blocks
+    // (a wavefront with none still keeps the loads and barriers going)
+    switch (mvalid) {
+#define MOE_KLOOP_CASE(mv)                                                    \
+      case mv:                                                                \
+        if (mv <= MB)                                                         \
+          gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1)>(        \
+              acc, gsrc, smem, lds0, wave_off, KT, lane, wrow0, brow0);       \
+        break;
+      MOE_KLOOP_CASE(1)
+      MOE_KLOOP_CASE(2)
+      MOE_KLOOP_CASE(3)
+      MOE_KLOOP_CASE(4)
+#undef MOE_KLOOP_CASE
+      default:
+        gemm_kloop<BM, BN, WM, WN, BK, STAGES, 0>(
+            acc, gsrc, smem, lds0, wave_off, KT, lane, wrow0, brow0);
+    }
+    // every wavefront is done reading the ring before the next tile refills it
+    wait_loads_barrier<0>();
 
     // Epilogue.  Lane holds column (lane & 31) of each 32x32 block and rows
     // 8*(r/4) + 4*(lane/32) + (r%4), r < 16.
@@ -264,27 +372,71 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
 
 namespace {
 
-template <int BM, int BN, int WM, int WN, int EPI>
-hipError_t launch_cfg(GemmArgs p, int num_cus, int32_t *tile_ws,
-                      int64_t max_rows, hipStream_t s) {
-  p.NT = EPI == EPI_SWIGLU ? (p.N + BN / 2 - 1) / (BN / 2)
-                           : (p.N + BN - 1) / BN;
-  int64_t max_tiles;
-  if (p.offsets) {
-    p.tile_prefix = tile_ws;
-    gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, BM, p.NT, tile_ws);
-    max_tiles = ((max_rows + BM - 1) / BM + p.G) * (int64_t)p.NT;
-  } else {
-    max_tiles = (max_rows + BM - 1) / BM * (int64_t)p.NT;
-  }
-  int64_t grid = num_cus;  // one 256-thread workgroup per CU
+// BM, BN, WM, WN, BK, STAGES of the wide large-expert shape.
+#ifndef MOE_WIDE_CFG
+#define MOE_WIDE_CFG 128, 256, 2, 2, 64, 3
+#endif
+
+int ntiles(int N, int BN, bool swiglu) {
+  const int cols = swiglu ? BN / 2 : BN;
+  return (N + cols - 1) / cols;
+}
+
+template <int BM, int BN, int WM, int WN, int BK, int ST, int EPI>
+hipError_t launch_one(GemmArgs p, int num_cus, int64_t max_tiles,
+                      hipStream_t s) {
+  // Workgroups resident per CU: 160 KiB of LDS shared out.
+  constexpr int lds_bytes = ST * (BM + BN) * BK * 2;
+  constexpr int occ = lds_bytes <= 80 * 1024 ? 2 : 1;
+  int64_t grid = (int64_t)num_cus * occ;
   if (max_tiles < grid) grid = (max_tiles + 7) / 8 * 8;
   if (grid < 8) grid = 8;
-  grouped_gemm_kernel<BM, BN, WM, WN, EPI><<<(unsigned)grid, 256, 0, s>>>(p);
+  grouped_gemm_kernel<BM, BN, WM, WN, BK, ST, EPI>
+      <<<(unsigned)grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
+// Tile shapes.  Large experts: 128 rows x 256 B-rows (BK 64, 3 stages), or
+// 256 x 64 (BK 64, 3 stages) when there are too few experts to give every CU
+// two n-tiles of the wide shape.  Small experts: 64 x 256 (BK 64, 3 stages).
+template <int EPI>
+hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
+                          int64_t R_cap, hipStream_t s) {
+  const bool sw = EPI == EPI_SWIGLU;
+  constexpr int wide_cfg[6] = {MOE_WIDE_CFG};
+  constexpr int WBM = wide_cfg[0], WBN = wide_cfg[1];
+  const bool wide = (int64_t)p.G * ntiles(p.N, WBN, sw) >= 2LL * num_cus;
+  const int bm_l = wide ? WBM : 256;
+  const int nt_l = ntiles(p.N, wide ? WBN : 64, sw);
+  const int nt_s = ntiles(p.N, 256, sw);
+  int32_t *pre_s = tile_ws;
+  int32_t *pre_l = tile_ws + (p.G + 1);
+  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, 64, nt_s, bm_l, nt_l,
+                                      pre_s, pre_l);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // small-row class
+  GemmArgs ps = p;
+  ps.tile_prefix = pre_s;
+  ps.NT = nt_s;
+  err = launch_one<64, 256, 1, 4, 64, 3, EPI>(ps, num_cus,
+                                              (int64_t)p.G * nt_s, s);
+  if (err != hipSuccess) return err;
+  // large-row class
+  GemmArgs pl = p;
+  pl.tile_prefix = pre_l;
+  pl.NT = nt_l;
+  const int64_t max_l = ((R_cap + bm_l - 1) / bm_l + p.G) * (int64_t)nt_l;
+  if (wide)
+    return launch_one<MOE_WIDE_CFG, EPI>(pl, num_cus, max_l, s);
+  return launch_one<256, 64, 4, 1, 64, 3, EPI>(pl, num_cus, max_l, s);
+}
+
 }  // namespace
+
+size_t gemm_workspace_bytes(int64_t n_local) {
+  return (size_t)((2 * (n_local + 1) * 4 + 255) / 256 * 256);
+}
 
 hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                const float *s_perm, int n_local, int64_t R_cap,
@@ -296,7 +448,7 @@ hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
   p.b_stride = (int64_t)I * H;
   p.C = a; p.ldc = I; p.row_scale = s_perm;
   p.offsets = offsets; p.G = n_local; p.N = I; p.K = H;
-  return launch_cfg<128, 256, 2, 2, EPI_SWIGLU>(p, num_cus, tile_ws, R_cap, s);
+  return launch_grouped<EPI_SWIGLU>(p, num_cus, tile_ws, R_cap, s);
 }
 
 hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
@@ -308,7 +460,7 @@ hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
   p.b_stride = (int64_t)H * I;
   p.C = y; p.ldc = H;
   p.offsets = offsets; p.G = n_local; p.N = H; p.K = I;
-  return launch_cfg<128, 256, 2, 2, EPI_BF16>(p, num_cus, tile_ws, R_cap, s);
+  return launch_grouped<EPI_BF16>(p, num_cus, tile_ws, R_cap, s);
 }
 
 hipError_t launch_router_gemm_bf16(const uint16_t *x, const uint16_t *w,
@@ -319,7 +471,9 @@ hipError_t launch_router_gemm_bf16(const uint16_t *x, const uint16_t *w,
   p.C = logits; p.ldc = E;
   p.bias = bias;
   p.offsets = nullptr; p.single_rows = (int)T; p.G = 1; p.N = E; p.K = H;
-  return launch_cfg<64, 64, 2, 2, EPI_F32_BIAS>(p, num_cus, nullptr, T, s);
+  p.NT = ntiles(E, 64, false);
+  const int64_t max_tiles = (T + 63) / 64 * (int64_t)p.NT;
+  return launch_one<64, 64, 2, 2, 64, 4, EPI_F32_BIAS>(p, num_cus, max_tiles, s);
 }
 
 }  // namespace moe

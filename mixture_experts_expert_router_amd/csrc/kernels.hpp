@@ -28,6 +28,9 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
                           int32_t *counts, int32_t *offsets, void *ws,
                           int num_cus, hipStream_t s);
 
+// Workspace of one grouped GEMM launch: two tile prefixes of n_local + 1.
+size_t gemm_workspace_bytes(int64_t n_local);
+
 hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                const float *s_perm, int n_local, int64_t R_cap,
                                int H, int I, const uint16_t *w_gate,
