@@ -70,6 +70,7 @@ def _lib():
         L.orc_mx_quantize_rows.argtypes = [vp, i64, i64, vp, vp]
         L.orc_mx_dequantize_rows.argtypes = [vp, vp, i64, i64, vp]
         L.orc_matmul_nt.argtypes = [vp, vp, i64, i64, i64, vp]
+        L.orc_round_bf16.argtypes = [vp, i64, vp]
         L.orc_swiglu_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp,
                                           vp]
         _L = L
@@ -303,6 +304,14 @@ def to_f64(a):
     return a.astype(np.float64)
 
 
+def round_bf16(v):
+    """Nearest bfloat16 value of each element (ties to even), as fp64."""
+    v = _c(v, np.float64)
+    out = np.empty_like(v)
+    _lib().orc_round_bf16(_p(v), v.size, _p(out))
+    return out
+
+
 def matmul_nt(A, B):
     A, B = _c(A, np.float64), _c(B, np.float64)
     M, K = A.shape
@@ -322,7 +331,7 @@ def swiglu_bwd(da, g, u, s):
 
 
 def mxfp8_mlp_step(x_perm, offsets, s_perm, w_gate, w_up, w_down, dy,
-                   quantize=True):
+                   quantize=True, handoff=None):
     """MXFP8 grouped MLP forward + backward on permuted rows, fp64.
 
     Every GEMM operand is MX-quantised (blocks of 32) along that GEMM's
@@ -337,7 +346,18 @@ def mxfp8_mlp_step(x_perm, offsets, s_perm, w_gate, w_up, w_down, dy,
     All inputs are bf16 bits (uint16) or fp64; returns fp64 arrays.
     ``quantize=False`` replaces every Q by the identity (the same chain rule
     on unquantised operands), which the finite-difference pins check.
+
+    ``handoff`` (default: same as ``quantize``) stores the tensors that pass
+    from one operation to the next in bf16 before they are used, as in a
+    BF16 training step whose GEMMs run in MXFP8 ([TE-MXFP8]): a before the
+    down projection and its weight gradient, the saved g and u before the
+    SwiGLU backward, dg and du before their GEMMs.  Each quantisation then
+    starts from the bf16 tensor, as it does on the device.  The returned
+    g, u, a, dg, du are the fp64 values before that rounding.
     """
+    if handoff is None:
+        handoff = quantize
+    bf = round_bf16 if handoff else (lambda v: v)
     if quantize:
         q_rows, q_cols = mx_roundtrip_rows, mx_roundtrip_cols
     else:
@@ -365,22 +385,24 @@ def mxfp8_mlp_step(x_perm, offsets, s_perm, w_gate, w_up, w_down, dy,
         g[r0:r1] = matmul_nt(xe, q_rows(Wg))
         u[r0:r1] = matmul_nt(xe, q_rows(Wu))
         a[r0:r1] = s[r0:r1, None] * (g[r0:r1] / (1.0 + np.exp(-g[r0:r1]))) * u[r0:r1]
-        y[r0:r1] = matmul_nt(q_rows(a[r0:r1]), q_rows(Wd))
+        a_h = bf(a[r0:r1])
+        y[r0:r1] = matmul_nt(q_rows(a_h), q_rows(Wd))
         # dgrad of down: da[r, i] = sum_h dY[r, h] Wd[h, i], K = H
         da[r0:r1] = matmul_nt(dyq_h[r0:r1], np.ascontiguousarray(q_cols(Wd).T))
-        dg[r0:r1], du[r0:r1], ds[r0:r1] = swiglu_bwd(da[r0:r1], g[r0:r1],
-                                                      u[r0:r1], s[r0:r1])
+        dg[r0:r1], du[r0:r1], ds[r0:r1] = swiglu_bwd(
+            da[r0:r1], bf(g[r0:r1]), bf(u[r0:r1]), s[r0:r1])
+        dg_h, du_h = bf(dg[r0:r1]), bf(du[r0:r1])
         # dgrad of gate/up: dX[r, h] = sum_i dg[r,i] Wg[i,h] + du[r,i] Wu[i,h]
         WgT = np.ascontiguousarray(q_cols(Wg).T)
         WuT = np.ascontiguousarray(q_cols(Wu).T)
-        dx[r0:r1] = (matmul_nt(q_rows(dg[r0:r1]), WgT)
-                     + matmul_nt(q_rows(du[r0:r1]), WuT))
+        dx[r0:r1] = (matmul_nt(q_rows(dg_h), WgT)
+                     + matmul_nt(q_rows(du_h), WuT))
         # wgrad: reduction over the segment's rows
         dyr = np.ascontiguousarray(q_cols(dY[r0:r1]).T)   # [H, n]
-        ar = np.ascontiguousarray(q_cols(a[r0:r1]).T)     # [I, n]
+        ar = np.ascontiguousarray(q_cols(a_h).T)          # [I, n]
         xr = np.ascontiguousarray(q_cols(x[r0:r1]).T)     # [H, n]
-        dgr = np.ascontiguousarray(q_cols(dg[r0:r1]).T)   # [I, n]
-        dur = np.ascontiguousarray(q_cols(du[r0:r1]).T)
+        dgr = np.ascontiguousarray(q_cols(dg_h).T)        # [I, n]
+        dur = np.ascontiguousarray(q_cols(du_h).T)
         dwd[e] = matmul_nt(dyr, ar)
         dwg[e] = matmul_nt(dgr, xr)
         dwu[e] = matmul_nt(dur, xr)

@@ -25,6 +25,7 @@
 //
 // Data type codes for tensors passed as void*: 0 = fp32, 1 = bf16 (raw
 // uint16 bits), 2 = fp64.
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -349,6 +350,30 @@ void orc_mx_dequantize_rows(const uint8_t *codes, const uint8_t *scales,
     for (int64_t c = 0; c < cols; ++c)
       v[r * cols + c] = std::ldexp(orc_e4m3_value(codes[r * cols + c]),
                                    (int)scales[r * nb + c / 32] - 127);
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16 storage of a value: 8 significant bits (1 implicit + 7 stored),
+// 8 exponent bits like fp32.  [TE-MXFP8]: the tensors handed from one
+// operation to the next stay in BF16; only the GEMM inputs are MX-quantised.
+// Nearest bf16 value, ties to the even significand; values below bf16's
+// normal range use its subnormal spacing 2^-133.  Inputs are finite and
+// below bf16's largest finite value.
+void orc_round_bf16(const double *v, int64_t n, double *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const double a = std::fabs(v[i]);
+    if (a == 0.0) { out[i] = v[i]; continue; }
+    int e2;
+    std::frexp(a, &e2);                    // a in [2^(e2-1), 2^e2)
+    const int e = std::max(e2 - 1, -126);  // exponent of the binade
+    const double ulp = std::ldexp(1.0, e - 7);
+    const double q = a / ulp;              // exact: power-of-two division
+    double lo = std::floor(q);
+    const double frac = q - lo;
+    if (frac > 0.5 || (frac == 0.5 && std::fmod(lo, 2.0) == 1.0)) lo += 1.0;
+    const double r = lo * ulp;
+    out[i] = std::signbit(v[i]) ? -r : r;
+  }
 }
 
 // ---------------------------------------------------------------------------

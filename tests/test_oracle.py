@@ -412,3 +412,36 @@ def test_mlp_step_forward_matches_bf16_ffn_without_quantization():
     a, y = orc.expert_ffn_rows(x, ex, s, wg, wu, wd)
     np.testing.assert_allclose(res["a"], a, rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(res["y"], y, rtol=1e-12, atol=1e-14)
+
+
+def test_round_bf16_hand_values_and_ties():
+    u = 2.0 ** -7                                    # bf16 spacing in [1, 2)
+    cases = [
+        (1.0 + u / 2, 1.0),                          # tie -> even significand
+        (1.0 + 3 * u / 2, 1.0 + 2 * u),              # tie -> even (up)
+        (1.0 + u / 2 + 2.0 ** -30, 1.0 + u),         # just above the tie
+        (-(1.0 + 3 * u / 2), -(1.0 + 2 * u)),        # sign symmetric
+        (2.0 - 3 * u / 4, 2.0 - u),                  # stays in the binade
+        (2.0 - u / 4, 2.0),                          # rounds up into the next
+        (2.0 - u / 2, 2.0),                          # tie at the top -> 2 (even)
+        (3.0 * 2.0 ** -134, 2.0 ** -132),            # subnormal tie -> even
+        (2.0 ** -134, 0.0),                          # subnormal tie -> zero
+        (2.0 ** -133, 2.0 ** -133),                  # smallest subnormal kept
+        (0.0, 0.0),
+    ]
+    v = np.array([c[0] for c in cases])
+    np.testing.assert_array_equal(orc.round_bf16(v), [c[1] for c in cases])
+    assert np.signbit(orc.round_bf16(np.array([-0.0]))[0])
+
+
+def test_round_bf16_matches_torch_on_fp32_values():
+    # Every fp32 value is exact in fp64, and torch rounds fp32 -> bf16 to
+    # nearest even: both must give the same bf16 value.
+    rng = np.random.default_rng(11)
+    bits = rng.integers(0, 2 ** 31, size=200000, dtype=np.uint64).astype(np.uint32)
+    f = bits.view(np.float32)
+    f = f[np.isfinite(f) & (np.abs(f) < 3.0e38)]
+    ties = (np.arange(1, 4000, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    f = np.concatenate([f, ties, -ties])
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.round_bf16(f.astype(np.float64)), want)
