@@ -96,7 +96,7 @@ int moe_version(void);
  * The top-k decision is taken on the fp32 logits.  The weights are
  * exp(l_j - l_max) / sum over the kept experts of exp(l - l_max).
  * Limits: 1 <= k <= min(E, 32), 1 <= E <= 1024, T >= 0 (T == 0 enqueues
- * nothing), H >= 1; in GEMM mode with bf16, H % 8 == 0.
+ * nothing), H >= 1; in GEMM mode with bf16, H % 64 == 0.
  */
 int moe_route_topk(const void *x, const void *w_router, const float *bias,
                    float *logits, int64_t T, int64_t H, int64_t E, int64_t k,
@@ -189,6 +189,165 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
 int moe_unpermute_combine(const void *y, const int32_t *inv,
                           const float *topk_w, int64_t T, int64_t k,
                           int64_t H, int dtype, void *out, hipStream_t stream);
+
+/*
+ * ---- MXFP8 (BioNeMo MoE article, "MXFP8 Precision Reduces Memory Footprint
+ * for Biological Models": 8-bit values with one scale per block of 32
+ * consecutive values; "GroupedLinear Optimizes Expert Computation in MoE
+ * Models": the GroupedLinear -> ScaledSwiGLU -> GroupedLinear chain as one
+ * fused forward and one fused backward).
+ * Element format FP8 E4M3 (OCP "FN": bias 7, max 448, 0x7F/0xFF NaN), scale
+ * E8M0 (2^(byte - 127)).  Conversion rule (the pages give none; OCP MX v1.0):
+ * X = floor(log2(max|v|)) - 8 per block, scale byte X + 127 (clamped to
+ * [0, 254]), code = v * 2^-X rounded to nearest E4M3, ties to even,
+ * saturating at +-448, sign kept for values rounding to zero; an all-zero
+ * block has scale byte 0.
+ */
+
+/*
+ * moe_mxfp8_quantize - MX-quantise a bf16 matrix in[rows, cols] (row pitch
+ * ld_in elements, ld_in % 8 == 0 for axis 0), cols % 32 == 0.
+ * axis 0: blocks of 32 along each row.  codes [rows, ld_codes] bytes
+ *   (ld_codes % 16 == 0), scales [rows, ld_scales] (>= cols/32).
+ * axis 1: blocks of 32 down each column, output transposed for a GEMM whose
+ *   reduction runs over rows: codes [cols, ld_codes], scales [cols,
+ *   ld_scales].  Rows may be split into segments seg_offsets[0..n_seg]
+ *   (device, non-decreasing; NULL = one segment [0, rows)); each segment is
+ *   zero-padded to a multiple of `align` (32 or 512) and starts at column
+ *   pad_offsets[s] of the output (written to pad_offsets [n_seg + 1], device,
+ *   when seg_offsets is given).  ld_codes must hold the padded total
+ *   (>= rows + (align - 1) * n_seg), ld_scales >= ld_codes / 32.
+ * Codes and scales of a given input match the rule above bit for bit.
+ */
+int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
+                       int64_t ld_in, int axis, const int32_t *seg_offsets,
+                       int64_t n_seg, int64_t align, uint8_t *codes,
+                       int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                       int32_t *pad_offsets, hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_mxfp8_fwd - MXFP8 grouped MLP forward on permuted rows:
+ *   g, u = MX(x) . MX(W_gate)^T, MX(x) . MX(W_up)^T     (blocks along H)
+ *   a    = s * SiLU(g) * u                               (bf16, written)
+ *   y    = MX(a) . MX(W_down)^T                          (blocks along I)
+ * Inputs: xq/xs = x_perm quantised along H (axis 0: [R_cap, H] codes,
+ * [R_cap, H/32] scales); W_gate/W_up codes [n_local*I, H] + scales
+ * [n_local*I, H/32] and W_down codes [n_local*H, I] + scales [n_local*H,
+ * I/32] (axis 0 of the stacked weights); offsets, s_perm as in
+ * moe_grouped_gate_up (s_perm may be NULL).
+ * Outputs (bf16): a [R_cap, I]; gu [R_cap, 2I] = [g | u] per row (may be
+ * NULL; the backward needs it); y [R_cap, H].  Rows < R are written.
+ * workspace: moe_grouped_mlp_mxfp8_fwd_workspace_bytes() bytes.
+ * Limits: H % 512 == 0, I % 512 == 0, 1 <= n_local <= 4096.
+ */
+size_t moe_grouped_mlp_mxfp8_fwd_workspace_bytes(int64_t R_cap,
+                                                 int64_t n_local, int64_t H,
+                                                 int64_t I);
+int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
+                              const int32_t *offsets, const float *s_perm,
+                              int64_t n_local, int64_t R_cap, int64_t H,
+                              int64_t I, const uint8_t *wg, const uint8_t *wgs,
+                              const uint8_t *wu, const uint8_t *wus,
+                              const uint8_t *wd, const uint8_t *wds, void *a,
+                              void *gu, void *y, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_linear_mxfp8 - one MXFP8 GroupedLinear on permuted rows (the
+ * GroupedLinear of "GroupedLinear Optimizes Expert Computation in MoE
+ * Models", operands as in the MXFP8 section of the BioNeMo MoE article):
+ *   y[r, :] = MX(x[r, :]) . MX(W_e)^T   for rows r of expert e's segment
+ * x [R_cap, K] bf16 is quantised along K inside the call (rows past
+ * offsets[n_local] are not read); W codes [n_local*N, K] + scales
+ * [n_local*N, K/32] (axis 0 of the stacked [n_local, N, K] weights);
+ * y [R_cap, N] bf16, rows < R written.  The forward's down projection is
+ * this call with x = a, K = I, N = H.
+ * workspace: moe_grouped_linear_mxfp8_workspace_bytes() bytes.
+ * Limits: K % 512 == 0, N >= 1, 1 <= n_local <= 4096.
+ */
+size_t moe_grouped_linear_mxfp8_workspace_bytes(int64_t R_cap,
+                                                int64_t n_local, int64_t K);
+int moe_grouped_linear_mxfp8(const void *x, const int32_t *offsets,
+                             int64_t n_local, int64_t R_cap, int64_t K,
+                             int64_t N, const uint8_t *w,
+                             const uint8_t *w_scales, void *y, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_mxfp8_bwd - backward of the forward above by the chain
+ * rule, every GEMM operand MX-quantised along that GEMM's reduction axis:
+ *   da = MX(dY) . MX_H(W_down)                 (K = H)
+ *   dg = da*s*u*SiLU'(g), du = da*s*SiLU(g), ds = sum_i da*SiLU(g)*u
+ *   dX = MX(dg) . MX_I(W_gate) + MX(du) . MX_I(W_up)   (K = I)
+ *   dW_down[e] = MX_R(dY_e)^T . MX_R(a_e), dW_gate[e] = MX_R(dg_e)^T .
+ *   MX_R(x_e), dW_up[e] = MX_R(du_e)^T . MX_R(x_e)   (K = rows of expert e)
+ * Inputs (bf16): dy [R_cap, H], x_perm [R_cap, H], a [R_cap, I], gu [R_cap,
+ * 2I] from the forward; offsets, s_perm; the weights quantised along the
+ * other axis (axis 1 of the stacked weights): wdt/wdts = W_down as [n_local*H,
+ * I] -> codes [I, n_local*H], scales [I, n_local*H/32]; wgt/wgts, wut/wuts =
+ * W_gate, W_up as [n_local*I, H] -> codes [H, n_local*I], scales [H,
+ * n_local*I/32].
+ * Outputs: dx [R_cap, H] bf16, ds [R_cap] fp32 (sum in a fixed order),
+ * dw_gate, dw_up [n_local, I, H] bf16, dw_down [n_local, H, I] bf16 (an
+ * expert without rows gets zero gradients).
+ * The call runs moe_grouped_mlp_mxfp8_bwd_down, then
+ * moe_grouped_mlp_mxfp8_bwd_gate_up, with [dg | du] kept in the workspace.
+ * workspace: moe_grouped_mlp_mxfp8_bwd_workspace_bytes() bytes.
+ * Limits as for the forward.
+ */
+size_t moe_grouped_mlp_mxfp8_bwd_workspace_bytes(int64_t R_cap,
+                                                 int64_t n_local, int64_t H,
+                                                 int64_t I);
+int moe_grouped_mlp_mxfp8_bwd(
+    const void *dy, const void *x_perm, const void *a, const void *gu,
+    const int32_t *offsets, const float *s_perm, int64_t n_local,
+    int64_t R_cap, int64_t H, int64_t I, const uint8_t *wdt,
+    const uint8_t *wdts, const uint8_t *wgt, const uint8_t *wgts,
+    const uint8_t *wut, const uint8_t *wuts, void *dx, float *ds,
+    void *dw_gate, void *dw_up, void *dw_down, void *workspace,
+    size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_mxfp8_bwd_down - first half of the backward: the down
+ * projection's data and weight gradients and the ScaledSwiGLU backward.
+ *   da = MX(dY) . MX_H(W_down);  dg, du, ds as above;
+ *   dW_down[e] = MX_R(dY_e)^T . MX_R(a_e)
+ * Inputs: dy [R_cap, H], a [R_cap, I], gu [R_cap, 2I] (bf16), offsets,
+ * s_perm (may be NULL: s = 1), wdt/wdts as for moe_grouped_mlp_mxfp8_bwd.
+ * Outputs: dgu [R_cap, 2I] bf16 = [dg | du] per row, ds [R_cap] fp32,
+ * dw_down [n_local, H, I] bf16.
+ * workspace: moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes() bytes.
+ */
+size_t moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(int64_t R_cap,
+                                                      int64_t n_local,
+                                                      int64_t H, int64_t I);
+int moe_grouped_mlp_mxfp8_bwd_down(
+    const void *dy, const void *a, const void *gu, const int32_t *offsets,
+    const float *s_perm, int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
+    const uint8_t *wdt, const uint8_t *wdts, void *dgu, float *ds,
+    void *dw_down, void *workspace, size_t workspace_bytes,
+    hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_mxfp8_bwd_gate_up - second half of the backward: the
+ * gate/up projection's data and weight gradients from [dg | du].
+ *   dX = MX(dg) . MX_I(W_gate) + MX(du) . MX_I(W_up);
+ *   dW_gate[e] = MX_R(dg_e)^T . MX_R(x_e), dW_up[e] = MX_R(du_e)^T . MX_R(x_e)
+ * Inputs: dgu [R_cap, 2I] bf16, x_perm [R_cap, H] bf16, offsets, wgt/wgts,
+ * wut/wuts as for moe_grouped_mlp_mxfp8_bwd.  Outputs: dx [R_cap, H],
+ * dw_gate, dw_up [n_local, I, H] (bf16).
+ * workspace: moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes() bytes.
+ */
+size_t moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes(int64_t R_cap,
+                                                         int64_t n_local,
+                                                         int64_t H,
+                                                         int64_t I);
+int moe_grouped_mlp_mxfp8_bwd_gate_up(
+    const void *dgu, const void *x_perm, const int32_t *offsets,
+    int64_t n_local, int64_t R_cap, int64_t H, int64_t I, const uint8_t *wgt,
+    const uint8_t *wgts, const uint8_t *wut, const uint8_t *wuts, void *dx,
+    void *dw_gate, void *dw_up, void *workspace, size_t workspace_bytes,
+    hipStream_t stream);
 
 /* Waits for `stream` and reports a pending HIP error as MOE_E_HIP (tests). */
 int moe_debug_sync(hipStream_t stream);

@@ -66,6 +66,34 @@ def lib():
         L.moe_unpermute_combine.argtypes = [vp, vp, vp, i64, i64, i64, i32,
                                             vp, vp]
         L.moe_debug_sync.argtypes = [vp]
+        L.moe_mxfp8_quantize.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64,
+                                         vp, i64, vp, i64, vp, vp]
+        L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes.restype = sz
+        L.moe_grouped_mlp_mxfp8_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64,
+                                                i64, vp, vp, vp, vp, vp, vp,
+                                                vp, vp, vp, vp, sz, vp]
+        L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes.restype = sz
+        L.moe_grouped_mlp_mxfp8_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64,
+                                                i64, i64, i64, vp, vp, vp, vp,
+                                                vp, vp, vp, vp, vp, vp, vp, vp,
+                                                sz, vp]
+        L.moe_grouped_linear_mxfp8_workspace_bytes.argtypes = [i64, i64, i64]
+        L.moe_grouped_linear_mxfp8_workspace_bytes.restype = sz
+        L.moe_grouped_linear_mxfp8.argtypes = [vp, vp, i64, i64, i64, i64, vp,
+                                               vp, vp, vp, sz, vp]
+        L.moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes.restype = sz
+        L.moe_grouped_mlp_mxfp8_bwd_down.argtypes = [vp, vp, vp, vp, vp, i64,
+                                                     i64, i64, i64, vp, vp, vp,
+                                                     vp, vp, vp, sz, vp]
+        L.moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes.restype = sz
+        L.moe_grouped_mlp_mxfp8_bwd_gate_up.argtypes = [vp, vp, vp, i64, i64,
+                                                        i64, i64, vp, vp, vp,
+                                                        vp, vp, vp, vp, vp, sz,
+                                                        vp]
         for name in declared_functions():
             getattr(L, name).restype = getattr(L, name).restype or i32
         _lib = L
@@ -232,3 +260,166 @@ def unpermute_combine(y, inv, topk_w=None, out=None, stream=None):
 
 def debug_sync(stream=None):
     _call("moe_debug_sync", _stream(stream))
+
+
+# ---------------------------------------------------------------- MXFP8
+
+
+def mxfp8_quantize(x, axis=0, seg_offsets=None, align=32, stream=None):
+    """MX-quantise a bf16 matrix [rows, cols].
+
+    axis 0 -> (codes [rows, cols] u8, scales [rows, cols/32] u8).
+    axis 1 -> (codesT [cols, P] u8, scalesT [cols, P/32] u8, pad_offsets or
+    None) with rows padded per segment to a multiple of `align`.  Without
+    segments P is rows rounded up to `align` (the transposed stacked weights
+    the backward reads have exactly that pitch); with segments P is a
+    capacity rounded up to 512 and the used width is pad_offsets[-1].
+    """
+    rows, cols = x.shape
+    dev = x.device
+    ld_in = x.stride(0)
+    if axis == 0:
+        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        _call("moe_mxfp8_quantize", _p(x), rows, cols, ld_in, 0, None, 0, 32,
+              _p(codes), cols, _p(scales), cols // 32, None, _stream(stream))
+        return codes, scales
+    nseg = 0 if seg_offsets is None else seg_offsets.numel() - 1
+    if seg_offsets is None:
+        cap = (rows + align - 1) // align * align    # exact padded width
+    else:
+        cap = (rows + (align - 1) * nseg + 511) // 512 * 512
+    codes = torch.zeros((cols, cap), dtype=torch.uint8, device=dev)
+    scales = torch.zeros((cols, cap // 32), dtype=torch.uint8, device=dev)
+    pad = (torch.empty(nseg + 1, dtype=torch.int32, device=dev)
+           if seg_offsets is not None else None)
+    _call("moe_mxfp8_quantize", _p(x), rows, cols, ld_in, 1, _p(seg_offsets),
+          nseg, align, _p(codes), cap, _p(scales), cap // 32, _p(pad),
+          _stream(stream))
+    return codes, scales, pad
+
+
+class MxWeights:
+    """Stacked expert weights quantised for the MXFP8 grouped MLP:
+    row-wise copies for the forward, transposed column-wise copies for the
+    data gradients of the backward."""
+
+    def __init__(self, w_gate, w_up, w_down, stream=None):
+        n, I, H = w_gate.shape
+        self.n_local, self.I, self.H = n, I, H
+        g2, u2 = w_gate.reshape(n * I, H), w_up.reshape(n * I, H)
+        d2 = w_down.reshape(n * H, I)
+        self.wg, self.wgs = mxfp8_quantize(g2, 0, stream=stream)
+        self.wu, self.wus = mxfp8_quantize(u2, 0, stream=stream)
+        self.wd, self.wds = mxfp8_quantize(d2, 0, stream=stream)
+        self.wgt, self.wgts, _ = mxfp8_quantize(g2, 1, stream=stream)
+        self.wut, self.wuts, _ = mxfp8_quantize(u2, 1, stream=stream)
+        self.wdt, self.wdts, _ = mxfp8_quantize(d2, 1, stream=stream)
+
+
+def mxfp8_mlp_fwd(xq, xs, offsets, s_perm, mw, a=None, gu=None, y=None,
+                  workspace=None, stream=None):
+    R_cap = xq.shape[0]
+    H, I, n = mw.H, mw.I, mw.n_local
+    dev = xq.device
+    if a is None:
+        a = torch.empty((R_cap, I), dtype=torch.bfloat16, device=dev)
+    if gu is None:
+        gu = torch.empty((R_cap, 2 * I), dtype=torch.bfloat16, device=dev)
+    if y is None:
+        y = torch.empty((R_cap, H), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        nb = lib().moe_grouped_mlp_mxfp8_fwd_workspace_bytes(R_cap, n, H, I)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    _call("moe_grouped_mlp_mxfp8_fwd", _p(xq), _p(xs), _p(offsets),
+          _p(s_perm), n, R_cap, H, I, _p(mw.wg), _p(mw.wgs), _p(mw.wu),
+          _p(mw.wus), _p(mw.wd), _p(mw.wds), _p(a), _p(gu), _p(y),
+          _p(workspace), workspace.numel(), _stream(stream))
+    return a, gu, y
+
+
+def mxfp8_mlp_bwd(dy, x_perm, a, gu, offsets, s_perm, mw, dx=None, ds=None,
+                  dw_gate=None, dw_up=None, dw_down=None, workspace=None,
+                  stream=None):
+    R_cap, H = dy.shape
+    I, n = mw.I, mw.n_local
+    dev = dy.device
+    bf = torch.bfloat16
+    if dx is None:
+        dx = torch.empty((R_cap, H), dtype=bf, device=dev)
+    if ds is None:
+        ds = torch.empty(R_cap, dtype=torch.float32, device=dev)
+    if dw_gate is None:
+        dw_gate = torch.empty((n, I, H), dtype=bf, device=dev)
+    if dw_up is None:
+        dw_up = torch.empty((n, I, H), dtype=bf, device=dev)
+    if dw_down is None:
+        dw_down = torch.empty((n, H, I), dtype=bf, device=dev)
+    if workspace is None:
+        nb = lib().moe_grouped_mlp_mxfp8_bwd_workspace_bytes(R_cap, n, H, I)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    _call("moe_grouped_mlp_mxfp8_bwd", _p(dy), _p(x_perm), _p(a), _p(gu),
+          _p(offsets), _p(s_perm), n, R_cap, H, I, _p(mw.wdt), _p(mw.wdts),
+          _p(mw.wgt), _p(mw.wgts), _p(mw.wut), _p(mw.wuts), _p(dx), _p(ds),
+          _p(dw_gate), _p(dw_up), _p(dw_down), _p(workspace),
+          workspace.numel(), _stream(stream))
+    return dict(dx=dx, ds=ds, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
+
+
+def grouped_linear_mxfp8(x, offsets, n_local, w, w_scales, y=None,
+                         workspace=None, stream=None):
+    """y = MX(x) MX(W_e)^T per expert segment; w codes [n_local*N, K]."""
+    R_cap, K = x.shape
+    N = w.shape[0] // n_local
+    dev = x.device
+    if y is None:
+        y = torch.empty((R_cap, N), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        nb = lib().moe_grouped_linear_mxfp8_workspace_bytes(R_cap, n_local, K)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    _call("moe_grouped_linear_mxfp8", _p(x), _p(offsets), n_local, R_cap, K,
+          N, _p(w), _p(w_scales), _p(y), _p(workspace), workspace.numel(),
+          _stream(stream))
+    return y
+
+
+def mxfp8_mlp_bwd_down(dy, a, gu, offsets, s_perm, mw, dgu=None, ds=None,
+                       dw_down=None, workspace=None, stream=None):
+    R_cap, H = dy.shape
+    I, n = mw.I, mw.n_local
+    dev = dy.device
+    if dgu is None:
+        dgu = torch.empty((R_cap, 2 * I), dtype=torch.bfloat16, device=dev)
+    if ds is None:
+        ds = torch.empty(R_cap, dtype=torch.float32, device=dev)
+    if dw_down is None:
+        dw_down = torch.empty((n, H, I), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        nb = lib().moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(R_cap, n, H, I)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    _call("moe_grouped_mlp_mxfp8_bwd_down", _p(dy), _p(a), _p(gu), _p(offsets),
+          _p(s_perm), n, R_cap, H, I, _p(mw.wdt), _p(mw.wdts), _p(dgu), _p(ds),
+          _p(dw_down), _p(workspace), workspace.numel(), _stream(stream))
+    return dict(dgu=dgu, ds=ds, dw_down=dw_down)
+
+
+def mxfp8_mlp_bwd_gate_up(dgu, x_perm, offsets, mw, dx=None, dw_gate=None,
+                          dw_up=None, workspace=None, stream=None):
+    R_cap, H = x_perm.shape
+    I, n = mw.I, mw.n_local
+    dev = x_perm.device
+    bf = torch.bfloat16
+    if dx is None:
+        dx = torch.empty((R_cap, H), dtype=bf, device=dev)
+    if dw_gate is None:
+        dw_gate = torch.empty((n, I, H), dtype=bf, device=dev)
+    if dw_up is None:
+        dw_up = torch.empty((n, I, H), dtype=bf, device=dev)
+    if workspace is None:
+        nb = lib().moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes(R_cap, n, H, I)
+        workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    _call("moe_grouped_mlp_mxfp8_bwd_gate_up", _p(dgu), _p(x_perm),
+          _p(offsets), n, R_cap, H, I, _p(mw.wgt), _p(mw.wgts), _p(mw.wut),
+          _p(mw.wuts), _p(dx), _p(dw_gate), _p(dw_up), _p(workspace),
+          workspace.numel(), _stream(stream))
+    return dict(dx=dx, dw_gate=dw_gate, dw_up=dw_up)

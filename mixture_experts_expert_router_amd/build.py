@@ -9,7 +9,7 @@ CSRC = os.path.join(HERE, "csrc")
 SO = os.path.join(HERE, "libmoe_mi355x.so")
 
 SOURCES = ["api.hip", "route.hip", "permute.hip", "grouped_gemm.hip",
-           "ffn_f32.hip", "combine.hip"]
+           "ffn_f32.hip", "combine.hip", "mx_quant.hip", "mx_gemm.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

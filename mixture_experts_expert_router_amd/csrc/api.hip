@@ -1,7 +1,9 @@
 // C-ABI entry points: argument validation, workspace sizing and dispatch to
 // the gfx950 kernels.  Declarations, contracts and the passages of the pages
 // each operation follows are in include/moe_mi355x.h.
+#include <algorithm>
 #include <atomic>
+#include <initializer_list>
 
 #include "../../include/moe_mi355x.h"
 #include "kernels.hpp"
@@ -252,6 +254,451 @@ int moe_unpermute_combine(const void *y, const int32_t *inv,
 int moe_debug_sync(hipStream_t stream) {
   if (hipStreamSynchronize(stream) != hipSuccess) return MOE_E_HIP;
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- MXFP8
+namespace {
+
+// Bump allocator over a caller workspace (256-byte aligned pieces).
+struct Carve {
+  char *base;
+  size_t used = 0;
+  explicit Carve(void *b) : base((char *)b) {}
+  template <typename T>
+  T *take(size_t count) {
+    T *p = base ? (T *)(base + used) : nullptr;
+    used += (count * sizeof(T) + 255) / 256 * 256;
+    return p;
+  }
+};
+
+bool mx_shape_ok(int64_t n_local, int64_t R_cap, int64_t H, int64_t I) {
+  return n_local >= 1 && n_local <= 4096 && R_cap >= 0 && R_cap < kMaxRows &&
+         H >= 512 && I >= 512 && H % 512 == 0 && I % 512 == 0 &&
+         (int64_t)n_local * I < kMaxRows && (int64_t)n_local * H < kMaxRows;
+}
+
+// Row capacity of transposed (column-quantised) expert segments padded
+// to 512 rows each.
+int64_t mx_kpad_cap(int64_t R_cap, int64_t n_local) {
+  return (R_cap + 511 * n_local + 511) / 512 * 512;
+}
+
+// Workspace layouts.  Sizes depend only on the arguments, so the same
+// carving gives the byte count (base == null) and the pointers.
+struct LinWs {                     // grouped linear: tile plan + MX(x)
+  int32_t *tiles;
+  uint8_t *xq, *xs;
+};
+LinWs carve_lin(Carve &c, int64_t R_cap, int64_t n_local, int64_t K) {
+  LinWs w;
+  w.tiles = c.take<int32_t>(n_local + 1);
+  w.xq = c.take<uint8_t>((size_t)R_cap * K);
+  w.xs = c.take<uint8_t>((size_t)R_cap * (K / 32));
+  return w;
+}
+
+struct DownBwdWs {                 // backward of the down projection
+  int32_t *tiles, *kpad;
+  uint8_t *dyq, *dys;
+  float *ds_part;
+  uint8_t *dyT, *dyTs, *aT, *aTs;
+  int64_t kcap;
+};
+DownBwdWs carve_down_bwd(Carve &c, int64_t R_cap, int64_t n_local, int64_t H,
+                         int64_t I) {
+  DownBwdWs w;
+  w.kcap = mx_kpad_cap(R_cap, n_local);
+  w.tiles = c.take<int32_t>(n_local + 1);
+  w.kpad = c.take<int32_t>(n_local + 1);
+  w.dyq = c.take<uint8_t>((size_t)R_cap * H);
+  w.dys = c.take<uint8_t>((size_t)R_cap * (H / 32));
+  w.ds_part = c.take<float>((size_t)R_cap * (I / 128) * 2);
+  w.dyT = c.take<uint8_t>((size_t)H * w.kcap);
+  w.dyTs = c.take<uint8_t>((size_t)H * (w.kcap / 32));
+  w.aT = c.take<uint8_t>((size_t)I * w.kcap);
+  w.aTs = c.take<uint8_t>((size_t)I * (w.kcap / 32));
+  return w;
+}
+
+struct GateUpBwdWs {               // backward of the gate/up projection
+  int32_t *tiles, *kpad;
+  uint8_t *dguq, *dgus;
+  uint8_t *xT, *xTs, *dgT, *dgTs, *duT, *duTs;
+  int64_t kcap;
+};
+GateUpBwdWs carve_gate_up_bwd(Carve &c, int64_t R_cap, int64_t n_local,
+                              int64_t H, int64_t I) {
+  GateUpBwdWs w;
+  w.kcap = mx_kpad_cap(R_cap, n_local);
+  w.tiles = c.take<int32_t>(n_local + 1);
+  w.kpad = c.take<int32_t>(n_local + 1);
+  w.dguq = c.take<uint8_t>((size_t)R_cap * 2 * I);
+  w.dgus = c.take<uint8_t>((size_t)R_cap * (2 * I / 32));
+  w.xT = c.take<uint8_t>((size_t)H * w.kcap);
+  w.xTs = c.take<uint8_t>((size_t)H * (w.kcap / 32));
+  w.dgT = c.take<uint8_t>((size_t)I * w.kcap);
+  w.dgTs = c.take<uint8_t>((size_t)I * (w.kcap / 32));
+  w.duT = c.take<uint8_t>((size_t)I * w.kcap);
+  w.duTs = c.take<uint8_t>((size_t)I * (w.kcap / 32));
+  return w;
+}
+
+size_t fwd_bytes(int64_t R_cap, int64_t n_local, int64_t I) {
+  Carve c(nullptr);
+  carve_lin(c, R_cap, n_local, I);
+  return c.used;
+}
+size_t lin_bytes(int64_t R_cap, int64_t n_local, int64_t K) {
+  Carve c(nullptr);
+  carve_lin(c, R_cap, n_local, K);
+  return c.used;
+}
+size_t down_bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H, int64_t I) {
+  Carve c(nullptr);
+  carve_down_bwd(c, R_cap, n_local, H, I);
+  return c.used;
+}
+size_t gate_up_bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H,
+                         int64_t I) {
+  Carve c(nullptr);
+  carve_gate_up_bwd(c, R_cap, n_local, H, I);
+  return c.used;
+}
+// Fused backward: dgu, then one region that both halves use in turn.
+size_t bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H, int64_t I) {
+  Carve c(nullptr);
+  c.take<uint16_t>((size_t)R_cap * 2 * I);
+  return c.used + std::max(down_bwd_bytes(R_cap, n_local, H, I),
+                           gate_up_bwd_bytes(R_cap, n_local, H, I));
+}
+
+// y = MX(x) . MX(W_e)^T per row segment; the quantisation of x stops at the
+// device row count offsets[G].
+hipError_t run_linear(const void *x, const int32_t *offsets, int64_t n_local,
+                      int64_t R_cap, int64_t K, int64_t N, const uint8_t *w,
+                      const uint8_t *wsc, void *y, const LinWs &ws, int cus,
+                      hipStream_t stream) {
+  hipError_t err = moe::launch_mx_quant_rows(
+      (const uint16_t *)x, R_cap, K, K, ws.xq, K, ws.xs, K / 32,
+      offsets + n_local, stream);
+  if (err != hipSuccess) return err;
+  moe::MxGemmDesc e{};
+  e.A = ws.xq; e.As = ws.xs; e.lda = K; e.ldas = K / 32;
+  e.B0 = w; e.B0s = wsc; e.ldb = K; e.ldbs = K / 32;
+  e.b_stride = N * K; e.bs_stride = N * K / 32;
+  e.offsets = offsets; e.tile_ws = ws.tiles; e.G = (int)n_local;
+  e.N = (int)N; e.K = (int)K; e.R_cap = R_cap;
+  e.C = y; e.ldc = N;
+  return moe::launch_mx_rowseg(e, moe::MXE_BF16, cus, stream);
+}
+
+hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
+                        const int32_t *offsets, const float *s_perm,
+                        int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
+                        const uint8_t *wdt, const uint8_t *wdts, void *dgu,
+                        float *ds, void *dw_down, const DownBwdWs &w, int cus,
+                        hipStream_t stream) {
+  const int G = (int)n_local;
+  hipError_t err;
+#define MX_TRY(x) do { err = (x); if (err != hipSuccess) return err; } while (0)
+  // dY along H (row-wise)
+  MX_TRY(moe::launch_mx_quant_rows((const uint16_t *)dy, R_cap, H, H, w.dyq, H,
+                                   w.dys, H / 32, offsets + G, stream));
+  // da = dY W_d (K = H); SwiGLU backward in the epilogue -> dg, du, ds
+  {
+    moe::MxGemmDesc d{};
+    d.A = w.dyq; d.As = w.dys; d.lda = H; d.ldas = H / 32;
+    d.B0 = wdt; d.B0s = wdts; d.ldb = n_local * H; d.ldbs = n_local * H / 32;
+    d.b_stride = H; d.bs_stride = H / 32;
+    d.offsets = offsets; d.tile_ws = w.tiles; d.G = G;
+    d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
+    d.row_scale = s_perm; d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
+    d.dgu = (uint16_t *)dgu; d.ds_part = w.ds_part; d.ds = ds;
+    MX_TRY(moe::launch_mx_rowseg(d, moe::MXE_SWIGLU_BWD, cus, stream));
+  }
+  // dW_d[e] [H, I] = dY_e^T a_e: blocks of 32 rows inside each expert's
+  // segment, segments zero-padded to 512 rows
+  const int64_t kc = w.kcap;
+  MX_TRY(moe::launch_mx_quant_cols((const uint16_t *)dy, R_cap, H, H, offsets,
+                                   G, 512, w.kpad, w.dyT, kc, w.dyTs, kc / 32,
+                                   cus, stream));
+  MX_TRY(moe::launch_mx_quant_cols((const uint16_t *)a, R_cap, I, I, offsets,
+                                   G, 512, w.kpad, w.aT, kc, w.aTs, kc / 32,
+                                   cus, stream));
+  moe::MxGemmDesc d{};
+  d.kseg = w.kpad; d.G = G;
+  d.lda = kc; d.ldas = kc / 32; d.ldb = kc; d.ldbs = kc / 32;
+  d.A = w.dyT; d.As = w.dyTs; d.B0 = w.aT; d.B0s = w.aTs;
+  d.M = (int)H; d.N = (int)I; d.C = dw_down; d.ldc = I; d.c_stride = H * I;
+  return moe::launch_mx_kseg(d, cus, stream);
+}
+
+hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
+                           const int32_t *offsets, int64_t n_local,
+                           int64_t R_cap, int64_t H, int64_t I,
+                           const uint8_t *wgt, const uint8_t *wgts,
+                           const uint8_t *wut, const uint8_t *wuts, void *dx,
+                           void *dw_gate, void *dw_up, const GateUpBwdWs &w,
+                           int cus, hipStream_t stream) {
+  const int G = (int)n_local;
+  hipError_t err;
+  // [dg | du] along I (row-wise; blocks never straddle the two halves)
+  MX_TRY(moe::launch_mx_quant_rows((const uint16_t *)dgu, R_cap, 2 * I, 2 * I,
+                                   w.dguq, 2 * I, w.dgus, 2 * I / 32,
+                                   offsets + G, stream));
+  // dX = dg W_g + du W_u: one GEMM with K = 2I, B switching at K = I
+  {
+    moe::MxGemmDesc d{};
+    d.A = w.dguq; d.As = w.dgus; d.lda = 2 * I; d.ldas = 2 * I / 32;
+    d.B0 = wgt; d.B0s = wgts; d.B1 = wut; d.B1s = wuts;
+    d.ldb = n_local * I; d.ldbs = n_local * I / 32;
+    d.b_stride = I; d.bs_stride = I / 32;
+    d.offsets = offsets; d.tile_ws = w.tiles; d.G = G;
+    d.N = (int)H; d.K = (int)(2 * I); d.R_cap = R_cap; d.ksplit = (int)I;
+    d.C = dx; d.ldc = H;
+    MX_TRY(moe::launch_mx_rowseg(d, moe::MXE_BF16, cus, stream));
+  }
+  const int64_t kc = w.kcap;
+  const uint16_t *dg = (const uint16_t *)dgu;
+  MX_TRY(moe::launch_mx_quant_cols((const uint16_t *)x_perm, R_cap, H, H,
+                                   offsets, G, 512, w.kpad, w.xT, kc, w.xTs,
+                                   kc / 32, cus, stream));
+  MX_TRY(moe::launch_mx_quant_cols(dg, R_cap, I, 2 * I, offsets, G, 512,
+                                   w.kpad, w.dgT, kc, w.dgTs, kc / 32, cus,
+                                   stream));
+  MX_TRY(moe::launch_mx_quant_cols(dg + I, R_cap, I, 2 * I, offsets, G, 512,
+                                   w.kpad, w.duT, kc, w.duTs, kc / 32, cus,
+                                   stream));
+#undef MX_TRY
+  // dW_g[e] [I, H] = dg_e^T x_e ; dW_u likewise with du
+  moe::MxGemmDesc d{};
+  d.kseg = w.kpad; d.G = G;
+  d.lda = kc; d.ldas = kc / 32; d.ldb = kc; d.ldbs = kc / 32;
+  d.A = w.dgT; d.As = w.dgTs; d.B0 = w.xT; d.B0s = w.xTs;
+  d.M = (int)I; d.N = (int)H; d.C = dw_gate; d.ldc = H; d.c_stride = I * H;
+  err = moe::launch_mx_kseg(d, cus, stream);
+  if (err != hipSuccess) return err;
+  d.A = w.duT; d.As = w.duTs; d.C = dw_up;
+  return moe::launch_mx_kseg(d, cus, stream);
+}
+
+bool all_aligned(std::initializer_list<const void *> ps) {
+  for (const void *q : ps)
+    if (!aligned16(q)) return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
+                       int64_t ld_in, int axis, const int32_t *seg_offsets,
+                       int64_t n_seg, int64_t align, uint8_t *codes,
+                       int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                       int32_t *pad_offsets, hipStream_t stream) {
+  if (axis != 0 && axis != 1) return MOE_E_ARG;
+  if (rows < 0 || cols < 1 || cols % 32 != 0 || ld_in < cols) return MOE_E_SHAPE;
+  if (rows >= kMaxRows || cols >= kMaxRows) return MOE_E_SHAPE;
+  if (rows == 0) return MOE_OK;
+  if (!in || !codes || !scales) return MOE_E_ARG;
+  if (!aligned16(codes)) return MOE_E_ALIGN;
+  if (axis == 0) {
+    if (ld_in % 8 != 0 || ld_codes < cols || ld_codes % 16 != 0 ||
+        ld_scales < cols / 32)
+      return MOE_E_SHAPE;
+    if (!aligned16(in)) return MOE_E_ALIGN;
+    return status_of(moe::launch_mx_quant_rows(
+        (const uint16_t *)in, rows, cols, ld_in, codes, ld_codes, scales,
+        ld_scales, nullptr, stream));
+  }
+  if (align != 32 && align != 512) return MOE_E_SHAPE;
+  if (ld_codes % 16 != 0) return MOE_E_SHAPE;
+  if (seg_offsets) {
+    if (n_seg < 1 || n_seg > 1 << 20 || pad_offsets == nullptr) return MOE_E_ARG;
+    if (ld_codes < rows + (align - 1) * n_seg) return MOE_E_SHAPE;
+  } else {
+    if (ld_codes < (rows + align - 1) / align * align) return MOE_E_SHAPE;
+  }
+  if (ld_scales < ld_codes / 32) return MOE_E_SHAPE;
+  return status_of(moe::launch_mx_quant_cols(
+      (const uint16_t *)in, rows, cols, ld_in, seg_offsets, (int)n_seg,
+      (int)align, pad_offsets, codes, ld_codes, scales, ld_scales, num_cus(),
+      stream));
+}
+
+size_t moe_grouped_mlp_mxfp8_fwd_workspace_bytes(int64_t R_cap,
+                                                 int64_t n_local, int64_t H,
+                                                 int64_t I) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return 0;
+  return fwd_bytes(R_cap, n_local, I);
+}
+
+int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
+                              const int32_t *offsets, const float *s_perm,
+                              int64_t n_local, int64_t R_cap, int64_t H,
+                              int64_t I, const uint8_t *wg, const uint8_t *wgs,
+                              const uint8_t *wu, const uint8_t *wus,
+                              const uint8_t *wd, const uint8_t *wds, void *a,
+                              void *gu, void *y, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!xq || !xs || !offsets || !wg || !wgs || !wu || !wus || !wd || !wds ||
+      !a || !y)
+    return MOE_E_ARG;
+  if (!all_aligned({xq, xs, wg, wgs, wu, wus, wd, wds, a, y}) ||
+      (gu && !aligned16(gu)))
+    return MOE_E_ALIGN;
+  if (!workspace || workspace_bytes < fwd_bytes(R_cap, n_local, I))
+    return MOE_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  Carve c(workspace);
+  const LinWs w = carve_lin(c, R_cap, n_local, I);
+  const int cus = num_cus();
+  moe::MxGemmDesc d{};
+  // gate/up: x (along H) x W_g, W_u (along H); SwiGLU x scale epilogue
+  d.A = xq; d.As = xs; d.lda = H; d.ldas = H / 32;
+  d.B0 = wg; d.B0s = wgs; d.B1 = wu; d.B1s = wus;
+  d.ldb = H; d.ldbs = H / 32; d.b_stride = I * H; d.bs_stride = I * H / 32;
+  d.offsets = offsets; d.tile_ws = w.tiles; d.G = (int)n_local;
+  d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
+  d.C = a; d.ldc = I; d.row_scale = s_perm;
+  d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
+  hipError_t err = moe::launch_mx_rowseg(d, moe::MXE_SWIGLU, cus, stream);
+  if (err != hipSuccess) return MOE_E_HIP;
+  // down: a (quantised along I) x W_d (along I)
+  return status_of(run_linear(a, offsets, n_local, R_cap, I, H, wd, wds, y, w,
+                              cus, stream));
+}
+
+size_t moe_grouped_linear_mxfp8_workspace_bytes(int64_t R_cap,
+                                                int64_t n_local, int64_t K) {
+  if (!mx_shape_ok(n_local, R_cap, K, 512)) return 0;
+  return lin_bytes(R_cap, n_local, K);
+}
+
+int moe_grouped_linear_mxfp8(const void *x, const int32_t *offsets,
+                             int64_t n_local, int64_t R_cap, int64_t K,
+                             int64_t N, const uint8_t *w,
+                             const uint8_t *w_scales, void *y, void *workspace,
+                             size_t workspace_bytes, hipStream_t stream) {
+  if (!mx_shape_ok(n_local, R_cap, K, 512)) return MOE_E_SHAPE;
+  if (N < 1 || (int64_t)n_local * N >= kMaxRows) return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!x || !offsets || !w || !w_scales || !y) return MOE_E_ARG;
+  if (!all_aligned({x, w, w_scales, y})) return MOE_E_ALIGN;
+  if (!workspace || workspace_bytes < lin_bytes(R_cap, n_local, K))
+    return MOE_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  Carve c(workspace);
+  const LinWs ws = carve_lin(c, R_cap, n_local, K);
+  return status_of(run_linear(x, offsets, n_local, R_cap, K, N, w, w_scales,
+                              y, ws, num_cus(), stream));
+}
+
+size_t moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(int64_t R_cap,
+                                                      int64_t n_local,
+                                                      int64_t H, int64_t I) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return 0;
+  return down_bwd_bytes(R_cap, n_local, H, I);
+}
+
+int moe_grouped_mlp_mxfp8_bwd_down(
+    const void *dy, const void *a, const void *gu, const int32_t *offsets,
+    const float *s_perm, int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
+    const uint8_t *wdt, const uint8_t *wdts, void *dgu, float *ds,
+    void *dw_down, void *workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!dy || !a || !gu || !offsets || !wdt || !wdts || !dgu || !ds || !dw_down)
+    return MOE_E_ARG;
+  if (!all_aligned({dy, a, gu, wdt, wdts, dgu, ds, dw_down}))
+    return MOE_E_ALIGN;
+  if (!workspace || workspace_bytes < down_bwd_bytes(R_cap, n_local, H, I))
+    return MOE_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  Carve c(workspace);
+  const DownBwdWs w = carve_down_bwd(c, R_cap, n_local, H, I);
+  return status_of(run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap, H,
+                                I, wdt, wdts, dgu, ds, dw_down, w, num_cus(),
+                                stream));
+}
+
+size_t moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes(int64_t R_cap,
+                                                         int64_t n_local,
+                                                         int64_t H,
+                                                         int64_t I) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return 0;
+  return gate_up_bwd_bytes(R_cap, n_local, H, I);
+}
+
+int moe_grouped_mlp_mxfp8_bwd_gate_up(
+    const void *dgu, const void *x_perm, const int32_t *offsets,
+    int64_t n_local, int64_t R_cap, int64_t H, int64_t I, const uint8_t *wgt,
+    const uint8_t *wgts, const uint8_t *wut, const uint8_t *wuts, void *dx,
+    void *dw_gate, void *dw_up, void *workspace, size_t workspace_bytes,
+    hipStream_t stream) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!dgu || !x_perm || !offsets || !wgt || !wgts || !wut || !wuts || !dx ||
+      !dw_gate || !dw_up)
+    return MOE_E_ARG;
+  if (!all_aligned({dgu, x_perm, wgt, wgts, wut, wuts, dx, dw_gate, dw_up}))
+    return MOE_E_ALIGN;
+  if (!workspace || workspace_bytes < gate_up_bwd_bytes(R_cap, n_local, H, I))
+    return MOE_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  Carve c(workspace);
+  const GateUpBwdWs w = carve_gate_up_bwd(c, R_cap, n_local, H, I);
+  return status_of(run_gate_up_bwd(dgu, x_perm, offsets, n_local, R_cap, H, I,
+                                   wgt, wgts, wut, wuts, dx, dw_gate, dw_up, w,
+                                   num_cus(), stream));
+}
+
+size_t moe_grouped_mlp_mxfp8_bwd_workspace_bytes(int64_t R_cap,
+                                                 int64_t n_local, int64_t H,
+                                                 int64_t I) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return 0;
+  return bwd_bytes(R_cap, n_local, H, I);
+}
+
+int moe_grouped_mlp_mxfp8_bwd(
+    const void *dy, const void *x_perm, const void *a, const void *gu,
+    const int32_t *offsets, const float *s_perm, int64_t n_local,
+    int64_t R_cap, int64_t H, int64_t I, const uint8_t *wdt,
+    const uint8_t *wdts, const uint8_t *wgt, const uint8_t *wgts,
+    const uint8_t *wut, const uint8_t *wuts, void *dx, float *ds,
+    void *dw_gate, void *dw_up, void *dw_down, void *workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!dy || !x_perm || !a || !gu || !offsets || !wdt || !wdts || !wgt ||
+      !wgts || !wut || !wuts || !dx || !ds || !dw_gate || !dw_up || !dw_down)
+    return MOE_E_ARG;
+  if (!all_aligned({dy, x_perm, a, gu, wdt, wdts, wgt, wgts, wut, wuts, dx, ds,
+                    dw_gate, dw_up, dw_down}))
+    return MOE_E_ALIGN;
+  if (!workspace || workspace_bytes < bwd_bytes(R_cap, n_local, H, I))
+    return MOE_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  Carve c(workspace);
+  uint16_t *dgu = c.take<uint16_t>((size_t)R_cap * 2 * I);
+  Carve shared = c;   // both halves carve the same region, one after the other
+  const int cus = num_cus();
+  const DownBwdWs wd = carve_down_bwd(c, R_cap, n_local, H, I);
+  hipError_t err = run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap, H,
+                                I, wdt, wdts, dgu, ds, dw_down, wd, cus,
+                                stream);
+  if (err != hipSuccess) return MOE_E_HIP;
+  const GateUpBwdWs wg = carve_gate_up_bwd(shared, R_cap, n_local, H, I);
+  return status_of(run_gate_up_bwd(dgu, x_perm, offsets, n_local, R_cap, H, I,
+                                   wgt, wgts, wut, wuts, dx, dw_gate, dw_up,
+                                   wg, cus, stream));
 }
 
 }  // extern "C"

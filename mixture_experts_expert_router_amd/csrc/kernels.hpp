@@ -53,4 +53,44 @@ hipError_t launch_combine(const void *y, const int32_t *inv,
                           const float *topk_w, int64_t T, int k, int64_t H,
                           int dtype, void *out, int num_cus, hipStream_t s);
 
+// ---- MXFP8 ----
+hipError_t launch_mx_quant_rows(const uint16_t *in, int64_t rows, int64_t cols,
+                                int64_t ld_in, uint8_t *codes,
+                                int64_t ld_codes, uint8_t *scales,
+                                int64_t ld_scales, const int32_t *rows_dev,
+                                hipStream_t s);
+hipError_t launch_mx_quant_cols(const uint16_t *in, int64_t rows,
+                                int64_t cols, int64_t ld_in,
+                                const int32_t *seg, int nseg, int align,
+                                int32_t *pad, uint8_t *codes,
+                                int64_t ld_codes, uint8_t *scales,
+                                int64_t ld_scales, int num_cus,
+                                hipStream_t s);
+
+// One MXFP8 grouped GEMM (see mx_gemm.hip for the modes and epilogues).
+struct MxGemmDesc {
+  const uint8_t *A, *As;           // codes / scales, K-contiguous
+  int64_t lda, ldas;
+  const uint8_t *B0, *B0s, *B1, *B1s;
+  int64_t ldb, ldbs, b_stride, bs_stride;
+  const int32_t *offsets;          // row-segment mode: [G + 1]
+  const int32_t *kseg;             // K-segment mode: [G + 1]
+  int32_t *tile_ws;                // row-segment mode: [G + 1] scratch
+  int G, M, N, K;
+  int64_t R_cap;
+  void *C;
+  int64_t ldc, c_stride;
+  const float *row_scale;
+  uint16_t *gu;
+  int64_t ldgu;
+  uint16_t *dgu;
+  float *ds_part;
+  float *ds;
+  int ksplit;
+};
+enum { MXE_BF16 = 0, MXE_SWIGLU = 1, MXE_SWIGLU_BWD = 2 };
+hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
+                            hipStream_t s);
+hipError_t launch_mx_kseg(const MxGemmDesc &d, int num_cus, hipStream_t s);
+
 }  // namespace moe

@@ -179,7 +179,7 @@ WORKLOADS = {
                               8, 8, "logits", 1.1),
     "mid_bf16": Workload("mid_bf16", "bf16", 1024, 1024, 768, 32, 4, 0, 32,
                          "gemm", 1.2),
-    "small_mxfp8": Workload("small_mxfp8", "mxfp8", 200, 256, 512, 4, 2, 0, 4,
+    "small_mxfp8": Workload("small_mxfp8", "mxfp8", 200, 512, 512, 4, 2, 0, 4,
                             "logits", None),
     "mid_mxfp8": Workload("mid_mxfp8", "mxfp8", 1000, 512, 1024, 8, 2, 0, 8,
                           "logits", None),

@@ -120,6 +120,61 @@ def test_combine_validation(L):
     assert c(None, None, None, 0, 2, 16, BF16, None, None) == 0
 
 
+def test_mxfp8_validation(L):
+    q = L.moe_mxfp8_quantize
+    # axis, cols % 32, alignment, align value, capacity, segments need pad
+    assert q(P, 64, 64, 64, 2, None, 0, 32, P, 64, P, 2, None, None) == E_ARG
+    assert q(P, 64, 48, 48, 0, None, 0, 32, P, 48, P, 2, None, None) == E_SHAPE
+    assert q(P, 64, 64, 64, 0, None, 0, 32, P_ODD, 64, P, 2, None, None) == E_ALIGN
+    assert q(P, 64, 64, 64, 1, None, 0, 16, P, 64, P, 2, None, None) == E_SHAPE
+    assert q(P, 64, 64, 64, 1, None, 0, 32, P, 48, P, 2, None, None) == E_SHAPE
+    assert q(P, 64, 64, 64, 1, P, 2, 32, P, 128, P, 4, None, None) == E_ARG
+    assert q(P, 64, 64, 64, 1, P, 2, 32, P, 80, P, 4, P, None) == E_SHAPE
+    assert q(P, 0, 64, 64, 0, None, 0, 32, P, 64, P, 2, None, None) == 0
+
+    fb = L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes
+    assert fb(100, 4, 512, 512) > 0 and fb(100, 4, 500, 512) == 0
+    assert fb(100, 4, 512, 256) == 0 and fb(100, 0, 512, 512) == 0
+    ws = fb(64, 2, 512, 512)
+    f = L.moe_grouped_mlp_mxfp8_fwd
+
+    def fwd(H=512, I=512, xq=P, wsp=P, wsb=ws, R=64):
+        return f(xq, P, P, None, 2, R, H, I, P, P, P, P, P, P, P, P, P, wsp,
+                 wsb, None)
+
+    assert fwd(H=256) == E_SHAPE and fwd(I=520) == E_SHAPE
+    assert fwd(xq=None) == E_ARG and fwd(xq=P_ODD) == E_ALIGN
+    assert fwd(wsp=None) == E_WS and fwd(wsb=ws - 1) == E_WS
+    assert fwd(R=0) == 0
+
+    lb = L.moe_grouped_linear_mxfp8_workspace_bytes(64, 2, 1024)
+    assert lb > 0 and L.moe_grouped_linear_mxfp8_workspace_bytes(64, 2, 1000) == 0
+    g = L.moe_grouped_linear_mxfp8
+    assert g(P, P, 2, 64, 1024, 0, P, P, P, P, lb, None) == E_SHAPE
+    assert g(P, P, 2, 64, 1000, 64, P, P, P, P, lb, None) == E_SHAPE
+    assert g(P, None, 2, 64, 1024, 64, P, P, P, P, lb, None) == E_ARG
+    assert g(P, P, 2, 64, 1024, 64, P, P, P_ODD, P, lb, None) == E_ALIGN
+    assert g(P, P, 2, 64, 1024, 64, P, P, P, P, lb - 1, None) == E_WS
+
+    db = L.moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(64, 2, 512, 512)
+    gb = L.moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes(64, 2, 512, 512)
+    bb = L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes(64, 2, 512, 512)
+    assert db > 0 and gb > 0 and bb >= max(db, gb) + 64 * 2 * 512 * 2
+    d = L.moe_grouped_mlp_mxfp8_bwd_down
+    assert d(P, P, None, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db, None) == E_ARG
+    assert d(P, P, P, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db - 1, None) == E_WS
+    u = L.moe_grouped_mlp_mxfp8_bwd_gate_up
+    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, None, P, P, P, gb, None) == E_ARG
+    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P_ODD, P, gb, None) == E_ALIGN
+    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P, P, gb - 1, None) == E_WS
+    b = L.moe_grouped_mlp_mxfp8_bwd
+    args = [P, P, P, P, P, None, 2, 64, 512, 512] + [P] * 11 + [P, bb, None]
+    bad = list(args); bad[-2] = bb - 1
+    assert b(*bad) == E_WS
+    bad = list(args); bad[0] = None
+    assert b(*bad) == E_ARG
+
+
 def _py_sources(d):
     for root, _, files in os.walk(os.path.join(ROOT, d)):
         for fn in files:

@@ -1,0 +1,193 @@
+"""MXFP8 path through the C ABI against the CPU oracle.
+
+Codes and scales of given bf16 inputs must match bit for bit.  Float
+outputs must meet max(|err| - bf16 slack) <= 6e-2 * RMS of each row of the
+reference (the oracle dequantises exactly and works in fp64).
+
+Tensors handed from one operation to the next are bf16 and are quantised
+again by the next GEMM.  When such a tensor is computed on both sides (fp32
+on the device, fp64 in the oracle), a value near an E4M3 rounding boundary
+can be quantised to neighbouring codes on the two sides; each code choice is
+correct for its input.  So every GEMM stage is checked on the oracle's own
+bf16 hand-off tensors, where both sides quantise identical values, and the
+fused calls are checked end to end on what no such decision feeds (g, u, a,
+ds) plus an aggregate bound on the rest.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mixture_experts_expert_router_amd as moe
+import moe_synth as synth
+import oracle as orc
+from gpu_util import print_case, rel_err, scaled_excess, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+TAU = 6e-2
+
+
+def bf16_bits(a):
+    t = torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def special_rows(cols, rng):
+    rows = [rng.standard_normal(cols) * 10.0 ** rng.integers(-3, 3)]
+    z = np.zeros(cols); rows.append(z)                            # all-zero block
+    p2 = 2.0 ** rng.integers(-20, 20, cols) * rng.choice([-1, 1], cols)
+    rows.append(p2)                                               # powers of two
+    mid = np.full(cols, 448.0); mid[1::2] = 1.0625 * 2 ** 0       # ties after scaling
+    rows.append(mid)
+    tiny = rng.standard_normal(cols); tiny[::3] = -1e-30          # rounds to -0
+    rows.append(tiny)
+    big = rng.standard_normal(cols) * 1e30; rows.append(big)
+    return np.stack(rows)
+
+
+def test_quantize_rows_bit_exact():
+    rng = np.random.default_rng(5)
+    cols = 256
+    v = np.concatenate([rng.standard_normal((61, cols)), special_rows(cols, rng)])
+    xb = bf16_bits(v)
+    codes, scales = moe.mxfp8_quantize(to_dev(xb), 0)
+    moe.debug_sync()
+    rc, rs = orc.mx_quantize_rows(orc.to_f64(xb))
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("align", [32, 512])
+def test_quantize_cols_segments_bit_exact(align):
+    rng = np.random.default_rng(6)
+    rows, cols = 100, 96
+    xb = bf16_bits(rng.standard_normal((rows, cols)))
+    seg = np.array([0, 5, 5, 70, 100], dtype=np.int32)
+    codes, scales, pad = moe.mxfp8_quantize(to_dev(xb), 1, to_dev(seg), align)
+    moe.debug_sync()
+    pad = pad.cpu().numpy()
+    lens = np.diff(seg)
+    np.testing.assert_array_equal(pad, np.concatenate([[0], np.cumsum((lens + align - 1) // align * align)]))
+    c, s = codes.cpu().numpy(), scales.cpu().numpy()
+    x64 = orc.to_f64(xb)
+    for i in range(len(seg) - 1):
+        n = seg[i + 1] - seg[i]
+        if n == 0:
+            continue
+        npad = (n + align - 1) // align * align
+        blk = np.zeros((cols, npad))
+        blk[:, :n] = x64[seg[i]:seg[i + 1]].T
+        rc, rs = orc.mx_quantize_rows(blk)
+        np.testing.assert_array_equal(c[:, pad[i]:pad[i] + npad], rc)
+        np.testing.assert_array_equal(s[:, pad[i] // 32:(pad[i] + npad) // 32], rs)
+
+
+def _mx_case(name):
+    wl = synth.WORKLOADS[name]
+    inp = synth.make_inputs(wl)
+    idx, w = orc.topk_softmax(inp["logits"], wl.k)
+    p = orc.permute(idx, 0, wl.n_local)
+    x_perm = orc.gather_rows(inp["x"], p["row_src"], wl.k)
+    s = w.reshape(-1)[p["row_src"]].astype(np.float32)
+    dy = synth.make_dy(wl, p["R"])
+    ref = orc.mxfp8_mlp_step(x_perm, p["offsets"], s.astype(np.float64),
+                             inp["w_gate"], inp["w_up"], inp["w_down"], dy)
+    return wl, inp, p, x_perm, s, dy, ref
+
+
+def _bits(v):
+    """bf16 bits of values the oracle already rounded to bf16 (exact)."""
+    v = orc.round_bf16(v)
+    return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _check(got, ref, what, bad):
+    e = scaled_excess(got, ref, "bf16")
+    print_case(what, f"row excess {e:.2e}, plain {rel_err(got, ref):.2e}")
+    if not e <= TAU:
+        bad.append(f"{what}: {e:.3e}")
+
+
+def _frob(got, ref, what, bad, bound=2e-2):
+    r = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    print_case(what, f"relative Frobenius error {r:.2e}")
+    if not r <= bound:
+        bad.append(f"{what}: frobenius {r:.3e}")
+
+
+@pytest.fixture(scope="module", params=["small_mxfp8", "mid_mxfp8"])
+def case(request):
+    name = request.param
+    print_case(name)
+    wl, inp, p, x_perm, s, dy, ref = _mx_case(name)
+    d = {k: to_dev(inp[k]) for k in ("w_gate", "w_up", "w_down")}
+    mw = moe.MxWeights(d["w_gate"], d["w_up"], d["w_down"])
+    return dict(name=name, wl=wl, p=p, x_perm=x_perm, s=s, dy=dy, ref=ref,
+                mw=mw, offs=to_dev(p["offsets"]), st=to_dev(s))
+
+
+def test_mxfp8_down_projection_stage(case):
+    """y = MX(a) MX(W_d)^T on the oracle's bf16 a."""
+    c, ref, R = case, case["ref"], case["p"]["R"]
+    y = moe.grouped_linear_mxfp8(to_dev(_bits(ref["a"])), c["offs"],
+                                 c["wl"].n_local, c["mw"].wd, c["mw"].wds)
+    moe.debug_sync()
+    bad = []
+    _check(to_f64(y[:R]), ref["y"], f"{c['name']} stage y", bad)
+    assert not bad, bad
+
+
+def test_mxfp8_backward_down_stage(case):
+    """da -> SwiGLU backward -> dg, du, ds, and dW_down, on the oracle's
+    bf16 a, g, u."""
+    c, ref, R, I = case, case["ref"], case["p"]["R"], case["wl"].I
+    gu = np.concatenate([_bits(ref["g"]), _bits(ref["u"])], axis=1)
+    out = moe.mxfp8_mlp_bwd_down(to_dev(c["dy"]), to_dev(_bits(ref["a"])),
+                                 to_dev(gu), c["offs"], c["st"], c["mw"])
+    moe.debug_sync()
+    bad = []
+    n = c["name"]
+    _check(to_f64(out["dgu"][:R, :I]), ref["dg"], f"{n} stage dg", bad)
+    _check(to_f64(out["dgu"][:R, I:]), ref["du"], f"{n} stage du", bad)
+    _check(out["ds"][:R].cpu().numpy().astype(np.float64), ref["ds"],
+           f"{n} stage ds", bad)
+    for e in range(c["wl"].n_local):
+        _check(to_f64(out["dw_down"][e]), ref["dw_down"][e],
+               f"{n} stage dw_down[{e}]", bad)
+    assert not bad, bad
+
+
+def test_mxfp8_backward_gate_up_stage(case):
+    """dX, dW_gate, dW_up on the oracle's bf16 dg, du."""
+    c, ref, R = case, case["ref"], case["p"]["R"]
+    dgu = np.concatenate([_bits(ref["dg"]), _bits(ref["du"])], axis=1)
+    out = moe.mxfp8_mlp_bwd_gate_up(to_dev(dgu), to_dev(c["x_perm"]),
+                                    c["offs"], c["mw"])
+    moe.debug_sync()
+    bad = []
+    n = c["name"]
+    _check(to_f64(out["dx"][:R]), ref["dx"], f"{n} stage dx", bad)
+    for key in ("dw_gate", "dw_up"):
+        for e in range(c["wl"].n_local):
+            _check(to_f64(out[key][e]), ref[key][e], f"{n} stage {key}[{e}]", bad)
+    assert not bad, bad
+
+
+def test_mxfp8_fused_forward_backward(case):
+    c, ref, R, I = case, case["ref"], case["p"]["R"], case["wl"].I
+    xt = to_dev(c["x_perm"])
+    xq, xs = moe.mxfp8_quantize(xt, 0)
+    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, c["offs"], c["st"], c["mw"])
+    g = moe.mxfp8_mlp_bwd(to_dev(c["dy"]), xt, a, gu, c["offs"], c["st"],
+                          c["mw"])
+    moe.debug_sync()
+    bad = []
+    n = c["name"]
+    _check(to_f64(gu[:R, :I]), ref["g"], f"{n} g", bad)
+    _check(to_f64(gu[:R, I:]), ref["u"], f"{n} u", bad)
+    _check(to_f64(a[:R]), ref["a"], f"{n} a", bad)
+    _check(g["ds"][:R].cpu().numpy().astype(np.float64), ref["ds"], f"{n} ds", bad)
+    _frob(to_f64(y[:R]), ref["y"], f"{n} y", bad)
+    _frob(to_f64(g["dx"][:R]), ref["dx"], f"{n} dx", bad)
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        _frob(to_f64(g[key]), ref[key], f"{n} {key}", bad)
+    assert not bad, bad
