@@ -29,6 +29,8 @@ import moe_synth as synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 (MX-scaled) MFMA
+METRIC = "grouped MoE FFN TFLOP/s + rows/s per layer; % MFMA peak or % HBM BW"
 
 
 def to_dev(a, dev):
@@ -115,6 +117,177 @@ def cpu_baseline(wl, inp, tokens):
                       f"chosen local experts + weighted sum; {dt:.1f} s"}
 
 
+def cpu_baseline_mx(wl, inp, x_perm, offsets, s_perm, dy, rows, inter):
+    """The oracle's MXFP8 step on a slice: the first `rows` rows of expert 0
+    and its first `inter` intermediate channels (weights sliced to match)."""
+    import oracle
+    r = min(rows, int(offsets[1]))
+    sl = slice(0, inter)
+    wg = np.ascontiguousarray(inp["w_gate"][:1, sl, :])
+    wu = np.ascontiguousarray(inp["w_up"][:1, sl, :])
+    wd = np.ascontiguousarray(inp["w_down"][:1, :, sl])
+    t0 = time.perf_counter()
+    oracle.mxfp8_mlp_step(x_perm[:r], np.array([0, r]), s_perm[:r], wg, wu, wd,
+                          dy[:r])
+    dt = time.perf_counter() - t0
+    flop = 18.0 * r * wl.H * inter
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{r} rows of expert 0 with its first {inter} of {wl.I} "
+                      f"intermediate channels: fp64 MX quantisation of every "
+                      f"GEMM operand (weights included), forward, dgrad and "
+                      f"wgrad; {dt:.1f} s"}
+
+
+def run_mx(args, wl, dev):
+    """MXFP8 grouped-MLP training step: permute, quantise x, forward (gate/up
+    + SwiGLU x scale, then down), backward (down + SwiGLU backward, then
+    gate/up data and weight gradients).  Routing runs before timing; the
+    master weights are quantised once per step in training, timed apart."""
+    log(f"workload {wl.name}: generating inputs")
+    t0 = time.time()
+    inp = synth.make_inputs(wl, with_weights=False)
+    d = {k: to_dev(v, dev) for k, v in inp.items()}
+    W = {k: torch.empty(shape, dtype=torch.bfloat16, device=dev) for k, shape in
+         (("w_gate", (wl.n_local, wl.I, wl.H)), ("w_up", (wl.n_local, wl.I, wl.H)),
+          ("w_down", (wl.n_local, wl.H, wl.I)))}
+    host_w = {k: [] for k in W}
+    for e0 in range(0, wl.n_local, 2):
+        e1 = min(wl.n_local, e0 + 2)
+        part = synth.make_weights(wl, range(wl.e_begin + e0, wl.e_begin + e1))
+        for key in W:
+            W[key][e0:e1].copy_(to_dev(part[key], dev))
+            host_w[key].append(part[key])
+    for key in host_w:
+        inp[key] = np.concatenate(host_w[key])
+    T, k, H, I, n = wl.T, wl.k, wl.H, wl.I, wl.n_local
+    F = T * k
+    logits = d["logits"].clone()
+    topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    moe.route_topk(k, logits=logits, topk_idx=topk_idx, topk_w=topk_w)
+    pout = moe.PermuteOut(T, k, H, n, torch.bfloat16, dev)
+    moe.permute(topk_idx, d["x"], wl.e_begin, n, topk_w=topk_w, out=pout)
+    torch.cuda.synchronize()
+    R = int(pout.offsets[-1].item())
+    dy_host = synth.make_dy(wl, R)
+    dy = torch.zeros((F, H), dtype=torch.bfloat16, device=dev)
+    dy[:R].copy_(to_dev(dy_host, dev))
+    log(f"inputs ready in {time.time() - t0:.1f} s, R = {R}")
+
+    # Buffers and workspaces, allocated once.
+    bf = torch.bfloat16
+    xq = torch.empty((F, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((F, H // 32), dtype=torch.uint8, device=dev)
+    a = torch.empty((F, I), dtype=bf, device=dev)
+    gu = torch.empty((F, 2 * I), dtype=bf, device=dev)
+    y = torch.empty((F, H), dtype=bf, device=dev)
+    dx = torch.empty((F, H), dtype=bf, device=dev)
+    ds = torch.empty(F, dtype=torch.float32, device=dev)
+    dwg = torch.empty((n, I, H), dtype=bf, device=dev)
+    dwu = torch.empty_like(dwg)
+    dwd = torch.empty((n, H, I), dtype=bf, device=dev)
+    L = moe.lib()
+    ws_f = torch.empty(L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes(F, n, H, I),
+                       dtype=torch.uint8, device=dev)
+    ws_l = torch.empty(L.moe_grouped_linear_mxfp8_workspace_bytes(F, n, I),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes(F, n, H, I),
+                       dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    qev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    mw_holder = {}
+
+    def quant_masters():
+        mw_holder["mw"] = moe.MxWeights(W["w_gate"], W["w_up"], W["w_down"])
+
+    def step(timed_ev=None):
+        mw = mw_holder["mw"]
+        moe.permute(topk_idx, d["x"], wl.e_begin, n, topk_w=topk_w, out=pout)
+        moe.mxfp8_quantize(pout.x_perm, 0, codes=xq, scales=xs)
+        if timed_ev is not None:
+            timed_ev[0].record(stream)
+        moe.mxfp8_mlp_fwd(xq, xs, pout.offsets, pout.s_perm, mw, a=a, gu=gu,
+                          workspace=ws_f, down=False)
+        if timed_ev is not None:
+            timed_ev[1].record(stream)
+        moe.grouped_linear_mxfp8(a, pout.offsets, n, mw.wd, mw.wds, y=y,
+                                 workspace=ws_l)
+        moe.mxfp8_mlp_bwd(dy, pout.x_perm, a, gu, pout.offsets, pout.s_perm,
+                          mw, dx=dx, ds=ds, dw_gate=dwg, dw_up=dwu,
+                          dw_down=dwd, workspace=ws_b)
+
+    quant_masters()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    qev[0].record(stream)
+    quant_masters()
+    qev[1].record(stream)
+    torch.cuda.synchronize()
+    master_ms = qev[0].elapsed_time(qev[1])
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    gu_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev]))
+
+    flop_fwd = 6.0 * R * H * I
+    flop = 3.0 * flop_fwd                       # forward + dgrad + wgrad
+    tflops = flop / (ms_step * 1e-3) / 1e12
+    gu_flop = 4.0 * R * H * I
+    gu_tflops = gu_flop / (gu_ms * 1e-3) / 1e12
+    res = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8 (e4m3 + e8m0 per 32), fp32 accumulate",
+        "data": "synthetic (seeded generator; random-init weights)",
+        "config": {
+            "workload": f"{wl.name}: MXFP8 grouped-MLP training step, T={T} "
+                        f"hidden={H} intermediate={I} E={wl.E} top-{k}; "
+                        f"permute + quantise x + forward + dgrad + wgrad",
+            "rows": R,
+            "router": "routed before timing",
+        },
+        "rows_per_s": round(R / (ms_step * 1e-3), 1),
+        "step_mfma_frac_fp8": round(tflops / FP8_PEAK_TFLOPS, 4),
+        "step_mfma_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "master_quant_ms": round(master_ms, 4),
+        "roofline": {
+            "kernel": "MXFP8 grouped gate/up GEMM + SwiGLU x scale (forward)",
+            "bound": "mfma",
+            "achieved": round(gu_tflops, 2),
+            "peak": FP8_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(gu_tflops / FP8_PEAK_TFLOPS, 4),
+            "traffic": None,
+            "avg_ms": round(gu_ms, 4),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline: oracle MXFP8 step on a slice")
+        offs = pout.offsets.cpu().numpy()
+        xp = pout.x_perm[:R].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        sp = pout.s_perm[:R].cpu().numpy().astype(np.float64)
+        res["cpu_baseline"] = cpu_baseline_mx(wl, inp, xp, offs, sp, dy_host,
+                                              rows=512, inter=2048)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -122,7 +295,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4_full_bf16",
                     choices=["c4_full_bf16", "c2_ep64_bf16", "c3_ep8_bf16",
-                             "mid_bf16"])
+                             "mid_bf16", "c5_mxfp8", "mid_mxfp8"])
     ap.add_argument("--cpu-tokens", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -139,6 +312,8 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if wl.dtype == "mxfp8":
+        return run_mx(args, wl, dev)
     # Weight copies rotate across steps when the weights are small enough for
     # the 256 MB last-level cache to hold them between steps.
     wbytes = 3 * wl.n_local * wl.H * wl.I * 2
@@ -220,7 +395,7 @@ def main():
     gu_gbs = alg["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
     gu_tflops = alg["gate_up_flop"] / (gate_up_ms * 1e-3) / 1e12
     res = {
-        "metric": "grouped MoE FFN TFLOP/s + rows/s per layer; % MFMA peak or % HBM BW",
+        "metric": METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,

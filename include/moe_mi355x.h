@@ -237,6 +237,8 @@ int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
  * moe_grouped_gate_up (s_perm may be NULL).
  * Outputs (bf16): a [R_cap, I]; gu [R_cap, 2I] = [g | u] per row (may be
  * NULL; the backward needs it); y [R_cap, H].  Rows < R are written.
+ * y == NULL stops after a (wd, wds are then not read); the down projection
+ * is then moe_grouped_linear_mxfp8 on a.
  * workspace: moe_grouped_mlp_mxfp8_fwd_workspace_bytes() bytes.
  * Limits: H % 512 == 0, I % 512 == 0, 1 <= n_local <= 4096.
  */

@@ -265,7 +265,8 @@ def debug_sync(stream=None):
 # ---------------------------------------------------------------- MXFP8
 
 
-def mxfp8_quantize(x, axis=0, seg_offsets=None, align=32, stream=None):
+def mxfp8_quantize(x, axis=0, seg_offsets=None, align=32, stream=None,
+                   codes=None, scales=None):
     """MX-quantise a bf16 matrix [rows, cols].
 
     axis 0 -> (codes [rows, cols] u8, scales [rows, cols/32] u8).
@@ -279,8 +280,11 @@ def mxfp8_quantize(x, axis=0, seg_offsets=None, align=32, stream=None):
     dev = x.device
     ld_in = x.stride(0)
     if axis == 0:
-        codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
-        scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        if codes is None:
+            codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+        if scales is None:
+            scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
+        assert codes.shape == (rows, cols) and scales.shape == (rows, cols // 32)
         _call("moe_mxfp8_quantize", _p(x), rows, cols, ld_in, 0, None, 0, 32,
               _p(codes), cols, _p(scales), cols // 32, None, _stream(stream))
         return codes, scales
@@ -318,7 +322,8 @@ class MxWeights:
 
 
 def mxfp8_mlp_fwd(xq, xs, offsets, s_perm, mw, a=None, gu=None, y=None,
-                  workspace=None, stream=None):
+                  workspace=None, stream=None, down=True):
+    """down=False stops after a (y is returned as None)."""
     R_cap = xq.shape[0]
     H, I, n = mw.H, mw.I, mw.n_local
     dev = xq.device
@@ -326,7 +331,9 @@ def mxfp8_mlp_fwd(xq, xs, offsets, s_perm, mw, a=None, gu=None, y=None,
         a = torch.empty((R_cap, I), dtype=torch.bfloat16, device=dev)
     if gu is None:
         gu = torch.empty((R_cap, 2 * I), dtype=torch.bfloat16, device=dev)
-    if y is None:
+    if not down:
+        y = None
+    elif y is None:
         y = torch.empty((R_cap, H), dtype=torch.bfloat16, device=dev)
     if workspace is None:
         nb = lib().moe_grouped_mlp_mxfp8_fwd_workspace_bytes(R_cap, n, H, I)

@@ -547,11 +547,10 @@ int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
                               size_t workspace_bytes, hipStream_t stream) {
   if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
   if (R_cap == 0) return MOE_OK;
-  if (!xq || !xs || !offsets || !wg || !wgs || !wu || !wus || !wd || !wds ||
-      !a || !y)
+  if (!xq || !xs || !offsets || !wg || !wgs || !wu || !wus || !a)
     return MOE_E_ARG;
-  if (!all_aligned({xq, xs, wg, wgs, wu, wus, wd, wds, a, y}) ||
-      (gu && !aligned16(gu)))
+  if (y && (!wd || !wds)) return MOE_E_ARG;
+  if (!all_aligned({xq, xs, wg, wgs, wu, wus, wd, wds, a, y, gu}))
     return MOE_E_ALIGN;
   if (!workspace || workspace_bytes < fwd_bytes(R_cap, n_local, I))
     return MOE_E_WORKSPACE;
@@ -570,6 +569,7 @@ int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
   d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
   hipError_t err = moe::launch_mx_rowseg(d, moe::MXE_SWIGLU, cus, stream);
   if (err != hipSuccess) return MOE_E_HIP;
+  if (!y) return MOE_OK;
   // down: a (quantised along I) x W_d (along I)
   return status_of(run_linear(a, offsets, n_local, R_cap, I, H, wd, wds, y, w,
                               cus, stream));

@@ -45,4 +45,38 @@ __device__ __forceinline__ int upper_bound_minus1(const int32_t *p, int n,
   return lo;
 }
 
+// Tile of workgroup `bid` when every tile has its own workgroup and the
+// grid is launched for an upper bound of `total` (the real count lives on
+// the device).  Workgroups are handed to the 8 XCDs round-robin by id and,
+// on one XCD, in id order; XCD x gets the contiguous range [x*per,
+// (x+1)*per), so neighbouring tiles (which share operands) run at the same
+// time behind one L2.  Returns -1 for a workgroup without a tile.
+__device__ __forceinline__ int xcd_tile(int bid, int total) {
+  const int per = (total + 7) >> 3;
+  const int j = bid >> 3;
+  if (j >= per) return -1;
+  const int t = (bid & 7) * per + j;
+  return t < total ? t : -1;
+}
+
+// (m-tile, n-tile) of tile `local` among one group's mtiles x NT tiles, in
+// bands of GM m-tiles: inside a band the m-tile runs fastest, so a run of
+// consecutive tiles covers a GM x (run / GM) block and re-reads neither
+// operand from HBM.
+__device__ __forceinline__ void banded_mn(int local, int mtiles, int NT,
+                                          int GM, int &mt, int &nt) {
+  const int band = local / (GM * NT);
+  const int first = band * GM;
+  const int gm = min(GM, mtiles - first);
+  const int r = local - band * GM * NT;
+  mt = first + r % gm;
+  nt = r / gm;
+}
+
+// Workgroups to launch for at most `max_tiles` tiles (see xcd_tile).
+inline int64_t tile_grid(int64_t max_tiles) {
+  int64_t g = (max_tiles + 7) / 8 * 8;
+  return g < 8 ? 8 : g;
+}
+
 }  // namespace moe

@@ -237,10 +237,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
   if (p.offsets) total = p.tile_prefix[p.G];
   else total = (p.single_rows + BM - 1) / BM * p.NT;
 
-  const int nwg = gridDim.x, bid = blockIdx.x;
-  const int Lg = (bid & 7) * (nwg >> 3) + (bid >> 3);
-
-  for (int t = Lg; t < total; t += nwg) {
+  const int t = xcd_tile(blockIdx.x, total);
+  if (t < 0) return;
+  {
     int e, r_begin, r_end, local;
     if (p.offsets) {
       e = upper_bound_minus1(p.tile_prefix, p.G, t);
@@ -251,7 +250,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
       e = 0; r_begin = 0; r_end = p.single_rows; local = t;
     }
     const int mtiles = (r_end - r_begin + BM - 1) / BM;
-    const int nt = local / mtiles, mt = local - nt * mtiles;
+    int mt, nt;
+    banded_mn(local, mtiles, p.NT, 8, mt, nt);
     const int row0 = r_begin + mt * BM;
     const int rows = min(BM, r_end - row0);
 
@@ -385,14 +385,9 @@ int ntiles(int N, int BN, bool swiglu) {
 template <int BM, int BN, int WM, int WN, int BK, int ST, int EPI>
 hipError_t launch_one(GemmArgs p, int num_cus, int64_t max_tiles,
                       hipStream_t s) {
-  // Workgroups resident per CU: 160 KiB of LDS shared out.
-  constexpr int lds_bytes = ST * (BM + BN) * BK * 2;
-  constexpr int occ = lds_bytes <= 80 * 1024 ? 2 : 1;
-  int64_t grid = (int64_t)num_cus * occ;
-  if (max_tiles < grid) grid = (max_tiles + 7) / 8 * 8;
-  if (grid < 8) grid = 8;
+  (void)num_cus;
   grouped_gemm_kernel<BM, BN, WM, WN, BK, ST, EPI>
-      <<<(unsigned)grid, 256, 0, s>>>(p);
+      <<<(unsigned)tile_grid(max_tiles), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -117,18 +117,16 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   int total;
   if (MODE == MX_ROWSEG) total = p.tile_prefix[p.G];
   else total = p.G * p.MT * p.NT;
-  const int nwg = gridDim.x, bid = blockIdx.x;
-  const int Lg = (bid & 7) * (nwg >> 3) + (bid >> 3);
-
-  for (int t = Lg; t < total; t += nwg) {
-    int e, row0, rows, nt, k0, KT;
+  const int t = xcd_tile(blockIdx.x, total);
+  if (t < 0) return;
+  {
+    int e, row0, rows, nt, mt, k0, KT;
     if (MODE == MX_ROWSEG) {
       e = upper_bound_minus1(p.tile_prefix, p.G, t);
       const int r_begin = p.offsets[e], r_end = p.offsets[e + 1];
       const int local = t - p.tile_prefix[e];
       const int mtiles = (r_end - r_begin + BM - 1) / BM;
-      nt = local / mtiles;
-      const int mt = local - nt * mtiles;
+      banded_mn(local, mtiles, p.NT, 8, mt, nt);
       row0 = r_begin + mt * BM;
       rows = min(BM, r_end - row0);
       k0 = 0;
@@ -136,9 +134,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     } else {
       const int per_g = p.MT * p.NT;
       e = t / per_g;
-      const int local = t - e * per_g;
-      nt = local / p.MT;
-      const int mt = local - nt * p.MT;
+      banded_mn(t - e * per_g, p.MT, p.NT, 8, mt, nt);
       row0 = mt * BM;
       rows = min(BM, p.M - row0);
       k0 = p.kseg[e];
@@ -382,10 +378,8 @@ namespace {
 template <int MODE, int EPI>
 hipError_t mx_launch(const MxArgs &p, int num_cus, int64_t max_tiles,
                      hipStream_t s) {
-  int64_t grid = num_cus;
-  if (max_tiles < grid) grid = (max_tiles + 7) / 8 * 8;
-  if (grid < 8) grid = 8;
-  mx_gemm_kernel<MODE, EPI><<<(unsigned)grid, 256, 0, s>>>(p);
+  (void)num_cus;
+  mx_gemm_kernel<MODE, EPI><<<(unsigned)tile_grid(max_tiles), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
