@@ -33,6 +33,38 @@ FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 (MX-scaled) MFMA
 METRIC = "grouped MoE FFN TFLOP/s + rows/s per layer; % MFMA peak or % HBM BW"
 
 
+def measured_traffic(workload):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), or None
+    when there are none or the kernel's sources changed since they were
+    taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        rec = json.load(open(path))[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    h = hashlib.sha256()
+    for f in rec["sources"]:
+        with open(os.path.join(ROOT, "mixture_experts_expert_router_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != rec["sources_sha256"]:
+        return None
+    return int(rec["bytes"])
+
+
+def copy_probe(mb, dev):
+    """One elementwise copy of `mb` MiB (read + write) after the timed
+    region: the reference for scaling HBM byte counters."""
+    n = mb * (1 << 20) // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    log(f"copy probe: {n * 2} bytes read, {n * 2} bytes written")
+
+
 def to_dev(a, dev):
     if a.dtype == np.uint16:
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(
@@ -237,6 +269,8 @@ def run_mx(args, wl, dev):
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     gu_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev]))
+    if args.copy_probe_mb > 0:
+        copy_probe(args.copy_probe_mb, dev)
 
     flop_fwd = 6.0 * R * H * I
     flop = 3.0 * flop_fwd                       # forward + dgrad + wgrad
@@ -274,7 +308,8 @@ def run_mx(args, wl, dev):
             "peak": FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gu_tflops / FP8_PEAK_TFLOPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "avg_ms": round(gu_ms, 4),
         },
     }
@@ -380,14 +415,7 @@ def main():
     gate_up_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
 
     if args.copy_probe_mb > 0:
-        n = args.copy_probe_mb * (1 << 20) // 2
-        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        torch.mul(src, 1.0, out=dst)
-        torch.cuda.synchronize()
-        log(f"copy probe: {n * 2} bytes read, {n * 2} bytes written")
-        del src, dst
+        copy_probe(args.copy_probe_mb, dev)
 
     alg = algorithmic(wl, R, n_touched)
     flop = alg["flop_ffn"] + alg["flop_router"]
@@ -426,7 +454,9 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(wl.name),
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "algorithmic_bytes": int(alg["gate_up_bytes"]),
             "avg_ms": round(gate_up_ms, 4),
             "tflops": round(gu_tflops, 2),
             "mfma_frac": round(gu_tflops / BF16_PEAK_TFLOPS, 4),
