@@ -206,7 +206,7 @@ int moe_unpermute_combine(const void *y, const int32_t *inv,
 
 /*
  * moe_mxfp8_quantize - MX-quantise a bf16 matrix in[rows, cols] (row pitch
- * ld_in elements, ld_in % 8 == 0 for axis 0), cols % 32 == 0.
+ * ld_in elements, ld_in % 8 == 0, `in` 16-byte aligned), cols % 32 == 0.
  * axis 0: blocks of 32 along each row.  codes [rows, ld_codes] bytes
  *   (ld_codes % 16 == 0), scales [rows, ld_scales] (>= cols/32).
  * axis 1: blocks of 32 down each column, output transposed for a GEMM whose

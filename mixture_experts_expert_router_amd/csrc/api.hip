@@ -516,7 +516,8 @@ int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
         ld_scales, nullptr, stream));
   }
   if (align != 32 && align != 512) return MOE_E_SHAPE;
-  if (ld_codes % 16 != 0) return MOE_E_SHAPE;
+  if (ld_codes % 16 != 0 || ld_in % 8 != 0) return MOE_E_SHAPE;
+  if (!aligned16(in)) return MOE_E_ALIGN;
   if (seg_offsets) {
     if (n_seg < 1 || n_seg > 1 << 20 || pad_offsets == nullptr) return MOE_E_ARG;
     if (ld_codes < rows + (align - 1) * n_seg) return MOE_E_SHAPE;

@@ -95,49 +95,81 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(
 // axis 1: blocks of 32 rows down each column, inside segments of rows
 // [seg[s], seg[s+1]) zero-padded to a multiple of `align` (32 or 512); output
 // transposed: codesT[c, pad[s] + j] for row seg[s] + j, scalesT[c, blk].
-// seg == null: one segment of all `rows`.  One thread per (column, padded
-// 32-row block); the grid walks all blocks.
+// seg == null: one segment of all `rows`.
+// One workgroup per tile of 128 padded rows x 64 columns: the tile is read
+// with coalesced 16-byte loads (8 threads per 128-byte row piece) into LDS,
+// then wavefront b quantises block b (32 rows) of all 64 columns, a lane per
+// column, and writes that column's 32 codes; the four wavefronts together
+// write each column's 128 codes as one 128-byte line.
+// Requires ld_in % 8 == 0, cols % 32 == 0 and a 16-byte aligned input.
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
     const uint16_t *__restrict__ in, int64_t rows, int64_t cols,
     int64_t ld_in, const int32_t *__restrict__ seg,
     const int32_t *__restrict__ pad, int nseg, int align,
     uint8_t *__restrict__ codes, int64_t ld_codes,
     uint8_t *__restrict__ scales, int64_t ld_scales) {
+  constexpr int TR = 128, TC = 64, LDT = TC + 2;   // +2: row pitch 132 B
+  __shared__ uint16_t tile[TR * LDT];
+  __shared__ int32_t src[TR];
+  const int tid = threadIdx.x;
   const int padded = seg ? pad[nseg] : (int)((rows + align - 1) / align * align);
-  const int total_blocks = padded / 32;
-  const int64_t n = (int64_t)total_blocks * cols;
-  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < n;
-       t += (int64_t)gridDim.x * blockDim.x) {
-    const int blk = (int)(t / cols);
-    const int64_t c = t % cols;
-    const int prow = blk * 32;                     // padded row of the block
-    int r0, r1;
-    if (seg) {
-      const int s = upper_bound_minus1(pad, nseg, prow);
-      r0 = seg[s] + (prow - pad[s]);
-      r1 = seg[s + 1];
-    } else {
-      r0 = prow;
-      r1 = (int)rows;
+  const int ngrp = (padded + TR - 1) / TR;
+  const int ncg = (int)((cols + TC - 1) / TC);
+  const int64_t ntiles = (int64_t)ngrp * ncg;
+  for (int64_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
+    const int rg = (int)(g / ncg), cg = (int)(g % ncg);
+    const int prow0 = rg * TR;
+    const int64_t c0 = (int64_t)cg * TC;
+    if (tid < TR) {
+      const int prow = prow0 + tid;
+      int sr = -1;
+      if (prow < padded) {
+        if (seg) {
+          const int s = upper_bound_minus1(pad, nseg, prow);
+          const int r = seg[s] + (prow - pad[s]);
+          if (r < seg[s + 1]) sr = r;
+        } else if (prow < rows) {
+          sr = prow;
+        }
+      }
+      src[tid] = sr;
     }
-    float v[32];
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 32; ++j)
-      v[j] = (r0 + j < r1) ? bf16_bits_to_f32(in[(int64_t)(r0 + j) * ld_in + c]) : 0.f;
-    float amax = 0.f;
+    for (int p = 0; p < TR / 32; ++p) {
+      const int r = p * 32 + (tid >> 3);
+      const int cc = (tid & 7) * 8;
+      const int sr = src[r];
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (sr >= 0 && c0 + cc < cols)
+        v = *(const uint4 *)(in + (int64_t)sr * ld_in + c0 + cc);
+      uint32_t *d = (uint32_t *)(tile + r * LDT + cc);
+      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+    }
+    __syncthreads();
+    const int b = tid >> 6, c = tid & 63;
+    const int prow = prow0 + b * 32;
+    if (prow < padded && c0 + c < cols) {
+      float v[32];
+      float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    const uint32_t sb = mx_scale_byte(amax);
-    uint32_t packed[8];
+      for (int j = 0; j < 32; ++j) {
+        v[j] = bf16_bits_to_f32(tile[(b * 32 + j) * LDT + c]);
+        amax = fmaxf(amax, fabsf(v[j]));
+      }
+      const uint32_t sb = mx_scale_byte(amax);
+      uint32_t packed[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      packed[j] = e4m3_code(v[4 * j], sb) | (e4m3_code(v[4 * j + 1], sb) << 8) |
-                  (e4m3_code(v[4 * j + 2], sb) << 16) |
-                  (e4m3_code(v[4 * j + 3], sb) << 24);
-    uint4 *dst = (uint4 *)(codes + c * ld_codes + prow);
-    dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-    scales[c * ld_scales + blk] = (uint8_t)sb;
+      for (int j = 0; j < 8; ++j)
+        packed[j] = e4m3_code(v[4 * j], sb) | (e4m3_code(v[4 * j + 1], sb) << 8) |
+                    (e4m3_code(v[4 * j + 2], sb) << 16) |
+                    (e4m3_code(v[4 * j + 3], sb) << 24);
+      uint4 *dst = (uint4 *)(codes + (c0 + c) * ld_codes + prow);
+      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+      scales[(c0 + c) * ld_scales + prow / 32] = (uint8_t)sb;
+    }
+    __syncthreads();
   }
 }
 
