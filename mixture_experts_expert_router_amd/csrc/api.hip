@@ -315,7 +315,7 @@ DownBwdWs carve_down_bwd(Carve &c, int64_t R_cap, int64_t n_local, int64_t H,
   w.kpad = c.take<int32_t>(n_local + 1);
   w.dyq = c.take<uint8_t>((size_t)R_cap * H);
   w.dys = c.take<uint8_t>((size_t)R_cap * (H / 32));
-  w.ds_part = c.take<float>((size_t)R_cap * (I / 128) * 2);
+  w.ds_part = c.take<float>((size_t)R_cap * moe::mx_ds_parts(I));
   w.dyT = c.take<uint8_t>((size_t)H * w.kcap);
   w.dyTs = c.take<uint8_t>((size_t)H * (w.kcap / 32));
   w.aT = c.take<uint8_t>((size_t)I * w.kcap);

@@ -14,14 +14,14 @@
 //   * Work unit = tile of BM rows x BN B-rows of one expert.  A plan kernel
 //     turns the device-side offsets into tile prefixes for two classes of
 //     experts: those with at most kSmallRows rows (decode-like shares, run
-//     with 64-row tiles) and the rest (128- or 256-row tiles).  Each class has its
-//     own persistent launch; a launch whose class is empty exits at once.
-//     The host never needs the per-expert counts.
-//   * Persistent grid: every workgroup walks its tile list with stride
-//     gridDim.x.  Workgroups are renumbered so consecutive logical workgroups
-//     sit on the same XCD (hardware places workgroup b on XCD b % 8); tiles
-//     are ordered (expert, n-tile, m-tile), so the m-tiles of one weight strip
-//     and the neighbouring n-tiles run together on one XCD and share its L2.
+//     with 64-row tiles) and the rest (128- or 256-row tiles).  Each class has
+//     its own launch; the host never needs the per-expert counts.
+//   * One tile per workgroup; the grid is launched for an upper bound and
+//     each workgroup derives its tile from the device-side count (xcd_tile):
+//     XCD x (workgroup id mod 8) takes a contiguous tile range in dispatch
+//     order, and inside an expert tiles run in bands of 8 m-tiles with the
+//     m-tile fastest (banded_mn), so workgroups running together on one L2
+//     share the weight strip and the expert's rows.
 //   * 256 threads = 4 wavefronts in a WM x WN grid; each wavefront owns a
 //     (BM/WM) x (BN/WN) sub-tile of 32x32 blocks, v_mfma_f32_32x32x16_bf16
 //     with fp32 accumulators.
@@ -157,9 +157,13 @@ __device__ __forceinline__ void load_frags(const uint4 *As, const uint4 *Bs,
 }
 
 // The K loop of one tile for a wavefront with MV valid 32-row blocks.
-// Stages 0 .. STAGES-2 have been issued by the caller.  Fragment reads of
-// k-substep kk+1 are issued before the MFMAs of kk so LDS latency overlaps
-// matrix work; the loop body has no data-dependent branches.
+// Stages 0 .. STAGES-2 have been issued by the caller; every iteration
+// issues one more (clamped to the last stage at the tail, a harmless
+// re-read that keeps (STAGES-2)*L loads in flight at every wait).  The
+// stage's L loads are spread over its MFMAs (scheduling barriers keep them
+// there) instead of being issued in one burst, so the vector-memory queue
+// never stalls the matrix work; fragment reads of k-substep kk+1 are issued
+// before the MFMAs of kk.  The loop body has no data-dependent branches.
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MV>
 __device__ __forceinline__ void gemm_kloop(
     f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
@@ -169,24 +173,15 @@ __device__ __forceinline__ void gemm_kloop(
   constexpr int CPR = BK / 8, NB = BN / WN / 32, KK = BK / 16;
   constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
   constexpr int L = STAGE_CHUNKS / 256;
+  constexpr int NMF = MV * NB * KK;
   for (int kt = 0; kt < KT; ++kt) {
-    // Stage kt has landed once at most min(STAGES-2, KT-1-kt) later stages
-    // of this wavefront are still in flight; the barrier then also says
-    // every wavefront is done with the buffer refilled just below.
-    const int after = min(STAGES - 2, KT - 1 - kt);
-    if (after >= 4) wait_loads_barrier<(STAGES >= 6 ? 4 : 0) * L>();
-    else if (after == 3) wait_loads_barrier<(STAGES >= 5 ? 3 : 0) * L>();
-    else if (after == 2) wait_loads_barrier<(STAGES >= 4 ? 2 : 0) * L>();
-    else if (after == 1) wait_loads_barrier<L>();
-    else wait_loads_barrier<0>();
-    if (kt + STAGES - 1 < KT) {
-      const int st = (kt + STAGES - 1) % STAGES;
-      const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
-      const int64_t koff = (int64_t)(kt + STAGES - 1) * (BK * 2);
-#pragma unroll
-      for (int i = 0; i < L; ++i)
-        load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
-    }
+    wait_loads_barrier<(STAGES - 2) * L>();
+    // Loads of stage kt + STAGES - 1 (clamped to the last stage at the tail:
+    // the re-read is harmless and keeps the in-flight count fixed).
+    const int ks = min(kt + STAGES - 1, KT - 1);
+    const int st = (kt + STAGES - 1) % STAGES;
+    const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
+    const int64_t koff = (int64_t)ks * (BK * 2);
     if constexpr (MV > 0) {
       const uint4 *As = smem + (kt % STAGES) * STAGE_CHUNKS;
       const uint4 *Bs = As + BM * CPR;
@@ -201,13 +196,26 @@ __device__ __forceinline__ void gemm_kloop(
 #pragma unroll
         for (int m = 0; m < MV; ++m)
 #pragma unroll
-          for (int n = 0; n < NB; ++n)
+          for (int n = 0; n < NB; ++n) {
             acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 (kk & 1) ? a1[m] : a0[m], (kk & 1) ? b1[n] : b0[n], acc[m][n],
                 0, 0, 0);
+            const int f = (kk * MV + m) * NB + n;
+#pragma unroll
+            for (int i = f * L / NMF; i < (f + 1) * L / NMF; ++i) {
+              __builtin_amdgcn_sched_barrier(0);
+              load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          }
       }
+    } else {
+#pragma unroll
+      for (int i = 0; i < L; ++i)
+        load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
     }
   }
+  wait_loads_barrier<0>();
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
@@ -303,12 +311,11 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     // prologue: stages 0 .. STAGES-2
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st) {
-      if (st < KT) {
-        const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
+      const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
+      const int64_t koff = (int64_t)min(st, KT - 1) * (BK * 2);
 #pragma unroll
-        for (int i = 0; i < L; ++i)
-          load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + (int64_t)st * (BK * 2));
-      }
+      for (int i = 0; i < L; ++i)
+        load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
     }
     // the K loop, specialised for this wavefront's number of valid blocks
     // (a wavefront with none still keeps the loads and barriers going)

@@ -92,5 +92,7 @@ enum { MXE_BF16 = 0, MXE_SWIGLU = 1, MXE_SWIGLU_BWD = 2 };
 hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
                             hipStream_t s);
 hipError_t launch_mx_kseg(const MxGemmDesc &d, int num_cus, hipStream_t s);
+// Partial ds values per row that the SwiGLU-backward epilogue writes.
+size_t mx_ds_parts(int64_t N);
 
 }  // namespace moe

@@ -17,14 +17,17 @@
 //           [kseg[g], kseg[g+1]) of transposed operands (weight gradients:
 //           K runs over an expert's rows, zero-padded to 512).
 // KSPLIT (data gradient through gate and up): B rows are [B0 row | B1 row]
-// along K, the switch at K/2.
+// along K, the switch at `ksplit`.
 //
-// Pipeline as in the bf16 grouped GEMM: 128 x 128 tiles (4 wavefronts of
-// 64 x 64), K advances 128 values per stage, 4-stage LDS ring filled by
-// direct global->LDS loads from inline assembly (explicit vmcnt waits).  A
-// stage holds A and B code rows (128 B each, chunks swizzled against bank
-// conflicts) plus, per row, the 16-byte scale chunk covering the 512 K
-// values around the stage (so K must be a multiple of 512).
+// Pipeline: BM x BN tiles on 4 wavefronts (each a (BM/WM) x (BN/WN) block of
+// 32x32 MFMA tiles; 128 x 128 per wavefront at the 256 x 256 shape, which
+// halves the LDS bytes read per FLOP against 64 x 64), K advancing 128
+// values per stage through a STAGES-deep LDS ring filled by direct
+// global->LDS loads from inline assembly (explicit vmcnt waits).  A stage
+// holds the A and B code rows (128 B each, 16-byte chunks XOR-swizzled
+// against bank conflicts) and, per row, the 4 scale bytes of the stage's
+// four 32-value blocks (one dword load per row, packed row after row).  The
+// stage's loads are spread over its MFMAs.  K must be a multiple of 128.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -45,7 +48,7 @@ struct MxArgs {
   uint16_t *gu;                 // SWIGLU: g,u out; SWIGLU_BWD: g,u in
   int64_t ldgu;                 // u at column offset N of gu
   uint16_t *dgu;                // SWIGLU_BWD: dg, du out [rows, ldgu]
-  float *ds_part;               // SWIGLU_BWD: [rows, NT * 2]
+  float *ds_part;               // SWIGLU_BWD: [rows, NT * WN]
   int ksplit;                   // KSPLIT: K of the B0 part (0 = none)
 };
 
@@ -54,8 +57,14 @@ enum MxEpi { MX_EPI_BF16 = 0, MX_EPI_SWIGLU = 1, MX_EPI_SWIGLU_BWD = 2 };
 
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
+// Direct global -> LDS loads: lane l's 16 (or 4) bytes go to LDS byte
+// address lds_base + 16 * l (or 4 * l); lds_base is uniform.
 __device__ __forceinline__ void mx_load_lds16(uint32_t lds_base, const void *g) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+               :: "s"(lds_base), "v"(g) : "memory");
+}
+__device__ __forceinline__ void mx_load_lds4(uint32_t lds_base, const void *g) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds_base), "v"(g) : "memory");
 }
 
@@ -97,267 +106,282 @@ __global__ __launch_bounds__(1024) void mx_plan_kernel(
   if (tid == 1023) prefix[G] = part[1023];
 }
 
-template <int MODE, int EPI>
+// Source row of B-tile row j (0 <= j < BN) and whether it comes from B1:
+// SWIGLU interleaves 16 gate rows and 16 up rows per 32, so one tile yields
+// both operands of SwiGLU for BN/2 output columns.
+template <int EPI, int BN>
+__device__ __forceinline__ int mx_brow(int nt, int j, int N, bool &up) {
+  int col;
+  if (EPI == MX_EPI_SWIGLU) {
+    const int w = j & 31;
+    col = nt * (BN / 2) + (j >> 5) * 16 + (w & 15);
+    up = w >= 16;
+  } else {
+    col = nt * BN + j;
+    up = false;
+  }
+  return min(col, N - 1);
+}
+
+// Epilogue of one 32-row block (rows mrow0 .. mrow0+31 of the tile): lane
+// holds column (lane & 31) of each 32x32 block and rows 8*(r/4) +
+// 4*(lane/32) + (r%4) of it.
+template <int MODE, int EPI, int BN, int WN, int NB>
+__device__ __forceinline__ void mx_epilogue_block(
+    const MxArgs &p, const f32x16 (&am)[NB], int mrow0, int lane, int rows,
+    int row0, int nt, int brow0, int wn, int e) {
+  if (EPI == MX_EPI_SWIGLU_BWD) {
+    // per row: partial ds over this wavefront's columns
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = mrow0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const bool row_ok = i < rows;
+      const int64_t grow = row0 + (row_ok ? i : 0);
+      const float s = p.row_scale ? p.row_scale[grow] : 1.f;
+      float part = 0.f;
+#pragma unroll
+      for (int n = 0; n < NB; ++n) {
+        const int col = nt * BN + brow0 + n * 32 + (lane & 31);
+        const bool ok = row_ok && col < p.N;
+        const float da = am[n][r];
+        float g = 0.f, u = 0.f;
+        if (ok) {
+          g = bf16_bits_to_f32(p.gu[grow * p.ldgu + col]);
+          u = bf16_bits_to_f32(p.gu[grow * p.ldgu + p.N + col]);
+        }
+        const float sg = 1.f / (1.f + __expf(-g));
+        const float sl = g * sg;
+        const float dsl = sg * (1.f + g * (1.f - sg));
+        if (ok) {
+          p.dgu[grow * p.ldgu + col] = (uint16_t)f32_to_bf16_bits(da * s * u * dsl);
+          p.dgu[grow * p.ldgu + p.N + col] = (uint16_t)f32_to_bf16_bits(da * s * sl);
+          part += da * sl * u;
+        }
+      }
+      // sum over the 32 columns held by this half-wavefront
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+      if ((lane & 31) == 0 && row_ok)
+        p.ds_part[grow * (p.NT * WN) + nt * WN + wn] = part;
+    }
+  } else {
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = mrow0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const float v = am[n][r];
+        if (EPI == MX_EPI_SWIGLU) {
+          const float other = __shfl_xor(v, 16, 64);
+          if ((lane & 31) < 16 && i < rows) {
+            const int col = nt * (BN / 2) + (brow0 + n * 32) / 2 + (lane & 15);
+            if (col < p.N) {
+              const int64_t grow = row0 + i;
+              const float s = p.row_scale ? p.row_scale[grow] : 1.f;
+              ((uint16_t *)p.C)[grow * p.ldc + col] =
+                  (uint16_t)f32_to_bf16_bits(s * silu_f32(v) * other);
+              if (p.gu) {
+                p.gu[grow * p.ldgu + col] = (uint16_t)f32_to_bf16_bits(v);
+                p.gu[grow * p.ldgu + p.N + col] = (uint16_t)f32_to_bf16_bits(other);
+              }
+            }
+          }
+        } else {
+          const int col = nt * BN + brow0 + n * 32 + (lane & 31);
+          if (i < rows && col < p.N) {
+            const int64_t base = (MODE == MX_KSEG) ? (int64_t)e * p.c_stride : 0;
+            ((uint16_t *)p.C)[base + (int64_t)(row0 + i) * p.ldc + col] =
+                (uint16_t)f32_to_bf16_bits(v);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
-  constexpr int BM = 128, BN = 128, WM = 2, WN = 2, STAGES = 4;
+  constexpr int CPR = 8;                               // 16-byte chunks per row
   constexpr int WTM = BM / WM, WTN = BN / WN, MB = WTM / 32, NB = WTN / 32;
-  constexpr int CODE_CHUNKS = (BM + BN) * 8;
-  constexpr int STAGE_CHUNKS = CODE_CHUNKS + BM + BN;   // + scale chunks
-  constexpr int L = STAGE_CHUNKS / 256;                 // loads per thread
-  static_assert(STAGE_CHUNKS % 256 == 0, "load split");
+  constexpr int CODE_CHUNKS = (BM + BN) * CPR;
+  constexpr int LC = CODE_CHUNKS / 256;                // code loads per thread
+  constexpr int LS = (BM + BN) / 256;                  // scale loads per thread
+  constexpr int L = LC + LS;
+  constexpr int SCALE_OFF = CODE_CHUNKS * 16;          // bytes
+  constexpr int STAGE_BYTES = SCALE_OFF + (BM + BN) * 4;
+  constexpr int NMF = 2 * MB * NB;                     // MFMAs per stage
+  static_assert(WM * WN == 4 && MB >= 1 && MB <= 4 && NB >= 1, "tile");
+  static_assert(CODE_CHUNKS % 256 == 0 && (BM + BN) % 256 == 0, "load split");
   static_assert((STAGES - 2) * L <= 63, "vmcnt range");
-  __shared__ uint4 smem[STAGES * STAGE_CHUNKS];
+  static_assert(STAGE_BYTES % 16 == 0, "stage alignment");
+  __shared__ uint4 smem[STAGES * STAGE_BYTES / 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / WN, wn = wid % WN;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-  const uint32_t wave_off = (uint32_t)(wid * L * 64 * 16);
 
   int total;
   if (MODE == MX_ROWSEG) total = p.tile_prefix[p.G];
   else total = p.G * p.MT * p.NT;
   const int t = xcd_tile(blockIdx.x, total);
   if (t < 0) return;
-  {
-    int e, row0, rows, nt, mt, k0, KT;
-    if (MODE == MX_ROWSEG) {
-      e = upper_bound_minus1(p.tile_prefix, p.G, t);
-      const int r_begin = p.offsets[e], r_end = p.offsets[e + 1];
-      const int local = t - p.tile_prefix[e];
-      const int mtiles = (r_end - r_begin + BM - 1) / BM;
-      banded_mn(local, mtiles, p.NT, 8, mt, nt);
-      row0 = r_begin + mt * BM;
-      rows = min(BM, r_end - row0);
-      k0 = 0;
-      KT = p.K / 128;
-    } else {
-      const int per_g = p.MT * p.NT;
-      e = t / per_g;
-      banded_mn(t - e * per_g, p.MT, p.NT, 8, mt, nt);
-      row0 = mt * BM;
-      rows = min(BM, p.M - row0);
-      k0 = p.kseg[e];
-      KT = (p.kseg[e + 1] - k0) / 128;
-    }
 
-    // sources of this thread's loads: chunk q = (wid*L + i)*64 + lane
-    const char *gsrc[L];
-    const char *gsrc1[L];   // KSPLIT: B rows taken from B1 past the split
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int q = (wid * L + i) * 64 + lane;
-      gsrc1[i] = nullptr;
-      if (q < CODE_CHUNKS) {
-        const int row = q / 8;
-        const int kc = mx_swz(row, q % 8);
-        if (row < BM) {
-          gsrc[i] = (const char *)p.A + (int64_t)(row0 + min(row, rows - 1)) * p.lda + k0 + kc * 16;
-        } else {
-          const int j = row - BM;
-          int col;
-          const uint8_t *base;
-          if (EPI == MX_EPI_SWIGLU) {
-            const int w = j & 31;
-            col = nt * (BN / 2) + (j >> 5) * 16 + (w & 15);
-            base = w < 16 ? p.B0 : p.B1;
-          } else {
-            col = nt * BN + j;
-            base = p.B0;
-          }
-          col = min(col, p.N - 1);
-          const int64_t ro = (int64_t)e * p.b_stride + (int64_t)col * p.ldb + k0 + kc * 16;
-          gsrc[i] = (const char *)base + ro;
-          if (p.ksplit) gsrc1[i] = (const char *)p.B1 + ro - p.ksplit;
-        }
-      } else {
-        const int row = q - CODE_CHUNKS;  // scale chunk of A row or B row
-        if (row < BM) {
-          gsrc[i] = (const char *)p.As + (int64_t)(row0 + min(row, rows - 1)) * p.ldas + k0 / 32;
-        } else {
-          const int j = row - BM;
-          int col;
-          const uint8_t *base;
-          if (EPI == MX_EPI_SWIGLU) {
-            const int w = j & 31;
-            col = nt * (BN / 2) + (j >> 5) * 16 + (w & 15);
-            base = w < 16 ? p.B0s : p.B1s;
-          } else {
-            col = nt * BN + j;
-            base = p.B0s;
-          }
-          col = min(col, p.N - 1);
-          const int64_t ro = (int64_t)e * p.bs_stride + (int64_t)col * p.ldbs + k0 / 32;
-          gsrc[i] = (const char *)base + ro;
-          if (p.ksplit) gsrc1[i] = (const char *)p.B1s + ro - p.ksplit / 32;
-        }
-      }
-    }
-
-    f32x16 acc[MB][NB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int n = 0; n < NB; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
-
-    // Stage kt's load i: codes advance 128 bytes per stage, scale chunks
-    // (16 blocks = 512 K values) every 4 stages.
-#define MX_ISSUE(stage_, kt_)                                                   \
-  {                                                                             \
-    const uint32_t sb = lds0 + (uint32_t)((stage_) * STAGE_CHUNKS * 16) + wave_off; \
-    const int kk_ = (kt_);                                                      \
-    const bool hi = p.ksplit && kk_ * 128 >= p.ksplit;                          \
-    _Pragma("unroll") for (int i = 0; i < L; ++i) {                             \
-      const int q = (wid * L + i) * 64 + lane;                                  \
-      const int64_t off = q < CODE_CHUNKS ? (int64_t)kk_ * 128 : (int64_t)(kk_ >> 2) * 16; \
-      const char *src = (hi && gsrc1[i]) ? gsrc1[i] : gsrc[i];                  \
-      mx_load_lds16(sb + (uint32_t)(i * 64 * 16), src + off);                   \
-    }                                                                           \
+  int e, row0, rows, nt, mt, k0, KT;
+  if (MODE == MX_ROWSEG) {
+    e = upper_bound_minus1(p.tile_prefix, p.G, t);
+    const int r_begin = p.offsets[e], r_end = p.offsets[e + 1];
+    const int local = t - p.tile_prefix[e];
+    const int mtiles = (r_end - r_begin + BM - 1) / BM;
+    banded_mn(local, mtiles, p.NT, 8, mt, nt);
+    row0 = r_begin + mt * BM;
+    rows = min(BM, r_end - row0);
+    k0 = 0;
+    KT = p.K / 128;
+  } else {
+    const int per_g = p.MT * p.NT;
+    e = t / per_g;
+    banded_mn(t - e * per_g, p.MT, p.NT, 8, mt, nt);
+    row0 = mt * BM;
+    rows = min(BM, p.M - row0);
+    k0 = p.kseg[e];
+    KT = (p.kseg[e + 1] - k0) / 128;
   }
 
+  // Sources of this thread's loads.  Code load i (< LC) moves chunks
+  // q = (wid*LC + i)*64 + lane of the stage; scale load j moves the dwords of
+  // rows d = (wid*LS + j)*64 + lane.  Rows < BM are A rows, the rest B rows.
+  // gsrc1: the B1 source of a B row past the K split (KSPLIT), else null.
+  const char *gsrc[L];
+  const char *gsrc1[L];
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-      if (st < KT) MX_ISSUE(st, st);
+  for (int i = 0; i < L; ++i) {
+    const bool code = i < LC;
+    const int q = code ? (wid * LC + i) * 64 + lane : 0;
+    const int row = code ? q / CPR : (wid * LS + (i - LC)) * 64 + lane;
+    gsrc1[i] = nullptr;
+    if (row < BM) {
+      const int64_t r = row0 + min(row, rows - 1);
+      gsrc[i] = code ? (const char *)p.A + r * p.lda + k0 + mx_swz(row, q % CPR) * 16
+                     : (const char *)p.As + r * p.ldas + k0 / 32;
+    } else {
+      bool up;
+      const int col = mx_brow<EPI, BN>(nt, row - BM, p.N, up);
+      const int64_t g = (int64_t)e;
+      if (code) {
+        const int64_t ro = g * p.b_stride + (int64_t)col * p.ldb + k0 + mx_swz(row, q % CPR) * 16;
+        gsrc[i] = (const char *)(up ? p.B1 : p.B0) + ro;
+        if (p.ksplit) gsrc1[i] = (const char *)p.B1 + ro - p.ksplit;
+      } else {
+        const int64_t ro = g * p.bs_stride + (int64_t)col * p.ldbs + k0 / 32;
+        gsrc[i] = (const char *)(up ? p.B1s : p.B0s) + ro;
+        if (p.ksplit) gsrc1[i] = (const char *)p.B1s + ro - p.ksplit / 32;
+      }
+    }
+  }
 
-    const int arow0 = wm * WTM, brow0 = wn * WTN;
-    for (int kt = 0; kt < KT; ++kt) {
-      const int after = min(STAGES - 2, KT - 1 - kt);
-      if (after >= 2) mx_wait_barrier<2 * L>();
-      else if (after == 1) mx_wait_barrier<L>();
-      else mx_wait_barrier<0>();
-      if (kt + STAGES - 1 < KT) MX_ISSUE((kt + STAGES - 1) % STAGES, kt + STAGES - 1);
+  // Issue load i of stage ks into ring buffer b (i is a compile-time index
+  // once unrolled; ks and b are uniform).
+  auto issue = [&](int i, int b, int ks) {
+    const uint32_t sb = lds0 + (uint32_t)(b * STAGE_BYTES);
+    const bool hi = p.ksplit && ks * 128 >= p.ksplit;
+    const char *src = (hi && gsrc1[i]) ? gsrc1[i] : gsrc[i];
+    if (i < LC)
+      mx_load_lds16(sb + (uint32_t)((wid * LC + i) * 1024), src + (int64_t)ks * 128);
+    else
+      mx_load_lds4(sb + (uint32_t)(SCALE_OFF + (wid * LS + (i - LC)) * 256),
+                   src + (int64_t)ks * 4);
+  };
 
-      const uint4 *S = smem + (kt % STAGES) * STAGE_CHUNKS;
-      const uint4 *As = S, *Bs = S + BM * 8;
-      const uint8_t *Ssc = (const uint8_t *)(S + CODE_CHUNKS);  // scale chunks
-      const int h = lane >> 5;
-      // scale dwords (4 blocks of this stage) for this lane's rows
-      uint32_t sa[MB], sbv[NB];
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
+
+  // Prologue: stages 0 .. STAGES-2 (clamped to the last stage).
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) issue(i, st, min(st, KT - 1));
+  }
+
+  const int arow0 = wm * WTM, brow0 = wn * WTN;
+  const int h = lane >> 5;
+  for (int kt = 0; kt < KT; ++kt) {
+    // Stage kt has landed once (STAGES-2)*L later loads of this wavefront
+    // are in flight; the barrier also frees the buffer refilled below.
+    mx_wait_barrier<(STAGES - 2) * L>();
+    const int ks = min(kt + STAGES - 1, KT - 1);
+    const int bnext = (kt + STAGES - 1) % STAGES;
+
+    const char *S = (const char *)smem + (kt % STAGES) * STAGE_BYTES;
+    const uint4 *As = (const uint4 *)S, *Bs = As + BM * CPR;
+    const uint32_t *Ssc = (const uint32_t *)(S + SCALE_OFF);
+    uint32_t sa[MB], sbv[NB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) sa[m] = Ssc[arow0 + m * 32 + (lane & 31)];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) sbv[n] = Ssc[BM + brow0 + n * 32 + (lane & 31)];
+
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      // Operand layout of the 32x32x64 f8 instruction: lane half h holds
+      // K [16h, 16h+16) in its first four registers and [32+16h, 48+16h)
+      // in the last four; block b (K [32b, 32b+32)) takes its scale from
+      // lane half b.  In 16-byte chunks of the 64-value step: h and 2 + h.
+      const int c0 = 4 * kk + h, c1 = 4 * kk + 2 + h;
+      i32x8_t af[MB], bfr[NB];
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         const int row = arow0 + m * 32 + (lane & 31);
-        sa[m] = *(const uint32_t *)(Ssc + row * 16 + (kt & 3) * 4);
+        const uint4 v0 = As[row * CPR + mx_swz(row, c0)];
+        const uint4 v1 = As[row * CPR + mx_swz(row, c1)];
+        af[m] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                        (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
       }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const int row = BM + brow0 + n * 32 + (lane & 31);
-        sbv[n] = *(const uint32_t *)(Ssc + row * 16 + (kt & 3) * 4);
+        const int row = brow0 + n * 32 + (lane & 31);
+        const uint4 v0 = Bs[row * CPR + mx_swz(row, c0)];
+        const uint4 v1 = Bs[row * CPR + mx_swz(row, c1)];
+        bfr[n] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                         (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
       }
+      const int sh = 8 * (2 * kk + h);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // Operand layout of the 32x32x64 f8 instruction: lane half h holds
-        // K [16h, 16h+16) in its first four registers and [32+16h, 48+16h)
-        // in the last four; block b (K [32b, 32b+32)) takes its scale from
-        // lane half b.  In 16-byte chunks of the 64-value step: h and 2 + h.
-        const int c0 = 4 * kk + h, c1 = 4 * kk + 2 + h;
-        i32x8_t af[MB], bfr[NB];
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-          const int row = arow0 + m * 32 + (lane & 31);
-          const uint4 v0 = As[row * 8 + mx_swz(row, c0)];
-          const uint4 v1 = As[row * 8 + mx_swz(row, c1)];
-          af[m] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                          (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-        }
+      for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int n = 0; n < NB; ++n) {
-          const int row = brow0 + n * 32 + (lane & 31);
-          const uint4 v0 = Bs[row * 8 + mx_swz(row, c0)];
-          const uint4 v1 = Bs[row * 8 + mx_swz(row, c1)];
-          bfr[n] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                           (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-        }
-        const int sh = 8 * (2 * kk + h);
+          acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af[m], bfr[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> sh) & 0xffu),
+              0, (int)((sbv[n] >> sh) & 0xffu));
+          const int f = (kk * MB + m) * NB + n;
 #pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-          for (int n = 0; n < NB; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                af[m], bfr[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> sh) & 0xffu),
-                0, (int)((sbv[n] >> sh) & 0xffu));
-      }
-    }
-#undef MX_ISSUE
-    mx_wait_barrier<0>();
-
-    // Epilogue: lane holds column (lane & 31) of each 32x32 block and rows
-    // 8*(r/4) + 4*(lane/32) + (r%4).
-    if (EPI == MX_EPI_SWIGLU_BWD) {
-      // per row: partial ds over this wavefront's columns
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = arow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const bool row_ok = i < rows;
-          const int64_t grow = row0 + (row_ok ? i : 0);
-          const float s = p.row_scale ? p.row_scale[grow] : 1.f;
-          float part = 0.f;
-#pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            const int col = nt * BN + brow0 + n * 32 + (lane & 31);
-            const bool ok = row_ok && col < p.N;
-            const float da = acc[m][n][r];
-            float g = 0.f, u = 0.f;
-            if (ok) {
-              g = bf16_bits_to_f32(p.gu[grow * p.ldgu + col]);
-              u = bf16_bits_to_f32(p.gu[grow * p.ldgu + p.N + col]);
-            }
-            const float sg = 1.f / (1.f + __expf(-g));
-            const float sl = g * sg;
-            const float dsl = sg * (1.f + g * (1.f - sg));
-            if (ok) {
-              p.dgu[grow * p.ldgu + col] = (uint16_t)f32_to_bf16_bits(da * s * u * dsl);
-              p.dgu[grow * p.ldgu + p.N + col] = (uint16_t)f32_to_bf16_bits(da * s * sl);
-              part += da * sl * u;
-            }
-          }
-          // sum over the 32 columns held by this half-wavefront
-#pragma unroll
-          for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-          if ((lane & 31) == 0 && row_ok)
-            p.ds_part[grow * (p.NT * WN) + nt * WN + wn] = part;
-        }
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-#pragma unroll
-        for (int n = 0; n < NB; ++n) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = arow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const float v = acc[m][n][r];
-            if (EPI == MX_EPI_SWIGLU) {
-              const float other = __shfl_xor(v, 16, 64);
-              if ((lane & 31) < 16 && i < rows) {
-                const int col = nt * (BN / 2) + (brow0 + n * 32) / 2 + (lane & 15);
-                if (col < p.N) {
-                  const int64_t grow = row0 + i;
-                  const float s = p.row_scale ? p.row_scale[grow] : 1.f;
-                  ((uint16_t *)p.C)[grow * p.ldc + col] =
-                      (uint16_t)f32_to_bf16_bits(s * silu_f32(v) * other);
-                  if (p.gu) {
-                    p.gu[grow * p.ldgu + col] = (uint16_t)f32_to_bf16_bits(v);
-                    p.gu[grow * p.ldgu + p.N + col] = (uint16_t)f32_to_bf16_bits(other);
-                  }
-                }
-              }
-            } else {
-              const int col = nt * BN + brow0 + n * 32 + (lane & 31);
-              if (i < rows && col < p.N) {
-                const int64_t base = (MODE == MX_KSEG) ? (int64_t)e * p.c_stride : 0;
-                ((uint16_t *)p.C)[base + (int64_t)(row0 + i) * p.ldc + col] =
-                    (uint16_t)f32_to_bf16_bits(v);
-              }
-            }
+          for (int i = f * L / NMF; i < (f + 1) * L / NMF; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue(i, bnext, ks);
+            __builtin_amdgcn_sched_barrier(0);
           }
         }
-      }
     }
   }
+  mx_wait_barrier<0>();
+
+  // Epilogue, one 32-row block at a time with a constant block index (the
+  // accumulators stay in registers).
+#define MX_EPI_BLOCK(m)                                                      \
+  if constexpr (MB > (m))                                                    \
+    mx_epilogue_block<MODE, EPI, BN, WN, NB>(p, acc[m], arow0 + (m) * 32,   \
+                                             lane, rows, row0, nt, brow0,    \
+                                             wn, e);
+  MX_EPI_BLOCK(0)
+  MX_EPI_BLOCK(1)
+  MX_EPI_BLOCK(2)
+  MX_EPI_BLOCK(3)
+#undef MX_EPI_BLOCK
 }
 
 // ds[r] = sum_j ds_part[r, j] in ascending j (fixed order: deterministic).
@@ -375,15 +399,26 @@ __global__ void mx_ds_reduce_kernel(const float *__restrict__ part, int nparts,
 
 namespace {
 
+// Tile shape: 256 x 256 on 2 x 2 wavefronts of 128 x 128, 2 stages of
+// (256 + 256) x 128 code bytes + scales (132 KB of LDS).
+#ifndef MOE_MX_CFG
+#define MOE_MX_CFG 256, 256, 2, 2, 2
+#endif
+constexpr int kMxCfg[5] = {MOE_MX_CFG};
+constexpr int kMxBM = kMxCfg[0], kMxBN = kMxCfg[1], kMxWN = kMxCfg[3];
+
 template <int MODE, int EPI>
-hipError_t mx_launch(const MxArgs &p, int num_cus, int64_t max_tiles,
-                     hipStream_t s) {
-  (void)num_cus;
-  mx_gemm_kernel<MODE, EPI><<<(unsigned)tile_grid(max_tiles), 256, 0, s>>>(p);
+hipError_t mx_launch(const MxArgs &p, int64_t max_tiles, hipStream_t s) {
+  mx_gemm_kernel<MODE, EPI, MOE_MX_CFG>
+      <<<(unsigned)tile_grid(max_tiles), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
 }  // namespace
+
+size_t mx_ds_parts(int64_t N) {
+  return (size_t)((N + kMxBN - 1) / kMxBN) * kMxWN;
+}
 
 hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
                             hipStream_t s) {
@@ -395,33 +430,33 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
   p.C = d.C; p.ldc = d.ldc; p.row_scale = d.row_scale;
   p.gu = d.gu; p.ldgu = d.ldgu; p.dgu = d.dgu; p.ds_part = d.ds_part;
   p.ksplit = d.ksplit;
-  const int cols = epi == MX_EPI_SWIGLU ? 64 : 128;
+  const int cols = epi == MX_EPI_SWIGLU ? kMxBN / 2 : kMxBN;
   p.NT = (d.N + cols - 1) / cols;
   p.tile_prefix = d.tile_ws;
-  mx_plan_kernel<<<1, 1024, 0, s>>>(d.offsets, d.G, 128, p.NT, d.tile_ws);
+  mx_plan_kernel<<<1, 1024, 0, s>>>(d.offsets, d.G, kMxBM, p.NT, d.tile_ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int64_t max_tiles = ((d.R_cap + 127) / 128 + d.G) * (int64_t)p.NT;
-  if (epi == MX_EPI_SWIGLU) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU>(p, num_cus, max_tiles, s);
-  else if (epi == MX_EPI_SWIGLU_BWD) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU_BWD>(p, num_cus, max_tiles, s);
-  else err = mx_launch<MX_ROWSEG, MX_EPI_BF16>(p, num_cus, max_tiles, s);
+  const int64_t max_tiles = ((d.R_cap + kMxBM - 1) / kMxBM + d.G) * (int64_t)p.NT;
+  if (epi == MX_EPI_SWIGLU) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU>(p, max_tiles, s);
+  else if (epi == MX_EPI_SWIGLU_BWD) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU_BWD>(p, max_tiles, s);
+  else err = mx_launch<MX_ROWSEG, MX_EPI_BF16>(p, max_tiles, s);
   if (err != hipSuccess || epi != MX_EPI_SWIGLU_BWD) return err;
   mx_ds_reduce_kernel<<<(unsigned)num_cus, 256, 0, s>>>(
-      d.ds_part, p.NT * 2, d.offsets + d.G, d.ds);
+      d.ds_part, p.NT * kMxWN, d.offsets + d.G, d.ds);
   return hipGetLastError();
 }
 
 hipError_t launch_mx_kseg(const MxGemmDesc &d, int num_cus, hipStream_t s) {
+  (void)num_cus;
   MxArgs p{};
   p.A = d.A; p.As = d.As; p.lda = d.lda; p.ldas = d.ldas;
   p.B0 = d.B0; p.B0s = d.B0s; p.ldb = d.ldb; p.ldbs = d.ldbs;
   p.b_stride = 0; p.bs_stride = 0;
   p.kseg = d.kseg; p.G = d.G; p.M = d.M; p.N = d.N;
-  p.MT = (d.M + 127) / 128;
-  p.NT = (d.N + 127) / 128;
+  p.MT = (d.M + kMxBM - 1) / kMxBM;
+  p.NT = (d.N + kMxBN - 1) / kMxBN;
   p.C = d.C; p.ldc = d.ldc; p.c_stride = d.c_stride;
-  return mx_launch<MX_KSEG, MX_EPI_BF16>(p, num_cus,
-                                         (int64_t)d.G * p.MT * p.NT, s);
+  return mx_launch<MX_KSEG, MX_EPI_BF16>(p, (int64_t)d.G * p.MT * p.NT, s);
 }
 
 }  // namespace moe
