@@ -35,6 +35,9 @@ STREAM_W_GATE = 10
 STREAM_W_UP = 11
 STREAM_W_DOWN = 12
 STREAM_DY = 20
+STREAM_A = 21
+STREAM_GU = 22
+STREAM_DGU = 23
 
 
 def build(force: bool = True) -> str:
@@ -239,3 +242,19 @@ def make_dy(w: Workload, rows: int) -> np.ndarray:
     """Upstream gradient of the expert outputs, [rows, H] bf16 N(0,1)."""
     return normal_bf16(w.seed, STREAM_DY, 0, rows * w.H, 0.0,
                        1.0).reshape(rows, w.H)
+
+
+def make_handoffs(w: Workload, rows: int) -> dict:
+    """Stand-alone bf16 tensors of the shapes the MXFP8 MLP step hands from
+    one operation to the next, for testing each GEMM stage on its own:
+    a [rows, I] ~ N(0, 0.5), gu = [g | u] [rows, 2I] ~ N(0, 1.25) (the spread
+    of x . W for x ~ N(0,1), W ~ N(0, 0.02), H = 4096), dgu = [dg | du]
+    [rows, 2I] ~ N(0, 0.5)."""
+    I = w.I
+    return {
+        "a": normal_bf16(w.seed, STREAM_A, 0, rows * I, 0.0, 0.5).reshape(rows, I),
+        "gu": normal_bf16(w.seed, STREAM_GU, 0, rows * 2 * I, 0.0,
+                          1.25).reshape(rows, 2 * I),
+        "dgu": normal_bf16(w.seed, STREAM_DGU, 0, rows * 2 * I, 0.0,
+                           0.5).reshape(rows, 2 * I),
+    }
