@@ -18,19 +18,24 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {
 }
 
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
+// fp32 -> bf16 bits, round to nearest even (the hardware conversion,
+// v_cvt_pk_bf16_f32, in the default round-to-nearest-even mode).
 __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+// 1 / (1 + e^-z) with the hardware reciprocal (1 ulp).
+__device__ __forceinline__ float sigmoid_f32(float z) {
+  return __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 // SiLU(z) = z * sigmoid(z)
 __device__ __forceinline__ float silu_f32(float z) {
-  return z / (1.0f + __expf(-z));
+  return z * sigmoid_f32(z);
 }
 
 // Index of the last entry of the non-decreasing array p[0..n] that is <= v,

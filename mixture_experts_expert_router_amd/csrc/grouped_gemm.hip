@@ -340,6 +340,32 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
 
     // Epilogue.  Lane holds column (lane & 31) of each 32x32 block and rows
     // 8*(r/4) + 4*(lane/32) + (r%4), r < 16.
+    if (EPI == EPI_SWIGLU) {
+      // Lanes 0..15 of each half hold gate columns, 16..31 the matching up
+      // columns; after a lane swap both have the pair, and lanes 0..15
+      // finish rows r = 0..7, lanes 16..31 rows r = 8..15.
+      const bool lo = (lane & 31) < 16;
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m >= mvalid) continue;
+#pragma unroll
+        for (int rp = 0; rp < 8; ++rp) {
+          const int r = lo ? rp : rp + 8;
+          const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const float s = (i < rows && p.row_scale) ? p.row_scale[row0 + i] : 1.f;
+#pragma unroll
+          for (int n = 0; n < NB; ++n) {
+            const float vlo = acc[m][n][rp], vhi = acc[m][n][rp + 8];
+            const float olo = __shfl_xor(vlo, 16, 64), ohi = __shfl_xor(vhi, 16, 64);
+            const float g = lo ? vlo : ohi, u = lo ? olo : vhi;
+            const int col = nt * (BN / 2) + (wn * WTN + n * 32) / 2 + (lane & 15);
+            if (i < rows && col < p.N)
+              ((uint16_t *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
+                  (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
+          }
+        }
+      }
+    } else {
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       if (m >= mvalid) continue;
@@ -349,18 +375,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
         for (int r = 0; r < 16; ++r) {
           const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const float v = acc[m][n][r];
-          if (EPI == EPI_SWIGLU) {
-            const float other = __shfl_xor(v, 16, 64);
-            if ((lane & 31) < 16 && i < rows) {
-              const int col = nt * (BN / 2) + (wn * WTN + n * 32) / 2 + (lane & 15);
-              if (col < p.N) {
-                const float s = p.row_scale ? p.row_scale[row0 + i] : 1.f;
-                const float a = s * silu_f32(v) * other;
-                ((uint16_t *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
-                    (uint16_t)f32_to_bf16_bits(a);
-              }
-            }
-          } else {
+          {
             const int col = nt * BN + wn * WTN + n * 32 + (lane & 31);
             if (i < rows && col < p.N) {
               if (EPI == EPI_BF16)
@@ -373,6 +388,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
           }
         }
       }
+    }
     }
   }
 }

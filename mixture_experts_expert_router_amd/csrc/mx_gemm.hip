@@ -149,7 +149,7 @@ __device__ __forceinline__ void mx_epilogue_block(
           g = bf16_bits_to_f32(p.gu[grow * p.ldgu + col]);
           u = bf16_bits_to_f32(p.gu[grow * p.ldgu + p.N + col]);
         }
-        const float sg = 1.f / (1.f + __expf(-g));
+        const float sg = sigmoid_f32(g);
         const float sl = g * sg;
         const float dsl = sg * (1.f + g * (1.f - sg));
         if (ok) {
@@ -196,6 +196,118 @@ __device__ __forceinline__ void mx_epilogue_block(
         }
       }
     }
+  }
+}
+
+// ---- LDS-staged epilogues ------------------------------------------------
+// After the K loop the LDS ring is free.  Each wavefront stages its part of
+// the output in a region of its own and writes it back to HBM as 16-byte
+// row pieces (8 lanes per 128-byte row), instead of 2-byte stores per lane.
+// Region rows are 128 bytes (64 bf16) for SwiGLU outputs, 256 bytes (128
+// bf16) for the SwiGLU-backward g, u, dg, du tiles.
+
+// SwiGLU forward, one 32-row block.  Lanes 0..15 of each half-wavefront
+// hold gate column (lane & 15), lanes 16..31 the matching up column; after
+// a lane swap both have the (gate, up) pair.  Lanes 0..15 then finish rows
+// r = 0..7 of their 16 and lanes 16..31 rows r = 8..15, so every lane
+// computes distinct outputs.
+template <int NB>
+__device__ __forceinline__ void mx_swiglu_stage(
+    const MxArgs &p, const f32x16 (&am)[NB], int mloc, int lane, int arow0,
+    int rows, int row0, uint16_t *l0, uint16_t *l1, int phase) {
+  const bool lo = (lane & 31) < 16;
+#pragma unroll
+  for (int rp = 0; rp < 8; ++rp) {
+    const int r = lo ? rp : rp + 8;
+    const int row = mloc + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    const bool ok = arow0 + row < rows;
+    const float s = (phase == 0 && ok && p.row_scale) ? p.row_scale[row0 + arow0 + row] : 1.f;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const float vlo = am[n][rp], vhi = am[n][rp + 8];
+      const float olo = __shfl_xor(vlo, 16, 64), ohi = __shfl_xor(vhi, 16, 64);
+      const float g = lo ? vlo : ohi, u = lo ? olo : vhi;
+      const int col = n * 16 + (lane & 15);
+      if (phase == 0) {
+        l0[row * 64 + col] = (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
+        l1[row * 64 + col] = (uint16_t)f32_to_bf16_bits(g);
+      } else {
+        l0[row * 64 + col] = (uint16_t)f32_to_bf16_bits(u);
+      }
+    }
+  }
+}
+
+// Write rows [0, nrows) of a staged [nrows][W] bf16 region to
+// dst[(grow0 + r) * ld + col0 + c] for tile rows arow0 + r < rows and
+// columns col0 + c < N (N % 8 == 0).
+template <int W, int NROWS>
+__device__ __forceinline__ void mx_store_staged(const uint16_t *l, uint16_t *dst,
+                                                int64_t ld, int64_t col0, int N,
+                                                int64_t grow0, int arow0,
+                                                int rows, int lane) {
+  constexpr int LPR = W / 8;                 // lanes per row
+  constexpr int RPI = 64 / LPR;              // rows per instruction
+#pragma unroll
+  for (int it = 0; it < NROWS / RPI; ++it) {
+    const int r = it * RPI + lane / LPR;
+    const int c8 = (lane % LPR) * 8;
+    if (arow0 + r < rows && col0 + c8 < N)
+      *(uint4 *)(dst + (grow0 + r) * ld + col0 + c8) = *(const uint4 *)(l + r * W + c8);
+  }
+}
+
+// Load rows [0, NROWS) of src (bf16, row pitch ld) into a [NROWS][W] region;
+// rows past the tile's valid rows, or columns past N, read as zero.
+template <int W, int NROWS>
+__device__ __forceinline__ void mx_load_staged(uint16_t *l, const uint16_t *src,
+                                               int64_t ld, int64_t col0, int N,
+                                               int64_t grow0, int arow0,
+                                               int rows, int lane) {
+  constexpr int LPR = W / 8;
+  constexpr int RPI = 64 / LPR;
+#pragma unroll
+  for (int it = 0; it < NROWS / RPI; ++it) {
+    const int r = it * RPI + lane / LPR;
+    const int c8 = (lane % LPR) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (arow0 + r < rows && col0 + c8 < N)
+      v = *(const uint4 *)(src + (grow0 + r) * ld + col0 + c8);
+    *(uint4 *)(l + r * W + c8) = v;
+  }
+}
+
+// SwiGLU backward of one 32-row block against the staged g, u of its rows
+// (region rows `mloc` relative): dg, du replace g, u in place; the partial
+// ds of each row (over this wavefront's 128 columns) goes to ds_part.
+template <int BN, int WN, int NB>
+__device__ __forceinline__ void mx_swiglu_bwd_stage(
+    const MxArgs &p, const f32x16 (&am)[NB], int mloc, int mrow, int lane,
+    int arow0, int rows, int row0, int nt, int wn, uint16_t *lg, uint16_t *lu) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    const int row = mloc + rr;                 // region row
+    const bool ok = arow0 + mrow + rr < rows;  // tile row valid
+    const int64_t grow = row0 + arow0 + mrow + rr;
+    const float s = (ok && p.row_scale) ? p.row_scale[grow] : 1.f;
+    float part = 0.f;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      const int col = n * 32 + (lane & 31);
+      const float da = am[n][r];
+      const float g = bf16_bits_to_f32(lg[row * 128 + col]);
+      const float u = bf16_bits_to_f32(lu[row * 128 + col]);
+      const float sg = sigmoid_f32(g);
+      const float sl = g * sg;
+      const float dsl = sg * (1.f + g * (1.f - sg));
+      lg[row * 128 + col] = (uint16_t)f32_to_bf16_bits(da * s * u * dsl);
+      lu[row * 128 + col] = (uint16_t)f32_to_bf16_bits(da * s * sl);
+      part += da * sl * u;
+    }
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    if ((lane & 31) == 0 && ok) p.ds_part[grow * (p.NT * WN) + nt * WN + wn] = part;
   }
 }
 
@@ -370,18 +482,66 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   }
   mx_wait_barrier<0>();
 
-  // Epilogue, one 32-row block at a time with a constant block index (the
+  // Epilogues, one 32-row block at a time with constant block indices (the
   // accumulators stay in registers).
+  uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * WTN);   // per-wavefront region
+  if constexpr (EPI == MX_EPI_SWIGLU) {
+    static_assert(WTM == 128 && WTN == 128, "SwiGLU staging expects 128x128 wavefront tiles");
+    // region: two [128][64] arrays (a | g, then u)
+    uint16_t *l0 = lw, *l1 = lw + 128 * 64;
+    const int64_t col0 = (int64_t)nt * (BN / 2) + brow0 / 2;
+    const int64_t grow0 = row0 + arow0;
+#pragma unroll
+    for (int phase = 0; phase < 2; ++phase) {
+#define MX_SW_BLOCK(m) \
+      if constexpr (MB > (m)) mx_swiglu_stage<NB>(p, acc[m], (m) * 32, lane, arow0, rows, row0, l0, l1, phase);
+      MX_SW_BLOCK(0) MX_SW_BLOCK(1) MX_SW_BLOCK(2) MX_SW_BLOCK(3)
+#undef MX_SW_BLOCK
+      __syncthreads();
+      if (phase == 0) {
+        mx_store_staged<64, 128>(l0, (uint16_t *)p.C, p.ldc, col0, p.N, grow0, arow0, rows, lane);
+        if (p.gu) mx_store_staged<64, 128>(l1, p.gu, p.ldgu, col0, p.N, grow0, arow0, rows, lane);
+      } else if (p.gu) {
+        mx_store_staged<64, 128>(l0, p.gu, p.ldgu, p.N + col0, 2 * p.N, grow0, arow0, rows, lane);
+      }
+      __syncthreads();
+    }
+  } else if constexpr (EPI == MX_EPI_SWIGLU_BWD) {
+    static_assert(WTM == 128 && WTN == 128 && MB == 4, "staging expects 128x128 wavefront tiles");
+    // region: g and u of 64 rows x 128 columns, two halves of the 128 rows
+    uint16_t *lg = lw, *lu = lw + 64 * 128;
+    const int64_t col0 = (int64_t)nt * BN + brow0;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int64_t grow0 = row0 + arow0 + half * 64;
+      const int ar0 = arow0 + half * 64;
+      mx_load_staged<128, 64>(lg, p.gu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      mx_load_staged<128, 64>(lu, p.gu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      __syncthreads();
+      if (half == 0) {
+        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[0], 0, 0, lane, arow0, rows, row0, nt, wn, lg, lu);
+        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[1], 32, 32, lane, arow0, rows, row0, nt, wn, lg, lu);
+      } else {
+        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[2], 0, 64, lane, arow0, rows, row0, nt, wn, lg, lu);
+        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[3], 32, 96, lane, arow0, rows, row0, nt, wn, lg, lu);
+      }
+      __syncthreads();
+      mx_store_staged<128, 64>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      mx_store_staged<128, 64>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      __syncthreads();
+    }
+  } else {
 #define MX_EPI_BLOCK(m)                                                      \
-  if constexpr (MB > (m))                                                    \
-    mx_epilogue_block<MODE, EPI, BN, WN, NB>(p, acc[m], arow0 + (m) * 32,   \
-                                             lane, rows, row0, nt, brow0,    \
-                                             wn, e);
-  MX_EPI_BLOCK(0)
-  MX_EPI_BLOCK(1)
-  MX_EPI_BLOCK(2)
-  MX_EPI_BLOCK(3)
+    if constexpr (MB > (m))                                                  \
+      mx_epilogue_block<MODE, EPI, BN, WN, NB>(p, acc[m], arow0 + (m) * 32, \
+                                               lane, rows, row0, nt, brow0,  \
+                                               wn, e);
+    MX_EPI_BLOCK(0)
+    MX_EPI_BLOCK(1)
+    MX_EPI_BLOCK(2)
+    MX_EPI_BLOCK(3)
 #undef MX_EPI_BLOCK
+  }
 }
 
 // ds[r] = sum_j ds_part[r, j] in ascending j (fixed order: deterministic).
