@@ -35,8 +35,8 @@
 //     fragment reads) while every 8 lanes still read one contiguous row piece.
 //   * 32-row sub-tiles past the end of an expert's segment are skipped
 //     (uniform per wavefront).
-//   * Epilogues: SWIGLU (B rows interleaved as 16 gate + 16 up per 32-row
-//     block, one lane swap pairs g and u of the same output; writes
+//   * Epilogues: SWIGLU (B rows alternate 32 gate and the 32 matching up
+//     rows, so each lane holds g and u of the same outputs; writes
 //     a = s * SiLU(g) * u in bf16), BF16 (plain store) and F32_BIAS (router
 //     logits + bias).
 #include "common.hpp"
@@ -283,9 +283,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
         const uint16_t *base;
         int col;
         if (EPI == EPI_SWIGLU) {
-          const int w = j & 31;
-          col = nt * (BN / 2) + (j >> 5) * 16 + (w & 15);
-          base = w < 16 ? p.B0 : p.B1;
+          const int w = j & 63;
+          col = nt * (BN / 2) + (j >> 6) * 32 + (w & 31);
+          base = w < 32 ? p.B0 : p.B1;
         } else {
           col = nt * BN + j;
           base = p.B0;
@@ -341,24 +341,19 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     // Epilogue.  Lane holds column (lane & 31) of each 32x32 block and rows
     // 8*(r/4) + 4*(lane/32) + (r%4), r < 16.
     if (EPI == EPI_SWIGLU) {
-      // Lanes 0..15 of each half hold gate columns, 16..31 the matching up
-      // columns; after a lane swap both have the pair, and lanes 0..15
-      // finish rows r = 0..7, lanes 16..31 rows r = 8..15.
-      const bool lo = (lane & 31) < 16;
+      // B rows alternate 32 gate rows and the 32 matching up rows, so block
+      // 2q holds g and block 2q+1 holds u of the same outputs in every lane.
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         if (m >= mvalid) continue;
 #pragma unroll
-        for (int rp = 0; rp < 8; ++rp) {
-          const int r = lo ? rp : rp + 8;
+        for (int r = 0; r < 16; ++r) {
           const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const float s = (i < rows && p.row_scale) ? p.row_scale[row0 + i] : 1.f;
 #pragma unroll
-          for (int n = 0; n < NB; ++n) {
-            const float vlo = acc[m][n][rp], vhi = acc[m][n][rp + 8];
-            const float olo = __shfl_xor(vlo, 16, 64), ohi = __shfl_xor(vhi, 16, 64);
-            const float g = lo ? vlo : ohi, u = lo ? olo : vhi;
-            const int col = nt * (BN / 2) + (wn * WTN + n * 32) / 2 + (lane & 15);
+          for (int q = 0; q < NB / 2; ++q) {
+            const float g = acc[m][2 * q][r], u = acc[m][2 * q + 1][r];
+            const int col = nt * (BN / 2) + wn * (WTN / 2) + q * 32 + (lane & 31);
             if (i < rows && col < p.N)
               ((uint16_t *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
                   (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);

@@ -107,15 +107,16 @@ __global__ __launch_bounds__(1024) void mx_plan_kernel(
 }
 
 // Source row of B-tile row j (0 <= j < BN) and whether it comes from B1:
-// SWIGLU interleaves 16 gate rows and 16 up rows per 32, so one tile yields
-// both operands of SwiGLU for BN/2 output columns.
+// SWIGLU alternates 32 gate rows and the 32 matching up rows, so one tile
+// yields both operands of SwiGLU for BN/2 output columns, and MFMA blocks
+// 2q and 2q+1 of a wavefront hold g and u of the same outputs in each lane.
 template <int EPI, int BN>
 __device__ __forceinline__ int mx_brow(int nt, int j, int N, bool &up) {
   int col;
   if (EPI == MX_EPI_SWIGLU) {
-    const int w = j & 31;
-    col = nt * (BN / 2) + (j >> 5) * 16 + (w & 15);
-    up = w >= 16;
+    const int w = j & 63;
+    col = nt * (BN / 2) + (j >> 6) * 32 + (w & 31);
+    up = w >= 32;
   } else {
     col = nt * BN + j;
     up = false;
@@ -123,78 +124,23 @@ __device__ __forceinline__ int mx_brow(int nt, int j, int N, bool &up) {
   return min(col, N - 1);
 }
 
-// Epilogue of one 32-row block (rows mrow0 .. mrow0+31 of the tile): lane
-// holds column (lane & 31) of each 32x32 block and rows 8*(r/4) +
-// 4*(lane/32) + (r%4) of it.
-template <int MODE, int EPI, int BN, int WN, int NB>
+// Plain bf16 epilogue of one 32-row block (rows mrow0 .. mrow0+31 of the
+// tile): lane holds column (lane & 31) of each 32x32 block and rows
+// 8*(r/4) + 4*(lane/32) + (r%4) of it.
+template <int MODE, int BN, int NB>
 __device__ __forceinline__ void mx_epilogue_block(
     const MxArgs &p, const f32x16 (&am)[NB], int mrow0, int lane, int rows,
-    int row0, int nt, int brow0, int wn, int e) {
-  if (EPI == MX_EPI_SWIGLU_BWD) {
-    // per row: partial ds over this wavefront's columns
+    int row0, int nt, int brow0, int e) {
+  const int64_t base = (MODE == MX_KSEG) ? (int64_t)e * p.c_stride : 0;
+#pragma unroll
+  for (int n = 0; n < NB; ++n) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int i = mrow0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const bool row_ok = i < rows;
-      const int64_t grow = row0 + (row_ok ? i : 0);
-      const float s = p.row_scale ? p.row_scale[grow] : 1.f;
-      float part = 0.f;
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int col = nt * BN + brow0 + n * 32 + (lane & 31);
-        const bool ok = row_ok && col < p.N;
-        const float da = am[n][r];
-        float g = 0.f, u = 0.f;
-        if (ok) {
-          g = bf16_bits_to_f32(p.gu[grow * p.ldgu + col]);
-          u = bf16_bits_to_f32(p.gu[grow * p.ldgu + p.N + col]);
-        }
-        const float sg = sigmoid_f32(g);
-        const float sl = g * sg;
-        const float dsl = sg * (1.f + g * (1.f - sg));
-        if (ok) {
-          p.dgu[grow * p.ldgu + col] = (uint16_t)f32_to_bf16_bits(da * s * u * dsl);
-          p.dgu[grow * p.ldgu + p.N + col] = (uint16_t)f32_to_bf16_bits(da * s * sl);
-          part += da * sl * u;
-        }
-      }
-      // sum over the 32 columns held by this half-wavefront
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-      if ((lane & 31) == 0 && row_ok)
-        p.ds_part[grow * (p.NT * WN) + nt * WN + wn] = part;
-    }
-  } else {
-#pragma unroll
-    for (int n = 0; n < NB; ++n) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int i = mrow0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const float v = am[n][r];
-        if (EPI == MX_EPI_SWIGLU) {
-          const float other = __shfl_xor(v, 16, 64);
-          if ((lane & 31) < 16 && i < rows) {
-            const int col = nt * (BN / 2) + (brow0 + n * 32) / 2 + (lane & 15);
-            if (col < p.N) {
-              const int64_t grow = row0 + i;
-              const float s = p.row_scale ? p.row_scale[grow] : 1.f;
-              ((uint16_t *)p.C)[grow * p.ldc + col] =
-                  (uint16_t)f32_to_bf16_bits(s * silu_f32(v) * other);
-              if (p.gu) {
-                p.gu[grow * p.ldgu + col] = (uint16_t)f32_to_bf16_bits(v);
-                p.gu[grow * p.ldgu + p.N + col] = (uint16_t)f32_to_bf16_bits(other);
-              }
-            }
-          }
-        } else {
-          const int col = nt * BN + brow0 + n * 32 + (lane & 31);
-          if (i < rows && col < p.N) {
-            const int64_t base = (MODE == MX_KSEG) ? (int64_t)e * p.c_stride : 0;
-            ((uint16_t *)p.C)[base + (int64_t)(row0 + i) * p.ldc + col] =
-                (uint16_t)f32_to_bf16_bits(v);
-          }
-        }
-      }
+      const int col = nt * BN + brow0 + n * 32 + (lane & 31);
+      if (i < rows && col < p.N)
+        ((uint16_t *)p.C)[base + (int64_t)(row0 + i) * p.ldc + col] =
+            (uint16_t)f32_to_bf16_bits(am[n][r]);
     }
   }
 }
@@ -206,28 +152,21 @@ __device__ __forceinline__ void mx_epilogue_block(
 // Region rows are 128 bytes (64 bf16) for SwiGLU outputs, 256 bytes (128
 // bf16) for the SwiGLU-backward g, u, dg, du tiles.
 
-// SwiGLU forward, one 32-row block.  Lanes 0..15 of each half-wavefront
-// hold gate column (lane & 15), lanes 16..31 the matching up column; after
-// a lane swap both have the (gate, up) pair.  Lanes 0..15 then finish rows
-// r = 0..7 of their 16 and lanes 16..31 rows r = 8..15, so every lane
-// computes distinct outputs.
+// SwiGLU forward, one 32-row block: block 2q holds g and block 2q+1 the
+// matching u in every lane.
 template <int NB>
 __device__ __forceinline__ void mx_swiglu_stage(
     const MxArgs &p, const f32x16 (&am)[NB], int mloc, int lane, int arow0,
     int rows, int row0, uint16_t *l0, uint16_t *l1, int phase) {
-  const bool lo = (lane & 31) < 16;
 #pragma unroll
-  for (int rp = 0; rp < 8; ++rp) {
-    const int r = lo ? rp : rp + 8;
+  for (int r = 0; r < 16; ++r) {
     const int row = mloc + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     const bool ok = arow0 + row < rows;
     const float s = (phase == 0 && ok && p.row_scale) ? p.row_scale[row0 + arow0 + row] : 1.f;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const float vlo = am[n][rp], vhi = am[n][rp + 8];
-      const float olo = __shfl_xor(vlo, 16, 64), ohi = __shfl_xor(vhi, 16, 64);
-      const float g = lo ? vlo : ohi, u = lo ? olo : vhi;
-      const int col = n * 16 + (lane & 15);
+    for (int q = 0; q < NB / 2; ++q) {
+      const float g = am[2 * q][r], u = am[2 * q + 1][r];
+      const int col = q * 32 + (lane & 31);
       if (phase == 0) {
         l0[row * 64 + col] = (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
         l1[row * 64 + col] = (uint16_t)f32_to_bf16_bits(g);
@@ -533,9 +472,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   } else {
 #define MX_EPI_BLOCK(m)                                                      \
     if constexpr (MB > (m))                                                  \
-      mx_epilogue_block<MODE, EPI, BN, WN, NB>(p, acc[m], arow0 + (m) * 32, \
-                                               lane, rows, row0, nt, brow0,  \
-                                               wn, e);
+      mx_epilogue_block<MODE, BN, NB>(p, acc[m], arow0 + (m) * 32, lane,    \
+                                      rows, row0, nt, brow0, e);
     MX_EPI_BLOCK(0)
     MX_EPI_BLOCK(1)
     MX_EPI_BLOCK(2)
