@@ -21,13 +21,16 @@
 //
 // Pipeline: BM x BN tiles on 4 wavefronts (each a (BM/WM) x (BN/WN) block of
 // 32x32 MFMA tiles; 128 x 128 per wavefront at the 256 x 256 shape, which
-// halves the LDS bytes read per FLOP against 64 x 64), K advancing 128
+// halves the LDS bytes read per FLOP against 64 x 64), K advancing BKB
 // values per stage through a STAGES-deep LDS ring filled by direct
 // global->LDS loads from inline assembly (explicit vmcnt waits).  A stage
-// holds the A and B code rows (128 B each, 16-byte chunks XOR-swizzled
-// against bank conflicts) and, per row, the 4 scale bytes of the stage's
-// four 32-value blocks (one dword load per row, packed row after row).  The
-// stage's loads are spread over its MFMAs.  K must be a multiple of 128.
+// holds the A and B code rows (BKB bytes each, 16-byte chunks XOR-swizzled
+// against bank conflicts) and, per row, the scale dword of the 128 values
+// the stage lies in (one dword load per row, packed row after row).  The
+// loads run STAGES-1 stages ahead, spread over the MFMAs of the stage being
+// computed.  Two 128-value stages measured faster than four 64-value ones
+// (fewer barriers per K, twice the MFMAs per stage).  K must be a multiple
+// of 128.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -74,9 +77,13 @@ __device__ __forceinline__ void mx_wait_barrier() {
                :: "i"(N) : "memory");
 }
 
-// 128-byte rows, 16 consecutive rows at one logical chunk hit 16 bank groups.
+// Physical 16-byte chunk of logical chunk c of an LDS code row with CPR
+// chunks: 16 consecutive rows at one logical chunk hit 16 bank groups
+// (128-byte rows: rows of equal parity get distinct chunks; 64-byte rows:
+// rows equal mod 4 do).
+template <int CPR>
 __device__ __forceinline__ int mx_swz(int row, int c) {
-  return c ^ ((row >> 1) & 7);
+  return CPR == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
 }
 
 // tile_prefix[e+1] = tile_prefix[e] + ceil(rows_e / BM) * NT.  One block.
@@ -124,33 +131,20 @@ __device__ __forceinline__ int mx_brow(int nt, int j, int N, bool &up) {
   return min(col, N - 1);
 }
 
-// Plain bf16 epilogue of one 32-row block (rows mrow0 .. mrow0+31 of the
-// tile): lane holds column (lane & 31) of each 32x32 block and rows
-// 8*(r/4) + 4*(lane/32) + (r%4) of it.
-template <int MODE, int BN, int NB>
-__device__ __forceinline__ void mx_epilogue_block(
-    const MxArgs &p, const f32x16 (&am)[NB], int mrow0, int lane, int rows,
-    int row0, int nt, int brow0, int e) {
-  const int64_t base = (MODE == MX_KSEG) ? (int64_t)e * p.c_stride : 0;
-#pragma unroll
-  for (int n = 0; n < NB; ++n) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int i = mrow0 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      const int col = nt * BN + brow0 + n * 32 + (lane & 31);
-      if (i < rows && col < p.N)
-        ((uint16_t *)p.C)[base + (int64_t)(row0 + i) * p.ldc + col] =
-            (uint16_t)f32_to_bf16_bits(am[n][r]);
-    }
-  }
-}
-
 // ---- LDS-staged epilogues ------------------------------------------------
 // After the K loop the LDS ring is free.  Each wavefront stages its part of
 // the output in a region of its own and writes it back to HBM as 16-byte
 // row pieces (8 lanes per 128-byte row), instead of 2-byte stores per lane.
 // Region rows are 128 bytes (64 bf16) for SwiGLU outputs, 256 bytes (128
 // bf16) for the SwiGLU-backward g, u, dg, du tiles.
+
+// Staged regions swizzle columns by bit 2 of the row: the two halves of a
+// wavefront write rows i and i + 4 of one 32x32 block at once, which would
+// otherwise fall on the same banks.  The XOR moves whole 8-column chunks,
+// so 16-byte row pieces stay contiguous.
+__device__ __forceinline__ int st_col(int row, int col) {
+  return col ^ (((row >> 2) & 1) << 5);
+}
 
 // SwiGLU forward, one 32-row block: block 2q holds g and block 2q+1 the
 // matching u in every lane.
@@ -167,13 +161,28 @@ __device__ __forceinline__ void mx_swiglu_stage(
     for (int q = 0; q < NB / 2; ++q) {
       const float g = am[2 * q][r], u = am[2 * q + 1][r];
       const int col = q * 32 + (lane & 31);
+      const int o = row * 64 + st_col(row, col);
       if (phase == 0) {
-        l0[row * 64 + col] = (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
-        l1[row * 64 + col] = (uint16_t)f32_to_bf16_bits(g);
+        l0[o] = (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
+        l1[o] = (uint16_t)f32_to_bf16_bits(g);
       } else {
-        l0[row * 64 + col] = (uint16_t)f32_to_bf16_bits(u);
+        l0[o] = (uint16_t)f32_to_bf16_bits(u);
       }
     }
+  }
+}
+
+// Plain bf16 output of one 32-row block into a staged [128][128] region.
+template <int NB>
+__device__ __forceinline__ void mx_plain_stage(const f32x16 (&am)[NB], int mloc,
+                                               int lane, uint16_t *l) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = mloc + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      l[row * 128 + st_col(row, n * 32 + (lane & 31))] =
+          (uint16_t)f32_to_bf16_bits(am[n][r]);
   }
 }
 
@@ -192,7 +201,8 @@ __device__ __forceinline__ void mx_store_staged(const uint16_t *l, uint16_t *dst
     const int r = it * RPI + lane / LPR;
     const int c8 = (lane % LPR) * 8;
     if (arow0 + r < rows && col0 + c8 < N)
-      *(uint4 *)(dst + (grow0 + r) * ld + col0 + c8) = *(const uint4 *)(l + r * W + c8);
+      *(uint4 *)(dst + (grow0 + r) * ld + col0 + c8) =
+          *(const uint4 *)(l + r * W + st_col(r, c8));
   }
 }
 
@@ -212,7 +222,7 @@ __device__ __forceinline__ void mx_load_staged(uint16_t *l, const uint16_t *src,
     uint4 v = make_uint4(0u, 0u, 0u, 0u);
     if (arow0 + r < rows && col0 + c8 < N)
       v = *(const uint4 *)(src + (grow0 + r) * ld + col0 + c8);
-    *(uint4 *)(l + r * W + c8) = v;
+    *(uint4 *)(l + r * W + st_col(r, c8)) = v;
   }
 }
 
@@ -233,15 +243,15 @@ __device__ __forceinline__ void mx_swiglu_bwd_stage(
     float part = 0.f;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const int col = n * 32 + (lane & 31);
+      const int o = row * 128 + st_col(row, n * 32 + (lane & 31));
       const float da = am[n][r];
-      const float g = bf16_bits_to_f32(lg[row * 128 + col]);
-      const float u = bf16_bits_to_f32(lu[row * 128 + col]);
+      const float g = bf16_bits_to_f32(lg[o]);
+      const float u = bf16_bits_to_f32(lu[o]);
       const float sg = sigmoid_f32(g);
       const float sl = g * sg;
       const float dsl = sg * (1.f + g * (1.f - sg));
-      lg[row * 128 + col] = (uint16_t)f32_to_bf16_bits(da * s * u * dsl);
-      lu[row * 128 + col] = (uint16_t)f32_to_bf16_bits(da * s * sl);
+      lg[o] = (uint16_t)f32_to_bf16_bits(da * s * u * dsl);
+      lu[o] = (uint16_t)f32_to_bf16_bits(da * s * sl);
       part += da * sl * u;
     }
 #pragma unroll
@@ -250,9 +260,13 @@ __device__ __forceinline__ void mx_swiglu_bwd_stage(
   }
 }
 
-template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES>
+template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES, int BKB>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
-  constexpr int CPR = 8;                               // 16-byte chunks per row
+  // BKB: K values (code bytes) per stage, 128 or 64.  A stage always carries
+  // the scale dword of the 128 values it lies in (a 64-value stage uses half).
+  static_assert(BKB == 128 || BKB == 64, "stage width");
+  constexpr int CPR = BKB / 16;                        // 16-byte chunks per row
+  constexpr int KK = BKB / 64;                         // 64-value MFMA steps
   constexpr int WTM = BM / WM, WTN = BN / WN, MB = WTM / 32, NB = WTN / 32;
   constexpr int CODE_CHUNKS = (BM + BN) * CPR;
   constexpr int LC = CODE_CHUNKS / 256;                // code loads per thread
@@ -260,7 +274,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   constexpr int L = LC + LS;
   constexpr int SCALE_OFF = CODE_CHUNKS * 16;          // bytes
   constexpr int STAGE_BYTES = SCALE_OFF + (BM + BN) * 4;
-  constexpr int NMF = 2 * MB * NB;                     // MFMAs per stage
+  constexpr int NMF = KK * MB * NB;                    // MFMAs per stage
   static_assert(WM * WN == 4 && MB >= 1 && MB <= 4 && NB >= 1, "tile");
   static_assert(CODE_CHUNKS % 256 == 0 && (BM + BN) % 256 == 0, "load split");
   static_assert((STAGES - 2) * L <= 63, "vmcnt range");
@@ -288,7 +302,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     row0 = r_begin + mt * BM;
     rows = min(BM, r_end - row0);
     k0 = 0;
-    KT = p.K / 128;
+    KT = p.K / BKB;
   } else {
     const int per_g = p.MT * p.NT;
     e = t / per_g;
@@ -296,7 +310,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     row0 = mt * BM;
     rows = min(BM, p.M - row0);
     k0 = p.kseg[e];
-    KT = (p.kseg[e + 1] - k0) / 128;
+    KT = (p.kseg[e + 1] - k0) / BKB;
   }
 
   // Sources of this thread's loads.  Code load i (< LC) moves chunks
@@ -313,14 +327,14 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     gsrc1[i] = nullptr;
     if (row < BM) {
       const int64_t r = row0 + min(row, rows - 1);
-      gsrc[i] = code ? (const char *)p.A + r * p.lda + k0 + mx_swz(row, q % CPR) * 16
+      gsrc[i] = code ? (const char *)p.A + r * p.lda + k0 + mx_swz<CPR>(row, q % CPR) * 16
                      : (const char *)p.As + r * p.ldas + k0 / 32;
     } else {
       bool up;
       const int col = mx_brow<EPI, BN>(nt, row - BM, p.N, up);
       const int64_t g = (int64_t)e;
       if (code) {
-        const int64_t ro = g * p.b_stride + (int64_t)col * p.ldb + k0 + mx_swz(row, q % CPR) * 16;
+        const int64_t ro = g * p.b_stride + (int64_t)col * p.ldb + k0 + mx_swz<CPR>(row, q % CPR) * 16;
         gsrc[i] = (const char *)(up ? p.B1 : p.B0) + ro;
         if (p.ksplit) gsrc1[i] = (const char *)p.B1 + ro - p.ksplit;
       } else {
@@ -335,13 +349,13 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   // once unrolled; ks and b are uniform).
   auto issue = [&](int i, int b, int ks) {
     const uint32_t sb = lds0 + (uint32_t)(b * STAGE_BYTES);
-    const bool hi = p.ksplit && ks * 128 >= p.ksplit;
+    const bool hi = p.ksplit && ks * BKB >= p.ksplit;
     const char *src = (hi && gsrc1[i]) ? gsrc1[i] : gsrc[i];
     if (i < LC)
-      mx_load_lds16(sb + (uint32_t)((wid * LC + i) * 1024), src + (int64_t)ks * 128);
+      mx_load_lds16(sb + (uint32_t)((wid * LC + i) * 1024), src + (int64_t)ks * BKB);
     else
       mx_load_lds4(sb + (uint32_t)(SCALE_OFF + (wid * LS + (i - LC)) * 256),
-                   src + (int64_t)ks * 4);
+                   src + (int64_t)(ks * BKB / 128) * 4);
   };
 
   f32x16 acc[MB][NB];
@@ -377,8 +391,10 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
     for (int n = 0; n < NB; ++n) sbv[n] = Ssc[BM + brow0 + n * 32 + (lane & 31)];
 
+    // first scale byte of this stage in its 128-value dword
+    const int sb0 = (kt * BKB % 128) / 32;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KK; ++kk) {
       // Operand layout of the 32x32x64 f8 instruction: lane half h holds
       // K [16h, 16h+16) in its first four registers and [32+16h, 48+16h)
       // in the last four; block b (K [32b, 32b+32)) takes its scale from
@@ -388,20 +404,20 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         const int row = arow0 + m * 32 + (lane & 31);
-        const uint4 v0 = As[row * CPR + mx_swz(row, c0)];
-        const uint4 v1 = As[row * CPR + mx_swz(row, c1)];
+        const uint4 v0 = As[row * CPR + mx_swz<CPR>(row, c0)];
+        const uint4 v1 = As[row * CPR + mx_swz<CPR>(row, c1)];
         af[m] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                         (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
       }
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
         const int row = brow0 + n * 32 + (lane & 31);
-        const uint4 v0 = Bs[row * CPR + mx_swz(row, c0)];
-        const uint4 v1 = Bs[row * CPR + mx_swz(row, c1)];
+        const uint4 v0 = Bs[row * CPR + mx_swz<CPR>(row, c0)];
+        const uint4 v1 = Bs[row * CPR + mx_swz<CPR>(row, c1)];
         bfr[n] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
                          (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
       }
-      const int sh = 8 * (2 * kk + h);
+      const int sh = 8 * (sb0 + 2 * kk + h);
 #pragma unroll
       for (int m = 0; m < MB; ++m)
 #pragma unroll
@@ -470,15 +486,16 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
       __syncthreads();
     }
   } else {
-#define MX_EPI_BLOCK(m)                                                      \
-    if constexpr (MB > (m))                                                  \
-      mx_epilogue_block<MODE, BN, NB>(p, acc[m], arow0 + (m) * 32, lane,    \
-                                      rows, row0, nt, brow0, e);
-    MX_EPI_BLOCK(0)
-    MX_EPI_BLOCK(1)
-    MX_EPI_BLOCK(2)
-    MX_EPI_BLOCK(3)
-#undef MX_EPI_BLOCK
+    static_assert(WTM == 128 && WTN == 128, "staging expects 128x128 wavefront tiles");
+    const int64_t base = (MODE == MX_KSEG) ? (int64_t)e * p.c_stride : 0;
+#define MX_PL_BLOCK(m) \
+    if constexpr (MB > (m)) mx_plain_stage<NB>(acc[m], (m) * 32, lane, lw);
+    MX_PL_BLOCK(0) MX_PL_BLOCK(1) MX_PL_BLOCK(2) MX_PL_BLOCK(3)
+#undef MX_PL_BLOCK
+    __syncthreads();
+    mx_store_staged<128, 128>(lw, (uint16_t *)p.C + base, p.ldc,
+                              (int64_t)nt * BN + brow0, p.N, row0 + arow0,
+                              arow0, rows, lane);
   }
 }
 
@@ -497,12 +514,12 @@ __global__ void mx_ds_reduce_kernel(const float *__restrict__ part, int nparts,
 
 namespace {
 
-// Tile shape: 256 x 256 on 2 x 2 wavefronts of 128 x 128, 2 stages of
-// (256 + 256) x 128 code bytes + scales (132 KB of LDS).
+// Tile shape: 256 x 256 on 2 x 2 wavefronts of 128 x 128; STAGES stages of
+// BKB K values: (256 + 256) x BKB code bytes + 2 KB of scales each.
 #ifndef MOE_MX_CFG
-#define MOE_MX_CFG 256, 256, 2, 2, 2
+#define MOE_MX_CFG 256, 256, 2, 2, 2, 128
 #endif
-constexpr int kMxCfg[5] = {MOE_MX_CFG};
+constexpr int kMxCfg[6] = {MOE_MX_CFG};
 constexpr int kMxBM = kMxCfg[0], kMxBN = kMxCfg[1], kMxWN = kMxCfg[3];
 
 template <int MODE, int EPI>
