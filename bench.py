@@ -2,10 +2,12 @@
 
 One step = one pass of the whole path over one batch of synthetic input:
 router GEMM + softmax/top-k, permute, grouped gate/up with the SwiGLU x
-routing-scale epilogue, grouped down, combine (default workload: the full
-layer, 8192 tokens, hidden 7168, 256 experts, top-8, intermediate 2048).
-The EP-share workloads (--workload c2_ep64_bf16 | c3_ep8_bf16) route before
-the timed region and time permute + FFN + combine.
+routing-scale epilogue (reading the token rows through row_src), grouped
+down, combine (default workload: the full layer, 8192 tokens, hidden 7168,
+256 experts, top-8, intermediate 2048).  The EP-share workloads (--workload
+c2_ep64_bf16 | c3_ep8_bf16) route before the timed region and time permute
++ FFN + combine; --workload c5_mxfp8 times the MXFP8 grouped-MLP training
+step.
 
 Prints one JSON line.  `value` is the grouped-FFN (+ router) TFLOP/s of the
 whole step with inputs resident in HBM; `roofline` is for the dominant kernel
@@ -101,16 +103,19 @@ def make_device_workload(wl, dev, weight_copies):
     return inp, d, copies
 
 
-def algorithmic(wl, R, n_touched):
-    """FLOPs and HBM bytes of one step (see the design doc for the accounting)."""
+def algorithmic(wl, R, n_touched, gather=True):
+    """FLOPs and HBM bytes of one step: every touched expert's weights once,
+    the expert rows of x read once per row (gathered by the gate/up GEMM, or
+    read by the permute and written + re-read as x_perm), a and y written and
+    read once, out written once."""
     H, I, T, E, k = wl.H, wl.I, wl.T, wl.E, wl.k
     flop_ffn = 6.0 * R * H * I
     flop_router = 2.0 * T * H * E if wl.router == "gemm" else 0.0
     w_bytes = 3.0 * n_touched * H * I * 2
     act = 2.0
     gate_up_bytes = 2.0 * n_touched * H * I * 2 + R * H * act + R * I * act
-    step_bytes = (w_bytes + T * H * act            # x read by the permute
-                  + 2 * R * H * act                # x_perm write + read
+    x_bytes = R * H * act if gather else T * H * act + 2 * R * H * act
+    step_bytes = (w_bytes + x_bytes
                   + 2 * R * I * act                # a write + read
                   + 2 * R * H * act                # y write + read
                   + T * H * act)                   # out write
@@ -333,6 +338,10 @@ def main():
                              "mid_bf16", "c5_mxfp8", "mid_mxfp8"])
     ap.add_argument("--cpu-tokens", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="full layer: permute writes x_perm and the gate/up "
+                         "GEMM reads it, instead of reading token rows of x "
+                         "through row_src (EP shares always read x_perm)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one elementwise copy of this many "
                          "MiB (read + write) to calibrate HBM byte counters")
@@ -366,7 +375,11 @@ def main():
     logits = torch.empty((T, wl.E), dtype=torch.float32, device=dev)
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    pout = moe.PermuteOut(T, k, H, wl.n_local, torch.bfloat16, dev)
+    # The full layer on one GPU reads token rows through row_src; an EP share
+    # gets its rows already permuted by the dispatch, so it reads x_perm.
+    gather = not args.no_gather and wl.n_local == wl.E
+    pout = moe.PermuteOut(T, k, H, wl.n_local, torch.bfloat16, dev,
+                          with_x=not gather)
     a = torch.empty((F, I), dtype=torch.bfloat16, device=dev)
     y = torch.empty((F, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
@@ -386,12 +399,16 @@ def main():
         wg, wu, wd = wcopies[i % len(wcopies)]
         if wl.router == "gemm":
             route()
-        moe.permute(topk_idx, d["x"], wl.e_begin, wl.n_local, topk_w=topk_w,
-                    out=pout)
+        moe.permute(topk_idx, None if gather else d["x"], wl.e_begin,
+                    wl.n_local, topk_w=topk_w, out=pout)
         if timed_ev is not None:
             timed_ev[0].record(stream)
-        moe.grouped_gate_up(pout.x_perm, pout.offsets, pout.s_perm, wg, wu,
-                            a=a, workspace=ws)
+        if gather:
+            moe.grouped_gate_up_gather(d["x"], pout.row_src, k, pout.offsets,
+                                       pout.s_perm, wg, wu, a=a, workspace=ws)
+        else:
+            moe.grouped_gate_up(pout.x_perm, pout.offsets, pout.s_perm, wg, wu,
+                                a=a, workspace=ws)
         if timed_ev is not None:
             timed_ev[1].record(stream)
         moe.grouped_down(a, pout.offsets, wd, y=y, workspace=ws)
@@ -417,7 +434,7 @@ def main():
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
-    alg = algorithmic(wl, R, n_touched)
+    alg = algorithmic(wl, R, n_touched, gather)
     flop = alg["flop_ffn"] + alg["flop_router"]
     tflops = flop / (ms_step * 1e-3) / 1e12
     gu_gbs = alg["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
@@ -442,6 +459,8 @@ def main():
             "rows": R, "experts_touched": n_touched,
             "router": "router GEMM + softmax/top-k in the step"
                       if wl.router == "gemm" else "routed before timing",
+            "gate_up_input": "token rows gathered on load through row_src"
+                             if gather else "permuted copy x_perm",
         },
         "rows_per_s": round(R / (ms_step * 1e-3), 1),
         "step_hbm_gbs": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9, 1),

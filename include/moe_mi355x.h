@@ -155,6 +155,24 @@ int moe_grouped_gate_up(const void *x_perm, const int32_t *offsets,
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * moe_grouped_gate_up_gather - moe_grouped_gate_up with the expert rows
+ * read straight from the token rows: permuted row r is x[row_src[r] / k]
+ * (row_src as written by moe_permute, which may then skip x_perm by passing
+ * x = NULL).  Saves writing and re-reading the permuted copy of x.
+ * x [T, H] bf16; row_src [R_cap] int32 (rows < offsets[n_local] are read;
+ * an index past the last token is clamped to it).  Other arguments as for
+ * moe_grouped_gate_up; results are identical to it on x_perm.
+ * dtype: MOE_DT_BF16 only (MOE_E_UNSUPPORTED otherwise); R_cap <= T * k.
+ */
+int moe_grouped_gate_up_gather(const void *x, const int32_t *row_src,
+                               int64_t T, int64_t k, const int32_t *offsets,
+                               const float *s_perm, int64_t n_local,
+                               int64_t R_cap, int64_t H, int64_t I,
+                               const void *w_gate, const void *w_up, int dtype,
+                               void *a, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/*
  * moe_grouped_down - y[r] = a[r] . W_down[e]^T for every local expert's rows
  * (fp32 accumulation, dtype output), rows < R of y [R_cap, H].
  * Same limits and workspace as moe_grouped_gate_up.

@@ -79,6 +79,9 @@ def lib():
                                                 i64, i64, i64, vp, vp, vp, vp,
                                                 vp, vp, vp, vp, vp, vp, vp, vp,
                                                 sz, vp]
+        L.moe_grouped_gate_up_gather.argtypes = [vp, vp, i64, i64, vp, vp, i64,
+                                                 i64, i64, i64, vp, vp, i32, vp,
+                                                 vp, sz, vp]
         L.moe_grouped_linear_mxfp8_workspace_bytes.argtypes = [i64, i64, i64]
         L.moe_grouped_linear_mxfp8_workspace_bytes.restype = sz
         L.moe_grouped_linear_mxfp8.argtypes = [vp, vp, i64, i64, i64, i64, vp,
@@ -215,6 +218,22 @@ def grouped_gate_up(x_perm, offsets, s_perm, w_gate, w_up, a=None,
     _call("moe_grouped_gate_up", _p(x_perm), _p(offsets), _p(s_perm),
           n_local, R_cap, H, I, _p(w_gate), _p(w_up), _dt(x_perm), _p(a),
           _p(workspace), workspace.numel(), _stream(stream))
+    return a
+
+
+def grouped_gate_up_gather(x, row_src, k, offsets, s_perm, w_gate, w_up,
+                           a=None, workspace=None, stream=None):
+    """grouped_gate_up with permuted row r read as x[row_src[r] // k]."""
+    T, H = x.shape
+    R_cap = row_src.shape[0]
+    n_local, I, _ = w_gate.shape
+    if a is None:
+        a = torch.empty((R_cap, I), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = ffn_workspace(R_cap, n_local, H, I, x.dtype, x.device)
+    _call("moe_grouped_gate_up_gather", _p(x), _p(row_src), T, k, _p(offsets),
+          _p(s_perm), n_local, R_cap, H, I, _p(w_gate), _p(w_up), _dt(x),
+          _p(a), _p(workspace), workspace.numel(), _stream(stream))
     return a
 
 

@@ -192,6 +192,30 @@ int moe_grouped_gate_up(const void *x_perm, const int32_t *offsets,
   return status_of(err);
 }
 
+int moe_grouped_gate_up_gather(const void *x, const int32_t *row_src,
+                               int64_t T, int64_t k, const int32_t *offsets,
+                               const float *s_perm, int64_t n_local,
+                               int64_t R_cap, int64_t H, int64_t I,
+                               const void *w_gate, const void *w_up, int dtype,
+                               void *a, void *workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  int st = check_ffn(offsets, n_local, R_cap, H, I, dtype, workspace,
+                     workspace_bytes);
+  if (st != MOE_OK) return st;
+  if (dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
+  if (T < 1 || k < 1 || k > 32 || T * k >= kMaxRows || R_cap > T * k)
+    return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!x || !row_src || !w_gate || !w_up || !a) return MOE_E_ARG;
+  if (!aligned16(x) || !aligned16(w_gate) || !aligned16(w_up) ||
+      !aligned16(a))
+    return MOE_E_ALIGN;
+  return status_of(moe::launch_gate_up_bf16(
+      (const uint16_t *)x, offsets, s_perm, (int)n_local, R_cap, (int)H,
+      (int)I, (const uint16_t *)w_gate, (const uint16_t *)w_up, (uint16_t *)a,
+      (int32_t *)workspace, num_cus(), stream, row_src, (int)k, T));
+}
+
 int moe_grouped_down(const void *a, const int32_t *offsets, int64_t n_local,
                      int64_t R_cap, int64_t H, int64_t I, const void *w_down,
                      int dtype, void *y, void *workspace,

@@ -35,6 +35,8 @@
 //     fragment reads) while every 8 lanes still read one contiguous row piece.
 //   * 32-row sub-tiles past the end of an expert's segment are skipped
 //     (uniform per wavefront).
+//   * Gather on load (gate/up): A rows may be read straight from the token
+//     rows x[row_src[r] / k] instead of a permuted copy.
 //   * Epilogues: SWIGLU (B rows alternate 32 gate and the 32 matching up
 //     rows, so each lane holds g and u of the same outputs; writes
 //     a = s * SiLU(g) * u in bf16), BF16 (plain store) and F32_BIAS (router
@@ -55,6 +57,8 @@ struct GemmArgs {
   const float *bias;        // F32_BIAS: [N] or null
   const int32_t *offsets;   // [G + 1] row offsets, or null: one group
   const int32_t *tile_prefix;  // [G + 1] tile prefix of this launch's class
+  const int32_t *a_rows;    // gather-on-load: A row of permuted row r is
+  int a_div, a_rows_max;    //   min(a_rows[r] / a_div, a_rows_max); or null
   int single_rows;          // rows of the single group (offsets == null)
   int G;                    // groups
   int N;                    // output columns (a-columns for SWIGLU)
@@ -276,7 +280,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
       const int row = q / CPR;
       if (row < BM) {
         const int kc = swz<CPR>(row, q % CPR);
-        gsrc[i] = (const char *)(p.A + (int64_t)(row0 + min(row, rows - 1)) * K + kc * 8);
+        int64_t ar = row0 + min(row, rows - 1);
+        if (p.a_rows) ar = min(p.a_rows[ar] / p.a_div, p.a_rows_max);
+        gsrc[i] = (const char *)(p.A + ar * K + kc * 8);
       } else {
         const int j = row - BM;
         const int kc = swz<CPR>(j, q % CPR);
@@ -455,9 +461,11 @@ hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                const float *s_perm, int n_local, int64_t R_cap,
                                int H, int I, const uint16_t *w_gate,
                                const uint16_t *w_up, uint16_t *a,
-                               int32_t *tile_ws, int num_cus, hipStream_t s) {
+                               int32_t *tile_ws, int num_cus, hipStream_t s,
+                               const int32_t *row_src, int k, int64_t T) {
   GemmArgs p{};
   p.A = x_perm; p.B0 = w_gate; p.B1 = w_up;
+  p.a_rows = row_src; p.a_div = k; p.a_rows_max = (int)(T - 1);
   p.b_stride = (int64_t)I * H;
   p.C = a; p.ldc = I; p.row_scale = s_perm;
   p.offsets = offsets; p.G = n_local; p.N = I; p.K = H;

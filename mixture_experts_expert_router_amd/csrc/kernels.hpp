@@ -35,7 +35,9 @@ hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                const float *s_perm, int n_local, int64_t R_cap,
                                int H, int I, const uint16_t *w_gate,
                                const uint16_t *w_up, uint16_t *a,
-                               int32_t *tile_ws, int num_cus, hipStream_t s);
+                               int32_t *tile_ws, int num_cus, hipStream_t s,
+                               const int32_t *row_src = nullptr,
+                               int k = 1, int64_t T = 1);
 hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
                             int n_local, int64_t R_cap, int H, int I,
                             const uint16_t *w_down, uint16_t *y,

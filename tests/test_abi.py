@@ -105,6 +105,17 @@ def test_ffn_validation(L):
     assert call(x=None) == E_ARG
     assert call(x=P_ODD) == E_ALIGN
     assert call(R=0) == 0  # no rows: nothing enqueued
+    gg = L.moe_grouped_gate_up_gather
+
+    def gat(x=P, rs=P, T=32, k=2, R=64, dt=BF16):
+        return gg(x, rs, T, k, P, None, 4, R, 128, 128, P, P, dt, P, P, ws, None)
+
+    assert gat(dt=F32) == 5                      # MOE_E_UNSUPPORTED
+    assert gat(k=0) == E_SHAPE and gat(T=0) == E_SHAPE
+    assert gat(R=65) == E_SHAPE                  # R_cap > T * k
+    assert gat(rs=None) == E_ARG and gat(x=None) == E_ARG
+    assert gat(x=P_ODD) == E_ALIGN
+    assert gat(R=0) == 0
     d = L.moe_grouped_down
     assert d(P, P, 4, 64, 100, 128, P, BF16, P, P, ws, None) == E_SHAPE
     assert d(P, P, 4, 64, 128, 128, None, BF16, P, P, ws, None) == E_ARG

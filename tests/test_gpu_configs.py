@@ -145,6 +145,11 @@ def test_c4_permute_ffn_combine_sampled(c4):
                            wl.n_local, inp["w_gate"], inp["w_up"], inp["w_down"])
     eo = assert_close(to_f64(out[toks]), o_ref, "bf16", "c4 out")
     print_case("c4", f"err/RMS a {ea:.2e} y {ey:.2e} out {eo:.2e}")
+    # the gather-on-load gate/up the benchmark times: same bits as on x_perm
+    a_g = moe.grouped_gate_up_gather(d["x"], p.row_src, wl.k, p.offsets,
+                                     p.s_perm, d["w_gate"], d["w_up"])
+    moe.debug_sync()
+    assert torch.equal(a_g[:R], a[:R])
 
 
 @pytest.mark.timeout(300)

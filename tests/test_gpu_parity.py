@@ -77,6 +77,26 @@ def test_small_workload_stepwise(name):
     assert_close(to_f64(g["out"]), ref["out"], dt, f"{name} out")
 
 
+@pytest.mark.parametrize("name", ["tiny_bf16", "small_bf16", "small_ep_bf16", "mid_bf16"])
+def test_gate_up_gather_on_load(name):
+    """Reading the token rows through row_src gives the same bits as the
+    permuted copy, and the permute without x writes no x_perm."""
+    wl = synth.WORKLOADS[name]
+    print_case(name, "gather on load")
+    inp = synth.make_inputs(wl)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    g = gpu_chain(wl, d)
+    p = g["p"]
+    p2 = moe.permute(g["idx"], None, wl.e_begin, wl.n_local, topk_w=g["w"])
+    assert p2.x_perm is None
+    a2 = moe.grouped_gate_up_gather(d["x"], p2.row_src, wl.k, p2.offsets,
+                                    p2.s_perm, d["w_gate"], d["w_up"])
+    moe.debug_sync()
+    R = int(p.offsets[-1].item())
+    assert torch.equal(p2.offsets, p.offsets)
+    np.testing.assert_array_equal(bits(a2[:R]), bits(g["a"][:R]))
+
+
 def test_topk_bit_exact_on_generated_logits():
     wl = synth.WORKLOADS["c2_ep64_bf16"]
     print_case("topk", wl.name)
