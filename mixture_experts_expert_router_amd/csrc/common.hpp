@@ -50,6 +50,60 @@ __device__ __forceinline__ int upper_bound_minus1(const int32_t *p, int n,
   return lo;
 }
 
+// ---- staged epilogues ----------------------------------------------------
+// After a GEMM's K loop its LDS ring is free; each wavefront stages its part
+// of the output in a region of its own ([NROWS][W] bf16) and writes it back
+// to HBM as 16-byte row pieces instead of 2-byte stores per lane.
+// Staged regions swizzle columns by bit 2 of the row: the two halves of a
+// wavefront write rows i and i + 4 of one 32x32 block at once, which would
+// otherwise fall on the same banks.  The XOR moves whole 8-column chunks,
+// so 16-byte row pieces stay contiguous.
+template <int W>
+__device__ __forceinline__ int st_col(int row, int col) {
+  constexpr int X = W >= 64 ? 32 : W / 2;   // a multiple of 8 below W
+  return col ^ (((row >> 2) & 1) * X);
+}
+
+// Write rows [0, nrows) of a staged [nrows][W] bf16 region to
+// dst[(grow0 + r) * ld + col0 + c] for tile rows arow0 + r < rows and
+// columns col0 + c < N (N % 8 == 0).
+template <int W, int NROWS>
+__device__ __forceinline__ void store_staged(const uint16_t *l, uint16_t *dst,
+                                                int64_t ld, int64_t col0, int N,
+                                                int64_t grow0, int arow0,
+                                                int rows, int lane) {
+  constexpr int LPR = W / 8;                 // lanes per row
+  constexpr int RPI = 64 / LPR;              // rows per instruction
+#pragma unroll
+  for (int it = 0; it < NROWS / RPI; ++it) {
+    const int r = it * RPI + lane / LPR;
+    const int c8 = (lane % LPR) * 8;
+    if (arow0 + r < rows && col0 + c8 < N)
+      *(uint4 *)(dst + (grow0 + r) * ld + col0 + c8) =
+          *(const uint4 *)(l + r * W + st_col<W>(r, c8));
+  }
+}
+
+// Load rows [0, NROWS) of src (bf16, row pitch ld) into a [NROWS][W] region;
+// rows past the tile's valid rows, or columns past N, read as zero.
+template <int W, int NROWS>
+__device__ __forceinline__ void load_staged(uint16_t *l, const uint16_t *src,
+                                               int64_t ld, int64_t col0, int N,
+                                               int64_t grow0, int arow0,
+                                               int rows, int lane) {
+  constexpr int LPR = W / 8;
+  constexpr int RPI = 64 / LPR;
+#pragma unroll
+  for (int it = 0; it < NROWS / RPI; ++it) {
+    const int r = it * RPI + lane / LPR;
+    const int c8 = (lane % LPR) * 8;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (arow0 + r < rows && col0 + c8 < N)
+      v = *(const uint4 *)(src + (grow0 + r) * ld + col0 + c8);
+    *(uint4 *)(l + r * W + st_col<W>(r, c8)) = v;
+  }
+}
+
 // Tile of workgroup `bid` when every tile has its own workgroup and the
 // grid is launched for an upper bound of `total` (the real count lives on
 // the device).  Workgroups are handed to the 8 XCDs round-robin by id and,

@@ -345,51 +345,66 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
     wait_loads_barrier<0>();
 
     // Epilogue.  Lane holds column (lane & 31) of each 32x32 block and rows
-    // 8*(r/4) + 4*(lane/32) + (r%4), r < 16.
+    // 8*(r/4) + 4*(lane/32) + (r%4), r < 16.  bf16 outputs are staged in a
+    // per-wavefront LDS region and leave as 16-byte row pieces.
     if (EPI == EPI_SWIGLU) {
       // B rows alternate 32 gate rows and the 32 matching up rows, so block
       // 2q holds g and block 2q+1 holds u of the same outputs in every lane.
+      constexpr int W = WTN / 2;
+      uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * W);
 #pragma unroll
       for (int m = 0; m < MB; ++m) {
         if (m >= mvalid) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int rw = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int i = wrow0 + rw;
           const float s = (i < rows && p.row_scale) ? p.row_scale[row0 + i] : 1.f;
 #pragma unroll
           for (int q = 0; q < NB / 2; ++q) {
             const float g = acc[m][2 * q][r], u = acc[m][2 * q + 1][r];
-            const int col = nt * (BN / 2) + wn * (WTN / 2) + q * 32 + (lane & 31);
-            if (i < rows && col < p.N)
-              ((uint16_t *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
-                  (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
+            lw[rw * W + st_col<W>(rw, q * 32 + (lane & 31))] =
+                (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
           }
         }
       }
+      __syncthreads();
+      store_staged<W, WTM>(lw, (uint16_t *)p.C, p.ldc,
+                           (int64_t)nt * (BN / 2) + wn * W, p.N, row0 + wrow0,
+                           wrow0, rows, lane);
+    } else if (EPI == EPI_BF16) {
+      uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * WTN);
+#pragma unroll
+      for (int m = 0; m < MB; ++m) {
+        if (m >= mvalid) continue;
+#pragma unroll
+        for (int n = 0; n < NB; ++n)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rw = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+            lw[rw * WTN + st_col<WTN>(rw, n * 32 + (lane & 31))] =
+                (uint16_t)f32_to_bf16_bits(acc[m][n][r]);
+          }
+      }
+      __syncthreads();
+      store_staged<WTN, WTM>(lw, (uint16_t *)p.C, p.ldc,
+                             (int64_t)nt * BN + wn * WTN, p.N, row0 + wrow0,
+                             wrow0, rows, lane);
     } else {
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-      if (m >= mvalid) continue;
+      for (int m = 0; m < MB; ++m) {
+        if (m >= mvalid) continue;
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
+        for (int n = 0; n < NB; ++n)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const float v = acc[m][n][r];
-          {
+          for (int r = 0; r < 16; ++r) {
+            const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
             const int col = nt * BN + wn * WTN + n * 32 + (lane & 31);
-            if (i < rows && col < p.N) {
-              if (EPI == EPI_BF16)
-                ((uint16_t *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
-                    (uint16_t)f32_to_bf16_bits(v);
-              else
-                ((float *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
-                    v + (p.bias ? p.bias[col] : 0.f);
-            }
+            if (i < rows && col < p.N)
+              ((float *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
+                  acc[m][n][r] + (p.bias ? p.bias[col] : 0.f);
           }
-        }
       }
-    }
     }
   }
 }

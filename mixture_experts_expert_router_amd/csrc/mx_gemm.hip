@@ -138,14 +138,6 @@ __device__ __forceinline__ int mx_brow(int nt, int j, int N, bool &up) {
 // Region rows are 128 bytes (64 bf16) for SwiGLU outputs, 256 bytes (128
 // bf16) for the SwiGLU-backward g, u, dg, du tiles.
 
-// Staged regions swizzle columns by bit 2 of the row: the two halves of a
-// wavefront write rows i and i + 4 of one 32x32 block at once, which would
-// otherwise fall on the same banks.  The XOR moves whole 8-column chunks,
-// so 16-byte row pieces stay contiguous.
-__device__ __forceinline__ int st_col(int row, int col) {
-  return col ^ (((row >> 2) & 1) << 5);
-}
-
 // SwiGLU forward, one 32-row block: block 2q holds g and block 2q+1 the
 // matching u in every lane.
 template <int NB>
@@ -161,7 +153,7 @@ __device__ __forceinline__ void mx_swiglu_stage(
     for (int q = 0; q < NB / 2; ++q) {
       const float g = am[2 * q][r], u = am[2 * q + 1][r];
       const int col = q * 32 + (lane & 31);
-      const int o = row * 64 + st_col(row, col);
+      const int o = row * 64 + st_col<64>(row, col);
       if (phase == 0) {
         l0[o] = (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
         l1[o] = (uint16_t)f32_to_bf16_bits(g);
@@ -181,48 +173,8 @@ __device__ __forceinline__ void mx_plain_stage(const f32x16 (&am)[NB], int mloc,
     const int row = mloc + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 #pragma unroll
     for (int n = 0; n < NB; ++n)
-      l[row * 128 + st_col(row, n * 32 + (lane & 31))] =
+      l[row * 128 + st_col<128>(row, n * 32 + (lane & 31))] =
           (uint16_t)f32_to_bf16_bits(am[n][r]);
-  }
-}
-
-// Write rows [0, nrows) of a staged [nrows][W] bf16 region to
-// dst[(grow0 + r) * ld + col0 + c] for tile rows arow0 + r < rows and
-// columns col0 + c < N (N % 8 == 0).
-template <int W, int NROWS>
-__device__ __forceinline__ void mx_store_staged(const uint16_t *l, uint16_t *dst,
-                                                int64_t ld, int64_t col0, int N,
-                                                int64_t grow0, int arow0,
-                                                int rows, int lane) {
-  constexpr int LPR = W / 8;                 // lanes per row
-  constexpr int RPI = 64 / LPR;              // rows per instruction
-#pragma unroll
-  for (int it = 0; it < NROWS / RPI; ++it) {
-    const int r = it * RPI + lane / LPR;
-    const int c8 = (lane % LPR) * 8;
-    if (arow0 + r < rows && col0 + c8 < N)
-      *(uint4 *)(dst + (grow0 + r) * ld + col0 + c8) =
-          *(const uint4 *)(l + r * W + st_col(r, c8));
-  }
-}
-
-// Load rows [0, NROWS) of src (bf16, row pitch ld) into a [NROWS][W] region;
-// rows past the tile's valid rows, or columns past N, read as zero.
-template <int W, int NROWS>
-__device__ __forceinline__ void mx_load_staged(uint16_t *l, const uint16_t *src,
-                                               int64_t ld, int64_t col0, int N,
-                                               int64_t grow0, int arow0,
-                                               int rows, int lane) {
-  constexpr int LPR = W / 8;
-  constexpr int RPI = 64 / LPR;
-#pragma unroll
-  for (int it = 0; it < NROWS / RPI; ++it) {
-    const int r = it * RPI + lane / LPR;
-    const int c8 = (lane % LPR) * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (arow0 + r < rows && col0 + c8 < N)
-      v = *(const uint4 *)(src + (grow0 + r) * ld + col0 + c8);
-    *(uint4 *)(l + r * W + st_col(r, c8)) = v;
   }
 }
 
@@ -243,7 +195,7 @@ __device__ __forceinline__ void mx_swiglu_bwd_stage(
     float part = 0.f;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
-      const int o = row * 128 + st_col(row, n * 32 + (lane & 31));
+      const int o = row * 128 + st_col<128>(row, n * 32 + (lane & 31));
       const float da = am[n][r];
       const float g = bf16_bits_to_f32(lg[o]);
       const float u = bf16_bits_to_f32(lu[o]);
@@ -454,10 +406,10 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
 #undef MX_SW_BLOCK
       __syncthreads();
       if (phase == 0) {
-        mx_store_staged<64, 128>(l0, (uint16_t *)p.C, p.ldc, col0, p.N, grow0, arow0, rows, lane);
-        if (p.gu) mx_store_staged<64, 128>(l1, p.gu, p.ldgu, col0, p.N, grow0, arow0, rows, lane);
+        store_staged<64, 128>(l0, (uint16_t *)p.C, p.ldc, col0, p.N, grow0, arow0, rows, lane);
+        if (p.gu) store_staged<64, 128>(l1, p.gu, p.ldgu, col0, p.N, grow0, arow0, rows, lane);
       } else if (p.gu) {
-        mx_store_staged<64, 128>(l0, p.gu, p.ldgu, p.N + col0, 2 * p.N, grow0, arow0, rows, lane);
+        store_staged<64, 128>(l0, p.gu, p.ldgu, p.N + col0, 2 * p.N, grow0, arow0, rows, lane);
       }
       __syncthreads();
     }
@@ -470,8 +422,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     for (int half = 0; half < 2; ++half) {
       const int64_t grow0 = row0 + arow0 + half * 64;
       const int ar0 = arow0 + half * 64;
-      mx_load_staged<128, 64>(lg, p.gu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
-      mx_load_staged<128, 64>(lu, p.gu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      load_staged<128, 64>(lg, p.gu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      load_staged<128, 64>(lu, p.gu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
       __syncthreads();
       if (half == 0) {
         mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[0], 0, 0, lane, arow0, rows, row0, nt, wn, lg, lu);
@@ -481,8 +433,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
         mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[3], 32, 96, lane, arow0, rows, row0, nt, wn, lg, lu);
       }
       __syncthreads();
-      mx_store_staged<128, 64>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
-      mx_store_staged<128, 64>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      store_staged<128, 64>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      store_staged<128, 64>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
       __syncthreads();
     }
   } else {
@@ -493,7 +445,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     MX_PL_BLOCK(0) MX_PL_BLOCK(1) MX_PL_BLOCK(2) MX_PL_BLOCK(3)
 #undef MX_PL_BLOCK
     __syncthreads();
-    mx_store_staged<128, 128>(lw, (uint16_t *)p.C + base, p.ldc,
+    store_staged<128, 128>(lw, (uint16_t *)p.C + base, p.ldc,
                               (int64_t)nt * BN + brow0, p.N, row0 + arow0,
                               arow0, rows, lane);
   }
