@@ -8,46 +8,37 @@
 // E4M3 value (ties to even), saturating at +-448; an all-zero block gets
 // scale byte 0.  The sign of a value that rounds to zero is kept (0x80).
 //
-// The E4M3 rounding is done with exact fp32 arithmetic (scaling by a power
-// of two is exact; rintf rounds half to even), so the codes do not depend on
-// any conversion instruction's rounding mode.
+// Element conversion: v * 2^-X by v_ldexp_f32 (exact for every result that
+// can round to a non-zero code), a clamp to +-448 (the saturation), then
+// gfx950's v_cvt_pk_fp8_f32, which rounds to nearest, ties to even, in the
+// default rounding mode.  Four values cost about five VALU instructions.
+// The GPU tests run every finite bf16 value under every shared exponent
+// through both kernels and compare the codes with the oracle bit for bit.
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace moe {
 
-// floor(log2(a)) for a finite a > 0.
-__device__ __forceinline__ int ilog2f(float a) {
+// Shared exponent X of a block whose largest magnitude is amax (finite).
+// Blocks with amax < 2^-118 (all-zero ones included) get the floor -127;
+// a finite fp32 amax gives X <= 119, so the scale byte X + 127 <= 246.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (!(amax >= 0x1p-118f)) return -127;
   int e;
-  frexpf(a, &e);  // a = m * 2^e, m in [0.5, 1)
-  return e - 1;
+  frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
+  return e - 9;
 }
 
-__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
-  if (!(amax > 0.f)) return 0u;
-  int X = ilog2f(amax) - 8;
-  X = X < -127 ? -127 : (X > 127 ? 127 : X);
-  return (uint32_t)(X + 127);
-}
-
-// E4M3 code of v * 2^-(scale_byte - 127).
-__device__ __forceinline__ uint32_t e4m3_code(float v, uint32_t scale_byte) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  const float f = ldexpf(fabsf(v), 127 - (int)scale_byte);
-  uint32_t code;
-  if (f >= 464.f) {
-    code = 0x7E;                                   // saturate to 448
-  } else if (f < 0.015625f) {                      // below 2^-6: subnormal
-    code = (uint32_t)rintf(f * 512.f);             // m * 2^-9, m = 0..8
-  } else {
-    int e = ilog2f(f);
-    const float m = ldexpf(f, -e) - 1.f;           // [0, 1), exact
-    uint32_t q = (uint32_t)rintf(m * 8.f);         // 0..8
-    if (q == 8) { q = 0; ++e; }
-    code = ((uint32_t)(e + 7) << 3) | q;
-    if (code > 0x7E) code = 0x7E;
-  }
-  return sign | code;
+// E4M3 codes of a * 2^nX .. d * 2^nX (nX = -X), packed low byte first.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c,
+                                               float d, int nX) {
+  a = __builtin_amdgcn_fmed3f(ldexpf(a, nX), -448.f, 448.f);
+  b = __builtin_amdgcn_fmed3f(ldexpf(b, nX), -448.f, 448.f);
+  c = __builtin_amdgcn_fmed3f(ldexpf(c, nX), -448.f, 448.f);
+  d = __builtin_amdgcn_fmed3f(ldexpf(d, nX), -448.f, 448.f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
 }
 
 // axis 0: one thread per block of 32 values along a row.
@@ -79,29 +70,30 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(
   float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  const uint32_t sb = mx_scale_byte(amax);
+  const int X = mx_shared_exp(amax);
   uint32_t packed[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    packed[j] = e4m3_code(v[4 * j], sb) | (e4m3_code(v[4 * j + 1], sb) << 8) |
-                (e4m3_code(v[4 * j + 2], sb) << 16) |
-                (e4m3_code(v[4 * j + 3], sb) << 24);
+    packed[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], -X);
   uint4 *dst = (uint4 *)(codes + r * ld_codes + b * 32);
   dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-  scales[r * ld_scales + b] = (uint8_t)sb;
+  scales[r * ld_scales + b] = (uint8_t)(X + 127);
 }
 
 // axis 1: blocks of 32 rows down each column, inside segments of rows
 // [seg[s], seg[s+1]) zero-padded to a multiple of `align` (32 or 512); output
 // transposed: codesT[c, pad[s] + j] for row seg[s] + j, scalesT[c, blk].
 // seg == null: one segment of all `rows`.
-// One workgroup per tile of 128 padded rows x 64 columns: the tile is read
-// with coalesced 16-byte loads (8 threads per 128-byte row piece) into LDS,
-// then wavefront b quantises block b (32 rows) of all 64 columns, a lane per
-// column, and writes that column's 32 codes; the four wavefronts together
-// write each column's 128 codes as one 128-byte line.
-// Requires ld_in % 8 == 0, cols % 32 == 0 and a 16-byte aligned input.
+// A workgroup walks tiles of 128 padded rows x 64 columns, one tile ahead:
+// the next tile's 16-byte loads are in flight while the current one is
+// quantised.  The tile goes through LDS (8 lanes per 128-byte row piece);
+// wavefront b quantises block b (32 rows) of the 64 columns, a lane per
+// column, and stages the codes transposed in LDS, so that the write-back
+// stores whole 128-byte lines of codesT (8 lanes per line) and each
+// column's four scale bytes as one dword.
+// Requires ld_in % 8 == 0, ld_codes % 16 == 0, cols % 32 == 0 and 16-byte
+// aligned input and codes.
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
     const uint16_t *__restrict__ in, int64_t rows, int64_t cols,
     int64_t ld_in, const int32_t *__restrict__ seg,
@@ -109,19 +101,23 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
     uint8_t *__restrict__ codes, int64_t ld_codes,
     uint8_t *__restrict__ scales, int64_t ld_scales) {
   constexpr int TR = 128, TC = 64, LDT = TC + 2;   // +2: row pitch 132 B
+  constexpr int LDO = TR + 16;                     // staged code row pitch
   __shared__ uint16_t tile[TR * LDT];
-  __shared__ int32_t src[TR];
+  __shared__ __align__(16) uint8_t ostage[TC * LDO];
+  __shared__ uint32_t sstage[TC];
+  __shared__ int32_t src[2][TR];
   const int tid = threadIdx.x;
   const int padded = seg ? pad[nseg] : (int)((rows + align - 1) / align * align);
   const int ngrp = (padded + TR - 1) / TR;
   const int ncg = (int)((cols + TC - 1) / TC);
   const int64_t ntiles = (int64_t)ngrp * ncg;
-  for (int64_t g = blockIdx.x; g < ntiles; g += gridDim.x) {
-    const int rg = (int)(g / ncg), cg = (int)(g % ncg);
-    const int prow0 = rg * TR;
-    const int64_t c0 = (int64_t)cg * TC;
+  const bool dword_scales =
+      ld_scales % 4 == 0 && ((uintptr_t)scales & 3) == 0;
+
+  // Source row of each padded row of tile g (-1: padding).
+  auto lookup = [&](int64_t g, int buf) {
     if (tid < TR) {
-      const int prow = prow0 + tid;
+      const int prow = (int)(g / ncg) * TR + tid;
       int sr = -1;
       if (prow < padded) {
         if (seg) {
@@ -132,44 +128,81 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
           sr = prow;
         }
       }
-      src[tid] = sr;
+      src[buf][tid] = sr;
     }
-    __syncthreads();
+  };
+  auto load = [&](int64_t g, int buf, uint4 (&v)[TR / 32]) {
+    const int64_t c0 = (g % ncg) * TC;
+    const int cc = (tid & 7) * 8;
 #pragma unroll
     for (int p = 0; p < TR / 32; ++p) {
-      const int r = p * 32 + (tid >> 3);
-      const int cc = (tid & 7) * 8;
-      const int sr = src[r];
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      const int sr = src[buf][p * 32 + (tid >> 3)];
+      v[p] = make_uint4(0u, 0u, 0u, 0u);
       if (sr >= 0 && c0 + cc < cols)
-        v = *(const uint4 *)(in + (int64_t)sr * ld_in + c0 + cc);
-      uint32_t *d = (uint32_t *)(tile + r * LDT + cc);
-      d[0] = v.x; d[1] = v.y; d[2] = v.z; d[3] = v.w;
+        v[p] = *(const uint4 *)(in + (int64_t)sr * ld_in + c0 + cc);
     }
+  };
+
+  int64_t g = blockIdx.x;
+  if (g >= ntiles) return;
+  int buf = 0;
+  lookup(g, 0);
+  __syncthreads();
+  uint4 v[TR / 32];
+  load(g, 0, v);
+  for (; g < ntiles; g += gridDim.x, buf ^= 1) {
+    const int prow0 = (int)(g / ncg) * TR;
+    const int64_t c0 = (g % ncg) * TC;
+#pragma unroll
+    for (int p = 0; p < TR / 32; ++p) {
+      uint32_t *d = (uint32_t *)(tile + (p * 32 + (tid >> 3)) * LDT + (tid & 7) * 8);
+      d[0] = v[p].x; d[1] = v[p].y; d[2] = v[p].z; d[3] = v[p].w;
+    }
+    const int64_t gn = g + gridDim.x;
+    if (gn < ntiles) lookup(gn, buf ^ 1);
     __syncthreads();
+    if (gn < ntiles) load(gn, buf ^ 1, v);
+
     const int b = tid >> 6, c = tid & 63;
-    const int prow = prow0 + b * 32;
-    if (prow < padded && c0 + c < cols) {
-      float v[32];
+    {
+      float x[32];
       float amax = 0.f;
 #pragma unroll
       for (int j = 0; j < 32; ++j) {
-        v[j] = bf16_bits_to_f32(tile[(b * 32 + j) * LDT + c]);
-        amax = fmaxf(amax, fabsf(v[j]));
+        x[j] = bf16_bits_to_f32(tile[(b * 32 + j) * LDT + c]);
+        amax = fmaxf(amax, fabsf(x[j]));
       }
-      const uint32_t sb = mx_scale_byte(amax);
-      uint32_t packed[8];
+      const int X = mx_shared_exp(amax);
+      uint32_t pk[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        packed[j] = e4m3_code(v[4 * j], sb) | (e4m3_code(v[4 * j + 1], sb) << 8) |
-                    (e4m3_code(v[4 * j + 2], sb) << 16) |
-                    (e4m3_code(v[4 * j + 3], sb) << 24);
-      uint4 *dst = (uint4 *)(codes + (c0 + c) * ld_codes + prow);
-      dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
-      dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
-      scales[(c0 + c) * ld_scales + prow / 32] = (uint8_t)sb;
+        pk[j] = e4m3_pack4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], -X);
+      uint4 *o = (uint4 *)(ostage + c * LDO + b * 32);
+      o[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+      o[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+      ((uint8_t *)sstage)[c * 4 + b] = (uint8_t)(X + 127);
     }
     __syncthreads();
+
+    // Write-back: piece q = (column q/8, 16 bytes q%8) of the staged codes.
+#pragma unroll
+    for (int i = 0; i < (TC * TR / 16) / 256; ++i) {
+      const int q = tid + 256 * i;
+      const int cq = q >> 3, j = q & 7;
+      if (c0 + cq < cols && prow0 + j * 16 < padded)
+        *(uint4 *)(codes + (c0 + cq) * ld_codes + prow0 + j * 16) =
+            *(const uint4 *)(ostage + cq * LDO + j * 16);
+    }
+    if (tid < TC && c0 + tid < cols) {
+      const uint32_t w = sstage[tid];
+      uint8_t *sd = scales + (c0 + tid) * ld_scales + prow0 / 32;
+      if (dword_scales && prow0 + TR <= padded) {
+        *(uint32_t *)sd = w;
+      } else {
+        for (int k = 0; k < TR / 32; ++k)
+          if (prow0 + 32 * k < padded) sd[k] = (uint8_t)(w >> (8 * k));
+      }
+    }
   }
 }
 
@@ -223,7 +256,17 @@ hipError_t launch_mx_quant_cols(const uint16_t *in, int64_t rows,
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  const int64_t grid = (int64_t)num_cus * 8;
+  // As many workgroups as fit on the chip at once (LDS bounds them).
+  static int per_cu = 0;
+  if (per_cu == 0) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mx_quant_cols_kernel,
+                                                     256, 0) != hipSuccess ||
+        n < 1)
+      n = 4;
+    per_cu = n;
+  }
+  const int64_t grid = (int64_t)num_cus * per_cu;
   mx_quant_cols_kernel<<<(unsigned)grid, 256, 0, s>>>(
       in, rows, cols, ld_in, seg, pad, nseg, align, codes, ld_codes, scales,
       ld_scales);

@@ -81,6 +81,64 @@ def test_quantize_cols_segments_bit_exact(align):
         np.testing.assert_array_equal(s[:, pad[i] // 32:(pad[i] + npad) // 32], rs)
 
 
+def exhaustive_blocks():
+    """Blocks of 32 bf16 bit patterns that put every finite bf16 value under
+    every shared exponent X = -127..119.  For each biased bf16 exponent eb
+    (0..254) the anchor is the largest magnitude with that exponent
+    (mantissa 0x7F), which fixes the block's X (clamped to -127 for small
+    eb); the other 31 slots run through every magnitude up to the anchor, with
+    both signs.  Two all-zero blocks (+0, -0) close the list.  Returns
+    [n, 32] uint16, n a multiple of 1024."""
+    out = []
+    for eb in range(255):
+        a = (eb << 7) | 0x7F
+        mags = np.arange(a + 1, dtype=np.uint16)
+        vals = np.concatenate([mags, mags | np.uint16(0x8000)])
+        n = -(-len(vals) // 31)
+        vals = np.concatenate([vals, np.zeros(n * 31 - len(vals), np.uint16)])
+        b = np.empty((n, 32), np.uint16)
+        b[:, 0] = a | (0x8000 if eb & 1 else 0)
+        b[:, 1:] = vals.reshape(n, 31)
+        out.append(b)
+    out.append(np.zeros((1, 32), np.uint16))
+    out.append(np.full((1, 32), 0x8000, np.uint16))
+    blk = np.concatenate(out)
+    pad = -len(blk) % 1024
+    return np.concatenate([blk, np.zeros((pad, 32), np.uint16)])
+
+
+@pytest.fixture(scope="module")
+def exhaustive():
+    blk = exhaustive_blocks()
+    print_case("exhaustive quantisation blocks", blk.shape[0])
+    rc, rs = orc.mx_quantize_rows(orc.to_f64(blk))
+    return blk, rc, rs.reshape(-1)
+
+
+@pytest.mark.timeout(300)
+def test_quantize_rows_every_bf16_at_every_scale(exhaustive):
+    blk, rc, rs = exhaustive
+    C = 1024                                       # 32 blocks per row
+    x = np.ascontiguousarray(blk.reshape(-1, C))
+    codes, scales = moe.mxfp8_quantize(to_dev(x), 0)
+    moe.debug_sync()
+    np.testing.assert_array_equal(scales.cpu().numpy().reshape(-1), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy().reshape(-1, 32), rc)
+
+
+@pytest.mark.timeout(300)
+def test_quantize_cols_every_bf16_at_every_scale(exhaustive):
+    blk, rc, rs = exhaustive
+    C = 1024                                       # block g*C + c -> column c
+    g = blk.shape[0] // C
+    x = np.ascontiguousarray(blk.reshape(g, C, 32).transpose(0, 2, 1).reshape(g * 32, C))
+    codes, scales, _ = moe.mxfp8_quantize(to_dev(x), 1)
+    moe.debug_sync()
+    np.testing.assert_array_equal(
+        codes.cpu().numpy(), rc.reshape(g, C, 32).transpose(1, 0, 2).reshape(C, g * 32))
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs.reshape(g, C).T)
+
+
 def _mx_case(name):
     wl = synth.WORKLOADS[name]
     inp = synth.make_inputs(wl)
