@@ -84,26 +84,6 @@ __device__ __forceinline__ void store_staged(const uint16_t *l, uint16_t *dst,
   }
 }
 
-// Load rows [0, NROWS) of src (bf16, row pitch ld) into a [NROWS][W] region;
-// rows past the tile's valid rows, or columns past N, read as zero.
-template <int W, int NROWS>
-__device__ __forceinline__ void load_staged(uint16_t *l, const uint16_t *src,
-                                               int64_t ld, int64_t col0, int N,
-                                               int64_t grow0, int arow0,
-                                               int rows, int lane) {
-  constexpr int LPR = W / 8;
-  constexpr int RPI = 64 / LPR;
-#pragma unroll
-  for (int it = 0; it < NROWS / RPI; ++it) {
-    const int r = it * RPI + lane / LPR;
-    const int c8 = (lane % LPR) * 8;
-    uint4 v = make_uint4(0u, 0u, 0u, 0u);
-    if (arow0 + r < rows && col0 + c8 < N)
-      v = *(const uint4 *)(src + (grow0 + r) * ld + col0 + c8);
-    *(uint4 *)(l + r * W + st_col<W>(r, c8)) = v;
-  }
-}
-
 // Tile of workgroup `bid` when every tile has its own workgroup and the
 // grid is launched for an upper bound of `total` (the real count lives on
 // the device).  Workgroups are handed to the 8 XCDs round-robin by id and,

@@ -66,6 +66,23 @@ __device__ __forceinline__ void mx_load_lds16(uint32_t lds_base, const void *g) 
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                :: "s"(lds_base), "v"(g) : "memory");
 }
+// A pointer the wavefront holds in common, in scalar registers.
+template <typename T>
+__device__ __forceinline__ T *mx_uniform(T *q) {
+  const uint64_t v = (uint64_t)(uintptr_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The same 16 bytes per lane from sbase + voff: a uniform base and a 32-bit
+// byte offset per lane (the instruction's SGPR-address form).
+__device__ __forceinline__ void mx_load_lds16_so(uint32_t lds_base,
+                                                 const void *sbase,
+                                                 uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :: "s"(lds_base), "v"(voff), "s"(sbase) : "memory");
+}
 __device__ __forceinline__ void mx_load_lds4(uint32_t lds_base, const void *g) {
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off"
                :: "s"(lds_base), "v"(g) : "memory");
@@ -138,17 +155,44 @@ __device__ __forceinline__ int mx_brow(int nt, int j, int N, bool &up) {
 // Region rows are 128 bytes (64 bf16) for SwiGLU outputs, 256 bytes (128
 // bf16) for the SwiGLU-backward g, u, dg, du tiles.
 
+// g and u rows [arow0, arow0 + NROWS) of a tile (tile-relative; g_base and
+// u_base point at the tile's row 0 and first column, both uniform) into a
+// wavefront's staged [NROWS][128] regions at LDS byte addresses lg, lu
+// (st_col<128> layout) by direct global -> LDS loads, four 256-byte rows per
+// instruction: lane i fills region row 4*it + i/16 at column position
+// 8*(i%16), so it reads the column that st_col maps there.  Rows past the
+// tile (`rows`) read the tile's last row (their outputs are never stored):
+// no branches, and one 32-bit offset per row serves both loads, so every
+// load is in flight at once.  The launcher keeps 256 * ld * 2 below 2^32.
+// The caller waits on vmcnt before reading the regions.
+template <int NROWS>
+__device__ __forceinline__ void mx_load_gu_staged(uint32_t lg, uint32_t lu,
+                                                  const uint16_t *g_base,
+                                                  const uint16_t *u_base,
+                                                  int64_t ld, int arow0,
+                                                  int rows, int lane) {
+#pragma unroll
+  for (int it = 0; it < NROWS / 4; ++it) {
+    const int r = it * 4 + (lane >> 4);
+    const int c = ((lane & 15) * 8) ^ ((it & 1) * 32);   // st_col<128>(r, .)
+    const int trow = min(arow0 + r, rows - 1);
+    const uint32_t voff = (uint32_t)(trow * (uint32_t)ld + (uint32_t)c) * 2u;
+    mx_load_lds16_so(lg + (uint32_t)(it * 1024), g_base, voff);
+    mx_load_lds16_so(lu + (uint32_t)(it * 1024), u_base, voff);
+  }
+}
+
 // SwiGLU forward, one 32-row block: block 2q holds g and block 2q+1 the
-// matching u in every lane.
+// matching u in every lane.  s_reg: lane l holds the routing scale of
+// region row (mloc & 64) + l.
 template <int NB>
 __device__ __forceinline__ void mx_swiglu_stage(
-    const MxArgs &p, const f32x16 (&am)[NB], int mloc, int lane, int arow0,
-    int rows, int row0, uint16_t *l0, uint16_t *l1, int phase) {
+    const f32x16 (&am)[NB], int mloc, int lane, float s_reg, uint16_t *l0,
+    uint16_t *l1, int phase) {
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int row = mloc + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    const bool ok = arow0 + row < rows;
-    const float s = (phase == 0 && ok && p.row_scale) ? p.row_scale[row0 + arow0 + row] : 1.f;
+    const float s = phase == 0 ? __shfl(s_reg, row & 63, 64) : 1.f;
 #pragma unroll
     for (int q = 0; q < NB / 2; ++q) {
       const float g = am[2 * q][r], u = am[2 * q + 1][r];
@@ -178,21 +222,54 @@ __device__ __forceinline__ void mx_plain_stage(const f32x16 (&am)[NB], int mloc,
   }
 }
 
+// Lane-xor exchanges inside 32-lane groups: ds_swizzle in bit mode
+// (and-mask 31, xor-mask m) for 16, 8, 4; DPP quad permutations for 2, 1.
+template <int M>
+__device__ __forceinline__ float mx_xor32(float v) {
+  const int x = __builtin_bit_cast(int, v);
+  int y;
+  if constexpr (M == 1) y = __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);
+  else if constexpr (M == 2) y = __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);
+  else y = __builtin_amdgcn_ds_swizzle(x, (M << 10) | 0x1F);
+  return __builtin_bit_cast(float, y);
+}
+
+// Sums v[0..15] over the 32 lanes of each wavefront half by reduce-scatter:
+// each exchange step halves the values a lane keeps (the half picked by its
+// lane bit) and adds its partner's other half, 8 + 4 + 2 + 1 + 1 exchanges in
+// all.  Returns in lane l the total of v[((l & 31) >> 1)].
+__device__ __forceinline__ float mx_sum16_over32(const float (&v)[16], int lane) {
+  const bool b4 = lane & 16, b3 = lane & 8, b2 = lane & 4, b1 = lane & 2;
+  float w[8], x[4], y[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    w[j] = (b4 ? v[j + 8] : v[j]) + mx_xor32<16>(b4 ? v[j] : v[j + 8]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    x[j] = (b3 ? w[j + 4] : w[j]) + mx_xor32<8>(b3 ? w[j] : w[j + 4]);
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    y[j] = (b2 ? x[j + 2] : x[j]) + mx_xor32<4>(b2 ? x[j] : x[j + 2]);
+  const float z = (b1 ? y[1] : y[0]) + mx_xor32<2>(b1 ? y[0] : y[1]);
+  return z + mx_xor32<1>(z);
+}
+
 // SwiGLU backward of one 32-row block against the staged g, u of its rows
 // (region rows `mloc` relative): dg, du replace g, u in place; the partial
 // ds of each row (over this wavefront's 128 columns) goes to ds_part.
+// s_reg: lane l holds the routing scale of wavefront row (mrow & 64) + l.
 template <int BN, int WN, int NB>
 __device__ __forceinline__ void mx_swiglu_bwd_stage(
     const MxArgs &p, const f32x16 (&am)[NB], int mloc, int mrow, int lane,
-    int arow0, int rows, int row0, int nt, int wn, uint16_t *lg, uint16_t *lu) {
+    int arow0, int rows, int row0, int nt, int wn, float s_reg, uint16_t *lg,
+    uint16_t *lu) {
+  float part[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
     const int row = mloc + rr;                 // region row
-    const bool ok = arow0 + mrow + rr < rows;  // tile row valid
-    const int64_t grow = row0 + arow0 + mrow + rr;
-    const float s = (ok && p.row_scale) ? p.row_scale[grow] : 1.f;
-    float part = 0.f;
+    const float s = __shfl(s_reg, (mrow + rr) & 63, 64);
+    part[r] = 0.f;
 #pragma unroll
     for (int n = 0; n < NB; ++n) {
       const int o = row * 128 + st_col<128>(row, n * 32 + (lane & 31));
@@ -204,21 +281,23 @@ __device__ __forceinline__ void mx_swiglu_bwd_stage(
       const float dsl = sg * (1.f + g * (1.f - sg));
       lg[o] = (uint16_t)f32_to_bf16_bits(da * s * u * dsl);
       lu[o] = (uint16_t)f32_to_bf16_bits(da * s * sl);
-      part += da * sl * u;
+      part[r] += da * sl * u;
     }
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
-    if ((lane & 31) == 0 && ok) p.ds_part[grow * (p.NT * WN) + nt * WN + wn] = part;
   }
+  const float tot = mx_sum16_over32(part, lane);
+  const int r = (lane & 31) >> 1;
+  const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+  if ((lane & 1) == 0 && arow0 + mrow + rr < rows)
+    p.ds_part[(int64_t)(row0 + arow0 + mrow + rr) * (p.NT * WN) + nt * WN + wn] = tot;
 }
 
 template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES, int BKB>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
-  // BKB: K values (code bytes) per stage, 128 or 64.  A stage always carries
-  // the scale dword of the 128 values it lies in (a 64-value stage uses half).
-  static_assert(BKB == 128 || BKB == 64, "stage width");
+  // BKB: K values (code bytes) per stage; a stage carries, for every A and B
+  // row, its 128 codes and the scale dword of their four 32-value blocks.
+  // The K loop below is pipelined for two such stages.
+  static_assert(BKB == 128 && STAGES == 2, "two stages of 128 K values");
   constexpr int CPR = BKB / 16;                        // 16-byte chunks per row
-  constexpr int KK = BKB / 64;                         // 64-value MFMA steps
   constexpr int WTM = BM / WM, WTN = BN / WN, MB = WTM / 32, NB = WTN / 32;
   constexpr int CODE_CHUNKS = (BM + BN) * CPR;
   constexpr int LC = CODE_CHUNKS / 256;                // code loads per thread
@@ -226,11 +305,12 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   constexpr int L = LC + LS;
   constexpr int SCALE_OFF = CODE_CHUNKS * 16;          // bytes
   constexpr int STAGE_BYTES = SCALE_OFF + (BM + BN) * 4;
-  constexpr int NMF = KK * MB * NB;                    // MFMAs per stage
   static_assert(WM * WN == 4 && MB >= 1 && MB <= 4 && NB >= 1, "tile");
   static_assert(CODE_CHUNKS % 256 == 0 && (BM + BN) % 256 == 0, "load split");
-  static_assert((STAGES - 2) * L <= 63, "vmcnt range");
+  static_assert(L <= 63, "vmcnt range");
   static_assert(STAGE_BYTES % 16 == 0, "stage alignment");
+  static_assert(STAGES * STAGE_BYTES >= WM * WN * WTM * WTN * 2,
+                "the ring must hold every wavefront's epilogue region");
   __shared__ uint4 smem[STAGES * STAGE_BYTES / 16];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -264,50 +344,80 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     k0 = p.kseg[e];
     KT = (p.kseg[e + 1] - k0) / BKB;
   }
+  // The tile's coordinates come from memory the kernel cannot prove
+  // unchanged; say that they are uniform, so that the addressing below
+  // stays in scalar registers.
+  e = __builtin_amdgcn_readfirstlane(e);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  rows = __builtin_amdgcn_readfirstlane(rows);
+  nt = __builtin_amdgcn_readfirstlane(nt);
+  k0 = __builtin_amdgcn_readfirstlane(k0);
+  KT = __builtin_amdgcn_readfirstlane(KT);
 
-  // Sources of this thread's loads.  Code load i (< LC) moves chunks
-  // q = (wid*LC + i)*64 + lane of the stage; scale load j moves the dwords of
-  // rows d = (wid*LS + j)*64 + lane.  Rows < BM are A rows, the rest B rows.
-  // gsrc1: the B1 source of a B row past the K split (KSPLIT), else null.
-  const char *gsrc[L];
-  const char *gsrc1[L];
+  // ---- load sources ------------------------------------------------------
+  // Code load i moves chunks q = (wid*LC + i)*64 + lane of a stage: stage row
+  // q / CPR (eight 128-byte rows per instruction), chunk q % CPR.  Rows < BM
+  // are A rows (tile rows), the rest B rows (output columns).  The eight rows
+  // of one instruction are all A or all B rows, and for SwiGLU all gate or
+  // all up rows, so the instruction reads from one uniform base plus a 32-bit
+  // per-lane offset below 256 row pitches (the stage's K offset is added to
+  // it).  Past the K split (KSPLIT) B rows read B1 at K - ksplit.
+  // Scale load j moves the dword of row (wid*LS + j)*64 + lane through a
+  // per-lane pointer; past the K split a uniform delta moves B rows to B1.
+  const int colstep = EPI == MX_EPI_SWIGLU ? BN / 2 : BN;
+  const int64_t bcol0 = (int64_t)nt * colstep;
+  const char *baseA = (const char *)p.A + (int64_t)row0 * p.lda + k0;
+  const int64_t gB = (int64_t)e * p.b_stride + bcol0 * p.ldb + k0;
+  const char *baseB0 = (const char *)p.B0 + gB;
+  const char *baseB1 = (const char *)p.B1 + gB;
+  const char *baseBk = p.ksplit ? (const char *)p.B1 + gB - p.ksplit : baseB0;
+  uint32_t voff[LC];
+  const char *blo[LC], *bhi[LC];      // bases below / past the K split
 #pragma unroll
-  for (int i = 0; i < L; ++i) {
-    const bool code = i < LC;
-    const int q = code ? (wid * LC + i) * 64 + lane : 0;
-    const int row = code ? q / CPR : (wid * LS + (i - LC)) * 64 + lane;
-    gsrc1[i] = nullptr;
+  for (int i = 0; i < LC; ++i) {
+    const int row8 = (wid * LC + i) * (64 / CPR);            // first stage row
+    const bool up = EPI == MX_EPI_SWIGLU && ((row8 - BM) & 63) >= 32;
+    blo[i] = mx_uniform(row8 < BM ? baseA : up ? baseB1 : baseB0);
+    bhi[i] = mx_uniform(row8 < BM ? baseA : baseBk);
+    const int q = (wid * LC + i) * 64 + lane;
+    const int row = q / CPR, c = q % CPR;
     if (row < BM) {
-      const int64_t r = row0 + min(row, rows - 1);
-      gsrc[i] = code ? (const char *)p.A + r * p.lda + k0 + mx_swz<CPR>(row, q % CPR) * 16
-                     : (const char *)p.As + r * p.ldas + k0 / 32;
+      voff[i] = (uint32_t)(min(row, rows - 1) * p.lda) + (uint32_t)(mx_swz<CPR>(row, c) * 16);
     } else {
       bool up;
       const int col = mx_brow<EPI, BN>(nt, row - BM, p.N, up);
-      const int64_t g = (int64_t)e;
-      if (code) {
-        const int64_t ro = g * p.b_stride + (int64_t)col * p.ldb + k0 + mx_swz<CPR>(row, q % CPR) * 16;
-        gsrc[i] = (const char *)(up ? p.B1 : p.B0) + ro;
-        if (p.ksplit) gsrc1[i] = (const char *)p.B1 + ro - p.ksplit;
-      } else {
-        const int64_t ro = g * p.bs_stride + (int64_t)col * p.ldbs + k0 / 32;
-        gsrc[i] = (const char *)(up ? p.B1s : p.B0s) + ro;
-        if (p.ksplit) gsrc1[i] = (const char *)p.B1s + ro - p.ksplit / 32;
-      }
+      voff[i] = (uint32_t)((col - bcol0) * p.ldb) + (uint32_t)(mx_swz<CPR>(row, c) * 16);
+    }
+  }
+  const char *sptr[LS];
+  const int64_t sdelta = p.ksplit ? ((const char *)p.B1s - (const char *)p.B0s) - p.ksplit / 32 : 0;
+#pragma unroll
+  for (int j = 0; j < LS; ++j) {
+    const int row = (wid * LS + j) * 64 + lane;
+    if (row < BM) {
+      sptr[j] = (const char *)p.As + (int64_t)(row0 + min(row, rows - 1)) * p.ldas + k0 / 32;
+    } else {
+      bool up;
+      const int col = mx_brow<EPI, BN>(nt, row - BM, p.N, up);
+      sptr[j] = (const char *)(up ? p.B1s : p.B0s) + (int64_t)e * p.bs_stride +
+                (int64_t)col * p.ldbs + k0 / 32;
     }
   }
 
-  // Issue load i of stage ks into ring buffer b (i is a compile-time index
-  // once unrolled; ks and b are uniform).
+  // Load i of stage ks into ring buffer b (i a compile-time index once
+  // unrolled; ks and b uniform).
   auto issue = [&](int i, int b, int ks) {
     const uint32_t sb = lds0 + (uint32_t)(b * STAGE_BYTES);
     const bool hi = p.ksplit && ks * BKB >= p.ksplit;
-    const char *src = (hi && gsrc1[i]) ? gsrc1[i] : gsrc[i];
-    if (i < LC)
-      mx_load_lds16(sb + (uint32_t)((wid * LC + i) * 1024), src + (int64_t)ks * BKB);
-    else
-      mx_load_lds4(sb + (uint32_t)(SCALE_OFF + (wid * LS + (i - LC)) * 256),
-                   src + (int64_t)(ks * BKB / 128) * 4);
+    if (i < LC) {
+      mx_load_lds16_so(sb + (uint32_t)((wid * LC + i) * 1024), hi ? bhi[i] : blo[i],
+                       voff[i] + (uint32_t)(ks * BKB));
+    } else {
+      const int j = i - LC;
+      const bool isB = (wid * LS + j) * 64 >= BM;
+      mx_load_lds4(sb + (uint32_t)(SCALE_OFF + (wid * LS + j) * 256),
+                   sptr[j] + (int64_t)(ks * BKB / 128) * 4 + (hi && isB ? sdelta : 0));
+    }
   };
 
   f32x16 acc[MB][NB];
@@ -318,80 +428,127 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
 
-  // Prologue: stages 0 .. STAGES-2 (clamped to the last stage).
-#pragma unroll
-  for (int st = 0; st < STAGES - 1; ++st) {
-#pragma unroll
-    for (int i = 0; i < L; ++i) issue(i, st, min(st, KT - 1));
-  }
-
   const int arow0 = wm * WTM, brow0 = wn * WTN;
   const int h = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    // Stage kt has landed once (STAGES-2)*L later loads of this wavefront
-    // are in flight; the barrier also frees the buffer refilled below.
-    mx_wait_barrier<(STAGES - 2) * L>();
-    const int ks = min(kt + STAGES - 1, KT - 1);
-    const int bnext = (kt + STAGES - 1) % STAGES;
 
-    const char *S = (const char *)smem + (kt % STAGES) * STAGE_BYTES;
-    const uint4 *As = (const uint4 *)S, *Bs = As + BM * CPR;
-    const uint32_t *Ssc = (const uint32_t *)(S + SCALE_OFF);
-    uint32_t sa[MB], sbv[NB];
+  // Fragments of one 64-value step: A block m and B block n.  Operand layout
+  // of the 32x32x64 f8 instruction: lane half h holds K [16h, 16h+16) in its
+  // first four registers and [32+16h, 48+16h) in the last four; block b (K
+  // [32b, 32b+32)) takes its scale from lane half b.  In 16-byte chunks of
+  // the 64-value step: h and 2 + h.
+  auto read_a = [&](int b, int kk, i32x8 &dst, int m) {
+    const uint4 *As = (const uint4 *)((const char *)smem + b * STAGE_BYTES);
+    const int row = arow0 + m * 32 + (lane & 31);
+    const uint4 v0 = As[row * CPR + mx_swz<CPR>(row, 4 * kk + h)];
+    const uint4 v1 = As[row * CPR + mx_swz<CPR>(row, 4 * kk + 2 + h)];
+    dst = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+  };
+  auto read_b = [&](int b, int kk, i32x8 &dst, int n) {
+    const uint4 *Bs = (const uint4 *)((const char *)smem + b * STAGE_BYTES) + BM * CPR;
+    const int row = brow0 + n * 32 + (lane & 31);
+    const uint4 v0 = Bs[row * CPR + mx_swz<CPR>(row, 4 * kk + h)];
+    const uint4 v1 = Bs[row * CPR + mx_swz<CPR>(row, 4 * kk + 2 + h)];
+    dst = i32x8{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
+                (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+  };
+  // Scale dwords of a stage (four E8M0 bytes: the 32-value blocks of its 128
+  // values) for this lane's A rows and B rows.
+  auto read_s = [&](int b, uint32_t (&sa)[MB], uint32_t (&sbv)[NB]) {
+    const uint32_t *Ssc = (const uint32_t *)((const char *)smem + b * STAGE_BYTES + SCALE_OFF);
 #pragma unroll
     for (int m = 0; m < MB; ++m) sa[m] = Ssc[arow0 + m * 32 + (lane & 31)];
 #pragma unroll
     for (int n = 0; n < NB; ++n) sbv[n] = Ssc[BM + brow0 + n * 32 + (lane & 31)];
+  };
+  // Order in which a step consumes fragments (m-major MFMAs): A0, B0..B(NB-1),
+  // A1..A(MB-1).  read_next(k) reads the k-th of them into (af, bf).
+  auto read_next = [&](int k, int b, int kk, i32x8 (&af)[MB], i32x8 (&bf)[NB]) {
+    if (k == 0) read_a(b, kk, af[0], 0);
+    else if (k <= NB) read_b(b, kk, bf[k - 1], k - 1);
+    else read_a(b, kk, af[k - NB], k - NB);
+  };
+  constexpr int NFR = MB + NB;                          // fragments per step
 
-    // first scale byte of this stage in its 128-value dword
-    const int sb0 = (kt * BKB % 128) / 32;
+  // Prologue: stages 0 and 1 (clamped) in flight, stage 0 landed, its scales
+  // and first step's fragments read.
+  i32x8 af0[MB], bf0[NB], af1[MB], bf1[NB];
+  uint32_t sa[MB], sbv[NB], sa_n[MB], sbv_n[NB];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      // Operand layout of the 32x32x64 f8 instruction: lane half h holds
-      // K [16h, 16h+16) in its first four registers and [32+16h, 48+16h)
-      // in the last four; block b (K [32b, 32b+32)) takes its scale from
-      // lane half b.  In 16-byte chunks of the 64-value step: h and 2 + h.
-      const int c0 = 4 * kk + h, c1 = 4 * kk + 2 + h;
-      i32x8_t af[MB], bfr[NB];
+  for (int i = 0; i < L; ++i) issue(i, 0, 0);
 #pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        const int row = arow0 + m * 32 + (lane & 31);
-        const uint4 v0 = As[row * CPR + mx_swz<CPR>(row, c0)];
-        const uint4 v1 = As[row * CPR + mx_swz<CPR>(row, c1)];
-        af[m] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                        (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
-      }
+  for (int i = 0; i < L; ++i) issue(i, 1, min(1, KT - 1));
+  mx_wait_barrier<L>();
+  read_s(0, sa, sbv);
+#pragma unroll
+  for (int k = 0; k < NFR; ++k) read_next(k, 0, 0, af0, bf0);
+
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = kt & 1, nb = cur ^ 1;
+    const int ks = min(kt + 2, KT - 1);
+    // Step 0 on (af0, bf0); the fragments of step 1 are read meanwhile.
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
       for (int n = 0; n < NB; ++n) {
-        const int row = brow0 + n * 32 + (lane & 31);
-        const uint4 v0 = Bs[row * CPR + mx_swz<CPR>(row, c0)];
-        const uint4 v1 = Bs[row * CPR + mx_swz<CPR>(row, c1)];
-        bfr[n] = i32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w,
-                         (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+        const int f = m * NB + n;
+        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            af0[m], bf0[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> (8 * h)) & 0xffu),
+            0, (int)((sbv[n] >> (8 * h)) & 0xffu));
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k = 0; k < NFR; ++k)
+          if (f == k + k / 2) read_next(k, cur, 1, af1, bf1);
+        __builtin_amdgcn_sched_barrier(0);
       }
-      const int sh = 8 * (sb0 + 2 * kk + h);
+    // Step 1 on (af1, bf1).  After its first two MFMAs: stage kt+1 has landed
+    // (own loads, then the barrier for everyone's) and nobody reads buffer
+    // `cur` any more; so the loads of stage kt+2 go into it, and the scales
+    // and first fragments of stage kt+1 are read from buffer nb.
 #pragma unroll
-      for (int m = 0; m < MB; ++m)
+    for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int n = 0; n < NB; ++n) {
-          acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af[m], bfr[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> sh) & 0xffu),
-              0, (int)((sbv[n] >> sh) & 0xffu));
-          const int f = (kk * MB + m) * NB + n;
-#pragma unroll
-          for (int i = f * L / NMF; i < (f + 1) * L / NMF; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            issue(i, bnext, ks);
-            __builtin_amdgcn_sched_barrier(0);
-          }
+      for (int n = 0; n < NB; ++n) {
+        const int g = m * NB + n;
+        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            af1[m], bf1[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> (8 * (2 + h))) & 0xffu),
+            0, (int)((sbv[n] >> (8 * (2 + h))) & 0xffu));
+        __builtin_amdgcn_sched_barrier(0);
+        if (g == 1) {
+          mx_wait_barrier<0>();
+          read_s(nb, sa_n, sbv_n);
         }
-    }
+        if (g >= 2) {
+          constexpr int SL = MB * NB - 2;                 // slots for the rest
+#pragma unroll
+          for (int i = 0; i < L; ++i)
+            if (i * SL / L == g - 2) issue(i, cur, ks);
+#pragma unroll
+          for (int k = 0; k < NFR; ++k)
+            if (g - 2 == k) read_next(k, nb, 0, af0, bf0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) sa[m] = sa_n[m];
+#pragma unroll
+    for (int n = 0; n < NB; ++n) sbv[n] = sbv_n[n];
   }
   mx_wait_barrier<0>();
 
   // Epilogues, one 32-row block at a time with constant block indices (the
   // accumulators stay in registers).
   uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * WTN);   // per-wavefront region
+  // Routing scales of the wavefront's 128 rows, lane l: rows l and 64 + l.
+  // Loaded once here: read inside the epilogue loops, each load would wait
+  // behind the previous row's ds_part store (the pointers may alias).
+  float s_lo = 1.f, s_hi = 1.f;
+  if constexpr (EPI != MX_EPI_BF16) {
+    if (p.row_scale) {
+      if (arow0 + lane < rows) s_lo = p.row_scale[row0 + arow0 + lane];
+      if (arow0 + 64 + lane < rows) s_hi = p.row_scale[row0 + arow0 + 64 + lane];
+    }
+  }
   if constexpr (EPI == MX_EPI_SWIGLU) {
     static_assert(WTM == 128 && WTN == 128, "SwiGLU staging expects 128x128 wavefront tiles");
     // region: two [128][64] arrays (a | g, then u)
@@ -401,7 +558,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
 #pragma unroll
     for (int phase = 0; phase < 2; ++phase) {
 #define MX_SW_BLOCK(m) \
-      if constexpr (MB > (m)) mx_swiglu_stage<NB>(p, acc[m], (m) * 32, lane, arow0, rows, row0, l0, l1, phase);
+      if constexpr (MB > (m)) mx_swiglu_stage<NB>(acc[m], (m) * 32, lane, (m) < 2 ? s_lo : s_hi, l0, l1, phase);
       MX_SW_BLOCK(0) MX_SW_BLOCK(1) MX_SW_BLOCK(2) MX_SW_BLOCK(3)
 #undef MX_SW_BLOCK
       __syncthreads();
@@ -417,20 +574,22 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     static_assert(WTM == 128 && WTN == 128 && MB == 4, "staging expects 128x128 wavefront tiles");
     // region: g and u of 64 rows x 128 columns, two halves of the 128 rows
     uint16_t *lg = lw, *lu = lw + 64 * 128;
+    const uint32_t lgb = lds0 + (uint32_t)(wid * WTM * WTN * 2);
+    const uint32_t lub = lgb + 64 * 128 * 2;
     const int64_t col0 = (int64_t)nt * BN + brow0;
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       const int64_t grow0 = row0 + arow0 + half * 64;
       const int ar0 = arow0 + half * 64;
-      load_staged<128, 64>(lg, p.gu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
-      load_staged<128, 64>(lu, p.gu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
-      __syncthreads();
+      const uint16_t *gb = mx_uniform(p.gu + (int64_t)row0 * p.ldgu + col0);
+      mx_load_gu_staged<64>(lgb, lub, gb, mx_uniform(gb + p.N), p.ldgu, ar0, rows, lane);
+      mx_wait_barrier<0>();
       if (half == 0) {
-        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[0], 0, 0, lane, arow0, rows, row0, nt, wn, lg, lu);
-        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[1], 32, 32, lane, arow0, rows, row0, nt, wn, lg, lu);
+        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[0], 0, 0, lane, arow0, rows, row0, nt, wn, s_lo, lg, lu);
+        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[1], 32, 32, lane, arow0, rows, row0, nt, wn, s_lo, lg, lu);
       } else {
-        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[2], 0, 64, lane, arow0, rows, row0, nt, wn, lg, lu);
-        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[3], 32, 96, lane, arow0, rows, row0, nt, wn, lg, lu);
+        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[2], 0, 64, lane, arow0, rows, row0, nt, wn, s_hi, lg, lu);
+        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[3], 32, 96, lane, arow0, rows, row0, nt, wn, s_hi, lg, lu);
       }
       __syncthreads();
       store_staged<128, 64>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
@@ -503,6 +662,9 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
   mx_plan_kernel<<<1, 1024, 0, s>>>(d.offsets, d.G, kMxBM, p.NT, d.tile_ws);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // SwiGLU backward: 32-bit byte offsets within a tile's rows of g|u.
+  if (epi == MX_EPI_SWIGLU_BWD && (int64_t)kMxBM * d.ldgu * 2 >= (1ll << 32))
+    return hipErrorInvalidValue;
   const int64_t max_tiles = ((d.R_cap + kMxBM - 1) / kMxBM + d.G) * (int64_t)p.NT;
   if (epi == MX_EPI_SWIGLU) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU>(p, max_tiles, s);
   else if (epi == MX_EPI_SWIGLU_BWD) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU_BWD>(p, max_tiles, s);
