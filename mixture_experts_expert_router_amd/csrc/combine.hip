@@ -14,18 +14,40 @@ __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const float *__restrict__ w, int64_t T, int k, int64_t vecs,
     uint4 *__restrict__ out) {
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
+    // First local slot of the token (uniform); none -> a zero row.
+    int rdef = -1;
+    for (int j = 0; j < k && rdef < 0; ++j) rdef = inv[t * k + j];
+    rdef = __builtin_amdgcn_readfirstlane(rdef);
+    if (rdef < 0) {
+      for (int64_t c = threadIdx.x; c < vecs; c += blockDim.x)
+        out[t * vecs + c] = make_uint4(0u, 0u, 0u, 0u);
+      continue;
+    }
     for (int64_t c = threadIdx.x; c < vecs; c += blockDim.x) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < k; ++j) {
-        const int r = inv[t * k + j];
-        if (r < 0) continue;
-        const float cj = w ? w[t * k + j] : 1.f;
-        const uint4 v = y[(int64_t)r * vecs + c];
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+      // Slots in groups of four, without branches: a non-local slot loads
+      // the token's first local row and its sum is dropped by a select, so
+      // the four row loads are in flight together.  Sums run in slot order.
+      for (int j0 = 0; j0 < k; j0 += 4) {
+        int r[4];
+        uint4 v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          acc[2 * q] = fmaf(cj, bf16_bits_to_f32(u[q] & 0xffffu), acc[2 * q]);
-          acc[2 * q + 1] = fmaf(cj, bf16_bits_to_f32(u[q] >> 16), acc[2 * q + 1]);
+          r[q] = j0 + q < k ? inv[t * k + j0 + q] : -1;
+          v[q] = y[(int64_t)(r[q] >= 0 ? r[q] : rdef) * vecs + c];
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const bool ok = r[q] >= 0;
+          const float cj = (ok && w) ? w[t * k + j0 + q] : 1.f;
+          const uint32_t u[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float lo = fmaf(cj, bf16_bits_to_f32(u[e] & 0xffffu), acc[2 * e]);
+            const float hi = fmaf(cj, bf16_bits_to_f32(u[e] >> 16), acc[2 * e + 1]);
+            acc[2 * e] = ok ? lo : acc[2 * e];
+            acc[2 * e + 1] = ok ? hi : acc[2 * e + 1];
+          }
         }
       }
       uint4 o;

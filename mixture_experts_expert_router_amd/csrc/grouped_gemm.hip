@@ -232,6 +232,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int LA = BM * CPR / 256;           // of which A rows
   static_assert(WM * WN == 4, "four wavefronts");
   static_assert(MB >= 1 && NB >= 1, "wave tile is a multiple of 32x32");
+  static_assert(EPI != EPI_SWIGLU || NB % 2 == 0,
+                "SwiGLU pairs a gate block with the up block next to it");
   static_assert(BM * CPR % 256 == 0 && BN * CPR % 256 == 0, "load split");
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 2) * L <= 63,
@@ -412,6 +414,9 @@ __global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
 namespace {
 
 // BM, BN, WM, WN, BK, STAGES of the wide large-expert shape.
+#ifndef MOE_NARROW_CFG
+#define MOE_NARROW_CFG 256, 64, 4, 1, 64, 3
+#endif
 #ifndef MOE_WIDE_CFG
 #define MOE_WIDE_CFG 128, 256, 2, 2, 64, 3
 #endif
@@ -440,8 +445,9 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
   constexpr int wide_cfg[6] = {MOE_WIDE_CFG};
   constexpr int WBM = wide_cfg[0], WBN = wide_cfg[1];
   const bool wide = (int64_t)p.G * ntiles(p.N, WBN, sw) >= 2LL * num_cus;
-  const int bm_l = wide ? WBM : 256;
-  const int nt_l = ntiles(p.N, wide ? WBN : 64, sw);
+  constexpr int narrow_cfg[6] = {MOE_NARROW_CFG};
+  const int bm_l = wide ? WBM : narrow_cfg[0];
+  const int nt_l = ntiles(p.N, wide ? WBN : narrow_cfg[1], sw);
   const int nt_s = ntiles(p.N, 256, sw);
   int32_t *pre_s = tile_ws;
   int32_t *pre_l = tile_ws + (p.G + 1);
@@ -463,7 +469,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
   const int64_t max_l = ((R_cap + bm_l - 1) / bm_l + p.G) * (int64_t)nt_l;
   if (wide)
     return launch_one<MOE_WIDE_CFG, EPI>(pl, num_cus, max_l, s);
-  return launch_one<256, 64, 4, 1, 64, 3, EPI>(pl, num_cus, max_l, s);
+  return launch_one<MOE_NARROW_CFG, EPI>(pl, num_cus, max_l, s);
 }
 
 }  // namespace

@@ -39,6 +39,9 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(
 
 // Exclusive scan of hist[n_local * nblk] (expert-major), in place, one block
 // of 1024 threads.  Also writes offsets[0..n_local] and counts[0..n_local).
+// The array is walked in tiles of 4096 entries, four consecutive entries per
+// thread (so a wavefront's loads and stores cover contiguous 1 KB), with a
+// block scan per tile and a running carry.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
     int32_t *__restrict__ hist, int n_local, int nblk,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
@@ -46,27 +49,36 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   __shared__ int32_t offs[4097];
   const int64_t total = (int64_t)n_local * nblk;
   const int tid = threadIdx.x;
-  const int64_t per = (total + 1023) / 1024;
-  const int64_t i0 = min(total, tid * per), i1 = min(total, i0 + per);
-  int32_t s = 0;
-  for (int64_t i = i0; i < i1; ++i) s += hist[i];
-  part[tid] = s;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the 1024 partial sums
-  for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v = tid >= off ? part[tid - off] : 0;
+  int32_t carry = 0;
+  for (int64_t base = 0; base < total; base += 4096) {
+    const int64_t i0 = base + 4 * tid;
+    int32_t v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = i0 + j < total ? hist[i0 + j] : 0;
+    const int32_t s = v[0] + v[1] + v[2] + v[3];
+    part[tid] = s;
     __syncthreads();
-    part[tid] += v;
-    __syncthreads();
+    // Hillis-Steele inclusive scan over the 1024 partial sums
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t x = tid >= off ? part[tid - off] : 0;
+      __syncthreads();
+      part[tid] += x;
+      __syncthreads();
+    }
+    int32_t run = carry + part[tid] - s;  // exclusive prefix of entry i0
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t i = i0 + j;
+      if (i < total) {
+        hist[i] = run;
+        if (i % nblk == 0) offs[i / nblk] = run;
+        run += v[j];
+      }
+    }
+    carry += part[1023];
+    __syncthreads();  // part is rewritten by the next tile
   }
-  int32_t run = part[tid] - s;  // exclusive prefix of this thread's run
-  for (int64_t i = i0; i < i1; ++i) {
-    const int32_t c = hist[i];
-    hist[i] = run;
-    if (i % nblk == 0) offs[i / nblk] = run;
-    run += c;
-  }
-  if (tid == 1023) offs[n_local] = part[1023];
+  if (tid == 0) offs[n_local] = carry;
   __syncthreads();
   for (int e = tid; e <= n_local; e += 1024) {
     offsets[e] = offs[e];
