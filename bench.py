@@ -228,8 +228,6 @@ def run_mx(args, wl, dev):
     L = moe.lib()
     ws_f = torch.empty(L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes(F, n, H, I),
                        dtype=torch.uint8, device=dev)
-    ws_l = torch.empty(L.moe_grouped_linear_mxfp8_workspace_bytes(F, n, I),
-                       dtype=torch.uint8, device=dev)
     ws_b = torch.empty(L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes(F, n, H, I),
                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -251,8 +249,7 @@ def run_mx(args, wl, dev):
                           workspace=ws_f, down=False)
         if timed_ev is not None:
             timed_ev[1].record(stream)
-        moe.grouped_linear_mxfp8(a, pout.offsets, n, mw.wd, mw.wds, y=y,
-                                 workspace=ws_l)
+        moe.mxfp8_mlp_fwd_down(pout.offsets, mw, ws_f, F, y=y)
         moe.mxfp8_mlp_bwd(dy, pout.x_perm, a, gu, pout.offsets, pout.s_perm,
                           mw, dx=dx, ds=ds, dw_gate=dwg, dw_up=dwu,
                           dw_down=dwd, workspace=ws_b)

@@ -255,8 +255,12 @@ int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
  * moe_grouped_gate_up (s_perm may be NULL).
  * Outputs (bf16): a [R_cap, I]; gu [R_cap, 2I] = [g | u] per row (may be
  * NULL; the backward needs it); y [R_cap, H].  Rows < R are written.
+ * The SwiGLU epilogue also writes MX(a) (blocks along I, from the bf16 a it
+ * stores) into the workspace, and the down projection reads those codes
+ * (the fused quantisation of the MXFP8 section).
  * y == NULL stops after a (wd, wds are then not read); the down projection
- * is then moe_grouped_linear_mxfp8 on a.
+ * is then moe_grouped_mlp_mxfp8_fwd_down with the same workspace, or
+ * moe_grouped_linear_mxfp8 on a (same result).
  * workspace: moe_grouped_mlp_mxfp8_fwd_workspace_bytes() bytes.
  * Limits: H % 512 == 0, I % 512 == 0, 1 <= n_local <= 4096.
  */
@@ -271,6 +275,20 @@ int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
                               const uint8_t *wd, const uint8_t *wds, void *a,
                               void *gu, void *y, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_mlp_mxfp8_fwd_down - the down projection of
+ * moe_grouped_mlp_mxfp8_fwd, y = MX(a) . MX(W_down)^T, reading the MX(a)
+ * that a preceding moe_grouped_mlp_mxfp8_fwd call with y == NULL left in
+ * `workspace` (same stream or ordered after it; same offsets, n_local,
+ * R_cap, H, I).  Result identical to the one-call forward.
+ * wd, wds, y as in moe_grouped_mlp_mxfp8_fwd; the same workspace size.
+ */
+int moe_grouped_mlp_mxfp8_fwd_down(const int32_t *offsets, int64_t n_local,
+                                   int64_t R_cap, int64_t H, int64_t I,
+                                   const uint8_t *wd, const uint8_t *wds,
+                                   void *y, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_grouped_linear_mxfp8 - one MXFP8 GroupedLinear on permuted rows (the

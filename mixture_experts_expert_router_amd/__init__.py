@@ -73,6 +73,8 @@ def lib():
         L.moe_grouped_mlp_mxfp8_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64,
                                                 i64, vp, vp, vp, vp, vp, vp,
                                                 vp, vp, vp, vp, sz, vp]
+        L.moe_grouped_mlp_mxfp8_fwd_down.argtypes = [vp, i64, i64, i64, i64, vp,
+                                                     vp, vp, vp, sz, vp]
         L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes.restype = sz
         L.moe_grouped_mlp_mxfp8_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64,
@@ -390,6 +392,17 @@ def mxfp8_mlp_bwd(dy, x_perm, a, gu, offsets, s_perm, mw, dx=None, ds=None,
           _p(dw_gate), _p(dw_up), _p(dw_down), _p(workspace),
           workspace.numel(), _stream(stream))
     return dict(dx=dx, ds=ds, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
+
+
+def mxfp8_mlp_fwd_down(offsets, mw, workspace, R_cap, y=None, stream=None):
+    """The down projection of mxfp8_mlp_fwd(..., down=False) called with
+    `workspace`: reads the MX(a) that call left there."""
+    if y is None:
+        y = torch.empty((R_cap, mw.H), dtype=torch.bfloat16, device=workspace.device)
+    _call("moe_grouped_mlp_mxfp8_fwd_down", _p(offsets), mw.n_local, R_cap,
+          mw.H, mw.I, _p(mw.wd), _p(mw.wds), _p(y), _p(workspace),
+          workspace.numel(), _stream(stream))
+    return y
 
 
 def grouped_linear_mxfp8(x, offsets, n_local, w, w_scales, y=None,

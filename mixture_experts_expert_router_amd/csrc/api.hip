@@ -391,24 +391,31 @@ size_t gate_up_bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H,
   carve_gate_up_bwd(c, R_cap, n_local, H, I);
   return c.used;
 }
-// Fused backward: dgu, then one region that both halves use in turn.
+// Fused backward: dgu (bf16 and MX), then one region that both halves use
+// in turn.
 size_t bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H, int64_t I) {
   Carve c(nullptr);
   c.take<uint16_t>((size_t)R_cap * 2 * I);
+  c.take<uint8_t>((size_t)R_cap * 2 * I);
+  c.take<uint8_t>((size_t)R_cap * (2 * I / 32));
   return c.used + std::max(down_bwd_bytes(R_cap, n_local, H, I),
                            gate_up_bwd_bytes(R_cap, n_local, H, I));
 }
 
 // y = MX(x) . MX(W_e)^T per row segment; the quantisation of x stops at the
 // device row count offsets[G].
+// quantised: ws.xq / ws.xs already hold MX(x) (written by the producing
+// GEMM's epilogue), and x itself is not read.
 hipError_t run_linear(const void *x, const int32_t *offsets, int64_t n_local,
                       int64_t R_cap, int64_t K, int64_t N, const uint8_t *w,
                       const uint8_t *wsc, void *y, const LinWs &ws, int cus,
-                      hipStream_t stream) {
-  hipError_t err = moe::launch_mx_quant_rows(
-      (const uint16_t *)x, R_cap, K, K, ws.xq, K, ws.xs, K / 32,
-      offsets + n_local, stream);
-  if (err != hipSuccess) return err;
+                      hipStream_t stream, bool quantised = false) {
+  if (!quantised) {
+    hipError_t err = moe::launch_mx_quant_rows(
+        (const uint16_t *)x, R_cap, K, K, ws.xq, K, ws.xs, K / 32,
+        offsets + n_local, stream);
+    if (err != hipSuccess) return err;
+  }
   moe::MxGemmDesc e{};
   e.A = ws.xq; e.As = ws.xs; e.lda = K; e.ldas = K / 32;
   e.B0 = w; e.B0s = wsc; e.ldb = K; e.ldbs = K / 32;
@@ -424,7 +431,8 @@ hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
                         int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
                         const uint8_t *wdt, const uint8_t *wdts, void *dgu,
                         float *ds, void *dw_down, const DownBwdWs &w, int cus,
-                        hipStream_t stream) {
+                        hipStream_t stream, uint8_t *dguq = nullptr,
+                        uint8_t *dgus = nullptr) {
   const int G = (int)n_local;
   hipError_t err;
 #define MX_TRY(x) do { err = (x); if (err != hipSuccess) return err; } while (0)
@@ -441,6 +449,8 @@ hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
     d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
     d.row_scale = s_perm; d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
     d.dgu = (uint16_t *)dgu; d.ds_part = w.ds_part; d.ds = ds;
+    // optionally also [dg | du] quantised along 2I, for the dX GEMM
+    d.q = dguq; d.qs = dgus; d.ldq = 2 * I; d.ldqs = 2 * I / 32;
     MX_TRY(moe::launch_mx_rowseg(d, moe::MXE_SWIGLU_BWD, cus, stream));
   }
   // dW_d[e] [H, I] = dY_e^T a_e: blocks of 32 rows inside each expert's
@@ -466,17 +476,24 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
                            const uint8_t *wgt, const uint8_t *wgts,
                            const uint8_t *wut, const uint8_t *wuts, void *dx,
                            void *dw_gate, void *dw_up, const GateUpBwdWs &w,
-                           int cus, hipStream_t stream) {
+                           int cus, hipStream_t stream,
+                           const uint8_t *dguq = nullptr,
+                           const uint8_t *dgus = nullptr) {
   const int G = (int)n_local;
   hipError_t err;
-  // [dg | du] along I (row-wise; blocks never straddle the two halves)
-  MX_TRY(moe::launch_mx_quant_rows((const uint16_t *)dgu, R_cap, 2 * I, 2 * I,
-                                   w.dguq, 2 * I, w.dgus, 2 * I / 32,
-                                   offsets + G, stream));
+  // [dg | du] along I (row-wise; blocks never straddle the two halves),
+  // unless the producing epilogue already wrote it
+  if (!dguq) {
+    MX_TRY(moe::launch_mx_quant_rows((const uint16_t *)dgu, R_cap, 2 * I, 2 * I,
+                                     w.dguq, 2 * I, w.dgus, 2 * I / 32,
+                                     offsets + G, stream));
+    dguq = w.dguq;
+    dgus = w.dgus;
+  }
   // dX = dg W_g + du W_u: one GEMM with K = 2I, B switching at K = I
   {
     moe::MxGemmDesc d{};
-    d.A = w.dguq; d.As = w.dgus; d.lda = 2 * I; d.ldas = 2 * I / 32;
+    d.A = dguq; d.As = dgus; d.lda = 2 * I; d.ldas = 2 * I / 32;
     d.B0 = wgt; d.B0s = wgts; d.B1 = wut; d.B1s = wuts;
     d.ldb = n_local * I; d.ldbs = n_local * I / 32;
     d.b_stride = I; d.bs_stride = I / 32;
@@ -592,12 +609,32 @@ int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
   d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
   d.C = a; d.ldc = I; d.row_scale = s_perm;
   d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
+  // the epilogue also quantises a along I, for the down projection
+  d.q = w.xq; d.qs = w.xs; d.ldq = I; d.ldqs = I / 32;
   hipError_t err = moe::launch_mx_rowseg(d, moe::MXE_SWIGLU, cus, stream);
   if (err != hipSuccess) return MOE_E_HIP;
   if (!y) return MOE_OK;
-  // down: a (quantised along I) x W_d (along I)
+  // down: MX(a) (along I) x W_d (along I)
   return status_of(run_linear(a, offsets, n_local, R_cap, I, H, wd, wds, y, w,
-                              cus, stream));
+                              cus, stream, /*quantised=*/true));
+}
+
+int moe_grouped_mlp_mxfp8_fwd_down(const int32_t *offsets, int64_t n_local,
+                                   int64_t R_cap, int64_t H, int64_t I,
+                                   const uint8_t *wd, const uint8_t *wds,
+                                   void *y, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!offsets || !wd || !wds || !y) return MOE_E_ARG;
+  if (!all_aligned({wd, wds, y})) return MOE_E_ALIGN;
+  if (!workspace || workspace_bytes < fwd_bytes(R_cap, n_local, I))
+    return MOE_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  Carve c(workspace);
+  const LinWs w = carve_lin(c, R_cap, n_local, I);
+  return status_of(run_linear(nullptr, offsets, n_local, R_cap, I, H, wd, wds,
+                              y, w, num_cus(), stream, /*quantised=*/true));
 }
 
 size_t moe_grouped_linear_mxfp8_workspace_bytes(int64_t R_cap,
@@ -713,17 +750,20 @@ int moe_grouped_mlp_mxfp8_bwd(
   if (!aligned16(workspace)) return MOE_E_ALIGN;
   Carve c(workspace);
   uint16_t *dgu = c.take<uint16_t>((size_t)R_cap * 2 * I);
+  // [dg | du] quantised along 2I by the SwiGLU-backward epilogue itself
+  uint8_t *dguq = c.take<uint8_t>((size_t)R_cap * 2 * I);
+  uint8_t *dgus = c.take<uint8_t>((size_t)R_cap * (2 * I / 32));
   Carve shared = c;   // both halves carve the same region, one after the other
   const int cus = num_cus();
   const DownBwdWs wd = carve_down_bwd(c, R_cap, n_local, H, I);
   hipError_t err = run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap, H,
                                 I, wdt, wdts, dgu, ds, dw_down, wd, cus,
-                                stream);
+                                stream, dguq, dgus);
   if (err != hipSuccess) return MOE_E_HIP;
   const GateUpBwdWs wg = carve_gate_up_bwd(shared, R_cap, n_local, H, I);
   return status_of(run_gate_up_bwd(dgu, x_perm, offsets, n_local, R_cap, H, I,
                                    wgt, wgts, wut, wuts, dx, dw_gate, dw_up,
-                                   wg, cus, stream));
+                                   wg, cus, stream, dguq, dgus));
 }
 
 }  // extern "C"

@@ -89,6 +89,10 @@ struct MxGemmDesc {
   float *ds_part;
   float *ds;
   int ksplit;
+  // SwiGLU: MX codes / scales of a along I; SwiGLU backward: of [dg | du]
+  // along 2I (row-wise, blocks of 32 columns).  Null: not written.
+  uint8_t *q, *qs;
+  int64_t ldq, ldqs;
 };
 enum { MXE_BF16 = 0, MXE_SWIGLU = 1, MXE_SWIGLU_BWD = 2 };
 hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,

@@ -1,0 +1,56 @@
+// E8M0 / E4M3 encoding of one MX block on the device, shared by the
+// quantisation kernels and the GEMM epilogues that quantise their output.
+// The rule (OCP Microscaling v1.0, the reading of the BioNeMo MoE article's
+// MXFP8 section): X = floor(log2(max |v|)) - 8, scale byte X + 127, codes
+// RNE(v * 2^-X) in E4M3 saturating at +-448, sign kept on zero.
+#pragma once
+#include "common.hpp"
+
+namespace moe {
+
+// Shared exponent X of a block whose largest magnitude is amax (finite).
+// Blocks with amax < 2^-118 (all-zero ones included) get the floor -127;
+// a finite fp32 amax gives X <= 119, so the scale byte X + 127 <= 246.
+__device__ __forceinline__ int mx_shared_exp(float amax) {
+  if (!(amax >= 0x1p-118f)) return -127;
+  int e;
+  frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
+  return e - 9;
+}
+
+// E4M3 codes of a * 2^nX .. d * 2^nX (nX = -X), packed low byte first.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c,
+                                               float d, int nX) {
+  a = __builtin_amdgcn_fmed3f(ldexpf(a, nX), -448.f, 448.f);
+  b = __builtin_amdgcn_fmed3f(ldexpf(b, nX), -448.f, 448.f);
+  c = __builtin_amdgcn_fmed3f(ldexpf(c, nX), -448.f, 448.f);
+  d = __builtin_amdgcn_fmed3f(ldexpf(d, nX), -448.f, 448.f);
+  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
+  return (uint32_t)r;
+}
+
+// Codes and scale byte of 32 bf16 values (bit patterns, 16 per uint4 pair
+// half): codes[0..7] get the packed bytes, the return value the scale byte.
+__device__ __forceinline__ uint32_t mx_encode32(const uint4 (&in)[4], uint32_t (&codes)[8]) {
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t u[4] = {in[q].x, in[q].y, in[q].z, in[q].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      v[q * 8 + 2 * j] = bf16_bits_to_f32(u[j] & 0xffffu);
+      v[q * 8 + 2 * j + 1] = bf16_bits_to_f32(u[j] >> 16);
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const int X = mx_shared_exp(amax);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    codes[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], -X);
+  return (uint32_t)(X + 127);
+}
+
+}  // namespace moe

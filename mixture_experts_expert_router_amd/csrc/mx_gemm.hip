@@ -32,6 +32,7 @@
 // (fewer barriers per K, twice the MFMAs per stage).  K must be a multiple
 // of 128.
 #include "common.hpp"
+#include "mx_codec.hpp"
 #include "kernels.hpp"
 
 namespace moe {
@@ -53,6 +54,8 @@ struct MxArgs {
   uint16_t *dgu;                // SWIGLU_BWD: dg, du out [rows, ldgu]
   float *ds_part;               // SWIGLU_BWD: [rows, NT * WN]
   int ksplit;                   // KSPLIT: K of the B0 part (0 = none)
+  uint8_t *q, *qs;              // SWIGLU(_BWD): row-wise MX copy of the
+  int64_t ldq, ldqs;            //   bf16 output (null: none)
 };
 
 enum MxMode { MX_ROWSEG = 0, MX_KSEG = 1 };
@@ -154,6 +157,41 @@ __device__ __forceinline__ int mx_brow(int nt, int j, int N, bool &up) {
 // row pieces (8 lanes per 128-byte row), instead of 2-byte stores per lane.
 // Region rows are 128 bytes (64 bf16) for SwiGLU outputs, 256 bytes (128
 // bf16) for the SwiGLU-backward g, u, dg, du tiles.
+
+// Row-wise MX encoding of a staged [NROWS][W] bf16 region (st_col<W>
+// layout: the XOR by 32 columns moves whole 32-column blocks, so every block
+// is 64 contiguous bytes).  Block b of region row r goes to codes
+// q[(grow0 + r) * ldq + col0 + 32 b] and scale qs[(grow0 + r) * ldqs +
+// col0 / 32 + b], for tile rows arow0 + r < rows.  The values are the bf16
+// values staged for the output, so the codes equal a row quantisation of
+// that output.
+template <int W, int NROWS>
+__device__ __forceinline__ void mx_quant_staged(const uint16_t *l, uint8_t *q,
+                                                int64_t ldq, uint8_t *qs,
+                                                int64_t ldqs, int64_t col0,
+                                                int64_t grow0, int arow0,
+                                                int rows, int lane) {
+  static_assert(W % 32 == 0 && (NROWS * W / 32) % 64 == 0, "region");
+  constexpr int BPR = W / 32;                  // blocks per row
+#pragma unroll
+  for (int it = 0; it < NROWS * BPR / 64; ++it) {
+    const int item = it * 64 + lane;
+    const int r = item / BPR, b = item % BPR;
+    const int pb = st_col<W>(r, b * 32) / 32;  // physical block
+    const uint4 *src = (const uint4 *)(l + r * W + pb * 32);
+    uint4 in[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) in[k] = src[k];
+    uint32_t c[8];
+    const uint32_t sb = mx_encode32(in, c);
+    if (arow0 + r < rows) {
+      uint4 *dst = (uint4 *)(q + (grow0 + r) * ldq + col0 + 32 * b);
+      dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
+      dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
+      qs[(grow0 + r) * ldqs + col0 / 32 + b] = (uint8_t)sb;
+    }
+  }
+}
 
 // g and u rows [arow0, arow0 + NROWS) of a tile (tile-relative; g_base and
 // u_base point at the tile's row 0 and first column, both uniform) into a
@@ -564,6 +602,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
       __syncthreads();
       if (phase == 0) {
         store_staged<64, 128>(l0, (uint16_t *)p.C, p.ldc, col0, p.N, grow0, arow0, rows, lane);
+        if (p.q) mx_quant_staged<64, 128>(l0, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, arow0, rows, lane);
         if (p.gu) store_staged<64, 128>(l1, p.gu, p.ldgu, col0, p.N, grow0, arow0, rows, lane);
       } else if (p.gu) {
         store_staged<64, 128>(l0, p.gu, p.ldgu, p.N + col0, 2 * p.N, grow0, arow0, rows, lane);
@@ -594,6 +633,10 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
       __syncthreads();
       store_staged<128, 64>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
       store_staged<128, 64>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      if (p.q) {
+        mx_quant_staged<128, 64>(lg, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, ar0, rows, lane);
+        mx_quant_staged<128, 64>(lu, p.q, p.ldq, p.qs, p.ldqs, p.N + col0, grow0, ar0, rows, lane);
+      }
       __syncthreads();
     }
   } else {
@@ -655,6 +698,7 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
   p.offsets = d.offsets; p.G = d.G; p.N = d.N; p.K = d.K;
   p.C = d.C; p.ldc = d.ldc; p.row_scale = d.row_scale;
   p.gu = d.gu; p.ldgu = d.ldgu; p.dgu = d.dgu; p.ds_part = d.ds_part;
+  p.q = d.q; p.qs = d.qs; p.ldq = d.ldq; p.ldqs = d.ldqs;
   p.ksplit = d.ksplit;
   const int cols = epi == MX_EPI_SWIGLU ? kMxBN / 2 : kMxBN;
   p.NT = (d.N + cols - 1) / cols;

@@ -16,30 +16,9 @@
 // through both kernels and compare the codes with the oracle bit for bit.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "mx_codec.hpp"
 
 namespace moe {
-
-// Shared exponent X of a block whose largest magnitude is amax (finite).
-// Blocks with amax < 2^-118 (all-zero ones included) get the floor -127;
-// a finite fp32 amax gives X <= 119, so the scale byte X + 127 <= 246.
-__device__ __forceinline__ int mx_shared_exp(float amax) {
-  if (!(amax >= 0x1p-118f)) return -127;
-  int e;
-  frexpf(amax, &e);  // amax = m * 2^e, m in [0.5, 1)
-  return e - 9;
-}
-
-// E4M3 codes of a * 2^nX .. d * 2^nX (nX = -X), packed low byte first.
-__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c,
-                                               float d, int nX) {
-  a = __builtin_amdgcn_fmed3f(ldexpf(a, nX), -448.f, 448.f);
-  b = __builtin_amdgcn_fmed3f(ldexpf(b, nX), -448.f, 448.f);
-  c = __builtin_amdgcn_fmed3f(ldexpf(c, nX), -448.f, 448.f);
-  d = __builtin_amdgcn_fmed3f(ldexpf(d, nX), -448.f, 448.f);
-  int r = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  r = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, r, true);
-  return (uint32_t)r;
-}
 
 // axis 0: one thread per block of 32 values along a row.
 //   in [rows, cols] bf16 (row pitch ld_in), codes [rows, ld_codes] (first

@@ -158,6 +158,13 @@ def test_mxfp8_validation(L):
     assert fwd(wsp=None) == E_WS and fwd(wsb=ws - 1) == E_WS
     assert fwd(R=0) == 0
 
+    fd = L.moe_grouped_mlp_mxfp8_fwd_down
+    assert fd(P, 2, 64, 256, 512, P, P, P, P, ws, None) == E_SHAPE
+    assert fd(None, 2, 64, 512, 512, P, P, P, P, ws, None) == E_ARG
+    assert fd(P, 2, 64, 512, 512, P, P, P_ODD, P, ws, None) == E_ALIGN
+    assert fd(P, 2, 64, 512, 512, P, P, P, P, ws - 1, None) == E_WS
+    assert fd(P, 2, 0, 512, 512, P, P, P, P, ws, None) == 0
+
     lb = L.moe_grouped_linear_mxfp8_workspace_bytes(64, 2, 1024)
     assert lb > 0 and L.moe_grouped_linear_mxfp8_workspace_bytes(64, 2, 1000) == 0
     g = L.moe_grouped_linear_mxfp8

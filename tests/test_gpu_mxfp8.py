@@ -230,6 +230,40 @@ def test_mxfp8_backward_gate_up_stage(case):
     assert not bad, bad
 
 
+def test_mxfp8_fused_quantisation_equals_separate(case):
+    """The SwiGLU epilogue quantises a (forward) and [dg | du] (backward) from
+    the bf16 values it stores; the fused calls must therefore equal the
+    stage calls, which quantise the stored bf16 tensors with the row
+    quantiser (pinned to the oracle bit for bit, every bf16 value at every
+    scale), bit for bit: y against the grouped linear on the returned a and
+    against the two-call forward (gate/up, then the down projection from the
+    workspace codes), and dX, dW against the two backward stages."""
+    c, R = case, case["p"]["R"]
+    wl = c["wl"]
+    xt = to_dev(c["x_perm"])
+    xq, xs = moe.mxfp8_quantize(xt, 0)
+    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, c["offs"], c["st"], c["mw"])
+    y_sep = moe.grouped_linear_mxfp8(a, c["offs"], wl.n_local, c["mw"].wd, c["mw"].wds)
+    R_cap = xq.shape[0]
+    nb = moe.lib().moe_grouped_mlp_mxfp8_fwd_workspace_bytes(R_cap, wl.n_local, wl.H, wl.I)
+    ws = torch.empty(nb, dtype=torch.uint8, device=xq.device)
+    moe.mxfp8_mlp_fwd(xq, xs, c["offs"], c["st"], c["mw"], workspace=ws, down=False)
+    y_two = moe.mxfp8_mlp_fwd_down(c["offs"], c["mw"], ws, R_cap)
+    dy = to_dev(c["dy"])
+    g = moe.mxfp8_mlp_bwd(dy, xt, a, gu, c["offs"], c["st"], c["mw"])
+    d1 = moe.mxfp8_mlp_bwd_down(dy, a, gu, c["offs"], c["st"], c["mw"])
+    d2 = moe.mxfp8_mlp_bwd_gate_up(d1["dgu"], xt, c["offs"], c["mw"])
+    moe.debug_sync()
+    print_case(c["name"], "fused vs stage calls, rows", R)
+    assert torch.equal(y[:R], y_sep[:R])
+    assert torch.equal(y[:R], y_two[:R])
+    assert torch.equal(g["ds"][:R], d1["ds"][:R])
+    assert torch.equal(g["dw_down"], d1["dw_down"])
+    assert torch.equal(g["dx"][:R], d2["dx"][:R])
+    assert torch.equal(g["dw_gate"], d2["dw_gate"])
+    assert torch.equal(g["dw_up"], d2["dw_up"])
+
+
 def test_mxfp8_fused_forward_backward(case):
     c, ref, R, I = case, case["ref"], case["p"]["R"], case["wl"].I
     xt = to_dev(c["x_perm"])
