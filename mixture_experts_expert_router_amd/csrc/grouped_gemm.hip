@@ -171,12 +171,12 @@ __device__ __forceinline__ void load_frags(const uint4 *As, const uint4 *Bs,
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MV>
 __device__ __forceinline__ void gemm_kloop(
     f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
-    const char *const (&gsrc)[(BM + BN) * (BK / 8) / 256], const uint4 *smem,
-    uint32_t lds0, uint32_t wave_off, int KT, int lane, int arow0,
-    int brow0) {
+    const char *const (&gsrc)[(BM + BN) * (BK / 8) / (WM * WN * 64)],
+    const uint4 *smem, uint32_t lds0, uint32_t wave_off, int KT, int lane,
+    int arow0, int brow0) {
   constexpr int CPR = BK / 8, NB = BN / WN / 32, KK = BK / 16;
   constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
-  constexpr int L = STAGE_CHUNKS / 256;
+  constexpr int L = STAGE_CHUNKS / (WM * WN * 64);
   constexpr int NMF = MV * NB * KK;
   for (int kt = 0; kt < KT; ++kt) {
     wait_loads_barrier<(STAGES - 2) * L>();
@@ -223,18 +223,20 @@ __device__ __forceinline__ void gemm_kloop(
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
-__global__ __launch_bounds__(256) void grouped_gemm_kernel(GemmArgs p) {
+__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) {
+  constexpr int NTH = WM * WN * 64;            // 4 or 8 wavefronts
   constexpr int CPR = BK / 8;                  // 16-byte chunks per row
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int MB = WTM / 32, NB = WTN / 32;
   constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
-  constexpr int L = STAGE_CHUNKS / 256;        // loads per thread per stage
-  constexpr int LA = BM * CPR / 256;           // of which A rows
-  static_assert(WM * WN == 4, "four wavefronts");
+  constexpr int L = STAGE_CHUNKS / NTH;        // loads per thread per stage
+  static_assert(WM * WN == 4 || WM * WN == 8, "four or eight wavefronts");
   static_assert(MB >= 1 && NB >= 1, "wave tile is a multiple of 32x32");
   static_assert(EPI != EPI_SWIGLU || NB % 2 == 0,
                 "SwiGLU pairs a gate block with the up block next to it");
-  static_assert(BM * CPR % 256 == 0 && BN * CPR % 256 == 0, "load split");
+  static_assert(BM * CPR % NTH == 0 && BN * CPR % NTH == 0, "load split");
+  static_assert(STAGES * STAGE_CHUNKS * 16 >= WM * WN * WTM * WTN * 2,
+                "the ring must hold every wavefront's epilogue region");
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 2) * L <= 63,
                 "vmcnt range");
@@ -431,7 +433,7 @@ hipError_t launch_one(GemmArgs p, int num_cus, int64_t max_tiles,
                       hipStream_t s) {
   (void)num_cus;
   grouped_gemm_kernel<BM, BN, WM, WN, BK, ST, EPI>
-      <<<(unsigned)tile_grid(max_tiles), 256, 0, s>>>(p);
+      <<<(unsigned)tile_grid(max_tiles), WM * WN * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
