@@ -328,8 +328,10 @@ int moe_grouped_linear_mxfp8(const void *x, const int32_t *offsets,
  * Outputs: dx [R_cap, H] bf16, ds [R_cap] fp32 (sum in a fixed order),
  * dw_gate, dw_up [n_local, I, H] bf16, dw_down [n_local, H, I] bf16 (an
  * expert without rows gets zero gradients).
- * The call runs moe_grouped_mlp_mxfp8_bwd_down, then
- * moe_grouped_mlp_mxfp8_bwd_gate_up, with [dg | du] kept in the workspace.
+ * The call computes what moe_grouped_mlp_mxfp8_bwd_down followed by
+ * moe_grouped_mlp_mxfp8_bwd_gate_up compute, with identical bits, but [dg |
+ * du] never exists in bf16: the epilogue that produces it writes its MX codes
+ * (along 2I, and down each expert's rows) into the workspace directly.
  * workspace: moe_grouped_mlp_mxfp8_bwd_workspace_bytes() bytes.
  * Limits as for the forward.
  */

@@ -353,21 +353,48 @@ struct GateUpBwdWs {               // backward of the gate/up projection
   uint8_t *xT, *xTs, *dgT, *dgTs, *duT, *duTs;
   int64_t kcap;
 };
+// own_dgu == false: the MX copies of [dg | du] come from DguCodes instead.
 GateUpBwdWs carve_gate_up_bwd(Carve &c, int64_t R_cap, int64_t n_local,
-                              int64_t H, int64_t I) {
-  GateUpBwdWs w;
+                              int64_t H, int64_t I, bool own_dgu = true) {
+  GateUpBwdWs w{};
   w.kcap = mx_kpad_cap(R_cap, n_local);
   w.tiles = c.take<int32_t>(n_local + 1);
   w.kpad = c.take<int32_t>(n_local + 1);
-  w.dguq = c.take<uint8_t>((size_t)R_cap * 2 * I);
-  w.dgus = c.take<uint8_t>((size_t)R_cap * (2 * I / 32));
+  if (own_dgu) {
+    w.dguq = c.take<uint8_t>((size_t)R_cap * 2 * I);
+    w.dgus = c.take<uint8_t>((size_t)R_cap * (2 * I / 32));
+  }
   w.xT = c.take<uint8_t>((size_t)H * w.kcap);
   w.xTs = c.take<uint8_t>((size_t)H * (w.kcap / 32));
-  w.dgT = c.take<uint8_t>((size_t)I * w.kcap);
-  w.dgTs = c.take<uint8_t>((size_t)I * (w.kcap / 32));
-  w.duT = c.take<uint8_t>((size_t)I * w.kcap);
-  w.duTs = c.take<uint8_t>((size_t)I * (w.kcap / 32));
+  if (own_dgu) {
+    w.dgT = c.take<uint8_t>((size_t)I * w.kcap);
+    w.dgTs = c.take<uint8_t>((size_t)I * (w.kcap / 32));
+    w.duT = c.take<uint8_t>((size_t)I * w.kcap);
+    w.duTs = c.take<uint8_t>((size_t)I * (w.kcap / 32));
+  }
   return w;
+}
+
+// The fused backward's MX copies of [dg | du], written by the SwiGLU-backward
+// epilogue: row-wise along 2I (for dX) and column-wise per expert segment,
+// segments padded to 256 rows at tpad (for dW_g, dW_u).
+struct DguCodes {
+  int32_t *tpad;
+  uint8_t *q, *qs;                 // [R_cap, 2I], [R_cap, 2I/32]
+  uint8_t *gT, *gTs, *uT, *uTs;    // [I, kcap], [I, kcap/32]
+  int64_t kcap;
+};
+DguCodes carve_dgu_codes(Carve &c, int64_t R_cap, int64_t n_local, int64_t I) {
+  DguCodes d;
+  d.kcap = mx_kpad_cap(R_cap, n_local);
+  d.tpad = c.take<int32_t>(n_local + 1);
+  d.q = c.take<uint8_t>((size_t)R_cap * 2 * I);
+  d.qs = c.take<uint8_t>((size_t)R_cap * (2 * I / 32));
+  d.gT = c.take<uint8_t>((size_t)I * d.kcap);
+  d.gTs = c.take<uint8_t>((size_t)I * (d.kcap / 32));
+  d.uT = c.take<uint8_t>((size_t)I * d.kcap);
+  d.uTs = c.take<uint8_t>((size_t)I * (d.kcap / 32));
+  return d;
 }
 
 size_t fwd_bytes(int64_t R_cap, int64_t n_local, int64_t I) {
@@ -395,11 +422,10 @@ size_t gate_up_bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H,
 // in turn.
 size_t bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H, int64_t I) {
   Carve c(nullptr);
-  c.take<uint16_t>((size_t)R_cap * 2 * I);
-  c.take<uint8_t>((size_t)R_cap * 2 * I);
-  c.take<uint8_t>((size_t)R_cap * (2 * I / 32));
-  return c.used + std::max(down_bwd_bytes(R_cap, n_local, H, I),
-                           gate_up_bwd_bytes(R_cap, n_local, H, I));
+  carve_dgu_codes(c, R_cap, n_local, I);
+  Carve g(nullptr);
+  carve_gate_up_bwd(g, R_cap, n_local, H, I, /*own_dgu=*/false);
+  return c.used + std::max(down_bwd_bytes(R_cap, n_local, H, I), g.used);
 }
 
 // y = MX(x) . MX(W_e)^T per row segment; the quantisation of x stops at the
@@ -431,8 +457,7 @@ hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
                         int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
                         const uint8_t *wdt, const uint8_t *wdts, void *dgu,
                         float *ds, void *dw_down, const DownBwdWs &w, int cus,
-                        hipStream_t stream, uint8_t *dguq = nullptr,
-                        uint8_t *dgus = nullptr) {
+                        hipStream_t stream, const DguCodes *codes = nullptr) {
   const int G = (int)n_local;
   hipError_t err;
 #define MX_TRY(x) do { err = (x); if (err != hipSuccess) return err; } while (0)
@@ -449,8 +474,14 @@ hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
     d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
     d.row_scale = s_perm; d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
     d.dgu = (uint16_t *)dgu; d.ds_part = w.ds_part; d.ds = ds;
-    // optionally also [dg | du] quantised along 2I, for the dX GEMM
-    d.q = dguq; d.qs = dgus; d.ldq = 2 * I; d.ldqs = 2 * I / 32;
+    if (codes) {
+      // [dg | du] quantised by the epilogue: along 2I for the dX GEMM, and
+      // down each expert segment (padded to 256 rows) for dW_g, dW_u
+      MX_TRY(moe::launch_mx_pad_offsets(offsets, G, 256, codes->tpad, stream));
+      d.q = codes->q; d.qs = codes->qs; d.ldq = 2 * I; d.ldqs = 2 * I / 32;
+      d.t0 = codes->gT; d.t0s = codes->gTs; d.t1 = codes->uT; d.t1s = codes->uTs;
+      d.ldt = codes->kcap; d.ldts = codes->kcap / 32; d.tpad = codes->tpad;
+    }
     MX_TRY(moe::launch_mx_rowseg(d, moe::MXE_SWIGLU_BWD, cus, stream));
   }
   // dW_d[e] [H, I] = dY_e^T a_e: blocks of 32 rows inside each expert's
@@ -477,19 +508,17 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
                            const uint8_t *wut, const uint8_t *wuts, void *dx,
                            void *dw_gate, void *dw_up, const GateUpBwdWs &w,
                            int cus, hipStream_t stream,
-                           const uint8_t *dguq = nullptr,
-                           const uint8_t *dgus = nullptr) {
+                           const DguCodes *codes = nullptr) {
   const int G = (int)n_local;
   hipError_t err;
   // [dg | du] along I (row-wise; blocks never straddle the two halves),
   // unless the producing epilogue already wrote it
-  if (!dguq) {
+  const uint8_t *dguq = codes ? codes->q : w.dguq;
+  const uint8_t *dgus = codes ? codes->qs : w.dgus;
+  if (!codes)
     MX_TRY(moe::launch_mx_quant_rows((const uint16_t *)dgu, R_cap, 2 * I, 2 * I,
                                      w.dguq, 2 * I, w.dgus, 2 * I / 32,
                                      offsets + G, stream));
-    dguq = w.dguq;
-    dgus = w.dgus;
-  }
   // dX = dg W_g + du W_u: one GEMM with K = 2I, B switching at K = I
   {
     moe::MxGemmDesc d{};
@@ -502,27 +531,35 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
     d.C = dx; d.ldc = H;
     MX_TRY(moe::launch_mx_rowseg(d, moe::MXE_BF16, cus, stream));
   }
+  // Column-wise copies for the weight gradients: segments padded to 512
+  // rows, or to 256 rows to match the epilogue's dg, du copies.
   const int64_t kc = w.kcap;
-  const uint16_t *dg = (const uint16_t *)dgu;
+  const int align = codes ? 256 : 512;
+  int32_t *kpad = codes ? codes->tpad : w.kpad;
   MX_TRY(moe::launch_mx_quant_cols((const uint16_t *)x_perm, R_cap, H, H,
-                                   offsets, G, 512, w.kpad, w.xT, kc, w.xTs,
+                                   offsets, G, align, kpad, w.xT, kc, w.xTs,
                                    kc / 32, cus, stream));
-  MX_TRY(moe::launch_mx_quant_cols(dg, R_cap, I, 2 * I, offsets, G, 512,
-                                   w.kpad, w.dgT, kc, w.dgTs, kc / 32, cus,
-                                   stream));
-  MX_TRY(moe::launch_mx_quant_cols(dg + I, R_cap, I, 2 * I, offsets, G, 512,
-                                   w.kpad, w.duT, kc, w.duTs, kc / 32, cus,
-                                   stream));
+  const uint8_t *dgT = codes ? codes->gT : w.dgT, *dgTs = codes ? codes->gTs : w.dgTs;
+  const uint8_t *duT = codes ? codes->uT : w.duT, *duTs = codes ? codes->uTs : w.duTs;
+  if (!codes) {
+    const uint16_t *dg = (const uint16_t *)dgu;
+    MX_TRY(moe::launch_mx_quant_cols(dg, R_cap, I, 2 * I, offsets, G, 512,
+                                     w.kpad, w.dgT, kc, w.dgTs, kc / 32, cus,
+                                     stream));
+    MX_TRY(moe::launch_mx_quant_cols(dg + I, R_cap, I, 2 * I, offsets, G, 512,
+                                     w.kpad, w.duT, kc, w.duTs, kc / 32, cus,
+                                     stream));
+  }
 #undef MX_TRY
   // dW_g[e] [I, H] = dg_e^T x_e ; dW_u likewise with du
   moe::MxGemmDesc d{};
-  d.kseg = w.kpad; d.G = G;
+  d.kseg = kpad; d.G = G;
   d.lda = kc; d.ldas = kc / 32; d.ldb = kc; d.ldbs = kc / 32;
-  d.A = w.dgT; d.As = w.dgTs; d.B0 = w.xT; d.B0s = w.xTs;
+  d.A = dgT; d.As = dgTs; d.B0 = w.xT; d.B0s = w.xTs;
   d.M = (int)I; d.N = (int)H; d.C = dw_gate; d.ldc = H; d.c_stride = I * H;
   err = moe::launch_mx_kseg(d, cus, stream);
   if (err != hipSuccess) return err;
-  d.A = w.duT; d.As = w.duTs; d.C = dw_up;
+  d.A = duT; d.As = duTs; d.C = dw_up;
   return moe::launch_mx_kseg(d, cus, stream);
 }
 
@@ -749,21 +786,21 @@ int moe_grouped_mlp_mxfp8_bwd(
     return MOE_E_WORKSPACE;
   if (!aligned16(workspace)) return MOE_E_ALIGN;
   Carve c(workspace);
-  uint16_t *dgu = c.take<uint16_t>((size_t)R_cap * 2 * I);
-  // [dg | du] quantised along 2I by the SwiGLU-backward epilogue itself
-  uint8_t *dguq = c.take<uint8_t>((size_t)R_cap * 2 * I);
-  uint8_t *dgus = c.take<uint8_t>((size_t)R_cap * (2 * I / 32));
+  // [dg | du] never exists in bf16 here: the SwiGLU-backward epilogue writes
+  // its MX copies (row-wise and per segment column-wise) directly.
+  const DguCodes codes = carve_dgu_codes(c, R_cap, n_local, I);
   Carve shared = c;   // both halves carve the same region, one after the other
   const int cus = num_cus();
   const DownBwdWs wd = carve_down_bwd(c, R_cap, n_local, H, I);
   hipError_t err = run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap, H,
-                                I, wdt, wdts, dgu, ds, dw_down, wd, cus,
-                                stream, dguq, dgus);
+                                I, wdt, wdts, nullptr, ds, dw_down, wd, cus,
+                                stream, &codes);
   if (err != hipSuccess) return MOE_E_HIP;
-  const GateUpBwdWs wg = carve_gate_up_bwd(shared, R_cap, n_local, H, I);
-  return status_of(run_gate_up_bwd(dgu, x_perm, offsets, n_local, R_cap, H, I,
-                                   wgt, wgts, wut, wuts, dx, dw_gate, dw_up,
-                                   wg, cus, stream, dguq, dgus));
+  const GateUpBwdWs wg =
+      carve_gate_up_bwd(shared, R_cap, n_local, H, I, /*own_dgu=*/false);
+  return status_of(run_gate_up_bwd(nullptr, x_perm, offsets, n_local, R_cap,
+                                   H, I, wgt, wgts, wut, wuts, dx, dw_gate,
+                                   dw_up, wg, cus, stream, &codes));
 }
 
 }  // extern "C"

@@ -61,6 +61,9 @@ hipError_t launch_mx_quant_rows(const uint16_t *in, int64_t rows, int64_t cols,
                                 int64_t ld_codes, uint8_t *scales,
                                 int64_t ld_scales, const int32_t *rows_dev,
                                 hipStream_t s);
+// pad[s+1] = pad[s] + ceil((seg[s+1] - seg[s]) / align) * align, pad[0] = 0.
+hipError_t launch_mx_pad_offsets(const int32_t *seg, int nseg, int align,
+                                 int32_t *pad, hipStream_t s);
 hipError_t launch_mx_quant_cols(const uint16_t *in, int64_t rows,
                                 int64_t cols, int64_t ld_in,
                                 const int32_t *seg, int nseg, int align,
@@ -93,6 +96,11 @@ struct MxGemmDesc {
   // along 2I (row-wise, blocks of 32 columns).  Null: not written.
   uint8_t *q, *qs;
   int64_t ldq, ldqs;
+  // SwiGLU backward: column-wise MX codes / scales of dg (t0) and du (t1),
+  // [N, ldt] / [N, ldts], segments padded to 256 rows at tpad (null: none).
+  uint8_t *t0, *t0s, *t1, *t1s;
+  int64_t ldt, ldts;
+  const int32_t *tpad;
 };
 enum { MXE_BF16 = 0, MXE_SWIGLU = 1, MXE_SWIGLU_BWD = 2 };
 hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,

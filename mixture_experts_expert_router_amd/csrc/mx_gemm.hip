@@ -15,7 +15,7 @@
 //           data gradients); K fixed.  Tiles listed by a plan kernel.
 //   KSEG:   every group has all M x N outputs and its own K range
 //           [kseg[g], kseg[g+1]) of transposed operands (weight gradients:
-//           K runs over an expert's rows, zero-padded to 512).
+//           K runs over an expert's rows, zero-padded to 256 or 512).
 // KSPLIT (data gradient through gate and up): B rows are [B0 row | B1 row]
 // along K, the switch at `ksplit`.
 //
@@ -44,7 +44,7 @@ struct MxArgs {
   int64_t ldb, ldbs, b_stride, bs_stride;
   const int32_t *offsets;       // ROWSEG: [G + 1]
   const int32_t *tile_prefix;   // ROWSEG: [G + 1]
-  const int32_t *kseg;          // KSEG: [G + 1] K ranges (multiples of 512)
+  const int32_t *kseg;          // KSEG: [G + 1] K ranges (multiples of 128)
   int G, M, N, K, NT, MT;
   void *C;
   int64_t ldc, c_stride;
@@ -56,6 +56,12 @@ struct MxArgs {
   int ksplit;                   // KSPLIT: K of the B0 part (0 = none)
   uint8_t *q, *qs;              // SWIGLU(_BWD): row-wise MX copy of the
   int64_t ldq, ldqs;            //   bf16 output (null: none)
+  // SWIGLU_BWD: column-wise MX copies of dg (t0) and du (t1) for the weight
+  // gradients: codes [N, ldt], scales [N, ldts]; row r of expert e lands at
+  // position tpad[e] + (r - offsets[e]) (segments padded to BM rows).
+  uint8_t *t0, *t0s, *t1, *t1s;
+  int64_t ldt, ldts;
+  const int32_t *tpad;
 };
 
 enum MxMode { MX_ROWSEG = 0, MX_KSEG = 1 };
@@ -190,6 +196,43 @@ __device__ __forceinline__ void mx_quant_staged(const uint16_t *l, uint8_t *q,
       dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
       qs[(grow0 + r) * ldqs + col0 / 32 + b] = (uint8_t)sb;
     }
+  }
+}
+
+// Column-wise MX encoding of a staged [NROWS][W] bf16 region: blocks of 32
+// region rows down each column.  Block b of column c goes to codes
+// qt[(col0 + c) * ldt + pos0 + 32 b] and scale qts[(col0 + c) * ldts +
+// (pos0 + 32 b) / 32]; region rows at or past `valid` count as zeros (the
+// segment's padding).  Two neighbouring lanes write one column's 64 bytes.
+template <int W, int NROWS>
+__device__ __forceinline__ void mx_quant_staged_cols(const uint16_t *l,
+                                                     uint8_t *qt, uint8_t *qts,
+                                                     int64_t ldt, int64_t ldts,
+                                                     int64_t col0, int64_t pos0,
+                                                     int valid, int lane) {
+  constexpr int BPC = NROWS / 32;              // blocks per column
+  static_assert(NROWS % 32 == 0 && (W * BPC) % 64 == 0, "region");
+#pragma unroll 1
+  for (int it = 0; it < W * BPC / 64; ++it) {
+    const int item = it * 64 + lane;
+    const int c = item / BPC, b = item % BPC;
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int r = b * 32 + j;
+      v[j] = r < valid ? bf16_bits_to_f32(l[r * W + st_col<W>(r, c)]) : 0.f;
+      amax = fmaxf(amax, fabsf(v[j]));
+    }
+    const int X = mx_shared_exp(amax);
+    uint32_t pk[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      pk[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], -X);
+    uint4 *dst = (uint4 *)(qt + (col0 + c) * ldt + pos0 + 32 * b);
+    dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
+    qts[(col0 + c) * ldts + (pos0 + 32 * b) / 32] = (uint8_t)(X + 127);
   }
 }
 
@@ -509,68 +552,71 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   constexpr int NFR = MB + NB;                          // fragments per step
 
   // Prologue: stages 0 and 1 (clamped) in flight, stage 0 landed, its scales
-  // and first step's fragments read.
+  // and first step's fragments read.  An expert without rows (KSEG, KT == 0)
+  // loads nothing and stores zeros.
   i32x8 af0[MB], bf0[NB], af1[MB], bf1[NB];
   uint32_t sa[MB], sbv[NB], sa_n[MB], sbv_n[NB];
+  if (KT > 0) {
 #pragma unroll
-  for (int i = 0; i < L; ++i) issue(i, 0, 0);
+    for (int i = 0; i < L; ++i) issue(i, 0, 0);
 #pragma unroll
-  for (int i = 0; i < L; ++i) issue(i, 1, min(1, KT - 1));
-  mx_wait_barrier<L>();
-  read_s(0, sa, sbv);
+    for (int i = 0; i < L; ++i) issue(i, 1, min(1, KT - 1));
+    mx_wait_barrier<L>();
+    read_s(0, sa, sbv);
 #pragma unroll
-  for (int k = 0; k < NFR; ++k) read_next(k, 0, 0, af0, bf0);
+    for (int k = 0; k < NFR; ++k) read_next(k, 0, 0, af0, bf0);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1, nb = cur ^ 1;
-    const int ks = min(kt + 2, KT - 1);
-    // Step 0 on (af0, bf0); the fragments of step 1 are read meanwhile.
+    for (int kt = 0; kt < KT; ++kt) {
+      const int cur = kt & 1, nb = cur ^ 1;
+      const int ks = min(kt + 2, KT - 1);
+      // Step 0 on (af0, bf0); the fragments of step 1 are read meanwhile.
 #pragma unroll
-    for (int m = 0; m < MB; ++m)
+      for (int m = 0; m < MB; ++m)
 #pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int f = m * NB + n;
-        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            af0[m], bf0[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> (8 * h)) & 0xffu),
-            0, (int)((sbv[n] >> (8 * h)) & 0xffu));
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int k = 0; k < NFR; ++k)
-          if (f == k + k / 2) read_next(k, cur, 1, af1, bf1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    // Step 1 on (af1, bf1).  After its first two MFMAs: stage kt+1 has landed
-    // (own loads, then the barrier for everyone's) and nobody reads buffer
-    // `cur` any more; so the loads of stage kt+2 go into it, and the scales
-    // and first fragments of stage kt+1 are read from buffer nb.
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int n = 0; n < NB; ++n) {
-        const int g = m * NB + n;
-        acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            af1[m], bf1[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> (8 * (2 + h))) & 0xffu),
-            0, (int)((sbv[n] >> (8 * (2 + h))) & 0xffu));
-        __builtin_amdgcn_sched_barrier(0);
-        if (g == 1) {
-          mx_wait_barrier<0>();
-          read_s(nb, sa_n, sbv_n);
-        }
-        if (g >= 2) {
-          constexpr int SL = MB * NB - 2;                 // slots for the rest
-#pragma unroll
-          for (int i = 0; i < L; ++i)
-            if (i * SL / L == g - 2) issue(i, cur, ks);
+        for (int n = 0; n < NB; ++n) {
+          const int f = m * NB + n;
+          acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af0[m], bf0[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> (8 * h)) & 0xffu),
+              0, (int)((sbv[n] >> (8 * h)) & 0xffu));
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int k = 0; k < NFR; ++k)
-            if (g - 2 == k) read_next(k, nb, 0, af0, bf0);
+            if (f == k + k / 2) read_next(k, cur, 1, af1, bf1);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      // Step 1 on (af1, bf1).  After its first two MFMAs: stage kt+1 has landed
+      // (own loads, then the barrier for everyone's) and nobody reads buffer
+      // `cur` any more; so the loads of stage kt+2 go into it, and the scales
+      // and first fragments of stage kt+1 are read from buffer nb.
 #pragma unroll
-    for (int m = 0; m < MB; ++m) sa[m] = sa_n[m];
+      for (int m = 0; m < MB; ++m)
 #pragma unroll
-    for (int n = 0; n < NB; ++n) sbv[n] = sbv_n[n];
+        for (int n = 0; n < NB; ++n) {
+          const int g = m * NB + n;
+          acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              af1[m], bf1[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> (8 * (2 + h))) & 0xffu),
+              0, (int)((sbv[n] >> (8 * (2 + h))) & 0xffu));
+          __builtin_amdgcn_sched_barrier(0);
+          if (g == 1) {
+            mx_wait_barrier<0>();
+            read_s(nb, sa_n, sbv_n);
+          }
+          if (g >= 2) {
+            constexpr int SL = MB * NB - 2;                 // slots for the rest
+#pragma unroll
+            for (int i = 0; i < L; ++i)
+              if (i * SL / L == g - 2) issue(i, cur, ks);
+#pragma unroll
+            for (int k = 0; k < NFR; ++k)
+              if (g - 2 == k) read_next(k, nb, 0, af0, bf0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+      for (int m = 0; m < MB; ++m) sa[m] = sa_n[m];
+#pragma unroll
+      for (int n = 0; n < NB; ++n) sbv[n] = sbv_n[n];
+    }
   }
   mx_wait_barrier<0>();
 
@@ -631,8 +677,17 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
         mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[3], 32, 96, lane, arow0, rows, row0, nt, wn, s_hi, lg, lu);
       }
       __syncthreads();
-      store_staged<128, 64>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
-      store_staged<128, 64>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      if (p.dgu) {
+        store_staged<128, 64>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+        store_staged<128, 64>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+      }
+      if (p.t0) {
+        // tile rows start at offsets[e] + mt * BM, padded position tpad[e] + mt * BM
+        const int64_t pos0 = (int64_t)p.tpad[e] + (row0 - p.offsets[e]) + ar0;
+        const int valid = min(max(rows - ar0, 0), 64);
+        mx_quant_staged_cols<128, 64>(lg, p.t0, p.t0s, p.ldt, p.ldts, col0, pos0, valid, lane);
+        mx_quant_staged_cols<128, 64>(lu, p.t1, p.t1s, p.ldt, p.ldts, col0, pos0, valid, lane);
+      }
       if (p.q) {
         mx_quant_staged<128, 64>(lg, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, ar0, rows, lane);
         mx_quant_staged<128, 64>(lu, p.q, p.ldq, p.qs, p.ldqs, p.N + col0, grow0, ar0, rows, lane);
@@ -699,6 +754,8 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
   p.C = d.C; p.ldc = d.ldc; p.row_scale = d.row_scale;
   p.gu = d.gu; p.ldgu = d.ldgu; p.dgu = d.dgu; p.ds_part = d.ds_part;
   p.q = d.q; p.qs = d.qs; p.ldq = d.ldq; p.ldqs = d.ldqs;
+  p.t0 = d.t0; p.t0s = d.t0s; p.t1 = d.t1; p.t1s = d.t1s;
+  p.ldt = d.ldt; p.ldts = d.ldts; p.tpad = d.tpad;
   p.ksplit = d.ksplit;
   const int cols = epi == MX_EPI_SWIGLU ? kMxBN / 2 : kMxBN;
   p.NT = (d.N + cols - 1) / cols;

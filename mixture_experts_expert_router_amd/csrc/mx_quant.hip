@@ -223,6 +223,12 @@ hipError_t launch_mx_quant_rows(const uint16_t *in, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
+hipError_t launch_mx_pad_offsets(const int32_t *seg, int nseg, int align,
+                                 int32_t *pad, hipStream_t s) {
+  mx_pad_offsets_kernel<<<1, 1024, 0, s>>>(seg, nseg, align, pad);
+  return hipGetLastError();
+}
+
 hipError_t launch_mx_quant_cols(const uint16_t *in, int64_t rows,
                                 int64_t cols, int64_t ld_in,
                                 const int32_t *seg, int nseg, int align,

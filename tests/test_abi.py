@@ -177,7 +177,8 @@ def test_mxfp8_validation(L):
     db = L.moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(64, 2, 512, 512)
     gb = L.moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes(64, 2, 512, 512)
     bb = L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes(64, 2, 512, 512)
-    assert db > 0 and gb > 0 and bb >= max(db, gb) + 64 * 2 * 512 * 2
+    # the fused call keeps the MX codes of [dg | du] beside the down workspace
+    assert db > 0 and gb > 0 and bb >= db + 64 * 2 * 512
     d = L.moe_grouped_mlp_mxfp8_bwd_down
     assert d(P, P, None, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db, None) == E_ARG
     assert d(P, P, P, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db - 1, None) == E_WS

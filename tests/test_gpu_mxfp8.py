@@ -283,3 +283,45 @@ def test_mxfp8_fused_forward_backward(case):
     for key in ("dw_gate", "dw_up", "dw_down"):
         _frob(to_f64(g[key]), ref[key], f"{n} {key}", bad)
     assert not bad, bad
+
+
+def test_mxfp8_experts_without_rows():
+    """Experts 0 and 2 of four receive no rows: their weight-gradient GEMMs
+    run over empty K ranges and must return exact zeros, and the fused calls
+    must still equal the stage calls bit for bit."""
+    wl = synth.WORKLOADS["small_mxfp8"]
+    R = 300
+    inp = synth.make_inputs(wl, tokens=R)
+    offsets = np.array([0, 0, 127, 127, R], np.int32)
+    x_perm = inp["x"]
+    s = np.random.default_rng(11).uniform(0.05, 1.0, R).astype(np.float32)
+    dy = synth.make_dy(wl, R)
+    ref = orc.mxfp8_mlp_step(x_perm, offsets, s.astype(np.float64),
+                             inp["w_gate"], inp["w_up"], inp["w_down"], dy)
+    d = {k: to_dev(inp[k]) for k in ("w_gate", "w_up", "w_down")}
+    mw = moe.MxWeights(d["w_gate"], d["w_up"], d["w_down"])
+    offs, st, xt, dyt = to_dev(offsets), to_dev(s), to_dev(x_perm), to_dev(dy)
+    print_case("small_mxfp8 experts 0, 2 empty", "rows", R)
+    xq, xs = moe.mxfp8_quantize(xt, 0)
+    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, offs, st, mw)
+    g = moe.mxfp8_mlp_bwd(dyt, xt, a, gu, offs, st, mw)
+    d1 = moe.mxfp8_mlp_bwd_down(dyt, a, gu, offs, st, mw)
+    d2 = moe.mxfp8_mlp_bwd_gate_up(d1["dgu"], xt, offs, mw)
+    moe.debug_sync()
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        for e in (0, 2):
+            assert not g[key][e].any(), (key, e)
+    assert torch.equal(g["dw_down"], d1["dw_down"])
+    assert torch.equal(g["dx"][:R], d2["dx"][:R])
+    assert torch.equal(g["dw_gate"], d2["dw_gate"])
+    assert torch.equal(g["dw_up"], d2["dw_up"])
+    bad = []
+    _check(to_f64(a[:R]), ref["a"], "empty-expert a", bad)
+    _check(g["ds"][:R].cpu().numpy().astype(np.float64), ref["ds"],
+           "empty-expert ds", bad)
+    _frob(to_f64(y[:R]), ref["y"], "empty-expert y", bad)
+    _frob(to_f64(g["dx"][:R]), ref["dx"], "empty-expert dx", bad)
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        for e in (1, 3):
+            _frob(to_f64(g[key][e]), ref[key][e], f"empty-expert {key}[{e}]", bad)
+    assert not bad, bad
