@@ -126,6 +126,13 @@ def algorithmic(wl, R, n_touched, gather=True):
                 step_bytes=step_bytes)
 
 
+def percentiles(ms):
+    """p10 / median / p90 of per-step event times (ms)."""
+    q = np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])
+    return {"p10": round(float(q[0]), 4), "p50": round(float(q[1]), 4),
+            "p90": round(float(q[2]), 4)}
+
+
 def cpu_baseline(wl, inp, tokens):
     """The oracle as it stands, on the first `tokens` tokens of the batch."""
     import oracle
@@ -231,7 +238,8 @@ def run_mx(args, wl, dev):
     ws_b = torch.empty(L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes(F, n, H, I),
                        dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # per timed step: step start, gate/up start, gate/up end, step end
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)]
           for _ in range(args.steps)]
     qev = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     mw_holder = {}
@@ -241,18 +249,22 @@ def run_mx(args, wl, dev):
 
     def step(timed_ev=None):
         mw = mw_holder["mw"]
+        if timed_ev is not None:
+            timed_ev[0].record(stream)
         moe.permute(topk_idx, d["x"], wl.e_begin, n, topk_w=topk_w, out=pout)
         moe.mxfp8_quantize(pout.x_perm, 0, codes=xq, scales=xs)
         if timed_ev is not None:
-            timed_ev[0].record(stream)
+            timed_ev[1].record(stream)
         moe.mxfp8_mlp_fwd(xq, xs, pout.offsets, pout.s_perm, mw, a=a, gu=gu,
                           workspace=ws_f, down=False)
         if timed_ev is not None:
-            timed_ev[1].record(stream)
+            timed_ev[2].record(stream)
         moe.mxfp8_mlp_fwd_down(pout.offsets, mw, ws_f, F, y=y)
         moe.mxfp8_mlp_bwd(dy, pout.x_perm, a, gu, pout.offsets, pout.s_perm,
                           mw, dx=dx, ds=ds, dw_gate=dwg, dw_up=dwu,
                           dw_down=dwd, workspace=ws_b)
+        if timed_ev is not None:
+            timed_ev[3].record(stream)
 
     quant_masters()
     for _ in range(args.warmup):
@@ -270,7 +282,8 @@ def run_mx(args, wl, dev):
         step(ev[i])
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    gu_ms = float(np.mean([s_.elapsed_time(e_) for s_, e_ in ev]))
+    gu_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    step_pct = percentiles([e[0].elapsed_time(e[3]) for e in ev])
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
@@ -303,6 +316,7 @@ def run_mx(args, wl, dev):
         "step_mfma_frac_fp8": round(tflops / FP8_PEAK_TFLOPS, 4),
         "step_mfma_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
         "master_quant_ms": round(master_ms, 4),
+        "step_ms_events": step_pct,
         "roofline": {
             "kernel": "MXFP8 grouped gate/up GEMM + SwiGLU x scale (forward)",
             "bound": "mfma",
@@ -332,6 +346,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="c4_full_bf16",
                     choices=["c4_full_bf16", "c2_ep64_bf16", "c3_ep8_bf16",
+                             "c3_literal_ep8_bf16", "c5_shape_bf16",
                              "mid_bf16", "c5_mxfp8", "mid_mxfp8"])
     ap.add_argument("--cpu-tokens", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -381,7 +396,8 @@ def main():
     y = torch.empty((F, H), dtype=torch.bfloat16, device=dev)
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     ws = moe.ffn_workspace(F, wl.n_local, H, I, torch.bfloat16, dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # per timed step: step start, gate/up start, gate/up end, down end, step end
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)]
           for _ in range(args.steps)]
 
     def route():
@@ -394,12 +410,14 @@ def main():
 
     def step(i, timed_ev=None):
         wg, wu, wd = wcopies[i % len(wcopies)]
+        if timed_ev is not None:
+            timed_ev[0].record(stream)
         if wl.router == "gemm":
             route()
         moe.permute(topk_idx, None if gather else d["x"], wl.e_begin,
                     wl.n_local, topk_w=topk_w, out=pout)
         if timed_ev is not None:
-            timed_ev[0].record(stream)
+            timed_ev[1].record(stream)
         if gather:
             moe.grouped_gate_up_gather(d["x"], pout.row_src, k, pout.offsets,
                                        pout.s_perm, wg, wu, a=a, workspace=ws)
@@ -407,9 +425,13 @@ def main():
             moe.grouped_gate_up(pout.x_perm, pout.offsets, pout.s_perm, wg, wu,
                                 a=a, workspace=ws)
         if timed_ev is not None:
-            timed_ev[1].record(stream)
+            timed_ev[2].record(stream)
         moe.grouped_down(a, pout.offsets, wd, y=y, workspace=ws)
+        if timed_ev is not None:
+            timed_ev[3].record(stream)
         moe.unpermute_combine(y, pout.inv, out=out)
+        if timed_ev is not None:
+            timed_ev[4].record(stream)
 
     if wl.router != "gemm":
         route()
@@ -426,7 +448,9 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_step = elapsed * 1e3 / args.steps
-    gate_up_ms = float(np.mean([s.elapsed_time(e) for s, e in ev]))
+    gate_up_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    step_pct = percentiles([e[0].elapsed_time(e[4]) for e in ev])
+    ffn_pct = percentiles([e[1].elapsed_time(e[3]) for e in ev])
 
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
@@ -436,6 +460,19 @@ def main():
     tflops = flop / (ms_step * 1e-3) / 1e12
     gu_gbs = alg["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
     gu_tflops = alg["gate_up_flop"] / (gate_up_ms * 1e-3) / 1e12
+    # The gate/up kernel's bound: HBM below the bf16 ridge point (peak FLOP/s
+    # over peak bytes/s), the matrix cores above it.
+    ai = alg["gate_up_flop"] / alg["gate_up_bytes"]
+    ridge = BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai < ridge:
+        gate_up_bound = {"bound": "hbm", "achieved": round(gu_gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gu_gbs / HBM_PEAK_GBS, 4)}
+    else:
+        gate_up_bound = {"bound": "mfma", "achieved": round(gu_tflops, 2),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(gu_tflops / BF16_PEAK_TFLOPS, 4)}
+    gate_up_bound["flop_per_byte"] = round(ai, 1)
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -463,20 +500,19 @@ def main():
         "step_hbm_gbs": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-        "roofline": {
+        "step_ms_events": step_pct,
+        "ffn_ms_events": ffn_pct,
+        "ffn_tflops_p50": round(alg["flop_ffn"] / (ffn_pct["p50"] * 1e-3) / 1e12, 2),
+        "roofline": dict(**gate_up_bound, **{
             "kernel": "grouped gate/up GEMM + SwiGLU x scale",
-            "bound": "hbm",
-            "achieved": round(gu_gbs, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(wl.name),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "algorithmic_bytes": int(alg["gate_up_bytes"]),
             "avg_ms": round(gate_up_ms, 4),
+            "gbs": round(gu_gbs, 1),
             "tflops": round(gu_tflops, 2),
             "mfma_frac": round(gu_tflops / BF16_PEAK_TFLOPS, 4),
-        },
+        }),
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")

@@ -165,12 +165,20 @@ WORKLOADS = {
     # EP8 share: tokens 0-511 of the same routing, experts 0-31 kept.
     "c3_ep8_bf16": Workload("c3_ep8_bf16", "bf16", 512, 7168, 2048, 256, 8,
                             0, 32, "logits", 1.1),
+    # EP8 share read literally: all 4096 tokens of the same routing, experts
+    # 0-31 kept (about 128 rows per expert).
+    "c3_literal_ep8_bf16": Workload("c3_literal_ep8_bf16", "bf16", 4096, 7168,
+                                    2048, 256, 8, 0, 32, "logits", 1.1),
     # Full layer on one GPU: router GEMM + Zipf(1.2) bias, all 256 experts.
     "c4_full_bf16": Workload("c4_full_bf16", "bf16", 8192, 7168, 2048, 256, 8,
                              0, 256, "gemm", 1.2),
     # MXFP8 grouped MLP training step, uniform Gaussian routing top-2 of 8.
     "c5_mxfp8": Workload("c5_mxfp8", "mxfp8", 16384, 4096, 8192, 8, 2, 0, 8,
                          "logits", None),
+    # The bf16 forward on the MXFP8 step's shapes (about 4096 rows per
+    # expert): a compute-bound grouped FFN.
+    "c5_shape_bf16": Workload("c5_shape_bf16", "bf16", 16384, 4096, 8192, 8, 2,
+                              0, 8, "logits", None),
     # Small presets for tests (several tiles plus ragged tails).
     "tiny_f32": Workload("tiny_f32", "f32", 16, 64, 128, 4, 2, 0, 4,
                          "gemm", None),

@@ -1,10 +1,12 @@
 """The full-size workloads through the C ABI, against the oracle.
 
-EP64 share (4 experts) and EP8 share (32 experts): every row and token is
-checked.  Full layer (8192 tokens, 256 experts): the router GEMM and top-k
+EP64 share (4 experts) and EP8 share (32 experts, on 512 tokens and on all
+4096): every row and token is checked.  Full layer (8192 tokens, 256 experts): the router GEMM and top-k
 over all tokens, the permute in full (bit-exact), and the FFN / combine on a
 seeded sample of rows and tokens (every expert's first and last row plus 512
-random rows; 96 random tokens), which the oracle computes one by one.
+random rows; 96 random tokens), which the oracle computes one by one.  The
+bf16 forward on the MXFP8 step's shapes (8 experts of about 4096 rows) is
+sampled the same way.
 """
 import numpy as np
 import pytest
@@ -23,7 +25,8 @@ def _bits(t):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("name", ["c2_ep64_bf16", "c3_ep8_bf16"])
+@pytest.mark.parametrize("name", ["c2_ep64_bf16", "c3_ep8_bf16",
+                                  "c3_literal_ep8_bf16"])
 def test_ep_share_full(name):
     wl = synth.WORKLOADS[name]
     print_case(name)
@@ -169,3 +172,55 @@ def test_c4_end_to_end_sampled(c4):
     o_ref = orc.moe_tokens(inp["x"], r["idx"], r["w"], toks, 0, wl.n_local,
                            inp["w_gate"], inp["w_up"], inp["w_down"])
     assert_close(to_f64(out[toks]), o_ref, "bf16", "c4 end-to-end out")
+
+
+@pytest.mark.timeout(300)
+def test_c5_shape_bf16_sampled():
+    """16384 tokens, top-2 of 8 experts, H 4096, I 8192 in bf16: the permute
+    in full, a and y on every expert's first and last row plus 256 random
+    rows, out on 64 random tokens; the gather-on-load gate/up the benchmark
+    times gives the same bits as the one on x_perm."""
+    wl = synth.WORKLOADS["c5_shape_bf16"]
+    print_case("c5-shape bf16 generate")
+    inp = synth.make_inputs(wl)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    idx, w, _ = moe.route_topk(wl.k, logits=d["logits"].clone())
+    ridx, rw = orc.topk_softmax(inp["logits"], wl.k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    p_ref = orc.permute(ridx, 0, wl.n_local)
+    R = p_ref["R"]
+    # the FFN scales rows by the oracle's weights (rounded to fp32), so that
+    # every expected value below derives from the oracle alone
+    w32 = rw.astype(np.float32)
+    p = moe.permute(idx, d["x"], 0, wl.n_local, topk_w=to_dev(w32))
+    a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
+                           d["w_up"], d["w_down"])
+    out = moe.unpermute_combine(y, p.inv)
+    a_g = moe.grouped_gate_up_gather(d["x"], p.row_src, wl.k, p.offsets,
+                                     p.s_perm, d["w_gate"], d["w_up"])
+    moe.debug_sync()
+    np.testing.assert_array_equal(p.offsets.cpu().numpy(), p_ref["offsets"])
+    np.testing.assert_array_equal(p.row_src.cpu().numpy()[:R], p_ref["row_src"])
+    np.testing.assert_array_equal(p.inv.cpu().numpy(), p_ref["inv"])
+    assert torch.equal(a_g[:R], a[:R])
+    print_case("c5-shape bf16 rows per expert", p_ref["counts"].tolist())
+    rng = np.random.default_rng(2)
+    off = p_ref["offsets"]
+    rows = set(rng.choice(R, 256, replace=False).tolist())
+    for e in range(wl.n_local):
+        if off[e + 1] > off[e]:
+            rows.update((int(off[e]), int(off[e + 1]) - 1))
+    rows = np.array(sorted(rows))
+    ex = (np.searchsorted(off, rows, side="right") - 1).astype(np.int32)
+    xs = inp["x"][p_ref["row_src"][rows] // wl.k]
+    s = w32.reshape(-1)[p_ref["row_src"][rows]].astype(np.float64)
+    a_ref, y_ref = orc.expert_ffn_rows(xs, ex, s, inp["w_gate"], inp["w_up"],
+                                       inp["w_down"])
+    ea = assert_close(to_f64(a[rows]), a_ref, "bf16", "c5-shape a")
+    ey = assert_close(to_f64(y[rows]), y_ref, "bf16", "c5-shape y")
+    toks = rng.choice(wl.T, 64, replace=False)
+    o_ref = orc.moe_tokens(inp["x"], ridx, w32.astype(np.float64), toks, 0,
+                           wl.n_local, inp["w_gate"], inp["w_up"], inp["w_down"])
+    eo = assert_close(to_f64(out[toks]), o_ref, "bf16", "c5-shape out")
+    print_case("c5-shape bf16", f"err/RMS a {ea:.2e} y {ey:.2e} out {eo:.2e}")

@@ -56,6 +56,13 @@ def test_presets_follow_the_pages_shapes():
     assert W["c3_ep8_bf16"].n_local == g["experts_per_layer"] / 8 == g["ep8_experts_per_gpu"]
     assert 1 - g["experts_per_token"] / W["c3_ep8_bf16"].n_local == g["ep8_cold_fraction"]
     assert W["c5_mxfp8"].E == g["mixtral_ep"] and W["c5_mxfp8"].H % g["mx_block"] == 0
+    # the two supplementary presets differ from their parents only where named
+    c3, c3l = W["c3_ep8_bf16"], W["c3_literal_ep8_bf16"]
+    assert (c3l.T, c3l.n_local) == (W["c2_ep64_bf16"].T, c3.n_local)
+    assert (c3l.H, c3l.I, c3l.E, c3l.k, c3l.zipf_s) == (c3.H, c3.I, c3.E, c3.k, c3.zipf_s)
+    c5, c5b = W["c5_mxfp8"], W["c5_shape_bf16"]
+    assert (c5b.T, c5b.H, c5b.I, c5b.E, c5b.k) == (c5.T, c5.H, c5.I, c5.E, c5.k)
+    assert c5b.dtype == "bf16" and c5b.router == c5.router and c5b.zipf_s is None
 
 
 def test_ep_share_rows_per_expert_ratio():
