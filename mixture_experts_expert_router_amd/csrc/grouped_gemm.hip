@@ -41,6 +41,8 @@
 //     rows, so each lane holds g and u of the same outputs; writes
 //     a = s * SiLU(g) * u in bf16), BF16 (plain store) and F32_BIAS (router
 //     logits + bias).
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -69,44 +71,63 @@ struct GemmArgs {
 // Experts with at most this many rows run on the 64-row-tile kernel.
 constexpr int kSmallRows = 64;
 
-// Per class c (0 = small, 1 = large): prefix_c[e+1] = prefix_c[e] +
-// ceil(rows_e / BM_c) * NT_c when expert e belongs to class c.  One block.
+// Tile prefixes per row class: prefix_c[e+1] = prefix_c[e] + ceil(rows_e /
+// BM_c) * NT_c when expert e belongs to class c.  Experts with at most
+// kSmallRows rows form the small class (0); the others are tiled either with
+// the wide shape (1) or with the narrow one (2).  Without prefix_narrow the
+// wide shape is used.  Otherwise the narrow one is used when the wide shape
+// would give fewer than wide_min tiles in all, and its tiles fit in
+// narrow_cap; the other shape's prefix is then all zeros.  One block.
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     const int32_t *__restrict__ offsets, int G, int bm_small, int nt_small,
-    int bm_large, int nt_large, int32_t *__restrict__ prefix_small,
-    int32_t *__restrict__ prefix_large) {
-  __shared__ int32_t part[2][1024];
+    int bm_wide, int nt_wide, int bm_narrow, int nt_narrow, int wide_min,
+    int narrow_cap, int32_t *__restrict__ prefix_small,
+    int32_t *__restrict__ prefix_wide, int32_t *__restrict__ prefix_narrow) {
+  __shared__ int32_t part[3][1024];
   const int tid = threadIdx.x;
   const int per = (G + 1023) / 1024;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
-  int32_t s0 = 0, s1 = 0;
-  for (int e = e0; e < e1; ++e) {
+  auto tiles = [&](int e, int32_t &t0, int32_t &t1, int32_t &t2) {
     const int n = offsets[e + 1] - offsets[e];
-    if (n <= kSmallRows) s0 += (n + bm_small - 1) / bm_small * nt_small;
-    else s1 += (n + bm_large - 1) / bm_large * nt_large;
+    t0 = t1 = t2 = 0;
+    if (n <= kSmallRows) {
+      t0 = (n + bm_small - 1) / bm_small * nt_small;
+    } else {
+      t1 = (n + bm_wide - 1) / bm_wide * nt_wide;
+      t2 = (n + bm_narrow - 1) / bm_narrow * nt_narrow;
+    }
+  };
+  int32_t s[3] = {0, 0, 0};
+  for (int e = e0; e < e1; ++e) {
+    int32_t t[3];
+    tiles(e, t[0], t[1], t[2]);
+    for (int c = 0; c < 3; ++c) s[c] += t[c];
   }
-  part[0][tid] = s0;
-  part[1][tid] = s1;
+  for (int c = 0; c < 3; ++c) part[c][tid] = s[c];
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
-    const int32_t v0 = tid >= off ? part[0][tid - off] : 0;
-    const int32_t v1 = tid >= off ? part[1][tid - off] : 0;
+    int32_t v[3];
+    for (int c = 0; c < 3; ++c) v[c] = tid >= off ? part[c][tid - off] : 0;
     __syncthreads();
-    part[0][tid] += v0;
-    part[1][tid] += v1;
+    for (int c = 0; c < 3; ++c) part[c][tid] += v[c];
     __syncthreads();
   }
-  int32_t r0 = part[0][tid] - s0, r1 = part[1][tid] - s1;
+  const bool narrow = prefix_narrow != nullptr && part[1][1023] < wide_min &&
+                      part[2][1023] <= narrow_cap;
+  int32_t r[3];
+  for (int c = 0; c < 3; ++c) r[c] = part[c][tid] - s[c];
   for (int e = e0; e < e1; ++e) {
-    prefix_small[e] = r0;
-    prefix_large[e] = r1;
-    const int n = offsets[e + 1] - offsets[e];
-    if (n <= kSmallRows) r0 += (n + bm_small - 1) / bm_small * nt_small;
-    else r1 += (n + bm_large - 1) / bm_large * nt_large;
+    prefix_small[e] = r[0];
+    prefix_wide[e] = narrow ? 0 : r[1];
+    if (prefix_narrow) prefix_narrow[e] = narrow ? r[2] : 0;
+    int32_t t[3];
+    tiles(e, t[0], t[1], t[2]);
+    for (int c = 0; c < 3; ++c) r[c] += t[c];
   }
   if (tid == 1023) {
     prefix_small[G] = part[0][1023];
-    prefix_large[G] = part[1][1023];
+    prefix_wide[G] = narrow ? 0 : part[1][1023];
+    if (prefix_narrow) prefix_narrow[G] = narrow ? part[2][1023] : 0;
   }
 }
 
@@ -438,23 +459,33 @@ hipError_t launch_one(GemmArgs p, int num_cus, int64_t max_tiles,
 }
 
 // Tile shapes.  Large experts: 128 rows x 256 B-rows (BK 64, 3 stages), or
-// 256 x 64 (BK 64, 3 stages) when there are too few experts to give every CU
-// two n-tiles of the wide shape.  Small experts: 64 x 256 (BK 64, 3 stages).
+// 256 x 64 (BK 64, 3 stages) when the wide shape would give fewer than two
+// tiles per CU.  Small experts: 64 x 256 (BK 64, 3 stages).  When the host
+// cannot rule the narrow shape out (few experts times n-tiles), the plan
+// kernel chooses from the actual rows and both kernels are launched; the one
+// not chosen finds no tiles.
 template <int EPI>
 hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
                           int64_t R_cap, hipStream_t s) {
   const bool sw = EPI == EPI_SWIGLU;
   constexpr int wide_cfg[6] = {MOE_WIDE_CFG};
-  constexpr int WBM = wide_cfg[0], WBN = wide_cfg[1];
-  const bool wide = (int64_t)p.G * ntiles(p.N, WBN, sw) >= 2LL * num_cus;
   constexpr int narrow_cfg[6] = {MOE_NARROW_CFG};
-  const int bm_l = wide ? WBM : narrow_cfg[0];
-  const int nt_l = ntiles(p.N, wide ? WBN : narrow_cfg[1], sw);
+  constexpr int WBM = wide_cfg[0], WBN = wide_cfg[1];
+  constexpr int NBM = narrow_cfg[0], NBN = narrow_cfg[1];
+  const int wide_min = 2 * num_cus;
+  const int nt_w = ntiles(p.N, WBN, sw), nt_n = ntiles(p.N, NBN, sw);
   const int nt_s = ntiles(p.N, 256, sw);
+  const bool wide_sure = (int64_t)p.G * nt_w >= wide_min;
+  // The narrow kernel's grid; the plan kernel keeps the wide shape when the
+  // narrow one would need more tiles than this.
+  const int64_t max_n = ((R_cap + NBM - 1) / NBM + p.G) * (int64_t)nt_n;
+  const int narrow_cap = (int)std::min<int64_t>(max_n, 8LL * num_cus);
   int32_t *pre_s = tile_ws;
-  int32_t *pre_l = tile_ws + (p.G + 1);
-  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, 64, nt_s, bm_l, nt_l,
-                                      pre_s, pre_l);
+  int32_t *pre_w = tile_ws + (p.G + 1);
+  int32_t *pre_n = tile_ws + 2 * (p.G + 1);
+  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, 64, nt_s, WBM, nt_w,
+                                      NBM, nt_n, wide_min, narrow_cap, pre_s,
+                                      pre_w, wide_sure ? nullptr : pre_n);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // small-row class
@@ -465,19 +496,24 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
                                               (int64_t)p.G * nt_s, s);
   if (err != hipSuccess) return err;
   // large-row class
-  GemmArgs pl = p;
-  pl.tile_prefix = pre_l;
-  pl.NT = nt_l;
-  const int64_t max_l = ((R_cap + bm_l - 1) / bm_l + p.G) * (int64_t)nt_l;
-  if (wide)
-    return launch_one<MOE_WIDE_CFG, EPI>(pl, num_cus, max_l, s);
-  return launch_one<MOE_NARROW_CFG, EPI>(pl, num_cus, max_l, s);
+  if (!wide_sure) {
+    GemmArgs pn = p;
+    pn.tile_prefix = pre_n;
+    pn.NT = nt_n;
+    err = launch_one<MOE_NARROW_CFG, EPI>(pn, num_cus, narrow_cap, s);
+    if (err != hipSuccess) return err;
+  }
+  GemmArgs pw = p;
+  pw.tile_prefix = pre_w;
+  pw.NT = nt_w;
+  const int64_t max_w = ((R_cap + WBM - 1) / WBM + p.G) * (int64_t)nt_w;
+  return launch_one<MOE_WIDE_CFG, EPI>(pw, num_cus, max_w, s);
 }
 
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t n_local) {
-  return (size_t)((2 * (n_local + 1) * 4 + 255) / 256 * 256);
+  return (size_t)((3 * (n_local + 1) * 4 + 255) / 256 * 256);
 }
 
 hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
