@@ -203,7 +203,11 @@ __device__ __forceinline__ void mx_quant_staged(const uint16_t *l, uint8_t *q,
 // region rows down each column.  Block b of column c goes to codes
 // qt[(col0 + c) * ldt + pos0 + 32 b] and scale qts[(col0 + c) * ldts +
 // (pos0 + 32 b) / 32]; region rows at or past `valid` count as zeros (the
-// segment's padding).  Two neighbouring lanes write one column's 64 bytes.
+// segment's padding).  Pass it handles block b of 64 neighbouring columns,
+// one per lane, so each of its 32 LDS reads covers 128 contiguous bytes of
+// one region row; every read is issued unconditionally (rows past `valid`
+// are read and then replaced by zero), so the reads are all in flight
+// together instead of each behind its own branch and wait.
 template <int W, int NROWS>
 __device__ __forceinline__ void mx_quant_staged_cols(const uint16_t *l,
                                                      uint8_t *qt, uint8_t *qts,
@@ -211,17 +215,17 @@ __device__ __forceinline__ void mx_quant_staged_cols(const uint16_t *l,
                                                      int64_t col0, int64_t pos0,
                                                      int valid, int lane) {
   constexpr int BPC = NROWS / 32;              // blocks per column
-  static_assert(NROWS % 32 == 0 && (W * BPC) % 64 == 0, "region");
+  static_assert(NROWS % 32 == 0 && W % 64 == 0, "region");
 #pragma unroll 1
-  for (int it = 0; it < W * BPC / 64; ++it) {
-    const int item = it * 64 + lane;
-    const int c = item / BPC, b = item % BPC;
+  for (int it = 0; it < (W / 64) * BPC; ++it) {
+    const int b = it % BPC, c = (it / BPC) * 64 + lane;
     float v[32];
     float amax = 0.f;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const int r = b * 32 + j;
-      v[j] = r < valid ? bf16_bits_to_f32(l[r * W + st_col<W>(r, c)]) : 0.f;
+      const float x = bf16_bits_to_f32(l[r * W + st_col<W>(r, c)]);
+      v[j] = r < valid ? x : 0.f;
       amax = fmaxf(amax, fabsf(v[j]));
     }
     const int X = mx_shared_exp(amax);
