@@ -30,26 +30,39 @@ __device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c,
   return (uint32_t)r;
 }
 
-// Codes and scale byte of 32 bf16 values (bit patterns, 16 per uint4 pair
-// half): codes[0..7] get the packed bytes, the return value the scale byte.
+// Shared exponent X from the bf16 bit pattern of a block's largest
+// magnitude (sign bit clear, finite).  With exponent field E >= 1 the value
+// lies in [2^(E-127), 2^(E-126)), so X = E - 127 - 8; below 2^-118 (E < 9,
+// zero and subnormals included) X takes the floor -127.  For a bf16 amax
+// this equals mx_shared_exp of its fp32 value.
+__device__ __forceinline__ int mx_shared_exp_bf16(uint32_t mag) {
+  const int E = (int)(mag >> 7);
+  return E >= 9 ? E - 135 : -127;
+}
+
+// Codes and scale byte of 32 bf16 values (bit patterns, two per word, low
+// half first): codes[0..7] get the packed bytes, the return value the scale
+// byte.  The largest magnitude is found on the bit patterns (for values of
+// one sign, integer order is float order), and each value is widened to
+// fp32 only where it is encoded, so no 32-value fp32 copy is held.
 __device__ __forceinline__ uint32_t mx_encode32(const uint4 (&in)[4], uint32_t (&codes)[8]) {
-  float v[32];
+  uint32_t mag = 0;
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const uint32_t u[4] = {in[q].x, in[q].y, in[q].z, in[q].w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      v[q * 8 + 2 * j] = bf16_bits_to_f32(u[j] & 0xffffu);
-      v[q * 8 + 2 * j + 1] = bf16_bits_to_f32(u[j] >> 16);
-    }
+    for (int j = 0; j < 4; ++j) mag = max(mag, max(u[j] & 0x7fffu, (u[j] >> 16) & 0x7fffu));
   }
-  float amax = 0.f;
+  const int X = mx_shared_exp_bf16(mag);
 #pragma unroll
-  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  const int X = mx_shared_exp(amax);
+  for (int q = 0; q < 4; ++q) {
+    const uint32_t u[4] = {in[q].x, in[q].y, in[q].z, in[q].w};
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    codes[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], -X);
+    for (int j = 0; j < 2; ++j)
+      codes[2 * q + j] = e4m3_pack4(
+          bf16_bits_to_f32(u[2 * j] & 0xffffu), bf16_bits_to_f32(u[2 * j] >> 16),
+          bf16_bits_to_f32(u[2 * j + 1] & 0xffffu), bf16_bits_to_f32(u[2 * j + 1] >> 16), -X);
+  }
   return (uint32_t)(X + 127);
 }
 

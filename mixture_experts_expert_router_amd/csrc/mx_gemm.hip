@@ -179,7 +179,7 @@ __device__ __forceinline__ void mx_quant_staged(const uint16_t *l, uint8_t *q,
                                                 int rows, int lane) {
   static_assert(W % 32 == 0 && (NROWS * W / 32) % 64 == 0, "region");
   constexpr int BPR = W / 32;                  // blocks per row
-#pragma unroll
+#pragma unroll 1
   for (int it = 0; it < NROWS * BPR / 64; ++it) {
     const int item = it * 64 + lane;
     const int r = item / BPR, b = item % BPR;
@@ -219,20 +219,21 @@ __device__ __forceinline__ void mx_quant_staged_cols(const uint16_t *l,
 #pragma unroll 1
   for (int it = 0; it < (W / 64) * BPC; ++it) {
     const int b = it % BPC, c = (it / BPC) * 64 + lane;
-    float v[32];
-    float amax = 0.f;
+    uint32_t v[32];                            // bf16 bit patterns
+    uint32_t mag = 0;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const int r = b * 32 + j;
-      const float x = bf16_bits_to_f32(l[r * W + st_col<W>(r, c)]);
-      v[j] = r < valid ? x : 0.f;
-      amax = fmaxf(amax, fabsf(v[j]));
+      const uint32_t x = l[r * W + st_col<W>(r, c)];
+      v[j] = r < valid ? x : 0u;
+      mag = max(mag, v[j] & 0x7fffu);
     }
-    const int X = mx_shared_exp(amax);
+    const int X = mx_shared_exp_bf16(mag);
     uint32_t pk[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      pk[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], -X);
+      pk[j] = e4m3_pack4(bf16_bits_to_f32(v[4 * j]), bf16_bits_to_f32(v[4 * j + 1]),
+                         bf16_bits_to_f32(v[4 * j + 2]), bf16_bits_to_f32(v[4 * j + 3]), -X);
     uint4 *dst = (uint4 *)(qt + (col0 + c) * ldt + pos0 + 32 * b);
     dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
     dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
