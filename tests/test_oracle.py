@@ -378,6 +378,50 @@ def test_mlp_step_backward_finite_differences():
     assert not res["dw_gate"][1].any() and not res["dw_down"][1].any()
 
 
+def test_mlp_step_backward_adjoint_identity():
+    # Dot-product test of the backward: for random directions V of every
+    # input, <dY, J V> (J the forward's Jacobian, its product with V written
+    # out here in forward mode, per expert) equals the sum of <grad, V> over
+    # the oracle's gradients.  A transposed operand, a dropped term or a wrong
+    # sign in any gradient breaks the identity.
+    x, offs, s, wg, wu, wd, dy = _mlp_inputs(R=14, H=8, I=6, n_local=3)
+    offs = np.array([0, 6, 6, 14])
+    res = orc.mxfp8_mlp_step(x, offs, s, wg, wu, wd, dy, quantize=False)
+    vx, vs = rng.standard_normal(x.shape), rng.standard_normal(s.shape)
+    vg, vu, vd = (rng.standard_normal(w.shape) for w in (wg, wu, wd))
+    jv = np.zeros_like(dy)
+    for e in range(3):
+        r = slice(offs[e], offs[e + 1])
+        g, u = x[r] @ wg[e].T, x[r] @ wu[e].T
+        sig = 1.0 / (1.0 + np.exp(-g))
+        silu, dsilu = g * sig, sig * (1.0 + g * (1.0 - sig))
+        dg = vx[r] @ wg[e].T + x[r] @ vg[e].T
+        du = vx[r] @ wu[e].T + x[r] @ vu[e].T
+        a = s[r, None] * silu * u
+        da = vs[r, None] * silu * u + s[r, None] * (dsilu * dg * u + silu * du)
+        jv[r] = da @ wd[e].T + a @ vd[e].T
+    lhs = float((dy * jv).sum())
+    rhs = float((res["dx"] * vx).sum() + (res["ds"] * vs).sum()
+                + (res["dw_gate"] * vg).sum() + (res["dw_up"] * vu).sum()
+                + (res["dw_down"] * vd).sum())
+    assert abs(lhs - rhs) <= 1e-10 * max(1.0, abs(lhs))
+
+
+def test_ffn_linear_in_scale_and_down_weights():
+    # a = s * SiLU(g) * u is linear in the routing scale s, and y = a W_d^T
+    # is linear in W_d; powers of two keep both identities exact in fp64.
+    x, offs, s, wg, wu, wd, dy = _mlp_inputs()
+    ex = np.repeat(np.arange(3, dtype=np.int32), np.diff(offs))
+    a1, y1 = orc.expert_ffn_rows(x, ex, s, wg, wu, wd)
+    a2, y2 = orc.expert_ffn_rows(x, ex, 4.0 * s, wg, wu, wd)
+    np.testing.assert_array_equal(a2, 4.0 * a1)
+    np.testing.assert_array_equal(y2, 4.0 * y1)
+    wd2 = rng.standard_normal(wd.shape) * 0.2
+    _, y3 = orc.expert_ffn_rows(x, ex, s, wg, wu, wd2)
+    _, y4 = orc.expert_ffn_rows(x, ex, s, wg, wu, wd + wd2)
+    np.testing.assert_allclose(y4, y1 + y3, rtol=1e-12, atol=1e-12)
+
+
 def test_swiglu_textbook_values():
     dg, du, ds = orc.swiglu_bwd(np.ones((1, 1)), np.zeros((1, 1)),
                                 np.ones((1, 1)), np.ones(1))
