@@ -305,7 +305,7 @@ bool mx_shape_ok(int64_t n_local, int64_t R_cap, int64_t H, int64_t I) {
 }
 
 // Row capacity of transposed (column-quantised) expert segments padded
-// to 512 rows each.
+// to 512 rows each (also enough for padding to 256).
 int64_t mx_kpad_cap(int64_t R_cap, int64_t n_local) {
   return (R_cap + 511 * n_local + 511) / 512 * 512;
 }
