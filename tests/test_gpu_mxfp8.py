@@ -325,3 +325,55 @@ def test_mxfp8_experts_without_rows():
         for e in (1, 3):
             _frob(to_f64(g[key][e]), ref[key][e], f"empty-expert {key}[{e}]", bad)
     assert not bad, bad
+
+
+def test_mxfp8_tiny_ragged_segments():
+    """Segments of 3, 0, 1 and 37 rows at the smallest shapes (H = I = 512):
+    every tile is mostly padding and the weight-gradient K ranges are one
+    256-row block or empty.  The fused calls equal the stage calls bit for
+    bit; a, ds and the aggregate y, dX meet the oracle; the weight gradients
+    are checked row by row on the oracle's own bf16 hand-off tensors (with
+    one or three rows a segment's MX blocks hold single values, so a code
+    decided differently on the two sides would not average out)."""
+    wl = synth.WORKLOADS["small_mxfp8"]
+    counts = [3, 0, 1, 37]
+    R = sum(counts)
+    inp = synth.make_inputs(wl, tokens=R)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    x_perm = inp["x"]
+    s = np.random.default_rng(5).uniform(0.05, 1.0, R).astype(np.float32)
+    dy = synth.make_dy(wl, R)
+    ref = orc.mxfp8_mlp_step(x_perm, offsets, s.astype(np.float64),
+                             inp["w_gate"], inp["w_up"], inp["w_down"], dy)
+    d = {k: to_dev(inp[k]) for k in ("w_gate", "w_up", "w_down")}
+    mw = moe.MxWeights(d["w_gate"], d["w_up"], d["w_down"])
+    offs, st, xt, dyt = to_dev(offsets), to_dev(s), to_dev(x_perm), to_dev(dy)
+    print_case("small_mxfp8 segments", counts)
+    xq, xs = moe.mxfp8_quantize(xt, 0)
+    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, offs, st, mw)
+    g = moe.mxfp8_mlp_bwd(dyt, xt, a, gu, offs, st, mw)
+    d1 = moe.mxfp8_mlp_bwd_down(dyt, a, gu, offs, st, mw)
+    d2 = moe.mxfp8_mlp_bwd_gate_up(d1["dgu"], xt, offs, mw)
+    # the weight gradients on the oracle's hand-off tensors
+    gu_ref = np.concatenate([_bits(ref["g"]), _bits(ref["u"])], axis=1)
+    h1 = moe.mxfp8_mlp_bwd_down(dyt, to_dev(_bits(ref["a"])), to_dev(gu_ref),
+                                offs, st, mw)
+    dgu_ref = np.concatenate([_bits(ref["dg"]), _bits(ref["du"])], axis=1)
+    h2 = moe.mxfp8_mlp_bwd_gate_up(to_dev(dgu_ref), xt, offs, mw)
+    moe.debug_sync()
+    for key in ("dw_gate", "dw_up", "dw_down"):
+        assert not g[key][1].any(), key
+    assert torch.equal(g["dw_down"], d1["dw_down"])
+    assert torch.equal(g["dx"][:R], d2["dx"][:R])
+    assert torch.equal(g["dw_gate"], d2["dw_gate"])
+    assert torch.equal(g["dw_up"], d2["dw_up"])
+    bad = []
+    _check(to_f64(a[:R]), ref["a"], "tiny a", bad)
+    _check(g["ds"][:R].cpu().numpy().astype(np.float64), ref["ds"], "tiny ds", bad)
+    _frob(to_f64(y[:R]), ref["y"], "tiny y", bad)
+    _frob(to_f64(g["dx"][:R]), ref["dx"], "tiny dx", bad)
+    for e in (0, 2, 3):
+        _check(to_f64(h1["dw_down"][e]), ref["dw_down"][e], f"tiny dw_down[{e}]", bad)
+        _check(to_f64(h2["dw_gate"][e]), ref["dw_gate"][e], f"tiny dw_gate[{e}]", bad)
+        _check(to_f64(h2["dw_up"][e]), ref["dw_up"][e], f"tiny dw_up[{e}]", bad)
+    assert not bad, bad
