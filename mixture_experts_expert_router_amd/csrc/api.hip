@@ -123,11 +123,7 @@ int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
   if (!aligned16(workspace)) return MOE_E_ALIGN;
   if (T == 0) {
     // nothing routed: zero counts and offsets on the device
-    if (hipMemsetAsync(counts, 0, (size_t)n_local * 4, stream) != hipSuccess ||
-        hipMemsetAsync(offsets, 0, (size_t)(n_local + 1) * 4, stream) !=
-            hipSuccess)
-      return MOE_E_HIP;
-    return MOE_OK;
+    return status_of(moe::launch_permute_empty(counts, offsets, n_local, stream));
   }
   return status_of(moe::launch_permute(
       topk_idx, topk_w, x, T, k, row_bytes, e_begin, n_local, x_perm, s_perm,

@@ -21,6 +21,8 @@ hipError_t launch_topk(const float *logits, int64_t T, int E, int k,
                        int32_t *idx, float *w, hipStream_t s);
 
 size_t permute_workspace_bytes(int64_t T, int64_t k, int64_t n_local);
+hipError_t launch_permute_empty(int32_t *counts, int32_t *offsets,
+                                int64_t n_local, hipStream_t s);
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
                           int64_t T, int64_t k, int64_t row_bytes,
                           int64_t e_begin, int64_t n_local, void *x_perm,

@@ -148,6 +148,25 @@ int permute_chunk(int64_t F, int64_t n_local) {
   return n_local <= 64 ? 256 : 1024;
 }
 
+// counts[0, n) = 0 and offsets[0, n] = 0 (an empty batch).  A kernel rather
+// than a memset, so that a caller may capture the call in a graph.
+__global__ __launch_bounds__(256) void permute_zero_kernel(int32_t *counts,
+                                                           int32_t *offsets,
+                                                           int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i <= n; i += gridDim.x * 256) {
+    if (i < n) counts[i] = 0;
+    offsets[i] = 0;
+  }
+}
+
+hipError_t launch_permute_empty(int32_t *counts, int32_t *offsets,
+                                int64_t n_local, hipStream_t s) {
+  const int64_t blocks = (n_local + 1 + 255) / 256;
+  permute_zero_kernel<<<(unsigned)(blocks < 64 ? blocks : 64), 256, 0, s>>>(
+      counts, offsets, (int)n_local);
+  return hipGetLastError();
+}
+
 size_t permute_workspace_bytes(int64_t T, int64_t k, int64_t n_local) {
   const int64_t F = T * k;
   const int chunk = permute_chunk(F, n_local);
