@@ -243,3 +243,58 @@ def test_bitwise_deterministic():
     for key in ("a", "y"):
         assert torch.equal(g1[key][:R], g2[key][:R]), key
     assert torch.equal(g1["p"].row_src[:R], g2["p"].row_src[:R])
+
+
+def test_step_captured_in_a_graph_replays_bit_exactly():
+    """The whole bf16 step (router GEMM + top-k, permute, gate/up, down,
+    combine) captured once in a HIP graph and replayed: every replay, with
+    eager work and synchronisation between replays, gives the eager result
+    bit for bit (the path launches kernels only, no memsets or host syncs)."""
+    wl = synth.WORKLOADS["mid_bf16"]
+    print_case("graph capture", wl.name)
+    inp = synth.make_inputs(wl)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    dev = d["x"].device
+    T, k, H, I = wl.T, wl.k, wl.H, wl.I
+    F = T * k
+    logits = torch.empty((T, wl.E), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    w = torch.empty((T, k), dtype=torch.float32, device=dev)
+    pout = moe.PermuteOut(T, k, H, wl.n_local, torch.bfloat16, dev)
+    a = torch.empty((F, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((F, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    ws = moe.ffn_workspace(F, wl.n_local, H, I, torch.bfloat16, dev)
+
+    def step():
+        moe.route_topk(k, logits=logits, x=d["x"], w_router=d["w_router"],
+                       bias=d.get("bias"), topk_idx=idx, topk_w=w)
+        moe.permute(idx, d["x"], wl.e_begin, wl.n_local, topk_w=w, out=pout)
+        moe.grouped_gate_up(pout.x_perm, pout.offsets, pout.s_perm,
+                            d["w_gate"], d["w_up"], a=a, workspace=ws)
+        moe.grouped_down(a, pout.offsets, d["w_down"], y=y, workspace=ws)
+        moe.unpermute_combine(y, pout.inv, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref = out.clone()
+    ref_idx = idx.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(4):
+        out.zero_()
+        idx.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(idx, ref_idx), rep
+        assert torch.equal(out, ref), rep
+        # eager work between the replays
+        _ = (d["x"].float() @ d["w_router"].float().T).sum().item()
