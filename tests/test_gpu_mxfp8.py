@@ -377,3 +377,67 @@ def test_mxfp8_tiny_ragged_segments():
         _check(to_f64(h2["dw_gate"][e]), ref["dw_gate"][e], f"tiny dw_gate[{e}]", bad)
         _check(to_f64(h2["dw_up"][e]), ref["dw_up"][e], f"tiny dw_up[{e}]", bad)
     assert not bad, bad
+
+
+def test_mxfp8_step_captured_in_a_graph_replays_bit_exactly(case):
+    """Quantise x, fused forward, fused backward captured in one HIP graph:
+    every replay (eager work and synchronisation between them) equals the
+    eager step bit for bit."""
+    c, R = case, case["p"]["R"]
+    wl = c["wl"]
+    xt = to_dev(c["x_perm"])
+    dyt = to_dev(c["dy"])
+    R_cap, H = xt.shape
+    I, n = wl.I, wl.n_local
+    bf = torch.bfloat16
+    dev = xt.device
+    xq = torch.empty((R_cap, H), dtype=torch.uint8, device=dev)
+    xs = torch.empty((R_cap, H // 32), dtype=torch.uint8, device=dev)
+    a = torch.empty((R_cap, I), dtype=bf, device=dev)
+    gu = torch.empty((R_cap, 2 * I), dtype=bf, device=dev)
+    y = torch.empty((R_cap, H), dtype=bf, device=dev)
+    outs = dict(dx=torch.empty((R_cap, H), dtype=bf, device=dev),
+                ds=torch.empty(R_cap, dtype=torch.float32, device=dev),
+                dw_gate=torch.empty((n, I, H), dtype=bf, device=dev),
+                dw_up=torch.empty((n, I, H), dtype=bf, device=dev),
+                dw_down=torch.empty((n, H, I), dtype=bf, device=dev))
+    L = moe.lib()
+    ws_f = torch.empty(L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes(R_cap, n, H, I),
+                       dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes(R_cap, n, H, I),
+                       dtype=torch.uint8, device=dev)
+
+    def step():
+        moe.mxfp8_quantize(xt, 0, codes=xq, scales=xs)
+        moe.mxfp8_mlp_fwd(xq, xs, c["offs"], c["st"], c["mw"], a=a, gu=gu, y=y,
+                          workspace=ws_f)
+        moe.mxfp8_mlp_bwd(dyt, xt, a, gu, c["offs"], c["st"], c["mw"],
+                          workspace=ws_b, **outs)
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in outs.items()}
+    ref["y"] = y.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    print_case(c["name"], "graph replays")
+    for rep in range(3):
+        for v in outs.values():
+            v.zero_()
+        y.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y[:R], ref["y"][:R]), rep
+        assert torch.equal(outs["dx"][:R], ref["dx"][:R]), rep
+        assert torch.equal(outs["ds"][:R], ref["ds"][:R]), rep
+        for key in ("dw_gate", "dw_up", "dw_down"):
+            assert torch.equal(outs[key], ref[key]), (rep, key)
+        _ = (xt.float().sum() + dyt.float().sum()).item()
