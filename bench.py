@@ -126,6 +126,34 @@ def algorithmic(wl, R, n_touched, gather=True):
                 step_bytes=step_bytes)
 
 
+def graph_ms_per_step(steps_fn, n_steps, reps):
+    """Milliseconds per step when `steps_fn` (which runs `n_steps` steps) is
+    captured once in a HIP graph and replayed `reps` times: the step without
+    host launch overhead.  None if the capture fails."""
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            steps_fn()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            steps_fn()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / (reps * n_steps)
+        del g
+        return round(ms, 4)
+    except RuntimeError as exc:           # capture not possible here
+        log(f"graph capture failed: {exc}")
+        return None
+
+
 def percentiles(ms):
     """p10 / median / p90 of per-step event times (ms)."""
     q = np.percentile(np.asarray(ms, dtype=np.float64), [10, 50, 90])
@@ -284,6 +312,8 @@ def run_mx(args, wl, dev):
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     gu_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     step_pct = percentiles([e[0].elapsed_time(e[3]) for e in ev])
+    graph_ms = (None if args.no_graph else
+                graph_ms_per_step(step, 1, max(1, args.steps)))
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
@@ -317,6 +347,7 @@ def run_mx(args, wl, dev):
         "step_mfma_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
         "master_quant_ms": round(master_ms, 4),
         "step_ms_events": step_pct,
+        "step_ms_graph": graph_ms,
         "roofline": {
             "kernel": "MXFP8 grouped gate/up GEMM + SwiGLU x scale (forward)",
             "bound": "mfma",
@@ -354,6 +385,9 @@ def main():
                     help="full layer: permute writes x_perm and the gate/up "
                          "GEMM reads it, instead of reading token rows of x "
                          "through row_src (EP shares always read x_perm)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the extra timing of the step replayed from a "
+                         "captured HIP graph (step_ms_graph)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one elementwise copy of this many "
                          "MiB (read + write) to calibrate HBM byte counters")
@@ -452,6 +486,13 @@ def main():
     step_pct = percentiles([e[0].elapsed_time(e[4]) for e in ev])
     ffn_pct = percentiles([e[1].elapsed_time(e[3]) for e in ev])
 
+    def rotation():                    # one step per weight copy
+        for i in range(len(wcopies)):
+            step(i)
+    graph_ms = (None if args.no_graph else
+                graph_ms_per_step(rotation, len(wcopies),
+                                  max(1, args.steps // len(wcopies))))
+
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
@@ -501,6 +542,7 @@ def main():
         "step_hbm_frac": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
         "step_ms_events": step_pct,
+        "step_ms_graph": graph_ms,
         "ffn_ms_events": ffn_pct,
         "ffn_tflops_p50": round(alg["flop_ffn"] / (ffn_pct["p50"] * 1e-3) / 1e12, 2),
         "roofline": dict(**gate_up_bound, **{
