@@ -10,9 +10,12 @@ c2_ep64_bf16 | c3_ep8_bf16) route before the timed region and time permute
 step.
 
 Prints one JSON line.  `value` is the grouped-FFN (+ router) TFLOP/s of the
-whole step with inputs resident in HBM; `roofline` is for the dominant kernel
-(the grouped gate/up GEMM), timed with HIP events on its stream; `cpu_baseline`
-is the CPU oracle timed on a bounded sample of the same workload.
+whole step with inputs resident in HBM, timed over exactly K steps replayed
+from a HIP graph of the step (the same kernels without host launch overhead;
+--no-graph times eager launches, and the eager time is reported beside it);
+`roofline` is for the dominant kernel (the grouped gate/up GEMM), timed with
+HIP events on its stream during K eager steps; `cpu_baseline` is the CPU
+oracle timed on a bounded sample of the same workload.
 """
 import argparse
 import json
@@ -33,6 +36,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 (MX-scaled) MFMA
 METRIC = "grouped MoE FFN TFLOP/s + rows/s per layer; % MFMA peak or % HBM BW"
+TIMING_GRAPH = ("K replays of the step captured in a HIP graph (same kernels, no host "
+                "launch overhead), after W eager warmup steps and K eager steps timed "
+                "with HIP events")
+TIMING_EAGER = "K eager steps"
 
 
 def measured_traffic(workload):
@@ -126,32 +133,41 @@ def algorithmic(wl, R, n_touched, gather=True):
                 step_bytes=step_bytes)
 
 
-def graph_ms_per_step(steps_fn, n_steps, reps):
-    """Milliseconds per step when `steps_fn` (which runs `n_steps` steps) is
-    captured once in a HIP graph and replayed `reps` times: the step without
-    host launch overhead.  None if the capture fails."""
+def capture_steps(step_fns):
+    """One HIP graph per callable (each runs one step with preallocated
+    buffers), or None when capture is not possible here."""
     try:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            steps_fn()
+            for fn in step_fns:
+                fn()
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            steps_fn()
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(reps):
+        graphs = []
+        for fn in step_fns:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            graphs.append(g)
+        for g in graphs:
             g.replay()
         torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / (reps * n_steps)
-        del g
-        return round(ms, 4)
+        return graphs
     except RuntimeError as exc:           # capture not possible here
-        log(f"graph capture failed: {exc}")
+        log(f"graph capture failed, timing eager launches: {exc}")
         return None
+
+
+def time_graph_steps(graphs, steps):
+    """Milliseconds per step over exactly `steps` replays (graph j % n for
+    step j), bracketed by device synchronisation."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(steps):
+        graphs[j % len(graphs)].replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
 
 
 def percentiles(ms):
@@ -309,11 +325,12 @@ def run_mx(args, wl, dev):
     for i in range(args.steps):
         step(ev[i])
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     gu_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     step_pct = percentiles([e[0].elapsed_time(e[3]) for e in ev])
-    graph_ms = (None if args.no_graph else
-                graph_ms_per_step(step, 1, max(1, args.steps)))
+    graphs = None if args.no_graph else capture_steps([step])
+    ms_step = time_graph_steps(graphs, args.steps) if graphs else ms_eager
+    timing = TIMING_GRAPH if graphs else TIMING_EAGER
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
@@ -346,8 +363,9 @@ def run_mx(args, wl, dev):
         "step_mfma_frac_fp8": round(tflops / FP8_PEAK_TFLOPS, 4),
         "step_mfma_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
         "master_quant_ms": round(master_ms, 4),
+        "timing": timing,
+        "ms_per_step_eager": round(ms_eager, 4),
         "step_ms_events": step_pct,
-        "step_ms_graph": graph_ms,
         "roofline": {
             "kernel": "MXFP8 grouped gate/up GEMM + SwiGLU x scale (forward)",
             "bound": "mfma",
@@ -386,8 +404,8 @@ def main():
                          "GEMM reads it, instead of reading token rows of x "
                          "through row_src (EP shares always read x_perm)")
     ap.add_argument("--no-graph", action="store_true",
-                    help="skip the extra timing of the step replayed from a "
-                         "captured HIP graph (step_ms_graph)")
+                    help="time eager launches instead of replays of the step "
+                         "captured in a HIP graph")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one elementwise copy of this many "
                          "MiB (read + write) to calibrate HBM byte counters")
@@ -480,18 +498,16 @@ def main():
     for i in range(args.steps):
         step(i, ev[i])
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_step = elapsed * 1e3 / args.steps
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     gate_up_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     step_pct = percentiles([e[0].elapsed_time(e[4]) for e in ev])
     ffn_pct = percentiles([e[1].elapsed_time(e[3]) for e in ev])
 
-    def rotation():                    # one step per weight copy
-        for i in range(len(wcopies)):
-            step(i)
-    graph_ms = (None if args.no_graph else
-                graph_ms_per_step(rotation, len(wcopies),
-                                  max(1, args.steps // len(wcopies))))
+    # the same steps replayed from captured graphs, one per weight copy
+    graphs = (None if args.no_graph else
+              capture_steps([lambda i=i: step(i) for i in range(len(wcopies))]))
+    ms_step = time_graph_steps(graphs, args.steps) if graphs else ms_eager
+    timing = TIMING_GRAPH if graphs else TIMING_EAGER
 
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
@@ -541,8 +557,9 @@ def main():
         "step_hbm_gbs": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9, 1),
         "step_hbm_frac": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "step_mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+        "timing": timing,
+        "ms_per_step_eager": round(ms_eager, 4),
         "step_ms_events": step_pct,
-        "step_ms_graph": graph_ms,
         "ffn_ms_events": ffn_pct,
         "ffn_tflops_p50": round(alg["flop_ffn"] / (ffn_pct["p50"] * 1e-3) / 1e12, 2),
         "roofline": dict(**gate_up_bound, **{
