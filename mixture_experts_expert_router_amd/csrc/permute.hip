@@ -40,43 +40,62 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(
 // Exclusive scan of hist[n_local * nblk] (expert-major), in place, one block
 // of 1024 threads.  Also writes offsets[0..n_local] and counts[0..n_local).
 // The array is walked in tiles of 4096 entries, four consecutive entries per
-// thread (so a wavefront's loads and stores cover contiguous 1 KB), with a
-// block scan per tile and a running carry.
+// thread (so a wavefront's loads and stores cover contiguous 1 KB).  Per
+// tile: an inclusive scan of the thread sums inside each wavefront (lane
+// shuffles), the 16 wavefront totals through LDS, and a running carry, so a
+// tile costs two barriers; the next tile's loads overlap the current scan.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
     int32_t *__restrict__ hist, int n_local, int nblk,
     int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
-  __shared__ int32_t part[1024];
+  constexpr int NWAVE = 1024 / 64;
+  __shared__ int32_t wsum[NWAVE];
   __shared__ int32_t offs[4097];
   const int64_t total = (int64_t)n_local * nblk;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   int32_t carry = 0;
+  int32_t v[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) v[j] = 4 * tid + j < total ? hist[4 * tid + j] : 0;
   for (int64_t base = 0; base < total; base += 4096) {
     const int64_t i0 = base + 4 * tid;
-    int32_t v[4];
+    // the next tile's entries are loaded while this one is scanned
+    int32_t vn[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) v[j] = i0 + j < total ? hist[i0 + j] : 0;
+    for (int j = 0; j < 4; ++j)
+      vn[j] = i0 + 4096 + j < total ? hist[i0 + 4096 + j] : 0;
     const int32_t s = v[0] + v[1] + v[2] + v[3];
-    part[tid] = s;
-    __syncthreads();
-    // Hillis-Steele inclusive scan over the 1024 partial sums
-    for (int off = 1; off < 1024; off <<= 1) {
-      const int32_t x = tid >= off ? part[tid - off] : 0;
-      __syncthreads();
-      part[tid] += x;
-      __syncthreads();
+    int32_t x = s;  // inclusive prefix of s over the wavefront
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int32_t y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
     }
-    int32_t run = carry + part[tid] - s;  // exclusive prefix of entry i0
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int32_t before = 0, tile = 0;  // sums of the wavefronts before this one, of all
+#pragma unroll
+    for (int q = 0; q < NWAVE; ++q) {
+      const int32_t t = wsum[q];
+      before += q < wv ? t : 0;
+      tile += t;
+    }
+    int32_t run = carry + before + x - s;  // exclusive prefix of entry i0
+    // expert e and block r of entry i0 (one division per tile, not per entry)
+    int e = (int)(i0 / nblk), r = (int)(i0 - (int64_t)e * nblk);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t i = i0 + j;
       if (i < total) {
         hist[i] = run;
-        if (i % nblk == 0) offs[i / nblk] = run;
+        if (r == 0) offs[e] = run;
         run += v[j];
       }
+      if (++r == nblk) { r = 0; ++e; }
     }
-    carry += part[1023];
-    __syncthreads();  // part is rewritten by the next tile
+    carry += tile;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = vn[j];
+    __syncthreads();  // wsum is rewritten by the next tile
   }
   if (tid == 0) offs[n_local] = carry;
   __syncthreads();
