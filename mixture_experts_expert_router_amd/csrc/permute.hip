@@ -105,22 +105,36 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   }
 }
 
-// One wavefront per chunk of flat slots.
+// One wavefront per chunk of CHUNK flat slots.  The chunk's expert ids and
+// weights, and the chunk's base row of every local expert, are loaded up
+// front with independent loads; the ranking then runs on ballots and LDS
+// alone, so the chunk costs a few memory round trips, not one per 64 slots.
+template <int CHUNK>
 __global__ __launch_bounds__(64) void permute_scatter_kernel(
     const int32_t *__restrict__ idx, const float *__restrict__ w, int64_t F,
-    int e_begin, int n_local, int nbits, int chunk, int nblk,
+    int e_begin, int n_local, int nbits, int nblk,
     const int32_t *__restrict__ base, int32_t *__restrict__ row_src,
     int32_t *__restrict__ inv, float *__restrict__ s_perm) {
-  extern __shared__ int32_t running[];
+  constexpr int STEPS = CHUNK / 64;
+  extern __shared__ int32_t running[];  // next row of each local expert
   const int lane = threadIdx.x;
-  for (int e = lane; e < n_local; e += 64) running[e] = 0;
+  const int64_t f0 = (int64_t)blockIdx.x * CHUNK;
+  uint32_t ev[STEPS];
+  float wv[STEPS];
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int64_t f = f0 + st * 64 + lane;
+    ev[st] = f < F ? (uint32_t)(idx[f] - e_begin) : 0xffffffffu;
+    wv[st] = (f < F && s_perm) ? w[f] : 0.f;
+  }
+  for (int e = lane; e < n_local; e += 64)
+    running[e] = base[(int64_t)e * nblk + blockIdx.x];
   __syncthreads();
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int64_t f0 = (int64_t)blockIdx.x * chunk;
-  for (int step = 0; step < chunk; step += 64) {
-    const int64_t f = f0 + step + lane;
-    const bool valid = f < F;
-    const uint32_t e = valid ? (uint32_t)(idx[f] - e_begin) : 0xffffffffu;
+#pragma unroll
+  for (int st = 0; st < STEPS; ++st) {
+    const int64_t f = f0 + st * 64 + lane;
+    const uint32_t e = ev[st];
     const bool local = e < (uint32_t)n_local;
     uint64_t match = __ballot(local);
     for (int b = 0; b < nbits; ++b) {
@@ -129,20 +143,17 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
       match &= bit ? bb : ~bb;
     }
     int32_t r = -1;
-    if (local) {
-      const int rank = __popcll(match & lt_mask);
-      r = base[(int64_t)e * nblk + blockIdx.x] + running[e] + rank;
-    }
+    if (local) r = running[e] + __popcll(match & lt_mask);
     // every lane has read running[] above before any leader updates it
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
     if (local && (match & lt_mask) == 0) running[e] += __popcll(match);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
-    if (valid) inv[f] = r;
+    if (f < F) inv[f] = r;
     if (local) {
       row_src[r] = (int32_t)f;
-      if (s_perm) s_perm[r] = w[f];
+      if (s_perm) s_perm[r] = wv[st];
     }
   }
 }
@@ -210,9 +221,14 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
                                               (int)n_local, chunk, nblk, hist);
   permute_scan_kernel<<<1, 1024, 0, s>>>(hist, (int)n_local, nblk, counts,
                                          offsets);
-  permute_scatter_kernel<<<nblk, 64, lds, s>>>(
-      idx, w, F, (int)e_begin, (int)n_local, nbits, chunk, nblk, hist,
-      row_src, inv, (w ? s_perm : nullptr));
+  if (chunk == 256)
+    permute_scatter_kernel<256><<<nblk, 64, lds, s>>>(
+        idx, w, F, (int)e_begin, (int)n_local, nbits, nblk, hist, row_src,
+        inv, (w ? s_perm : nullptr));
+  else
+    permute_scatter_kernel<1024><<<nblk, 64, lds, s>>>(
+        idx, w, F, (int)e_begin, (int)n_local, nbits, nblk, hist, row_src,
+        inv, (w ? s_perm : nullptr));
   if (x && x_perm) {
     const int64_t vecs = row_bytes / 16;
     int64_t grid = F < (int64_t)num_cus * 8 ? F : (int64_t)num_cus * 8;
