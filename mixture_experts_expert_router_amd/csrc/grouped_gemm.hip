@@ -83,7 +83,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     int bm_wide, int nt_wide, int bm_narrow, int nt_narrow, int wide_min,
     int narrow_cap, int32_t *__restrict__ prefix_small,
     int32_t *__restrict__ prefix_wide, int32_t *__restrict__ prefix_narrow) {
-  __shared__ int32_t part[3][1024];
+  __shared__ int32_t wsum[3][16];
   const int tid = threadIdx.x;
   const int per = (G + 1023) / 1024;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
@@ -103,19 +103,37 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     tiles(e, t[0], t[1], t[2]);
     for (int c = 0; c < 3; ++c) s[c] += t[c];
   }
-  for (int c = 0; c < 3; ++c) part[c][tid] = s[c];
-  __syncthreads();
-  for (int off = 1; off < 1024; off <<= 1) {
-    int32_t v[3];
-    for (int c = 0; c < 3; ++c) v[c] = tid >= off ? part[c][tid - off] : 0;
-    __syncthreads();
-    for (int c = 0; c < 3; ++c) part[c][tid] += v[c];
-    __syncthreads();
+  // Inclusive scan of s over the block: lane shuffles inside each
+  // wavefront, then the 16 wavefront totals through LDS (one barrier).
+  const int lane = tid & 63, wv = tid >> 6;
+  int32_t x[3] = {s[0], s[1], s[2]};
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int32_t y = __shfl_up(x[c], off, 64);
+      if (lane >= off) x[c] += y;
+    }
   }
-  const bool narrow = prefix_narrow != nullptr && part[1][1023] < wide_min &&
-                      part[2][1023] <= narrow_cap;
+  if (lane == 63)
+    for (int c = 0; c < 3; ++c) wsum[c][wv] = x[c];
+  __syncthreads();
+  int32_t incl[3], total[3];
+  for (int c = 0; c < 3; ++c) {
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int32_t v = wsum[c][q];
+      before += q < wv ? v : 0;
+      all += v;
+    }
+    incl[c] = before + x[c];
+    total[c] = all;
+  }
+  const bool narrow = prefix_narrow != nullptr && total[1] < wide_min &&
+                      total[2] <= narrow_cap;
   int32_t r[3];
-  for (int c = 0; c < 3; ++c) r[c] = part[c][tid] - s[c];
+  for (int c = 0; c < 3; ++c) r[c] = incl[c] - s[c];
   for (int e = e0; e < e1; ++e) {
     prefix_small[e] = r[0];
     prefix_wide[e] = narrow ? 0 : r[1];
@@ -125,9 +143,9 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     for (int c = 0; c < 3; ++c) r[c] += t[c];
   }
   if (tid == 1023) {
-    prefix_small[G] = part[0][1023];
-    prefix_wide[G] = narrow ? 0 : part[1][1023];
-    if (prefix_narrow) prefix_narrow[G] = narrow ? part[2][1023] : 0;
+    prefix_small[G] = total[0];
+    prefix_wide[G] = narrow ? 0 : total[1];
+    if (prefix_narrow) prefix_narrow[G] = narrow ? total[2] : 0;
   }
 }
 
