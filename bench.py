@@ -256,7 +256,7 @@ def run_mx(args, wl, dev):
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
     moe.route_topk(k, logits=logits, topk_idx=topk_idx, topk_w=topk_w)
     pout = moe.PermuteOut(T, k, H, n, torch.bfloat16, dev)
-    moe.permute(topk_idx, d["x"], wl.e_begin, n, topk_w=topk_w, out=pout)
+    moe.permute(topk_idx, d["x"], wl.e_begin, n, topk_w=topk_w, out=pout, E=wl.E)
     torch.cuda.synchronize()
     R = int(pout.offsets[-1].item())
     dy_host = synth.make_dy(wl, R)
@@ -295,7 +295,7 @@ def run_mx(args, wl, dev):
         mw = mw_holder["mw"]
         if timed_ev is not None:
             timed_ev[0].record(stream)
-        moe.permute(topk_idx, d["x"], wl.e_begin, n, topk_w=topk_w, out=pout)
+        moe.permute(topk_idx, d["x"], wl.e_begin, n, topk_w=topk_w, out=pout, E=wl.E)
         moe.mxfp8_quantize(pout.x_perm, 0, codes=xq, scales=xs)
         if timed_ev is not None:
             timed_ev[1].record(stream)
@@ -467,7 +467,7 @@ def main():
         if wl.router == "gemm":
             route()
         moe.permute(topk_idx, None if gather else d["x"], wl.e_begin,
-                    wl.n_local, topk_w=topk_w, out=pout)
+                    wl.n_local, topk_w=topk_w, out=pout, E=wl.E)
         if timed_ev is not None:
             timed_ev[1].record(stream)
         if gather:

@@ -74,6 +74,22 @@ enum moe_status {
 
 enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
 
+/*
+ * Device error word.  Every workspace the library takes begins with a
+ * 256-byte header whose first int32 the call's kernels set: 0 when nothing
+ * went wrong, otherwise an OR of the bits below.  Read it with
+ * moe_read_device_error after the call.  (NVL72 news item, "Kernel
+ * Optimization and Load Balancing": routing moves data whose sizes are not
+ * static, so bad sizes and indices surface on the device, not the host.)
+ */
+enum moe_device_error {
+  MOE_DEVERR_EXPERT_INDEX = 1,  /* moe_permute: a topk_idx outside [0, E);
+                                   its slot was dropped (inv = -1)      */
+  MOE_DEVERR_ROWS = 2           /* grouped GEMMs: offsets decrease or run
+                                   past R_cap; rows at or past R_cap were
+                                   not computed                          */
+};
+
 /* Human-readable name of a status code (static string, host). */
 const char *moe_status_string(int status);
 
@@ -95,6 +111,11 @@ int moe_version(void);
  * the lower expert index first) and topk_w [T, k] fp32.
  * The top-k decision is taken on the fp32 logits.  The weights are
  * exp(l_j - l_max) / sum over the kept experts of exp(l - l_max).
+ * Non-finite logits: -0 equals +0; NaN ranks below every number (-inf
+ * included), so every token gets k distinct indices in [0, E).  With l_max
+ * finite, NaN and -inf logits weigh 0; with l_max = +inf the +inf logits
+ * share the weight equally; with l_max = -inf or NaN the k kept experts
+ * share it equally.
  * Limits: 1 <= k <= min(E, 32), 1 <= E <= 1024, T >= 0 (T == 0 enqueues
  * nothing), H >= 1; in GEMM mode with bf16, H % 64 == 0.
  */
@@ -111,8 +132,10 @@ int moe_route_topk(const void *x, const void *w_router, const float *bias,
  *
  * Flat slot f = t*k + j.  Inside an expert, slots keep ascending f (a stable
  * counting sort), so the result is unique and deterministic.
- * Inputs:  topk_idx [T, k] int32; topk_w [T, k] fp32 or NULL;
- *          x [T, H] of dtype or NULL (then x_perm is not written).
+ * Inputs:  topk_idx [T, k] int32 with values in [0, E); topk_w [T, k] fp32
+ *          or NULL; x [T, H] of dtype or NULL (then x_perm is not written).
+ *          E is the number of experts of the layer; this GPU's experts
+ *          [e_begin, e_begin + n_local) must lie inside [0, E).
  * Outputs: counts [n_local], offsets [n_local + 1] (exclusive scan,
  *          offsets[n_local] = R, the rows this GPU computes),
  *          row_src [T*k] (rows < R: the flat slot placed there),
@@ -121,15 +144,19 @@ int moe_route_topk(const void *x, const void *w_router, const float *bias,
  *          s_perm [T*k] fp32 (rows < R: topk_w of that slot; skipped when
  *          topk_w is NULL or s_perm is NULL).
  * Rows >= R of the capacity-sized outputs are left untouched.
- * Indices outside [e_begin, e_begin + n_local) are non-local: dropped.
+ * Indices outside [e_begin, e_begin + n_local) are non-local: dropped.  An
+ * index outside [0, E) is dropped too and sets MOE_DEVERR_EXPERT_INDEX in
+ * the workspace's error word (which the call otherwise clears): nothing is
+ * ever written out of bounds.
  * workspace: moe_permute_workspace_bytes(T, k, n_local) bytes, 16-aligned.
- * Limits: 1 <= k <= 32, T*k < 2^31, 1 <= n_local <= 4096, H % 8 == 0 when
- * x is given (bf16) or H % 4 == 0 (fp32).
+ * Limits: 1 <= k <= 32, T*k < 2^31, 1 <= n_local <= 4096,
+ * 0 <= e_begin <= E - n_local, E < 2^31, H % 8 == 0 when x is given (bf16)
+ * or H % 4 == 0 (fp32).
  */
 size_t moe_permute_workspace_bytes(int64_t T, int64_t k, int64_t n_local);
 int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
-                int64_t T, int64_t k, int64_t H, int dtype, int64_t e_begin,
-                int64_t n_local, void *x_perm, float *s_perm,
+                int64_t T, int64_t k, int64_t H, int dtype, int64_t E,
+                int64_t e_begin, int64_t n_local, void *x_perm, float *s_perm,
                 int32_t *row_src, int32_t *inv, int32_t *counts,
                 int32_t *offsets, void *workspace, size_t workspace_bytes,
                 hipStream_t stream);
@@ -142,6 +169,13 @@ int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
  *   a = s_perm[r] * SiLU(g) * u   (ScaledSwiGLU; s_perm NULL -> scale 1)
  * g and u never leave the chip; only `a` [R_cap, I] (dtype) is written, rows
  * < R.  SiLU(z) = z * sigmoid(z).
+ * offsets [n_local + 1] (device) must satisfy 0 <= offsets[e] <=
+ * offsets[e+1] <= R_cap.  Segments that break this are cut to fit: expert e
+ * then computes rows [b, max(b, min(offsets[e+1], R_cap))) with b =
+ * min(max(offsets[e], 0), R_cap), so rows at or past R_cap are never read or
+ * written (rows two cut segments share hold unspecified values), and
+ * MOE_DEVERR_ROWS is set in the workspace's error word, which the call
+ * otherwise clears.
  * workspace: moe_grouped_ffn_workspace_bytes(...) bytes, 16-aligned.
  * Limits (bf16): H % 64 == 0, I % 64 == 0, 1 <= n_local <= 4096,
  * R_cap < 2^31.  (fp32): H % 4 == 0, I % 4 == 0.
@@ -391,6 +425,18 @@ int moe_grouped_mlp_mxfp8_bwd_gate_up(
 
 /* Waits for `stream` and reports a pending HIP error as MOE_E_HIP (tests). */
 int moe_debug_sync(hipStream_t stream);
+
+/*
+ * moe_read_device_error - copy the device error word of `workspace` (a
+ * workspace previously passed to a call on `stream`) to *host_code, after
+ * waiting for the stream: 0, or an OR of MOE_DEVERR_* bits describing what
+ * the last call that used this workspace found on the device.  This call
+ * synchronises the stream; it is meant for tests and debugging, not for the
+ * hot path.  host_code is a host pointer.  Returns MOE_E_ARG for NULL
+ * arguments, MOE_E_HIP when the copy or the wait fails.
+ */
+int moe_read_device_error(const void *workspace, hipStream_t stream,
+                          int32_t *host_code);
 
 #ifdef __cplusplus
 }

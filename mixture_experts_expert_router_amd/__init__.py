@@ -54,7 +54,7 @@ def lib():
         L.moe_permute_workspace_bytes.argtypes = [i64, i64, i64]
         L.moe_permute_workspace_bytes.restype = sz
         L.moe_permute.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64, i64,
-                                  vp, vp, vp, vp, vp, vp, vp, sz, vp]
+                                  i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_grouped_ffn_workspace_bytes.argtypes = [i64, i64, i64, i64, i32]
         L.moe_grouped_ffn_workspace_bytes.restype = sz
         L.moe_grouped_gate_up.argtypes = [vp, vp, vp, i64, i64, i64, i64, vp,
@@ -66,6 +66,7 @@ def lib():
         L.moe_unpermute_combine.argtypes = [vp, vp, vp, i64, i64, i64, i32,
                                             vp, vp]
         L.moe_debug_sync.argtypes = [vp]
+        L.moe_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
         L.moe_mxfp8_quantize.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64,
                                          vp, i64, vp, i64, vp, vp]
         L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
@@ -187,7 +188,10 @@ class PermuteOut:
 
 
 def permute(topk_idx, x, e_begin, n_local, topk_w=None, out=None,
-            stream=None):
+            stream=None, *, E):
+    """Local dispatch of the slots routed to experts [e_begin, e_begin +
+    n_local) of the layer's E experts.  Indices outside [0, E) are dropped
+    and flagged in out.workspace's error word (see read_device_error)."""
     T, k = topk_idx.shape
     H = x.shape[1] if x is not None else 0
     dtype = x.dtype if x is not None else torch.bfloat16
@@ -195,7 +199,7 @@ def permute(topk_idx, x, e_begin, n_local, topk_w=None, out=None,
         out = PermuteOut(T, k, max(H, 1), n_local, dtype, topk_idx.device,
                          with_x=x is not None)
     _call("moe_permute", _p(topk_idx), _p(topk_w), _p(x), T, k, H,
-          _DT[dtype], e_begin, n_local, _p(out.x_perm),
+          _DT[dtype], E, e_begin, n_local, _p(out.x_perm),
           _p(out.s_perm) if topk_w is not None else None, _p(out.row_src),
           _p(out.inv), _p(out.counts), _p(out.offsets), _p(out.workspace),
           out.workspace.numel(), _stream(stream))
@@ -281,6 +285,19 @@ def unpermute_combine(y, inv, topk_w=None, out=None, stream=None):
 
 def debug_sync(stream=None):
     _call("moe_debug_sync", _stream(stream))
+
+
+DEVERR_EXPERT_INDEX = 1
+DEVERR_ROWS = 2
+
+
+def read_device_error(workspace, stream=None) -> int:
+    """The device error word of a workspace a call used (0 = no error, else
+    an OR of DEVERR_* bits).  Synchronises the stream."""
+    v = ctypes.c_int32(-1)
+    _call("moe_read_device_error", _p(workspace), _stream(stream),
+          ctypes.byref(v))
+    return int(v.value)
 
 
 # ---------------------------------------------------------------- MXFP8

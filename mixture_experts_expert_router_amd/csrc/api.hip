@@ -97,14 +97,14 @@ size_t moe_permute_workspace_bytes(int64_t T, int64_t k, int64_t n_local) {
 }
 
 int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
-                int64_t T, int64_t k, int64_t H, int dtype, int64_t e_begin,
-                int64_t n_local, void *x_perm, float *s_perm,
+                int64_t T, int64_t k, int64_t H, int dtype, int64_t E,
+                int64_t e_begin, int64_t n_local, void *x_perm, float *s_perm,
                 int32_t *row_src, int32_t *inv, int32_t *counts,
                 int32_t *offsets, void *workspace, size_t workspace_bytes,
                 hipStream_t stream) {
   if (dtype != MOE_DT_F32 && dtype != MOE_DT_BF16) return MOE_E_ARG;
   if (T < 0 || k < 1 || k > 32 || n_local < 1 || n_local > 4096 ||
-      e_begin < 0 || e_begin > INT32_MAX - n_local)
+      E < 1 || E > INT32_MAX || e_begin < 0 || e_begin > E - n_local)
     return MOE_E_SHAPE;
   if (T * k >= kMaxRows) return MOE_E_SHAPE;
   if (counts == nullptr || offsets == nullptr) return MOE_E_ARG;
@@ -123,10 +123,11 @@ int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
   if (!aligned16(workspace)) return MOE_E_ALIGN;
   if (T == 0) {
     // nothing routed: zero counts and offsets on the device
-    return status_of(moe::launch_permute_empty(counts, offsets, n_local, stream));
+    return status_of(
+        moe::launch_permute_empty(counts, offsets, n_local, workspace, stream));
   }
   return status_of(moe::launch_permute(
-      topk_idx, topk_w, x, T, k, row_bytes, e_begin, n_local, x_perm, s_perm,
+      topk_idx, topk_w, x, T, k, row_bytes, E, e_begin, n_local, x_perm, s_perm,
       row_src, inv, counts, offsets, workspace, num_cus(), stream));
 }
 
@@ -180,11 +181,15 @@ int moe_grouped_gate_up(const void *x_perm, const int32_t *offsets,
         (const uint16_t *)x_perm, offsets, s_perm, (int)n_local, R_cap,
         (int)H, (int)I, (const uint16_t *)w_gate, (const uint16_t *)w_up,
         (uint16_t *)a, (int32_t *)workspace, num_cus(), stream);
-  else
-    err = moe::launch_gate_up_f32((const float *)x_perm, offsets, s_perm,
-                                  (int)n_local, R_cap, H, I,
-                                  (const float *)w_gate, (const float *)w_up,
-                                  (float *)a, stream);
+  else {
+    err = moe::launch_check_offsets(offsets, (int)n_local, R_cap,
+                                    (int32_t *)workspace, stream);
+    if (err == hipSuccess)
+      err = moe::launch_gate_up_f32((const float *)x_perm, offsets, s_perm,
+                                    (int)n_local, R_cap, H, I,
+                                    (const float *)w_gate, (const float *)w_up,
+                                    (float *)a, stream);
+  }
   return status_of(err);
 }
 
@@ -229,10 +234,14 @@ int moe_grouped_down(const void *a, const int32_t *offsets, int64_t n_local,
                                 R_cap, (int)H, (int)I,
                                 (const uint16_t *)w_down, (uint16_t *)y,
                                 (int32_t *)workspace, num_cus(), stream);
-  else
-    err = moe::launch_down_f32((const float *)a, offsets, (int)n_local, R_cap,
-                               H, I, (const float *)w_down, (float *)y,
-                               stream);
+  else {
+    err = moe::launch_check_offsets(offsets, (int)n_local, R_cap,
+                                    (int32_t *)workspace, stream);
+    if (err == hipSuccess)
+      err = moe::launch_down_f32((const float *)a, offsets, (int)n_local,
+                                 R_cap, H, I, (const float *)w_down, (float *)y,
+                                 stream);
+  }
   return status_of(err);
 }
 
@@ -276,6 +285,19 @@ int moe_debug_sync(hipStream_t stream) {
   return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
+int moe_read_device_error(const void *workspace, hipStream_t stream,
+                          int32_t *host_code) {
+  if (workspace == nullptr || host_code == nullptr) return MOE_E_ARG;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof v, hipMemcpyDeviceToHost,
+                     stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MOE_E_HIP;
+  *host_code = v;
+  return MOE_OK;
+}
+
 }  // extern "C"
 
 // ---------------------------------------------------------------- MXFP8
@@ -308,12 +330,18 @@ int64_t mx_kpad_cap(int64_t R_cap, int64_t n_local) {
 
 // Workspace layouts.  Sizes depend only on the arguments, so the same
 // carving gives the byte count (base == null) and the pointers.
+// Every workspace begins with the error header (device error word first).
+int32_t *carve_err(Carve &c) {
+  return c.take<int32_t>(moe::kErrHeaderBytes / 4);
+}
+
 struct LinWs {                     // grouped linear: tile plan + MX(x)
-  int32_t *tiles;
+  int32_t *err, *tiles;
   uint8_t *xq, *xs;
 };
 LinWs carve_lin(Carve &c, int64_t R_cap, int64_t n_local, int64_t K) {
   LinWs w;
+  w.err = carve_err(c);
   w.tiles = c.take<int32_t>(n_local + 1);
   w.xq = c.take<uint8_t>((size_t)R_cap * K);
   w.xs = c.take<uint8_t>((size_t)R_cap * (K / 32));
@@ -321,7 +349,7 @@ LinWs carve_lin(Carve &c, int64_t R_cap, int64_t n_local, int64_t K) {
 }
 
 struct DownBwdWs {                 // backward of the down projection
-  int32_t *tiles, *kpad;
+  int32_t *err, *tiles, *kpad;
   uint8_t *dyq, *dys;
   float *ds_part;
   uint8_t *dyT, *dyTs, *aT, *aTs;
@@ -331,6 +359,7 @@ DownBwdWs carve_down_bwd(Carve &c, int64_t R_cap, int64_t n_local, int64_t H,
                          int64_t I) {
   DownBwdWs w;
   w.kcap = mx_kpad_cap(R_cap, n_local);
+  w.err = carve_err(c);
   w.tiles = c.take<int32_t>(n_local + 1);
   w.kpad = c.take<int32_t>(n_local + 1);
   w.dyq = c.take<uint8_t>((size_t)R_cap * H);
@@ -344,7 +373,7 @@ DownBwdWs carve_down_bwd(Carve &c, int64_t R_cap, int64_t n_local, int64_t H,
 }
 
 struct GateUpBwdWs {               // backward of the gate/up projection
-  int32_t *tiles, *kpad;
+  int32_t *err, *tiles, *kpad;
   uint8_t *dguq, *dgus;
   uint8_t *xT, *xTs, *dgT, *dgTs, *duT, *duTs;
   int64_t kcap;
@@ -354,6 +383,7 @@ GateUpBwdWs carve_gate_up_bwd(Carve &c, int64_t R_cap, int64_t n_local,
                               int64_t H, int64_t I, bool own_dgu = true) {
   GateUpBwdWs w{};
   w.kcap = mx_kpad_cap(R_cap, n_local);
+  w.err = carve_err(c);
   w.tiles = c.take<int32_t>(n_local + 1);
   w.kpad = c.take<int32_t>(n_local + 1);
   if (own_dgu) {
@@ -418,6 +448,7 @@ size_t gate_up_bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H,
 // in turn.
 size_t bwd_bytes(int64_t R_cap, int64_t n_local, int64_t H, int64_t I) {
   Carve c(nullptr);
+  carve_err(c);
   carve_dgu_codes(c, R_cap, n_local, I);
   Carve g(nullptr);
   carve_gate_up_bwd(g, R_cap, n_local, H, I, /*own_dgu=*/false);
@@ -442,7 +473,7 @@ hipError_t run_linear(const void *x, const int32_t *offsets, int64_t n_local,
   e.A = ws.xq; e.As = ws.xs; e.lda = K; e.ldas = K / 32;
   e.B0 = w; e.B0s = wsc; e.ldb = K; e.ldbs = K / 32;
   e.b_stride = N * K; e.bs_stride = N * K / 32;
-  e.offsets = offsets; e.tile_ws = ws.tiles; e.G = (int)n_local;
+  e.offsets = offsets; e.tile_ws = ws.tiles; e.err = ws.err; e.G = (int)n_local;
   e.N = (int)N; e.K = (int)K; e.R_cap = R_cap;
   e.C = y; e.ldc = N;
   return moe::launch_mx_rowseg(e, moe::MXE_BF16, cus, stream);
@@ -452,8 +483,9 @@ hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
                         const int32_t *offsets, const float *s_perm,
                         int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
                         const uint8_t *wdt, const uint8_t *wdts, void *dgu,
-                        float *ds, void *dw_down, const DownBwdWs &w, int cus,
-                        hipStream_t stream, const DguCodes *codes = nullptr) {
+                        float *ds, void *dw_down, const DownBwdWs &w,
+                        int32_t *errw, int cus, hipStream_t stream,
+                        const DguCodes *codes = nullptr) {
   const int G = (int)n_local;
   hipError_t err;
 #define MX_TRY(x) do { err = (x); if (err != hipSuccess) return err; } while (0)
@@ -466,14 +498,15 @@ hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
     d.A = w.dyq; d.As = w.dys; d.lda = H; d.ldas = H / 32;
     d.B0 = wdt; d.B0s = wdts; d.ldb = n_local * H; d.ldbs = n_local * H / 32;
     d.b_stride = H; d.bs_stride = H / 32;
-    d.offsets = offsets; d.tile_ws = w.tiles; d.G = G;
+    d.offsets = offsets; d.tile_ws = w.tiles; d.err = errw; d.G = G;
     d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
     d.row_scale = s_perm; d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
     d.dgu = (uint16_t *)dgu; d.ds_part = w.ds_part; d.ds = ds;
     if (codes) {
       // [dg | du] quantised by the epilogue: along 2I for the dX GEMM, and
       // down each expert segment (padded to 256 rows) for dW_g, dW_u
-      MX_TRY(moe::launch_mx_pad_offsets(offsets, G, 256, codes->tpad, stream));
+      MX_TRY(moe::launch_mx_pad_offsets(offsets, G, R_cap, 256, codes->tpad,
+                                        stream));
       d.q = codes->q; d.qs = codes->qs; d.ldq = 2 * I; d.ldqs = 2 * I / 32;
       d.t0 = codes->gT; d.t0s = codes->gTs; d.t1 = codes->uT; d.t1s = codes->uTs;
       d.ldt = codes->kcap; d.ldts = codes->kcap / 32; d.tpad = codes->tpad;
@@ -503,7 +536,7 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
                            const uint8_t *wgt, const uint8_t *wgts,
                            const uint8_t *wut, const uint8_t *wuts, void *dx,
                            void *dw_gate, void *dw_up, const GateUpBwdWs &w,
-                           int cus, hipStream_t stream,
+                           int32_t *errw, int cus, hipStream_t stream,
                            const DguCodes *codes = nullptr) {
   const int G = (int)n_local;
   hipError_t err;
@@ -522,7 +555,7 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
     d.B0 = wgt; d.B0s = wgts; d.B1 = wut; d.B1s = wuts;
     d.ldb = n_local * I; d.ldbs = n_local * I / 32;
     d.b_stride = I; d.bs_stride = I / 32;
-    d.offsets = offsets; d.tile_ws = w.tiles; d.G = G;
+    d.offsets = offsets; d.tile_ws = w.tiles; d.err = errw; d.G = G;
     d.N = (int)H; d.K = (int)(2 * I); d.R_cap = R_cap; d.ksplit = (int)I;
     d.C = dx; d.ldc = H;
     MX_TRY(moe::launch_mx_rowseg(d, moe::MXE_BF16, cus, stream));
@@ -638,7 +671,7 @@ int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
   d.A = xq; d.As = xs; d.lda = H; d.ldas = H / 32;
   d.B0 = wg; d.B0s = wgs; d.B1 = wu; d.B1s = wus;
   d.ldb = H; d.ldbs = H / 32; d.b_stride = I * H; d.bs_stride = I * H / 32;
-  d.offsets = offsets; d.tile_ws = w.tiles; d.G = (int)n_local;
+  d.offsets = offsets; d.tile_ws = w.tiles; d.err = w.err; d.G = (int)n_local;
   d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
   d.C = a; d.ldc = I; d.row_scale = s_perm;
   d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
@@ -720,8 +753,8 @@ int moe_grouped_mlp_mxfp8_bwd_down(
   Carve c(workspace);
   const DownBwdWs w = carve_down_bwd(c, R_cap, n_local, H, I);
   return status_of(run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap, H,
-                                I, wdt, wdts, dgu, ds, dw_down, w, num_cus(),
-                                stream));
+                                I, wdt, wdts, dgu, ds, dw_down, w, w.err,
+                                num_cus(), stream));
 }
 
 size_t moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes(int64_t R_cap,
@@ -752,7 +785,7 @@ int moe_grouped_mlp_mxfp8_bwd_gate_up(
   const GateUpBwdWs w = carve_gate_up_bwd(c, R_cap, n_local, H, I);
   return status_of(run_gate_up_bwd(dgu, x_perm, offsets, n_local, R_cap, H, I,
                                    wgt, wgts, wut, wuts, dx, dw_gate, dw_up, w,
-                                   num_cus(), stream));
+                                   w.err, num_cus(), stream));
 }
 
 size_t moe_grouped_mlp_mxfp8_bwd_workspace_bytes(int64_t R_cap,
@@ -782,21 +815,22 @@ int moe_grouped_mlp_mxfp8_bwd(
     return MOE_E_WORKSPACE;
   if (!aligned16(workspace)) return MOE_E_ALIGN;
   Carve c(workspace);
+  int32_t *err = carve_err(c);
   // [dg | du] never exists in bf16 here: the SwiGLU-backward epilogue writes
   // its MX copies (row-wise and per segment column-wise) directly.
   const DguCodes codes = carve_dgu_codes(c, R_cap, n_local, I);
   Carve shared = c;   // both halves carve the same region, one after the other
   const int cus = num_cus();
   const DownBwdWs wd = carve_down_bwd(c, R_cap, n_local, H, I);
-  hipError_t err = run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap, H,
-                                I, wdt, wdts, nullptr, ds, dw_down, wd, cus,
-                                stream, &codes);
-  if (err != hipSuccess) return MOE_E_HIP;
+  hipError_t herr = run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap,
+                                 H, I, wdt, wdts, nullptr, ds, dw_down, wd, err,
+                                 cus, stream, &codes);
+  if (herr != hipSuccess) return MOE_E_HIP;
   const GateUpBwdWs wg =
       carve_gate_up_bwd(shared, R_cap, n_local, H, I, /*own_dgu=*/false);
   return status_of(run_gate_up_bwd(nullptr, x_perm, offsets, n_local, R_cap,
                                    H, I, wgt, wgts, wut, wuts, dx, dw_gate,
-                                   dw_up, wg, cus, stream, &codes));
+                                   dw_up, wg, err, cus, stream, &codes));
 }
 
 }  // extern "C"

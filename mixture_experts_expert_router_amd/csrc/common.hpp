@@ -38,6 +38,22 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * sigmoid_f32(z);
 }
 
+// Rows [b, e) of segment g of a device offsets array, clamped to [0, cap]:
+// a segment running past the row capacity is cut there, a decreasing one is
+// empty (the plan kernels report both in the error word).
+__device__ __forceinline__ void seg_rows(const int32_t *offsets, int g,
+                                         int cap, int &b, int &e) {
+  b = min(max(offsets[g], 0), cap);
+  e = min(max(offsets[g + 1], b), cap);
+}
+
+// Whether segment g of `offsets` breaks 0 <= offsets[g] <= offsets[g+1] <= cap.
+__device__ __forceinline__ bool seg_bad(const int32_t *offsets, int g,
+                                        int cap) {
+  const int32_t b = offsets[g], e = offsets[g + 1];
+  return b < 0 || e < b || e > cap;
+}
+
 // Index of the last entry of the non-decreasing array p[0..n] that is <= v,
 // for p[0] <= v < p[n].
 __device__ __forceinline__ int upper_bound_minus1(const int32_t *p, int n,

@@ -9,7 +9,7 @@
 namespace moe {
 
 // a[r, i] = s[r] * SiLU(x[r] . Wg[e, i]) * (x[r] . Wu[e, i]), one thread per
-// output.
+// output.  Rows at or past R_cap are never touched.
 __global__ void gate_up_f32_kernel(const float *__restrict__ x,
                                    const int32_t *__restrict__ offsets,
                                    const float *__restrict__ s, int n_local,
@@ -18,7 +18,7 @@ __global__ void gate_up_f32_kernel(const float *__restrict__ x,
                                    const float *__restrict__ wu,
                                    float *__restrict__ a) {
   const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int R = offsets[n_local];
+  const int R = min(max(offsets[n_local], 0), (int)R_cap);
   if (o >= (int64_t)R * I) return;
   const int r = (int)(o / I);
   const int64_t i = o % I;
@@ -37,11 +37,11 @@ __global__ void gate_up_f32_kernel(const float *__restrict__ x,
 // y[r, h] = a[r] . Wd[e, h], one thread per output.
 __global__ void down_f32_kernel(const float *__restrict__ a,
                                 const int32_t *__restrict__ offsets,
-                                int n_local, int64_t H, int64_t I,
-                                const float *__restrict__ wd,
+                                int n_local, int64_t R_cap, int64_t H,
+                                int64_t I, const float *__restrict__ wd,
                                 float *__restrict__ y) {
   const int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int R = offsets[n_local];
+  const int R = min(max(offsets[n_local], 0), (int)R_cap);
   if (o >= (int64_t)R * H) return;
   const int r = (int)(o / H);
   const int64_t h = o % H;
@@ -71,8 +71,25 @@ hipError_t launch_down_f32(const float *a, const int32_t *offsets,
   const int64_t n = R_cap * H;
   const int64_t grid = (n + 255) / 256;
   if (grid > 0)
-    down_f32_kernel<<<(unsigned)grid, 256, 0, s>>>(a, offsets, n_local, H, I,
-                                                   w_down, y);
+    down_f32_kernel<<<(unsigned)grid, 256, 0, s>>>(a, offsets, n_local, R_cap,
+                                                   H, I, w_down, y);
+  return hipGetLastError();
+}
+
+// *err = kDevErrRows when the offsets decrease or run past R_cap, else 0.
+__global__ __launch_bounds__(256) void check_offsets_kernel(
+    const int32_t *__restrict__ offsets, int n_local, int R_cap,
+    int32_t *__restrict__ err) {
+  int bad = 0;
+  for (int e = threadIdx.x; e < n_local; e += 256)
+    bad |= seg_bad(offsets, e, R_cap);
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) *err = bad ? kDevErrRows : 0;
+}
+
+hipError_t launch_check_offsets(const int32_t *offsets, int n_local,
+                                int64_t R_cap, int32_t *err, hipStream_t s) {
+  check_offsets_kernel<<<1, 256, 0, s>>>(offsets, n_local, (int)R_cap, err);
   return hipGetLastError();
 }
 

@@ -62,6 +62,7 @@ struct GemmArgs {
   const int32_t *a_rows;    // gather-on-load: A row of permuted row r is
   int a_div, a_rows_max;    //   min(a_rows[r] / a_div, a_rows_max); or null
   int single_rows;          // rows of the single group (offsets == null)
+  int r_cap;                // row capacity: segments are cut at it
   int G;                    // groups
   int N;                    // output columns (a-columns for SWIGLU)
   int K;
@@ -77,9 +78,12 @@ constexpr int kSmallRows = 64;
 // the wide shape (1) or with the narrow one (2).  Without prefix_narrow the
 // wide shape is used.  Otherwise the narrow one is used when the wide shape
 // would give fewer than wide_min tiles in all, and its tiles fit in
-// narrow_cap; the other shape's prefix is then all zeros.  One block.
+// narrow_cap; the other shape's prefix is then all zeros.  Segments are cut
+// at the row capacity r_cap; the error word `err` gets kDevErrRows when the
+// offsets run past it or decrease, else 0.  One block.
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(
-    const int32_t *__restrict__ offsets, int G, int bm_small, int nt_small,
+    const int32_t *__restrict__ offsets, int G, int r_cap, int32_t *err,
+    int bm_small, int nt_small,
     int bm_wide, int nt_wide, int bm_narrow, int nt_narrow, int wide_min,
     int narrow_cap, int32_t *__restrict__ prefix_small,
     int32_t *__restrict__ prefix_wide, int32_t *__restrict__ prefix_narrow) {
@@ -88,7 +92,9 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
   const int per = (G + 1023) / 1024;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
   auto tiles = [&](int e, int32_t &t0, int32_t &t1, int32_t &t2) {
-    const int n = offsets[e + 1] - offsets[e];
+    int b, en;
+    seg_rows(offsets, e, r_cap, b, en);
+    const int n = en - b;
     t0 = t1 = t2 = 0;
     if (n <= kSmallRows) {
       t0 = (n + bm_small - 1) / bm_small * nt_small;
@@ -98,10 +104,12 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     }
   };
   int32_t s[3] = {0, 0, 0};
+  int bad = 0;
   for (int e = e0; e < e1; ++e) {
     int32_t t[3];
     tiles(e, t[0], t[1], t[2]);
     for (int c = 0; c < 3; ++c) s[c] += t[c];
+    bad |= seg_bad(offsets, e, r_cap);
   }
   // Inclusive scan of s over the block: lane shuffles inside each
   // wavefront, then the 16 wavefront totals through LDS (one barrier).
@@ -147,6 +155,8 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     prefix_wide[G] = narrow ? 0 : total[1];
     if (prefix_narrow) prefix_narrow[G] = narrow ? total[2] : 0;
   }
+  bad = __syncthreads_or(bad);
+  if (tid == 0) *err = bad ? kDevErrRows : 0;
 }
 
 // Wait until at most N of this wavefront's vector-memory loads are in flight
@@ -298,8 +308,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
     int e, r_begin, r_end, local;
     if (p.offsets) {
       e = upper_bound_minus1(p.tile_prefix, p.G, t);
-      r_begin = p.offsets[e];
-      r_end = p.offsets[e + 1];
+      seg_rows(p.offsets, e, p.r_cap, r_begin, r_end);
       local = t - p.tile_prefix[e];
     } else {
       e = 0; r_begin = 0; r_end = p.single_rows; local = t;
@@ -498,10 +507,12 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
   // narrow one would need more tiles than this.
   const int64_t max_n = ((R_cap + NBM - 1) / NBM + p.G) * (int64_t)nt_n;
   const int narrow_cap = (int)std::min<int64_t>(max_n, 8LL * num_cus);
-  int32_t *pre_s = tile_ws;
-  int32_t *pre_w = tile_ws + (p.G + 1);
-  int32_t *pre_n = tile_ws + 2 * (p.G + 1);
-  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, 64, nt_s, WBM, nt_w,
+  p.r_cap = (int)R_cap;
+  int32_t *errw = tile_ws;
+  int32_t *pre_s = tile_ws + kErrHeaderBytes / 4;
+  int32_t *pre_w = pre_s + (p.G + 1);
+  int32_t *pre_n = pre_s + 2 * (p.G + 1);
+  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.r_cap, errw, 64, nt_s, WBM, nt_w,
                                       NBM, nt_n, wide_min, narrow_cap, pre_s,
                                       pre_w, wide_sure ? nullptr : pre_n);
   hipError_t err = hipGetLastError();
@@ -531,7 +542,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
 }  // namespace
 
 size_t gemm_workspace_bytes(int64_t n_local) {
-  return (size_t)((3 * (n_local + 1) * 4 + 255) / 256 * 256);
+  return kErrHeaderBytes + (size_t)((3 * (n_local + 1) * 4 + 255) / 256 * 256);
 }
 
 hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,

@@ -9,6 +9,12 @@
 
 namespace moe {
 
+// Every workspace begins with a header of kErrHeaderBytes whose first int32
+// is the device error word (bit values as MOE_DEVERR_* in moe_mi355x.h).
+constexpr size_t kErrHeaderBytes = 256;
+constexpr int32_t kDevErrExpertIndex = 1;  // a top-k index outside [0, E)
+constexpr int32_t kDevErrRows = 2;         // offsets past R_cap or decreasing
+
 enum GemmEpilogue { EPI_SWIGLU = 0, EPI_BF16 = 1, EPI_F32_BIAS = 2 };
 
 hipError_t launch_router_gemm_f32(const float *x, const float *w,
@@ -22,15 +28,16 @@ hipError_t launch_topk(const float *logits, int64_t T, int E, int k,
 
 size_t permute_workspace_bytes(int64_t T, int64_t k, int64_t n_local);
 hipError_t launch_permute_empty(int32_t *counts, int32_t *offsets,
-                                int64_t n_local, hipStream_t s);
+                                int64_t n_local, void *ws, hipStream_t s);
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
-                          int64_t T, int64_t k, int64_t row_bytes,
+                          int64_t T, int64_t k, int64_t row_bytes, int64_t E,
                           int64_t e_begin, int64_t n_local, void *x_perm,
                           float *s_perm, int32_t *row_src, int32_t *inv,
                           int32_t *counts, int32_t *offsets, void *ws,
                           int num_cus, hipStream_t s);
 
-// Workspace of one grouped GEMM launch: two tile prefixes of n_local + 1.
+// Workspace of one grouped GEMM launch: the error header and three tile
+// prefixes of n_local + 1.
 size_t gemm_workspace_bytes(int64_t n_local);
 
 hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
@@ -49,6 +56,9 @@ hipError_t launch_gate_up_f32(const float *x_perm, const int32_t *offsets,
                               const float *s_perm, int n_local, int64_t R_cap,
                               int64_t H, int64_t I, const float *w_gate,
                               const float *w_up, float *a, hipStream_t s);
+// Writes the error word of a grouped call that has no plan kernel (fp32).
+hipError_t launch_check_offsets(const int32_t *offsets, int n_local,
+                                int64_t R_cap, int32_t *err, hipStream_t s);
 hipError_t launch_down_f32(const float *a, const int32_t *offsets,
                            int n_local, int64_t R_cap, int64_t H, int64_t I,
                            const float *w_down, float *y, hipStream_t s);
@@ -63,9 +73,10 @@ hipError_t launch_mx_quant_rows(const uint16_t *in, int64_t rows, int64_t cols,
                                 int64_t ld_codes, uint8_t *scales,
                                 int64_t ld_scales, const int32_t *rows_dev,
                                 hipStream_t s);
-// pad[s+1] = pad[s] + ceil((seg[s+1] - seg[s]) / align) * align, pad[0] = 0.
-hipError_t launch_mx_pad_offsets(const int32_t *seg, int nseg, int align,
-                                 int32_t *pad, hipStream_t s);
+// pad[s+1] = pad[s] + ceil(len_s / align) * align, pad[0] = 0, where len_s
+// is the length of segment s cut at `rows` (see seg_rows).
+hipError_t launch_mx_pad_offsets(const int32_t *seg, int nseg, int64_t rows,
+                                 int align, int32_t *pad, hipStream_t s);
 hipError_t launch_mx_quant_cols(const uint16_t *in, int64_t rows,
                                 int64_t cols, int64_t ld_in,
                                 const int32_t *seg, int nseg, int align,
@@ -83,6 +94,7 @@ struct MxGemmDesc {
   const int32_t *offsets;          // row-segment mode: [G + 1]
   const int32_t *kseg;             // K-segment mode: [G + 1]
   int32_t *tile_ws;                // row-segment mode: [G + 1] scratch
+  int32_t *err;                    // row-segment mode: error word or null
   int G, M, N, K;
   int64_t R_cap;
   void *C;

@@ -46,6 +46,7 @@ struct MxArgs {
   const int32_t *tile_prefix;   // ROWSEG: [G + 1]
   const int32_t *kseg;          // KSEG: [G + 1] K ranges (multiples of 128)
   int G, M, N, K, NT, MT;
+  int r_cap;                    // ROWSEG: row capacity (segments cut at it)
   void *C;
   int64_t ldc, c_stride;
   const float *row_scale;       // SWIGLU, SWIGLU_BWD: s per row (or null)
@@ -112,17 +113,29 @@ __device__ __forceinline__ int mx_swz(int row, int c) {
   return CPR == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
 }
 
-// tile_prefix[e+1] = tile_prefix[e] + ceil(rows_e / BM) * NT.  One block.
+// tile_prefix[e+1] = tile_prefix[e] + ceil(rows_e / BM) * NT, with the
+// segments cut at the row capacity r_cap; *err = kDevErrRows when the
+// offsets run past it or decrease, else 0 (err may be null).  One block.
 __global__ __launch_bounds__(1024) void mx_plan_kernel(
-    const int32_t *__restrict__ offsets, int G, int BM, int NT,
-    int32_t *__restrict__ prefix) {
+    const int32_t *__restrict__ offsets, int G, int r_cap, int BM, int NT,
+    int32_t *__restrict__ prefix, int32_t *__restrict__ err) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   const int per = (G + 1023) / 1024;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
+  auto tiles = [&](int e) {
+    int b, en;
+    seg_rows(offsets, e, r_cap, b, en);
+    return (en - b + BM - 1) / BM * NT;
+  };
   int32_t s = 0;
-  for (int e = e0; e < e1; ++e)
-    s += (offsets[e + 1] - offsets[e] + BM - 1) / BM * NT;
+  int bad = 0;
+  for (int e = e0; e < e1; ++e) {
+    s += tiles(e);
+    bad |= seg_bad(offsets, e, r_cap);
+  }
+  bad = __syncthreads_or(bad);
+  if (tid == 0 && err) *err = bad ? kDevErrRows : 0;
   part[tid] = s;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -134,7 +147,7 @@ __global__ __launch_bounds__(1024) void mx_plan_kernel(
   int32_t run = part[tid] - s;
   for (int e = e0; e < e1; ++e) {
     prefix[e] = run;
-    run += (offsets[e + 1] - offsets[e] + BM - 1) / BM * NT;
+    run += tiles(e);
   }
   if (tid == 1023) prefix[G] = part[1023];
 }
@@ -411,9 +424,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   if (t < 0) return;
 
   int e, row0, rows, nt, mt, k0, KT;
+  int r_begin = 0;                // ROWSEG: first row of the tile's segment
   if (MODE == MX_ROWSEG) {
     e = upper_bound_minus1(p.tile_prefix, p.G, t);
-    const int r_begin = p.offsets[e], r_end = p.offsets[e + 1];
+    int r_end;
+    seg_rows(p.offsets, e, p.r_cap, r_begin, r_end);
     const int local = t - p.tile_prefix[e];
     const int mtiles = (r_end - r_begin + BM - 1) / BM;
     banded_mn(local, mtiles, p.NT, 8, mt, nt);
@@ -434,6 +449,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   // unchanged; say that they are uniform, so that the addressing below
   // stays in scalar registers.
   e = __builtin_amdgcn_readfirstlane(e);
+  r_begin = __builtin_amdgcn_readfirstlane(r_begin);
   row0 = __builtin_amdgcn_readfirstlane(row0);
   rows = __builtin_amdgcn_readfirstlane(rows);
   nt = __builtin_amdgcn_readfirstlane(nt);
@@ -688,7 +704,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
       }
       if (p.t0) {
         // tile rows start at offsets[e] + mt * BM, padded position tpad[e] + mt * BM
-        const int64_t pos0 = (int64_t)p.tpad[e] + (row0 - p.offsets[e]) + ar0;
+        const int64_t pos0 = (int64_t)p.tpad[e] + (row0 - r_begin) + ar0;
         const int valid = min(max(rows - ar0, 0), 64);
         mx_quant_staged_cols<128, 64>(lg, p.t0, p.t0s, p.ldt, p.ldts, col0, pos0, valid, lane);
         mx_quant_staged_cols<128, 64>(lu, p.t1, p.t1s, p.ldt, p.ldts, col0, pos0, valid, lane);
@@ -765,7 +781,9 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
   const int cols = epi == MX_EPI_SWIGLU ? kMxBN / 2 : kMxBN;
   p.NT = (d.N + cols - 1) / cols;
   p.tile_prefix = d.tile_ws;
-  mx_plan_kernel<<<1, 1024, 0, s>>>(d.offsets, d.G, kMxBM, p.NT, d.tile_ws);
+  p.r_cap = (int)d.R_cap;
+  mx_plan_kernel<<<1, 1024, 0, s>>>(d.offsets, d.G, p.r_cap, kMxBM, p.NT,
+                                    d.tile_ws, d.err);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // SwiGLU backward: 32-bit byte offsets within a tile's rows of g|u.

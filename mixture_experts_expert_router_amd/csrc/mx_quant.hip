@@ -101,8 +101,10 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
       if (prow < padded) {
         if (seg) {
           const int s = upper_bound_minus1(pad, nseg, prow);
-          const int r = seg[s] + (prow - pad[s]);
-          if (r < seg[s + 1]) sr = r;
+          int b, e;
+          seg_rows(seg, s, (int)rows, b, e);
+          const int r = b + (prow - pad[s]);
+          if (r < e) sr = r;
         } else if (prow < rows) {
           sr = prow;
         }
@@ -185,16 +187,22 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
   }
 }
 
-// pad[s+1] = pad[s] + ceil(len_s / align) * align, pad[0] = 0.  One block.
+// pad[s+1] = pad[s] + ceil(len_s / align) * align, pad[0] = 0, len_s the
+// length of segment s cut at `rows`.  One block.
 __global__ __launch_bounds__(1024) void mx_pad_offsets_kernel(
-    const int32_t *__restrict__ seg, int nseg, int align,
+    const int32_t *__restrict__ seg, int nseg, int rows, int align,
     int32_t *__restrict__ pad) {
   __shared__ int32_t part[1024];
   const int tid = threadIdx.x;
   const int per = (nseg + 1023) / 1024;
   const int s0 = min(nseg, tid * per), s1 = min(nseg, s0 + per);
+  auto padded = [&](int s) {
+    int b, e;
+    seg_rows(seg, s, rows, b, e);
+    return (e - b + align - 1) / align * align;
+  };
   int32_t sum = 0;
-  for (int s = s0; s < s1; ++s) sum += (seg[s + 1] - seg[s] + align - 1) / align * align;
+  for (int s = s0; s < s1; ++s) sum += padded(s);
   part[tid] = sum;
   __syncthreads();
   for (int off = 1; off < 1024; off <<= 1) {
@@ -206,7 +214,7 @@ __global__ __launch_bounds__(1024) void mx_pad_offsets_kernel(
   int32_t run = part[tid] - sum;
   for (int s = s0; s < s1; ++s) {
     pad[s] = run;
-    run += (seg[s + 1] - seg[s] + align - 1) / align * align;
+    run += padded(s);
   }
   if (tid == 1023) pad[nseg] = part[1023];
 }
@@ -223,9 +231,9 @@ hipError_t launch_mx_quant_rows(const uint16_t *in, int64_t rows, int64_t cols,
   return hipGetLastError();
 }
 
-hipError_t launch_mx_pad_offsets(const int32_t *seg, int nseg, int align,
-                                 int32_t *pad, hipStream_t s) {
-  mx_pad_offsets_kernel<<<1, 1024, 0, s>>>(seg, nseg, align, pad);
+hipError_t launch_mx_pad_offsets(const int32_t *seg, int nseg, int64_t rows,
+                                 int align, int32_t *pad, hipStream_t s) {
+  mx_pad_offsets_kernel<<<1, 1024, 0, s>>>(seg, nseg, (int)rows, align, pad);
   return hipGetLastError();
 }
 
@@ -237,7 +245,7 @@ hipError_t launch_mx_quant_cols(const uint16_t *in, int64_t rows,
                                 int64_t ld_scales, int num_cus,
                                 hipStream_t s) {
   if (seg) {
-    mx_pad_offsets_kernel<<<1, 1024, 0, s>>>(seg, nseg, align, pad);
+    mx_pad_offsets_kernel<<<1, 1024, 0, s>>>(seg, nseg, (int)rows, align, pad);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

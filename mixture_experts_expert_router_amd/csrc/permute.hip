@@ -6,10 +6,12 @@
 // Four launches, all on the caller's stream, none needing the host to know a
 // count:
 //   1. hist:    each block counts its chunk of flat slots per local expert
-//               (LDS histogram) -> hist[e][blk]
+//               (LDS histogram) -> hist[e][blk], and flags the chunk when
+//               one of its indices lies outside [0, E)
 //   2. scan:    one block turns hist (expert-major) into exclusive prefixes:
 //               base[e][blk] = offsets[e] + slots of e in earlier chunks;
-//               writes counts and offsets
+//               writes counts and offsets, and the workspace's error word
+//               (kDevErrExpertIndex when a chunk was flagged, else 0)
 //   3. scatter: one wavefront per chunk walks its slots in order, 64 at a
 //               time; a slot's rank among equal experts inside the 64 comes
 //               from ballots over the expert id bits (a wave-level match),
@@ -20,21 +22,29 @@
 
 namespace moe {
 
+// Per-expert counts of one chunk of flat slots (LDS histogram), and a flag
+// for the chunk: 1 when one of its indices lies outside [0, E) (such a slot
+// is dropped like a non-local one; the scan reports it in the error word).
 __global__ __launch_bounds__(256) void permute_hist_kernel(
-    const int32_t *__restrict__ idx, int64_t F, int e_begin, int n_local,
-    int chunk, int nblk, int32_t *__restrict__ hist) {
+    const int32_t *__restrict__ idx, int64_t F, int E, int e_begin,
+    int n_local, int chunk, int nblk, int32_t *__restrict__ hist,
+    int32_t *__restrict__ bad_blk) {
   extern __shared__ int32_t bins[];
   for (int e = threadIdx.x; e < n_local; e += blockDim.x) bins[e] = 0;
   __syncthreads();
   const int64_t f0 = (int64_t)blockIdx.x * chunk;
   const int64_t f1 = min(F, f0 + chunk);
+  int bad = 0;
   for (int64_t f = f0 + threadIdx.x; f < f1; f += blockDim.x) {
-    const uint32_t e = (uint32_t)(idx[f] - e_begin);
+    const int32_t g = idx[f];
+    bad |= (uint32_t)g >= (uint32_t)E;
+    const uint32_t e = (uint32_t)(g - e_begin);
     if (e < (uint32_t)n_local) atomicAdd(&bins[e], 1);
   }
-  __syncthreads();
+  bad = __syncthreads_or(bad);
   for (int e = threadIdx.x; e < n_local; e += blockDim.x)
     hist[(int64_t)e * nblk + blockIdx.x] = bins[e];
+  if (threadIdx.x == 0) bad_blk[blockIdx.x] = bad;
 }
 
 // Exclusive scan of hist[n_local * nblk] (expert-major), in place, one block
@@ -46,7 +56,8 @@ __global__ __launch_bounds__(256) void permute_hist_kernel(
 // tile costs two barriers; the next tile's loads overlap the current scan.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(
     int32_t *__restrict__ hist, int n_local, int nblk,
-    int32_t *__restrict__ counts, int32_t *__restrict__ offsets) {
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ bad_blk, int32_t *__restrict__ err) {
   constexpr int NWAVE = 1024 / 64;
   __shared__ int32_t wsum[NWAVE];
   __shared__ int32_t offs[4097];
@@ -98,7 +109,10 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
     __syncthreads();  // wsum is rewritten by the next tile
   }
   if (tid == 0) offs[n_local] = carry;
-  __syncthreads();
+  int bad = 0;
+  for (int b = tid; b < nblk; b += 1024) bad |= bad_blk[b];
+  bad = __syncthreads_or(bad);
+  if (tid == 0) *err = bad ? kDevErrExpertIndex : 0;
   for (int e = tid; e <= n_local; e += 1024) {
     offsets[e] = offs[e];
     if (e < n_local) counts[e] = offs[e + 1] - offs[e];
@@ -182,7 +196,9 @@ int permute_chunk(int64_t F, int64_t n_local) {
 // than a memset, so that a caller may capture the call in a graph.
 __global__ __launch_bounds__(256) void permute_zero_kernel(int32_t *counts,
                                                            int32_t *offsets,
-                                                           int n) {
+                                                           int n,
+                                                           int32_t *err) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) *err = 0;
   for (int i = blockIdx.x * 256 + threadIdx.x; i <= n; i += gridDim.x * 256) {
     if (i < n) counts[i] = 0;
     offsets[i] = 0;
@@ -190,22 +206,25 @@ __global__ __launch_bounds__(256) void permute_zero_kernel(int32_t *counts,
 }
 
 hipError_t launch_permute_empty(int32_t *counts, int32_t *offsets,
-                                int64_t n_local, hipStream_t s) {
+                                int64_t n_local, void *ws, hipStream_t s) {
   const int64_t blocks = (n_local + 1 + 255) / 256;
   permute_zero_kernel<<<(unsigned)(blocks < 64 ? blocks : 64), 256, 0, s>>>(
-      counts, offsets, (int)n_local);
+      counts, offsets, (int)n_local, (int32_t *)ws);
   return hipGetLastError();
 }
 
+// Workspace: the error header, then hist [n_local][nblk], then the chunk
+// flags [nblk].
 size_t permute_workspace_bytes(int64_t T, int64_t k, int64_t n_local) {
   const int64_t F = T * k;
   const int chunk = permute_chunk(F, n_local);
   const int64_t nblk = F > 0 ? (F + chunk - 1) / chunk : 1;
-  return (size_t)(((nblk * n_local * 4) + 255) / 256 * 256);
+  return kErrHeaderBytes +
+         (size_t)(((nblk * (n_local + 1) * 4) + 255) / 256 * 256);
 }
 
 hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
-                          int64_t T, int64_t k, int64_t row_bytes,
+                          int64_t T, int64_t k, int64_t row_bytes, int64_t E,
                           int64_t e_begin, int64_t n_local, void *x_perm,
                           float *s_perm, int32_t *row_src, int32_t *inv,
                           int32_t *counts, int32_t *offsets, void *ws,
@@ -213,14 +232,17 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
   const int64_t F = T * k;
   const int chunk = permute_chunk(F, n_local);
   const int nblk = (int)((F + chunk - 1) / chunk);
-  int32_t *hist = (int32_t *)ws;
+  int32_t *err = (int32_t *)ws;
+  int32_t *hist = (int32_t *)((char *)ws + kErrHeaderBytes);
+  int32_t *bad_blk = hist + (int64_t)n_local * nblk;
   int nbits = 0;
   while ((1ll << nbits) < n_local) ++nbits;
   const size_t lds = (size_t)n_local * 4;
-  permute_hist_kernel<<<nblk, 256, lds, s>>>(idx, F, (int)e_begin,
-                                              (int)n_local, chunk, nblk, hist);
+  permute_hist_kernel<<<nblk, 256, lds, s>>>(idx, F, (int)E, (int)e_begin,
+                                              (int)n_local, chunk, nblk, hist,
+                                              bad_blk);
   permute_scan_kernel<<<1, 1024, 0, s>>>(hist, (int)n_local, nblk, counts,
-                                         offsets);
+                                         offsets, bad_blk, err);
   if (chunk == 256)
     permute_scatter_kernel<256><<<nblk, 64, lds, s>>>(
         idx, w, F, (int)e_begin, (int)n_local, nbits, nblk, hist, row_src,

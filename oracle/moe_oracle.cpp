@@ -76,33 +76,51 @@ void orc_router_logits(const void *x, const void *w_r, int dt,
 // Softmax over all E experts, keep the k most probable, renormalise the kept
 // probabilities to sum to one.  [WideEP-Premise] gives "the router picks k of
 // E"; the softmax / top-k / renormalise form is the workload definition.
-// Reading for ties (the pages are silent): equal probabilities are ordered by
-// lower expert index first; kept experts are listed by descending
-// probability.  logits [T, E] fp32 in; idx [T, k] int32, w [T, k] fp64 out.
+// Softmax is monotone, so the k most probable experts are the k largest
+// logits, and the full-softmax denominator cancels in the renormalisation:
+//   w_j = exp(l_j - l_max) / sum over kept i of exp(l_i - l_max).
+// Readings where the pages are silent:
+//   - ties: equal logits are taken lower expert index first; kept experts
+//     are listed by descending logit; -0 equals +0;
+//   - a NaN logit ranks below every number (-inf included), so a token with
+//     fewer than k finite logits still gets k distinct experts;
+//   - weights of non-finite logits: with l_max finite, a NaN or -inf logit
+//     weighs 0; with l_max = +inf, the +inf logits share the weight equally;
+//     with l_max = -inf or NaN (no kept logit above -inf), the k kept
+//     experts share it equally.
+// logits [T, E] fp32 in; idx [T, k] int32, w [T, k] fp64 out.
+namespace {
+// a ranks above b
+bool logit_above(double a, double b) {
+  if (std::isnan(a)) return false;
+  if (std::isnan(b)) return true;
+  return a > b;
+}
+}  // namespace
+
 void orc_topk_softmax(const float *logits, int64_t T, int64_t E, int64_t k,
                       int32_t *idx, double *w) {
 #pragma omp parallel for schedule(static)
   for (int64_t t = 0; t < T; ++t) {
     const float *l = logits + t * E;
-    std::vector<double> p(E);
-    double mx = -INFINITY;
-    for (int64_t e = 0; e < E; ++e) mx = std::fmax(mx, (double)l[e]);
-    double z = 0.0;
-    for (int64_t e = 0; e < E; ++e) {
-      p[e] = std::exp((double)l[e] - mx);
-      z += p[e];
-    }
-    for (int64_t e = 0; e < E; ++e) p[e] /= z;
     std::vector<char> taken(E, 0);
-    double kept = 0.0;
     for (int64_t j = 0; j < k; ++j) {
       int64_t best = -1;
       for (int64_t e = 0; e < E; ++e)
-        if (!taken[e] && (best < 0 || p[e] > p[best])) best = e;
+        if (!taken[e] && (best < 0 || logit_above(l[e], l[best]))) best = e;
       taken[best] = 1;
       idx[t * k + j] = (int32_t)best;
-      w[t * k + j] = p[best];
-      kept += p[best];
+    }
+    const double lmax = l[idx[t * k]];
+    double kept = 0.0;
+    for (int64_t j = 0; j < k; ++j) {
+      const double lj = l[idx[t * k + j]];
+      double p;
+      if (std::isnan(lmax) || lmax == -INFINITY) p = 1.0;
+      else if (lmax == INFINITY) p = lj == INFINITY ? 1.0 : 0.0;
+      else p = std::isnan(lj) ? 0.0 : std::exp(lj - lmax);
+      w[t * k + j] = p;
+      kept += p;
     }
     for (int64_t j = 0; j < k; ++j) w[t * k + j] /= kept;
   }

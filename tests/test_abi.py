@@ -68,19 +68,23 @@ def test_route_topk_validation(L):
 def test_permute_validation(L):
     f = L.moe_permute
     ws = L.moe_permute_workspace_bytes(16, 2, 4)
-    ok = dict(idx=P, w=P, x=P, T=16, k=2, H=64, dt=BF16, eb=0, nl=4, xp=P,
-              sp=P, rs=P, inv=P, cnt=P, off=P, ws=P, wsb=ws)
+    ok = dict(idx=P, w=P, x=P, T=16, k=2, H=64, dt=BF16, E=8, eb=0, nl=4,
+              xp=P, sp=P, rs=P, inv=P, cnt=P, off=P, ws=P, wsb=ws)
 
     def call(**kw):
         a = dict(ok, **kw)
         return f(a["idx"], a["w"], a["x"], a["T"], a["k"], a["H"], a["dt"],
-                 a["eb"], a["nl"], a["xp"], a["sp"], a["rs"], a["inv"],
-                 a["cnt"], a["off"], a["ws"], a["wsb"], None)
+                 a["E"], a["eb"], a["nl"], a["xp"], a["sp"], a["rs"],
+                 a["inv"], a["cnt"], a["off"], a["ws"], a["wsb"], None)
 
     assert call(dt=5) == E_ARG
     assert call(k=0) == E_SHAPE and call(k=33) == E_SHAPE
     assert call(nl=0) == E_SHAPE and call(nl=5000) == E_SHAPE
     assert call(eb=-1) == E_SHAPE
+    # the local experts must lie inside [0, E)
+    assert call(E=0) == E_SHAPE and call(E=3) == E_SHAPE
+    assert call(eb=5) == E_SHAPE and call(eb=4) != E_SHAPE
+    assert call(E=1 << 31) == E_SHAPE
     assert call(cnt=None) == E_ARG and call(off=None) == E_ARG
     assert call(rs=None) == E_ARG and call(inv=None) == E_ARG
     assert call(xp=None) == E_ARG
@@ -88,6 +92,20 @@ def test_permute_validation(L):
     assert call(x=P_ODD) == E_ALIGN
     assert call(ws=None) == E_WS and call(wsb=ws - 1) == E_WS
     assert call(ws=P_ODD) == E_ALIGN
+
+
+def test_read_device_error_validation(L):
+    import ctypes
+    code = ctypes.c_int32(0)
+    assert L.moe_read_device_error(None, None, ctypes.byref(code)) == E_ARG
+    assert L.moe_read_device_error(P, None, None) == E_ARG
+    assert L.moe_read_device_error(P_ODD, None, ctypes.byref(code)) == E_ALIGN
+
+
+def test_workspaces_hold_the_error_header(L):
+    # every workspace size includes the 256-byte error header
+    assert L.moe_permute_workspace_bytes(0, 1, 1) >= 256 + 4
+    assert L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16) >= 256 + 3 * 5 * 4
 
 
 def test_ffn_validation(L):

@@ -34,7 +34,7 @@ def test_ep_share_full(name):
     ref = orc.moe_layer(wl, inp)
     d = {k: to_dev(v) for k, v in inp.items()}
     idx, w, _ = moe.route_topk(wl.k, logits=d["logits"].clone())
-    p = moe.permute(idx, d["x"], wl.e_begin, wl.n_local, topk_w=w)
+    p = moe.permute(idx, d["x"], wl.e_begin, wl.n_local, topk_w=w, E=wl.E)
     a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
                            d["w_up"], d["w_down"])
     out = moe.unpermute_combine(y, p.inv)
@@ -114,7 +114,7 @@ def test_c4_permute_ffn_combine_sampled(c4):
     R = p_ref["R"]
     assert R == wl.T * wl.k
     w32 = r["w"].astype(np.float32)
-    p = moe.permute(to_dev(r["idx"]), d["x"], 0, wl.n_local, topk_w=to_dev(w32))
+    p = moe.permute(to_dev(r["idx"]), d["x"], 0, wl.n_local, topk_w=to_dev(w32), E=wl.E)
     a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
                            d["w_up"], d["w_down"])
     out = moe.unpermute_combine(y, p.inv)
@@ -161,7 +161,7 @@ def test_c4_end_to_end_sampled(c4):
     print_case("c4 end to end")
     idx, w, _ = moe.route_topk(wl.k, x=d["x"], w_router=d["w_router"],
                                bias=d["bias"])
-    p = moe.permute(idx, d["x"], 0, wl.n_local, topk_w=w)
+    p = moe.permute(idx, d["x"], 0, wl.n_local, topk_w=w, E=wl.E)
     a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
                            d["w_up"], d["w_down"])
     out = moe.unpermute_combine(y, p.inv)
@@ -193,7 +193,7 @@ def test_c5_shape_bf16_sampled():
     # the FFN scales rows by the oracle's weights (rounded to fp32), so that
     # every expected value below derives from the oracle alone
     w32 = rw.astype(np.float32)
-    p = moe.permute(idx, d["x"], 0, wl.n_local, topk_w=to_dev(w32))
+    p = moe.permute(idx, d["x"], 0, wl.n_local, topk_w=to_dev(w32), E=wl.E)
     a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
                            d["w_up"], d["w_down"])
     out = moe.unpermute_combine(y, p.inv)

@@ -39,7 +39,7 @@ def gpu_chain(wl, d, logits=None):
                                     bias=d.get("bias"))
     else:
         idx, w, lg = moe.route_topk(wl.k, logits=d["logits"].clone())
-    p = moe.permute(idx, d["x"], wl.e_begin, wl.n_local, topk_w=w)
+    p = moe.permute(idx, d["x"], wl.e_begin, wl.n_local, topk_w=w, E=wl.E)
     a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
                            d["w_up"], d["w_down"])
     out = moe.unpermute_combine(y, p.inv)
@@ -87,7 +87,7 @@ def test_gate_up_gather_on_load(name):
     d = {k: to_dev(v) for k, v in inp.items()}
     g = gpu_chain(wl, d)
     p = g["p"]
-    p2 = moe.permute(g["idx"], None, wl.e_begin, wl.n_local, topk_w=g["w"])
+    p2 = moe.permute(g["idx"], None, wl.e_begin, wl.n_local, topk_w=g["w"], E=wl.E)
     assert p2.x_perm is None
     a2 = moe.grouped_gate_up_gather(d["x"], p2.row_src, wl.k, p2.offsets,
                                     p2.s_perm, d["w_gate"], d["w_up"])
@@ -177,7 +177,7 @@ def test_ffn_edge_segments(counts, e_begin, H, I):
     out_ref = orc.combine(y_ref, p_ref["inv"])
 
     wt = to_dev(w.astype(np.float32))
-    p = moe.permute(to_dev(idx), to_dev(x), e_begin, n_local, topk_w=wt)
+    p = moe.permute(to_dev(idx), to_dev(x), e_begin, n_local, topk_w=wt, E=E)
     a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, to_dev(wg),
                            to_dev(wu), to_dev(wd))
     out = moe.unpermute_combine(y, p.inv)
@@ -201,7 +201,7 @@ def test_scale_in_combine_matches_scale_in_ffn():
     d = {k: to_dev(v) for k, v in inp.items()}
     idx, w, _ = moe.route_topk(wl.k, x=d["x"], w_router=d["w_router"],
                                bias=d["bias"])
-    p = moe.permute(idx, d["x"], 0, wl.n_local, topk_w=w)
+    p = moe.permute(idx, d["x"], 0, wl.n_local, topk_w=w, E=wl.E)
     _, y1 = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, d["w_gate"],
                             d["w_up"], d["w_down"])
     o1 = moe.unpermute_combine(y1, p.inv)
@@ -221,7 +221,7 @@ def test_empty_token_batch():
     idx, w, _ = moe.route_topk(2, logits=l)
     assert idx.shape == (0, 2)
     x = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
-    p = moe.permute(idx, x, 0, 4, topk_w=w)
+    p = moe.permute(idx, x, 0, 4, topk_w=w, E=8)
     moe.debug_sync()
     assert p.offsets.cpu().tolist() == [0] * 5
     assert p.counts.cpu().tolist() == [0] * 4
@@ -269,7 +269,7 @@ def test_step_captured_in_a_graph_replays_bit_exactly():
     def step():
         moe.route_topk(k, logits=logits, x=d["x"], w_router=d["w_router"],
                        bias=d.get("bias"), topk_idx=idx, topk_w=w)
-        moe.permute(idx, d["x"], wl.e_begin, wl.n_local, topk_w=w, out=pout)
+        moe.permute(idx, d["x"], wl.e_begin, wl.n_local, topk_w=w, out=pout, E=wl.E)
         moe.grouped_gate_up(pout.x_perm, pout.offsets, pout.s_perm,
                             d["w_gate"], d["w_up"], a=a, workspace=ws)
         moe.grouped_down(a, pout.offsets, d["w_down"], y=y, workspace=ws)

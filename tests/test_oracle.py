@@ -79,6 +79,45 @@ def test_topk_closed_forms():
     np.testing.assert_allclose(wc, 1.0 / 3.0, rtol=1e-15)
 
 
+def test_topk_non_finite_logits():
+    """Brute force on the stated reading: NaN ranks below -inf, ties by lower
+    index; weights are the softmax over the finite kept logits, or equal
+    shares among +inf logits, or equal shares when no kept logit exceeds
+    -inf."""
+    E, k = 6, 3
+    ninf, pinf, nan = -np.inf, np.inf, np.nan
+    rows = np.array([
+        [0.5, nan, ninf, 1.0, nan, ninf],     # 2 finite: third pick is -inf
+        [nan, nan, nan, nan, nan, nan],        # all NaN: experts 0, 1, 2
+        [ninf, nan, ninf, ninf, nan, ninf],    # -inf ranks above NaN
+        [1.0, pinf, 2.0, pinf, nan, 0.0],      # two +inf share the weight
+        [-0.0, 0.0, -0.0, 0.0, -1.0, nan],     # -0 == +0: lower index first
+    ], dtype=np.float32)
+    idx, w = orc.topk_softmax(rows, k)
+    for t in range(rows.shape[0]):
+        l = rows[t].astype(np.float64)
+        isn = np.isnan(l)
+        key = np.where(isn, -np.inf, l)
+        # primary: key descending; secondary: NaN after -inf; then index
+        order = np.lexsort((np.arange(E), isn, -key))[:k]
+        np.testing.assert_array_equal(idx[t], order)
+        kept = l[order]
+        m = kept[0]
+        if np.isnan(m) or m == -np.inf:
+            p = np.ones(k)
+        elif m == np.inf:
+            p = (kept == np.inf).astype(np.float64)
+        else:
+            p = np.where(np.isnan(kept), 0.0, np.exp(np.where(np.isnan(kept), 0, kept) - m))
+        np.testing.assert_allclose(w[t], p / p.sum(), rtol=1e-15)
+    np.testing.assert_array_equal(idx[1], [0, 1, 2])
+    np.testing.assert_array_equal(idx[2], [0, 2, 3])
+    np.testing.assert_array_equal(idx[3][:2], [1, 3])
+    np.testing.assert_allclose(w[3], [0.5, 0.5, 0.0])
+    np.testing.assert_array_equal(idx[4], [0, 1, 2])
+    np.testing.assert_allclose(w[0], [np.e ** 0.5 / (1 + np.e ** 0.5), 1 / (1 + np.e ** 0.5), 0.0], rtol=1e-15)
+
+
 # ---------------------------------------------------------------- permute
 
 
