@@ -69,7 +69,9 @@ enum moe_status {
   MOE_E_ALIGN = 3,        /* pointer not 16-byte aligned                  */
   MOE_E_WORKSPACE = 4,    /* workspace missing or too small               */
   MOE_E_UNSUPPORTED = 5,  /* valid but not implemented combination        */
-  MOE_E_HIP = 6           /* a HIP launch or runtime call failed          */
+  MOE_E_HIP = 6,          /* a HIP launch or runtime call failed          */
+  MOE_E_SCRATCH = 7       /* needs more than the no-allocation variant's
+                             scratch (MOE_NOALLOC_SCRATCH_BYTES)          */
 };
 
 enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
@@ -422,6 +424,30 @@ int moe_grouped_mlp_mxfp8_bwd_gate_up(
     const uint8_t *wgts, const uint8_t *wut, const uint8_t *wuts, void *dx,
     void *dw_gate, void *dw_up, void *workspace, size_t workspace_bytes,
     hipStream_t stream);
+
+/*
+ * moe_permute_noalloc - moe_permute without a workspace argument, for
+ * callers that cannot allocate device memory: code under stream capture,
+ * tight serving loops, harnesses that forbid allocation.  Arguments,
+ * outputs, results and limits are those of moe_permute (identical bits).
+ * The scratch moe_permute would take from the workspace lives instead in a
+ * static device array of MOE_NOALLOC_SCRATCH_BYTES per GPU, held until the
+ * process ends; the call itself allocates and frees nothing.  A call whose
+ * moe_permute_workspace_bytes(T, k, n_local) exceeds that size returns
+ * MOE_E_SCRATCH and enqueues nothing (4 MiB holds, for example, T*k up to
+ * 2^20 slots over 256 local experts).  Every call on one GPU shares that
+ * GPU's array: calls that may overlap on one GPU (different streams without
+ * ordering between them) race and must not be issued.  Nothing in the array
+ * has to start at zero: each call rewrites every entry it reads.  The
+ * device error word of this variant stays in the array and is not exposed.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)4 << 20)
+int moe_permute_noalloc(const int32_t *topk_idx, const float *topk_w,
+                        const void *x, int64_t T, int64_t k, int64_t H,
+                        int dtype, int64_t E, int64_t e_begin,
+                        int64_t n_local, void *x_perm, float *s_perm,
+                        int32_t *row_src, int32_t *inv, int32_t *counts,
+                        int32_t *offsets, hipStream_t stream);
 
 /* Waits for `stream` and reports a pending HIP error as MOE_E_HIP (tests). */
 int moe_debug_sync(hipStream_t stream);

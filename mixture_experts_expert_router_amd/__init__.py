@@ -67,6 +67,8 @@ def lib():
                                             vp, vp]
         L.moe_debug_sync.argtypes = [vp]
         L.moe_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
+        L.moe_permute_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64,
+                                          i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.moe_mxfp8_quantize.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64,
                                          vp, i64, vp, i64, vp, vp]
         L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
@@ -203,6 +205,21 @@ def permute(topk_idx, x, e_begin, n_local, topk_w=None, out=None,
           _p(out.s_perm) if topk_w is not None else None, _p(out.row_src),
           _p(out.inv), _p(out.counts), _p(out.offsets), _p(out.workspace),
           out.workspace.numel(), _stream(stream))
+    return out
+
+
+def permute_noalloc(topk_idx, x, e_begin, n_local, out, topk_w=None,
+                    stream=None, *, E):
+    """permute into caller-provided outputs `out` (a PermuteOut; its
+    workspace is not used): the library allocates nothing and takes its
+    scratch from a static per-GPU array."""
+    T, k = topk_idx.shape
+    H = x.shape[1] if x is not None else 0
+    dtype = x.dtype if x is not None else torch.bfloat16
+    _call("moe_permute_noalloc", _p(topk_idx), _p(topk_w), _p(x), T, k, H,
+          _DT[dtype], E, e_begin, n_local, _p(out.x_perm),
+          _p(out.s_perm) if topk_w is not None else None, _p(out.row_src),
+          _p(out.inv), _p(out.counts), _p(out.offsets), _stream(stream))
     return out
 
 

@@ -51,6 +51,8 @@ const char *moe_status_string(int status) {
     case MOE_E_WORKSPACE: return "workspace missing or too small";
     case MOE_E_UNSUPPORTED: return "unsupported combination";
     case MOE_E_HIP: return "HIP runtime or launch error";
+    case MOE_E_SCRATCH:
+      return "needs more scratch than the no-allocation variant holds";
     default: return "unknown status";
   }
 }

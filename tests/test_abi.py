@@ -108,6 +108,15 @@ def test_workspaces_hold_the_error_header(L):
     assert L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16) >= 256 + 3 * 5 * 4
 
 
+def test_noalloc_permute_rejects_sizes_beyond_its_scratch(L):
+    # 2^30 slots over 256 experts need ~1 GB of scratch: refused on the host
+    # before any device call (status 7, MOE_E_SCRATCH)
+    st = L.moe_permute_noalloc(P, None, None, 1 << 27, 8, 0, BF16, 256, 0,
+                               256, None, None, P, P, P, P, None)
+    assert st == 7
+    assert L.moe_status_string(7)
+
+
 def test_ffn_validation(L):
     g = L.moe_grouped_gate_up
     ws = L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)
