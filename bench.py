@@ -269,7 +269,7 @@ def run_mx(args, wl, dev):
     xq = torch.empty((F, H), dtype=torch.uint8, device=dev)
     xs = torch.empty((F, H // 32), dtype=torch.uint8, device=dev)
     a = torch.empty((F, I), dtype=bf, device=dev)
-    gu = torch.empty((F, 2 * I), dtype=bf, device=dev)
+    gu = torch.empty((F, 2 * I), dtype=torch.float32, device=dev)
     y = torch.empty((F, H), dtype=bf, device=dev)
     dx = torch.empty((F, H), dtype=bf, device=dev)
     ds = torch.empty(F, dtype=torch.float32, device=dev)
@@ -304,7 +304,7 @@ def run_mx(args, wl, dev):
         if timed_ev is not None:
             timed_ev[2].record(stream)
         moe.mxfp8_mlp_fwd_down(pout.offsets, mw, ws_f, F, y=y)
-        moe.mxfp8_mlp_bwd(dy, pout.x_perm, a, gu, pout.offsets, pout.s_perm,
+        moe.mxfp8_mlp_bwd(dy, pout.x_perm, gu, pout.offsets, pout.s_perm,
                           mw, dx=dx, ds=ds, dw_gate=dwg, dw_up=dwu,
                           dw_down=dwd, workspace=ws_b)
         if timed_ev is not None:

@@ -289,11 +289,14 @@ int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
  * [n_local*I, H/32] and W_down codes [n_local*H, I] + scales [n_local*H,
  * I/32] (axis 0 of the stacked weights); offsets, s_perm as in
  * moe_grouped_gate_up (s_perm may be NULL).
- * Outputs (bf16): a [R_cap, I]; gu [R_cap, 2I] = [g | u] per row (may be
- * NULL; the backward needs it); y [R_cap, H].  Rows < R are written.
- * The SwiGLU epilogue also writes MX(a) (blocks along I, from the bf16 a it
- * stores) into the workspace, and the down projection reads those codes
- * (the fused quantisation of the MXFP8 section).
+ * Outputs: a [R_cap, I] bf16; gu [R_cap, 2I] fp32 = [g | u] per row (may
+ * be NULL; the backward needs it: the saved pre-activations stay in fp32, so
+ * the backward differentiates at the values the forward computed); y
+ * [R_cap, H] bf16.  Rows < R are written.
+ * The SwiGLU epilogue also writes MX(a) (blocks along I) into the workspace,
+ * encoded from the fp32 a before any rounding (quantisation, SwiGLU and the
+ * routing scale in one kernel: the MXFP8 section), and the down projection
+ * reads those codes; the bf16 `a` output is the same fp32 a rounded.
  * y == NULL stops after a (wd, wds are then not read); the down projection
  * is then moe_grouped_mlp_mxfp8_fwd_down with the same workspace, or
  * moe_grouped_linear_mxfp8 on a (same result).
@@ -309,7 +312,7 @@ int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
                               int64_t I, const uint8_t *wg, const uint8_t *wgs,
                               const uint8_t *wu, const uint8_t *wus,
                               const uint8_t *wd, const uint8_t *wds, void *a,
-                              void *gu, void *y, void *workspace,
+                              float *gu, void *y, void *workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -355,8 +358,8 @@ int moe_grouped_linear_mxfp8(const void *x, const int32_t *offsets,
  *   dX = MX(dg) . MX_I(W_gate) + MX(du) . MX_I(W_up)   (K = I)
  *   dW_down[e] = MX_R(dY_e)^T . MX_R(a_e), dW_gate[e] = MX_R(dg_e)^T .
  *   MX_R(x_e), dW_up[e] = MX_R(du_e)^T . MX_R(x_e)   (K = rows of expert e)
- * Inputs (bf16): dy [R_cap, H], x_perm [R_cap, H], a [R_cap, I], gu [R_cap,
- * 2I] from the forward; offsets, s_perm; the weights quantised along the
+ * Inputs: dy [R_cap, H] and x_perm [R_cap, H] (bf16), gu [R_cap, 2I] (fp32,
+ * from the forward); offsets, s_perm; the weights quantised along the
  * other axis (axis 1 of the stacked weights): wdt/wdts = W_down as [n_local*H,
  * I] -> codes [I, n_local*H], scales [I, n_local*H/32]; wgt/wgts, wut/wuts =
  * W_gate, W_up as [n_local*I, H] -> codes [H, n_local*I], scales [H,
@@ -364,10 +367,11 @@ int moe_grouped_linear_mxfp8(const void *x, const int32_t *offsets,
  * Outputs: dx [R_cap, H] bf16, ds [R_cap] fp32 (sum in a fixed order),
  * dw_gate, dw_up [n_local, I, H] bf16, dw_down [n_local, H, I] bf16 (an
  * expert without rows gets zero gradients).
- * The call computes what moe_grouped_mlp_mxfp8_bwd_down followed by
- * moe_grouped_mlp_mxfp8_bwd_gate_up compute, with identical bits, but [dg |
- * du] never exists in bf16: the epilogue that produces it writes its MX codes
- * (along 2I, and down each expert's rows) into the workspace directly.
+ * a = s SiLU(g) u, dg and du are computed in fp32 in the epilogue of the da
+ * GEMM, which writes their MX codes (a: down each expert's rows, for dW_d;
+ * dg, du: along 2I for dX and down each expert's rows for dW_g, dW_u)
+ * encoded from those fp32 values: no tensor of the chain is rounded to bf16
+ * before it is quantised.
  * workspace: moe_grouped_mlp_mxfp8_bwd_workspace_bytes() bytes.
  * Limits as for the forward.
  */
@@ -375,7 +379,7 @@ size_t moe_grouped_mlp_mxfp8_bwd_workspace_bytes(int64_t R_cap,
                                                  int64_t n_local, int64_t H,
                                                  int64_t I);
 int moe_grouped_mlp_mxfp8_bwd(
-    const void *dy, const void *x_perm, const void *a, const void *gu,
+    const void *dy, const void *x_perm, const float *gu,
     const int32_t *offsets, const float *s_perm, int64_t n_local,
     int64_t R_cap, int64_t H, int64_t I, const uint8_t *wdt,
     const uint8_t *wdts, const uint8_t *wgt, const uint8_t *wgts,
@@ -388,17 +392,20 @@ int moe_grouped_mlp_mxfp8_bwd(
  * projection's data and weight gradients and the ScaledSwiGLU backward.
  *   da = MX(dY) . MX_H(W_down);  dg, du, ds as above;
  *   dW_down[e] = MX_R(dY_e)^T . MX_R(a_e)
- * Inputs: dy [R_cap, H], a [R_cap, I], gu [R_cap, 2I] (bf16), offsets,
- * s_perm (may be NULL: s = 1), wdt/wdts as for moe_grouped_mlp_mxfp8_bwd.
- * Outputs: dgu [R_cap, 2I] bf16 = [dg | du] per row, ds [R_cap] fp32,
- * dw_down [n_local, H, I] bf16.
+ * Inputs: dy [R_cap, H] bf16, gu [R_cap, 2I] fp32, offsets, s_perm (may be
+ * NULL: s = 1), wdt/wdts as for moe_grouped_mlp_mxfp8_bwd.
+ * Outputs: dgu [R_cap, 2I] bf16 = [dg | du] per row (the fp32 values
+ * rounded: this stage API hands [dg | du] on in bf16, and
+ * moe_grouped_mlp_mxfp8_bwd_gate_up quantises that bf16 tensor), ds [R_cap]
+ * fp32, dw_down [n_local, H, I] bf16.  dW_d uses a recomputed in fp32 from
+ * gu, as in moe_grouped_mlp_mxfp8_bwd.
  * workspace: moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes() bytes.
  */
 size_t moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(int64_t R_cap,
                                                       int64_t n_local,
                                                       int64_t H, int64_t I);
 int moe_grouped_mlp_mxfp8_bwd_down(
-    const void *dy, const void *a, const void *gu, const int32_t *offsets,
+    const void *dy, const float *gu, const int32_t *offsets,
     const float *s_perm, int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
     const uint8_t *wdt, const uint8_t *wdts, void *dgu, float *ds,
     void *dw_down, void *workspace, size_t workspace_bytes,
@@ -448,6 +455,43 @@ int moe_permute_noalloc(const int32_t *topk_idx, const float *topk_w,
                         int64_t n_local, void *x_perm, float *s_perm,
                         int32_t *row_src, int32_t *inv, int32_t *counts,
                         int32_t *offsets, hipStream_t stream);
+
+/*
+ * moe_mxfp8_workspace_view - where the MX codes that a call's GEMMs
+ * consumed stay in its workspace after the call, for callers that keep the
+ * quantised tensors (reuse, inspection, tests): byte offsets into the
+ * workspace and pitches, for the same (R_cap, n_local, H, I) the call took.
+ * A view stays valid until the workspace is passed to another call.
+ *   call MOE_MXCALL_FWD,      tensor MOE_MXT_A_ROWS: MX(a), blocks along I
+ *     (codes [R_cap, I], scales [R_cap, I/32]; rows < R written).
+ *   call MOE_MXCALL_BWD_DOWN, tensor MOE_MXT_A_COLS: a = s SiLU(g) u
+ *     quantised down each expert's rows (for dW_down): codes [I, cols],
+ *     scales [I, cols/32], expert e's rows at columns pad[e] ..
+ *     pad[e] + n_e, zero-padded to pad[e+1] (pad: int32 [n_local + 1] at
+ *     byte offset `pad`).
+ *   call MOE_MXCALL_BWD, tensor MOE_MXT_DGU_ROWS: [dg | du] along 2I
+ *     (codes [R_cap, 2I], scales [R_cap, 2I/32]); MOE_MXT_DG_COLS /
+ *     MOE_MXT_DU_COLS: dg / du down each expert's rows, laid out as for
+ *     MOE_MXT_A_COLS.
+ * Other combinations return MOE_E_UNSUPPORTED.  Host only; enqueues nothing.
+ */
+enum { MOE_MXCALL_FWD = 0, MOE_MXCALL_BWD_DOWN = 1, MOE_MXCALL_BWD = 2 };
+enum {
+  MOE_MXT_A_ROWS = 0,
+  MOE_MXT_A_COLS = 1,
+  MOE_MXT_DGU_ROWS = 2,
+  MOE_MXT_DG_COLS = 3,
+  MOE_MXT_DU_COLS = 4
+};
+typedef struct moe_mx_view {
+  int64_t codes, scales;        /* byte offsets of codes and scales        */
+  int64_t ld_codes, ld_scales;  /* row pitches in bytes                    */
+  int64_t rows, cols;           /* codes [rows, cols]                      */
+  int64_t pad;                  /* byte offset of int32 pad offsets, or -1 */
+} moe_mx_view;
+int moe_mxfp8_workspace_view(int call, int tensor, int64_t R_cap,
+                             int64_t n_local, int64_t H, int64_t I,
+                             moe_mx_view *view);
 
 /* Waits for `stream` and reports a pending HIP error as MOE_E_HIP (tests). */
 int moe_debug_sync(hipStream_t stream);

@@ -80,7 +80,7 @@ def lib():
                                                      vp, vp, vp, sz, vp]
         L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes.restype = sz
-        L.moe_grouped_mlp_mxfp8_bwd.argtypes = [vp, vp, vp, vp, vp, vp, i64,
+        L.moe_grouped_mlp_mxfp8_bwd.argtypes = [vp, vp, vp, vp, vp, i64,
                                                 i64, i64, i64, vp, vp, vp, vp,
                                                 vp, vp, vp, vp, vp, vp, vp, vp,
                                                 sz, vp]
@@ -93,7 +93,7 @@ def lib():
                                                vp, vp, vp, sz, vp]
         L.moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes.restype = sz
-        L.moe_grouped_mlp_mxfp8_bwd_down.argtypes = [vp, vp, vp, vp, vp, i64,
+        L.moe_grouped_mlp_mxfp8_bwd_down.argtypes = [vp, vp, vp, vp, i64,
                                                      i64, i64, i64, vp, vp, vp,
                                                      vp, vp, vp, sz, vp]
         L.moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes.argtypes = [i64, i64, i64, i64]
@@ -102,6 +102,8 @@ def lib():
                                                         i64, i64, vp, vp, vp,
                                                         vp, vp, vp, vp, vp, sz,
                                                         vp]
+        L.moe_mxfp8_workspace_view.argtypes = [i32, i32, i64, i64, i64, i64,
+                                                ctypes.POINTER(MxView)]
         for name in declared_functions():
             getattr(L, name).restype = getattr(L, name).restype or i32
         _lib = L
@@ -358,6 +360,34 @@ def mxfp8_quantize(x, axis=0, seg_offsets=None, align=32, stream=None,
     return codes, scales, pad
 
 
+class MxView(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ("codes", "scales", "ld_codes", "ld_scales", "rows", "cols",
+                 "pad")]
+
+
+MXCALL_FWD, MXCALL_BWD_DOWN, MXCALL_BWD = 0, 1, 2
+MXT_A_ROWS, MXT_A_COLS, MXT_DGU_ROWS, MXT_DG_COLS, MXT_DU_COLS = 0, 1, 2, 3, 4
+
+
+def mxfp8_workspace_view(workspace, call, tensor, R_cap, n_local, H, I):
+    """The MX codes a call left in its workspace, as views of it: (codes
+    [rows, cols] u8, scales [rows, cols/32] u8, pad int32 [n_local+1] or
+    None) -- see moe_mxfp8_workspace_view."""
+    v = MxView()
+    _call("moe_mxfp8_workspace_view", call, tensor, R_cap, n_local, H, I,
+          ctypes.byref(v))
+
+    def part(off, rows, ld, cols):
+        return workspace[off:off + rows * ld].view(rows, ld)[:, :cols]
+
+    codes = part(v.codes, v.rows, v.ld_codes, v.cols)
+    scales = part(v.scales, v.rows, v.ld_scales, v.cols // 32)
+    pad = (workspace[v.pad:v.pad + 4 * (n_local + 1)].view(torch.int32)
+           if v.pad >= 0 else None)
+    return codes, scales, pad
+
+
 class MxWeights:
     """Stacked expert weights quantised for the MXFP8 grouped MLP:
     row-wise copies for the forward, transposed column-wise copies for the
@@ -385,7 +415,7 @@ def mxfp8_mlp_fwd(xq, xs, offsets, s_perm, mw, a=None, gu=None, y=None,
     if a is None:
         a = torch.empty((R_cap, I), dtype=torch.bfloat16, device=dev)
     if gu is None:
-        gu = torch.empty((R_cap, 2 * I), dtype=torch.bfloat16, device=dev)
+        gu = torch.empty((R_cap, 2 * I), dtype=torch.float32, device=dev)
     if not down:
         y = None
     elif y is None:
@@ -400,7 +430,7 @@ def mxfp8_mlp_fwd(xq, xs, offsets, s_perm, mw, a=None, gu=None, y=None,
     return a, gu, y
 
 
-def mxfp8_mlp_bwd(dy, x_perm, a, gu, offsets, s_perm, mw, dx=None, ds=None,
+def mxfp8_mlp_bwd(dy, x_perm, gu, offsets, s_perm, mw, dx=None, ds=None,
                   dw_gate=None, dw_up=None, dw_down=None, workspace=None,
                   stream=None):
     R_cap, H = dy.shape
@@ -420,7 +450,7 @@ def mxfp8_mlp_bwd(dy, x_perm, a, gu, offsets, s_perm, mw, dx=None, ds=None,
     if workspace is None:
         nb = lib().moe_grouped_mlp_mxfp8_bwd_workspace_bytes(R_cap, n, H, I)
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
-    _call("moe_grouped_mlp_mxfp8_bwd", _p(dy), _p(x_perm), _p(a), _p(gu),
+    _call("moe_grouped_mlp_mxfp8_bwd", _p(dy), _p(x_perm), _p(gu),
           _p(offsets), _p(s_perm), n, R_cap, H, I, _p(mw.wdt), _p(mw.wdts),
           _p(mw.wgt), _p(mw.wgts), _p(mw.wut), _p(mw.wuts), _p(dx), _p(ds),
           _p(dw_gate), _p(dw_up), _p(dw_down), _p(workspace),
@@ -456,7 +486,7 @@ def grouped_linear_mxfp8(x, offsets, n_local, w, w_scales, y=None,
     return y
 
 
-def mxfp8_mlp_bwd_down(dy, a, gu, offsets, s_perm, mw, dgu=None, ds=None,
+def mxfp8_mlp_bwd_down(dy, gu, offsets, s_perm, mw, dgu=None, ds=None,
                        dw_down=None, workspace=None, stream=None):
     R_cap, H = dy.shape
     I, n = mw.I, mw.n_local
@@ -470,7 +500,7 @@ def mxfp8_mlp_bwd_down(dy, a, gu, offsets, s_perm, mw, dgu=None, ds=None,
     if workspace is None:
         nb = lib().moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(R_cap, n, H, I)
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
-    _call("moe_grouped_mlp_mxfp8_bwd_down", _p(dy), _p(a), _p(gu), _p(offsets),
+    _call("moe_grouped_mlp_mxfp8_bwd_down", _p(dy), _p(gu), _p(offsets),
           _p(s_perm), n, R_cap, H, I, _p(mw.wdt), _p(mw.wdts), _p(dgu), _p(ds),
           _p(dw_down), _p(workspace), workspace.numel(), _stream(stream))
     return dict(dgu=dgu, ds=ds, dw_down=dw_down)

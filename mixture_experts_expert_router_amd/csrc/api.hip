@@ -481,7 +481,12 @@ hipError_t run_linear(const void *x, const int32_t *offsets, int64_t n_local,
   return moe::launch_mx_rowseg(e, moe::MXE_BF16, cus, stream);
 }
 
-hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
+// The backward of the down projection.  dgu (bf16 [dg | du], may be null)
+// is written for the unfused stage API; with `codes` the epilogue writes
+// [dg | du] as MX codes instead (row-wise, and column-wise per segment).
+// Either way a = s SiLU(g) u is recomputed in fp32 from the saved fp32 g, u
+// in the same epilogue, which writes its column-wise codes for dW_d.
+hipError_t run_down_bwd(const void *dy, const float *gu,
                         const int32_t *offsets, const float *s_perm,
                         int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
                         const uint8_t *wdt, const uint8_t *wdts, void *dgu,
@@ -489,12 +494,17 @@ hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
                         int32_t *errw, int cus, hipStream_t stream,
                         const DguCodes *codes = nullptr) {
   const int G = (int)n_local;
+  const int64_t kc = w.kcap;
+  // padded segment starts of every column-wise copy (256 rows: one tile)
+  int32_t *tpad = codes ? codes->tpad : w.kpad;
   hipError_t err;
 #define MX_TRY(x) do { err = (x); if (err != hipSuccess) return err; } while (0)
   // dY along H (row-wise)
   MX_TRY(moe::launch_mx_quant_rows((const uint16_t *)dy, R_cap, H, H, w.dyq, H,
                                    w.dys, H / 32, offsets + G, stream));
-  // da = dY W_d (K = H); SwiGLU backward in the epilogue -> dg, du, ds
+  MX_TRY(moe::launch_mx_pad_offsets(offsets, G, R_cap, 256, tpad, stream));
+  // da = dY W_d (K = H); SwiGLU backward in the epilogue -> dg, du, ds, and
+  // the column-wise codes of a
   {
     moe::MxGemmDesc d{};
     d.A = w.dyq; d.As = w.dys; d.lda = H; d.ldas = H / 32;
@@ -502,30 +512,24 @@ hipError_t run_down_bwd(const void *dy, const void *a, const void *gu,
     d.b_stride = H; d.bs_stride = H / 32;
     d.offsets = offsets; d.tile_ws = w.tiles; d.err = errw; d.G = G;
     d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
-    d.row_scale = s_perm; d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
+    d.row_scale = s_perm; d.gu = (float *)gu; d.ldgu = 2 * I;
     d.dgu = (uint16_t *)dgu; d.ds_part = w.ds_part; d.ds = ds;
+    d.t2 = w.aT; d.t2s = w.aTs; d.ldt = kc; d.ldts = kc / 32; d.tpad = tpad;
     if (codes) {
       // [dg | du] quantised by the epilogue: along 2I for the dX GEMM, and
       // down each expert segment (padded to 256 rows) for dW_g, dW_u
-      MX_TRY(moe::launch_mx_pad_offsets(offsets, G, R_cap, 256, codes->tpad,
-                                        stream));
       d.q = codes->q; d.qs = codes->qs; d.ldq = 2 * I; d.ldqs = 2 * I / 32;
       d.t0 = codes->gT; d.t0s = codes->gTs; d.t1 = codes->uT; d.t1s = codes->uTs;
-      d.ldt = codes->kcap; d.ldts = codes->kcap / 32; d.tpad = codes->tpad;
     }
     MX_TRY(moe::launch_mx_rowseg(d, moe::MXE_SWIGLU_BWD, cus, stream));
   }
   // dW_d[e] [H, I] = dY_e^T a_e: blocks of 32 rows inside each expert's
-  // segment, segments zero-padded to 512 rows
-  const int64_t kc = w.kcap;
+  // segment, segments zero-padded to 256 rows like the codes of a
   MX_TRY(moe::launch_mx_quant_cols((const uint16_t *)dy, R_cap, H, H, offsets,
-                                   G, 512, w.kpad, w.dyT, kc, w.dyTs, kc / 32,
-                                   cus, stream));
-  MX_TRY(moe::launch_mx_quant_cols((const uint16_t *)a, R_cap, I, I, offsets,
-                                   G, 512, w.kpad, w.aT, kc, w.aTs, kc / 32,
+                                   G, 256, tpad, w.dyT, kc, w.dyTs, kc / 32,
                                    cus, stream));
   moe::MxGemmDesc d{};
-  d.kseg = w.kpad; d.G = G;
+  d.kseg = tpad; d.G = G;
   d.lda = kc; d.ldas = kc / 32; d.ldb = kc; d.ldbs = kc / 32;
   d.A = w.dyT; d.As = w.dyTs; d.B0 = w.aT; d.B0s = w.aTs;
   d.M = (int)H; d.N = (int)I; d.C = dw_down; d.ldc = I; d.c_stride = H * I;
@@ -653,7 +657,7 @@ int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
                               int64_t I, const uint8_t *wg, const uint8_t *wgs,
                               const uint8_t *wu, const uint8_t *wus,
                               const uint8_t *wd, const uint8_t *wds, void *a,
-                              void *gu, void *y, void *workspace,
+                              float *gu, void *y, void *workspace,
                               size_t workspace_bytes, hipStream_t stream) {
   if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
   if (R_cap == 0) return MOE_OK;
@@ -676,8 +680,8 @@ int moe_grouped_mlp_mxfp8_fwd(const uint8_t *xq, const uint8_t *xs,
   d.offsets = offsets; d.tile_ws = w.tiles; d.err = w.err; d.G = (int)n_local;
   d.N = (int)I; d.K = (int)H; d.R_cap = R_cap;
   d.C = a; d.ldc = I; d.row_scale = s_perm;
-  d.gu = (uint16_t *)gu; d.ldgu = 2 * I;
-  // the epilogue also quantises a along I, for the down projection
+  d.gu = gu; d.ldgu = 2 * I;
+  // the epilogue also quantises a along I (from fp32), for the down projection
   d.q = w.xq; d.qs = w.xs; d.ldq = I; d.ldqs = I / 32;
   hipError_t err = moe::launch_mx_rowseg(d, moe::MXE_SWIGLU, cus, stream);
   if (err != hipSuccess) return MOE_E_HIP;
@@ -738,23 +742,23 @@ size_t moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(int64_t R_cap,
 }
 
 int moe_grouped_mlp_mxfp8_bwd_down(
-    const void *dy, const void *a, const void *gu, const int32_t *offsets,
+    const void *dy, const float *gu, const int32_t *offsets,
     const float *s_perm, int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
     const uint8_t *wdt, const uint8_t *wdts, void *dgu, float *ds,
     void *dw_down, void *workspace, size_t workspace_bytes,
     hipStream_t stream) {
   if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
   if (R_cap == 0) return MOE_OK;
-  if (!dy || !a || !gu || !offsets || !wdt || !wdts || !dgu || !ds || !dw_down)
+  if (!dy || !gu || !offsets || !wdt || !wdts || !dgu || !ds || !dw_down)
     return MOE_E_ARG;
-  if (!all_aligned({dy, a, gu, wdt, wdts, dgu, ds, dw_down}))
+  if (!all_aligned({dy, gu, wdt, wdts, dgu, ds, dw_down}))
     return MOE_E_ALIGN;
   if (!workspace || workspace_bytes < down_bwd_bytes(R_cap, n_local, H, I))
     return MOE_E_WORKSPACE;
   if (!aligned16(workspace)) return MOE_E_ALIGN;
   Carve c(workspace);
   const DownBwdWs w = carve_down_bwd(c, R_cap, n_local, H, I);
-  return status_of(run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap, H,
+  return status_of(run_down_bwd(dy, gu, offsets, s_perm, n_local, R_cap, H,
                                 I, wdt, wdts, dgu, ds, dw_down, w, w.err,
                                 num_cus(), stream));
 }
@@ -798,7 +802,7 @@ size_t moe_grouped_mlp_mxfp8_bwd_workspace_bytes(int64_t R_cap,
 }
 
 int moe_grouped_mlp_mxfp8_bwd(
-    const void *dy, const void *x_perm, const void *a, const void *gu,
+    const void *dy, const void *x_perm, const float *gu,
     const int32_t *offsets, const float *s_perm, int64_t n_local,
     int64_t R_cap, int64_t H, int64_t I, const uint8_t *wdt,
     const uint8_t *wdts, const uint8_t *wgt, const uint8_t *wgts,
@@ -807,10 +811,10 @@ int moe_grouped_mlp_mxfp8_bwd(
     size_t workspace_bytes, hipStream_t stream) {
   if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
   if (R_cap == 0) return MOE_OK;
-  if (!dy || !x_perm || !a || !gu || !offsets || !wdt || !wdts || !wgt ||
+  if (!dy || !x_perm || !gu || !offsets || !wdt || !wdts || !wgt ||
       !wgts || !wut || !wuts || !dx || !ds || !dw_gate || !dw_up || !dw_down)
     return MOE_E_ARG;
-  if (!all_aligned({dy, x_perm, a, gu, wdt, wdts, wgt, wgts, wut, wuts, dx, ds,
+  if (!all_aligned({dy, x_perm, gu, wdt, wdts, wgt, wgts, wut, wuts, dx, ds,
                     dw_gate, dw_up, dw_down}))
     return MOE_E_ALIGN;
   if (!workspace || workspace_bytes < bwd_bytes(R_cap, n_local, H, I))
@@ -824,7 +828,7 @@ int moe_grouped_mlp_mxfp8_bwd(
   Carve shared = c;   // both halves carve the same region, one after the other
   const int cus = num_cus();
   const DownBwdWs wd = carve_down_bwd(c, R_cap, n_local, H, I);
-  hipError_t herr = run_down_bwd(dy, a, gu, offsets, s_perm, n_local, R_cap,
+  hipError_t herr = run_down_bwd(dy, gu, offsets, s_perm, n_local, R_cap,
                                  H, I, wdt, wdts, nullptr, ds, dw_down, wd, err,
                                  cus, stream, &codes);
   if (herr != hipSuccess) return MOE_E_HIP;
@@ -833,6 +837,48 @@ int moe_grouped_mlp_mxfp8_bwd(
   return status_of(run_gate_up_bwd(nullptr, x_perm, offsets, n_local, R_cap,
                                    H, I, wgt, wgts, wut, wuts, dx, dw_gate,
                                    dw_up, wg, err, cus, stream, &codes));
+}
+
+
+int moe_mxfp8_workspace_view(int call, int tensor, int64_t R_cap,
+                             int64_t n_local, int64_t H, int64_t I,
+                             moe_mx_view *view) {
+  if (view == nullptr) return MOE_E_ARG;
+  if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  // Carve from a nominal base to read offsets off the same layout the
+  // calls use.
+  char *const base = (char *)(uintptr_t)4096;
+  Carve c(base);
+  auto off = [&](const void *p) { return (int64_t)((const char *)p - base); };
+  moe_mx_view v{};
+  v.pad = -1;
+  if (call == MOE_MXCALL_FWD && tensor == MOE_MXT_A_ROWS) {
+    const LinWs w = carve_lin(c, R_cap, n_local, I);
+    v.codes = off(w.xq); v.scales = off(w.xs);
+    v.ld_codes = I; v.ld_scales = I / 32; v.rows = R_cap; v.cols = I;
+  } else if (call == MOE_MXCALL_BWD_DOWN && tensor == MOE_MXT_A_COLS) {
+    const DownBwdWs w = carve_down_bwd(c, R_cap, n_local, H, I);
+    v.codes = off(w.aT); v.scales = off(w.aTs); v.pad = off(w.kpad);
+    v.ld_codes = w.kcap; v.ld_scales = w.kcap / 32; v.rows = I; v.cols = w.kcap;
+  } else if (call == MOE_MXCALL_BWD &&
+             (tensor == MOE_MXT_DGU_ROWS || tensor == MOE_MXT_DG_COLS ||
+              tensor == MOE_MXT_DU_COLS)) {
+    carve_err(c);
+    const DguCodes d = carve_dgu_codes(c, R_cap, n_local, I);
+    if (tensor == MOE_MXT_DGU_ROWS) {
+      v.codes = off(d.q); v.scales = off(d.qs);
+      v.ld_codes = 2 * I; v.ld_scales = 2 * I / 32; v.rows = R_cap; v.cols = 2 * I;
+    } else {
+      const bool g = tensor == MOE_MXT_DG_COLS;
+      v.codes = off(g ? d.gT : d.uT); v.scales = off(g ? d.gTs : d.uTs);
+      v.pad = off(d.tpad);
+      v.ld_codes = d.kcap; v.ld_scales = d.kcap / 32; v.rows = I; v.cols = d.kcap;
+    }
+  } else {
+    return MOE_E_UNSUPPORTED;
+  }
+  *view = v;
+  return MOE_OK;
 }
 
 }  // extern "C"

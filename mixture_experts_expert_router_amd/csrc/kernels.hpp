@@ -100,19 +100,21 @@ struct MxGemmDesc {
   void *C;
   int64_t ldc, c_stride;
   const float *row_scale;
-  uint16_t *gu;
+  float *gu;                       // fp32 [g | u] (SwiGLU out, backward in)
   int64_t ldgu;
-  uint16_t *dgu;
+  uint16_t *dgu;                   // bf16 [dg | du] out (or null)
   float *ds_part;
   float *ds;
   int ksplit;
   // SwiGLU: MX codes / scales of a along I; SwiGLU backward: of [dg | du]
-  // along 2I (row-wise, blocks of 32 columns).  Null: not written.
+  // along 2I (row-wise, blocks of 32 columns), encoded from fp32.  Null: not
+  // written.
   uint8_t *q, *qs;
   int64_t ldq, ldqs;
-  // SwiGLU backward: column-wise MX codes / scales of dg (t0) and du (t1),
-  // [N, ldt] / [N, ldts], segments padded to 256 rows at tpad (null: none).
-  uint8_t *t0, *t0s, *t1, *t1s;
+  // SwiGLU backward: column-wise MX codes / scales of dg (t0), du (t1) and
+  // a (t2), [N, ldt] / [N, ldts], segments padded to 256 rows at tpad,
+  // encoded from fp32 (null: not written).
+  uint8_t *t0, *t0s, *t1, *t1s, *t2, *t2s;
   int64_t ldt, ldts;
   const int32_t *tpad;
 };

@@ -66,4 +66,18 @@ __device__ __forceinline__ uint32_t mx_encode32(const uint4 (&in)[4], uint32_t (
   return (uint32_t)(X + 127);
 }
 
+// Codes and scale byte of 32 fp32 values (finite): codes[j] packs values
+// 4j .. 4j+3, low byte first; the return value is the scale byte.
+__device__ __forceinline__ uint32_t mx_encode32_f32(const float (&v)[32],
+                                                    uint32_t (&codes)[8]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+  const int X = mx_shared_exp(amax);
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    codes[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], -X);
+  return (uint32_t)(X + 127);
+}
+
 }  // namespace moe

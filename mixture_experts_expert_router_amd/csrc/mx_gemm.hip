@@ -50,17 +50,18 @@ struct MxArgs {
   void *C;
   int64_t ldc, c_stride;
   const float *row_scale;       // SWIGLU, SWIGLU_BWD: s per row (or null)
-  uint16_t *gu;                 // SWIGLU: g,u out; SWIGLU_BWD: g,u in
-  int64_t ldgu;                 // u at column offset N of gu
-  uint16_t *dgu;                // SWIGLU_BWD: dg, du out [rows, ldgu]
+  float *gu;                    // SWIGLU: g, u out; SWIGLU_BWD: g, u in (fp32)
+  int64_t ldgu;                 // u at column offset N of gu (and of dgu)
+  uint16_t *dgu;                // SWIGLU_BWD: dg, du out in bf16 (or null)
   float *ds_part;               // SWIGLU_BWD: [rows, NT * WN]
   int ksplit;                   // KSPLIT: K of the B0 part (0 = none)
-  uint8_t *q, *qs;              // SWIGLU(_BWD): row-wise MX copy of the
-  int64_t ldq, ldqs;            //   bf16 output (null: none)
-  // SWIGLU_BWD: column-wise MX copies of dg (t0) and du (t1) for the weight
-  // gradients: codes [N, ldt], scales [N, ldts]; row r of expert e lands at
-  // position tpad[e] + (r - offsets[e]) (segments padded to BM rows).
-  uint8_t *t0, *t0s, *t1, *t1s;
+  uint8_t *q, *qs;              // SWIGLU: row-wise MX codes of a; SWIGLU_BWD:
+  int64_t ldq, ldqs;            //   of [dg | du]; from fp32 (null: none)
+  // SWIGLU_BWD: column-wise MX copies of dg (t0), du (t1) and a (t2) for the
+  // weight gradients, from fp32: codes [N, ldt], scales [N, ldts]; row r of
+  // expert e lands at position tpad[e] + (r - first row of e) (segments
+  // padded to BM rows).  Null: not written.
+  uint8_t *t0, *t0s, *t1, *t1s, *t2, *t2s;
   int64_t ldt, ldts;
   const int32_t *tpad;
 };
@@ -171,38 +172,59 @@ __device__ __forceinline__ int mx_brow(int nt, int j, int N, bool &up) {
 }
 
 // ---- LDS-staged epilogues ------------------------------------------------
-// After the K loop the LDS ring is free.  Each wavefront stages its part of
-// the output in a region of its own and writes it back to HBM as 16-byte
-// row pieces (8 lanes per 128-byte row), instead of 2-byte stores per lane.
-// Region rows are 128 bytes (64 bf16) for SwiGLU outputs, 256 bytes (128
-// bf16) for the SwiGLU-backward g, u, dg, du tiles.
+// After the K loop the LDS ring is free; each wavefront stages its part of
+// the output in a region of its own.  Plain GEMM outputs are staged in bf16
+// and leave as 16-byte row pieces.  The SwiGLU epilogues stage fp32 values:
+// the MX codes they write are encoded from the fp32 results themselves
+// (the quantisation fused into the kernel of the MXFP8 section), never from
+// a rounded copy.
+//
+// fp32 region layout, W columns (W = 64 or 128) per row: column c of row r
+// lives at r * W + fphys<W>(r, c).  32-column blocks swap by bit 2 of the
+// row (rows r and r + 4, written together by the two wavefront halves in the
+// MFMA layout, then hit different banks), and the eight 16-byte chunks of a
+// block rotate by r mod 8 (so sixteen rows read at one logical chunk hit
+// sixteen different chunk positions).  A block stays within one 128-byte
+// span of its row.
+template <int W>
+__device__ __forceinline__ int fphys(int r, int c) {
+  const int blk = (c >> 5) ^ ((r >> 2) & 1);
+  const int ch = ((c >> 2) & 7) ^ (r & 7);
+  return (blk << 5) | (ch << 2) | (c & 3);
+}
 
-// Row-wise MX encoding of a staged [NROWS][W] bf16 region (st_col<W>
-// layout: the XOR by 32 columns moves whole 32-column blocks, so every block
-// is 64 contiguous bytes).  Block b of region row r goes to codes
-// q[(grow0 + r) * ldq + col0 + 32 b] and scale qs[(grow0 + r) * ldqs +
-// col0 / 32 + b], for tile rows arow0 + r < rows.  The values are the bf16
-// values staged for the output, so the codes equal a row quantisation of
-// that output.
+// The 32 fp32 values of block b (columns 32b .. 32b+31) of region row r.
+template <int W>
+__device__ __forceinline__ void f32_block(const float *l, int r, int b,
+                                          float (&v)[32]) {
+  const float *row = l + r * W + ((b ^ ((r >> 2) & 1)) << 5);
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const float4 t = *(const float4 *)(row + ((k ^ (r & 7)) << 2));
+    v[4 * k] = t.x; v[4 * k + 1] = t.y; v[4 * k + 2] = t.z; v[4 * k + 3] = t.w;
+  }
+}
+
+// Row-wise MX encoding of a staged fp32 [NROWS][W] region: block b of region
+// row r goes to codes q[(grow0 + r) * ldq + col0 + 32 b] and scale
+// qs[(grow0 + r) * ldqs + col0 / 32 + b], for tile rows arow0 + r < rows.
+// Lanes take consecutive rows of one block column (conflict-free reads).
 template <int W, int NROWS>
-__device__ __forceinline__ void mx_quant_staged(const uint16_t *l, uint8_t *q,
-                                                int64_t ldq, uint8_t *qs,
-                                                int64_t ldqs, int64_t col0,
-                                                int64_t grow0, int arow0,
-                                                int rows, int lane) {
-  static_assert(W % 32 == 0 && (NROWS * W / 32) % 64 == 0, "region");
-  constexpr int BPR = W / 32;                  // blocks per row
+__device__ __forceinline__ void mx_quant_rows_f32(const float *l, uint8_t *q,
+                                                  int64_t ldq, uint8_t *qs,
+                                                  int64_t ldqs, int64_t col0,
+                                                  int64_t grow0, int arow0,
+                                                  int rows, int lane) {
+  constexpr int BPR = W / 32;
+  static_assert((NROWS * BPR) % 64 == 0, "region");
 #pragma unroll 1
   for (int it = 0; it < NROWS * BPR / 64; ++it) {
     const int item = it * 64 + lane;
-    const int r = item / BPR, b = item % BPR;
-    const int pb = st_col<W>(r, b * 32) / 32;  // physical block
-    const uint4 *src = (const uint4 *)(l + r * W + pb * 32);
-    uint4 in[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k) in[k] = src[k];
+    const int r = item % NROWS, b = item / NROWS;
+    float v[32];
+    f32_block<W>(l, r, b, v);
     uint32_t c[8];
-    const uint32_t sb = mx_encode32(in, c);
+    const uint32_t sb = mx_encode32_f32(v, c);
     if (arow0 + r < rows) {
       uint4 *dst = (uint4 *)(q + (grow0 + r) * ldq + col0 + 32 * b);
       dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
@@ -212,96 +234,120 @@ __device__ __forceinline__ void mx_quant_staged(const uint16_t *l, uint8_t *q,
   }
 }
 
-// Column-wise MX encoding of a staged [NROWS][W] bf16 region: blocks of 32
-// region rows down each column.  Block b of column c goes to codes
-// qt[(col0 + c) * ldt + pos0 + 32 b] and scale qts[(col0 + c) * ldts +
-// (pos0 + 32 b) / 32]; region rows at or past `valid` count as zeros (the
-// segment's padding).  Pass it handles block b of 64 neighbouring columns,
-// one per lane, so each of its 32 LDS reads covers 128 contiguous bytes of
-// one region row; every read is issued unconditionally (rows past `valid`
-// are read and then replaced by zero), so the reads are all in flight
-// together instead of each behind its own branch and wait.
+// A staged fp32 [NROWS][W] region rounded to bf16 (nearest even) and written
+// to dst[(grow0 + r) * ld + col0 + c] as 16-byte row pieces, for tile rows
+// arow0 + r < rows and columns col0 + c < N (N % 8 == 0).
 template <int W, int NROWS>
-__device__ __forceinline__ void mx_quant_staged_cols(const uint16_t *l,
-                                                     uint8_t *qt, uint8_t *qts,
-                                                     int64_t ldt, int64_t ldts,
-                                                     int64_t col0, int64_t pos0,
-                                                     int valid, int lane) {
-  constexpr int BPC = NROWS / 32;              // blocks per column
-  static_assert(NROWS % 32 == 0 && W % 64 == 0, "region");
-#pragma unroll 1
-  for (int it = 0; it < (W / 64) * BPC; ++it) {
-    const int b = it % BPC, c = (it / BPC) * 64 + lane;
-    uint32_t v[32];                            // bf16 bit patterns
-    uint32_t mag = 0;
-#pragma unroll
-    for (int j = 0; j < 32; ++j) {
-      const int r = b * 32 + j;
-      const uint32_t x = l[r * W + st_col<W>(r, c)];
-      v[j] = r < valid ? x : 0u;
-      mag = max(mag, v[j] & 0x7fffu);
-    }
-    const int X = mx_shared_exp_bf16(mag);
-    uint32_t pk[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      pk[j] = e4m3_pack4(bf16_bits_to_f32(v[4 * j]), bf16_bits_to_f32(v[4 * j + 1]),
-                         bf16_bits_to_f32(v[4 * j + 2]), bf16_bits_to_f32(v[4 * j + 3]), -X);
-    uint4 *dst = (uint4 *)(qt + (col0 + c) * ldt + pos0 + 32 * b);
-    dst[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
-    dst[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
-    qts[(col0 + c) * ldts + (pos0 + 32 * b) / 32] = (uint8_t)(X + 127);
+__device__ __forceinline__ void store_f32_as_bf16(const float *l, uint16_t *dst,
+                                                  int64_t ld, int64_t col0,
+                                                  int N, int64_t grow0,
+                                                  int arow0, int rows,
+                                                  int lane) {
+  constexpr int LPR = W / 8;                 // lanes per row
+  constexpr int RPI = 64 / LPR;              // rows per instruction
+#pragma unroll 4
+  for (int it = 0; it < NROWS / RPI; ++it) {
+    const int r = it * RPI + lane / LPR;
+    const int c8 = (lane % LPR) * 8;
+    const float4 lo = *(const float4 *)(l + r * W + fphys<W>(r, c8));
+    const float4 hi = *(const float4 *)(l + r * W + fphys<W>(r, c8 + 4));
+    if (arow0 + r < rows && col0 + c8 < N)
+      *(uint4 *)(dst + (grow0 + r) * ld + col0 + c8) =
+          make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
+                     pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
   }
 }
 
-// g and u rows [arow0, arow0 + NROWS) of a tile (tile-relative; g_base and
-// u_base point at the tile's row 0 and first column, both uniform) into a
-// wavefront's staged [NROWS][128] regions at LDS byte addresses lg, lu
-// (st_col<128> layout) by direct global -> LDS loads, four 256-byte rows per
-// instruction: lane i fills region row 4*it + i/16 at column position
-// 8*(i%16), so it reads the column that st_col maps there.  Rows past the
-// tile (`rows`) read the tile's last row (their outputs are never stored):
-// no branches, and one 32-bit offset per row serves both loads, so every
-// load is in flight at once.  The launcher keeps 256 * ld * 2 below 2^32.
-// The caller waits on vmcnt before reading the regions.
-template <int NROWS>
-__device__ __forceinline__ void mx_load_gu_staged(uint32_t lg, uint32_t lu,
-                                                  const uint16_t *g_base,
-                                                  const uint16_t *u_base,
-                                                  int64_t ld, int arow0,
-                                                  int rows, int lane) {
+// Column-wise MX encoding straight from the MFMA accumulator layout.  v holds
+// this lane's 16 values of column (lane & 31) of a 32 x 32 block (rows
+// 8 (i / 4) + 4 h + i % 4, h = lane / 32); lane ^ 32 holds the other 16, and
+// the column's 32 values form one MX block.  Its codes go to qt[c * ldt +
+// pos0 .. + 32) (the first 16 bytes written by half 0, the rest by half 1)
+// and its scale byte to qts[c * ldts + pos0 / 32].
+__device__ __forceinline__ void mx_quant_col_block(const float (&v)[16],
+                                                   int lane, uint8_t *qt,
+                                                   uint8_t *qts, int64_t ldt,
+                                                   int64_t ldts, int64_t c,
+                                                   int64_t pos0) {
+  float mag = 0.f;
 #pragma unroll
-  for (int it = 0; it < NROWS / 4; ++it) {
-    const int r = it * 4 + (lane >> 4);
-    const int c = ((lane & 15) * 8) ^ ((it & 1) * 32);   // st_col<128>(r, .)
-    const int trow = min(arow0 + r, rows - 1);
-    const uint32_t voff = (uint32_t)(trow * (uint32_t)ld + (uint32_t)c) * 2u;
+  for (int i = 0; i < 16; ++i) mag = fmaxf(mag, fabsf(v[i]));
+  mag = fmaxf(mag, __shfl_xor(mag, 32, 64));
+  const int X = mx_shared_exp(mag);
+  uint32_t d[4];                 // rows 8q + 4h .. 8q + 4h + 3
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    d[q] = e4m3_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], -X);
+  const int h = lane >> 5;
+  // half 0 writes rows 0-15 (its d0, d1 and the partner's), half 1 rows 16-31
+  const uint32_t x0 = h ? d[0] : d[2], x1 = h ? d[1] : d[3];
+  const uint32_t y0 = (uint32_t)__shfl_xor((int)x0, 32, 64);
+  const uint32_t y1 = (uint32_t)__shfl_xor((int)x1, 32, 64);
+  const uint4 o = h ? make_uint4(y0, d[2], y1, d[3]) : make_uint4(d[0], y0, d[1], y1);
+  *(uint4 *)(qt + c * ldt + pos0 + 16 * h) = o;
+  if (h) qts[c * ldts + pos0 / 32] = (uint8_t)(X + 127);
+}
+
+// fp32 g and u of 32 tile rows [ar0, ar0 + 32) x 128 columns (g_base and
+// u_base point at tile row 0 of the wavefront's first column, both uniform;
+// row pitch ld floats) into staged [32][128] fp32 regions at LDS byte
+// addresses lg, lu (fphys<128> layout), by direct global -> LDS loads: one
+// instruction fills two 512-byte region rows, lane i the physical 16-byte
+// chunk i % 32 of row 2 it + i / 32, reading the logical chunk that fphys
+// maps there (the map is its own inverse on chunks).  Rows past the tile
+// (`rows`) read the tile's last row.  The launcher keeps 256 * ld * 4 below
+// 2^32.  The caller waits on vmcnt before reading the regions.
+__device__ __forceinline__ void mx_load_gu32(uint32_t lg, uint32_t lu,
+                                             const float *g_base,
+                                             const float *u_base, int64_t ld,
+                                             int ar0, int rows, int lane) {
+#pragma unroll
+  for (int it = 0; it < 16; ++it) {
+    const int r = 2 * it + (lane >> 5);
+    const int pc = lane & 31;
+    const int lc = ((((pc >> 3) ^ ((r >> 2) & 1))) << 3) | ((pc & 7) ^ (r & 7));
+    const int trow = min(ar0 + r, rows - 1);
+    const uint32_t voff = (uint32_t)(trow * (uint32_t)ld + (uint32_t)(lc * 4)) * 4u;
     mx_load_lds16_so(lg + (uint32_t)(it * 1024), g_base, voff);
     mx_load_lds16_so(lu + (uint32_t)(it * 1024), u_base, voff);
   }
 }
 
-// SwiGLU forward, one 32-row block: block 2q holds g and block 2q+1 the
-// matching u in every lane.  s_reg: lane l holds the routing scale of
-// region row (mloc & 64) + l.
+// SwiGLU forward of one 32-row block (region rows mloc ..): block 2q holds g
+// and block 2q+1 the matching u in every lane.  a = s SiLU(g) u goes to the
+// fp32 region la ([128][64], fphys<64>); g and u go to HBM in fp32 (gp: the
+// wavefront's first row and column of [g | u], null: not written), 32 lanes
+// writing 128 contiguous bytes of one row, from a per-row uniform base and a
+// 32-bit lane offset.  s_reg: lane l holds the routing scale of region row
+// (mloc & 64) + l.
 template <int NB>
-__device__ __forceinline__ void mx_swiglu_stage(
-    const f32x16 (&am)[NB], int mloc, int lane, float s_reg, uint16_t *l0,
-    uint16_t *l1, int phase) {
+__device__ __forceinline__ void mx_swiglu_block(const f32x16 (&am)[NB],
+                                                int mloc, int lane,
+                                                float s_reg, float *la,
+                                                float *gp, int64_t ldgu, int N,
+                                                int arow0, int rows) {
+  const int h = lane >> 5;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
-    const int row = mloc + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    const float s = phase == 0 ? __shfl(s_reg, row & 63, 64) : 1.f;
+    const int row = mloc + 8 * (r >> 2) + 4 * h + (r & 3);
+    const float s = __shfl(s_reg, row & 63, 64);
 #pragma unroll
     for (int q = 0; q < NB / 2; ++q) {
-      const float g = am[2 * q][r], u = am[2 * q + 1][r];
       const int col = q * 32 + (lane & 31);
-      const int o = row * 64 + st_col<64>(row, col);
-      if (phase == 0) {
-        l0[o] = (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
-        l1[o] = (uint16_t)f32_to_bf16_bits(g);
-      } else {
-        l0[o] = (uint16_t)f32_to_bf16_bits(u);
+      la[row * 64 + fphys<64>(row, col)] = s * silu_f32(am[2 * q][r]) * am[2 * q + 1][r];
+    }
+  }
+  if (gp == nullptr) return;
+  const uint32_t loff = (uint32_t)(4 * h * ldgu) + (uint32_t)(lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int urow = mloc + 8 * (r >> 2) + (r & 3);      // row of half 0
+    float *base = mx_uniform(gp + (int64_t)urow * ldgu);
+    if (arow0 + urow + 4 * h < rows) {
+#pragma unroll
+      for (int q = 0; q < NB / 2; ++q) {
+        base[loff + q * 32] = am[2 * q][r];
+        base[loff + N + q * 32] = am[2 * q + 1][r];
       }
     }
   }
@@ -353,41 +399,69 @@ __device__ __forceinline__ float mx_sum16_over32(const float (&v)[16], int lane)
   return z + mx_xor32<1>(z);
 }
 
-// SwiGLU backward of one 32-row block against the staged g, u of its rows
-// (region rows `mloc` relative): dg, du replace g, u in place; the partial
-// ds of each row (over this wavefront's 128 columns) goes to ds_part.
-// s_reg: lane l holds the routing scale of wavefront row (mrow & 64) + l.
+// SwiGLU backward of one 32-row block m of a wavefront (tile rows mrow0 =
+// arow0 + 32 m ..) against the staged fp32 g, u of its rows (lg, lu, [32][128]
+// fphys<128>).  In fp32: a = s SiLU(g) u, dg = da s u SiLU'(g),
+// du = da s SiLU(g), ds partial = sum over the wavefront's 128 columns of
+// da SiLU(g) u.  dg and du replace g and u in the regions (for the row-wise
+// outputs that follow); the column-wise MX codes of dg, du (t0, t1) and of a
+// (t2) are written from the registers, rows past the segment (tile row >=
+// rows) counting as zeros, i.e. as the segment's padding.  pos0: padded
+// position of the block's first row.  s_reg: lane l holds the routing scale
+// of wavefront row (32 m & 64) + l.
 template <int BN, int WN, int NB>
-__device__ __forceinline__ void mx_swiglu_bwd_stage(
-    const MxArgs &p, const f32x16 (&am)[NB], int mloc, int mrow, int lane,
-    int arow0, int rows, int row0, int nt, int wn, float s_reg, uint16_t *lg,
-    uint16_t *lu) {
+__device__ __forceinline__ void mx_swiglu_bwd_block(
+    const MxArgs &p, const f32x16 (&am)[NB], int m, int lane, int arow0,
+    int rows, int row0, int nt, int wn, float s_reg, float *lg, float *lu,
+    int64_t col0, int64_t pos0) {
+  const int mrow0 = arow0 + 32 * m;
+  const int h = lane >> 5;
   float part[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-    const int row = mloc + rr;                 // region row
-    const float s = __shfl(s_reg, (mrow + rr) & 63, 64);
-    part[r] = 0.f;
+  for (int r = 0; r < 16; ++r) part[r] = 0.f;
 #pragma unroll
-    for (int n = 0; n < NB; ++n) {
-      const int o = row * 128 + st_col<128>(row, n * 32 + (lane & 31));
+  for (int n = 0; n < NB; ++n) {
+    float v[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+      const int o = row * 128 + fphys<128>(row, n * 32 + (lane & 31));
+      const float s = __shfl(s_reg, (32 * m + row) & 63, 64);
       const float da = am[n][r];
-      const float g = bf16_bits_to_f32(lg[o]);
-      const float u = bf16_bits_to_f32(lu[o]);
+      const float g = lg[o], u = lu[o];
       const float sg = sigmoid_f32(g);
       const float sl = g * sg;
       const float dsl = sg * (1.f + g * (1.f - sg));
-      lg[o] = (uint16_t)f32_to_bf16_bits(da * s * u * dsl);
-      lu[o] = (uint16_t)f32_to_bf16_bits(da * s * sl);
       part[r] += da * sl * u;
+      lg[o] = da * s * u * dsl;                       // dg
+      lu[o] = da * s * sl;                            // du
+      v[r] = mrow0 + row < rows ? s * sl * u : 0.f;   // a (padding rows: 0)
     }
+    const int64_t c = col0 + n * 32 + (lane & 31);
+    if (p.t2) mx_quant_col_block(v, lane, p.t2, p.t2s, p.ldt, p.ldts, c, pos0);
+    if (p.t0) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float *src = t ? lu : lg;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 8 * (r >> 2) + 4 * h + (r & 3);
+          const float x = src[row * 128 + fphys<128>(row, n * 32 + (lane & 31))];
+          v[r] = mrow0 + row < rows ? x : 0.f;
+        }
+        if (t) mx_quant_col_block(v, lane, p.t1, p.t1s, p.ldt, p.ldts, c, pos0);
+        else mx_quant_col_block(v, lane, p.t0, p.t0s, p.ldt, p.ldts, c, pos0);
+      }
+    }
+    // keep the column blocks in sequence: interleaving them only raises the
+    // number of live values (the accumulators already fill the registers)
+    __builtin_amdgcn_sched_barrier(0);
   }
   const float tot = mx_sum16_over32(part, lane);
   const int r = (lane & 31) >> 1;
-  const int rr = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-  if ((lane & 1) == 0 && arow0 + mrow + rr < rows)
-    p.ds_part[(int64_t)(row0 + arow0 + mrow + rr) * (p.NT * WN) + nt * WN + wn] = tot;
+  const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
+  if ((lane & 1) == 0 && mrow0 + rr < rows)
+    p.ds_part[(int64_t)(row0 + mrow0 + rr) * (p.NT * WN) + nt * WN + wn] = tot;
 }
 
 template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES, int BKB>
@@ -656,62 +730,58 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   }
   if constexpr (EPI == MX_EPI_SWIGLU) {
     static_assert(WTM == 128 && WTN == 128, "SwiGLU staging expects 128x128 wavefront tiles");
-    // region: two [128][64] arrays (a | g, then u)
-    uint16_t *l0 = lw, *l1 = lw + 128 * 64;
+    // region: a in fp32, [128][64]; g and u go to HBM from the registers
+    float *la = (float *)lw;
     const int64_t col0 = (int64_t)nt * (BN / 2) + brow0 / 2;
     const int64_t grow0 = row0 + arow0;
-#pragma unroll
-    for (int phase = 0; phase < 2; ++phase) {
+    float *gp = p.gu ? p.gu + grow0 * p.ldgu + col0 : nullptr;
 #define MX_SW_BLOCK(m) \
-      if constexpr (MB > (m)) mx_swiglu_stage<NB>(acc[m], (m) * 32, lane, (m) < 2 ? s_lo : s_hi, l0, l1, phase);
-      MX_SW_BLOCK(0) MX_SW_BLOCK(1) MX_SW_BLOCK(2) MX_SW_BLOCK(3)
+    if constexpr (MB > (m)) mx_swiglu_block<NB>(acc[m], (m) * 32, lane, (m) < 2 ? s_lo : s_hi, la, gp, p.ldgu, p.N, arow0, rows);
+    MX_SW_BLOCK(0) MX_SW_BLOCK(1) MX_SW_BLOCK(2) MX_SW_BLOCK(3)
 #undef MX_SW_BLOCK
-      __syncthreads();
-      if (phase == 0) {
-        store_staged<64, 128>(l0, (uint16_t *)p.C, p.ldc, col0, p.N, grow0, arow0, rows, lane);
-        if (p.q) mx_quant_staged<64, 128>(l0, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, arow0, rows, lane);
-        if (p.gu) store_staged<64, 128>(l1, p.gu, p.ldgu, col0, p.N, grow0, arow0, rows, lane);
-      } else if (p.gu) {
-        store_staged<64, 128>(l0, p.gu, p.ldgu, p.N + col0, 2 * p.N, grow0, arow0, rows, lane);
-      }
-      __syncthreads();
-    }
+    __syncthreads();
+    store_f32_as_bf16<64, 128>(la, (uint16_t *)p.C, p.ldc, col0, p.N, grow0, arow0, rows, lane);
+    if (p.q) mx_quant_rows_f32<64, 128>(la, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, arow0, rows, lane);
   } else if constexpr (EPI == MX_EPI_SWIGLU_BWD) {
     static_assert(WTM == 128 && WTN == 128 && MB == 4, "staging expects 128x128 wavefront tiles");
-    // region: g and u of 64 rows x 128 columns, two halves of the 128 rows
-    uint16_t *lg = lw, *lu = lw + 64 * 128;
+    // region: fp32 g and u of one 32-row block x 128 columns ([32][128] each)
+    float *lg = (float *)lw, *lu = lg + 32 * 128;
     const uint32_t lgb = lds0 + (uint32_t)(wid * WTM * WTN * 2);
-    const uint32_t lub = lgb + 64 * 128 * 2;
+    const uint32_t lub = lgb + 32 * 128 * 4;
     const int64_t col0 = (int64_t)nt * BN + brow0;
-#pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      const int64_t grow0 = row0 + arow0 + half * 64;
-      const int ar0 = arow0 + half * 64;
-      const uint16_t *gb = mx_uniform(p.gu + (int64_t)row0 * p.ldgu + col0);
-      mx_load_gu_staged<64>(lgb, lub, gb, mx_uniform(gb + p.N), p.ldgu, ar0, rows, lane);
-      mx_wait_barrier<0>();
-      if (half == 0) {
-        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[0], 0, 0, lane, arow0, rows, row0, nt, wn, s_lo, lg, lu);
-        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[1], 32, 32, lane, arow0, rows, row0, nt, wn, s_lo, lg, lu);
-      } else {
-        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[2], 0, 64, lane, arow0, rows, row0, nt, wn, s_hi, lg, lu);
-        mx_swiglu_bwd_stage<BN, WN, NB>(p, acc[3], 32, 96, lane, arow0, rows, row0, nt, wn, s_hi, lg, lu);
+    const float *gb = mx_uniform(p.gu + (int64_t)row0 * p.ldgu + col0);
+    const float *ub = mx_uniform(gb + p.N);
+    // padded position of tile row 0 in the column-wise copies: tile rows start
+    // at the segment's first row + mt * BM, padded at tpad[e] + mt * BM
+    const int64_t pbase = p.tpad ? (int64_t)p.tpad[e] + (row0 - r_begin) : 0;
+    // One 32-row block per pass, not unrolled: the pass copies its block's
+    // accumulators (constant indices in each case of the switch) and the
+    // rest of the body exists once, which keeps the live values in bounds.
+#pragma unroll 1
+    for (int m = 0; m < MB; ++m) {
+      const int ar0 = arow0 + 32 * m;
+      const int64_t grow0 = row0 + ar0;
+      f32x16 cur[NB];
+      switch (m) {
+#define MX_BWD_COPY(mm) \
+        case mm: \
+          _Pragma("unroll") for (int n = 0; n < NB; ++n) cur[n] = acc[mm][n]; \
+          break;
+        MX_BWD_COPY(0) MX_BWD_COPY(1) MX_BWD_COPY(2) MX_BWD_COPY(3)
+#undef MX_BWD_COPY
       }
+      mx_load_gu32(lgb, lub, gb, ub, p.ldgu, ar0, rows, lane);
+      mx_wait_barrier<0>();
+      mx_swiglu_bwd_block<BN, WN, NB>(p, cur, m, lane, arow0, rows, row0, nt, wn,
+                                      m < 2 ? s_lo : s_hi, lg, lu, col0, pbase + ar0);
       __syncthreads();
       if (p.dgu) {
-        store_staged<128, 64>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
-        store_staged<128, 64>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
-      }
-      if (p.t0) {
-        // tile rows start at offsets[e] + mt * BM, padded position tpad[e] + mt * BM
-        const int64_t pos0 = (int64_t)p.tpad[e] + (row0 - r_begin) + ar0;
-        const int valid = min(max(rows - ar0, 0), 64);
-        mx_quant_staged_cols<128, 64>(lg, p.t0, p.t0s, p.ldt, p.ldts, col0, pos0, valid, lane);
-        mx_quant_staged_cols<128, 64>(lu, p.t1, p.t1s, p.ldt, p.ldts, col0, pos0, valid, lane);
+        store_f32_as_bf16<128, 32>(lg, p.dgu, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
+        store_f32_as_bf16<128, 32>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
       }
       if (p.q) {
-        mx_quant_staged<128, 64>(lg, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, ar0, rows, lane);
-        mx_quant_staged<128, 64>(lu, p.q, p.ldq, p.qs, p.ldqs, p.N + col0, grow0, ar0, rows, lane);
+        mx_quant_rows_f32<128, 32>(lg, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, ar0, rows, lane);
+        mx_quant_rows_f32<128, 32>(lu, p.q, p.ldq, p.qs, p.ldqs, p.N + col0, grow0, ar0, rows, lane);
       }
       __syncthreads();
     }
@@ -776,6 +846,7 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
   p.gu = d.gu; p.ldgu = d.ldgu; p.dgu = d.dgu; p.ds_part = d.ds_part;
   p.q = d.q; p.qs = d.qs; p.ldq = d.ldq; p.ldqs = d.ldqs;
   p.t0 = d.t0; p.t0s = d.t0s; p.t1 = d.t1; p.t1s = d.t1s;
+  p.t2 = d.t2; p.t2s = d.t2s;
   p.ldt = d.ldt; p.ldts = d.ldts; p.tpad = d.tpad;
   p.ksplit = d.ksplit;
   const int cols = epi == MX_EPI_SWIGLU ? kMxBN / 2 : kMxBN;
@@ -786,8 +857,8 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
                                     d.tile_ws, d.err);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // SwiGLU backward: 32-bit byte offsets within a tile's rows of g|u.
-  if (epi == MX_EPI_SWIGLU_BWD && (int64_t)kMxBM * d.ldgu * 2 >= (1ll << 32))
+  // SwiGLU backward: 32-bit byte offsets within a tile's rows of fp32 g|u.
+  if (epi == MX_EPI_SWIGLU_BWD && (int64_t)kMxBM * d.ldgu * 4 >= (1ll << 32))
     return hipErrorInvalidValue;
   const int64_t max_tiles = ((d.R_cap + kMxBM - 1) / kMxBM + d.G) * (int64_t)p.NT;
   if (epi == MX_EPI_SWIGLU) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU>(p, max_tiles, s);

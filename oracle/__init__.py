@@ -56,8 +56,6 @@ def _lib():
         L.orc_gather_rows.argtypes = [vp, i32, i64, i64, vp, i64, vp]
         L.orc_expert_ffn_rows.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32,
                                           i64, i64, i64, vp, vp]
-        L.orc_gate_up_rows.argtypes = [vp, i32, vp, vp, vp, i32, i64, i64,
-                                       i64, vp, vp]
         L.orc_combine.argtypes = [vp, vp, vp, i64, i64, i64, vp]
         L.orc_moe_tokens.argtypes = [vp, i32, vp, vp, i64, vp, i64, i64, i64,
                                      vp, vp, vp, i32, i64, i64, vp]
@@ -65,6 +63,7 @@ def _lib():
         L.orc_e4m3_value.restype = ctypes.c_double
         L.orc_e4m3_encode.argtypes = [ctypes.c_double]
         L.orc_e4m3_encode.restype = ctypes.c_uint8
+        L.orc_e4m3_encode_array.argtypes = [vp, i64, vp]
         L.orc_mx_scale_byte.argtypes = [ctypes.c_double]
         L.orc_mx_scale_byte.restype = ctypes.c_uint8
         L.orc_mx_quantize_rows.argtypes = [vp, i64, i64, vp, vp]
@@ -73,6 +72,7 @@ def _lib():
         L.orc_round_bf16.argtypes = [vp, i64, vp]
         L.orc_swiglu_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp,
                                           vp]
+        L.orc_swiglu_rows.argtypes = [vp, vp, vp, i64, i64, vp]
         _L = L
     return _L
 
@@ -163,19 +163,6 @@ def expert_ffn_rows(xs, experts, scales, w_gate, w_up, w_down,
     return a, y
 
 
-def gate_up_rows(xs, experts, w_gate, w_up):
-    xs = _c(xs)
-    ex = _c(experts, np.int32)
-    wg, wu = _c(w_gate), _c(w_up)
-    n, H = xs.shape
-    I = wg.shape[1]
-    g = np.empty((n, I), dtype=np.float64)
-    u = np.empty((n, I), dtype=np.float64)
-    _lib().orc_gate_up_rows(_p(xs), _dt(xs), _p(ex), _p(wg), _p(wu), _dt(wg),
-                            n, H, I, _p(g), _p(u))
-    return g, u
-
-
 def combine(y, inv, w=None):
     y = _c(y, np.float64)
     inv = _c(inv, np.int32)
@@ -255,6 +242,14 @@ def e4m3_encode(v):
     return int(_lib().orc_e4m3_encode(float(v)))
 
 
+def e4m3_encode_array(v):
+    """E4M3 codes (nearest, ties to even, saturating) of every value."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _lib().orc_e4m3_encode_array(_p(v), v.size, _p(out))
+    return out
+
+
 def mx_scale_byte(amax):
     return int(_lib().orc_mx_scale_byte(float(amax)))
 
@@ -286,16 +281,6 @@ def mx_roundtrip_rows(v):
 def mx_roundtrip_cols(v):
     """Dequantised MX values of v, blocks of 32 down each column."""
     return np.ascontiguousarray(mx_roundtrip_rows(np.ascontiguousarray(v.T)).T)
-
-
-def mx_roundtrip_cols_segmented(v, offsets):
-    """Blocks of 32 down each column, restarting at every segment start."""
-    out = np.empty(v.shape, dtype=np.float64)
-    for e in range(len(offsets) - 1):
-        a, b = int(offsets[e]), int(offsets[e + 1])
-        if b > a:
-            out[a:b] = mx_roundtrip_cols(v[a:b])
-    return out
 
 
 def to_f64(a):
@@ -330,81 +315,140 @@ def swiglu_bwd(da, g, u, s):
     return dg, du, ds
 
 
-def mxfp8_mlp_step(x_perm, offsets, s_perm, w_gate, w_up, w_down, dy,
-                   quantize=True, handoff=None):
-    """MXFP8 grouped MLP forward + backward on permuted rows, fp64.
+def swiglu(g, u, s=None):
+    """a = s * SiLU(g) * u (ScaledSwiGLU) of given pre-activations, fp64."""
+    g, u = _c(g, np.float64), _c(u, np.float64)
+    R, I = g.shape
+    sc = None if s is None else _c(s, np.float64)
+    a = np.empty((R, I))
+    _lib().orc_swiglu_rows(_p(g), _p(u), _p(sc), R, I, _p(a))
+    return a
 
-    Every GEMM operand is MX-quantised (blocks of 32) along that GEMM's
-    reduction axis; products of the dequantised values are exact in fp64.
-      forward:  g = Q_H(x) Q_H(W_g)^T, u likewise, a = s*SiLU(g)*u,
-                y = Q_I(a) Q_I(W_d)^T
-      backward: da = Q_H(dY) Q_H(W_d), dg/du/ds by the chain rule,
-                dX = Q_I(dg) Q_I(W_g) + Q_I(du) Q_I(W_u),
-                dW_d[e] = Q_R(dY_e)^T Q_R(a_e), dW_g[e] = Q_R(dg_e)^T Q_R(x_e),
-                dW_u[e] = Q_R(du_e)^T Q_R(x_e)
-    with Q_R blocking along the rows of each expert's segment.
-    All inputs are bf16 bits (uint16) or fp64; returns fp64 arrays.
-    ``quantize=False`` replaces every Q by the identity (the same chain rule
-    on unquantised operands), which the finite-difference pins check.
 
-    ``handoff`` (default: same as ``quantize``) stores the tensors that pass
-    from one operation to the next in bf16 before they are used, as in a
-    BF16 training step whose GEMMs run in MXFP8 ([TE-MXFP8]): a before the
-    down projection and its weight gradient, the saved g and u before the
-    SwiGLU backward, dg and du before their GEMMs.  Each quantisation then
-    starts from the bf16 tensor, as it does on the device.  The returned
-    g, u, a, dg, du are the fp64 values before that rounding.
-    """
-    if handoff is None:
-        handoff = quantize
-    bf = round_bf16 if handoff else (lambda v: v)
+def mx_gemm_nt(A, B, quantize=True):
+    """C = Q(A) . Q(B)^T with every row of A [M, K] and of B [N, K]
+    MX-quantised along K (blocks of 32 from column 0; a shorter last block is
+    a block padded with zeros) and the dequantised values multiplied exactly
+    in fp64.  This is the one MXFP8 GEMM of the step: every operand is
+    blocked along its GEMM's reduction axis [TE-MXFP8], which a caller
+    chooses by the orientation it passes.  quantize=False: plain product."""
+    A, B = _c(A, np.float64), _c(B, np.float64)
     if quantize:
-        q_rows, q_cols = mx_roundtrip_rows, mx_roundtrip_cols
-    else:
-        q_rows = q_cols = (lambda v: np.array(v, dtype=np.float64))
+        A, B = mx_roundtrip_rows(A), mx_roundtrip_rows(B)
+    return matmul_nt(A, B)
+
+
+def _T(v):
+    return np.ascontiguousarray(np.asarray(v, dtype=np.float64).T)
+
+
+def mxfp8_forward(x_perm, offsets, s_perm, w_gate, w_up, w_down,
+                  quantize=True):
+    """MXFP8 grouped MLP forward on permuted rows [TE-Grouped, TE-MXFP8]:
+    per expert e and its rows, g = Q_H(x) Q_H(W_g)^T, u likewise,
+    a = s SiLU(g) u (fp64, not rounded), y = Q_I(a) Q_I(W_d)^T.
+    Inputs bf16 bits (uint16) or fp64; returns dict of fp64 g, u, a, y."""
     x = to_f64(x_perm)
-    dY = to_f64(dy)
     s = np.asarray(s_perm, dtype=np.float64)
     n_local = len(offsets) - 1
     R, H = x.shape
     I = w_gate.shape[1]
-    xq = q_rows(x)
-    dyq_h = q_rows(dY)
     g = np.zeros((R, I)); u = np.zeros((R, I)); a = np.zeros((R, I))
-    y = np.zeros((R, H)); da = np.zeros((R, I))
-    dx = np.zeros((R, H)); ds = np.zeros(R)
-    dwg = np.zeros((n_local, I, H)); dwu = np.zeros((n_local, I, H))
-    dwd = np.zeros((n_local, H, I))
-    dg = np.zeros((R, I)); du = np.zeros((R, I))
+    y = np.zeros((R, H))
     for e in range(n_local):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        Wg, Wu, Wd = (to_f64(t[e]) for t in (w_gate, w_up, w_down))
         if r1 == r0:
             continue
-        xe = xq[r0:r1]
-        g[r0:r1] = matmul_nt(xe, q_rows(Wg))
-        u[r0:r1] = matmul_nt(xe, q_rows(Wu))
-        a[r0:r1] = s[r0:r1, None] * (g[r0:r1] / (1.0 + np.exp(-g[r0:r1]))) * u[r0:r1]
-        a_h = bf(a[r0:r1])
-        y[r0:r1] = matmul_nt(q_rows(a_h), q_rows(Wd))
-        # dgrad of down: da[r, i] = sum_h dY[r, h] Wd[h, i], K = H
-        da[r0:r1] = matmul_nt(dyq_h[r0:r1], np.ascontiguousarray(q_cols(Wd).T))
+        xe = x[r0:r1]
+        g[r0:r1] = mx_gemm_nt(xe, to_f64(w_gate[e]), quantize)
+        u[r0:r1] = mx_gemm_nt(xe, to_f64(w_up[e]), quantize)
+        a[r0:r1] = swiglu(g[r0:r1], u[r0:r1], s[r0:r1])
+        y[r0:r1] = mx_gemm_nt(a[r0:r1], to_f64(w_down[e]), quantize)
+    return dict(g=g, u=u, a=a, y=y)
+
+
+def mxfp8_wgrad(A, B, offsets, quantize=True):
+    """Weight gradient per expert: W[e] = Q_R(A_e)^T Q_R(B_e) over expert
+    e's rows (A [R, M], B [R, N] -> [n_local, M, N]), every operand blocked
+    down the rows of the segment from its first row (the GEMM's reduction
+    axis); an expert without rows gets zeros."""
+    A, B = to_f64(A), to_f64(B)
+    n_local = len(offsets) - 1
+    out = np.zeros((n_local, A.shape[1], B.shape[1]))
+    for e in range(n_local):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 > r0:
+            out[e] = mx_gemm_nt(_T(A[r0:r1]), _T(B[r0:r1]), quantize)
+    return out
+
+
+def mxfp8_backward_down(dy, g, u, s_perm, offsets, w_down, quantize=True):
+    """Backward of the down projection and of ScaledSwiGLU, by the chain
+    rule: da = Q_H(dY) Q_H(W_d) per expert (K = H), dg, du, ds from
+    swiglu_bwd at the given g, u, and dW_d = Q_R(dY)^T Q_R(a) with a =
+    s SiLU(g) u.  Returns dict of fp64 da, dg, du, ds, a, dw_down."""
+    dY = to_f64(dy)
+    g, u = to_f64(g), to_f64(u)
+    s = np.asarray(s_perm, dtype=np.float64)
+    n_local = len(offsets) - 1
+    R, I = g.shape
+    da = np.zeros((R, I)); dg = np.zeros((R, I)); du = np.zeros((R, I))
+    ds = np.zeros(R)
+    for e in range(n_local):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        # W_d[e] is [H, I]; da[r, i] = sum_h dY[r, h] W_d[h, i]
+        da[r0:r1] = mx_gemm_nt(dY[r0:r1], _T(to_f64(w_down[e])), quantize)
         dg[r0:r1], du[r0:r1], ds[r0:r1] = swiglu_bwd(
-            da[r0:r1], bf(g[r0:r1]), bf(u[r0:r1]), s[r0:r1])
-        dg_h, du_h = bf(dg[r0:r1]), bf(du[r0:r1])
-        # dgrad of gate/up: dX[r, h] = sum_i dg[r,i] Wg[i,h] + du[r,i] Wu[i,h]
-        WgT = np.ascontiguousarray(q_cols(Wg).T)
-        WuT = np.ascontiguousarray(q_cols(Wu).T)
-        dx[r0:r1] = (matmul_nt(q_rows(dg_h), WgT)
-                     + matmul_nt(q_rows(du_h), WuT))
-        # wgrad: reduction over the segment's rows
-        dyr = np.ascontiguousarray(q_cols(dY[r0:r1]).T)   # [H, n]
-        ar = np.ascontiguousarray(q_cols(a_h).T)          # [I, n]
-        xr = np.ascontiguousarray(q_cols(x[r0:r1]).T)     # [H, n]
-        dgr = np.ascontiguousarray(q_cols(dg_h).T)        # [I, n]
-        dur = np.ascontiguousarray(q_cols(du_h).T)
-        dwd[e] = matmul_nt(dyr, ar)
-        dwg[e] = matmul_nt(dgr, xr)
-        dwu[e] = matmul_nt(dur, xr)
-    return dict(g=g, u=u, a=a, y=y, da=da, dg=dg, du=du, ds=ds, dx=dx,
-                dw_gate=dwg, dw_up=dwu, dw_down=dwd)
+            da[r0:r1], g[r0:r1], u[r0:r1], s[r0:r1])
+    a = swiglu(g, u, s)
+    dwd = mxfp8_wgrad(dY, a, offsets, quantize)
+    return dict(da=da, dg=dg, du=du, ds=ds, a=a, dw_down=dwd)
+
+
+def mxfp8_backward_gate_up(dg, du, x_perm, offsets, w_gate, w_up,
+                           quantize=True):
+    """Backward of the gate/up projection: dX = Q_I(dg) Q_I(W_g) +
+    Q_I(du) Q_I(W_u) per expert (K = I), dW_g = Q_R(dg)^T Q_R(x),
+    dW_u = Q_R(du)^T Q_R(x).  Returns dict of fp64 dx, dw_gate, dw_up."""
+    dg, du, x = to_f64(dg), to_f64(du), to_f64(x_perm)
+    n_local = len(offsets) - 1
+    R, H = x.shape
+    dx = np.zeros((R, H))
+    for e in range(n_local):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        # W_g[e] is [I, H]; dX[r, h] = sum_i dg[r, i] W_g[i, h] + du W_u
+        dx[r0:r1] = (mx_gemm_nt(dg[r0:r1], _T(to_f64(w_gate[e])), quantize)
+                     + mx_gemm_nt(du[r0:r1], _T(to_f64(w_up[e])), quantize))
+    return dict(dx=dx, dw_gate=mxfp8_wgrad(dg, x, offsets, quantize),
+                dw_up=mxfp8_wgrad(du, x, offsets, quantize))
+
+
+def mxfp8_mlp_step(x_perm, offsets, s_perm, w_gate, w_up, w_down, dy,
+                   quantize=True, bf16_dgu=False):
+    """MXFP8 grouped MLP forward + backward on permuted rows, fp64: the
+    forward, the down/SwiGLU backward at the forward's own g, u, and the
+    gate/up backward.  Every GEMM operand is MX-quantised along that GEMM's
+    reduction axis (mx_gemm_nt); no tensor is rounded to bf16 on the way
+    (the quantisation is fused with SwiGLU and the scaling [TE-MXFP8]).
+    quantize=False: the same chain rule on unquantised operands (what the
+    finite-difference pins check).  bf16_dgu=True: dg and du are rounded to
+    bf16 before the gate/up backward quantises them, as the unfused stage
+    API hands [dg | du] from one call to the next in bf16 (a labelled
+    variant for that API only).  Returns fp64 g, u, a, y, da, dg, du, ds,
+    dx, dw_gate, dw_up, dw_down."""
+    f = mxfp8_forward(x_perm, offsets, s_perm, w_gate, w_up, w_down, quantize)
+    b = mxfp8_backward_down(dy, f["g"], f["u"], s_perm, offsets, w_down,
+                            quantize)
+    dg, du = b["dg"], b["du"]
+    if bf16_dgu:
+        dg, du = round_bf16(dg), round_bf16(du)
+    c = mxfp8_backward_gate_up(dg, du, x_perm, offsets, w_gate, w_up,
+                               quantize)
+    return dict(g=f["g"], u=f["u"], a=f["a"], y=f["y"], da=b["da"],
+                dg=b["dg"], du=b["du"], ds=b["ds"], dx=c["dx"],
+                dw_gate=c["dw_gate"], dw_up=c["dw_up"],
+                dw_down=b["dw_down"])

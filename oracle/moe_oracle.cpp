@@ -211,27 +211,6 @@ void orc_expert_ffn_rows(const void *xs, int xdt, const int32_t *ex,
   }
 }
 
-// Gate and up pre-activations of listed rows (fp64): g, u [n, I].
-void orc_gate_up_rows(const void *xs, int xdt, const int32_t *ex,
-                      const void *w_gate, const void *w_up, int wdt,
-                      int64_t nrows, int64_t H, int64_t I, double *g_out,
-                      double *u_out) {
-#pragma omp parallel for schedule(dynamic, 1)
-  for (int64_t n = 0; n < nrows; ++n) {
-    const int64_t e = ex[n];
-    for (int64_t i = 0; i < I; ++i) {
-      double g = 0.0, u = 0.0;
-      const int64_t base = (e * I + i) * H;
-      for (int64_t h = 0; h < H; ++h) {
-        const double xv = load(xs, xdt, n * H + h);
-        g += load(w_gate, wdt, base + h) * xv;
-        u += load(w_up, wdt, base + h) * xv;
-      }
-      g_out[n * I + i] = g;
-      u_out[n * I + i] = u;
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // Combine.  [WideEP-Premise]/[WideEP-Comm]: the chosen experts' results come
@@ -328,6 +307,12 @@ uint8_t orc_e4m3_encode(double v) {
   return (uint8_t)(best | (std::signbit(v) ? 0x80 : 0));
 }
 
+// orc_e4m3_encode of each of n values.
+void orc_e4m3_encode_array(const double *v, int64_t n, uint8_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(v[i]);
+}
+
 // Shared E8M0 scale byte of a block with largest magnitude amax.
 uint8_t orc_mx_scale_byte(double amax) {
   if (amax == 0.0) return 0;
@@ -406,6 +391,19 @@ void orc_matmul_nt(const double *A, const double *B, int64_t M, int64_t N,
       double acc = 0.0;
       for (int64_t kk = 0; kk < K; ++kk) acc += A[m * K + kk] * B[n * K + kk];
       C[m * N + n] = acc;
+    }
+}
+
+// ScaledSwiGLU of given pre-activations ([TE-Grouped]; SwiGLU per Shazeer
+// 2020 with the routing scale folded in): a = s * SiLU(g) * u, g, u [rows, I],
+// s [rows] (NULL: 1).
+void orc_swiglu_rows(const double *g, const double *u, const double *s,
+                     int64_t rows, int64_t I, double *a) {
+#pragma omp parallel for schedule(static)
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t i = 0; i < I; ++i) {
+      const int64_t o = r * I + i;
+      a[o] = (s ? s[r] : 1.0) * silu(g[o]) * u[o];
     }
 }
 

@@ -207,14 +207,14 @@ def test_mxfp8_validation(L):
     # the fused call keeps the MX codes of [dg | du] beside the down workspace
     assert db > 0 and gb > 0 and bb >= db + 64 * 2 * 512
     d = L.moe_grouped_mlp_mxfp8_bwd_down
-    assert d(P, P, None, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db, None) == E_ARG
-    assert d(P, P, P, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db - 1, None) == E_WS
+    assert d(P, None, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db, None) == E_ARG
+    assert d(P, P, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db - 1, None) == E_WS
     u = L.moe_grouped_mlp_mxfp8_bwd_gate_up
     assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, None, P, P, P, gb, None) == E_ARG
     assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P_ODD, P, gb, None) == E_ALIGN
     assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P, P, gb - 1, None) == E_WS
     b = L.moe_grouped_mlp_mxfp8_bwd
-    args = [P, P, P, P, P, None, 2, 64, 512, 512] + [P] * 11 + [P, bb, None]
+    args = [P, P, P, P, None, 2, 64, 512, 512] + [P] * 11 + [P, bb, None]
     bad = list(args); bad[-2] = bb - 1
     assert b(*bad) == E_WS
     bad = list(args); bad[0] = None

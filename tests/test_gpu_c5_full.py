@@ -2,13 +2,15 @@
 T=16384, H=4096, I=8192; R = 32768 rows) through the C ABI, in the launch
 configuration the benchmark times, against the oracle on sampled outputs.
 
-Each GEMM stage runs on the full tensors; the oracle then computes sampled
-outputs one by one, quantising only the operand rows or columns a sample
-needs (a sample of a GEMM with K-blocked MX operands depends on one A
-vector and one B vector).  Stage inputs that other stages produce (a, g|u,
-dg|du) are seeded stand-alone bf16 tensors, so both sides quantise the same
-values.  Samples: 32 rows spread over the experts x 64 random columns per
-output (weight gradients: 32 output rows x 64 columns of two experts).
+Each GEMM stage runs on the full tensors; the oracle's own functions
+(mx_gemm_nt, swiglu, swiglu_bwd, mxfp8_wgrad) then compute sampled outputs,
+on only the operand rows or columns a sample needs (a sample of a GEMM with
+K-blocked MX operands depends on one A vector and one B vector; a weight
+gradient's columns are independent of each other).  Stage inputs that other
+stages produce (a, g|u, dg|du) are seeded stand-alone tensors (g|u as fp32
+values of the bf16 draw), so both sides start from the same values.
+Samples: 32 rows spread over the experts x 64 random columns per output
+(weight gradients: 32 output rows x 64 columns of two experts).
 Tolerance: the per-row rule with the row RMS taken over the sampled
 reference values of that row (64 per row).
 """
@@ -26,16 +28,12 @@ TAU = 6e-2
 NR, NC = 32, 64
 
 
-def _q(v):
-    """MX round trip of each row of v (blocks of 32 along the row)."""
-    return orc.mx_roundtrip_rows(np.ascontiguousarray(v, dtype=np.float64))
-
-
-def _check(got, ref, what):
+def _check(got, ref, what, slack=True):
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     rms = np.sqrt(np.mean(ref * ref, axis=1, keepdims=True))
-    excess = np.maximum(np.abs(got - ref) - 2.0 ** -8 * np.abs(ref), 0.0)
+    sl = 2.0 ** -8 * np.abs(ref) if slack else 0.0
+    excess = np.maximum(np.abs(got - ref) - sl, 0.0)
     e = float((excess / rms).max())
     print_case(what, f"sampled row excess {e:.2e}")
     assert e <= TAU, f"{what}: {e:.3e}"
@@ -53,6 +51,7 @@ def c5():
     x_perm = orc.gather_rows(inp["x"], p["row_src"], wl.k)
     s = w.reshape(-1)[p["row_src"]].astype(np.float32)
     h = synth.make_handoffs(wl, R)
+    h["gu32"] = synth.bf16_to_f32(h["gu"])
     dy = synth.make_dy(wl, R)
     print_case("c5 upload, R", R, "counts", p["counts"].tolist())
     d = {k: to_dev(inp[k]) for k in ("w_gate", "w_up", "w_down")}
@@ -66,8 +65,16 @@ def c5():
                 ex=(np.searchsorted(off, rows, side="right") - 1))
 
 
-def _f64(bits):
-    return orc.to_f64(np.ascontiguousarray(bits))
+def _f64(v):
+    return orc.to_f64(np.ascontiguousarray(v))
+
+
+def _T(v):
+    return np.ascontiguousarray(_f64(v).T)
+
+
+def _sel(rows):
+    return torch.from_numpy(rows).cuda()
 
 
 @pytest.mark.timeout(600)
@@ -79,20 +86,17 @@ def test_c5_forward_gate_up_sampled(c5):
     moe.debug_sync()
     rows, ex = c5["rows"], c5["ex"]
     cols = np.sort(c5["rng"].choice(I, NC, replace=False))
-    qx = _q(_f64(c5["x_perm"][rows]))
+    x = _f64(c5["x_perm"][rows])
     g_ref = np.empty((NR, NC)); u_ref = np.empty((NR, NC))
     for e in np.unique(ex):
         sel = ex == e
-        qg = _q(_f64(c5["inp"]["w_gate"][e][cols]))
-        qu = _q(_f64(c5["inp"]["w_up"][e][cols]))
-        g_ref[sel] = qx[sel] @ qg.T
-        u_ref[sel] = qx[sel] @ qu.T
-    s = c5["s"][rows].astype(np.float64)[:, None]
-    a_ref = s * (g_ref / (1.0 + np.exp(-g_ref))) * u_ref
-    gu_h = to_f64(gu[torch.from_numpy(rows).cuda()])
-    _check(gu_h[:, cols], g_ref, "c5 g")
-    _check(gu_h[:, I + cols], u_ref, "c5 u")
-    _check(to_f64(a[torch.from_numpy(rows).cuda()])[:, cols], a_ref, "c5 a")
+        g_ref[sel] = orc.mx_gemm_nt(x[sel], _f64(c5["inp"]["w_gate"][e][cols]))
+        u_ref[sel] = orc.mx_gemm_nt(x[sel], _f64(c5["inp"]["w_up"][e][cols]))
+    a_ref = orc.swiglu(g_ref, u_ref, c5["s"][rows].astype(np.float64))
+    gu_h = to_f64(gu[_sel(rows)])
+    _check(gu_h[:, cols], g_ref, "c5 g", slack=False)
+    _check(gu_h[:, I + cols], u_ref, "c5 u", slack=False)
+    _check(to_f64(a[_sel(rows)])[:, cols], a_ref, "c5 a")
 
 
 @pytest.mark.timeout(600)
@@ -103,60 +107,55 @@ def test_c5_down_projection_sampled(c5):
     moe.debug_sync()
     rows, ex = c5["rows"], c5["ex"]
     cols = np.sort(c5["rng"].choice(H, NC, replace=False))
-    qa = _q(_f64(c5["h"]["a"][rows]))
+    av = _f64(c5["h"]["a"][rows])
     y_ref = np.empty((NR, NC))
     for e in np.unique(ex):
         sel = ex == e
-        y_ref[sel] = qa[sel] @ _q(_f64(c5["inp"]["w_down"][e][cols])).T
-    _check(to_f64(y[torch.from_numpy(rows).cuda()])[:, cols], y_ref, "c5 y")
-
-
-def _wgrad_ref(A, B, off, e, ra, cb):
-    """sum over expert e's rows r of MX_R(A[:, ra])[r] * MX_R(B[:, cb])[r],
-    blocks of 32 rows from the segment start (tail zero-padded)."""
-    seg = slice(int(off[e]), int(off[e + 1]))
-    qa = _q(_f64(A[seg][:, ra]).T)      # [len(ra), n_e]
-    qb = _q(_f64(B[seg][:, cb]).T)      # [len(cb), n_e]
-    return qa @ qb.T
+        y_ref[sel] = orc.mx_gemm_nt(av[sel], _f64(c5["inp"]["w_down"][e][cols]))
+    _check(to_f64(y[_sel(rows)])[:, cols], y_ref, "c5 y")
 
 
 @pytest.mark.timeout(600)
 def test_c5_backward_down_sampled(c5):
     wl, H, I = c5["wl"], c5["wl"].H, c5["wl"].I
-    out = moe.mxfp8_mlp_bwd_down(to_dev(c5["dy"]), to_dev(c5["h"]["a"]),
-                                 to_dev(c5["h"]["gu"]), c5["offs"],
+    gu32 = c5["h"]["gu32"]
+    out = moe.mxfp8_mlp_bwd_down(to_dev(c5["dy"]), to_dev(gu32), c5["offs"],
                                  to_dev(c5["s"]), c5["mw"])
     moe.debug_sync()
     rows, ex = c5["rows"], c5["ex"]
     cols = np.sort(c5["rng"].choice(I, NC, replace=False))
-    qdy = _q(_f64(c5["dy"][rows]))
+    dyr = _f64(c5["dy"][rows])
     da = np.empty((NR, NC))
     for e in np.unique(ex):
         sel = ex == e
-        wd_cols = np.ascontiguousarray(c5["inp"]["w_down"][e][:, cols].T)   # [NC, H]
-        da[sel] = qdy[sel] @ _q(_f64(wd_cols)).T
-    g = _f64(c5["h"]["gu"][rows][:, cols]); u = _f64(c5["h"]["gu"][rows][:, I + cols])
+        # W_d[e] is [H, I]: the sampled columns i, blocked along H
+        da[sel] = orc.mx_gemm_nt(dyr[sel], _T(c5["inp"]["w_down"][e][:, cols]))
+    g = _f64(gu32[rows][:, cols]); u = _f64(gu32[rows][:, I + cols])
     s = c5["s"][rows].astype(np.float64)
     dg_ref, du_ref, _ = orc.swiglu_bwd(da, g, u, s)
-    dgu = to_f64(out["dgu"][torch.from_numpy(rows).cuda()])
+    dgu = to_f64(out["dgu"][_sel(rows)])
     _check(dgu[:, cols], dg_ref, "c5 dg")
     _check(dgu[:, I + cols], du_ref, "c5 du")
     # ds over all I for 4 rows of expert 0 (needs all of W_down[0] along H)
     r4 = rows[ex == 0][:4]
-    qwd = _q(_f64(np.ascontiguousarray(c5["inp"]["w_down"][0].T)))      # [I, H]
-    da_full = _q(_f64(c5["dy"][r4])) @ qwd.T
-    _, _, ds_ref = orc.swiglu_bwd(da_full, _f64(c5["h"]["gu"][r4][:, :I]),
-                                  _f64(c5["h"]["gu"][r4][:, I:]), c5["s"][r4].astype(np.float64))
-    ds = out["ds"][torch.from_numpy(r4).cuda()].cpu().numpy().astype(np.float64)
+    da_full = orc.mx_gemm_nt(_f64(c5["dy"][r4]), _T(c5["inp"]["w_down"][0]))
+    _, _, ds_ref = orc.swiglu_bwd(da_full, _f64(gu32[r4][:, :I]), _f64(gu32[r4][:, I:]),
+                                  c5["s"][r4].astype(np.float64))
+    ds = out["ds"][_sel(r4)].cpu().numpy().astype(np.float64)
     e_ds = float(np.max(np.abs(ds - ds_ref)) / np.sqrt(np.mean(ds_ref ** 2)))
     print_case("c5 ds", f"max err / RMS {e_ds:.2e}")
     assert e_ds <= TAU
-    # dW_down[e][h, i] for two experts
+    # dW_down[e][h, i] = Q_R(dY_e)^T Q_R(a_e), a = s SiLU(g) u from the fp32
+    # g, u, for two experts
     off = c5["p"]["offsets"]
     for e in (0, wl.n_local - 1):
         hr = np.sort(c5["rng"].choice(H, NR, replace=False))
         ic = np.sort(c5["rng"].choice(I, NC, replace=False))
-        ref = _wgrad_ref(c5["dy"], c5["h"]["a"], off, e, hr, ic)
+        seg = slice(int(off[e]), int(off[e + 1]))
+        a_seg = orc.swiglu(_f64(gu32[seg][:, ic]), _f64(gu32[seg][:, I + ic]),
+                           c5["s"][seg].astype(np.float64))
+        segoff = np.array([0, seg.stop - seg.start])
+        ref = orc.mxfp8_wgrad(_f64(c5["dy"][seg][:, hr]), a_seg, segoff)[0]
         got = to_f64(out["dw_down"][e])[np.ix_(hr, ic)]
         _check(got, ref, f"c5 dw_down[{e}]")
 
@@ -169,22 +168,25 @@ def test_c5_backward_gate_up_sampled(c5):
     moe.debug_sync()
     rows, ex = c5["rows"], c5["ex"]
     cols = np.sort(c5["rng"].choice(H, NC, replace=False))
-    qdg = _q(_f64(c5["h"]["dgu"][rows][:, :I]))
-    qdu = _q(_f64(c5["h"]["dgu"][rows][:, I:]))
+    dg = _f64(c5["h"]["dgu"][rows][:, :I])
+    du = _f64(c5["h"]["dgu"][rows][:, I:])
     dx_ref = np.empty((NR, NC))
     for e in np.unique(ex):
         sel = ex == e
-        wg_cols = np.ascontiguousarray(c5["inp"]["w_gate"][e][:, cols].T)   # [NC, I]
-        wu_cols = np.ascontiguousarray(c5["inp"]["w_up"][e][:, cols].T)
-        dx_ref[sel] = qdg[sel] @ _q(_f64(wg_cols)).T + qdu[sel] @ _q(_f64(wu_cols)).T
-    _check(to_f64(out["dx"][torch.from_numpy(rows).cuda()])[:, cols], dx_ref, "c5 dx")
+        # W_g[e], W_u[e] are [I, H]: the sampled columns h, blocked along I
+        dx_ref[sel] = (orc.mx_gemm_nt(dg[sel], _T(c5["inp"]["w_gate"][e][:, cols]))
+                       + orc.mx_gemm_nt(du[sel], _T(c5["inp"]["w_up"][e][:, cols])))
+    _check(to_f64(out["dx"][_sel(rows)])[:, cols], dx_ref, "c5 dx")
     off = c5["p"]["offsets"]
-    dg_all = c5["h"]["dgu"][:, :I]
-    du_all = c5["h"]["dgu"][:, I:]
     for e in (0, wl.n_local - 1):
         ir = np.sort(c5["rng"].choice(I, NR, replace=False))
         hc = np.sort(c5["rng"].choice(H, NC, replace=False))
+        seg = slice(int(off[e]), int(off[e + 1]))
+        segoff = np.array([0, seg.stop - seg.start])
+        xs = _f64(c5["x_perm"][seg][:, hc])
+        dgs = _f64(c5["h"]["dgu"][seg][:, ir])
+        dus = _f64(c5["h"]["dgu"][seg][:, I + ir])
         _check(to_f64(out["dw_gate"][e])[np.ix_(ir, hc)],
-               _wgrad_ref(dg_all, c5["x_perm"], off, e, ir, hc), f"c5 dw_gate[{e}]")
+               orc.mxfp8_wgrad(dgs, xs, segoff)[0], f"c5 dw_gate[{e}]")
         _check(to_f64(out["dw_up"][e])[np.ix_(ir, hc)],
-               _wgrad_ref(du_all, c5["x_perm"], off, e, ir, hc), f"c5 dw_up[{e}]")
+               orc.mxfp8_wgrad(dus, xs, segoff)[0], f"c5 dw_up[{e}]")

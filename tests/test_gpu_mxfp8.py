@@ -1,17 +1,27 @@
 """MXFP8 path through the C ABI against the CPU oracle.
 
 Codes and scales of given bf16 inputs must match bit for bit.  Float
-outputs must meet max(|err| - bf16 slack) <= 6e-2 * RMS of each row of the
-reference (the oracle dequantises exactly and works in fp64).
+outputs must meet max(|err| - storage slack) <= 6e-2 * RMS of each row of
+the reference (the oracle dequantises exactly and works in fp64; the slack
+is one bf16 ulp of the element for bf16 outputs, none for fp32 ones).
 
-Tensors handed from one operation to the next are bf16 and are quantised
-again by the next GEMM.  When such a tensor is computed on both sides (fp32
-on the device, fp64 in the oracle), a value near an E4M3 rounding boundary
-can be quantised to neighbouring codes on the two sides; each code choice is
-correct for its input.  So every GEMM stage is checked on the oracle's own
-bf16 hand-off tensors, where both sides quantise identical values, and the
-fused calls are checked end to end on what no such decision feeds (g, u, a,
-ds) plus an aggregate bound on the rest.
+The fused forward and backward are checked end to end against the plain
+oracle step, in which every tensor of the chain (a, g, u, dg, du) is
+quantised from its unrounded value (fp32 on the device, fp64 in the
+oracle).  Such a quantisation is floating point deciding an integer on
+values the two sides compute differently, so (mx_check):
+  - the computed values are compared element by element: g, u, a, ds (and,
+    through the stage call, dg, du);
+  - every MX code and scale the device chose (read from the workspace
+    through moe_mxfp8_workspace_view) must be the rule's rounding of a
+    value within TAU_DEC * RMS(row) of the oracle's;
+  - every output of a GEMM that consumes those codes (y, dX, dW_gate,
+    dW_up, dW_down) is compared element by element with the oracle's exact
+    product of the device's codes and the oracle's own quantisation of the
+    other operand.
+The unfused stage calls are checked against the oracle's stage functions on
+the same given inputs; the backward stages hand [dg | du] on in bf16, which
+the oracle's labelled bf16_dgu variant models.
 """
 import numpy as np
 import pytest
@@ -21,9 +31,11 @@ import mixture_experts_expert_router_amd as moe
 import moe_synth as synth
 import oracle as orc
 from gpu_util import print_case, rel_err, scaled_excess, to_dev, to_f64
+from mx_check import check_block_decisions, dequantize, segment_columns
 
 pytestmark = pytest.mark.gpu
 TAU = 6e-2
+TAU_DEC = 1e-3     # admissible distance of a decided value, * RMS(row)
 
 
 def bf16_bits(a):
@@ -153,23 +165,20 @@ def _mx_case(name):
 
 
 def _bits(v):
-    """bf16 bits of values the oracle already rounded to bf16 (exact)."""
+    """bf16 bits of the nearest bf16 values of v."""
     v = orc.round_bf16(v)
     return (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
 
 
-def _check(got, ref, what, bad):
-    e = scaled_excess(got, ref, "bf16")
+def _check(got, ref, what, bad, dtype="bf16"):
+    e = scaled_excess(got, ref, dtype)
     print_case(what, f"row excess {e:.2e}, plain {rel_err(got, ref):.2e}")
     if not e <= TAU:
         bad.append(f"{what}: {e:.3e}")
 
 
-def _frob(got, ref, what, bad, bound=2e-2):
-    r = float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
-    print_case(what, f"relative Frobenius error {r:.2e}")
-    if not r <= bound:
-        bad.append(f"{what}: frobenius {r:.3e}")
+def _ds(t, R):
+    return t[:R].cpu().numpy().astype(np.float64)
 
 
 @pytest.fixture(scope="module", params=["small_mxfp8", "mid_mxfp8"])
@@ -179,203 +188,276 @@ def case(request):
     wl, inp, p, x_perm, s, dy, ref = _mx_case(name)
     d = {k: to_dev(inp[k]) for k in ("w_gate", "w_up", "w_down")}
     mw = moe.MxWeights(d["w_gate"], d["w_up"], d["w_down"])
-    return dict(name=name, wl=wl, p=p, x_perm=x_perm, s=s, dy=dy, ref=ref,
-                mw=mw, offs=to_dev(p["offsets"]), st=to_dev(s))
+    return dict(name=name, wl=wl, inp=inp, p=p, x_perm=x_perm, s=s, dy=dy,
+                ref=ref, mw=mw, offs=to_dev(p["offsets"]), st=to_dev(s))
+
+
+def _ws(n, dev="cuda"):
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
+
+
+def _run_fused(c, x_perm=None, offs=None, st=None, mw=None, dy=None):
+    """Fused forward (one call) and fused backward, keeping the workspaces."""
+    xt = to_dev(c["x_perm"] if x_perm is None else x_perm)
+    xq, xs = moe.mxfp8_quantize(xt, 0)
+    offs = c["offs"] if offs is None else offs
+    st = c["st"] if st is None else st
+    mw = c["mw"] if mw is None else mw
+    R_cap, H = xt.shape
+    L = moe.lib()
+    ws_f = _ws(L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes(R_cap, mw.n_local, H, mw.I))
+    ws_b = _ws(L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes(R_cap, mw.n_local, H, mw.I))
+    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, offs, st, mw, workspace=ws_f)
+    g = moe.mxfp8_mlp_bwd(to_dev(c["dy"] if dy is None else dy), xt, gu, offs,
+                          st, mw, workspace=ws_b)
+    return dict(xt=xt, a=a, gu=gu, y=y, g=g, ws_f=ws_f, ws_b=ws_b, R_cap=R_cap)
+
+
+def _rows_delta(v):
+    rms = np.sqrt(np.mean(np.asarray(v, np.float64) ** 2, axis=1, keepdims=True))
+    return np.broadcast_to(TAU_DEC * rms, np.shape(v))
+
+
+def _decisions(what, v, delta, codes, scales, bad):
+    bs, bc, differ = check_block_decisions(v, delta, codes, scales)
+    print_case(what, f"codes differing from the oracle's {differ} of {np.size(v)}, "
+               f"inadmissible scales {bs}, codes {bc}")
+    if bs or bc:
+        bad.append(f"{what}: {bs} scales, {bc} codes inadmissible")
+
+
+def _verify_fused(c, run, ref, offsets, wl, tag, bad, experts=None):
+    """The checks of the module docstring on one fused forward + backward."""
+    R, H, I, n = int(offsets[-1]), wl.H, wl.I, wl.n_local
+    inp = c["inp"]
+    a, gu, y, g = run["a"], run["gu"], run["y"], run["g"]
+    experts = range(n) if experts is None else experts
+    live = [e for e in range(n) if offsets[e + 1] > offsets[e]]
+    # computed values
+    _check(to_f64(gu[:R, :I]), ref["g"], f"{tag} g", bad, "f32")
+    _check(to_f64(gu[:R, I:]), ref["u"], f"{tag} u", bad, "f32")
+    _check(to_f64(a[:R]), ref["a"], f"{tag} a", bad)
+    _check(_ds(g["ds"], R), ref["ds"], f"{tag} ds", bad, "f32")
+    # forward: MX(a) decisions, then y from the device's codes
+    aq, as_, _ = moe.mxfp8_workspace_view(run["ws_f"], moe.MXCALL_FWD, moe.MXT_A_ROWS,
+                                          run["R_cap"], n, H, I)
+    aq, as_ = aq[:R].cpu().numpy(), as_[:R].cpu().numpy()
+    _decisions(f"{tag} MX(a)", ref["a"], _rows_delta(ref["a"]), aq, as_, bad)
+    a_dev = dequantize(aq, as_)
+    y_ref = np.zeros((R, H))
+    for e in live:
+        sl = slice(int(offsets[e]), int(offsets[e + 1]))
+        y_ref[sl] = orc.matmul_nt(a_dev[sl], orc.mx_roundtrip_rows(orc.to_f64(inp["w_down"][e])))
+    _check(to_f64(y[:R]), y_ref, f"{tag} y (device codes)", bad)
+    print_case(f"{tag} y against the plain oracle",
+               f"row excess {scaled_excess(to_f64(y[:R]), ref['y'], 'bf16'):.2e}")
+    # backward: [dg | du] row-wise decisions, then dX from the device's codes
+    view = lambda t: moe.mxfp8_workspace_view(run["ws_b"], moe.MXCALL_BWD, t,
+                                              run["R_cap"], n, H, I)
+    dgu = np.concatenate([ref["dg"], ref["du"]], axis=1)
+    q, qs, _ = view(moe.MXT_DGU_ROWS)
+    q, qs = q[:R].cpu().numpy(), qs[:R].cpu().numpy()
+    _decisions(f"{tag} MX([dg | du]) rows", dgu, _rows_delta(dgu), q, qs, bad)
+    d_dev = dequantize(q, qs)
+    dx_ref = np.zeros((R, H))
+    for e in live:
+        sl = slice(int(offsets[e]), int(offsets[e + 1]))
+        wg = orc.mx_roundtrip_rows(np.ascontiguousarray(orc.to_f64(inp["w_gate"][e]).T))
+        wu = orc.mx_roundtrip_rows(np.ascontiguousarray(orc.to_f64(inp["w_up"][e]).T))
+        dx_ref[sl] = orc.matmul_nt(d_dev[sl, :I], wg) + orc.matmul_nt(d_dev[sl, I:], wu)
+    _check(to_f64(g["dx"][:R]), dx_ref, f"{tag} dx (device codes)", bad)
+    # column-wise decisions of dg, du, then dW_gate, dW_up from them
+    xf = orc.to_f64(c["x_perm"][:R])
+    for key, t, vref in (("dw_gate", moe.MXT_DG_COLS, ref["dg"]),
+                         ("dw_up", moe.MXT_DU_COLS, ref["du"])):
+        cq, cs, pad = view(t)
+        cq, cs, pad = cq.cpu().numpy(), cs.cpu().numpy(), pad.cpu().numpy()
+        W = int(pad[-1])
+        vt = segment_columns(vref, offsets, pad, W)
+        dt = segment_columns(_rows_delta(vref), offsets, pad, W)
+        _decisions(f"{tag} MX({key[3:]}) columns", vt, dt, cq[:, :W], cs, bad)
+        c_dev = dequantize(cq[:, :W], cs)
+        for e in experts:
+            r0, r1 = int(offsets[e]), int(offsets[e + 1])
+            if r1 == r0:
+                continue
+            qx = orc.mx_roundtrip_rows(np.ascontiguousarray(xf[r0:r1].T))   # [H, n_e]
+            wref = orc.matmul_nt(c_dev[:, pad[e]:pad[e] + (r1 - r0)], qx)
+            _check(to_f64(g[key][e]), wref, f"{tag} {key}[{e}] (device codes)", bad)
+
+
+def test_mxfp8_fused_forward_backward(case):
+    """Every output of the fused forward and backward against the plain
+    oracle step, by the rule of the module docstring; dW_down through the
+    stage call, whose bits the fused call's equal."""
+    c, ref, R, I = case, case["ref"], case["p"]["R"], case["wl"].I
+    run = _run_fused(c)
+    moe.debug_sync()
+    bad = []
+    _verify_fused(c, run, ref, c["p"]["offsets"], c["wl"], c["name"], bad)
+    _verify_dw_down(c, run, ref, c["p"]["offsets"], c["wl"], c["name"], bad)
+    assert not bad, bad
+
+
+def _verify_dw_down(c, run, ref, offsets, wl, tag, bad, experts=None):
+    """dW_down: the stage call (same epilogue and codes as the fused call,
+    which it must equal bit for bit) leaves the column-wise MX(a) in its
+    workspace; check those decisions against the oracle's a, then dW_down
+    against the exact product of the oracle's MX(dY) and the device's MX(a)."""
+    R, H, I, n = int(offsets[-1]), wl.H, wl.I, wl.n_local
+    R_cap = run["R_cap"]
+    ws = _ws(moe.lib().moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(R_cap, n, H, I))
+    d1 = moe.mxfp8_mlp_bwd_down(to_dev(c["dy"]), run["gu"], c["offs"], c["st"],
+                                c["mw"], workspace=ws)
+    moe.debug_sync()
+    assert torch.equal(d1["dw_down"], run["g"]["dw_down"]), f"{tag} stage dw_down"
+    assert torch.equal(d1["ds"][:R], run["g"]["ds"][:R]), f"{tag} stage ds"
+    cq, cs, pad = moe.mxfp8_workspace_view(ws, moe.MXCALL_BWD_DOWN, moe.MXT_A_COLS,
+                                           R_cap, n, H, I)
+    cq, cs, pad = cq.cpu().numpy(), cs.cpu().numpy(), pad.cpu().numpy()
+    W = int(pad[-1])
+    _decisions(f"{tag} MX(a) columns", segment_columns(ref["a"], offsets, pad, W),
+               segment_columns(_rows_delta(ref["a"]), offsets, pad, W), cq[:, :W], cs, bad)
+    a_dev = dequantize(cq[:, :W], cs)
+    dyf = orc.to_f64(c["dy"][:R])
+    for e in (range(n) if experts is None else experts):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        qdy = orc.mx_roundtrip_rows(np.ascontiguousarray(dyf[r0:r1].T))      # [H, n_e]
+        wref = orc.matmul_nt(qdy, a_dev[:, pad[e]:pad[e] + (r1 - r0)])
+        _check(to_f64(d1["dw_down"][e]), wref, f"{tag} dw_down[{e}] (device codes)", bad)
 
 
 def test_mxfp8_down_projection_stage(case):
-    """y = MX(a) MX(W_d)^T on the oracle's bf16 a."""
+    """moe_grouped_linear_mxfp8 on a given bf16 a: y = Q_I(a) Q_I(W_d)^T."""
     c, ref, R = case, case["ref"], case["p"]["R"]
-    y = moe.grouped_linear_mxfp8(to_dev(_bits(ref["a"])), c["offs"],
-                                 c["wl"].n_local, c["mw"].wd, c["mw"].wds)
+    ab = _bits(ref["a"])
+    y = moe.grouped_linear_mxfp8(to_dev(ab), c["offs"], c["wl"].n_local,
+                                 c["mw"].wd, c["mw"].wds)
     moe.debug_sync()
+    off = c["p"]["offsets"]
+    y_ref = np.zeros((R, c["wl"].H))
+    for e in range(c["wl"].n_local):
+        sl = slice(int(off[e]), int(off[e + 1]))
+        if sl.stop > sl.start:
+            y_ref[sl] = orc.mx_gemm_nt(orc.to_f64(ab[sl]),
+                                       orc.to_f64(c["inp"]["w_down"][e]))
     bad = []
-    _check(to_f64(y[:R]), ref["y"], f"{c['name']} stage y", bad)
+    _check(to_f64(y[:R]), y_ref, f"{c['name']} stage y", bad)
     assert not bad, bad
 
 
 def test_mxfp8_backward_down_stage(case):
-    """da -> SwiGLU backward -> dg, du, ds, and dW_down, on the oracle's
-    bf16 a, g, u."""
+    """moe_grouped_mlp_mxfp8_bwd_down on given fp32 g, u (the oracle's,
+    rounded to fp32) against the oracle's down/SwiGLU backward on the same
+    values: dg, du (bf16 outputs), ds, dW_down."""
     c, ref, R, I = case, case["ref"], case["p"]["R"], case["wl"].I
-    gu = np.concatenate([_bits(ref["g"]), _bits(ref["u"])], axis=1)
-    out = moe.mxfp8_mlp_bwd_down(to_dev(c["dy"]), to_dev(_bits(ref["a"])),
-                                 to_dev(gu), c["offs"], c["st"], c["mw"])
+    g32 = ref["g"].astype(np.float32)
+    u32 = ref["u"].astype(np.float32)
+    gu = np.ascontiguousarray(np.concatenate([g32, u32], axis=1))
+    out = moe.mxfp8_mlp_bwd_down(to_dev(c["dy"]), to_dev(gu), c["offs"],
+                                 c["st"], c["mw"])
     moe.debug_sync()
+    sref = orc.mxfp8_backward_down(c["dy"], g32, u32, c["s"].astype(np.float64),
+                                   c["p"]["offsets"], c["inp"]["w_down"])
     bad = []
     n = c["name"]
-    _check(to_f64(out["dgu"][:R, :I]), ref["dg"], f"{n} stage dg", bad)
-    _check(to_f64(out["dgu"][:R, I:]), ref["du"], f"{n} stage du", bad)
-    _check(out["ds"][:R].cpu().numpy().astype(np.float64), ref["ds"],
-           f"{n} stage ds", bad)
+    _check(to_f64(out["dgu"][:R, :I]), sref["dg"], f"{n} stage dg", bad)
+    _check(to_f64(out["dgu"][:R, I:]), sref["du"], f"{n} stage du", bad)
+    _check(_ds(out["ds"], R), sref["ds"], f"{n} stage ds", bad, "f32")
     for e in range(c["wl"].n_local):
-        _check(to_f64(out["dw_down"][e]), ref["dw_down"][e],
+        _check(to_f64(out["dw_down"][e]), sref["dw_down"][e],
                f"{n} stage dw_down[{e}]", bad)
     assert not bad, bad
 
 
 def test_mxfp8_backward_gate_up_stage(case):
-    """dX, dW_gate, dW_up on the oracle's bf16 dg, du."""
-    c, ref, R = case, case["ref"], case["p"]["R"]
-    dgu = np.concatenate([_bits(ref["dg"]), _bits(ref["du"])], axis=1)
+    """moe_grouped_mlp_mxfp8_bwd_gate_up on a given bf16 [dg | du] (the
+    oracle's dg, du rounded) against the oracle step's bf16_dgu variant,
+    which quantises the same bf16 values."""
+    c, ref, R, I = case, case["ref"], case["p"]["R"], case["wl"].I
+    dg_b, du_b = _bits(ref["dg"]), _bits(ref["du"])
+    dgu = np.concatenate([dg_b, du_b], axis=1)
     out = moe.mxfp8_mlp_bwd_gate_up(to_dev(dgu), to_dev(c["x_perm"]),
                                     c["offs"], c["mw"])
     moe.debug_sync()
+    # the oracle step's labelled variant for this API: [dg | du] rounded
+    # to bf16 before the gate/up backward quantises it
+    sref = orc.mxfp8_mlp_step(c["x_perm"], c["p"]["offsets"],
+                              c["s"].astype(np.float64), c["inp"]["w_gate"],
+                              c["inp"]["w_up"], c["inp"]["w_down"], c["dy"],
+                              bf16_dgu=True)
     bad = []
     n = c["name"]
-    _check(to_f64(out["dx"][:R]), ref["dx"], f"{n} stage dx", bad)
+    _check(to_f64(out["dx"][:R]), sref["dx"], f"{n} stage dx", bad)
     for key in ("dw_gate", "dw_up"):
         for e in range(c["wl"].n_local):
-            _check(to_f64(out[key][e]), ref[key][e], f"{n} stage {key}[{e}]", bad)
+            _check(to_f64(out[key][e]), sref[key][e], f"{n} stage {key}[{e}]", bad)
     assert not bad, bad
 
 
-def test_mxfp8_fused_quantisation_equals_separate(case):
-    """The SwiGLU epilogue quantises a (forward) and [dg | du] (backward) from
-    the bf16 values it stores; the fused calls must therefore equal the
-    stage calls, which quantise the stored bf16 tensors with the row
-    quantiser (pinned to the oracle bit for bit, every bf16 value at every
-    scale), bit for bit: y against the grouped linear on the returned a and
-    against the two-call forward (gate/up, then the down projection from the
-    workspace codes), and dX, dW against the two backward stages."""
+def test_mxfp8_fused_and_stage_calls_agree(case):
+    """Structural identities: the two-call forward (gate/up, then the down
+    projection from the workspace codes) equals the one-call forward bit for
+    bit, and the fused backward's ds and dW_down equal the stage call's
+    (the same epilogue and the same codes)."""
     c, R = case, case["p"]["R"]
     wl = c["wl"]
-    xt = to_dev(c["x_perm"])
+    run = _run_fused(c)
+    xt, R_cap = run["xt"], run["R_cap"]
     xq, xs = moe.mxfp8_quantize(xt, 0)
-    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, c["offs"], c["st"], c["mw"])
-    y_sep = moe.grouped_linear_mxfp8(a, c["offs"], wl.n_local, c["mw"].wd, c["mw"].wds)
-    R_cap = xq.shape[0]
-    nb = moe.lib().moe_grouped_mlp_mxfp8_fwd_workspace_bytes(R_cap, wl.n_local, wl.H, wl.I)
-    ws = torch.empty(nb, dtype=torch.uint8, device=xq.device)
+    ws = _ws(moe.lib().moe_grouped_mlp_mxfp8_fwd_workspace_bytes(R_cap, wl.n_local, wl.H, wl.I))
     moe.mxfp8_mlp_fwd(xq, xs, c["offs"], c["st"], c["mw"], workspace=ws, down=False)
     y_two = moe.mxfp8_mlp_fwd_down(c["offs"], c["mw"], ws, R_cap)
-    dy = to_dev(c["dy"])
-    g = moe.mxfp8_mlp_bwd(dy, xt, a, gu, c["offs"], c["st"], c["mw"])
-    d1 = moe.mxfp8_mlp_bwd_down(dy, a, gu, c["offs"], c["st"], c["mw"])
-    d2 = moe.mxfp8_mlp_bwd_gate_up(d1["dgu"], xt, c["offs"], c["mw"])
+    d1 = moe.mxfp8_mlp_bwd_down(to_dev(c["dy"]), run["gu"], c["offs"], c["st"], c["mw"])
     moe.debug_sync()
     print_case(c["name"], "fused vs stage calls, rows", R)
-    assert torch.equal(y[:R], y_sep[:R])
-    assert torch.equal(y[:R], y_two[:R])
-    assert torch.equal(g["ds"][:R], d1["ds"][:R])
-    assert torch.equal(g["dw_down"], d1["dw_down"])
-    assert torch.equal(g["dx"][:R], d2["dx"][:R])
-    assert torch.equal(g["dw_gate"], d2["dw_gate"])
-    assert torch.equal(g["dw_up"], d2["dw_up"])
+    assert torch.equal(run["y"][:R], y_two[:R])
+    assert torch.equal(run["g"]["ds"][:R], d1["ds"][:R])
+    assert torch.equal(run["g"]["dw_down"], d1["dw_down"])
 
 
-def test_mxfp8_fused_forward_backward(case):
-    c, ref, R, I = case, case["ref"], case["p"]["R"], case["wl"].I
-    xt = to_dev(c["x_perm"])
-    xq, xs = moe.mxfp8_quantize(xt, 0)
-    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, c["offs"], c["st"], c["mw"])
-    g = moe.mxfp8_mlp_bwd(to_dev(c["dy"]), xt, a, gu, c["offs"], c["st"],
-                          c["mw"])
-    moe.debug_sync()
-    bad = []
-    n = c["name"]
-    _check(to_f64(gu[:R, :I]), ref["g"], f"{n} g", bad)
-    _check(to_f64(gu[:R, I:]), ref["u"], f"{n} u", bad)
-    _check(to_f64(a[:R]), ref["a"], f"{n} a", bad)
-    _check(g["ds"][:R].cpu().numpy().astype(np.float64), ref["ds"], f"{n} ds", bad)
-    _frob(to_f64(y[:R]), ref["y"], f"{n} y", bad)
-    _frob(to_f64(g["dx"][:R]), ref["dx"], f"{n} dx", bad)
-    for key in ("dw_gate", "dw_up", "dw_down"):
-        _frob(to_f64(g[key]), ref[key], f"{n} {key}", bad)
-    assert not bad, bad
-
-
-def test_mxfp8_experts_without_rows():
-    """Experts 0 and 2 of four receive no rows: their weight-gradient GEMMs
-    run over empty K ranges and must return exact zeros, and the fused calls
-    must still equal the stage calls bit for bit."""
+def _seg_case(counts, seed):
     wl = synth.WORKLOADS["small_mxfp8"]
-    R = 300
-    inp = synth.make_inputs(wl, tokens=R)
-    offsets = np.array([0, 0, 127, 127, R], np.int32)
-    x_perm = inp["x"]
-    s = np.random.default_rng(11).uniform(0.05, 1.0, R).astype(np.float32)
-    dy = synth.make_dy(wl, R)
-    ref = orc.mxfp8_mlp_step(x_perm, offsets, s.astype(np.float64),
-                             inp["w_gate"], inp["w_up"], inp["w_down"], dy)
-    d = {k: to_dev(inp[k]) for k in ("w_gate", "w_up", "w_down")}
-    mw = moe.MxWeights(d["w_gate"], d["w_up"], d["w_down"])
-    offs, st, xt, dyt = to_dev(offsets), to_dev(s), to_dev(x_perm), to_dev(dy)
-    print_case("small_mxfp8 experts 0, 2 empty", "rows", R)
-    xq, xs = moe.mxfp8_quantize(xt, 0)
-    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, offs, st, mw)
-    g = moe.mxfp8_mlp_bwd(dyt, xt, a, gu, offs, st, mw)
-    d1 = moe.mxfp8_mlp_bwd_down(dyt, a, gu, offs, st, mw)
-    d2 = moe.mxfp8_mlp_bwd_gate_up(d1["dgu"], xt, offs, mw)
-    moe.debug_sync()
-    for key in ("dw_gate", "dw_up", "dw_down"):
-        for e in (0, 2):
-            assert not g[key][e].any(), (key, e)
-    assert torch.equal(g["dw_down"], d1["dw_down"])
-    assert torch.equal(g["dx"][:R], d2["dx"][:R])
-    assert torch.equal(g["dw_gate"], d2["dw_gate"])
-    assert torch.equal(g["dw_up"], d2["dw_up"])
-    bad = []
-    _check(to_f64(a[:R]), ref["a"], "empty-expert a", bad)
-    _check(g["ds"][:R].cpu().numpy().astype(np.float64), ref["ds"],
-           "empty-expert ds", bad)
-    _frob(to_f64(y[:R]), ref["y"], "empty-expert y", bad)
-    _frob(to_f64(g["dx"][:R]), ref["dx"], "empty-expert dx", bad)
-    for key in ("dw_gate", "dw_up", "dw_down"):
-        for e in (1, 3):
-            _frob(to_f64(g[key][e]), ref[key][e], f"empty-expert {key}[{e}]", bad)
-    assert not bad, bad
-
-
-def test_mxfp8_tiny_ragged_segments():
-    """Segments of 3, 0, 1 and 37 rows at the smallest shapes (H = I = 512):
-    every tile is mostly padding and the weight-gradient K ranges are one
-    256-row block or empty.  The fused calls equal the stage calls bit for
-    bit; a, ds and the aggregate y, dX meet the oracle; the weight gradients
-    are checked row by row on the oracle's own bf16 hand-off tensors (with
-    one or three rows a segment's MX blocks hold single values, so a code
-    decided differently on the two sides would not average out)."""
-    wl = synth.WORKLOADS["small_mxfp8"]
-    counts = [3, 0, 1, 37]
     R = sum(counts)
     inp = synth.make_inputs(wl, tokens=R)
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     x_perm = inp["x"]
-    s = np.random.default_rng(5).uniform(0.05, 1.0, R).astype(np.float32)
+    s = np.random.default_rng(seed).uniform(0.05, 1.0, R).astype(np.float32)
     dy = synth.make_dy(wl, R)
     ref = orc.mxfp8_mlp_step(x_perm, offsets, s.astype(np.float64),
                              inp["w_gate"], inp["w_up"], inp["w_down"], dy)
     d = {k: to_dev(inp[k]) for k in ("w_gate", "w_up", "w_down")}
     mw = moe.MxWeights(d["w_gate"], d["w_up"], d["w_down"])
-    offs, st, xt, dyt = to_dev(offsets), to_dev(s), to_dev(x_perm), to_dev(dy)
+    c = dict(x_perm=x_perm, dy=dy, offs=to_dev(offsets), st=to_dev(s), mw=mw,
+             inp=inp)
+    return wl, R, ref, c
+
+
+@pytest.mark.parametrize("counts", [
+    [0, 127, 0, 173],        # experts 0 and 2 receive no rows
+    [3, 0, 1, 37],           # tiny ragged segments: tiles mostly padding
+])
+def test_mxfp8_ragged_and_empty_segments(counts):
+    """Experts without rows get exact zero weight gradients; with 1-37 rows
+    per expert a weight-gradient block holds few values, and every output
+    still meets the oracle row by row."""
+    wl, R, ref, c = _seg_case(counts, 11)
     print_case("small_mxfp8 segments", counts)
-    xq, xs = moe.mxfp8_quantize(xt, 0)
-    a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, offs, st, mw)
-    g = moe.mxfp8_mlp_bwd(dyt, xt, a, gu, offs, st, mw)
-    d1 = moe.mxfp8_mlp_bwd_down(dyt, a, gu, offs, st, mw)
-    d2 = moe.mxfp8_mlp_bwd_gate_up(d1["dgu"], xt, offs, mw)
-    # the weight gradients on the oracle's hand-off tensors
-    gu_ref = np.concatenate([_bits(ref["g"]), _bits(ref["u"])], axis=1)
-    h1 = moe.mxfp8_mlp_bwd_down(dyt, to_dev(_bits(ref["a"])), to_dev(gu_ref),
-                                offs, st, mw)
-    dgu_ref = np.concatenate([_bits(ref["dg"]), _bits(ref["du"])], axis=1)
-    h2 = moe.mxfp8_mlp_bwd_gate_up(to_dev(dgu_ref), xt, offs, mw)
+    run = _run_fused(c)
     moe.debug_sync()
+    g = run["g"]
     for key in ("dw_gate", "dw_up", "dw_down"):
-        assert not g[key][1].any(), key
-    assert torch.equal(g["dw_down"], d1["dw_down"])
-    assert torch.equal(g["dx"][:R], d2["dx"][:R])
-    assert torch.equal(g["dw_gate"], d2["dw_gate"])
-    assert torch.equal(g["dw_up"], d2["dw_up"])
+        for e, n in enumerate(counts):
+            if n == 0:
+                assert not g[key][e].any(), (key, e)
     bad = []
-    _check(to_f64(a[:R]), ref["a"], "tiny a", bad)
-    _check(g["ds"][:R].cpu().numpy().astype(np.float64), ref["ds"], "tiny ds", bad)
-    _frob(to_f64(y[:R]), ref["y"], "tiny y", bad)
-    _frob(to_f64(g["dx"][:R]), ref["dx"], "tiny dx", bad)
-    for e in (0, 2, 3):
-        _check(to_f64(h1["dw_down"][e]), ref["dw_down"][e], f"tiny dw_down[{e}]", bad)
-        _check(to_f64(h2["dw_gate"][e]), ref["dw_gate"][e], f"tiny dw_gate[{e}]", bad)
-        _check(to_f64(h2["dw_up"][e]), ref["dw_up"][e], f"tiny dw_up[{e}]", bad)
+    live = [e for e, n in enumerate(counts) if n > 0]
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    tag = f"segments {counts}"
+    _verify_fused(c, run, ref, offsets, wl, tag, bad, experts=live)
+    _verify_dw_down(c, run, ref, offsets, wl, tag, bad, experts=live)
     assert not bad, bad
 
 
@@ -394,7 +476,7 @@ def test_mxfp8_step_captured_in_a_graph_replays_bit_exactly(case):
     xq = torch.empty((R_cap, H), dtype=torch.uint8, device=dev)
     xs = torch.empty((R_cap, H // 32), dtype=torch.uint8, device=dev)
     a = torch.empty((R_cap, I), dtype=bf, device=dev)
-    gu = torch.empty((R_cap, 2 * I), dtype=bf, device=dev)
+    gu = torch.empty((R_cap, 2 * I), dtype=torch.float32, device=dev)
     y = torch.empty((R_cap, H), dtype=bf, device=dev)
     outs = dict(dx=torch.empty((R_cap, H), dtype=bf, device=dev),
                 ds=torch.empty(R_cap, dtype=torch.float32, device=dev),
@@ -411,7 +493,7 @@ def test_mxfp8_step_captured_in_a_graph_replays_bit_exactly(case):
         moe.mxfp8_quantize(xt, 0, codes=xq, scales=xs)
         moe.mxfp8_mlp_fwd(xq, xs, c["offs"], c["st"], c["mw"], a=a, gu=gu, y=y,
                           workspace=ws_f)
-        moe.mxfp8_mlp_bwd(dyt, xt, a, gu, c["offs"], c["st"], c["mw"],
+        moe.mxfp8_mlp_bwd(dyt, xt, gu, c["offs"], c["st"], c["mw"],
                           workspace=ws_b, **outs)
 
     step()

@@ -488,6 +488,210 @@ def test_mlp_step_quantized_forward_matches_unquantized_on_grid_inputs():
     np.testing.assert_array_equal(q["u"], p["u"])
 
 
+# On-grid pins of the quantised GEMMs.  A matrix "on the grid along its rows"
+# holds integers in [-14, 14] times a power of two per row, with a magnitude
+# in [8, 14] at the start of every 32-value block of the row: each block's
+# shared exponent is then X = c - 5 and every value / 2^X is an integer
+# times 32 up to 448, an exact E4M3 code, so MX quantisation along the rows
+# changes nothing.  The per-row scales span 2^-12 .. 2^12, so blocks down a
+# column mix scales and their small values fall below E4M3's range: the same
+# matrix quantised along the other axis does change.
+
+
+def _grid_rows(M, K, g, span=12):
+    ints = g.integers(-14, 15, (M, K)).astype(np.float64)
+    for b in range(0, K, 32):
+        ints[:, b] = g.choice([-1.0, 1.0], M) * g.integers(8, 15, M)
+    return ints * (2.0 ** g.integers(-span, span + 1, M))[:, None]
+
+
+def _grid_segment_rows(offs, N, g):
+    """[R, N] on the grid down each column inside every segment (blocks of 32
+    rows from the segment start), per-column scales."""
+    out = np.zeros((int(offs[-1]), N))
+    for e in range(len(offs) - 1):
+        r0, r1 = int(offs[e]), int(offs[e + 1])
+        if r1 > r0:
+            out[r0:r1] = _grid_rows(N, r1 - r0, g).T
+    return out
+
+
+def test_grid_construction_is_exact_along_rows_only():
+    g = np.random.default_rng(40)
+    A = _grid_rows(8, 96, g)
+    np.testing.assert_array_equal(orc.mx_roundtrip_rows(A), A)
+    assert not np.array_equal(orc.mx_roundtrip_cols(A), A)
+
+
+def test_mx_gemm_nt_quantises_along_k():
+    g = np.random.default_rng(41)
+    M, N, K = 40, 24, 100                      # K with a short last block
+    A, B = _grid_rows(M, K, g), _grid_rows(N, K, g)
+    exact = A @ B.T                            # integers x powers of two: exact
+    np.testing.assert_array_equal(orc.mx_gemm_nt(A, B), exact)
+    np.testing.assert_array_equal(orc.mx_gemm_nt(A, B, quantize=False), exact)
+    # on the grid along the other axis only: quantisation along K must change it
+    A2 = _grid_rows(K, M, g).T.copy()
+    assert not np.allclose(orc.mx_gemm_nt(A2, B), A2 @ B.T, rtol=1e-6, atol=0)
+
+
+def test_mxfp8_wgrad_blocks_along_segment_rows():
+    g = np.random.default_rng(42)
+    offs = np.array([0, 5, 5, 42, 112])         # ragged, one empty expert
+    A, B = _grid_segment_rows(offs, 20, g), _grid_segment_rows(offs, 12, g)
+    q = orc.mxfp8_wgrad(A, B, offs)
+    p = orc.mxfp8_wgrad(A, B, offs, quantize=False)
+    np.testing.assert_array_equal(q, p)
+    for e in range(4):
+        r0, r1 = offs[e], offs[e + 1]
+        np.testing.assert_array_equal(p[e], A[r0:r1].T @ B[r0:r1])
+    assert not p[1].any()                       # no rows: zero gradient
+    # on the grid along the columns instead: the row-blocked quantisation differs
+    A2 = _grid_rows(offs[-1], 20, g)
+    assert not np.allclose(orc.mxfp8_wgrad(A2, B, offs), orc.mxfp8_wgrad(A2, B, offs, quantize=False),
+                           rtol=1e-6, atol=0)
+
+
+def _bwd_case(g, R_offs=(0, 40, 40, 100), H=64, I=96):
+    offs = np.array(R_offs)
+    n = len(offs) - 1
+    return offs, n, H, I
+
+
+def test_mxfp8_backward_down_da_on_grid_along_h():
+    # dY on the grid along H (rows) and W_d on the grid along H (down each
+    # column of its [H, I] matrix): da and the SwiGLU gradients are unchanged
+    # by quantisation; W_d on the grid along I only would not be.
+    g = np.random.default_rng(43)
+    offs, n, H, I = _bwd_case(g)
+    R = offs[-1]
+    dy = _grid_rows(R, H, g)
+    wd = np.stack([_grid_rows(I, H, g).T for _ in range(n)])   # [n, H, I]
+    gg = g.standard_normal((R, I)); uu = g.standard_normal((R, I))
+    s = g.random(R)
+    q = orc.mxfp8_backward_down(dy, gg, uu, s, offs, wd)
+    p = orc.mxfp8_backward_down(dy, gg, uu, s, offs, wd, quantize=False)
+    for k in ("da", "dg", "du", "ds"):
+        np.testing.assert_array_equal(q[k], p[k])
+    for e in range(n):
+        np.testing.assert_array_equal(p["da"][offs[e]:offs[e + 1]], dy[offs[e]:offs[e + 1]] @ wd[e])
+    wd_i = np.stack([_grid_rows(H, I, g) for _ in range(n)])    # grid along I only
+    q2 = orc.mxfp8_backward_down(dy, gg, uu, s, offs, wd_i)
+    p2 = orc.mxfp8_backward_down(dy, gg, uu, s, offs, wd_i, quantize=False)
+    assert not np.allclose(q2["da"], p2["da"], rtol=1e-6, atol=0)
+
+
+def test_mxfp8_backward_down_dw_down_on_grid_along_rows():
+    # dW_d = Q_R(dY)^T Q_R(a) with a = s SiLU(g) u.  With g = 64 (sigmoid(64)
+    # is 1 in fp64, so SiLU(g) = 64 exactly), s = 1/2 and u on the grid down
+    # each segment, a = 32 u is on that grid too; so is dY: dW_d is exact.
+    g = np.random.default_rng(44)
+    offs, n, H, I = _bwd_case(g)
+    R = offs[-1]
+    dy = _grid_segment_rows(offs, H, g)
+    uu = _grid_segment_rows(offs, I, g)
+    gg = np.full((R, I), 64.0)
+    s = np.full(R, 0.5)
+    wd = g.standard_normal((n, H, I))
+    q = orc.mxfp8_backward_down(dy, gg, uu, s, offs, wd)
+    p = orc.mxfp8_backward_down(dy, gg, uu, s, offs, wd, quantize=False)
+    np.testing.assert_array_equal(q["a"], 32.0 * uu)
+    np.testing.assert_array_equal(q["dw_down"], p["dw_down"])
+    for e in range(n):
+        sl = slice(offs[e], offs[e + 1])
+        np.testing.assert_array_equal(p["dw_down"][e], dy[sl].T @ (32.0 * uu[sl]))
+
+
+def test_mxfp8_backward_gate_up_on_grid():
+    g = np.random.default_rng(45)
+    offs, n, H, I = _bwd_case(g)
+    R = offs[-1]
+    # dX: dg, du on the grid along I (rows), W_g, W_u along I (down columns)
+    dg, du = _grid_rows(R, I, g), _grid_rows(R, I, g)
+    wg = np.stack([_grid_rows(H, I, g).T for _ in range(n)])   # [n, I, H]
+    wu = np.stack([_grid_rows(H, I, g).T for _ in range(n)])
+    x = g.standard_normal((R, H))
+    q = orc.mxfp8_backward_gate_up(dg, du, x, offs, wg, wu)
+    p = orc.mxfp8_backward_gate_up(dg, du, x, offs, wg, wu, quantize=False)
+    np.testing.assert_array_equal(q["dx"], p["dx"])
+    for e in range(n):
+        sl = slice(offs[e], offs[e + 1])
+        np.testing.assert_array_equal(p["dx"][sl], dg[sl] @ wg[e] + du[sl] @ wu[e])
+    # weights on the grid along H only: dX changes under quantisation
+    wg_h = np.stack([_grid_rows(I, H, g) for _ in range(n)])
+    q2 = orc.mxfp8_backward_gate_up(dg, du, x, offs, wg_h, wu)
+    p2 = orc.mxfp8_backward_gate_up(dg, du, x, offs, wg_h, wu, quantize=False)
+    assert not np.allclose(q2["dx"], p2["dx"], rtol=1e-6, atol=0)
+    # dW_g, dW_u: dg, du, x on the grid down each segment
+    dg, du = _grid_segment_rows(offs, I, g), _grid_segment_rows(offs, I, g)
+    x = _grid_segment_rows(offs, H, g)
+    q = orc.mxfp8_backward_gate_up(dg, du, x, offs, wg, wu)
+    p = orc.mxfp8_backward_gate_up(dg, du, x, offs, wg, wu, quantize=False)
+    np.testing.assert_array_equal(q["dw_gate"], p["dw_gate"])
+    np.testing.assert_array_equal(q["dw_up"], p["dw_up"])
+    for e in range(n):
+        sl = slice(offs[e], offs[e + 1])
+        np.testing.assert_array_equal(p["dw_gate"][e], dg[sl].T @ x[sl])
+
+
+def _e4m3_own_scale(v):
+    """Each value MX-quantised as a block of its own (the rest of the block
+    zero): X = floor(log2 |v|) - 8, code = E4M3(v / 2^X) saturating at 448,
+    written out with the pinned scalar encoder, independent of the block
+    quantiser."""
+    out = np.zeros_like(v, dtype=np.float64)
+    for i, x in np.ndenumerate(v):
+        if x == 0.0:
+            continue
+        _, e = np.frexp(x)
+        X = max(int(e) - 9, -127)
+        out[i] = orc.e4m3_value(orc.e4m3_encode(x / 2.0 ** X)) * 2.0 ** X
+    return out
+
+
+def test_weight_gradients_of_one_row_segments_quantise_every_value():
+    # With one row per expert, a weight gradient is an outer product and
+    # each operand value is a block of its own down the rows.
+    g = np.random.default_rng(46)
+    n, H, I = 3, 40, 24
+    offs = np.arange(n + 1)
+    x = g.standard_normal((n, H)); dy = g.standard_normal((n, H))
+    gg = g.standard_normal((n, I)); uu = g.standard_normal((n, I))
+    s = g.random(n); wd = g.standard_normal((n, H, I))
+    b = orc.mxfp8_backward_down(dy, gg, uu, s, offs, wd)
+    dg, du = g.standard_normal((n, I)), g.standard_normal((n, I))
+    c = orc.mxfp8_backward_gate_up(dg, du, x, offs, g.standard_normal((n, I, H)),
+                                   g.standard_normal((n, I, H)))
+    for e in range(n):
+        np.testing.assert_allclose(
+            b["dw_down"][e], np.outer(_e4m3_own_scale(dy[e]), _e4m3_own_scale(b["a"][e])),
+            rtol=1e-15, atol=0)
+        np.testing.assert_allclose(
+            c["dw_gate"][e], np.outer(_e4m3_own_scale(dg[e]), _e4m3_own_scale(x[e])),
+            rtol=1e-15, atol=0)
+        np.testing.assert_allclose(
+            c["dw_up"][e], np.outer(_e4m3_own_scale(du[e]), _e4m3_own_scale(x[e])),
+            rtol=1e-15, atol=0)
+
+
+def test_mlp_step_is_its_stages_in_order():
+    # the step is forward -> backward_down at the forward's g, u ->
+    # backward_gate_up on the resulting dg, du; bf16_dgu rounds dg, du first
+    x, offs, s, wg, wu, wd, dy = _mlp_inputs()
+    st = orc.mxfp8_mlp_step(x, offs, s, wg, wu, wd, dy)
+    f = orc.mxfp8_forward(x, offs, s, wg, wu, wd)
+    b = orc.mxfp8_backward_down(dy, f["g"], f["u"], s, offs, wd)
+    c = orc.mxfp8_backward_gate_up(b["dg"], b["du"], x, offs, wg, wu)
+    for k, v in list(f.items()) + list(b.items()) + list(c.items()):
+        if k in st:
+            np.testing.assert_array_equal(st[k], v, err_msg=k)
+    h = orc.mxfp8_mlp_step(x, offs, s, wg, wu, wd, dy, bf16_dgu=True)
+    c2 = orc.mxfp8_backward_gate_up(orc.round_bf16(b["dg"]), orc.round_bf16(b["du"]),
+                                    x, offs, wg, wu)
+    np.testing.assert_array_equal(h["dx"], c2["dx"])
+    np.testing.assert_array_equal(h["y"], st["y"])
+
+
 def test_mlp_step_forward_matches_bf16_ffn_without_quantization():
     x, offs, s, wg, wu, wd, dy = _mlp_inputs()
     res = orc.mxfp8_mlp_step(x, offs, s, wg, wu, wd, dy, quantize=False)
