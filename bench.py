@@ -177,6 +177,20 @@ def percentiles(ms):
             "p90": round(float(q[2]), 4)}
 
 
+def host_cpu():
+    """The host's CPU model and logical CPU count (the oracle's threads are
+    reported as `cores`)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count()}
+
+
 def cpu_baseline(wl, inp, tokens):
     """The oracle as it stands, on the first `tokens` tokens of the batch."""
     import oracle
@@ -199,7 +213,7 @@ def cpu_baseline(wl, inp, tokens):
         flop += 2.0 * T * wl.H * wl.E
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", **host_cpu(),
             "sample": f"first {T} tokens of the batch ({rows} token-expert rows): "
                       f"fp64 router logits + top-k + per-token SwiGLU FFN of the "
                       f"chosen local experts + weighted sum; {dt:.1f} s"}
@@ -221,14 +235,14 @@ def cpu_baseline_mx(wl, inp, x_perm, offsets, s_perm, dy, rows, inter):
     flop = 18.0 * r * wl.H * inter
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", **host_cpu(),
             "sample": f"{r} rows of expert 0 with its first {inter} of {wl.I} "
                       f"intermediate channels: fp64 MX quantisation of every "
                       f"GEMM operand (weights included), forward, dgrad and "
                       f"wgrad; {dt:.1f} s"}
 
 
-def run_mx(args, wl, dev):
+def run_mx(args, wl, dev, cpu=True):
     """MXFP8 grouped-MLP training step: permute, quantise x, forward (gate/up
     + SwiGLU x scale, then down), backward (down + SwiGLU backward, then
     gate/up data and weight gradients).  Routing runs before timing; the
@@ -378,14 +392,14 @@ def run_mx(args, wl, dev):
             "avg_ms": round(gu_ms, 4),
         },
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         log("cpu baseline: oracle MXFP8 step on a slice")
         offs = pout.offsets.cpu().numpy()
         xp = pout.x_perm[:R].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         sp = pout.s_perm[:R].cpu().numpy().astype(np.float64)
         res["cpu_baseline"] = cpu_baseline_mx(wl, inp, xp, offs, sp, dy_host,
                                               rows=512, inter=2048)
-    print(json.dumps(res), flush=True)
+    return res
 
 
 def main():
@@ -406,6 +420,11 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replays of the step "
                          "captured in a HIP graph")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="default workload only: skip the EP8 share, the EP64 "
+                         "share and the MXFP8 step timed after it")
+    ap.add_argument("--no-loop", action="store_true",
+                    help="skip the per-expert-loop comparison of the grouped FFN")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one elementwise copy of this many "
                          "MiB (read + write) to calibrate HBM byte counters")
@@ -420,8 +439,88 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    cpu = not args.no_cpu_baseline
     if wl.dtype == "mxfp8":
-        return run_mx(args, wl, dev)
+        res = run_mx(args, wl, dev, cpu=cpu)
+    else:
+        res = run_bf16(args, wl, dev, cpu=cpu, loop=not args.no_loop)
+    if args.workload == "c4_full_bf16" and not args.no_extra:
+        # The other configurations of the metric, timed the same way (no CPU
+        # baseline, which is taken on the main workload only).
+        extra = {}
+        for name in ("c3_ep8_bf16", "c2_ep64_bf16", "c5_mxfp8"):
+            torch.cuda.empty_cache()
+            w2 = synth.WORKLOADS[name]
+            if w2.dtype == "mxfp8":
+                r = run_mx(args, w2, dev, cpu=False)
+            else:
+                r = run_bf16(args, w2, dev, cpu=False, loop=not args.no_loop)
+            extra[name] = compact(r)
+        res["extra_workloads"] = extra
+    print(json.dumps(res), flush=True)
+
+
+def compact(r):
+    """The figures of a result that the extra workloads report."""
+    keep = ("value", "unit", "ms_per_step", "ms_per_step_eager", "dtype",
+            "rows_per_s", "step_hbm_gbs", "step_hbm_frac", "step_mfma_frac",
+            "step_mfma_frac_fp8", "step_mfma_frac_bf16", "ffn_ms_events",
+            "step_ms_events", "loop_vs_grouped", "master_quant_ms")
+    out = {k: r[k] for k in keep if k in r}
+    out["workload"] = r["config"]["workload"]
+    out["rows"] = r["config"]["rows"]
+    out["roofline"] = {k: v for k, v in r["roofline"].items()
+                       if k not in ("traffic_unit",)}
+    return out
+
+
+def loop_vs_grouped(wl, x, topk_idx, topk_w, wcopies, steps, dev):
+    """The grouped FFN (one launch sequence for all experts) against the
+    per-expert loop (a launch sequence per expert, counts read back to the
+    host each step, as a loop must) on the same permuted rows: gate/up +
+    down, eager launches, mean over `steps` steps."""
+    T, k, H, I, n = wl.T, wl.k, wl.H, wl.I, wl.n_local
+    p = moe.PermuteOut(T, k, H, n, torch.bfloat16, dev)
+    moe.permute(topk_idx, x, wl.e_begin, n, topk_w=topk_w, out=p, E=wl.E)
+    F = T * k
+    a = torch.empty((F, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((F, H), dtype=torch.bfloat16, device=dev)
+    ws = moe.ffn_workspace(F, n, H, I, torch.bfloat16, dev)
+    counts_host = torch.empty(n, dtype=torch.int32, pin_memory=True)
+
+    def grouped(i):
+        wg, wu, wd = wcopies[i % len(wcopies)]
+        moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, wg, wu, wd, a=a, y=y,
+                        workspace=ws)
+
+    def looped(i):
+        wg, wu, wd = wcopies[i % len(wcopies)]
+        counts_host.copy_(p.counts)          # the loop needs the sizes on the host
+        torch.cuda.current_stream().synchronize()
+        moe.grouped_ffn_loop(p.x_perm, p.offsets, counts_host.tolist(),
+                             p.s_perm, wg, wu, wd, a=a, y=y, workspace=ws)
+
+    out = {}
+    for name, fn in (("grouped", grouped), ("loop", looped)):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        out[f"{name}_ms"] = round((time.perf_counter() - t0) * 1e3 / steps, 4)
+    nz = int((p.counts > 0).sum().item())
+    out["loop_over_grouped"] = round(out["loop_ms"] / out["grouped_ms"], 3)
+    out["experts_with_rows"] = nz
+    out["what"] = ("gate/up + down on the same permuted rows; the loop issues "
+                   "each expert's launches separately and reads the counts "
+                   "back to the host every step")
+    del p, a, y, ws
+    return out
+
+
+def run_bf16(args, wl, dev, cpu=True, loop=True):
     # Weight copies rotate across steps when the weights are small enough for
     # the 256 MB last-level cache to hold them between steps.
     wbytes = 3 * wl.n_local * wl.H * wl.I * 2
@@ -512,6 +611,10 @@ def main():
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
+    if loop:
+        log(f"{wl.name}: per-expert loop against the grouped FFN")
+        res_loop = loop_vs_grouped(wl, d["x"], topk_idx, topk_w, wcopies,
+                                   args.steps, dev)
     alg = algorithmic(wl, R, n_touched, gather)
     flop = alg["flop_ffn"] + alg["flop_router"]
     tflops = flop / (ms_step * 1e-3) / 1e12
@@ -573,10 +676,12 @@ def main():
             "mfma_frac": round(gu_tflops / BF16_PEAK_TFLOPS, 4),
         }),
     }
-    if not args.no_cpu_baseline:
+    if loop:
+        res["loop_vs_grouped"] = res_loop
+    if cpu:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_tokens, T))
-    print(json.dumps(res), flush=True)
+    return res
 
 
 if __name__ == "__main__":

@@ -230,6 +230,26 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
                     hipStream_t stream);
 
 /*
+ * moe_grouped_ffn_loop - the computation of moe_grouped_ffn (bf16 only,
+ * identical bits) issued the way the pages' baseline does it: expert by
+ * expert, each expert's gate/up and down as launches of their own (BioNeMo
+ * MoE article, "GroupedLinear Optimizes Expert Computation in MoE Models":
+ * iterating over the experts with a separate launch for each is what the
+ * grouped operation replaces).  It exists to measure that difference.  A
+ * per-expert loop needs the row counts on the host: host_counts [n_local]
+ * (host memory) must equal the device counts (offsets[e+1] - offsets[e]);
+ * experts with no rows get no launch.  Other arguments, workspace and
+ * limits as for moe_grouped_ffn.  MOE_E_SHAPE if sum(host_counts) > R_cap.
+ */
+int moe_grouped_ffn_loop(const void *x_perm, const int32_t *offsets,
+                         const int32_t *host_counts, const float *s_perm,
+                         int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
+                         const void *w_gate, const void *w_up,
+                         const void *w_down, int dtype, void *a, void *y,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/*
  * moe_unpermute_combine - bring expert outputs back to token order and add
  * them up (Wide-EP explainer, 前提:MoEとは and 前提条件:GPU間の高速通信):
  *   out[t] = sum over j ascending with inv[t,j] >= 0 of c_tj * y[inv[t,j]]

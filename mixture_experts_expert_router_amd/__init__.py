@@ -65,6 +65,8 @@ def lib():
                                       vp, i32, vp, vp, vp, sz, vp]
         L.moe_unpermute_combine.argtypes = [vp, vp, vp, i64, i64, i64, i32,
                                             vp, vp]
+        L.moe_grouped_ffn_loop.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64,
+                                           vp, vp, vp, i32, vp, vp, vp, sz, vp]
         L.moe_debug_sync.argtypes = [vp]
         L.moe_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
         L.moe_permute_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64,
@@ -289,6 +291,27 @@ def grouped_ffn(x_perm, offsets, s_perm, w_gate, w_up, w_down, a=None,
     _call("moe_grouped_ffn", _p(x_perm), _p(offsets), _p(s_perm), n_local,
           R_cap, H, I, _p(w_gate), _p(w_up), _p(w_down), _dt(x_perm), _p(a),
           _p(y), _p(workspace), workspace.numel(), _stream(stream))
+    return a, y
+
+
+def grouped_ffn_loop(x_perm, offsets, host_counts, s_perm, w_gate, w_up,
+                     w_down, a=None, y=None, workspace=None, stream=None):
+    """grouped_ffn issued expert by expert (one set of launches per expert
+    with rows); host_counts: the per-expert row counts as a host sequence."""
+    R_cap, H = x_perm.shape
+    n_local, I, _ = w_gate.shape
+    hc = (ctypes.c_int32 * n_local)(*[int(c) for c in host_counts])
+    if a is None:
+        a = torch.empty((R_cap, I), dtype=x_perm.dtype, device=x_perm.device)
+    if y is None:
+        y = torch.empty((R_cap, H), dtype=x_perm.dtype, device=x_perm.device)
+    if workspace is None:
+        workspace = ffn_workspace(R_cap, n_local, H, I, x_perm.dtype,
+                                  x_perm.device)
+    _call("moe_grouped_ffn_loop", _p(x_perm), _p(offsets), hc, _p(s_perm),
+          n_local, R_cap, H, I, _p(w_gate), _p(w_up), _p(w_down),
+          _dt(x_perm), _p(a), _p(y), _p(workspace), workspace.numel(),
+          _stream(stream))
     return a, y
 
 

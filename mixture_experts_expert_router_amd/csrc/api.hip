@@ -30,6 +30,12 @@ int num_cus() {
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+bool all_aligned16(std::initializer_list<const void *> ps) {
+  for (const void *q : ps)
+    if (!aligned16(q)) return false;
+  return true;
+}
+
 int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
 
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
@@ -265,6 +271,34 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
   if (st != MOE_OK) return st;
   return moe_grouped_down(a, offsets, n_local, R_cap, H, I, w_down, dtype, y,
                           workspace, workspace_bytes, stream);
+}
+
+int moe_grouped_ffn_loop(const void *x_perm, const int32_t *offsets,
+                         const int32_t *host_counts, const float *s_perm,
+                         int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
+                         const void *w_gate, const void *w_up,
+                         const void *w_down, int dtype, void *a, void *y,
+                         void *workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  int st = check_ffn(offsets, n_local, R_cap, H, I, dtype, workspace,
+                     workspace_bytes);
+  if (st != MOE_OK) return st;
+  if (dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
+  if (host_counts == nullptr) return MOE_E_ARG;
+  int64_t total = 0;
+  for (int64_t e = 0; e < n_local; ++e) {
+    if (host_counts[e] < 0) return MOE_E_SHAPE;
+    total += host_counts[e];
+  }
+  if (total > R_cap) return MOE_E_SHAPE;
+  if (R_cap == 0 || total == 0) return MOE_OK;
+  if (!x_perm || !w_gate || !w_up || !w_down || !a || !y) return MOE_E_ARG;
+  if (!all_aligned16({x_perm, w_gate, w_up, w_down, a, y})) return MOE_E_ALIGN;
+  return status_of(moe::launch_ffn_loop_bf16(
+      (const uint16_t *)x_perm, offsets, host_counts, s_perm, (int)n_local,
+      R_cap, (int)H, (int)I, (const uint16_t *)w_gate, (const uint16_t *)w_up,
+      (const uint16_t *)w_down, (uint16_t *)a, (uint16_t *)y,
+      (int32_t *)workspace, num_cus(), stream));
 }
 
 int moe_unpermute_combine(const void *y, const int32_t *inv,

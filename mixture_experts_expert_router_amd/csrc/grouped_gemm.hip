@@ -491,9 +491,13 @@ hipError_t launch_one(GemmArgs p, int num_cus, int64_t max_tiles,
 // cannot rule the narrow shape out (few experts times n-tiles), the plan
 // kernel chooses from the actual rows and both kernels are launched; the one
 // not chosen finds no tiles.
+// host_rows >= 0: the launch covers one group whose row count the host
+// knows (the per-expert loop); the grids are sized for it and the class of
+// kernels that cannot find a tile is not launched.
 template <int EPI>
 hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
-                          int64_t R_cap, hipStream_t s) {
+                          int64_t R_cap, hipStream_t s,
+                          int64_t host_rows = -1) {
   const bool sw = EPI == EPI_SWIGLU;
   constexpr int wide_cfg[6] = {MOE_WIDE_CFG};
   constexpr int narrow_cfg[6] = {MOE_NARROW_CFG};
@@ -505,7 +509,8 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
   const bool wide_sure = (int64_t)p.G * nt_w >= wide_min;
   // The narrow kernel's grid; the plan kernel keeps the wide shape when the
   // narrow one would need more tiles than this.
-  const int64_t max_n = ((R_cap + NBM - 1) / NBM + p.G) * (int64_t)nt_n;
+  const int64_t grid_rows = host_rows >= 0 ? host_rows : R_cap;
+  const int64_t max_n = ((grid_rows + NBM - 1) / NBM + p.G) * (int64_t)nt_n;
   const int narrow_cap = (int)std::min<int64_t>(max_n, 8LL * num_cus);
   p.r_cap = (int)R_cap;
   int32_t *errw = tile_ws;
@@ -518,12 +523,15 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // small-row class
-  GemmArgs ps = p;
-  ps.tile_prefix = pre_s;
-  ps.NT = nt_s;
-  err = launch_one<64, 256, 1, 4, 64, 3, EPI>(ps, num_cus,
-                                              (int64_t)p.G * nt_s, s);
-  if (err != hipSuccess) return err;
+  if (host_rows < 0 || host_rows <= kSmallRows) {
+    GemmArgs ps = p;
+    ps.tile_prefix = pre_s;
+    ps.NT = nt_s;
+    err = launch_one<64, 256, 1, 4, 64, 3, EPI>(ps, num_cus,
+                                                (int64_t)p.G * nt_s, s);
+    if (err != hipSuccess) return err;
+  }
+  if (host_rows >= 0 && host_rows <= kSmallRows) return hipSuccess;
   // large-row class
   if (!wide_sure) {
     GemmArgs pn = p;
@@ -535,7 +543,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
   GemmArgs pw = p;
   pw.tile_prefix = pre_w;
   pw.NT = nt_w;
-  const int64_t max_w = ((R_cap + WBM - 1) / WBM + p.G) * (int64_t)nt_w;
+  const int64_t max_w = ((grid_rows + WBM - 1) / WBM + p.G) * (int64_t)nt_w;
   return launch_one<MOE_WIDE_CFG, EPI>(pw, num_cus, max_w, s);
 }
 
@@ -570,6 +578,36 @@ hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
   p.C = y; p.ldc = H;
   p.offsets = offsets; p.G = n_local; p.N = H; p.K = I;
   return launch_grouped<EPI_BF16>(p, num_cus, tile_ws, R_cap, s);
+}
+
+hipError_t launch_ffn_loop_bf16(const uint16_t *x_perm, const int32_t *offsets,
+                               const int32_t *host_counts, const float *s_perm,
+                               int n_local, int64_t R_cap, int H, int I,
+                               const uint16_t *w_gate, const uint16_t *w_up,
+                               const uint16_t *w_down, uint16_t *a,
+                               uint16_t *y, int32_t *tile_ws, int num_cus,
+                               hipStream_t s) {
+  const int64_t IH = (int64_t)I * H;
+  for (int e = 0; e < n_local; ++e) {
+    const int64_t n = host_counts[e];
+    if (n <= 0) continue;
+    // one group: rows [offsets[e], offsets[e+1]) read through offsets + e
+    GemmArgs g{};
+    g.A = x_perm; g.B0 = w_gate + e * IH; g.B1 = w_up + e * IH;
+    g.b_stride = 0;
+    g.C = a; g.ldc = I; g.row_scale = s_perm;
+    g.offsets = offsets + e; g.G = 1; g.N = I; g.K = H;
+    hipError_t err = launch_grouped<EPI_SWIGLU>(g, num_cus, tile_ws, R_cap, s, n);
+    if (err != hipSuccess) return err;
+    GemmArgs d{};
+    d.A = a; d.B0 = w_down + e * IH; d.B1 = nullptr;
+    d.b_stride = 0;
+    d.C = y; d.ldc = H;
+    d.offsets = offsets + e; d.G = 1; d.N = H; d.K = I;
+    err = launch_grouped<EPI_BF16>(d, num_cus, tile_ws, R_cap, s, n);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_router_gemm_bf16(const uint16_t *x, const uint16_t *w,

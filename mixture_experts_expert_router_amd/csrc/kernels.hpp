@@ -52,6 +52,15 @@ hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
                             const uint16_t *w_down, uint16_t *y,
                             int32_t *tile_ws, int num_cus, hipStream_t s);
 
+// The grouped FFN issued expert by expert (gate/up, then down, per expert
+// with host_counts[e] > 0), each launch one group of the same kernels.
+hipError_t launch_ffn_loop_bf16(const uint16_t *x_perm, const int32_t *offsets,
+                               const int32_t *host_counts, const float *s_perm,
+                               int n_local, int64_t R_cap, int H, int I,
+                               const uint16_t *w_gate, const uint16_t *w_up,
+                               const uint16_t *w_down, uint16_t *a,
+                               uint16_t *y, int32_t *tile_ws, int num_cus,
+                               hipStream_t s);
 hipError_t launch_gate_up_f32(const float *x_perm, const int32_t *offsets,
                               const float *s_perm, int n_local, int64_t R_cap,
                               int64_t H, int64_t I, const float *w_gate,

@@ -117,6 +117,24 @@ def test_noalloc_permute_rejects_sizes_beyond_its_scratch(L):
     assert L.moe_status_string(7)
 
 
+def test_ffn_loop_validation(L):
+    import ctypes
+    f = L.moe_grouped_ffn_loop
+    ws = L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)
+    hc = (ctypes.c_int32 * 4)(10, 0, 20, 30)
+    big = (ctypes.c_int32 * 4)(10, 0, 20, 40)
+    neg = (ctypes.c_int32 * 4)(10, -1, 20, 30)
+
+    def call(h=hc, dt=BF16, R=64, x=P):
+        return f(x, P, h, None, 4, R, 128, 128, P, P, P, dt, P, P, P, ws, None)
+
+    assert call(h=None) == E_ARG
+    assert call(h=big) == E_SHAPE          # 70 rows > R_cap = 64
+    assert call(h=neg) == E_SHAPE
+    assert call(dt=F32) == 5               # MOE_E_UNSUPPORTED
+    assert call(x=P_ODD) == E_ALIGN
+
+
 def test_ffn_validation(L):
     g = L.moe_grouped_gate_up
     ws = L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)

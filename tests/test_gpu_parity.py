@@ -298,3 +298,43 @@ def test_step_captured_in_a_graph_replays_bit_exactly():
         assert torch.equal(out, ref), rep
         # eager work between the replays
         _ = (d["x"].float() @ d["w_router"].float().T).sum().item()
+
+
+@pytest.mark.parametrize("name", ["small_bf16", "small_ep_bf16", "mid_bf16"])
+def test_ffn_loop_equals_grouped_bit_for_bit(name):
+    """The per-expert loop (one set of launches per expert, host-known
+    counts) computes exactly what the grouped call computes."""
+    wl = synth.WORKLOADS[name]
+    print_case("loop vs grouped", name)
+    inp = synth.make_inputs(wl)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    g = gpu_chain(wl, d)
+    p = g["p"]
+    counts = p.counts.cpu().tolist()
+    a2, y2 = moe.grouped_ffn_loop(p.x_perm, p.offsets, counts, p.s_perm,
+                                  d["w_gate"], d["w_up"], d["w_down"])
+    moe.debug_sync()
+    R = int(p.offsets[-1].item())
+    assert torch.equal(bits_t(g["a"][:R]), bits_t(a2[:R]))
+    assert torch.equal(bits_t(g["y"][:R]), bits_t(y2[:R]))
+
+
+def bits_t(t):
+    return t.view(torch.int16)
+
+
+def test_ffn_loop_edge_segments():
+    counts, e_begin, H, I = [0, 1, 129, 256, 0, 64, 65], 0, 256, 320
+    n_local, E, k = len(counts), 16, 4
+    print_case("loop edge", counts)
+    idx, w, x, wg, wu, wd = _edge_inputs(counts, n_local, e_begin, E, k, H, I)
+    wt = to_dev(w.astype(np.float32))
+    p = moe.permute(to_dev(idx), to_dev(x), e_begin, n_local, topk_w=wt, E=E)
+    a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, to_dev(wg),
+                           to_dev(wu), to_dev(wd))
+    a2, y2 = moe.grouped_ffn_loop(p.x_perm, p.offsets, counts, p.s_perm,
+                                  to_dev(wg), to_dev(wu), to_dev(wd))
+    moe.debug_sync()
+    R = sum(counts)
+    assert torch.equal(bits_t(a[:R]), bits_t(a2[:R]))
+    assert torch.equal(bits_t(y[:R]), bits_t(y2[:R]))
