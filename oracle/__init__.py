@@ -73,6 +73,9 @@ def _lib():
         L.orc_swiglu_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp,
                                           vp]
         L.orc_swiglu_rows.argtypes = [vp, vp, vp, i64, i64, vp]
+        L.orc_eplb_plan.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.orc_permute_replicated.argtypes = [vp, i64, i64, i64, vp, vp, i64,
+                                             i64, vp, vp, vp, vp]
         _L = L
     return _L
 
@@ -228,6 +231,50 @@ def moe_layer(w, inputs, scale_in_ffn=True):
                 counts=p["counts"], offsets=p["offsets"],
                 row_src=p["row_src"], inv=p["inv"], R=R, x_perm=x_perm,
                 s_perm=s_perm, a=a, y=y, out=out)
+
+
+# --------------------------------------------------------------------------
+# Expert-parallel load balancing
+
+
+def eplb_plan(counts, n_slots, n_ranks):
+    """Replicas and placement of E experts with observed `counts` on n_slots
+    physical slots over n_ranks ranks (see orc_eplb_plan).  Returns dict rep
+    [E], rep_first [E+1], rep_slot [S], slot_expert [S], slot_copy [S]."""
+    c = _c(counts, np.int32)
+    E = c.shape[0]
+    S = int(n_slots)
+    out = dict(rep=np.empty(E, np.int32), rep_first=np.empty(E + 1, np.int32),
+               rep_slot=np.empty(S, np.int32), slot_expert=np.empty(S, np.int32),
+               slot_copy=np.empty(S, np.int32))
+    _lib().orc_eplb_plan(_p(c), E, S, int(n_ranks), _p(out["rep"]),
+                         _p(out["rep_first"]), _p(out["rep_slot"]),
+                         _p(out["slot_expert"]), _p(out["slot_copy"]))
+    return out
+
+
+def permute_replicated(idx, E, plan, s_begin, n_slots):
+    """Stable dispatch of the flat entries to the slots [s_begin, s_begin +
+    n_slots) of a plan, splitting each expert's current entries among its
+    copies (see orc_permute_replicated)."""
+    idx = _c(idx, np.int32)
+    T, k = idx.shape
+    counts = np.empty(n_slots, np.int32)
+    offsets = np.empty(n_slots + 1, np.int32)
+    row_src = np.empty(T * k, np.int32)
+    inv = np.empty((T, k), np.int32)
+    _lib().orc_permute_replicated(
+        _p(idx), T, k, int(E), _p(_c(plan["rep_first"], np.int32)),
+        _p(_c(plan["rep_slot"], np.int32)), int(s_begin), int(n_slots),
+        _p(counts), _p(offsets), _p(row_src), _p(inv))
+    R = int(offsets[-1])
+    return dict(counts=counts, offsets=offsets, row_src=row_src[:R].copy(),
+                inv=inv, R=R)
+
+
+def copy_rows(n, r, i):
+    """Rows [lo, hi) of copy i among r copies of an expert with n rows."""
+    return i * n // r, (i + 1) * n // r
 
 
 # --------------------------------------------------------------------------

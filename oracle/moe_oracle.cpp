@@ -20,6 +20,9 @@
 //   [TE-MXFP8]        same article, "MXFP8 Precision Reduces Memory Footprint
 //                     for Biological Models": 8-bit values with one scale per
 //                     block of 32 consecutive values.
+//   [WideEP-EPLB]     "Wide-EPとは?" explainer, section 負荷の偏り:EPLB: skewed
+//                     expert loads are evened out between forward passes by
+//                     moving experts and copying the heaviest ones.
 // Where the pages leave a step open, the reading taken is stated at the
 // function.  Parity pins for every function live in the CPU test suite.
 //
@@ -427,6 +430,133 @@ void orc_swiglu_bwd_rows(const double *da, const double *g, const double *u,
       acc += da[o] * sl * u[o];
     }
     ds[r] = acc;
+  }
+}
+
+
+
+// ---------------------------------------------------------------------------
+// Expert-parallel load balancing.  [WideEP-EPLB] "Wide-EPとは?" explainer,
+// section 負荷の偏り:EPLB: how often each expert is chosen is skewed; when
+// frequently chosen experts sit on one GPU it becomes the bottleneck while
+// the others idle; between forward passes the balancer looks at each
+// expert's load and rearranges the placement, and gives the heaviest
+// experts copies on several GPUs.  The pages give no algorithm; the plain
+// reading taken here.  The plan is made from observed loads (the per-expert
+// counts of earlier routing):
+//   1. replication: S physical slots for E experts (S >= E); every expert
+//      gets one slot, and each of the S - E spare slots goes, one at a time,
+//      to the expert with the largest load per copy (n_e / r_e; ties: lower
+//      expert index);
+//   2. the expected rows of copy i of expert e are those of the split in
+//      (dispatch, below) applied to the observed n_e;
+//   3. placement: G ranks of S / G slots each; copies are placed in order of
+//      decreasing expected rows (ties: lower expert, then lower copy), each
+//      on the rank with the smallest expected load so far among those with
+//      a free slot that do not yet hold the expert (if every rank with a
+//      free slot holds it: among those with a free slot; ties: lower rank);
+//   4. physical slot numbers: rank g owns slots [g S/G, (g+1) S/G), in
+//      increasing (expert, copy) order.
+// counts [E] in; out: rep [E] copies per expert, rep_first [E + 1] prefix of
+// rep, rep_slot [S] physical slot of copy i of expert e at rep_first[e] + i,
+// slot_expert / slot_copy [S] expert and copy index of each slot.
+void orc_eplb_plan(const int32_t *counts, int64_t E, int64_t S, int64_t G,
+                   int32_t *rep, int32_t *rep_first, int32_t *rep_slot,
+                   int32_t *slot_expert, int32_t *slot_copy) {
+  for (int64_t e = 0; e < E; ++e) rep[e] = 1;
+  for (int64_t extra = 0; extra < S - E; ++extra) {
+    int64_t best = 0;
+    for (int64_t e = 1; e < E; ++e)
+      // n_e / r_e > n_best / r_best, compared exactly
+      if ((int64_t)counts[e] * rep[best] > (int64_t)counts[best] * rep[e])
+        best = e;
+    ++rep[best];
+  }
+  rep_first[0] = 0;
+  for (int64_t e = 0; e < E; ++e) rep_first[e + 1] = rep_first[e] + rep[e];
+  struct Copy { int32_t e, i; int64_t rows; };
+  std::vector<Copy> cp;
+  for (int64_t e = 0; e < E; ++e)
+    for (int32_t i = 0; i < rep[e]; ++i) {
+      const int64_t n = counts[e], r = rep[e];
+      cp.push_back({(int32_t)e, i, (i + 1) * n / r - i * n / r});
+    }
+  std::stable_sort(cp.begin(), cp.end(), [](const Copy &a, const Copy &b) {
+    return a.rows > b.rows;
+  });
+  const int64_t per = S / G;
+  std::vector<int64_t> load(G, 0), used(G, 0);
+  std::vector<std::vector<char>> holds(G, std::vector<char>(E, 0));
+  std::vector<int32_t> rank_of(S);   // by copy index rep_first[e] + i
+  for (const Copy &c : cp) {
+    int64_t pick = -1;
+    for (int pass = 0; pass < 2 && pick < 0; ++pass)
+      for (int64_t g = 0; g < G; ++g) {
+        if (used[g] == per || (pass == 0 && holds[g][c.e])) continue;
+        if (pick < 0 || load[g] < load[pick]) pick = g;
+      }
+    load[pick] += c.rows;
+    ++used[pick];
+    holds[pick][c.e] = 1;
+    rank_of[rep_first[c.e] + c.i] = (int32_t)pick;
+  }
+  std::vector<int64_t> next(G);
+  for (int64_t g = 0; g < G; ++g) next[g] = g * per;
+  for (int64_t e = 0; e < E; ++e)
+    for (int32_t i = 0; i < rep[e]; ++i) {
+      const int64_t q = rep_first[e] + i;
+      const int64_t s = next[rank_of[q]]++;
+      rep_slot[q] = (int32_t)s;
+      slot_expert[s] = (int32_t)e;
+      slot_copy[s] = i;
+    }
+}
+
+// Dispatch to this rank's slots [s_begin, s_begin + n_slots) under a plan
+// (the current routing, not the loads the plan was made from): with n_e the
+// number of current entries of expert e, copy i of e takes the entries at
+// positions [floor(i n_e / r_e), floor((i+1) n_e / r_e)) among e's entries
+// in ascending flat order f = t*k + j (contiguous ranges, as even as
+// possible); inside a slot, entries keep ascending f.  Entries of other
+// ranks' slots and indices outside [0, E) are dropped (inv = -1).  Outputs
+// as orc_permute over the local slots: counts [n_slots], offsets
+// [n_slots + 1], row_src, inv.
+void orc_permute_replicated(const int32_t *idx, int64_t T, int64_t k,
+                            int64_t E, const int32_t *rep_first,
+                            const int32_t *rep_slot, int64_t s_begin,
+                            int64_t n_slots, int32_t *counts, int32_t *offsets,
+                            int32_t *row_src, int32_t *inv) {
+  const int64_t F = T * k;
+  std::vector<int64_t> n(E, 0), seen(E, 0);
+  for (int64_t f = 0; f < F; ++f)
+    if (idx[f] >= 0 && idx[f] < E) ++n[idx[f]];
+  std::vector<int64_t> slot_of(F, -1);
+  for (int64_t f = 0; f < F; ++f) {
+    inv[f] = -1;
+    const int32_t e = idx[f];
+    if (e < 0 || e >= E) continue;
+    const int64_t q = seen[e]++;
+    const int64_t r = rep_first[e + 1] - rep_first[e];
+    for (int64_t i = 0; i < r; ++i)
+      if (i * n[e] / r <= q && q < (i + 1) * n[e] / r)
+        slot_of[f] = rep_slot[rep_first[e] + i];
+  }
+  for (int64_t s = 0; s < n_slots; ++s) {
+    int32_t c = 0;
+    for (int64_t f = 0; f < F; ++f)
+      if (slot_of[f] == s_begin + s) ++c;
+    counts[s] = c;
+  }
+  offsets[0] = 0;
+  for (int64_t s = 0; s < n_slots; ++s) offsets[s + 1] = offsets[s] + counts[s];
+  for (int64_t s = 0; s < n_slots; ++s) {
+    int32_t r = offsets[s];
+    for (int64_t f = 0; f < F; ++f)
+      if (slot_of[f] == s_begin + s) {
+        row_src[r] = (int32_t)f;
+        inv[f] = r;
+        ++r;
+      }
   }
 }
 
