@@ -250,6 +250,92 @@ int moe_grouped_ffn_loop(const void *x_perm, const int32_t *offsets,
                          hipStream_t stream);
 
 /*
+ * ---- Expert-parallel load balancing ("Wide-EPとは?" explainer, section
+ * 負荷の偏り:EPLB: expert loads are skewed, and a GPU holding the hot
+ * experts becomes the bottleneck while the others idle; between forward
+ * passes the balancer looks at each expert's load, rearranges the placement
+ * and gives the heaviest experts copies on several GPUs.  The pages give no
+ * algorithm; the rule taken is stated below.)
+ *
+ * moe_eplb_plan - a placement of E experts on n_slots physical slots (one
+ * expert copy each) over n_ranks ranks of n_slots / n_ranks slots, from
+ * observed per-expert loads counts [E] (device; e.g. the counts of an
+ * earlier moe_permute over all experts; negative counts read as 0):
+ *   1. every expert gets one copy; each of the n_slots - E spare slots goes
+ *      to the expert with the largest load per copy, counts[e] / copies
+ *      (ties: lower expert);
+ *   2. copy i of r copies of an expert with n rows is expected to take
+ *      floor((i+1) n / r) - floor(i n / r) rows;
+ *   3. copies are placed in order of decreasing expected rows (ties: lower
+ *      expert, then lower copy), each on the rank with the smallest expected
+ *      load so far among those with a free slot that do not yet hold that
+ *      expert (if every rank with a free slot holds it: among those with a
+ *      free slot; ties: lower rank);
+ *   4. rank g owns slots [g S/G, (g+1) S/G), in increasing (expert, copy)
+ *      order.
+ * Outputs (device, int32): rep [E] copies per expert, rep_first [E + 1]
+ * prefix of rep, rep_slot [n_slots] the slot of copy i of expert e at
+ * rep_first[e] + i, slot_expert / slot_copy [n_slots] the expert and copy
+ * index each slot holds.  Integer arithmetic only: deterministic.  One
+ * workgroup.
+ * Limits: 1 <= E <= 1024, E <= n_slots <= 4096, 1 <= n_ranks <= 1024,
+ * n_slots % n_ranks == 0.
+ */
+int moe_eplb_plan(const int32_t *counts, int64_t E, int64_t n_slots,
+                  int64_t n_ranks, int32_t *rep, int32_t *rep_first,
+                  int32_t *rep_slot, int32_t *slot_expert, int32_t *slot_copy,
+                  hipStream_t stream);
+
+/*
+ * moe_permute_replicated - moe_permute onto this rank's slots [s_begin,
+ * s_begin + n_slots) of a plan, for the current routing topk_idx [T, k]:
+ * with n_e the current number of entries routed to expert e, copy i of its r
+ * copies takes the entries at positions [floor(i n_e / r), floor((i+1) n_e /
+ * r)) among e's entries in ascending flat order f = t*k + j (a hot expert's
+ * rows are split evenly among its copies); inside a slot entries keep
+ * ascending f.  Outputs as moe_permute with the local slots in place of the
+ * local experts: counts [n_slots], offsets [n_slots + 1], row_src, inv
+ * (-1 for entries of other ranks' slots), x_perm, s_perm (topk_w of each row;
+ * required when topk_w is given).  Indices outside [0, E) are dropped and set
+ * MOE_DEVERR_EXPERT_INDEX in the workspace's error word.
+ * rep_first, rep_slot, slot_expert, slot_copy: a plan of moe_eplb_plan for
+ * E experts on S slots; 0 <= s_begin <= S - n_slots.
+ * workspace: moe_permute_replicated_workspace_bytes(T, k, E, n_slots).
+ * Limits: T >= 1, 1 <= k <= 32, T*k < 2^31, E <= S <= 4096, H as for
+ * moe_permute.
+ */
+size_t moe_permute_replicated_workspace_bytes(int64_t T, int64_t k, int64_t E,
+                                              int64_t n_slots);
+int moe_permute_replicated(const int32_t *topk_idx, const float *topk_w,
+                           const void *x, int64_t T, int64_t k, int64_t H,
+                           int dtype, int64_t E, int64_t S,
+                           const int32_t *rep_first, const int32_t *rep_slot,
+                           const int32_t *slot_expert,
+                           const int32_t *slot_copy, int64_t s_begin,
+                           int64_t n_slots, void *x_perm, float *s_perm,
+                           int32_t *row_src, int32_t *inv, int32_t *counts,
+                           int32_t *offsets, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * moe_grouped_ffn_slots - moe_grouped_ffn over slots whose weights are
+ * looked up per slot: slot g (rows [offsets[g], offsets[g+1])) uses the
+ * stacked weights of expert slot_expert[g] (device int32 [n_slots], values
+ * in [0, n_experts); out-of-range values are clamped and set
+ * MOE_DEVERR_EXPERT_INDEX).  The copies of one expert on a rank share its
+ * weights.  bf16 only.  Workspace: moe_grouped_ffn_workspace_bytes(R_cap,
+ * n_slots, H, I, dtype).  Other arguments as for moe_grouped_ffn.
+ */
+int moe_grouped_ffn_slots(const void *x_perm, const int32_t *offsets,
+                          const float *s_perm, int64_t n_slots,
+                          const int32_t *slot_expert, int64_t n_experts,
+                          int64_t R_cap, int64_t H, int64_t I,
+                          const void *w_gate, const void *w_up,
+                          const void *w_down, int dtype, void *a, void *y,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream);
+
+/*
  * moe_unpermute_combine - bring expert outputs back to token order and add
  * them up (Wide-EP explainer, 前提:MoEとは and 前提条件:GPU間の高速通信):
  *   out[t] = sum over j ascending with inv[t,j] >= 0 of c_tj * y[inv[t,j]]

@@ -67,6 +67,15 @@ def lib():
                                             vp, vp]
         L.moe_grouped_ffn_loop.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64,
                                            vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_eplb_plan.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.moe_permute_replicated_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.moe_permute_replicated_workspace_bytes.restype = sz
+        L.moe_permute_replicated.argtypes = [vp, vp, vp, i64, i64, i64, i32,
+                                             i64, i64, vp, vp, vp, vp, i64, i64, vp,
+                                             vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_grouped_ffn_slots.argtypes = [vp, vp, vp, i64, vp, i64, i64, i64,
+                                            i64, vp, vp, vp, i32, vp, vp, vp,
+                                            sz, vp]
         L.moe_debug_sync.argtypes = [vp]
         L.moe_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
         L.moe_permute_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64,
@@ -312,6 +321,71 @@ def grouped_ffn_loop(x_perm, offsets, host_counts, s_perm, w_gate, w_up,
           n_local, R_cap, H, I, _p(w_gate), _p(w_up), _p(w_down),
           _dt(x_perm), _p(a), _p(y), _p(workspace), workspace.numel(),
           _stream(stream))
+    return a, y
+
+
+# ---------------------------------------------------------------- EPLB
+
+
+def eplb_plan(counts, n_slots, n_ranks, stream=None):
+    """Placement of len(counts) experts on n_slots slots over n_ranks ranks
+    from observed per-expert loads (device int32 [E]).  Returns a dict of
+    device int32 tensors: rep, rep_first, rep_slot, slot_expert, slot_copy."""
+    E = counts.numel()
+    dev = counts.device
+    plan = dict(rep=torch.empty(E, dtype=torch.int32, device=dev),
+                rep_first=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                rep_slot=torch.empty(n_slots, dtype=torch.int32, device=dev),
+                slot_expert=torch.empty(n_slots, dtype=torch.int32, device=dev),
+                slot_copy=torch.empty(n_slots, dtype=torch.int32, device=dev))
+    _call("moe_eplb_plan", _p(counts), E, n_slots, n_ranks, _p(plan["rep"]),
+          _p(plan["rep_first"]), _p(plan["rep_slot"]), _p(plan["slot_expert"]),
+          _p(plan["slot_copy"]), _stream(stream))
+    return plan
+
+
+def permute_replicated(topk_idx, x, plan, s_begin, n_slots, topk_w=None,
+                       out=None, stream=None, *, E):
+    """Dispatch of the current routing to the slots [s_begin, s_begin +
+    n_slots) of a plan (the rows of an expert's copies split evenly).
+    Returns a PermuteOut whose counts/offsets index the local slots."""
+    T, k = topk_idx.shape
+    H = x.shape[1] if x is not None else 0
+    dtype = x.dtype if x is not None else torch.bfloat16
+    dev = topk_idx.device
+    if out is None:
+        out = PermuteOut(T, k, max(H, 1), n_slots, dtype, dev,
+                         with_x=x is not None)
+        nb = lib().moe_permute_replicated_workspace_bytes(T, k, E, n_slots)
+        out.workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
+    _call("moe_permute_replicated", _p(topk_idx), _p(topk_w), _p(x), T, k, H,
+          _DT[dtype], E, plan["rep_slot"].numel(), _p(plan["rep_first"]),
+          _p(plan["rep_slot"]),
+          _p(plan["slot_expert"]), _p(plan["slot_copy"]), s_begin, n_slots,
+          _p(out.x_perm), _p(out.s_perm) if topk_w is not None else None,
+          _p(out.row_src), _p(out.inv), _p(out.counts), _p(out.offsets),
+          _p(out.workspace), out.workspace.numel(), _stream(stream))
+    return out
+
+
+def grouped_ffn_slots(x_perm, offsets, s_perm, slot_expert, w_gate, w_up,
+                      w_down, a=None, y=None, workspace=None, stream=None):
+    """grouped_ffn over slots; slot g uses the weights of expert
+    slot_expert[g] (device int32) of the stacked [n_experts, ...] weights."""
+    R_cap, H = x_perm.shape
+    n_slots = slot_expert.numel()
+    n_experts, I, _ = w_gate.shape
+    if a is None:
+        a = torch.empty((R_cap, I), dtype=x_perm.dtype, device=x_perm.device)
+    if y is None:
+        y = torch.empty((R_cap, H), dtype=x_perm.dtype, device=x_perm.device)
+    if workspace is None:
+        workspace = ffn_workspace(R_cap, n_slots, H, I, x_perm.dtype,
+                                  x_perm.device)
+    _call("moe_grouped_ffn_slots", _p(x_perm), _p(offsets), _p(s_perm),
+          n_slots, _p(slot_expert), n_experts, R_cap, H, I, _p(w_gate),
+          _p(w_up), _p(w_down), _dt(x_perm), _p(a), _p(y), _p(workspace),
+          workspace.numel(), _stream(stream))
     return a, y
 
 

@@ -301,6 +301,91 @@ int moe_grouped_ffn_loop(const void *x_perm, const int32_t *offsets,
       (int32_t *)workspace, num_cus(), stream));
 }
 
+int moe_eplb_plan(const int32_t *counts, int64_t E, int64_t n_slots,
+                  int64_t n_ranks, int32_t *rep, int32_t *rep_first,
+                  int32_t *rep_slot, int32_t *slot_expert, int32_t *slot_copy,
+                  hipStream_t stream) {
+  if (E < 1 || E > 1024 || n_slots < E || n_slots > 4096 || n_ranks < 1 ||
+      n_ranks > 1024 || n_slots % n_ranks != 0)
+    return MOE_E_SHAPE;
+  if (!counts || !rep || !rep_first || !rep_slot || !slot_expert || !slot_copy)
+    return MOE_E_ARG;
+  return status_of(moe::launch_eplb_plan(counts, (int)E, (int)n_slots,
+                                         (int)n_ranks, rep, rep_first, rep_slot,
+                                         slot_expert, slot_copy, stream));
+}
+
+size_t moe_permute_replicated_workspace_bytes(int64_t T, int64_t k, int64_t E,
+                                              int64_t n_slots) {
+  if (T < 0 || k < 1 || E < 1 || n_slots < 1) return 0;
+  return moe::permute_replicated_workspace_bytes(T, k, E, n_slots);
+}
+
+int moe_permute_replicated(const int32_t *topk_idx, const float *topk_w,
+                           const void *x, int64_t T, int64_t k, int64_t H,
+                           int dtype, int64_t E, int64_t S,
+                           const int32_t *rep_first, const int32_t *rep_slot,
+                           const int32_t *slot_expert,
+                           const int32_t *slot_copy, int64_t s_begin,
+                           int64_t n_slots, void *x_perm, float *s_perm,
+                           int32_t *row_src, int32_t *inv, int32_t *counts,
+                           int32_t *offsets, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  if (dtype != MOE_DT_F32 && dtype != MOE_DT_BF16) return MOE_E_ARG;
+  if (T < 1 || k < 1 || k > 32 || E < 1 || E > 4096 || S < E || S > 4096 ||
+      n_slots < 1 || s_begin < 0 || s_begin > S - n_slots)
+    return MOE_E_SHAPE;
+  if (T * k >= kMaxRows) return MOE_E_SHAPE;
+  if (!topk_idx || !rep_first || !rep_slot || !slot_expert || !slot_copy ||
+      !row_src || !inv || !counts || !offsets)
+    return MOE_E_ARG;
+  int64_t row_bytes = 0;
+  if (x != nullptr) {
+    if (x_perm == nullptr) return MOE_E_ARG;
+    const int64_t esz = dtype == MOE_DT_BF16 ? 2 : 4;
+    if (H < 1 || (H * esz) % 16 != 0) return MOE_E_SHAPE;
+    if (!aligned16(x) || !aligned16(x_perm)) return MOE_E_ALIGN;
+    row_bytes = H * esz;
+  }
+  if (topk_w && !s_perm) return MOE_E_ARG;
+  const size_t need = moe::permute_replicated_workspace_bytes(T, k, E, n_slots);
+  if (workspace == nullptr || workspace_bytes < need) return MOE_E_WORKSPACE;
+  if (!aligned16(workspace)) return MOE_E_ALIGN;
+  return status_of(moe::launch_permute_replicated(
+      topk_idx, topk_w, x, T, k, row_bytes, E, rep_first, rep_slot,
+      slot_expert, slot_copy, s_begin, n_slots, x_perm, s_perm, row_src, inv,
+      counts, offsets, workspace, num_cus(), stream));
+}
+
+int moe_grouped_ffn_slots(const void *x_perm, const int32_t *offsets,
+                          const float *s_perm, int64_t n_slots,
+                          const int32_t *slot_expert, int64_t n_experts,
+                          int64_t R_cap, int64_t H, int64_t I,
+                          const void *w_gate, const void *w_up,
+                          const void *w_down, int dtype, void *a, void *y,
+                          void *workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  int st = check_ffn(offsets, n_slots, R_cap, H, I, dtype, workspace,
+                     workspace_bytes);
+  if (st != MOE_OK) return st;
+  if (dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
+  if (n_experts < 1 || n_experts > (1 << 20)) return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!slot_expert || !x_perm || !w_gate || !w_up || !w_down || !a || !y)
+    return MOE_E_ARG;
+  if (!all_aligned16({x_perm, w_gate, w_up, w_down, a, y})) return MOE_E_ALIGN;
+  hipError_t err = moe::launch_gate_up_bf16(
+      (const uint16_t *)x_perm, offsets, s_perm, (int)n_slots, R_cap, (int)H,
+      (int)I, (const uint16_t *)w_gate, (const uint16_t *)w_up, (uint16_t *)a,
+      (int32_t *)workspace, num_cus(), stream, nullptr, 1, 1, slot_expert,
+      (int)n_experts);
+  if (err != hipSuccess) return MOE_E_HIP;
+  return status_of(moe::launch_down_bf16(
+      (const uint16_t *)a, offsets, (int)n_slots, R_cap, (int)H, (int)I,
+      (const uint16_t *)w_down, (uint16_t *)y, (int32_t *)workspace, num_cus(),
+      stream, slot_expert, (int)n_experts));
+}
+
 int moe_unpermute_combine(const void *y, const int32_t *inv,
                           const float *topk_w, int64_t T, int64_t k,
                           int64_t H, int dtype, void *out,

@@ -63,6 +63,8 @@ struct GemmArgs {
   int a_div, a_rows_max;    //   min(a_rows[r] / a_div, a_rows_max); or null
   int single_rows;          // rows of the single group (offsets == null)
   int r_cap;                // row capacity: segments are cut at it
+  const int32_t *group_w;   // weights of group g: stacked expert group_w[g]
+  int n_w;                  //   (of n_w, clamped), or g when null
   int G;                    // groups
   int N;                    // output columns (a-columns for SWIGLU)
   int K;
@@ -83,6 +85,7 @@ constexpr int kSmallRows = 64;
 // offsets run past it or decrease, else 0.  One block.
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     const int32_t *__restrict__ offsets, int G, int r_cap, int32_t *err,
+    const int32_t *__restrict__ group_w, int n_w,
     int bm_small, int nt_small,
     int bm_wide, int nt_wide, int bm_narrow, int nt_narrow, int wide_min,
     int narrow_cap, int32_t *__restrict__ prefix_small,
@@ -109,7 +112,8 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     int32_t t[3];
     tiles(e, t[0], t[1], t[2]);
     for (int c = 0; c < 3; ++c) s[c] += t[c];
-    bad |= seg_bad(offsets, e, r_cap);
+    bad |= seg_bad(offsets, e, r_cap) ? kDevErrRows : 0;
+    if (group_w && (uint32_t)group_w[e] >= (uint32_t)n_w) bad |= kDevErrExpertIndex;
   }
   // Inclusive scan of s over the block: lane shuffles inside each
   // wavefront, then the 16 wavefront totals through LDS (one barrier).
@@ -155,8 +159,13 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     prefix_wide[G] = narrow ? 0 : total[1];
     if (prefix_narrow) prefix_narrow[G] = narrow ? total[2] : 0;
   }
-  bad = __syncthreads_or(bad);
-  if (tid == 0) *err = bad ? kDevErrRows : 0;
+  // OR of the error bits over the block
+  __shared__ int32_t bad_or;
+  if (tid == 0) bad_or = 0;
+  __syncthreads();
+  if (bad) atomicOr(&bad_or, bad);
+  __syncthreads();
+  if (tid == 0) *err = bad_or;
 }
 
 // Wait until at most N of this wavefront's vector-memory loads are in flight
@@ -349,7 +358,8 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
           base = p.B0;
         }
         col = min(col, p.N - 1);
-        gsrc[i] = (const char *)(base + (int64_t)e * p.b_stride + (int64_t)col * K + kc * 8);
+        const int we = p.group_w ? min(max(p.group_w[e], 0), p.n_w - 1) : e;
+        gsrc[i] = (const char *)(base + (int64_t)we * p.b_stride + (int64_t)col * K + kc * 8);
       }
     }
     const uint32_t wave_off = (uint32_t)(wid * L * 64 * 16);
@@ -517,7 +527,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
   int32_t *pre_s = tile_ws + kErrHeaderBytes / 4;
   int32_t *pre_w = pre_s + (p.G + 1);
   int32_t *pre_n = pre_s + 2 * (p.G + 1);
-  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.r_cap, errw, 64, nt_s, WBM, nt_w,
+  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.r_cap, errw, p.group_w, p.n_w, 64, nt_s, WBM, nt_w,
                                       NBM, nt_n, wide_min, narrow_cap, pre_s,
                                       pre_w, wide_sure ? nullptr : pre_n);
   hipError_t err = hipGetLastError();
@@ -558,8 +568,10 @@ hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                int H, int I, const uint16_t *w_gate,
                                const uint16_t *w_up, uint16_t *a,
                                int32_t *tile_ws, int num_cus, hipStream_t s,
-                               const int32_t *row_src, int k, int64_t T) {
+                               const int32_t *row_src, int k, int64_t T,
+                               const int32_t *group_w, int n_w) {
   GemmArgs p{};
+  p.group_w = group_w; p.n_w = n_w;
   p.A = x_perm; p.B0 = w_gate; p.B1 = w_up;
   p.a_rows = row_src; p.a_div = k; p.a_rows_max = (int)(T - 1);
   p.b_stride = (int64_t)I * H;
@@ -571,8 +583,10 @@ hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
 hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
                             int n_local, int64_t R_cap, int H, int I,
                             const uint16_t *w_down, uint16_t *y,
-                            int32_t *tile_ws, int num_cus, hipStream_t s) {
+                            int32_t *tile_ws, int num_cus, hipStream_t s,
+                            const int32_t *group_w, int n_w) {
   GemmArgs p{};
+  p.group_w = group_w; p.n_w = n_w;
   p.A = a; p.B0 = w_down; p.B1 = nullptr;
   p.b_stride = (int64_t)H * I;
   p.C = y; p.ldc = H;

@@ -36,21 +36,46 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
                           int32_t *counts, int32_t *offsets, void *ws,
                           int num_cus, hipStream_t s);
 
+// x_perm[r] = x[row_src[r] / k] for r < *R_ptr (16-byte vectors).
+hipError_t launch_permute_gather(const void *x, int64_t row_bytes, int64_t k,
+                                 const int32_t *row_src, const int32_t *R_ptr,
+                                 void *x_perm, int64_t F, int num_cus,
+                                 hipStream_t s);
+
+// ---- expert-parallel load balancing ----
+hipError_t launch_eplb_plan(const int32_t *counts, int E, int S, int G,
+                            int32_t *rep, int32_t *rep_first,
+                            int32_t *rep_slot, int32_t *slot_expert,
+                            int32_t *slot_copy, hipStream_t s);
+size_t permute_replicated_workspace_bytes(int64_t T, int64_t k, int64_t E,
+                                          int64_t n_slots);
+hipError_t launch_permute_replicated(
+    const int32_t *idx, const float *w, const void *x, int64_t T, int64_t k,
+    int64_t row_bytes, int64_t E, const int32_t *rep_first,
+    const int32_t *rep_slot, const int32_t *slot_expert,
+    const int32_t *slot_copy, int64_t s_begin, int64_t n_slots, void *x_perm,
+    float *s_perm, int32_t *row_src, int32_t *inv, int32_t *counts,
+    int32_t *offsets, void *ws, int num_cus, hipStream_t s);
+
 // Workspace of one grouped GEMM launch: the error header and three tile
 // prefixes of n_local + 1.
 size_t gemm_workspace_bytes(int64_t n_local);
 
+// group_w (device [n_local] or null): group g uses the weights of stacked
+// expert group_w[g] (of n_w); null: expert g.
 hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                const float *s_perm, int n_local, int64_t R_cap,
                                int H, int I, const uint16_t *w_gate,
                                const uint16_t *w_up, uint16_t *a,
                                int32_t *tile_ws, int num_cus, hipStream_t s,
                                const int32_t *row_src = nullptr,
-                               int k = 1, int64_t T = 1);
+                               int k = 1, int64_t T = 1,
+                               const int32_t *group_w = nullptr, int n_w = 0);
 hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
                             int n_local, int64_t R_cap, int H, int I,
                             const uint16_t *w_down, uint16_t *y,
-                            int32_t *tile_ws, int num_cus, hipStream_t s);
+                            int32_t *tile_ws, int num_cus, hipStream_t s,
+                            const int32_t *group_w = nullptr, int n_w = 0);
 
 // The grouped FFN issued expert by expert (gate/up, then down, per expert
 // with host_counts[e] > 0), each launch one group of the same kernels.

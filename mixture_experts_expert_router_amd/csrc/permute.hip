@@ -187,6 +187,18 @@ __global__ __launch_bounds__(256) void permute_gather_kernel(
   }
 }
 
+hipError_t launch_permute_gather(const void *x, int64_t row_bytes, int64_t k,
+                                 const int32_t *row_src, const int32_t *R_ptr,
+                                 void *x_perm, int64_t F, int num_cus,
+                                 hipStream_t s) {
+  int64_t grid = F < (int64_t)num_cus * 8 ? F : (int64_t)num_cus * 8;
+  if (grid < 1) grid = 1;
+  permute_gather_kernel<<<(unsigned)grid, 256, 0, s>>>(
+      (const uint4 *)x, row_bytes / 16, (int)k, row_src, R_ptr,
+      (uint4 *)x_perm);
+  return hipGetLastError();
+}
+
 int permute_chunk(int64_t F, int64_t n_local) {
   (void)F;
   return n_local <= 64 ? 256 : 1024;
@@ -251,14 +263,9 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
     permute_scatter_kernel<1024><<<nblk, 64, lds, s>>>(
         idx, w, F, (int)e_begin, (int)n_local, nbits, nblk, hist, row_src,
         inv, (w ? s_perm : nullptr));
-  if (x && x_perm) {
-    const int64_t vecs = row_bytes / 16;
-    int64_t grid = F < (int64_t)num_cus * 8 ? F : (int64_t)num_cus * 8;
-    if (grid < 1) grid = 1;
-    permute_gather_kernel<<<(unsigned)grid, 256, 0, s>>>(
-        (const uint4 *)x, vecs, (int)k, row_src, offsets + n_local,
-        (uint4 *)x_perm);
-  }
+  if (x && x_perm)
+    return launch_permute_gather(x, row_bytes, k, row_src, offsets + n_local,
+                                 x_perm, F, num_cus, s);
   return hipGetLastError();
 }
 

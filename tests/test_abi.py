@@ -135,6 +135,32 @@ def test_ffn_loop_validation(L):
     assert call(x=P_ODD) == E_ALIGN
 
 
+def test_eplb_validation(L):
+    f = L.moe_eplb_plan
+    assert f(P, 0, 8, 1, P, P, P, P, P, None) == E_SHAPE       # E < 1
+    assert f(P, 8, 7, 1, P, P, P, P, P, None) == E_SHAPE       # slots < E
+    assert f(P, 8, 10, 4, P, P, P, P, P, None) == E_SHAPE      # 10 % 4 != 0
+    assert f(P, 1025, 2048, 2, P, P, P, P, P, None) == E_SHAPE
+    assert f(None, 8, 8, 2, P, P, P, P, P, None) == E_ARG
+    g = L.moe_permute_replicated
+    ws = L.moe_permute_replicated_workspace_bytes(16, 2, 8, 4)
+    assert ws > 0
+    args = [P, None, None, 16, 2, 0, BF16, 8, 12, P, P, P, P, 0, 4, None, None,
+            P, P, P, P, P, ws, None]
+    bad = list(args); bad[-2] = ws - 1
+    assert g(*bad) == E_WS
+    bad = list(args); bad[9] = None
+    assert g(*bad) == E_ARG
+    bad = list(args); bad[13] = 9                              # s_begin + n_slots > S
+    assert g(*bad) == E_SHAPE
+    bad = list(args); bad[8] = 7                               # S < E
+    assert g(*bad) == E_SHAPE
+    h = L.moe_grouped_ffn_slots
+    fws = L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)
+    assert h(P, P, None, 4, None, 8, 64, 128, 128, P, P, P, BF16, P, P, P, fws, None) == E_ARG
+    assert h(P, P, None, 4, P, 8, 64, 128, 128, P, P, P, F32, P, P, P, fws, None) == 5
+
+
 def test_ffn_validation(L):
     g = L.moe_grouped_gate_up
     ws = L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)
