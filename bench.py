@@ -423,6 +423,8 @@ def main():
     ap.add_argument("--no-extra", action="store_true",
                     help="default workload only: skip the EP8 share, the EP64 "
                          "share and the MXFP8 step timed after it")
+    ap.add_argument("--no-eplb", action="store_true",
+                    help="skip the EP8 load-balancing comparison of the full layer")
     ap.add_argument("--no-loop", action="store_true",
                     help="skip the per-expert-loop comparison of the grouped FFN")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -520,6 +522,92 @@ def loop_vs_grouped(wl, x, topk_idx, topk_w, wcopies, steps, dev):
     return out
 
 
+def eplb_ep8(wl, x, topk_idx, topk_w, weights, steps, dev, n_ranks=8):
+    """The full layer's routing split over n_ranks EP ranks, each rank's
+    share timed alone on this GPU (gate/up + down of its rows; HIP events,
+    mean over `steps`).  In EP the ranks run at once, so the busiest rank
+    sets the layer's time.  Two placements of the same routing:
+      "as_drawn": experts keep their numbers (the Zipf ranks are a seeded
+        shuffle, so hot experts are spread over the ranks);
+      "hot_first": experts renumbered by decreasing load, so that plain EP
+        puts the hottest E/G experts on rank 0 (the concentration the EPLB
+        section describes).
+    For each: plain EP (rank g owns experts [g E/G, (g+1) E/G)), the EPLB
+    placement without spare slots, and EPLB with E/8 spare slots; the plans
+    are made from this batch's per-expert counts."""
+    T, k, H, I, E = wl.T, wl.k, wl.H, wl.I, wl.E
+    wg, wu, wd = weights
+    F = T * k
+    a = torch.empty((F, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((F, H), dtype=torch.bfloat16, device=dev)
+    st = torch.cuda.current_stream()
+
+    def timed(fn):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(steps):
+            fn()
+        e1.record(st)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    def shares(idx, counts, S):
+        """Per-rank rows and FFN times; S = None: plain EP."""
+        rows, ms, perm_ms, plan_ms = [], [], [], None
+        if S is not None:
+            plan = moe.eplb_plan(counts, S, n_ranks)
+            plan_ms = timed(lambda: moe.eplb_plan(counts, S, n_ranks))
+        per = (E if S is None else S) // n_ranks
+        ws = moe.ffn_workspace(F, per, H, I, torch.bfloat16, dev)
+        for g in range(n_ranks):
+            if S is None:
+                p = moe.permute(idx, x, g * per, per, topk_w=topk_w, E=E)
+                sl = slice(g * per, (g + 1) * per)
+                fn = lambda: moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, wg[sl],
+                                             wu[sl], wd[sl], a=a, y=y, workspace=ws)
+            else:
+                p = moe.permute_replicated(idx, x, plan, g * per, per,
+                                           topk_w=topk_w, E=E)
+                perm_ms.append(timed(lambda: moe.permute_replicated(
+                    idx, x, plan, g * per, per, topk_w=topk_w, E=E, out=p)))
+                se = plan["slot_expert"][g * per:(g + 1) * per].contiguous()
+                fn = lambda: moe.grouped_ffn_slots(p.x_perm, p.offsets, p.s_perm, se,
+                                                   wg, wu, wd, a=a, y=y, workspace=ws)
+            torch.cuda.synchronize()
+            rows.append(int(p.offsets[-1].item()))
+            ms.append(timed(fn))
+            del p
+        r = {"slots": E if S is None else S,
+             "rows_per_rank": rows,
+             "rows_max_over_mean": round(max(rows) / (sum(rows) / n_ranks), 4),
+             "ffn_ms_max_rank": round(max(ms), 4),
+             "ffn_ms_mean_rank": round(sum(ms) / n_ranks, 4)}
+        if S is not None:
+            r["plan_ms"] = round(plan_ms, 4)
+            r["permute_ms_max_rank"] = round(max(perm_ms), 4)
+        return r
+
+    counts = torch.bincount(topk_idx.reshape(-1).long(), minlength=E).to(torch.int32)
+    order = torch.argsort(counts, descending=True, stable=True)
+    relabel = torch.empty_like(order)
+    relabel[order] = torch.arange(E, device=dev)
+    out = {"ranks": n_ranks, "experts": E}
+    for name, idx in (("as_drawn", topk_idx),
+                      ("hot_first", relabel[topk_idx.long()].to(torch.int32).contiguous())):
+        c = torch.bincount(idx.reshape(-1).long(), minlength=E).to(torch.int32)
+        res = {"plain_ep": shares(idx, c, None),
+               "eplb_placement": shares(idx, c, E),
+               "eplb_spare": shares(idx, c, E + E // 8)}
+        base = res["plain_ep"]["ffn_ms_max_rank"]
+        for key in ("eplb_placement", "eplb_spare"):
+            res[key]["max_rank_speedup_over_plain"] = round(base / res[key]["ffn_ms_max_rank"], 3)
+        out[name] = res
+    out["what"] = ("each rank's share of this batch timed alone on this GPU; plans made "
+                   "from this batch's counts (the loads they balance)")
+    return out
+
+
 def run_bf16(args, wl, dev, cpu=True, loop=True):
     # Weight copies rotate across steps when the weights are small enough for
     # the 256 MB last-level cache to hold them between steps.
@@ -611,6 +699,11 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
+    res_eplb = None
+    if wl.n_local == wl.E and not args.no_eplb:
+        log(f"{wl.name}: EP8 shares, plain and balanced")
+        res_eplb = eplb_ep8(wl, d["x"], topk_idx, topk_w, wcopies[0],
+                            args.steps, dev)
     if loop:
         log(f"{wl.name}: per-expert loop against the grouped FFN")
         res_loop = loop_vs_grouped(wl, d["x"], topk_idx, topk_w, wcopies,
@@ -678,6 +771,8 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
     }
     if loop:
         res["loop_vs_grouped"] = res_loop
+    if res_eplb is not None:
+        res["eplb_ep8"] = res_eplb
     if cpu:
         log(f"cpu baseline: oracle on {args.cpu_tokens} tokens")
         res["cpu_baseline"] = cpu_baseline(wl, inp, min(args.cpu_tokens, T))
