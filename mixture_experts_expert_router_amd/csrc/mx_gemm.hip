@@ -217,6 +217,10 @@ __device__ __forceinline__ void mx_quant_rows_f32(const float *l, uint8_t *q,
                                                   int rows, int lane) {
   constexpr int BPR = W / 32;
   static_assert((NROWS * BPR) % 64 == 0, "region");
+  // uniform bases (scalar registers) and 32-bit lane offsets: no 64-bit
+  // per-lane address has to stay live across the loop
+  uint8_t *qb = mx_uniform(q + grow0 * ldq + col0);
+  uint8_t *sbb = mx_uniform(qs + grow0 * ldqs + col0 / 32);
 #pragma unroll 1
   for (int it = 0; it < NROWS * BPR / 64; ++it) {
     const int item = it * 64 + lane;
@@ -226,10 +230,10 @@ __device__ __forceinline__ void mx_quant_rows_f32(const float *l, uint8_t *q,
     uint32_t c[8];
     const uint32_t sb = mx_encode32_f32(v, c);
     if (arow0 + r < rows) {
-      uint4 *dst = (uint4 *)(q + (grow0 + r) * ldq + col0 + 32 * b);
+      uint4 *dst = (uint4 *)(qb + ((uint32_t)r * (uint32_t)ldq + 32u * b));
       dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
       dst[1] = make_uint4(c[4], c[5], c[6], c[7]);
-      qs[(grow0 + r) * ldqs + col0 / 32 + b] = (uint8_t)sb;
+      sbb[(uint32_t)r * (uint32_t)ldqs + b] = (uint8_t)sb;
     }
   }
 }
@@ -245,6 +249,7 @@ __device__ __forceinline__ void store_f32_as_bf16(const float *l, uint16_t *dst,
                                                   int lane) {
   constexpr int LPR = W / 8;                 // lanes per row
   constexpr int RPI = 64 / LPR;              // rows per instruction
+  uint16_t *db = mx_uniform(dst + grow0 * ld + col0);
 #pragma unroll 4
   for (int it = 0; it < NROWS / RPI; ++it) {
     const int r = it * RPI + lane / LPR;
@@ -252,22 +257,23 @@ __device__ __forceinline__ void store_f32_as_bf16(const float *l, uint16_t *dst,
     const float4 lo = *(const float4 *)(l + r * W + fphys<W>(r, c8));
     const float4 hi = *(const float4 *)(l + r * W + fphys<W>(r, c8 + 4));
     if (arow0 + r < rows && col0 + c8 < N)
-      *(uint4 *)(dst + (grow0 + r) * ld + col0 + c8) =
+      *(uint4 *)(db + ((uint32_t)r * (uint32_t)ld + (uint32_t)c8)) =
           make_uint4(pack_bf16x2(lo.x, lo.y), pack_bf16x2(lo.z, lo.w),
                      pack_bf16x2(hi.x, hi.y), pack_bf16x2(hi.z, hi.w));
   }
 }
 
 // Column-wise MX encoding straight from the MFMA accumulator layout.  v holds
-// this lane's 16 values of column (lane & 31) of a 32 x 32 block (rows
-// 8 (i / 4) + 4 h + i % 4, h = lane / 32); lane ^ 32 holds the other 16, and
-// the column's 32 values form one MX block.  Its codes go to qt[c * ldt +
-// pos0 .. + 32) (the first 16 bytes written by half 0, the rest by half 1)
-// and its scale byte to qts[c * ldts + pos0 / 32].
+// this lane's 16 values of column c = c0 + (lane & 31) of a 32 x 32 block
+// (rows 8 (i / 4) + 4 h + i % 4, h = lane / 32); lane ^ 32 holds the other
+// 16, and the column's 32 values form one MX block.  Its codes go to
+// qt[c * ldt + pos0 .. + 32) (the first 16 bytes written by half 0, the rest
+// by half 1) and its scale byte to qts[c * ldts + pos0 / 32].  The launcher
+// keeps 32 * ldt below 2^32.
 __device__ __forceinline__ void mx_quant_col_block(const float (&v)[16],
                                                    int lane, uint8_t *qt,
                                                    uint8_t *qts, int64_t ldt,
-                                                   int64_t ldts, int64_t c,
+                                                   int64_t ldts, int64_t c0,
                                                    int64_t pos0) {
   float mag = 0.f;
 #pragma unroll
@@ -284,8 +290,12 @@ __device__ __forceinline__ void mx_quant_col_block(const float (&v)[16],
   const uint32_t y0 = (uint32_t)__shfl_xor((int)x0, 32, 64);
   const uint32_t y1 = (uint32_t)__shfl_xor((int)x1, 32, 64);
   const uint4 o = h ? make_uint4(y0, d[2], y1, d[3]) : make_uint4(d[0], y0, d[1], y1);
-  *(uint4 *)(qt + c * ldt + pos0 + 16 * h) = o;
-  if (h) qts[c * ldts + pos0 / 32] = (uint8_t)(X + 127);
+  // uniform base of the block's first column, 32-bit lane offsets
+  uint8_t *cb = mx_uniform(qt + c0 * ldt + pos0);
+  uint8_t *sb = mx_uniform(qts + c0 * ldts + pos0 / 32);
+  const uint32_t c = (uint32_t)(lane & 31);
+  *(uint4 *)(cb + (c * (uint32_t)ldt + 16u * h)) = o;
+  if (h) sb[c * (uint32_t)ldts] = (uint8_t)(X + 127);
 }
 
 // fp32 g and u of 32 tile rows [ar0, ar0 + 32) x 128 columns (g_base and
@@ -437,7 +447,7 @@ __device__ __forceinline__ void mx_swiglu_bwd_block(
       lu[o] = da * s * sl;                            // du
       v[r] = mrow0 + row < rows ? s * sl * u : 0.f;   // a (padding rows: 0)
     }
-    const int64_t c = col0 + n * 32 + (lane & 31);
+    const int64_t c = col0 + n * 32;
     if (p.t2) mx_quant_col_block(v, lane, p.t2, p.t2s, p.ldt, p.ldts, c, pos0);
     if (p.t0) {
 #pragma unroll
@@ -460,8 +470,9 @@ __device__ __forceinline__ void mx_swiglu_bwd_block(
   const float tot = mx_sum16_over32(part, lane);
   const int r = (lane & 31) >> 1;
   const int rr = 8 * (r >> 2) + 4 * h + (r & 3);
-  if ((lane & 1) == 0 && mrow0 + rr < rows)
-    p.ds_part[(int64_t)(row0 + mrow0 + rr) * (p.NT * WN) + nt * WN + wn] = tot;
+  const int ntw = p.NT * WN;
+  float *dp = mx_uniform(p.ds_part + (int64_t)(row0 + mrow0) * ntw + nt * WN + wn);
+  if ((lane & 1) == 0 && mrow0 + rr < rows) dp[(uint32_t)rr * (uint32_t)ntw] = tot;
 }
 
 template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES, int BKB>
@@ -735,10 +746,23 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     const int64_t col0 = (int64_t)nt * (BN / 2) + brow0 / 2;
     const int64_t grow0 = row0 + arow0;
     float *gp = p.gu ? p.gu + grow0 * p.ldgu + col0 : nullptr;
-#define MX_SW_BLOCK(m) \
-    if constexpr (MB > (m)) mx_swiglu_block<NB>(acc[m], (m) * 32, lane, (m) < 2 ? s_lo : s_hi, la, gp, p.ldgu, p.N, arow0, rows);
-    MX_SW_BLOCK(0) MX_SW_BLOCK(1) MX_SW_BLOCK(2) MX_SW_BLOCK(3)
-#undef MX_SW_BLOCK
+    // One 32-row block per pass (rolled; see the backward epilogue below).
+    const int lane_id = lane;
+#pragma unroll 1
+    for (int m = 0; m < MB; ++m) {
+      int ln = lane_id;
+      asm volatile("" : "+v"(ln));
+      f32x16 cur[NB];
+      switch (m) {
+#define MX_FWD_COPY(mm) \
+        case mm: \
+          _Pragma("unroll") for (int n = 0; n < NB; ++n) cur[n] = acc[mm][n]; \
+          break;
+        MX_FWD_COPY(0) MX_FWD_COPY(1) MX_FWD_COPY(2) MX_FWD_COPY(3)
+#undef MX_FWD_COPY
+      }
+      mx_swiglu_block<NB>(cur, m * 32, ln, m < 2 ? s_lo : s_hi, la, gp, p.ldgu, p.N, arow0, rows);
+    }
     __syncthreads();
     store_f32_as_bf16<64, 128>(la, (uint16_t *)p.C, p.ldc, col0, p.N, grow0, arow0, rows, lane);
     if (p.q) mx_quant_rows_f32<64, 128>(la, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, arow0, rows, lane);
@@ -754,6 +778,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     // padded position of tile row 0 in the column-wise copies: tile rows start
     // at the segment's first row + mt * BM, padded at tpad[e] + mt * BM
     const int64_t pbase = p.tpad ? (int64_t)p.tpad[e] + (row0 - r_begin) : 0;
+    const int lane_id = lane;
     // One 32-row block per pass, not unrolled: the pass copies its block's
     // accumulators (constant indices in each case of the switch) and the
     // rest of the body exists once, which keeps the live values in bounds.
@@ -761,6 +786,11 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     for (int m = 0; m < MB; ++m) {
       const int ar0 = arow0 + 32 * m;
       const int64_t grow0 = row0 + ar0;
+      // An opaque copy of the lane index: the LDS and global offsets derived
+      // from it are recomputed in each pass instead of being hoisted out of
+      // the loop and kept live (which spills them).
+      int lane = lane_id;
+      asm volatile("" : "+v"(lane));
       f32x16 cur[NB];
       switch (m) {
 #define MX_BWD_COPY(mm) \
@@ -857,6 +887,11 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
                                     d.tile_ws, d.err);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  // 32-bit lane offsets of the epilogues' stores (row pitches of the
+  // column-wise copies, of the row-wise codes and of the outputs).
+  if ((int64_t)32 * d.ldt >= (1ll << 32) || (int64_t)256 * d.ldq >= (1ll << 32) ||
+      (int64_t)256 * d.ldc * 2 >= (1ll << 32) || (int64_t)256 * d.ldgu * 4 >= (1ll << 32))
+    return hipErrorInvalidValue;
   // SwiGLU backward: 32-bit byte offsets within a tile's rows of fp32 g|u.
   if (epi == MX_EPI_SWIGLU_BWD && (int64_t)kMxBM * d.ldgu * 4 >= (1ll << 32))
     return hipErrorInvalidValue;
