@@ -128,9 +128,12 @@ def algorithmic(wl, R, n_touched, gather=True):
                   + T * H * act)                   # out write
     if wl.router == "gemm":
         step_bytes += T * H * act + E * H * act + 2 * T * E * 4
+    # the fused FFN kernel: all weights, the rows of x, a written and read
+    # back, y written
+    fused_bytes = (w_bytes + R * H * act + 2 * R * I * act + R * H * act)
     return dict(flop_ffn=flop_ffn, flop_router=flop_router,
                 gate_up_flop=4.0 * R * H * I, gate_up_bytes=gate_up_bytes,
-                step_bytes=step_bytes)
+                fused_bytes=fused_bytes, step_bytes=step_bytes)
 
 
 def capture_steps(step_fns):
@@ -425,6 +428,10 @@ def main():
                          "share and the MXFP8 step timed after it")
     ap.add_argument("--no-eplb", action="store_true",
                     help="skip the EP8 load-balancing comparison of the full layer")
+    ap.add_argument("--ffn", choices=("auto", "grouped", "fused"), default="auto",
+                    help="bf16 FFN path: the grouped GEMMs, the fused one-launch "
+                         "kernel, or auto (fused when the expected rows per "
+                         "expert, T*k/E, are at most 32)")
     ap.add_argument("--no-loop", action="store_true",
                     help="skip the per-expert-loop comparison of the grouped FFN")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -467,7 +474,8 @@ def compact(r):
     keep = ("value", "unit", "ms_per_step", "ms_per_step_eager", "dtype",
             "rows_per_s", "step_hbm_gbs", "step_hbm_frac", "step_mfma_frac",
             "step_mfma_frac_fp8", "step_mfma_frac_bf16", "ffn_ms_events",
-            "step_ms_events", "loop_vs_grouped", "master_quant_ms")
+            "step_ms_events", "loop_vs_grouped", "fused_vs_grouped",
+            "master_quant_ms")
     out = {k: r[k] for k in keep if k in r}
     out["workload"] = r["config"]["workload"]
     out["rows"] = r["config"]["rows"]
@@ -518,6 +526,45 @@ def loop_vs_grouped(wl, x, topk_idx, topk_w, wcopies, steps, dev):
     out["what"] = ("gate/up + down on the same permuted rows; the loop issues "
                    "each expert's launches separately and reads the counts "
                    "back to the host every step")
+    del p, a, y, ws
+    return out
+
+
+def fused_vs_grouped(wl, x, topk_idx, topk_w, wcopies, steps, dev):
+    """The grouped FFN (plan + gate/up launch, plan + down launch) against
+    the fused one-launch FFN on the same permuted rows, eager launches, mean
+    over `steps` steps."""
+    T, k, H, I, n = wl.T, wl.k, wl.H, wl.I, wl.n_local
+    p = moe.PermuteOut(T, k, H, n, torch.bfloat16, dev)
+    moe.permute(topk_idx, x, wl.e_begin, n, topk_w=topk_w, out=p, E=wl.E)
+    F = T * k
+    a = torch.empty((F, I), dtype=torch.bfloat16, device=dev)
+    y = torch.empty((F, H), dtype=torch.bfloat16, device=dev)
+    ws = moe.ffn_workspace(F, n, H, I, torch.bfloat16, dev)
+
+    def grouped(i):
+        wg, wu, wd = wcopies[i % len(wcopies)]
+        moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, wg, wu, wd, a=a, y=y,
+                        workspace=ws)
+
+    def fused(i):
+        wg, wu, wd = wcopies[i % len(wcopies)]
+        moe.grouped_ffn_fused(p.x_perm, p.offsets, p.s_perm, wg, wu, wd, a=a,
+                              y=y, workspace=ws)
+
+    out = {}
+    for name, fn in (("grouped", grouped), ("fused", fused)):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            fn(i)
+        torch.cuda.synchronize()
+        out[f"{name}_ms"] = round((time.perf_counter() - t0) * 1e3 / steps, 4)
+    out["grouped_over_fused"] = round(out["grouped_ms"] / out["fused_ms"], 3)
+    out["rows_per_expert"] = round(float(p.offsets[-1].item()) / n, 2)
+    out["what"] = "gate/up + down on the same permuted rows, eager launches"
     del p, a, y, ws
     return out
 
@@ -629,6 +676,8 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
     # The full layer on one GPU reads token rows through row_src; an EP share
     # gets its rows already permuted by the dispatch, so it reads x_perm.
     gather = not args.no_gather and wl.n_local == wl.E
+    fused = (args.ffn == "fused" or
+             (args.ffn == "auto" and wl.T * wl.k <= 32 * wl.E))
     pout = moe.PermuteOut(T, k, H, wl.n_local, torch.bfloat16, dev,
                           with_x=not gather)
     a = torch.empty((F, I), dtype=torch.bfloat16, device=dev)
@@ -657,17 +706,29 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
                     wl.n_local, topk_w=topk_w, out=pout, E=wl.E)
         if timed_ev is not None:
             timed_ev[1].record(stream)
-        if gather:
-            moe.grouped_gate_up_gather(d["x"], pout.row_src, k, pout.offsets,
-                                       pout.s_perm, wg, wu, a=a, workspace=ws)
+        if fused:
+            if gather:
+                moe.grouped_ffn_fused(d["x"], pout.offsets, pout.s_perm, wg, wu,
+                                      wd, row_src=pout.row_src, k=k, a=a, y=y,
+                                      workspace=ws)
+            else:
+                moe.grouped_ffn_fused(pout.x_perm, pout.offsets, pout.s_perm,
+                                      wg, wu, wd, a=a, y=y, workspace=ws)
+            if timed_ev is not None:
+                timed_ev[2].record(stream)
+                timed_ev[3].record(stream)
         else:
-            moe.grouped_gate_up(pout.x_perm, pout.offsets, pout.s_perm, wg, wu,
-                                a=a, workspace=ws)
-        if timed_ev is not None:
-            timed_ev[2].record(stream)
-        moe.grouped_down(a, pout.offsets, wd, y=y, workspace=ws)
-        if timed_ev is not None:
-            timed_ev[3].record(stream)
+            if gather:
+                moe.grouped_gate_up_gather(d["x"], pout.row_src, k, pout.offsets,
+                                           pout.s_perm, wg, wu, a=a, workspace=ws)
+            else:
+                moe.grouped_gate_up(pout.x_perm, pout.offsets, pout.s_perm, wg,
+                                    wu, a=a, workspace=ws)
+            if timed_ev is not None:
+                timed_ev[2].record(stream)
+            moe.grouped_down(a, pout.offsets, wd, y=y, workspace=ws)
+            if timed_ev is not None:
+                timed_ev[3].record(stream)
         moe.unpermute_combine(y, pout.inv, out=out)
         if timed_ev is not None:
             timed_ev[4].record(stream)
@@ -708,6 +769,11 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
         log(f"{wl.name}: per-expert loop against the grouped FFN")
         res_loop = loop_vs_grouped(wl, d["x"], topk_idx, topk_w, wcopies,
                                    args.steps, dev)
+    res_fused = None
+    if wl.n_local < wl.E:
+        log(f"{wl.name}: fused one-launch FFN against the grouped FFN")
+        res_fused = fused_vs_grouped(wl, d["x"], topk_idx, topk_w, wcopies,
+                                     args.steps, dev)
     alg = algorithmic(wl, R, n_touched, gather)
     flop = alg["flop_ffn"] + alg["flop_router"]
     tflops = flop / (ms_step * 1e-3) / 1e12
@@ -726,6 +792,13 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(gu_tflops / BF16_PEAK_TFLOPS, 4)}
     gate_up_bound["flop_per_byte"] = round(ai, 1)
+    if fused:
+        # one kernel streams every weight once: HBM-bound at these row counts
+        f_gbs = alg["fused_bytes"] / (gate_up_ms * 1e-3) / 1e9
+        gate_up_bound = {"bound": "hbm", "achieved": round(f_gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(f_gbs / HBM_PEAK_GBS, 4),
+                         "flop_per_byte": round(alg["flop_ffn"] / alg["fused_bytes"], 1)}
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -748,6 +821,8 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
                       if wl.router == "gemm" else "routed before timing",
             "gate_up_input": "token rows gathered on load through row_src"
                              if gather else "permuted copy x_perm",
+            "ffn": "fused gate/up + down, one persistent launch" if fused
+                   else "grouped gate/up GEMM, then grouped down GEMM",
         },
         "rows_per_s": round(R / (ms_step * 1e-3), 1),
         "step_hbm_gbs": round(alg["step_bytes"] / (ms_step * 1e-3) / 1e9, 1),
@@ -759,10 +834,11 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
         "ffn_ms_events": ffn_pct,
         "ffn_tflops_p50": round(alg["flop_ffn"] / (ffn_pct["p50"] * 1e-3) / 1e12, 2),
         "roofline": dict(**gate_up_bound, **{
-            "kernel": "grouped gate/up GEMM + SwiGLU x scale",
+            "kernel": ("fused FFN (gate/up + SwiGLU x scale + down) with its plan kernel"
+                       if fused else "grouped gate/up GEMM + SwiGLU x scale"),
             "traffic": measured_traffic(wl.name),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "algorithmic_bytes": int(alg["gate_up_bytes"]),
+            "algorithmic_bytes": int(alg["fused_bytes"] if fused else alg["gate_up_bytes"]),
             "avg_ms": round(gate_up_ms, 4),
             "gbs": round(gu_gbs, 1),
             "tflops": round(gu_tflops, 2),
@@ -771,6 +847,8 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
     }
     if loop:
         res["loop_vs_grouped"] = res_loop
+    if res_fused is not None:
+        res["fused_vs_grouped"] = res_fused
     if res_eplb is not None:
         res["eplb_ep8"] = res_eplb
     if cpu:

@@ -87,9 +87,12 @@ enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 };
 enum moe_device_error {
   MOE_DEVERR_EXPERT_INDEX = 1,  /* moe_permute: a topk_idx outside [0, E);
                                    its slot was dropped (inv = -1)      */
-  MOE_DEVERR_ROWS = 2           /* grouped GEMMs: offsets decrease or run
+  MOE_DEVERR_ROWS = 2,          /* grouped GEMMs: offsets decrease or run
                                    past R_cap; rows at or past R_cap were
                                    not computed                          */
+  MOE_DEVERR_WAIT = 4           /* moe_grouped_ffn_fused: a down unit
+                                   stopped waiting for its expert's a
+                                   (a bound of seconds; not expected)    */
 };
 
 /* Human-readable name of a status code (static string, host). */
@@ -228,6 +231,40 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
                     const void *w_up, const void *w_down, int dtype, void *a,
                     void *y, void *workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * moe_grouped_ffn_fused - the computation of moe_grouped_ffn (bf16) for
+ * decode-sized shares, gate/up and down in one persistent kernel (after a
+ * one-block plan kernel).  BioNeMo MoE article, "GroupedLinear Optimizes
+ * Expert Computation in MoE Models": all experts in one operation and the
+ * fused MLP without materialised intermediates.  With few rows per expert
+ * the layer streams each weight byte for a handful of rows; one launch
+ * saves the second launch, its ramp-up and drain, and the plan in between.
+ * Work units are (expert, <= 64 rows, 64 columns of a) for gate/up and
+ * (expert, <= 64 rows, 128 columns of y) for down; a down unit starts once
+ * all of its expert's gate/up units have written their part of a.  Any row
+ * count works (more than 64 rows per expert re-read the weights once per 64
+ * rows); the grouped path is the faster one beyond a few dozen rows.
+ * x: with row_src non-NULL the token rows [T, H] (permuted row r is
+ * x[row_src[r] / k], as moe_grouped_gate_up_gather; R_cap <= T * k); with
+ * row_src NULL, x_perm [R_cap, H] (T and k unused).
+ * a [R_cap, I] and y [R_cap, H] (bf16): outputs, rows < R, the same
+ * quantities as moe_grouped_ffn (fp32 accumulation in a different order, so
+ * not the same bits).  Deterministic: repeated calls give identical bits.
+ * Offsets, s_perm and the cut at R_cap as moe_grouped_gate_up; the error
+ * word gets MOE_DEVERR_ROWS as there, and MOE_DEVERR_WAIT if a down unit
+ * gave up waiting (its rows of y are then unspecified).
+ * workspace: moe_grouped_ffn_workspace_bytes(...) bytes, 16-aligned.
+ * Limits: dtype MOE_DT_BF16 (MOE_E_UNSUPPORTED otherwise), others as
+ * moe_grouped_ffn.
+ */
+int moe_grouped_ffn_fused(const void *x, const int32_t *row_src, int64_t T,
+                          int64_t k, const int32_t *offsets,
+                          const float *s_perm, int64_t n_local, int64_t R_cap,
+                          int64_t H, int64_t I, const void *w_gate,
+                          const void *w_up, const void *w_down, int dtype,
+                          void *a, void *y, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_grouped_ffn_loop - the computation of moe_grouped_ffn (bf16 only,

@@ -67,6 +67,9 @@ def lib():
                                             vp, vp]
         L.moe_grouped_ffn_loop.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64,
                                            vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_grouped_ffn_fused.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64,
+                                            i64, i64, vp, vp, vp, i32, vp, vp,
+                                            vp, sz, vp]
         L.moe_eplb_plan.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp, vp]
         L.moe_permute_replicated_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.moe_permute_replicated_workspace_bytes.restype = sz
@@ -324,6 +327,27 @@ def grouped_ffn_loop(x_perm, offsets, host_counts, s_perm, w_gate, w_up,
     return a, y
 
 
+def grouped_ffn_fused(x, offsets, s_perm, w_gate, w_up, w_down, row_src=None,
+                      k=1, a=None, y=None, workspace=None, stream=None):
+    """grouped_ffn in one persistent launch (decode-sized shares).  With
+    row_src, x holds the token rows and permuted row r is x[row_src[r] // k]
+    (R_cap = row_src.shape[0]); without it x is x_perm [R_cap, H]."""
+    T, H = x.shape
+    R_cap = row_src.shape[0] if row_src is not None else T
+    n_local, I, _ = w_gate.shape
+    if a is None:
+        a = torch.empty((R_cap, I), dtype=x.dtype, device=x.device)
+    if y is None:
+        y = torch.empty((R_cap, H), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = ffn_workspace(R_cap, n_local, H, I, x.dtype, x.device)
+    _call("moe_grouped_ffn_fused", _p(x), _p(row_src), T, k, _p(offsets),
+          _p(s_perm), n_local, R_cap, H, I, _p(w_gate), _p(w_up), _p(w_down),
+          _dt(x), _p(a), _p(y), _p(workspace), workspace.numel(),
+          _stream(stream))
+    return a, y
+
+
 # ---------------------------------------------------------------- EPLB
 
 
@@ -405,6 +429,7 @@ def debug_sync(stream=None):
 
 DEVERR_EXPERT_INDEX = 1
 DEVERR_ROWS = 2
+DEVERR_WAIT = 4
 
 
 def read_device_error(workspace, stream=None) -> int:

@@ -40,8 +40,11 @@ int status_of(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_E_HIP; }
 
 constexpr int64_t kMaxRows = (int64_t)1 << 31;
 
-size_t tile_ws_bytes(int64_t n_local) {
-  return moe::gemm_workspace_bytes(n_local);
+// One workspace size serves every FFN entry point (grouped, per-expert
+// loop, fused).
+size_t tile_ws_bytes(int64_t n_local, int64_t R_cap, int64_t I) {
+  return std::max(moe::gemm_workspace_bytes(n_local),
+                  moe::ffn_fused_workspace_bytes(n_local, R_cap, I));
 }
 
 }  // namespace
@@ -141,9 +144,9 @@ int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
 
 size_t moe_grouped_ffn_workspace_bytes(int64_t R_cap, int64_t n_local,
                                        int64_t H, int64_t I, int dtype) {
-  (void)R_cap; (void)H; (void)I; (void)dtype;
-  if (n_local < 1) return 0;
-  return tile_ws_bytes(n_local);
+  (void)H; (void)dtype;
+  if (n_local < 1 || R_cap < 0 || I < 1) return 0;
+  return tile_ws_bytes(n_local, R_cap, I);
 }
 
 namespace {
@@ -162,7 +165,8 @@ int check_ffn(const int32_t *offsets, int64_t n_local, int64_t R_cap,
     return MOE_E_SHAPE;
   }
   if (offsets == nullptr) return MOE_E_ARG;
-  if (workspace == nullptr || workspace_bytes < tile_ws_bytes(n_local))
+  if (workspace == nullptr ||
+      workspace_bytes < tile_ws_bytes(n_local, R_cap, I))
     return MOE_E_WORKSPACE;
   if (!aligned16(workspace)) return MOE_E_ALIGN;
   return MOE_OK;
@@ -271,6 +275,31 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
   if (st != MOE_OK) return st;
   return moe_grouped_down(a, offsets, n_local, R_cap, H, I, w_down, dtype, y,
                           workspace, workspace_bytes, stream);
+}
+
+int moe_grouped_ffn_fused(const void *x, const int32_t *row_src, int64_t T,
+                          int64_t k, const int32_t *offsets,
+                          const float *s_perm, int64_t n_local, int64_t R_cap,
+                          int64_t H, int64_t I, const void *w_gate,
+                          const void *w_up, const void *w_down, int dtype,
+                          void *a, void *y, void *workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  int st = check_ffn(offsets, n_local, R_cap, H, I, dtype, workspace,
+                     workspace_bytes);
+  if (st != MOE_OK) return st;
+  if (dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
+  if (row_src) {
+    if (T < 1 || k < 1 || k > 32 || T * k >= kMaxRows || R_cap > T * k)
+      return MOE_E_SHAPE;
+  }
+  if (R_cap == 0) return MOE_OK;
+  if (!x || !w_gate || !w_up || !w_down || !a || !y) return MOE_E_ARG;
+  if (!all_aligned16({x, w_gate, w_up, w_down, a, y})) return MOE_E_ALIGN;
+  return status_of(moe::launch_ffn_fused_bf16(
+      (const uint16_t *)x, row_src, (int)k, T, offsets, s_perm, (int)n_local,
+      R_cap, (int)H, (int)I, (const uint16_t *)w_gate, (const uint16_t *)w_up,
+      (const uint16_t *)w_down, (uint16_t *)a, (uint16_t *)y,
+      (int32_t *)workspace, num_cus(), stream));
 }
 
 int moe_grouped_ffn_loop(const void *x_perm, const int32_t *offsets,

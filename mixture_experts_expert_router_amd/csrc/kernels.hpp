@@ -14,6 +14,7 @@ namespace moe {
 constexpr size_t kErrHeaderBytes = 256;
 constexpr int32_t kDevErrExpertIndex = 1;  // a top-k index outside [0, E)
 constexpr int32_t kDevErrRows = 2;         // offsets past R_cap or decreasing
+constexpr int32_t kDevErrWait = 4;         // a fused down unit stopped waiting
 
 enum GemmEpilogue { EPI_SWIGLU = 0, EPI_BF16 = 1, EPI_F32_BIAS = 2 };
 
@@ -86,6 +87,18 @@ hipError_t launch_ffn_loop_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                const uint16_t *w_down, uint16_t *a,
                                uint16_t *y, int32_t *tile_ws, int num_cus,
                                hipStream_t s);
+// Decode-sized FFN (gate/up, ScaledSwiGLU, down) in one persistent launch
+// after a plan kernel; x is gathered through row_src (x [T, H]) or, with
+// row_src null, read as x_perm [R_cap, H].
+size_t ffn_fused_workspace_bytes(int64_t n_local, int64_t R_cap, int64_t I);
+hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
+                                 int k, int64_t T, const int32_t *offsets,
+                                 const float *s_perm, int n_local,
+                                 int64_t R_cap, int H, int I,
+                                 const uint16_t *w_gate, const uint16_t *w_up,
+                                 const uint16_t *w_down, uint16_t *a,
+                                 uint16_t *y, int32_t *ws, int num_cus,
+                                 hipStream_t s);
 hipError_t launch_gate_up_f32(const float *x_perm, const int32_t *offsets,
                               const float *s_perm, int n_local, int64_t R_cap,
                               int64_t H, int64_t I, const float *w_gate,

@@ -135,6 +135,24 @@ def test_ffn_loop_validation(L):
     assert call(x=P_ODD) == E_ALIGN
 
 
+def test_ffn_fused_validation(L):
+    f = L.moe_grouped_ffn_fused
+    ws = L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)
+
+    def call(dt=BF16, R=64, x=P, rs=P, T=32, k=2, H=128, I=128, w=ws, y=P):
+        return f(x, rs, T, k, P, None, 4, R, H, I, P, P, P, dt, P, y, P, w, None)
+
+    assert call(dt=F32) == 5               # MOE_E_UNSUPPORTED
+    assert call(rs=P, T=16, k=2) == E_SHAPE   # R_cap 64 > T*k = 32
+    assert call(rs=P, k=33) == E_SHAPE
+    assert call(H=96) == E_SHAPE           # H % 64
+    assert call(w=ws - 4) == E_WS
+    assert call(y=None) == E_ARG
+    assert call(x=P_ODD) == E_ALIGN
+    # without row_src, T and k are not used
+    assert call(rs=None, T=0, k=0, y=None) == E_ARG
+
+
 def test_eplb_validation(L):
     f = L.moe_eplb_plan
     assert f(P, 0, 8, 1, P, P, P, P, P, None) == E_SHAPE       # E < 1
