@@ -428,10 +428,9 @@ def main():
                          "share and the MXFP8 step timed after it")
     ap.add_argument("--no-eplb", action="store_true",
                     help="skip the EP8 load-balancing comparison of the full layer")
-    ap.add_argument("--ffn", choices=("auto", "grouped", "fused"), default="auto",
-                    help="bf16 FFN path: the grouped GEMMs, the fused one-launch "
-                         "kernel, or auto (fused when the expected rows per "
-                         "expert, T*k/E, are at most 32)")
+    ap.add_argument("--ffn", choices=("grouped", "fused"), default="grouped",
+                    help="bf16 FFN path: the grouped GEMMs (default, the faster "
+                         "on every workload here) or the fused one-launch kernel")
     ap.add_argument("--no-loop", action="store_true",
                     help="skip the per-expert-loop comparison of the grouped FFN")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
@@ -676,8 +675,7 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
     # The full layer on one GPU reads token rows through row_src; an EP share
     # gets its rows already permuted by the dispatch, so it reads x_perm.
     gather = not args.no_gather and wl.n_local == wl.E
-    fused = (args.ffn == "fused" or
-             (args.ffn == "auto" and wl.T * wl.k <= 32 * wl.E))
+    fused = args.ffn == "fused"
     pout = moe.PermuteOut(T, k, H, wl.n_local, torch.bfloat16, dev,
                           with_x=not gather)
     a = torch.empty((F, I), dtype=torch.bfloat16, device=dev)

@@ -240,11 +240,14 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
  * fused MLP without materialised intermediates.  With few rows per expert
  * the layer streams each weight byte for a handful of rows; one launch
  * saves the second launch, its ramp-up and drain, and the plan in between.
- * Work units are (expert, <= 64 rows, 64 columns of a) for gate/up and
- * (expert, <= 64 rows, 128 columns of y) for down; a down unit starts once
+ * Work units are (expert, <= 32 rows, 64 columns of a) for gate/up and
+ * (expert, <= 32 rows, 128 columns of y) for down; a down unit starts once
  * all of its expert's gate/up units have written their part of a.  Any row
- * count works (more than 64 rows per expert re-read the weights once per 64
- * rows); the grouped path is the faster one beyond a few dozen rows.
+ * count works (more than 32 rows per expert re-read the weights once per 32
+ * rows).  Measured against moe_grouped_ffn on EP shares of 7-34 and of
+ * 116-229 rows per expert, it is the slower of the two (the layer is a
+ * weight stream either way, and the grouped kernels stream it faster), so
+ * moe_grouped_ffn stays the default path.
  * x: with row_src non-NULL the token rows [T, H] (permuted row r is
  * x[row_src[r] / k], as moe_grouped_gate_up_gather; R_cap <= T * k); with
  * row_src NULL, x_perm [R_cap, H] (T and k unused).

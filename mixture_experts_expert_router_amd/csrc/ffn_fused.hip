@@ -9,21 +9,24 @@
 // grouped path then pays for two launches, their ramp-up and drain, and the
 // plan kernels between them.  Here one launch does both projections:
 //
-//   * Work units.  A gate/up unit is (expert e, group of <= 64 of its rows,
+//   * Work units.  A gate/up unit is (expert e, group of <= 32 of its rows,
 //     64 columns of a): it reads the 64 gate and the 64 matching up rows of
 //     W_gate[e] / W_up[e] once and writes a = s * SiLU(g) * u (bf16) for its
 //     rows.  A down unit is (expert e, row group, 128 columns of y): it reads
 //     128 rows of W_down[e] once and writes y (bf16).  A plan kernel turns
 //     the device offsets into unit prefixes (gate/up units of every expert
-//     first, then down units) and clears the counters.
-//   * Scheduling.  One workgroup per CU claims units from an atomic counter,
-//     in order.  A down unit of expert e waits until every gate/up unit of e
-//     has published its part of a.  Units are claimed in order and gate/up
-//     units never wait, so every unit a waiting workgroup depends on has
-//     already been claimed by a running workgroup and finishes: the wait
-//     always ends, however many workgroups are resident.  (A wall-clock
-//     bound on the wait sets MOE_DEVERR_WAIT and gives up instead of
-//     hanging.)
+//     first, then down units) and clears the flags.
+//   * Workers.  Two workgroups per CU claim units.  Inside a unit the four
+//     wavefronts split K into quarters, so the unit's rows of x (or of a)
+//     are read once per unit for 128 weight rows.
+//   * Scheduling.  Units are claimed in order through one atomic counter:
+//     the gate/up units of every expert, then the down units.  A down unit
+//     of expert e waits until every gate/up unit of e has published its part
+//     of a; those precede it and gate/up units never wait, so every unit a
+//     waiting workgroup depends on has already been claimed by a running
+//     workgroup and finishes: the wait always ends, however many workgroups
+//     are resident.  (A wall-clock bound on the wait sets MOE_DEVERR_WAIT
+//     and gives up instead of hanging.)
 //   * Hand-over of a, across the XCDs' separate L2 caches, without
 //     device-scope fences (on gfx950 those write back or invalidate a whole
 //     L2; in a polling loop run by many workgroups they would stall every
@@ -35,13 +38,18 @@
 //     ordering-only fence), then sets its flag; the down unit polls its
 //     expert's flags and then reads a the same way.  a is small (rows x I
 //     bf16) and is the one intermediate, as in the grouped path.
-//   * Inside a unit.  Four wavefronts split K into quarters and stream their
-//     operands straight into registers in the v_mfma_f32_16x16x32_bf16
-//     operand layout (lane l: row l % 16 of every 16-row block, K values
-//     8*(l/16) .. +8 of every 32), kDepth k-steps ahead; the four partial
-//     accumulators are summed in a fixed order through LDS and the epilogue
-//     writes 16-byte row pieces.  No split of K across workgroups: results
-//     are deterministic.
+//   * Inside a unit.  Each wavefront streams its quarter of K straight into
+//     registers in the v_mfma_f32_16x16x32_bf16 operand layout (lane l: row
+//     l % 16 of every 16-row block, 16 contiguous K values of every 64),
+//     kDepth k-steps ahead; the four partial accumulators are summed in a
+//     fixed order through LDS (deterministic results) and the epilogue
+//     writes whole row pieces.
+//   * Control flow branches only on workgroup-uniform values: with a
+//     per-lane condition around the claim or the loop exit, the compiler's
+//     structurizer may split the loop so that most lanes iterate without
+//     passing the claim.  So wavefront 0 claims with all its lanes (lane 0
+//     adds 1, the others 0; lane 0's result is the unit) and the unit index
+//     is made uniform with readfirstlane.
 #include <algorithm>
 
 #include "common.hpp"
@@ -50,18 +58,22 @@
 namespace moe {
 namespace {
 
-constexpr int kRG = 64;          // rows per row group (four 16-row blocks)
+constexpr int kRG = 32;          // rows per row group (two 16-row blocks)
 constexpr int kCI = 64;          // a-columns per gate/up unit
 constexpr int kCH = 128;         // y-columns per down unit
-constexpr int kNB = 8;           // 16-wide weight blocks per unit
-constexpr int kDepth = 4;        // k-steps of 32 in flight per wavefront
+constexpr int kNB = 8;           // 16-row weight blocks per unit
+#ifndef MOE_FUSED_DEPTH
+#define MOE_FUSED_DEPTH 3
+#endif
+constexpr int kDepth = MOE_FUSED_DEPTH;  // k-steps of 32 in flight per wavefront
 constexpr int kStride = 132;     // floats per staged row (128 + 4 pad)
 // Bound on one wait, in ticks of the 100 MHz constant clock (0.2 s).
 constexpr uint64_t kWaitTicks = 20000000;
 
-// Workspace (int32 words): the error header, then a control block (claim
-// counter, gate/up unit total, down unit total), then the per-expert arrays
-// (p1, p2 prefixes, row groups) and one flag per gate/up unit.
+// Workspace (int32 words): the error header; the claim counter; the gate/up
+// and down unit totals; then p1, p2 (exclusive prefixes of the gate/up and
+// of the down units over the experts, G + 1 entries each), ng (row groups
+// per expert) and one flag per gate/up unit (numbered by p1).
 constexpr int kCtl = (int)(kErrHeaderBytes / 4);
 constexpr int kArr = kCtl + 64;
 
@@ -81,8 +93,8 @@ struct FusedArgs {
 
 // Per expert: ng = row groups, gate/up units ng * I/kCI, down units
 // ng * ceil(H/kCH); exclusive prefixes p1, p2 of the unit counts (G + 1
-// entries each); the flags of all gate/up units cleared; error word set.
-// One block.
+// entries each); the counter and the flags of all gate/up units cleared;
+// error word set.  One block.
 __global__ __launch_bounds__(1024) void ffn_fused_plan_kernel(
     const int32_t *__restrict__ offsets, int G, int r_cap, int nci, int nch,
     int32_t *__restrict__ ws) {
@@ -180,8 +192,16 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 // acc[m][j] += sum over k-steps s in [s0, s1) of A_m(s) . B_j(s)^T.  ap[m]
-// and bp[j] point at the lane's first operand element of step 0 (row
-// l % 16 of the block, K offset 8*(l/16)); step s is 32 elements further.
+// points at the lane's first A element (row l % 16 of the block); B block
+// j's rows start at the workgroup-uniform bb[j] and the lane's element is
+// boff further (a 32-bit offset, so the loads take the scalar-base +
+// vector-offset form).  K order: the MFMA sums its 32 K values in any order
+// as long as A and B agree, so a pair of steps (64 K values, 128 bytes of a
+// row) is split so that lane l takes the 16 contiguous values 16*(l/16) ..
+// +16, the first 8 in the pair's first step and the last 8 in its second:
+// the two loads of a pair then touch each 128-byte line of a row once per
+// instruction (one L2 request per row, not two 64-byte halves).  ap[m] and
+// boff include the lane's 16*(l/16).
 // kCoherentA: A is another workgroup's output, read through coherent loads.
 // kDepth steps are in flight: each step's registers are refilled with the
 // step kDepth ahead right after its MFMAs (past the end: the last step
@@ -189,20 +209,24 @@ __device__ __forceinline__ void wait_vmem() {
 // last ns % kDepth steps run from registers after the loop.
 template <int MB, bool kCoherentA>
 __device__ __forceinline__ void stream_mma(const uint16_t *const (&ap)[MB],
-                                           const uint16_t *const (&bp)[kNB],
-                                           int s0, int s1,
+                                           const uint16_t *const (&bb)[kNB],
+                                           uint32_t boff, int s0, int s1,
                                            f32x4 (&acc)[MB][kNB]) {
   if (s1 <= s0) return;
   bf16x8 aq[kDepth][MB], bq[kDepth][kNB];
   const int last = s1 - 1;
   auto load = [&](int d, int step) {
-    const int64_t off = (int64_t)min(step, last) * 32;
+    const int st = min(step, last);
+    // element offset of step st: its pair's 64 values, then its half
+    const int64_t off = (int64_t)(st >> 1) * 64 + (st & 1) * 8;
 #pragma unroll
     for (int m = 0; m < MB; ++m)
       aq[d][m] = kCoherentA ? load_coherent16(ap[m] + off)
                             : *(const bf16x8 *)(ap[m] + off);
+    const uint32_t bo = (boff + (uint32_t)off) * 2u;
 #pragma unroll
-    for (int j = 0; j < kNB; ++j) bq[d][j] = *(const bf16x8 *)(bp[j] + off);
+    for (int j = 0; j < kNB; ++j)
+      bq[d][j] = *(const bf16x8 *)((const char *)bb[j] + bo);
   };
   auto mma = [&](int d) {
 #pragma unroll
@@ -212,14 +236,23 @@ __device__ __forceinline__ void stream_mma(const uint16_t *const (&ap)[MB],
         acc[m][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
             aq[d][m], bq[d][j], acc[m][j], 0, 0, 0);
   };
+  // Scheduling barriers keep each step's loads where they are written: the
+  // loop's first step then always waits for the oldest loads in flight, on
+  // entry as on every later iteration (reordered, the wait on entry can
+  // degrade to waiting for every load).
 #pragma unroll
-  for (int d = 0; d < kDepth; ++d) load(d, s0 + d);
+  for (int d = 0; d < kDepth; ++d) {
+    load(d, s0 + d);
+    __builtin_amdgcn_sched_barrier(0);
+  }
   int s = s0;
   for (; s + kDepth <= s1; s += kDepth) {
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
       mma(d);
+      __builtin_amdgcn_sched_barrier(0);
       load(d, s + d + kDepth);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 #pragma unroll
@@ -232,15 +265,14 @@ __device__ __forceinline__ void stream_mma(const uint16_t *const (&ap)[MB],
 template <int MB>
 __device__ __forceinline__ void unit_mma(const FusedArgs &p, bool gate_up,
                                          int e, int r0, int nr, int chunk,
-                                         float *red, int tid) {
-  const int lane = tid & 63;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+                                         int wid, int lane, float *red) {
   const int K = gate_up ? p.H : p.I;
-  const int ks = K / 32;
-  const int s0 = wid * ks / 4, s1 = (wid + 1) * ks / 4;
-  const int koff = 8 * (lane >> 4), l16 = lane & 15;
+  // K (a multiple of 64) in pairs of 32-value steps, a quarter per wavefront
+  const int kp = K / 64;
+  const int s0 = 2 * (wid * kp / 4), s1 = 2 * ((wid + 1) * kp / 4);
+  const int koff = 16 * (lane >> 4), l16 = lane & 15;
   const uint16_t *ap[MB];
-  const uint16_t *bp[kNB];
+  const uint16_t *bb[kNB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     const int r = r0 + min(m * 16 + l16, nr - 1);
@@ -252,15 +284,19 @@ __device__ __forceinline__ void unit_mma(const FusedArgs &p, bool gate_up,
     }
   }
   const int64_t wstride = (int64_t)p.I * p.H;
+  // lane offset inside a block of 16 weight rows (row stride K)
+  const uint32_t boff = (uint32_t)(l16 * K + koff);
 #pragma unroll
   for (int j = 0; j < kNB; ++j) {
     if (gate_up) {
       // blocks 0-3: gate rows of the chunk's 64 columns, 4-7: the up rows
-      const int c = chunk * kCI + (j & 3) * 16 + l16;
-      bp[j] = (j < 4 ? p.wg : p.wu) + e * wstride + (int64_t)c * p.H + koff;
+      const int c = chunk * kCI + (j & 3) * 16;
+      bb[j] = (j < 4 ? p.wg : p.wu) + e * wstride + (int64_t)c * p.H;
     } else {
-      const int h = min(chunk * kCH + j * 16 + l16, p.H - 1);
-      bp[j] = p.wd + e * wstride + (int64_t)h * p.I + koff;
+      // blocks past the last row of W_down re-read the last full block
+      // (H is a multiple of 64); their columns are not stored
+      const int h = min(chunk * kCH + j * 16, p.H - 16);
+      bb[j] = p.wd + e * wstride + (int64_t)h * p.I;
     }
   }
   f32x4 acc[MB][kNB];
@@ -270,8 +306,8 @@ __device__ __forceinline__ void unit_mma(const FusedArgs &p, bool gate_up,
     for (int j = 0; j < kNB; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) acc[m][j][r] = 0.f;
-  if (gate_up) stream_mma<MB, false>(ap, bp, s0, s1, acc);
-  else stream_mma<MB, true>(ap, bp, s0, s1, acc);
+  if (gate_up) stream_mma<MB, false>(ap, bb, boff, s0, s1, acc);
+  else stream_mma<MB, true>(ap, bb, boff, s0, s1, acc);
   // lane holds column l % 16 and rows 4*(l/16) .. +4 of each 16x16 block
   float *mine = red + wid * (kRG * kStride);
 #pragma unroll
@@ -291,23 +327,15 @@ __device__ __forceinline__ float red_sum(const float *red, int row, int col) {
   return ((red[o] + red[W + o]) + red[2 * W + o]) + red[3 * W + o];
 }
 
-__global__ __launch_bounds__(256, 1) void ffn_fused_kernel(FusedArgs p) {
+__global__ __launch_bounds__(256, 2) void ffn_fused_kernel(FusedArgs p) {
   __shared__ float red[4 * kRG * kStride];
   __shared__ int s_unit;
   int32_t *ctl = p.ws + kCtl;
   const int32_t *p1 = p.ws + kArr, *p2 = p1 + p.G + 1, *ngs = p2 + p.G + 1;
   int32_t *flags = p.ws + kArr + 3 * p.G + 2;
-  const int tid = threadIdx.x;
-  const int nci = p.I / kCI, nch = (p.H + kCH - 1) / kCH;
-  const int N1 = ctl[1], N = N1 + ctl[2];
-  const int lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
-  // Control flow in this loop branches only on workgroup-uniform values
-  // (scalar branches): with a per-lane condition around the claim or the
-  // exit, the compiler's structurizer may split the loop so that most lanes
-  // iterate without passing the claim.  So wavefront 0 claims with all its
-  // lanes (lane 0 adds 1, the others 0; lane 0's result is the unit) and
-  // the unit index is read back with readfirstlane.
+  const int N1 = ctl[1], N = N1 + ctl[2];
   for (;;) {
     if (wid == 0) {
       const int v = atomicAdd(&ctl[0], lane == 0 ? 1 : 0);
@@ -328,8 +356,8 @@ __global__ __launch_bounds__(256, 1) void ffn_fused_kernel(FusedArgs p) {
     seg_rows(p.offsets, e, p.r_cap, b, en);
     const int r0 = b + grp * kRG, nr = min(kRG, en - r0);
     if (!gate_up) {
-      // Wait for the flags of every gate/up unit of expert e (wavefront 0
-      // polls 64 flags per load; the others wait at the barrier).
+      // wait for the flags of every gate/up unit of expert e (wavefront 0
+      // polls 64 flags per load; the others wait at the barrier)
       if (wid == 0) {
         const int f0 = p1[e], nf = p1[e + 1] - f0;
         const uint64_t t0 = wall_clock64();
@@ -353,14 +381,9 @@ __global__ __launch_bounds__(256, 1) void ffn_fused_kernel(FusedArgs p) {
       }
       wait_vmem();
       __syncthreads();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     }
-    switch ((nr + 15) >> 4) {
-      case 1: unit_mma<1>(p, gate_up, e, r0, nr, chunk, red, tid); break;
-      case 2: unit_mma<2>(p, gate_up, e, r0, nr, chunk, red, tid); break;
-      case 3: unit_mma<3>(p, gate_up, e, r0, nr, chunk, red, tid); break;
-      default: unit_mma<4>(p, gate_up, e, r0, nr, chunk, red, tid); break;
-    }
+    if (nr <= 16) unit_mma<1>(p, gate_up, e, r0, nr, chunk, wid, lane, red);
+    else unit_mma<2>(p, gate_up, e, r0, nr, chunk, wid, lane, red);
     if (gate_up) {
       // a[r0 + row][c0 + c] = s * SiLU(g) * u, 8 columns per piece
       const int c0 = chunk * kCI;
@@ -368,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void ffn_fused_kernel(FusedArgs p) {
         const int q = q0 + tid;
         if (q >= nr * (kCI / 8)) continue;
         const int row = q / (kCI / 8), c8 = (q % (kCI / 8)) * 8;
-        const float s = p.s_perm ? p.s_perm[r0 + row] : 1.f;
+        const float sc = p.s_perm ? p.s_perm[r0 + row] : 1.f;
         uint32_t w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -377,7 +400,7 @@ __global__ __launch_bounds__(256, 1) void ffn_fused_kernel(FusedArgs p) {
           for (int h = 0; h < 2; ++h) {
             const int c = c8 + 2 * i + h;
             const float g = red_sum(red, row, c), uu = red_sum(red, row, kCI + c);
-            v2[h] = s * silu_f32(g) * uu;
+            v2[h] = sc * silu_f32(g) * uu;
           }
           w[i] = pack_bf16x2(v2[0], v2[1]);
         }
@@ -385,7 +408,6 @@ __global__ __launch_bounds__(256, 1) void ffn_fused_kernel(FusedArgs p) {
                          w[1], w[2], w[3]);
       }
       // publish: the coherent stores complete, then the unit's flag
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
       wait_vmem();
       __syncthreads();
       if (wid == 0)  // every lane stores the same flag
@@ -439,10 +461,12 @@ hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
   p.offsets = offsets; p.s_perm = s_perm;
   p.wg = w_gate; p.wu = w_up; p.wd = w_down; p.a = a; p.y = y; p.ws = ws;
   p.G = n_local; p.H = H; p.I = I; p.r_cap = (int)R_cap;
-  // one workgroup per CU (the staging buffer takes most of the LDS); a grid
-  // larger than the work only adds workgroups that claim nothing
+  // two workgroups per CU, so that one's claim, pipeline ramp and epilogue
+  // overlap the other's weight stream; a grid larger than the work only
+  // adds workgroups that claim nothing
   const int64_t upper = (R_cap / kRG + n_local) * (int64_t)(nci + nch);
-  const int grid = (int)std::max<int64_t>(1, std::min<int64_t>(num_cus, upper));
+  const int grid =
+      (int)std::max<int64_t>(1, std::min<int64_t>(2 * (int64_t)num_cus, upper));
   ffn_fused_kernel<<<grid, 256, 0, s>>>(p);
   return hipGetLastError();
 }
