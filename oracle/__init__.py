@@ -68,6 +68,15 @@ def _lib():
         L.orc_mx_scale_byte.restype = ctypes.c_uint8
         L.orc_mx_quantize_rows.argtypes = [vp, i64, i64, vp, vp]
         L.orc_mx_dequantize_rows.argtypes = [vp, vp, i64, i64, vp]
+        L.orc_e5m2_value.argtypes = [ctypes.c_uint8]
+        L.orc_e5m2_value.restype = ctypes.c_double
+        L.orc_e5m2_encode.argtypes = [ctypes.c_double]
+        L.orc_e5m2_encode.restype = ctypes.c_uint8
+        L.orc_e5m2_encode_array.argtypes = [vp, i64, vp]
+        L.orc_mx_scale_byte_fmt.argtypes = [ctypes.c_double, ctypes.c_int]
+        L.orc_mx_scale_byte_fmt.restype = ctypes.c_uint8
+        L.orc_mx_quantize_rows_fmt.argtypes = [vp, i64, i64, ctypes.c_int, vp, vp]
+        L.orc_mx_dequantize_rows_fmt.argtypes = [vp, vp, i64, i64, ctypes.c_int, vp]
         L.orc_matmul_nt.argtypes = [vp, vp, i64, i64, i64, vp]
         L.orc_round_bf16.argtypes = [vp, i64, vp]
         L.orc_swiglu_bwd_rows.argtypes = [vp, vp, vp, vp, i64, i64, vp, vp,
@@ -297,37 +306,66 @@ def e4m3_encode_array(v):
     return out
 
 
-def mx_scale_byte(amax):
-    return int(_lib().orc_mx_scale_byte(float(amax)))
+# Element formats of MX blocks: E4M3 (the default for every operand) and
+# E5M2 (the gradient option).
+MX_FORMATS = {"e4m3": 0, "e5m2": 1}
 
 
-def mx_quantize_rows(v):
-    """Blocks of 32 along each row: (codes [r, c] u8, scales [r, ceil(c/32)])."""
+def _fmt(fmt):
+    try:
+        return MX_FORMATS[fmt]
+    except KeyError:
+        raise ValueError(f"unknown MX element format {fmt!r}") from None
+
+
+def e5m2_value(code):
+    return _lib().orc_e5m2_value(int(code))
+
+
+def e5m2_encode(v):
+    return int(_lib().orc_e5m2_encode(float(v)))
+
+
+def e5m2_encode_array(v):
+    """E5M2 codes (nearest, ties to even, saturating) of every value."""
+    v = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint8)
+    _lib().orc_e5m2_encode_array(_p(v), v.size, _p(out))
+    return out
+
+
+def mx_scale_byte(amax, fmt="e4m3"):
+    return int(_lib().orc_mx_scale_byte_fmt(float(amax), _fmt(fmt)))
+
+
+def mx_quantize_rows(v, fmt="e4m3"):
+    """Blocks of 32 along each row: (codes [r, c] u8, scales [r, ceil(c/32)]),
+    elements of format fmt."""
     v = _c(v, np.float64)
     r, c = v.shape
     codes = np.empty((r, c), dtype=np.uint8)
     scales = np.empty((r, (c + 31) // 32), dtype=np.uint8)
-    _lib().orc_mx_quantize_rows(_p(v), r, c, _p(codes), _p(scales))
+    _lib().orc_mx_quantize_rows_fmt(_p(v), r, c, _fmt(fmt), _p(codes), _p(scales))
     return codes, scales
 
 
-def mx_dequantize_rows(codes, scales):
+def mx_dequantize_rows(codes, scales, fmt="e4m3"):
     codes = _c(codes, np.uint8)
     scales = _c(scales, np.uint8)
     r, c = codes.shape
     v = np.empty((r, c), dtype=np.float64)
-    _lib().orc_mx_dequantize_rows(_p(codes), _p(scales), r, c, _p(v))
+    _lib().orc_mx_dequantize_rows_fmt(_p(codes), _p(scales), r, c, _fmt(fmt), _p(v))
     return v
 
 
-def mx_roundtrip_rows(v):
+def mx_roundtrip_rows(v, fmt="e4m3"):
     """Dequantised MX values of v, blocks of 32 along each row."""
-    return mx_dequantize_rows(*mx_quantize_rows(v))
+    return mx_dequantize_rows(*mx_quantize_rows(v, fmt), fmt=fmt)
 
 
-def mx_roundtrip_cols(v):
+def mx_roundtrip_cols(v, fmt="e4m3"):
     """Dequantised MX values of v, blocks of 32 down each column."""
-    return np.ascontiguousarray(mx_roundtrip_rows(np.ascontiguousarray(v.T)).T)
+    return np.ascontiguousarray(mx_roundtrip_rows(np.ascontiguousarray(v.T), fmt).T)
 
 
 def to_f64(a):
@@ -372,16 +410,17 @@ def swiglu(g, u, s=None):
     return a
 
 
-def mx_gemm_nt(A, B, quantize=True):
+def mx_gemm_nt(A, B, quantize=True, fmt_a="e4m3", fmt_b="e4m3"):
     """C = Q(A) . Q(B)^T with every row of A [M, K] and of B [N, K]
     MX-quantised along K (blocks of 32 from column 0; a shorter last block is
     a block padded with zeros) and the dequantised values multiplied exactly
     in fp64.  This is the one MXFP8 GEMM of the step: every operand is
     blocked along its GEMM's reduction axis [TE-MXFP8], which a caller
-    chooses by the orientation it passes.  quantize=False: plain product."""
+    chooses by the orientation it passes.  fmt_a, fmt_b: element formats of
+    the two operands.  quantize=False: plain product."""
     A, B = _c(A, np.float64), _c(B, np.float64)
     if quantize:
-        A, B = mx_roundtrip_rows(A), mx_roundtrip_rows(B)
+        A, B = mx_roundtrip_rows(A, fmt_a), mx_roundtrip_rows(B, fmt_b)
     return matmul_nt(A, B)
 
 
@@ -414,26 +453,29 @@ def mxfp8_forward(x_perm, offsets, s_perm, w_gate, w_up, w_down,
     return dict(g=g, u=u, a=a, y=y)
 
 
-def mxfp8_wgrad(A, B, offsets, quantize=True):
+def mxfp8_wgrad(A, B, offsets, quantize=True, fmt_a="e4m3"):
     """Weight gradient per expert: W[e] = Q_R(A_e)^T Q_R(B_e) over expert
     e's rows (A [R, M], B [R, N] -> [n_local, M, N]), every operand blocked
     down the rows of the segment from its first row (the GEMM's reduction
-    axis); an expert without rows gets zeros."""
+    axis); an expert without rows gets zeros.  A is the gradient operand
+    (elements of format fmt_a), B an activation (E4M3)."""
     A, B = to_f64(A), to_f64(B)
     n_local = len(offsets) - 1
     out = np.zeros((n_local, A.shape[1], B.shape[1]))
     for e in range(n_local):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 > r0:
-            out[e] = mx_gemm_nt(_T(A[r0:r1]), _T(B[r0:r1]), quantize)
+            out[e] = mx_gemm_nt(_T(A[r0:r1]), _T(B[r0:r1]), quantize, fmt_a)
     return out
 
 
-def mxfp8_backward_down(dy, g, u, s_perm, offsets, w_down, quantize=True):
+def mxfp8_backward_down(dy, g, u, s_perm, offsets, w_down, quantize=True,
+                        grad_fmt="e4m3"):
     """Backward of the down projection and of ScaledSwiGLU, by the chain
     rule: da = Q_H(dY) Q_H(W_d) per expert (K = H), dg, du, ds from
     swiglu_bwd at the given g, u, and dW_d = Q_R(dY)^T Q_R(a) with a =
-    s SiLU(g) u.  Returns dict of fp64 da, dg, du, ds, a, dw_down."""
+    s SiLU(g) u.  grad_fmt: element format of the gradient operand dY (W_d
+    and a stay E4M3).  Returns dict of fp64 da, dg, du, ds, a, dw_down."""
     dY = to_f64(dy)
     g, u = to_f64(g), to_f64(u)
     s = np.asarray(s_perm, dtype=np.float64)
@@ -446,19 +488,22 @@ def mxfp8_backward_down(dy, g, u, s_perm, offsets, w_down, quantize=True):
         if r1 == r0:
             continue
         # W_d[e] is [H, I]; da[r, i] = sum_h dY[r, h] W_d[h, i]
-        da[r0:r1] = mx_gemm_nt(dY[r0:r1], _T(to_f64(w_down[e])), quantize)
+        da[r0:r1] = mx_gemm_nt(dY[r0:r1], _T(to_f64(w_down[e])), quantize,
+                               grad_fmt)
         dg[r0:r1], du[r0:r1], ds[r0:r1] = swiglu_bwd(
             da[r0:r1], g[r0:r1], u[r0:r1], s[r0:r1])
     a = swiglu(g, u, s)
-    dwd = mxfp8_wgrad(dY, a, offsets, quantize)
+    dwd = mxfp8_wgrad(dY, a, offsets, quantize, grad_fmt)
     return dict(da=da, dg=dg, du=du, ds=ds, a=a, dw_down=dwd)
 
 
 def mxfp8_backward_gate_up(dg, du, x_perm, offsets, w_gate, w_up,
-                           quantize=True):
+                           quantize=True, grad_fmt="e4m3"):
     """Backward of the gate/up projection: dX = Q_I(dg) Q_I(W_g) +
     Q_I(du) Q_I(W_u) per expert (K = I), dW_g = Q_R(dg)^T Q_R(x),
-    dW_u = Q_R(du)^T Q_R(x).  Returns dict of fp64 dx, dw_gate, dw_up."""
+    dW_u = Q_R(du)^T Q_R(x).  grad_fmt: element format of the gradient
+    operands dg, du (W_g, W_u and x stay E4M3).  Returns dict of fp64 dx,
+    dw_gate, dw_up."""
     dg, du, x = to_f64(dg), to_f64(du), to_f64(x_perm)
     n_local = len(offsets) - 1
     R, H = x.shape
@@ -468,14 +513,16 @@ def mxfp8_backward_gate_up(dg, du, x_perm, offsets, w_gate, w_up,
         if r1 == r0:
             continue
         # W_g[e] is [I, H]; dX[r, h] = sum_i dg[r, i] W_g[i, h] + du W_u
-        dx[r0:r1] = (mx_gemm_nt(dg[r0:r1], _T(to_f64(w_gate[e])), quantize)
-                     + mx_gemm_nt(du[r0:r1], _T(to_f64(w_up[e])), quantize))
-    return dict(dx=dx, dw_gate=mxfp8_wgrad(dg, x, offsets, quantize),
-                dw_up=mxfp8_wgrad(du, x, offsets, quantize))
+        dx[r0:r1] = (mx_gemm_nt(dg[r0:r1], _T(to_f64(w_gate[e])), quantize,
+                                grad_fmt)
+                     + mx_gemm_nt(du[r0:r1], _T(to_f64(w_up[e])), quantize,
+                                  grad_fmt))
+    return dict(dx=dx, dw_gate=mxfp8_wgrad(dg, x, offsets, quantize, grad_fmt),
+                dw_up=mxfp8_wgrad(du, x, offsets, quantize, grad_fmt))
 
 
 def mxfp8_mlp_step(x_perm, offsets, s_perm, w_gate, w_up, w_down, dy,
-                   quantize=True, bf16_dgu=False):
+                   quantize=True, bf16_dgu=False, grad_fmt="e4m3"):
     """MXFP8 grouped MLP forward + backward on permuted rows, fp64: the
     forward, the down/SwiGLU backward at the forward's own g, u, and the
     gate/up backward.  Every GEMM operand is MX-quantised along that GEMM's
@@ -485,16 +532,18 @@ def mxfp8_mlp_step(x_perm, offsets, s_perm, w_gate, w_up, w_down, dy,
     finite-difference pins check).  bf16_dgu=True: dg and du are rounded to
     bf16 before the gate/up backward quantises them, as the unfused stage
     API hands [dg | du] from one call to the next in bf16 (a labelled
-    variant for that API only).  Returns fp64 g, u, a, y, da, dg, du, ds,
-    dx, dw_gate, dw_up, dw_down."""
+    variant for that API only).  grad_fmt: element format of every gradient
+    operand (dY, dg, du) of the backward GEMMs, "e4m3" or "e5m2"; weights and
+    activations stay E4M3.  Returns fp64 g, u, a, y, da, dg, du, ds, dx,
+    dw_gate, dw_up, dw_down."""
     f = mxfp8_forward(x_perm, offsets, s_perm, w_gate, w_up, w_down, quantize)
     b = mxfp8_backward_down(dy, f["g"], f["u"], s_perm, offsets, w_down,
-                            quantize)
+                            quantize, grad_fmt)
     dg, du = b["dg"], b["du"]
     if bf16_dgu:
         dg, du = round_bf16(dg), round_bf16(du)
     c = mxfp8_backward_gate_up(dg, du, x_perm, offsets, w_gate, w_up,
-                               quantize)
+                               quantize, grad_fmt)
     return dict(g=f["g"], u=f["u"], a=f["a"], y=f["y"], da=b["da"],
                 dg=b["dg"], du=b["du"], ds=b["ds"], dx=c["dx"],
                 dw_gate=c["dw_gate"], dw_up=c["dw_up"],

@@ -316,22 +316,75 @@ void orc_e4m3_encode_array(const double *v, int64_t n, uint8_t *out) {
   for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_encode(v[i]);
 }
 
-// Shared E8M0 scale byte of a block with largest magnitude amax.
-uint8_t orc_mx_scale_byte(double amax) {
+// E5M2, the other OCP FP8 element format, for the gradient option: bias 15,
+// exponent field 31 holds the infinities and NaNs, largest finite value
+// 1.75 * 2^15 = 57344, subnormals m/4 * 2^-14.  Its wider range suits
+// gradients (the pages leave the gradients' element format open; this build
+// offers E4M3, the default, and E5M2).  MX shared exponent with E5M2
+// elements: X = floor(log2(max|v|)) - 15 (15 being E5M2's largest normal
+// exponent); elements v / 2^X rounded to nearest, ties to even, saturating at
+// +-57344.
+
+// Value of an E5M2 code, by the format's definition.
+double orc_e5m2_value(uint8_t code) {
+  const int s = code >> 7, ex = (code >> 2) & 31, m = code & 3;
+  double mag;
+  if (ex == 31) mag = m == 0 ? INFINITY : NAN;
+  else if (ex == 0) mag = std::ldexp((double)m / 4.0, -14);
+  else mag = std::ldexp(1.0 + (double)m / 4.0, ex - 15);
+  return s ? -mag : mag;
+}
+
+// Code of the E5M2 value nearest to v (ties: even code), saturating at the
+// largest finite value.
+uint8_t orc_e5m2_encode(double v) {
+  const double a = std::fabs(v);
+  int best = 0;
+  double best_err = INFINITY;
+  for (int c = 0; c <= 0x7B; ++c) {  // every finite non-negative code
+    const double err = std::fabs(orc_e5m2_value((uint8_t)c) - a);
+    if (err < best_err || (err == best_err && (c & 1) == 0 && (best & 1))) {
+      best = c;
+      best_err = err;
+    }
+  }
+  if (a > 57344.0) best = 0x7B;  // saturate
+  return (uint8_t)(best | (std::signbit(v) ? 0x80 : 0));
+}
+
+void orc_e5m2_encode_array(const double *v, int64_t n, uint8_t *out) {
+#pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_e5m2_encode(v[i]);
+}
+
+// Element formats of an MX block: 0 = E4M3, 1 = E5M2.
+static int elem_emax(int fmt) { return fmt == 1 ? 15 : 8; }
+static uint8_t elem_encode(int fmt, double v) {
+  return fmt == 1 ? orc_e5m2_encode(v) : orc_e4m3_encode(v);
+}
+static double elem_value(int fmt, uint8_t c) {
+  return fmt == 1 ? orc_e5m2_value(c) : orc_e4m3_value(c);
+}
+
+// Shared E8M0 scale byte of a block with largest magnitude amax and elements
+// of format fmt: X = floor(log2 amax) - emax, clamped to [-127, 127].
+uint8_t orc_mx_scale_byte_fmt(double amax, int fmt) {
   if (amax == 0.0) return 0;
   int e2;
   std::frexp(amax, &e2);  // amax = m * 2^e2, m in [0.5, 1)
-  int X = (e2 - 1) - 8;
+  int X = (e2 - 1) - elem_emax(fmt);
   if (X < -127) X = -127;
   if (X > 127) X = 127;
   return (uint8_t)(X + 127);
 }
 
+uint8_t orc_mx_scale_byte(double amax) { return orc_mx_scale_byte_fmt(amax, 0); }
+
 // Quantise each row of v [rows, cols] in blocks of 32 along the row (the last
-// block of a row may be shorter: it behaves as if zero-padded).
-// codes [rows, cols]; scales [rows, ceil(cols/32)].
-void orc_mx_quantize_rows(const double *v, int64_t rows, int64_t cols,
-                          uint8_t *codes, uint8_t *scales) {
+// block of a row may be shorter: it behaves as if zero-padded), elements of
+// format fmt.  codes [rows, cols]; scales [rows, ceil(cols/32)].
+void orc_mx_quantize_rows_fmt(const double *v, int64_t rows, int64_t cols,
+                              int fmt, uint8_t *codes, uint8_t *scales) {
   const int64_t nb = (cols + 31) / 32;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r)
@@ -339,23 +392,34 @@ void orc_mx_quantize_rows(const double *v, int64_t rows, int64_t cols,
       const int64_t c0 = b * 32, c1 = std::min<int64_t>(cols, c0 + 32);
       double amax = 0.0;
       for (int64_t c = c0; c < c1; ++c) amax = std::fmax(amax, std::fabs(v[r * cols + c]));
-      const uint8_t sb = orc_mx_scale_byte(amax);
+      const uint8_t sb = orc_mx_scale_byte_fmt(amax, fmt);
       scales[r * nb + b] = sb;
       const double inv_scale = std::ldexp(1.0, -((int)sb - 127));
       for (int64_t c = c0; c < c1; ++c)
-        codes[r * cols + c] = orc_e4m3_encode(v[r * cols + c] * inv_scale);
+        codes[r * cols + c] = elem_encode(fmt, v[r * cols + c] * inv_scale);
     }
 }
 
+void orc_mx_quantize_rows(const double *v, int64_t rows, int64_t cols,
+                          uint8_t *codes, uint8_t *scales) {
+  orc_mx_quantize_rows_fmt(v, rows, cols, 0, codes, scales);
+}
+
 // v[r, c] = value(codes[r, c]) * 2^(scales[r, c/32] - 127), exactly, in fp64.
-void orc_mx_dequantize_rows(const uint8_t *codes, const uint8_t *scales,
-                            int64_t rows, int64_t cols, double *v) {
+void orc_mx_dequantize_rows_fmt(const uint8_t *codes, const uint8_t *scales,
+                                int64_t rows, int64_t cols, int fmt,
+                                double *v) {
   const int64_t nb = (cols + 31) / 32;
 #pragma omp parallel for schedule(static)
   for (int64_t r = 0; r < rows; ++r)
     for (int64_t c = 0; c < cols; ++c)
-      v[r * cols + c] = std::ldexp(orc_e4m3_value(codes[r * cols + c]),
+      v[r * cols + c] = std::ldexp(elem_value(fmt, codes[r * cols + c]),
                                    (int)scales[r * nb + c / 32] - 127);
+}
+
+void orc_mx_dequantize_rows(const uint8_t *codes, const uint8_t *scales,
+                            int64_t rows, int64_t cols, double *v) {
+  orc_mx_dequantize_rows_fmt(codes, scales, rows, cols, 0, v);
 }
 
 // ---------------------------------------------------------------------------
