@@ -405,6 +405,16 @@ int moe_unpermute_combine(const void *y, const int32_t *inv,
  */
 
 /*
+ * MX element formats.  Every MXFP8 operand is E4M3 (the OCP FP8 "FN"
+ * format, largest finite 448, shared exponent floor(log2 amax) - 8) except
+ * that the backward entry points can take their gradient operands (dY, dg,
+ * du) in E5M2 (OCP FP8 E5M2, largest finite 57344, shared exponent
+ * floor(log2 amax) - 15), whose wider range suits gradients.  The pages fix
+ * neither; E4M3 everywhere is the default reading.
+ */
+enum moe_mx_format { MOE_MX_E4M3 = 0, MOE_MX_E5M2 = 1 };
+
+/*
  * moe_mxfp8_quantize - MX-quantise a bf16 matrix in[rows, cols] (row pitch
  * ld_in elements, ld_in % 8 == 0, `in` 16-byte aligned), cols % 32 == 0.
  * axis 0: blocks of 32 along each row.  codes [rows, ld_codes] bytes
@@ -417,12 +427,14 @@ int moe_unpermute_combine(const void *y, const int32_t *inv,
  *   pad_offsets[s] of the output (written to pad_offsets [n_seg + 1], device,
  *   when seg_offsets is given).  ld_codes must hold the padded total
  *   (>= rows + (align - 1) * n_seg), ld_scales >= ld_codes / 32.
+ * format: element format (moe_mx_format; MOE_E_ARG otherwise).
  * Codes and scales of a given input match the rule above bit for bit.
  */
 int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
-                       int64_t ld_in, int axis, const int32_t *seg_offsets,
-                       int64_t n_seg, int64_t align, uint8_t *codes,
-                       int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                       int64_t ld_in, int axis, int format,
+                       const int32_t *seg_offsets, int64_t n_seg,
+                       int64_t align, uint8_t *codes, int64_t ld_codes,
+                       uint8_t *scales, int64_t ld_scales,
                        int32_t *pad_offsets, hipStream_t stream);
 
 /*
@@ -518,8 +530,10 @@ int moe_grouped_linear_mxfp8(const void *x, const int32_t *offsets,
  * dg, du: along 2I for dX and down each expert's rows for dW_g, dW_u)
  * encoded from those fp32 values: no tensor of the chain is rounded to bf16
  * before it is quantised.
+ * grad_format: element format of the gradient operands dY, dg and du in
+ * every GEMM above (moe_mx_format); weights, x and a stay E4M3.
  * workspace: moe_grouped_mlp_mxfp8_bwd_workspace_bytes() bytes.
- * Limits as for the forward.
+ * Limits as for the forward; MOE_E_ARG for an unknown grad_format.
  */
 size_t moe_grouped_mlp_mxfp8_bwd_workspace_bytes(int64_t R_cap,
                                                  int64_t n_local, int64_t H,
@@ -530,8 +544,8 @@ int moe_grouped_mlp_mxfp8_bwd(
     int64_t R_cap, int64_t H, int64_t I, const uint8_t *wdt,
     const uint8_t *wdts, const uint8_t *wgt, const uint8_t *wgts,
     const uint8_t *wut, const uint8_t *wuts, void *dx, float *ds,
-    void *dw_gate, void *dw_up, void *dw_down, void *workspace,
-    size_t workspace_bytes, hipStream_t stream);
+    void *dw_gate, void *dw_up, void *dw_down, int grad_format,
+    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_grouped_mlp_mxfp8_bwd_down - first half of the backward: the down
@@ -544,7 +558,8 @@ int moe_grouped_mlp_mxfp8_bwd(
  * rounded: this stage API hands [dg | du] on in bf16, and
  * moe_grouped_mlp_mxfp8_bwd_gate_up quantises that bf16 tensor), ds [R_cap]
  * fp32, dw_down [n_local, H, I] bf16.  dW_d uses a recomputed in fp32 from
- * gu, as in moe_grouped_mlp_mxfp8_bwd.
+ * gu, as in moe_grouped_mlp_mxfp8_bwd.  grad_format: element format of dY
+ * (as for moe_grouped_mlp_mxfp8_bwd).
  * workspace: moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes() bytes.
  */
 size_t moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(int64_t R_cap,
@@ -554,7 +569,7 @@ int moe_grouped_mlp_mxfp8_bwd_down(
     const void *dy, const float *gu, const int32_t *offsets,
     const float *s_perm, int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
     const uint8_t *wdt, const uint8_t *wdts, void *dgu, float *ds,
-    void *dw_down, void *workspace, size_t workspace_bytes,
+    void *dw_down, int grad_format, void *workspace, size_t workspace_bytes,
     hipStream_t stream);
 
 /*
@@ -564,7 +579,8 @@ int moe_grouped_mlp_mxfp8_bwd_down(
  *   dW_gate[e] = MX_R(dg_e)^T . MX_R(x_e), dW_up[e] = MX_R(du_e)^T . MX_R(x_e)
  * Inputs: dgu [R_cap, 2I] bf16, x_perm [R_cap, H] bf16, offsets, wgt/wgts,
  * wut/wuts as for moe_grouped_mlp_mxfp8_bwd.  Outputs: dx [R_cap, H],
- * dw_gate, dw_up [n_local, I, H] (bf16).
+ * dw_gate, dw_up [n_local, I, H] (bf16).  grad_format: element format of
+ * dg and du (as for moe_grouped_mlp_mxfp8_bwd).
  * workspace: moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes() bytes.
  */
 size_t moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes(int64_t R_cap,
@@ -575,8 +591,8 @@ int moe_grouped_mlp_mxfp8_bwd_gate_up(
     const void *dgu, const void *x_perm, const int32_t *offsets,
     int64_t n_local, int64_t R_cap, int64_t H, int64_t I, const uint8_t *wgt,
     const uint8_t *wgts, const uint8_t *wut, const uint8_t *wuts, void *dx,
-    void *dw_gate, void *dw_up, void *workspace, size_t workspace_bytes,
-    hipStream_t stream);
+    void *dw_gate, void *dw_up, int grad_format, void *workspace,
+    size_t workspace_bytes, hipStream_t stream);
 
 /*
  * moe_permute_noalloc - moe_permute without a workspace argument, for

@@ -83,8 +83,8 @@ def lib():
         L.moe_read_device_error.argtypes = [vp, vp, ctypes.POINTER(ctypes.c_int32)]
         L.moe_permute_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i32, i64,
                                           i64, i64, vp, vp, vp, vp, vp, vp, vp]
-        L.moe_mxfp8_quantize.argtypes = [vp, i64, i64, i64, i32, vp, i64, i64,
-                                         vp, i64, vp, i64, vp, vp]
+        L.moe_mxfp8_quantize.argtypes = [vp, i64, i64, i64, i32, i32, vp, i64,
+                                         i64, vp, i64, vp, i64, vp, vp]
         L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes.restype = sz
         L.moe_grouped_mlp_mxfp8_fwd.argtypes = [vp, vp, vp, vp, i64, i64, i64,
@@ -96,8 +96,8 @@ def lib():
         L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes.restype = sz
         L.moe_grouped_mlp_mxfp8_bwd.argtypes = [vp, vp, vp, vp, vp, i64,
                                                 i64, i64, i64, vp, vp, vp, vp,
-                                                vp, vp, vp, vp, vp, vp, vp, vp,
-                                                sz, vp]
+                                                vp, vp, vp, vp, vp, vp, vp, i32,
+                                                vp, sz, vp]
         L.moe_grouped_gate_up_gather.argtypes = [vp, vp, i64, i64, vp, vp, i64,
                                                  i64, i64, i64, vp, vp, i32, vp,
                                                  vp, sz, vp]
@@ -109,13 +109,13 @@ def lib():
         L.moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes.restype = sz
         L.moe_grouped_mlp_mxfp8_bwd_down.argtypes = [vp, vp, vp, vp, i64,
                                                      i64, i64, i64, vp, vp, vp,
-                                                     vp, vp, vp, sz, vp]
+                                                     vp, vp, i32, vp, sz, vp]
         L.moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes.argtypes = [i64, i64, i64, i64]
         L.moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes.restype = sz
         L.moe_grouped_mlp_mxfp8_bwd_gate_up.argtypes = [vp, vp, vp, i64, i64,
                                                         i64, i64, vp, vp, vp,
-                                                        vp, vp, vp, vp, vp, sz,
-                                                        vp]
+                                                        vp, vp, vp, vp, i32, vp,
+                                                        sz, vp]
         L.moe_mxfp8_workspace_view.argtypes = [i32, i32, i64, i64, i64, i64,
                                                 ctypes.POINTER(MxView)]
         for name in declared_functions():
@@ -443,10 +443,21 @@ def read_device_error(workspace, stream=None) -> int:
 
 # ---------------------------------------------------------------- MXFP8
 
+# MX element formats (moe_mx_format): E4M3 for every operand by default, E5M2
+# as the option for the backward's gradient operands.
+MX_FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def _mxf(fmt):
+    try:
+        return MX_FORMATS[fmt]
+    except KeyError:
+        raise ValueError(f"unknown MX element format {fmt!r}") from None
+
 
 def mxfp8_quantize(x, axis=0, seg_offsets=None, align=32, stream=None,
-                   codes=None, scales=None):
-    """MX-quantise a bf16 matrix [rows, cols].
+                   codes=None, scales=None, fmt="e4m3"):
+    """MX-quantise a bf16 matrix [rows, cols] (elements of format fmt).
 
     axis 0 -> (codes [rows, cols] u8, scales [rows, cols/32] u8).
     axis 1 -> (codesT [cols, P] u8, scalesT [cols, P/32] u8, pad_offsets or
@@ -464,8 +475,9 @@ def mxfp8_quantize(x, axis=0, seg_offsets=None, align=32, stream=None,
         if scales is None:
             scales = torch.empty((rows, cols // 32), dtype=torch.uint8, device=dev)
         assert codes.shape == (rows, cols) and scales.shape == (rows, cols // 32)
-        _call("moe_mxfp8_quantize", _p(x), rows, cols, ld_in, 0, None, 0, 32,
-              _p(codes), cols, _p(scales), cols // 32, None, _stream(stream))
+        _call("moe_mxfp8_quantize", _p(x), rows, cols, ld_in, 0, _mxf(fmt),
+              None, 0, 32, _p(codes), cols, _p(scales), cols // 32, None,
+              _stream(stream))
         return codes, scales
     nseg = 0 if seg_offsets is None else seg_offsets.numel() - 1
     if seg_offsets is None:
@@ -476,9 +488,9 @@ def mxfp8_quantize(x, axis=0, seg_offsets=None, align=32, stream=None,
     scales = torch.zeros((cols, cap // 32), dtype=torch.uint8, device=dev)
     pad = (torch.empty(nseg + 1, dtype=torch.int32, device=dev)
            if seg_offsets is not None else None)
-    _call("moe_mxfp8_quantize", _p(x), rows, cols, ld_in, 1, _p(seg_offsets),
-          nseg, align, _p(codes), cap, _p(scales), cap // 32, _p(pad),
-          _stream(stream))
+    _call("moe_mxfp8_quantize", _p(x), rows, cols, ld_in, 1, _mxf(fmt),
+          _p(seg_offsets), nseg, align, _p(codes), cap, _p(scales), cap // 32,
+          _p(pad), _stream(stream))
     return codes, scales, pad
 
 
@@ -554,7 +566,7 @@ def mxfp8_mlp_fwd(xq, xs, offsets, s_perm, mw, a=None, gu=None, y=None,
 
 def mxfp8_mlp_bwd(dy, x_perm, gu, offsets, s_perm, mw, dx=None, ds=None,
                   dw_gate=None, dw_up=None, dw_down=None, workspace=None,
-                  stream=None):
+                  stream=None, grad_format="e4m3"):
     R_cap, H = dy.shape
     I, n = mw.I, mw.n_local
     dev = dy.device
@@ -575,8 +587,8 @@ def mxfp8_mlp_bwd(dy, x_perm, gu, offsets, s_perm, mw, dx=None, ds=None,
     _call("moe_grouped_mlp_mxfp8_bwd", _p(dy), _p(x_perm), _p(gu),
           _p(offsets), _p(s_perm), n, R_cap, H, I, _p(mw.wdt), _p(mw.wdts),
           _p(mw.wgt), _p(mw.wgts), _p(mw.wut), _p(mw.wuts), _p(dx), _p(ds),
-          _p(dw_gate), _p(dw_up), _p(dw_down), _p(workspace),
-          workspace.numel(), _stream(stream))
+          _p(dw_gate), _p(dw_up), _p(dw_down), _mxf(grad_format),
+          _p(workspace), workspace.numel(), _stream(stream))
     return dict(dx=dx, ds=ds, dw_gate=dw_gate, dw_up=dw_up, dw_down=dw_down)
 
 
@@ -609,7 +621,8 @@ def grouped_linear_mxfp8(x, offsets, n_local, w, w_scales, y=None,
 
 
 def mxfp8_mlp_bwd_down(dy, gu, offsets, s_perm, mw, dgu=None, ds=None,
-                       dw_down=None, workspace=None, stream=None):
+                       dw_down=None, workspace=None, stream=None,
+                       grad_format="e4m3"):
     R_cap, H = dy.shape
     I, n = mw.I, mw.n_local
     dev = dy.device
@@ -624,12 +637,14 @@ def mxfp8_mlp_bwd_down(dy, gu, offsets, s_perm, mw, dgu=None, ds=None,
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     _call("moe_grouped_mlp_mxfp8_bwd_down", _p(dy), _p(gu), _p(offsets),
           _p(s_perm), n, R_cap, H, I, _p(mw.wdt), _p(mw.wdts), _p(dgu), _p(ds),
-          _p(dw_down), _p(workspace), workspace.numel(), _stream(stream))
+          _p(dw_down), _mxf(grad_format), _p(workspace), workspace.numel(),
+          _stream(stream))
     return dict(dgu=dgu, ds=ds, dw_down=dw_down)
 
 
 def mxfp8_mlp_bwd_gate_up(dgu, x_perm, offsets, mw, dx=None, dw_gate=None,
-                          dw_up=None, workspace=None, stream=None):
+                          dw_up=None, workspace=None, stream=None,
+                          grad_format="e4m3"):
     R_cap, H = x_perm.shape
     I, n = mw.I, mw.n_local
     dev = x_perm.device
@@ -645,6 +660,6 @@ def mxfp8_mlp_bwd_gate_up(dgu, x_perm, offsets, mw, dx=None, dw_gate=None,
         workspace = torch.empty(max(nb, 16), dtype=torch.uint8, device=dev)
     _call("moe_grouped_mlp_mxfp8_bwd_gate_up", _p(dgu), _p(x_perm),
           _p(offsets), n, R_cap, H, I, _p(mw.wgt), _p(mw.wgts), _p(mw.wut),
-          _p(mw.wuts), _p(dx), _p(dw_gate), _p(dw_up), _p(workspace),
-          workspace.numel(), _stream(stream))
+          _p(mw.wuts), _p(dx), _p(dw_gate), _p(dw_up), _mxf(grad_format),
+          _p(workspace), workspace.numel(), _stream(stream))
     return dict(dx=dx, dw_gate=dw_gate, dw_up=dw_up)

@@ -639,7 +639,7 @@ hipError_t run_down_bwd(const void *dy, const float *gu,
                         int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
                         const uint8_t *wdt, const uint8_t *wdts, void *dgu,
                         float *ds, void *dw_down, const DownBwdWs &w,
-                        int32_t *errw, int cus, hipStream_t stream,
+                        int32_t *errw, int cus, hipStream_t stream, int gf,
                         const DguCodes *codes = nullptr) {
   const int G = (int)n_local;
   const int64_t kc = w.kcap;
@@ -649,7 +649,7 @@ hipError_t run_down_bwd(const void *dy, const float *gu,
 #define MX_TRY(x) do { err = (x); if (err != hipSuccess) return err; } while (0)
   // dY along H (row-wise)
   MX_TRY(moe::launch_mx_quant_rows((const uint16_t *)dy, R_cap, H, H, w.dyq, H,
-                                   w.dys, H / 32, offsets + G, stream));
+                                   w.dys, H / 32, offsets + G, stream, gf));
   MX_TRY(moe::launch_mx_pad_offsets(offsets, G, R_cap, 256, tpad, stream));
   // da = dY W_d (K = H); SwiGLU backward in the epilogue -> dg, du, ds, and
   // the column-wise codes of a
@@ -663,6 +663,7 @@ hipError_t run_down_bwd(const void *dy, const float *gu,
     d.row_scale = s_perm; d.gu = (float *)gu; d.ldgu = 2 * I;
     d.dgu = (uint16_t *)dgu; d.ds_part = w.ds_part; d.ds = ds;
     d.t2 = w.aT; d.t2s = w.aTs; d.ldt = kc; d.ldts = kc / 32; d.tpad = tpad;
+    d.fa = gf;
     if (codes) {
       // [dg | du] quantised by the epilogue: along 2I for the dX GEMM, and
       // down each expert segment (padded to 256 rows) for dW_g, dW_u
@@ -675,9 +676,9 @@ hipError_t run_down_bwd(const void *dy, const float *gu,
   // segment, segments zero-padded to 256 rows like the codes of a
   MX_TRY(moe::launch_mx_quant_cols((const uint16_t *)dy, R_cap, H, H, offsets,
                                    G, 256, tpad, w.dyT, kc, w.dyTs, kc / 32,
-                                   cus, stream));
+                                   cus, stream, gf));
   moe::MxGemmDesc d{};
-  d.kseg = tpad; d.G = G;
+  d.kseg = tpad; d.G = G; d.fa = gf;
   d.lda = kc; d.ldas = kc / 32; d.ldb = kc; d.ldbs = kc / 32;
   d.A = w.dyT; d.As = w.dyTs; d.B0 = w.aT; d.B0s = w.aTs;
   d.M = (int)H; d.N = (int)I; d.C = dw_down; d.ldc = I; d.c_stride = H * I;
@@ -690,7 +691,7 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
                            const uint8_t *wgt, const uint8_t *wgts,
                            const uint8_t *wut, const uint8_t *wuts, void *dx,
                            void *dw_gate, void *dw_up, const GateUpBwdWs &w,
-                           int32_t *errw, int cus, hipStream_t stream,
+                           int32_t *errw, int cus, hipStream_t stream, int gf,
                            const DguCodes *codes = nullptr) {
   const int G = (int)n_local;
   hipError_t err;
@@ -701,7 +702,7 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
   if (!codes)
     MX_TRY(moe::launch_mx_quant_rows((const uint16_t *)dgu, R_cap, 2 * I, 2 * I,
                                      w.dguq, 2 * I, w.dgus, 2 * I / 32,
-                                     offsets + G, stream));
+                                     offsets + G, stream, gf));
   // dX = dg W_g + du W_u: one GEMM with K = 2I, B switching at K = I
   {
     moe::MxGemmDesc d{};
@@ -711,7 +712,7 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
     d.b_stride = I; d.bs_stride = I / 32;
     d.offsets = offsets; d.tile_ws = w.tiles; d.err = errw; d.G = G;
     d.N = (int)H; d.K = (int)(2 * I); d.R_cap = R_cap; d.ksplit = (int)I;
-    d.C = dx; d.ldc = H;
+    d.C = dx; d.ldc = H; d.fa = gf;
     MX_TRY(moe::launch_mx_rowseg(d, moe::MXE_BF16, cus, stream));
   }
   // Column-wise copies for the weight gradients: segments padded to 512
@@ -728,15 +729,15 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
     const uint16_t *dg = (const uint16_t *)dgu;
     MX_TRY(moe::launch_mx_quant_cols(dg, R_cap, I, 2 * I, offsets, G, 512,
                                      w.kpad, w.dgT, kc, w.dgTs, kc / 32, cus,
-                                     stream));
+                                     stream, gf));
     MX_TRY(moe::launch_mx_quant_cols(dg + I, R_cap, I, 2 * I, offsets, G, 512,
                                      w.kpad, w.duT, kc, w.duTs, kc / 32, cus,
-                                     stream));
+                                     stream, gf));
   }
 #undef MX_TRY
   // dW_g[e] [I, H] = dg_e^T x_e ; dW_u likewise with du
   moe::MxGemmDesc d{};
-  d.kseg = kpad; d.G = G;
+  d.kseg = kpad; d.G = G; d.fa = gf;
   d.lda = kc; d.ldas = kc / 32; d.ldb = kc; d.ldbs = kc / 32;
   d.A = dgT; d.As = dgTs; d.B0 = w.xT; d.B0s = w.xTs;
   d.M = (int)I; d.N = (int)H; d.C = dw_gate; d.ldc = H; d.c_stride = I * H;
@@ -745,6 +746,8 @@ hipError_t run_gate_up_bwd(const void *dgu, const void *x_perm,
   d.A = duT; d.As = duTs; d.C = dw_up;
   return moe::launch_mx_kseg(d, cus, stream);
 }
+
+bool grad_format_ok(int f) { return f == MOE_MX_E4M3 || f == MOE_MX_E5M2; }
 
 bool all_aligned(std::initializer_list<const void *> ps) {
   for (const void *q : ps)
@@ -757,11 +760,13 @@ bool all_aligned(std::initializer_list<const void *> ps) {
 extern "C" {
 
 int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
-                       int64_t ld_in, int axis, const int32_t *seg_offsets,
-                       int64_t n_seg, int64_t align, uint8_t *codes,
-                       int64_t ld_codes, uint8_t *scales, int64_t ld_scales,
+                       int64_t ld_in, int axis, int format,
+                       const int32_t *seg_offsets, int64_t n_seg,
+                       int64_t align, uint8_t *codes, int64_t ld_codes,
+                       uint8_t *scales, int64_t ld_scales,
                        int32_t *pad_offsets, hipStream_t stream) {
   if (axis != 0 && axis != 1) return MOE_E_ARG;
+  if (format != MOE_MX_E4M3 && format != MOE_MX_E5M2) return MOE_E_ARG;
   if (rows < 0 || cols < 1 || cols % 32 != 0 || ld_in < cols) return MOE_E_SHAPE;
   if (rows >= kMaxRows || cols >= kMaxRows) return MOE_E_SHAPE;
   if (rows == 0) return MOE_OK;
@@ -774,7 +779,7 @@ int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
     if (!aligned16(in)) return MOE_E_ALIGN;
     return status_of(moe::launch_mx_quant_rows(
         (const uint16_t *)in, rows, cols, ld_in, codes, ld_codes, scales,
-        ld_scales, nullptr, stream));
+        ld_scales, nullptr, stream, format));
   }
   if (align != 32 && align != 512) return MOE_E_SHAPE;
   if (ld_codes % 16 != 0 || ld_in % 8 != 0) return MOE_E_SHAPE;
@@ -789,7 +794,7 @@ int moe_mxfp8_quantize(const void *in, int64_t rows, int64_t cols,
   return status_of(moe::launch_mx_quant_cols(
       (const uint16_t *)in, rows, cols, ld_in, seg_offsets, (int)n_seg,
       (int)align, pad_offsets, codes, ld_codes, scales, ld_scales, num_cus(),
-      stream));
+      stream, format));
 }
 
 size_t moe_grouped_mlp_mxfp8_fwd_workspace_bytes(int64_t R_cap,
@@ -893,9 +898,10 @@ int moe_grouped_mlp_mxfp8_bwd_down(
     const void *dy, const float *gu, const int32_t *offsets,
     const float *s_perm, int64_t n_local, int64_t R_cap, int64_t H, int64_t I,
     const uint8_t *wdt, const uint8_t *wdts, void *dgu, float *ds,
-    void *dw_down, void *workspace, size_t workspace_bytes,
+    void *dw_down, int grad_format, void *workspace, size_t workspace_bytes,
     hipStream_t stream) {
   if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  if (!grad_format_ok(grad_format)) return MOE_E_ARG;
   if (R_cap == 0) return MOE_OK;
   if (!dy || !gu || !offsets || !wdt || !wdts || !dgu || !ds || !dw_down)
     return MOE_E_ARG;
@@ -908,7 +914,7 @@ int moe_grouped_mlp_mxfp8_bwd_down(
   const DownBwdWs w = carve_down_bwd(c, R_cap, n_local, H, I);
   return status_of(run_down_bwd(dy, gu, offsets, s_perm, n_local, R_cap, H,
                                 I, wdt, wdts, dgu, ds, dw_down, w, w.err,
-                                num_cus(), stream));
+                                num_cus(), stream, grad_format));
 }
 
 size_t moe_grouped_mlp_mxfp8_bwd_gate_up_workspace_bytes(int64_t R_cap,
@@ -923,9 +929,10 @@ int moe_grouped_mlp_mxfp8_bwd_gate_up(
     const void *dgu, const void *x_perm, const int32_t *offsets,
     int64_t n_local, int64_t R_cap, int64_t H, int64_t I, const uint8_t *wgt,
     const uint8_t *wgts, const uint8_t *wut, const uint8_t *wuts, void *dx,
-    void *dw_gate, void *dw_up, void *workspace, size_t workspace_bytes,
-    hipStream_t stream) {
+    void *dw_gate, void *dw_up, int grad_format, void *workspace,
+    size_t workspace_bytes, hipStream_t stream) {
   if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  if (!grad_format_ok(grad_format)) return MOE_E_ARG;
   if (R_cap == 0) return MOE_OK;
   if (!dgu || !x_perm || !offsets || !wgt || !wgts || !wut || !wuts || !dx ||
       !dw_gate || !dw_up)
@@ -939,7 +946,7 @@ int moe_grouped_mlp_mxfp8_bwd_gate_up(
   const GateUpBwdWs w = carve_gate_up_bwd(c, R_cap, n_local, H, I);
   return status_of(run_gate_up_bwd(dgu, x_perm, offsets, n_local, R_cap, H, I,
                                    wgt, wgts, wut, wuts, dx, dw_gate, dw_up, w,
-                                   w.err, num_cus(), stream));
+                                   w.err, num_cus(), stream, grad_format));
 }
 
 size_t moe_grouped_mlp_mxfp8_bwd_workspace_bytes(int64_t R_cap,
@@ -955,9 +962,10 @@ int moe_grouped_mlp_mxfp8_bwd(
     int64_t R_cap, int64_t H, int64_t I, const uint8_t *wdt,
     const uint8_t *wdts, const uint8_t *wgt, const uint8_t *wgts,
     const uint8_t *wut, const uint8_t *wuts, void *dx, float *ds,
-    void *dw_gate, void *dw_up, void *dw_down, void *workspace,
-    size_t workspace_bytes, hipStream_t stream) {
+    void *dw_gate, void *dw_up, void *dw_down, int grad_format,
+    void *workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!mx_shape_ok(n_local, R_cap, H, I)) return MOE_E_SHAPE;
+  if (!grad_format_ok(grad_format)) return MOE_E_ARG;
   if (R_cap == 0) return MOE_OK;
   if (!dy || !x_perm || !gu || !offsets || !wdt || !wdts || !wgt ||
       !wgts || !wut || !wuts || !dx || !ds || !dw_gate || !dw_up || !dw_down)
@@ -978,13 +986,14 @@ int moe_grouped_mlp_mxfp8_bwd(
   const DownBwdWs wd = carve_down_bwd(c, R_cap, n_local, H, I);
   hipError_t herr = run_down_bwd(dy, gu, offsets, s_perm, n_local, R_cap,
                                  H, I, wdt, wdts, nullptr, ds, dw_down, wd, err,
-                                 cus, stream, &codes);
+                                 cus, stream, grad_format, &codes);
   if (herr != hipSuccess) return MOE_E_HIP;
   const GateUpBwdWs wg =
       carve_gate_up_bwd(shared, R_cap, n_local, H, I, /*own_dgu=*/false);
   return status_of(run_gate_up_bwd(nullptr, x_perm, offsets, n_local, R_cap,
                                    H, I, wgt, wgts, wut, wuts, dx, dw_gate,
-                                   dw_up, wg, err, cus, stream, &codes));
+                                   dw_up, wg, err, cus, stream, grad_format,
+                                   &codes));
 }
 
 

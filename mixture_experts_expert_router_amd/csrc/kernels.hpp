@@ -119,7 +119,7 @@ hipError_t launch_mx_quant_rows(const uint16_t *in, int64_t rows, int64_t cols,
                                 int64_t ld_in, uint8_t *codes,
                                 int64_t ld_codes, uint8_t *scales,
                                 int64_t ld_scales, const int32_t *rows_dev,
-                                hipStream_t s);
+                                hipStream_t s, int fmt = 0);
 // pad[s+1] = pad[s] + ceil(len_s / align) * align, pad[0] = 0, where len_s
 // is the length of segment s cut at `rows` (see seg_rows).
 hipError_t launch_mx_pad_offsets(const int32_t *seg, int nseg, int64_t rows,
@@ -130,7 +130,7 @@ hipError_t launch_mx_quant_cols(const uint16_t *in, int64_t rows,
                                 int32_t *pad, uint8_t *codes,
                                 int64_t ld_codes, uint8_t *scales,
                                 int64_t ld_scales, int num_cus,
-                                hipStream_t s);
+                                hipStream_t s, int fmt = 0);
 
 // One MXFP8 grouped GEMM (see mx_gemm.hip for the modes and epilogues).
 struct MxGemmDesc {
@@ -164,6 +164,10 @@ struct MxGemmDesc {
   uint8_t *t0, *t0s, *t1, *t1s, *t2, *t2s;
   int64_t ldt, ldts;
   const int32_t *tpad;
+  // Element format of A (0 = E4M3, 1 = E5M2 for gradient operands); with the
+  // SwiGLU-backward epilogue also the format of the dg, du codes (q, t0,
+  // t1), while t2 (a) stays E4M3.  B is always E4M3.
+  int fa;
 };
 enum { MXE_BF16 = 0, MXE_SWIGLU = 1, MXE_SWIGLU_BWD = 2 };
 hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,

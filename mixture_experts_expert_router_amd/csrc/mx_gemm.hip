@@ -31,6 +31,12 @@
 // computed.  Two 128-value stages measured faster than four 64-value ones
 // (fewer barriers per K, twice the MFMAs per stage).  K must be a multiple
 // of 128.
+//
+// Gradient option: FA = kMxE5M2 makes A's elements E5M2 (the matrix
+// instruction's A-format field selects bf8), for the backward GEMMs whose A
+// operand is a gradient (dY, [dg | du] and their transposes); B stays E4M3.
+// The SwiGLU-backward epilogue then also writes the codes of dg and du in
+// E5M2, while the codes of a (an activation) stay E4M3.
 #include "common.hpp"
 #include "mx_codec.hpp"
 #include "kernels.hpp"
@@ -209,7 +215,7 @@ __device__ __forceinline__ void f32_block(const float *l, int r, int b,
 // row r goes to codes q[(grow0 + r) * ldq + col0 + 32 b] and scale
 // qs[(grow0 + r) * ldqs + col0 / 32 + b], for tile rows arow0 + r < rows.
 // Lanes take consecutive rows of one block column (conflict-free reads).
-template <int W, int NROWS>
+template <int W, int NROWS, int F>
 __device__ __forceinline__ void mx_quant_rows_f32(const float *l, uint8_t *q,
                                                   int64_t ldq, uint8_t *qs,
                                                   int64_t ldqs, int64_t col0,
@@ -228,7 +234,7 @@ __device__ __forceinline__ void mx_quant_rows_f32(const float *l, uint8_t *q,
     float v[32];
     f32_block<W>(l, r, b, v);
     uint32_t c[8];
-    const uint32_t sb = mx_encode32_f32(v, c);
+    const uint32_t sb = mx_encode32_f32_t<F>(v, c);
     if (arow0 + r < rows) {
       uint4 *dst = (uint4 *)(qb + ((uint32_t)r * (uint32_t)ldq + 32u * b));
       dst[0] = make_uint4(c[0], c[1], c[2], c[3]);
@@ -270,6 +276,7 @@ __device__ __forceinline__ void store_f32_as_bf16(const float *l, uint16_t *dst,
 // qt[c * ldt + pos0 .. + 32) (the first 16 bytes written by half 0, the rest
 // by half 1) and its scale byte to qts[c * ldts + pos0 / 32].  The launcher
 // keeps 32 * ldt below 2^32.
+template <int F>
 __device__ __forceinline__ void mx_quant_col_block(const float (&v)[16],
                                                    int lane, uint8_t *qt,
                                                    uint8_t *qts, int64_t ldt,
@@ -279,11 +286,11 @@ __device__ __forceinline__ void mx_quant_col_block(const float (&v)[16],
 #pragma unroll
   for (int i = 0; i < 16; ++i) mag = fmaxf(mag, fabsf(v[i]));
   mag = fmaxf(mag, __shfl_xor(mag, 32, 64));
-  const int X = mx_shared_exp(mag);
+  const int X = mx_shared_exp_t<F>(mag);
   uint32_t d[4];                 // rows 8q + 4h .. 8q + 4h + 3
 #pragma unroll
   for (int q = 0; q < 4; ++q)
-    d[q] = e4m3_pack4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], -X);
+    d[q] = pack4_t<F>(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3], -X);
   const int h = lane >> 5;
   // half 0 writes rows 0-15 (its d0, d1 and the partner's), half 1 rows 16-31
   const uint32_t x0 = h ? d[0] : d[2], x1 = h ? d[1] : d[3];
@@ -415,11 +422,12 @@ __device__ __forceinline__ float mx_sum16_over32(const float (&v)[16], int lane)
 // du = da s SiLU(g), ds partial = sum over the wavefront's 128 columns of
 // da SiLU(g) u.  dg and du replace g and u in the regions (for the row-wise
 // outputs that follow); the column-wise MX codes of dg, du (t0, t1) and of a
-// (t2) are written from the registers, rows past the segment (tile row >=
+// (t2) are written from the registers (dg, du in the gradient format FG, a in
+// E4M3), rows past the segment (tile row >=
 // rows) counting as zeros, i.e. as the segment's padding.  pos0: padded
 // position of the block's first row.  s_reg: lane l holds the routing scale
 // of wavefront row (32 m & 64) + l.
-template <int BN, int WN, int NB>
+template <int BN, int WN, int NB, int FG>
 __device__ __forceinline__ void mx_swiglu_bwd_block(
     const MxArgs &p, const f32x16 (&am)[NB], int m, int lane, int arow0,
     int rows, int row0, int nt, int wn, float s_reg, float *lg, float *lu,
@@ -448,7 +456,7 @@ __device__ __forceinline__ void mx_swiglu_bwd_block(
       v[r] = mrow0 + row < rows ? s * sl * u : 0.f;   // a (padding rows: 0)
     }
     const int64_t c = col0 + n * 32;
-    if (p.t2) mx_quant_col_block(v, lane, p.t2, p.t2s, p.ldt, p.ldts, c, pos0);
+    if (p.t2) mx_quant_col_block<kMxE4M3>(v, lane, p.t2, p.t2s, p.ldt, p.ldts, c, pos0);
     if (p.t0) {
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
@@ -459,8 +467,8 @@ __device__ __forceinline__ void mx_swiglu_bwd_block(
           const float x = src[row * 128 + fphys<128>(row, n * 32 + (lane & 31))];
           v[r] = mrow0 + row < rows ? x : 0.f;
         }
-        if (t) mx_quant_col_block(v, lane, p.t1, p.t1s, p.ldt, p.ldts, c, pos0);
-        else mx_quant_col_block(v, lane, p.t0, p.t0s, p.ldt, p.ldts, c, pos0);
+        if (t) mx_quant_col_block<FG>(v, lane, p.t1, p.t1s, p.ldt, p.ldts, c, pos0);
+        else mx_quant_col_block<FG>(v, lane, p.t0, p.t0s, p.ldt, p.ldts, c, pos0);
       }
     }
     // keep the column blocks in sequence: interleaving them only raises the
@@ -475,7 +483,7 @@ __device__ __forceinline__ void mx_swiglu_bwd_block(
   if ((lane & 1) == 0 && mrow0 + rr < rows) dp[(uint32_t)rr * (uint32_t)ntw] = tot;
 }
 
-template <int MODE, int EPI, int BM, int BN, int WM, int WN, int STAGES, int BKB>
+template <int MODE, int EPI, int FA, int BM, int BN, int WM, int WN, int STAGES, int BKB>
 __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
   // BKB: K values (code bytes) per stage; a stage carries, for every A and B
   // row, its 128 codes and the scale dword of their four 32-value blocks.
@@ -682,7 +690,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
         for (int n = 0; n < NB; ++n) {
           const int f = m * NB + n;
           acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af0[m], bf0[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> (8 * h)) & 0xffu),
+              af0[m], bf0[n], acc[m][n], FA, kMxE4M3, 0, (int)((sa[m] >> (8 * h)) & 0xffu),
               0, (int)((sbv[n] >> (8 * h)) & 0xffu));
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -700,7 +708,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
         for (int n = 0; n < NB; ++n) {
           const int g = m * NB + n;
           acc[m][n] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              af1[m], bf1[n], acc[m][n], 0, 0, 0, (int)((sa[m] >> (8 * (2 + h))) & 0xffu),
+              af1[m], bf1[n], acc[m][n], FA, kMxE4M3, 0, (int)((sa[m] >> (8 * (2 + h))) & 0xffu),
               0, (int)((sbv[n] >> (8 * (2 + h))) & 0xffu));
           __builtin_amdgcn_sched_barrier(0);
           if (g == 1) {
@@ -765,7 +773,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
     }
     __syncthreads();
     store_f32_as_bf16<64, 128>(la, (uint16_t *)p.C, p.ldc, col0, p.N, grow0, arow0, rows, lane);
-    if (p.q) mx_quant_rows_f32<64, 128>(la, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, arow0, rows, lane);
+    if (p.q) mx_quant_rows_f32<64, 128, kMxE4M3>(la, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, arow0, rows, lane);
   } else if constexpr (EPI == MX_EPI_SWIGLU_BWD) {
     static_assert(WTM == 128 && WTN == 128 && MB == 4, "staging expects 128x128 wavefront tiles");
     // region: fp32 g and u of one 32-row block x 128 columns ([32][128] each)
@@ -802,7 +810,7 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
       }
       mx_load_gu32(lgb, lub, gb, ub, p.ldgu, ar0, rows, lane);
       mx_wait_barrier<0>();
-      mx_swiglu_bwd_block<BN, WN, NB>(p, cur, m, lane, arow0, rows, row0, nt, wn,
+      mx_swiglu_bwd_block<BN, WN, NB, FA>(p, cur, m, lane, arow0, rows, row0, nt, wn,
                                       m < 2 ? s_lo : s_hi, lg, lu, col0, pbase + ar0);
       __syncthreads();
       if (p.dgu) {
@@ -810,8 +818,8 @@ __global__ __launch_bounds__(256) void mx_gemm_kernel(MxArgs p) {
         store_f32_as_bf16<128, 32>(lu, p.dgu + p.N, p.ldgu, col0, p.N, grow0, ar0, rows, lane);
       }
       if (p.q) {
-        mx_quant_rows_f32<128, 32>(lg, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, ar0, rows, lane);
-        mx_quant_rows_f32<128, 32>(lu, p.q, p.ldq, p.qs, p.ldqs, p.N + col0, grow0, ar0, rows, lane);
+        mx_quant_rows_f32<128, 32, FA>(lg, p.q, p.ldq, p.qs, p.ldqs, col0, grow0, ar0, rows, lane);
+        mx_quant_rows_f32<128, 32, FA>(lu, p.q, p.ldq, p.qs, p.ldqs, p.N + col0, grow0, ar0, rows, lane);
       }
       __syncthreads();
     }
@@ -852,9 +860,9 @@ namespace {
 constexpr int kMxCfg[6] = {MOE_MX_CFG};
 constexpr int kMxBM = kMxCfg[0], kMxBN = kMxCfg[1], kMxWN = kMxCfg[3];
 
-template <int MODE, int EPI>
+template <int MODE, int EPI, int FA>
 hipError_t mx_launch(const MxArgs &p, int64_t max_tiles, hipStream_t s) {
-  mx_gemm_kernel<MODE, EPI, MOE_MX_CFG>
+  mx_gemm_kernel<MODE, EPI, FA, MOE_MX_CFG>
       <<<(unsigned)tile_grid(max_tiles), 256, 0, s>>>(p);
   return hipGetLastError();
 }
@@ -896,9 +904,17 @@ hipError_t launch_mx_rowseg(const MxGemmDesc &d, int epi, int num_cus,
   if (epi == MX_EPI_SWIGLU_BWD && (int64_t)kMxBM * d.ldgu * 4 >= (1ll << 32))
     return hipErrorInvalidValue;
   const int64_t max_tiles = ((d.R_cap + kMxBM - 1) / kMxBM + d.G) * (int64_t)p.NT;
-  if (epi == MX_EPI_SWIGLU) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU>(p, max_tiles, s);
-  else if (epi == MX_EPI_SWIGLU_BWD) err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU_BWD>(p, max_tiles, s);
-  else err = mx_launch<MX_ROWSEG, MX_EPI_BF16>(p, max_tiles, s);
+  // A in E5M2 only where A is a gradient: the SwiGLU backward and dX
+  if (d.fa == kMxE5M2 && epi == MX_EPI_SWIGLU) return hipErrorInvalidValue;
+  if (epi == MX_EPI_SWIGLU)
+    err = mx_launch<MX_ROWSEG, MX_EPI_SWIGLU, kMxE4M3>(p, max_tiles, s);
+  else if (epi == MX_EPI_SWIGLU_BWD)
+    err = d.fa == kMxE5M2
+              ? mx_launch<MX_ROWSEG, MX_EPI_SWIGLU_BWD, kMxE5M2>(p, max_tiles, s)
+              : mx_launch<MX_ROWSEG, MX_EPI_SWIGLU_BWD, kMxE4M3>(p, max_tiles, s);
+  else
+    err = d.fa == kMxE5M2 ? mx_launch<MX_ROWSEG, MX_EPI_BF16, kMxE5M2>(p, max_tiles, s)
+                          : mx_launch<MX_ROWSEG, MX_EPI_BF16, kMxE4M3>(p, max_tiles, s);
   if (err != hipSuccess || epi != MX_EPI_SWIGLU_BWD) return err;
   mx_ds_reduce_kernel<<<(unsigned)num_cus, 256, 0, s>>>(
       d.ds_part, p.NT * kMxWN, d.offsets + d.G, d.ds);
@@ -915,7 +931,9 @@ hipError_t launch_mx_kseg(const MxGemmDesc &d, int num_cus, hipStream_t s) {
   p.MT = (d.M + kMxBM - 1) / kMxBM;
   p.NT = (d.N + kMxBN - 1) / kMxBN;
   p.C = d.C; p.ldc = d.ldc; p.c_stride = d.c_stride;
-  return mx_launch<MX_KSEG, MX_EPI_BF16>(p, (int64_t)d.G * p.MT * p.NT, s);
+  const int64_t tiles = (int64_t)d.G * p.MT * p.NT;
+  return d.fa == kMxE5M2 ? mx_launch<MX_KSEG, MX_EPI_BF16, kMxE5M2>(p, tiles, s)
+                         : mx_launch<MX_KSEG, MX_EPI_BF16, kMxE4M3>(p, tiles, s);
 }
 
 }  // namespace moe

@@ -14,6 +14,10 @@
 // default rounding mode.  Four values cost about five VALU instructions.
 // The GPU tests run every finite bf16 value under every shared exponent
 // through both kernels and compare the codes with the oracle bit for bit.
+//
+// F = kMxE5M2 (the gradient option) quantises to E5M2 elements instead:
+// X = floor(log2(max |v|)) - 15, a clamp to +-57344 and gfx950's
+// v_cvt_pk_bf8_f32 (nearest, ties to even); tested the same way.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "mx_codec.hpp"
@@ -24,6 +28,7 @@ namespace moe {
 //   in [rows, cols] bf16 (row pitch ld_in), codes [rows, ld_codes] (first
 //   cols used), scales [rows, ld_scales].  rows_dev (may be null): a device
 //   row count below `rows`; rows past it are left alone.
+template <int F>
 __global__ __launch_bounds__(256) void mx_quant_rows_kernel(
     const uint16_t *__restrict__ in, int64_t rows, int64_t cols,
     int64_t ld_in, uint8_t *__restrict__ codes, int64_t ld_codes,
@@ -49,11 +54,11 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(
   float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-  const int X = mx_shared_exp(amax);
+  const int X = mx_shared_exp_t<F>(amax);
   uint32_t packed[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j)
-    packed[j] = e4m3_pack4(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], -X);
+    packed[j] = pack4_t<F>(v[4 * j], v[4 * j + 1], v[4 * j + 2], v[4 * j + 3], -X);
   uint4 *dst = (uint4 *)(codes + r * ld_codes + b * 32);
   dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
@@ -73,6 +78,7 @@ __global__ __launch_bounds__(256) void mx_quant_rows_kernel(
 // column's four scale bytes as one dword.
 // Requires ld_in % 8 == 0, ld_codes % 16 == 0, cols % 32 == 0 and 16-byte
 // aligned input and codes.
+template <int F>
 __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
     const uint16_t *__restrict__ in, int64_t rows, int64_t cols,
     int64_t ld_in, const int32_t *__restrict__ seg,
@@ -153,11 +159,11 @@ __global__ __launch_bounds__(256) void mx_quant_cols_kernel(
         x[j] = bf16_bits_to_f32(tile[(b * 32 + j) * LDT + c]);
         amax = fmaxf(amax, fabsf(x[j]));
       }
-      const int X = mx_shared_exp(amax);
+      const int X = mx_shared_exp_t<F>(amax);
       uint32_t pk[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)
-        pk[j] = e4m3_pack4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], -X);
+        pk[j] = pack4_t<F>(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3], -X);
       uint4 *o = (uint4 *)(ostage + c * LDO + b * 32);
       o[0] = make_uint4(pk[0], pk[1], pk[2], pk[3]);
       o[1] = make_uint4(pk[4], pk[5], pk[6], pk[7]);
@@ -223,11 +229,16 @@ hipError_t launch_mx_quant_rows(const uint16_t *in, int64_t rows, int64_t cols,
                                 int64_t ld_in, uint8_t *codes,
                                 int64_t ld_codes, uint8_t *scales,
                                 int64_t ld_scales, const int32_t *rows_dev,
-                                hipStream_t s) {
+                                hipStream_t s, int fmt) {
   const int64_t n = rows * (cols / 32);
   if (n == 0) return hipSuccess;
-  mx_quant_rows_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-      in, rows, cols, ld_in, codes, ld_codes, scales, ld_scales, rows_dev);
+  const unsigned grid = (unsigned)((n + 255) / 256);
+  if (fmt == kMxE5M2)
+    mx_quant_rows_kernel<kMxE5M2><<<grid, 256, 0, s>>>(
+        in, rows, cols, ld_in, codes, ld_codes, scales, ld_scales, rows_dev);
+  else
+    mx_quant_rows_kernel<kMxE4M3><<<grid, 256, 0, s>>>(
+        in, rows, cols, ld_in, codes, ld_codes, scales, ld_scales, rows_dev);
   return hipGetLastError();
 }
 
@@ -243,26 +254,32 @@ hipError_t launch_mx_quant_cols(const uint16_t *in, int64_t rows,
                                 int32_t *pad, uint8_t *codes,
                                 int64_t ld_codes, uint8_t *scales,
                                 int64_t ld_scales, int num_cus,
-                                hipStream_t s) {
+                                hipStream_t s, int fmt) {
   if (seg) {
     mx_pad_offsets_kernel<<<1, 1024, 0, s>>>(seg, nseg, (int)rows, align, pad);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  // As many workgroups as fit on the chip at once (LDS bounds them).
+  // As many workgroups as fit on the chip at once (LDS bounds them; both
+  // element formats use the same resources).
   static int per_cu = 0;
   if (per_cu == 0) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mx_quant_cols_kernel,
-                                                     256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &n, mx_quant_cols_kernel<kMxE4M3>, 256, 0) != hipSuccess ||
         n < 1)
       n = 4;
     per_cu = n;
   }
-  const int64_t grid = (int64_t)num_cus * per_cu;
-  mx_quant_cols_kernel<<<(unsigned)grid, 256, 0, s>>>(
-      in, rows, cols, ld_in, seg, pad, nseg, align, codes, ld_codes, scales,
-      ld_scales);
+  const unsigned grid = (unsigned)((int64_t)num_cus * per_cu);
+  if (fmt == kMxE5M2)
+    mx_quant_cols_kernel<kMxE5M2><<<grid, 256, 0, s>>>(
+        in, rows, cols, ld_in, seg, pad, nseg, align, codes, ld_codes, scales,
+        ld_scales);
+  else
+    mx_quant_cols_kernel<kMxE4M3><<<grid, 256, 0, s>>>(
+        in, rows, cols, ld_in, seg, pad, nseg, align, codes, ld_codes, scales,
+        ld_scales);
   return hipGetLastError();
 }
 

@@ -15,19 +15,22 @@ import numpy as np
 
 import oracle as orc
 
-_LUT = np.array([orc.e4m3_value(c) for c in range(256)])
+_LUT = {"e4m3": np.array([orc.e4m3_value(c) for c in range(256)]),
+        "e5m2": np.array([orc.e5m2_value(c) for c in range(256)])}
+_ENCODE = {"e4m3": orc.e4m3_encode_array, "e5m2": orc.e5m2_encode_array}
 
 
-def _scale_bytes(amax):
-    return np.vectorize(orc.mx_scale_byte, otypes=[np.uint8])(amax)
+def _scale_bytes(amax, fmt):
+    return np.vectorize(lambda a: orc.mx_scale_byte(a, fmt), otypes=[np.uint8])(amax)
 
 
-def check_block_decisions(v, delta, codes, scales):
+def check_block_decisions(v, delta, codes, scales, fmt="e4m3"):
     """v [rows, cols] fp64 (blocks of 32 along each row, a shorter last
     block padded with zeros), delta [rows, cols] >= 0, codes [rows, cols] u8
-    and scales [rows, ceil(cols/32)] u8 from the device.  Returns (number of
-    inadmissible scales, number of inadmissible codes, number of codes that
-    differ from the oracle's own quantisation of v)."""
+    and scales [rows, ceil(cols/32)] u8 from the device, elements of format
+    fmt.  Returns (number of inadmissible scales, number of inadmissible
+    codes, number of codes that differ from the oracle's own quantisation of
+    v)."""
     v = np.asarray(v, dtype=np.float64)
     rows, cols = v.shape
     nb = -(-cols // 32)
@@ -36,19 +39,20 @@ def check_block_decisions(v, delta, codes, scales):
     db = np.pad(delta, ((0, 0), (0, padc))).reshape(rows, nb, 32)
     amax = np.abs(vb).max(axis=2)
     dmax = db.max(axis=2)
-    lo = _scale_bytes(np.maximum(amax - dmax, 0.0))
-    hi = _scale_bytes(amax + dmax)
+    lo = _scale_bytes(np.maximum(amax - dmax, 0.0), fmt)
+    hi = _scale_bytes(amax + dmax, fmt)
     sc = np.asarray(scales, dtype=np.int64)[:, :nb]
     bad_s = int(((sc < lo) | (sc > hi)).sum())
     # codes at the scale the device chose: between the roundings of v - d
     # and v + d at that scale (rounding is monotone in the value)
     X = np.repeat(sc - 127, 32, axis=1)[:, :cols].astype(np.float64)
     inv = 2.0 ** (-X)
-    c_lo = orc.e4m3_encode_array((v - delta) * inv)
-    c_hi = orc.e4m3_encode_array((v + delta) * inv)
-    got = _LUT[np.asarray(codes)[:, :cols]]
-    bad_c = int(((got < _LUT[c_lo]) | (got > _LUT[c_hi])).sum())
-    rc, _ = orc.mx_quantize_rows(v)
+    lut = _LUT[fmt]
+    c_lo = _ENCODE[fmt]((v - delta) * inv)
+    c_hi = _ENCODE[fmt]((v + delta) * inv)
+    got = lut[np.asarray(codes)[:, :cols]]
+    bad_c = int(((got < lut[c_lo]) | (got > lut[c_hi])).sum())
+    rc, _ = orc.mx_quantize_rows(v, fmt)
     differ = int((np.asarray(codes)[:, :cols] != rc).sum())
     return bad_s, bad_c, differ
 
@@ -64,7 +68,8 @@ def segment_columns(v, offsets, pad, width):
     return out
 
 
-def dequantize(codes, scales):
+def dequantize(codes, scales, fmt="e4m3"):
     """Exact fp64 values of device codes and scales (blocks along rows)."""
     c = np.ascontiguousarray(np.asarray(codes, dtype=np.uint8))
-    return orc.mx_dequantize_rows(c, np.ascontiguousarray(scales[:, :-(-c.shape[1] // 32)]))
+    return orc.mx_dequantize_rows(c, np.ascontiguousarray(scales[:, :-(-c.shape[1] // 32)]),
+                                  fmt)

@@ -222,15 +222,17 @@ def test_combine_validation(L):
 
 def test_mxfp8_validation(L):
     q = L.moe_mxfp8_quantize
-    # axis, cols % 32, alignment, align value, capacity, segments need pad
-    assert q(P, 64, 64, 64, 2, None, 0, 32, P, 64, P, 2, None, None) == E_ARG
-    assert q(P, 64, 48, 48, 0, None, 0, 32, P, 48, P, 2, None, None) == E_SHAPE
-    assert q(P, 64, 64, 64, 0, None, 0, 32, P_ODD, 64, P, 2, None, None) == E_ALIGN
-    assert q(P, 64, 64, 64, 1, None, 0, 16, P, 64, P, 2, None, None) == E_SHAPE
-    assert q(P, 64, 64, 64, 1, None, 0, 32, P, 48, P, 2, None, None) == E_SHAPE
-    assert q(P, 64, 64, 64, 1, P, 2, 32, P, 128, P, 4, None, None) == E_ARG
-    assert q(P, 64, 64, 64, 1, P, 2, 32, P, 80, P, 4, P, None) == E_SHAPE
-    assert q(P, 0, 64, 64, 0, None, 0, 32, P, 64, P, 2, None, None) == 0
+    # axis, format, cols % 32, alignment, align value, capacity, segments
+    # need pad
+    assert q(P, 64, 64, 64, 2, 0, None, 0, 32, P, 64, P, 2, None, None) == E_ARG
+    assert q(P, 64, 64, 64, 0, 2, None, 0, 32, P, 64, P, 2, None, None) == E_ARG
+    assert q(P, 64, 48, 48, 0, 0, None, 0, 32, P, 48, P, 2, None, None) == E_SHAPE
+    assert q(P, 64, 64, 64, 0, 1, None, 0, 32, P_ODD, 64, P, 2, None, None) == E_ALIGN
+    assert q(P, 64, 64, 64, 1, 0, None, 0, 16, P, 64, P, 2, None, None) == E_SHAPE
+    assert q(P, 64, 64, 64, 1, 0, None, 0, 32, P, 48, P, 2, None, None) == E_SHAPE
+    assert q(P, 64, 64, 64, 1, 0, P, 2, 32, P, 128, P, 4, None, None) == E_ARG
+    assert q(P, 64, 64, 64, 1, 1, P, 2, 32, P, 80, P, 4, P, None) == E_SHAPE
+    assert q(P, 0, 64, 64, 0, 1, None, 0, 32, P, 64, P, 2, None, None) == 0
 
     fb = L.moe_grouped_mlp_mxfp8_fwd_workspace_bytes
     assert fb(100, 4, 512, 512) > 0 and fb(100, 4, 500, 512) == 0
@@ -269,17 +271,21 @@ def test_mxfp8_validation(L):
     # the fused call keeps the MX codes of [dg | du] beside the down workspace
     assert db > 0 and gb > 0 and bb >= db + 64 * 2 * 512
     d = L.moe_grouped_mlp_mxfp8_bwd_down
-    assert d(P, None, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db, None) == E_ARG
-    assert d(P, P, P, None, 2, 64, 512, 512, P, P, P, P, P, P, db - 1, None) == E_WS
+    assert d(P, None, P, None, 2, 64, 512, 512, P, P, P, P, P, 0, P, db, None) == E_ARG
+    assert d(P, P, P, None, 2, 64, 512, 512, P, P, P, P, P, 0, P, db - 1, None) == E_WS
+    assert d(P, P, P, None, 2, 64, 512, 512, P, P, P, P, P, 2, P, db, None) == E_ARG
     u = L.moe_grouped_mlp_mxfp8_bwd_gate_up
-    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, None, P, P, P, gb, None) == E_ARG
-    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P_ODD, P, gb, None) == E_ALIGN
-    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P, P, gb - 1, None) == E_WS
+    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, None, P, P, 0, P, gb, None) == E_ARG
+    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P_ODD, 1, P, gb, None) == E_ALIGN
+    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P, 1, P, gb - 1, None) == E_WS
+    assert u(P, P, P, 2, 64, 512, 512, P, P, P, P, P, P, P, -1, P, gb, None) == E_ARG
     b = L.moe_grouped_mlp_mxfp8_bwd
-    args = [P, P, P, P, None, 2, 64, 512, 512] + [P] * 11 + [P, bb, None]
+    args = [P, P, P, P, None, 2, 64, 512, 512] + [P] * 11 + [0, P, bb, None]
     bad = list(args); bad[-2] = bb - 1
     assert b(*bad) == E_WS
     bad = list(args); bad[0] = None
+    assert b(*bad) == E_ARG
+    bad = list(args); bad[-4] = 5
     assert b(*bad) == E_ARG
 
 

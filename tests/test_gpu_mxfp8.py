@@ -196,8 +196,9 @@ def _ws(n, dev="cuda"):
     return torch.empty(max(n, 16), dtype=torch.uint8, device=dev)
 
 
-def _run_fused(c, x_perm=None, offs=None, st=None, mw=None, dy=None):
-    """Fused forward (one call) and fused backward, keeping the workspaces."""
+def _run_fused(c, x_perm=None, offs=None, st=None, mw=None, dy=None, gf="e4m3"):
+    """Fused forward (one call) and fused backward (gradient operands in
+    format gf), keeping the workspaces."""
     xt = to_dev(c["x_perm"] if x_perm is None else x_perm)
     xq, xs = moe.mxfp8_quantize(xt, 0)
     offs = c["offs"] if offs is None else offs
@@ -209,7 +210,7 @@ def _run_fused(c, x_perm=None, offs=None, st=None, mw=None, dy=None):
     ws_b = _ws(L.moe_grouped_mlp_mxfp8_bwd_workspace_bytes(R_cap, mw.n_local, H, mw.I))
     a, gu, y = moe.mxfp8_mlp_fwd(xq, xs, offs, st, mw, workspace=ws_f)
     g = moe.mxfp8_mlp_bwd(to_dev(c["dy"] if dy is None else dy), xt, gu, offs,
-                          st, mw, workspace=ws_b)
+                          st, mw, workspace=ws_b, grad_format=gf)
     return dict(xt=xt, a=a, gu=gu, y=y, g=g, ws_f=ws_f, ws_b=ws_b, R_cap=R_cap)
 
 
@@ -218,16 +219,17 @@ def _rows_delta(v):
     return np.broadcast_to(TAU_DEC * rms, np.shape(v))
 
 
-def _decisions(what, v, delta, codes, scales, bad):
-    bs, bc, differ = check_block_decisions(v, delta, codes, scales)
+def _decisions(what, v, delta, codes, scales, bad, fmt="e4m3"):
+    bs, bc, differ = check_block_decisions(v, delta, codes, scales, fmt)
     print_case(what, f"codes differing from the oracle's {differ} of {np.size(v)}, "
                f"inadmissible scales {bs}, codes {bc}")
     if bs or bc:
         bad.append(f"{what}: {bs} scales, {bc} codes inadmissible")
 
 
-def _verify_fused(c, run, ref, offsets, wl, tag, bad, experts=None):
-    """The checks of the module docstring on one fused forward + backward."""
+def _verify_fused(c, run, ref, offsets, wl, tag, bad, experts=None, gf="e4m3"):
+    """The checks of the module docstring on one fused forward + backward
+    (gradient codes in format gf)."""
     R, H, I, n = int(offsets[-1]), wl.H, wl.I, wl.n_local
     inp = c["inp"]
     a, gu, y, g = run["a"], run["gu"], run["y"], run["g"]
@@ -257,8 +259,8 @@ def _verify_fused(c, run, ref, offsets, wl, tag, bad, experts=None):
     dgu = np.concatenate([ref["dg"], ref["du"]], axis=1)
     q, qs, _ = view(moe.MXT_DGU_ROWS)
     q, qs = q[:R].cpu().numpy(), qs[:R].cpu().numpy()
-    _decisions(f"{tag} MX([dg | du]) rows", dgu, _rows_delta(dgu), q, qs, bad)
-    d_dev = dequantize(q, qs)
+    _decisions(f"{tag} MX([dg | du]) rows", dgu, _rows_delta(dgu), q, qs, bad, gf)
+    d_dev = dequantize(q, qs, gf)
     dx_ref = np.zeros((R, H))
     for e in live:
         sl = slice(int(offsets[e]), int(offsets[e + 1]))
@@ -275,8 +277,8 @@ def _verify_fused(c, run, ref, offsets, wl, tag, bad, experts=None):
         W = int(pad[-1])
         vt = segment_columns(vref, offsets, pad, W)
         dt = segment_columns(_rows_delta(vref), offsets, pad, W)
-        _decisions(f"{tag} MX({key[3:]}) columns", vt, dt, cq[:, :W], cs, bad)
-        c_dev = dequantize(cq[:, :W], cs)
+        _decisions(f"{tag} MX({key[3:]}) columns", vt, dt, cq[:, :W], cs, bad, gf)
+        c_dev = dequantize(cq[:, :W], cs, gf)
         for e in experts:
             r0, r1 = int(offsets[e]), int(offsets[e + 1])
             if r1 == r0:
@@ -299,7 +301,7 @@ def test_mxfp8_fused_forward_backward(case):
     assert not bad, bad
 
 
-def _verify_dw_down(c, run, ref, offsets, wl, tag, bad, experts=None):
+def _verify_dw_down(c, run, ref, offsets, wl, tag, bad, experts=None, gf="e4m3"):
     """dW_down: the stage call (same epilogue and codes as the fused call,
     which it must equal bit for bit) leaves the column-wise MX(a) in its
     workspace; check those decisions against the oracle's a, then dW_down
@@ -308,7 +310,7 @@ def _verify_dw_down(c, run, ref, offsets, wl, tag, bad, experts=None):
     R_cap = run["R_cap"]
     ws = _ws(moe.lib().moe_grouped_mlp_mxfp8_bwd_down_workspace_bytes(R_cap, n, H, I))
     d1 = moe.mxfp8_mlp_bwd_down(to_dev(c["dy"]), run["gu"], c["offs"], c["st"],
-                                c["mw"], workspace=ws)
+                                c["mw"], workspace=ws, grad_format=gf)
     moe.debug_sync()
     assert torch.equal(d1["dw_down"], run["g"]["dw_down"]), f"{tag} stage dw_down"
     assert torch.equal(d1["ds"][:R], run["g"]["ds"][:R]), f"{tag} stage ds"
@@ -324,7 +326,7 @@ def _verify_dw_down(c, run, ref, offsets, wl, tag, bad, experts=None):
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 == r0:
             continue
-        qdy = orc.mx_roundtrip_rows(np.ascontiguousarray(dyf[r0:r1].T))      # [H, n_e]
+        qdy = orc.mx_roundtrip_rows(np.ascontiguousarray(dyf[r0:r1].T), gf)  # [H, n_e]
         wref = orc.matmul_nt(qdy, a_dev[:, pad[e]:pad[e] + (r1 - r0)])
         _check(to_f64(d1["dw_down"][e]), wref, f"{tag} dw_down[{e}] (device codes)", bad)
 
@@ -523,3 +525,92 @@ def test_mxfp8_step_captured_in_a_graph_replays_bit_exactly(case):
         for key in ("dw_gate", "dw_up", "dw_down"):
             assert torch.equal(outs[key], ref[key]), (rep, key)
         _ = (xt.float().sum() + dyt.float().sum()).item()
+
+
+# ---------------------------------------------------------------- E5M2 gradients
+
+
+@pytest.fixture(scope="module")
+def exhaustive5():
+    blk = exhaustive_blocks()
+    rc, rs = orc.mx_quantize_rows(orc.to_f64(blk), "e5m2")
+    return blk, rc, rs.reshape(-1)
+
+
+@pytest.mark.timeout(300)
+def test_quantize_e5m2_every_bf16_at_every_scale(exhaustive5):
+    """Every finite bf16 value under every E5M2 shared exponent, through the
+    row and the column quantiser, bit for bit against the oracle."""
+    blk, rc, rs = exhaustive5
+    C = 1024
+    print_case("exhaustive E5M2 quantisation blocks", blk.shape[0])
+    x = np.ascontiguousarray(blk.reshape(-1, C))
+    codes, scales = moe.mxfp8_quantize(to_dev(x), 0, fmt="e5m2")
+    g = blk.shape[0] // C
+    xc = np.ascontiguousarray(blk.reshape(g, C, 32).transpose(0, 2, 1).reshape(g * 32, C))
+    ccodes, cscales, _ = moe.mxfp8_quantize(to_dev(xc), 1, fmt="e5m2")
+    moe.debug_sync()
+    np.testing.assert_array_equal(scales.cpu().numpy().reshape(-1), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy().reshape(-1, 32), rc)
+    np.testing.assert_array_equal(
+        ccodes.cpu().numpy(), rc.reshape(g, C, 32).transpose(1, 0, 2).reshape(C, g * 32))
+    np.testing.assert_array_equal(cscales.cpu().numpy(), rs.reshape(g, C).T)
+
+
+def _ref5(c):
+    if "ref5" not in c:
+        c["ref5"] = orc.mxfp8_mlp_step(c["x_perm"], c["p"]["offsets"],
+                                       c["s"].astype(np.float64), c["inp"]["w_gate"],
+                                       c["inp"]["w_up"], c["inp"]["w_down"], c["dy"],
+                                       grad_fmt="e5m2")
+    return c["ref5"]
+
+
+def test_mxfp8_fused_backward_e5m2_gradients(case):
+    """The fused backward with dY, dg, du in E5M2 against the oracle step
+    with grad_fmt="e5m2", by the rule of the module docstring (decisions of
+    the [dg | du] codes in E5M2, every GEMM output from the device's codes)."""
+    c = case
+    ref = _ref5(c)
+    run = _run_fused(c, gf="e5m2")
+    moe.debug_sync()
+    bad = []
+    tag = f"{c['name']} e5m2"
+    _verify_fused(c, run, ref, c["p"]["offsets"], c["wl"], tag, bad, gf="e5m2")
+    _verify_dw_down(c, run, ref, c["p"]["offsets"], c["wl"], tag, bad, gf="e5m2")
+    assert not bad, bad
+
+
+def test_mxfp8_backward_stages_e5m2_gradients(case):
+    """The two backward stage calls with E5M2 gradient operands against the
+    oracle's stage functions with grad_fmt="e5m2" on the same given inputs."""
+    c, ref, R, I = case, case["ref"], case["p"]["R"], case["wl"].I
+    g32 = ref["g"].astype(np.float32)
+    u32 = ref["u"].astype(np.float32)
+    gu = np.ascontiguousarray(np.concatenate([g32, u32], axis=1))
+    out = moe.mxfp8_mlp_bwd_down(to_dev(c["dy"]), to_dev(gu), c["offs"],
+                                 c["st"], c["mw"], grad_format="e5m2")
+    moe.debug_sync()
+    sref = orc.mxfp8_backward_down(c["dy"], g32, u32, c["s"].astype(np.float64),
+                                   c["p"]["offsets"], c["inp"]["w_down"],
+                                   grad_fmt="e5m2")
+    bad = []
+    n = c["name"] + " e5m2"
+    _check(to_f64(out["dgu"][:R, :I]), sref["dg"], f"{n} stage dg", bad)
+    _check(to_f64(out["dgu"][:R, I:]), sref["du"], f"{n} stage du", bad)
+    _check(_ds(out["ds"], R), sref["ds"], f"{n} stage ds", bad, "f32")
+    for e in range(c["wl"].n_local):
+        _check(to_f64(out["dw_down"][e]), sref["dw_down"][e], f"{n} stage dw_down[{e}]", bad)
+    ref5 = _ref5(c)
+    dgu = np.concatenate([_bits(ref5["dg"]), _bits(ref5["du"])], axis=1)
+    out2 = moe.mxfp8_mlp_bwd_gate_up(to_dev(dgu), to_dev(c["x_perm"]), c["offs"],
+                                     c["mw"], grad_format="e5m2")
+    moe.debug_sync()
+    sref2 = orc.mxfp8_mlp_step(c["x_perm"], c["p"]["offsets"], c["s"].astype(np.float64),
+                               c["inp"]["w_gate"], c["inp"]["w_up"], c["inp"]["w_down"],
+                               c["dy"], bf16_dgu=True, grad_fmt="e5m2")
+    _check(to_f64(out2["dx"][:R]), sref2["dx"], f"{n} stage dx", bad)
+    for key in ("dw_gate", "dw_up"):
+        for e in range(c["wl"].n_local):
+            _check(to_f64(out2[key][e]), sref2[key][e], f"{n} stage {key}[{e}]", bad)
+    assert not bad, bad

@@ -21,6 +21,20 @@ def test_oracle_codes_are_admissible_and_far_flips_are_not():
     assert (bs, bc, differ) == (0, 1, 1)
 
 
+def test_e5m2_codes_are_checked_in_their_own_format():
+    rng = np.random.default_rng(4)
+    v = rng.standard_normal((6, 96)) * np.exp(2 * rng.standard_normal((6, 96)))
+    c, s = orc.mx_quantize_rows(v, "e5m2")
+    assert check_block_decisions(v, np.zeros_like(v), c, s, "e5m2") == (0, 0, 0)
+    np.testing.assert_array_equal(dequantize(c, s, "e5m2"), orc.mx_roundtrip_rows(v, "e5m2"))
+    # the same bytes read as E4M3 are inadmissible (scales and codes differ)
+    bs, bc, _ = check_block_decisions(v, np.zeros_like(v), c, s, "e4m3")
+    assert bs > 0 and bc > 0
+    c2 = c.copy()
+    c2[1, 7] ^= 0x08                         # another exponent, far away
+    assert check_block_decisions(v, np.full_like(v, 1e-9), c2, s, "e5m2")[1] == 1
+
+
 def test_neighbouring_code_near_a_tie_needs_delta():
     # one block: 448 fixes the scale (X = 0 for amax in [256, 512)), and
     # 9.5 + eps lies just above the tie between codes for 9 and 10
