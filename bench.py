@@ -323,7 +323,8 @@ def run_mx(args, wl, dev, cpu=True):
         moe.mxfp8_mlp_fwd_down(pout.offsets, mw, ws_f, F, y=y)
         moe.mxfp8_mlp_bwd(dy, pout.x_perm, gu, pout.offsets, pout.s_perm,
                           mw, dx=dx, ds=ds, dw_gate=dwg, dw_up=dwu,
-                          dw_down=dwd, workspace=ws_b)
+                          dw_down=dwd, workspace=ws_b,
+                          grad_format=args.grad_format)
         if timed_ev is not None:
             timed_ev[3].record(stream)
 
@@ -351,6 +352,24 @@ def run_mx(args, wl, dev, cpu=True):
     if args.copy_probe_mb > 0:
         copy_probe(args.copy_probe_mb, dev)
 
+    # the fused backward alone in both gradient formats (eager, same inputs)
+    bwd_ms = {}
+    for gfmt in ("e4m3", "e5m2"):
+        def bwd(g=gfmt):
+            moe.mxfp8_mlp_bwd(dy, pout.x_perm, gu, pout.offsets, pout.s_perm,
+                              mw_holder["mw"], dx=dx, ds=ds, dw_gate=dwg,
+                              dw_up=dwu, dw_down=dwd, workspace=ws_b,
+                              grad_format=g)
+        bwd()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            bwd()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bwd_ms[gfmt] = round(e0.elapsed_time(e1) / args.steps, 4)
+
     flop_fwd = 6.0 * R * H * I
     flop = 3.0 * flop_fwd                       # forward + dgrad + wgrad
     tflops = flop / (ms_step * 1e-3) / 1e12
@@ -367,7 +386,8 @@ def run_mx(args, wl, dev, cpu=True):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp8 (e4m3 + e8m0 per 32), fp32 accumulate",
+        "dtype": ("mxfp8 (e4m3 + e8m0 per 32), fp32 accumulate" if args.grad_format == "e4m3"
+                  else "mxfp8 (e4m3; e5m2 gradients; e8m0 per 32), fp32 accumulate"),
         "data": "synthetic (seeded generator; random-init weights)",
         "config": {
             "workload": f"{wl.name}: MXFP8 grouped-MLP training step, T={T} "
@@ -380,6 +400,7 @@ def run_mx(args, wl, dev, cpu=True):
         "step_mfma_frac_fp8": round(tflops / FP8_PEAK_TFLOPS, 4),
         "step_mfma_frac_bf16": round(tflops / BF16_PEAK_TFLOPS, 4),
         "master_quant_ms": round(master_ms, 4),
+        "backward_ms_by_grad_format": bwd_ms,
         "timing": timing,
         "ms_per_step_eager": round(ms_eager, 4),
         "step_ms_events": step_pct,
@@ -428,6 +449,9 @@ def main():
                          "share and the MXFP8 step timed after it")
     ap.add_argument("--no-eplb", action="store_true",
                     help="skip the EP8 load-balancing comparison of the full layer")
+    ap.add_argument("--grad-format", choices=("e4m3", "e5m2"), default="e4m3",
+                    help="MXFP8 step: element format of the backward's "
+                         "gradient operands (dY, dg, du)")
     ap.add_argument("--ffn", choices=("grouped", "fused"), default="grouped",
                     help="bf16 FFN path: the grouped GEMMs (default, the faster "
                          "on every workload here) or the fused one-launch kernel")
@@ -474,7 +498,7 @@ def compact(r):
             "rows_per_s", "step_hbm_gbs", "step_hbm_frac", "step_mfma_frac",
             "step_mfma_frac_fp8", "step_mfma_frac_bf16", "ffn_ms_events",
             "step_ms_events", "loop_vs_grouped", "fused_vs_grouped",
-            "master_quant_ms")
+            "master_quant_ms", "backward_ms_by_grad_format")
     out = {k: r[k] for k in keep if k in r}
     out["workload"] = r["config"]["workload"]
     out["rows"] = r["config"]["rows"]
