@@ -66,6 +66,46 @@ __device__ __forceinline__ int upper_bound_minus1(const int32_t *p, int n,
   return lo;
 }
 
+// ---- hand-over between workgroups ----------------------------------------
+// On gfx950 each XCD has its own L2, and device-scope fences write back or
+// invalidate a whole L2.  Data one workgroup hands to another (possibly on
+// another XCD) within a kernel goes instead through relaxed device-scope
+// atomic stores and loads, which the hardware serves at the device's
+// coherence point; s_waitcnt vmcnt(0) orders the stores before the signal
+// (a flag or a counter) that publishes them.
+
+__device__ __forceinline__ uint64_t load_coherent8(const void *p) {
+  return __hip_atomic_load((uint64_t *)p, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_coherent8(void *p, uint64_t v) {
+  __hip_atomic_store((uint64_t *)p, v, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// 16 bytes (8 bf16) through two coherent 8-byte loads.
+__device__ __forceinline__ bf16x8 load_coherent16(const uint16_t *p) {
+  uint64_t v[2] = {load_coherent8(p), load_coherent8(p + 4)};
+  bf16x8 r;
+  __builtin_memcpy(&r, v, 16);
+  return r;
+}
+
+__device__ __forceinline__ void store_coherent16(uint16_t *p, uint32_t w0,
+                                                 uint32_t w1, uint32_t w2,
+                                                 uint32_t w3) {
+  store_coherent8(p, (uint64_t)w0 | ((uint64_t)w1 << 32));
+  store_coherent8(p + 4, (uint64_t)w2 | ((uint64_t)w3 << 32));
+}
+
+// Wait for this wavefront's vector-memory operations (stores included): the
+// ordering point between coherent stores and the signal that publishes them.
+__device__ __forceinline__ void wait_vmem() {
+  // vmcnt 0; expcnt and lgkmcnt at their maxima (not waited for)
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
+}
+
 // ---- staged epilogues ----------------------------------------------------
 // After a GEMM's K loop its LDS ring is free; each wavefront stages its part
 // of the output in a region of its own ([NROWS][W] bf16) and writes it back

@@ -162,35 +162,6 @@ __global__ __launch_bounds__(1024) void ffn_fused_plan_kernel(
   if (tid == 0) ws[0] = bad_or;
 }
 
-// 16 bytes of a as two relaxed device-scope atomic loads (served at the
-// coherence point, so they see what another XCD stored the same way).
-__device__ __forceinline__ bf16x8 load_coherent16(const uint16_t *p) {
-  uint64_t *q = (uint64_t *)p;
-  uint64_t v[2];
-  v[0] = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  v[1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  bf16x8 r;
-  __builtin_memcpy(&r, v, 16);
-  return r;
-}
-
-__device__ __forceinline__ void store_coherent16(uint16_t *p, uint32_t w0,
-                                                 uint32_t w1, uint32_t w2,
-                                                 uint32_t w3) {
-  uint64_t *q = (uint64_t *)p;
-  __hip_atomic_store(q, (uint64_t)w0 | ((uint64_t)w1 << 32), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-  __hip_atomic_store(q + 1, (uint64_t)w2 | ((uint64_t)w3 << 32),
-                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait for this wavefront's vector-memory operations (stores included), as
-// an ordering point between the coherent stores of a and the flag.
-__device__ __forceinline__ void wait_vmem() {
-  // vmcnt 0; expcnt and lgkmcnt at their maxima (not waited for)
-  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xf << 8));
-}
-
 // acc[m][j] += sum over k-steps s in [s0, s1) of A_m(s) . B_j(s)^T.  ap[m]
 // points at the lane's first A element (row l % 16 of the block); B block
 // j's rows start at the workgroup-uniform bb[j] and the lane's element is
