@@ -181,7 +181,14 @@ int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
  * written (rows two cut segments share hold unspecified values), and
  * MOE_DEVERR_ROWS is set in the workspace's error word, which the call
  * otherwise clears.
- * workspace: moe_grouped_ffn_workspace_bytes(...) bytes, 16-aligned.
+ * bf16: experts with more than 64 rows run on 128-row tiles; when those are
+ * too few to fill the chip (a few experts of a few hundred rows) the call
+ * splits K into 2-4 ranges per tile and adds the fp32 partials (in a fixed
+ * order: repeated calls give identical bits; a different split, as the per
+ * expert loop may choose, rounds differently).
+ * workspace: moe_grouped_ffn_workspace_bytes(...) bytes, 16-aligned: the
+ * tile plan plus, for R_cap > 64, the split-K partial sums (up to 512 slots
+ * of 128 KiB: 64 MiB, fewer when R_cap, H and I allow fewer tiles).
  * Limits (bf16): H % 64 == 0, I % 64 == 0, 1 <= n_local <= 4096,
  * R_cap < 2^31.  (fp32): H % 4 == 0, I % 4 == 0.
  */
@@ -270,8 +277,8 @@ int moe_grouped_ffn_fused(const void *x, const int32_t *row_src, int64_t T,
                           size_t workspace_bytes, hipStream_t stream);
 
 /*
- * moe_grouped_ffn_loop - the computation of moe_grouped_ffn (bf16 only,
- * identical bits) issued the way the pages' baseline does it: expert by
+ * moe_grouped_ffn_loop - the computation of moe_grouped_ffn (bf16 only;
+ * identical bits unless the two calls split K differently) issued the way the pages' baseline does it: expert by
  * expert, each expert's gate/up and down as launches of their own (BioNeMo
  * MoE article, "GroupedLinear Optimizes Expert Computation in MoE Models":
  * iterating over the experts with a separate launch for each is what the

@@ -42,8 +42,8 @@ constexpr int64_t kMaxRows = (int64_t)1 << 31;
 
 // One workspace size serves every FFN entry point (grouped, per-expert
 // loop, fused).
-size_t tile_ws_bytes(int64_t n_local, int64_t R_cap, int64_t I) {
-  return std::max(moe::gemm_workspace_bytes(n_local),
+size_t tile_ws_bytes(int64_t n_local, int64_t R_cap, int64_t H, int64_t I) {
+  return std::max(moe::gemm_workspace_bytes(n_local, R_cap, H, I),
                   moe::ffn_fused_workspace_bytes(n_local, R_cap, I));
 }
 
@@ -144,9 +144,9 @@ int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
 
 size_t moe_grouped_ffn_workspace_bytes(int64_t R_cap, int64_t n_local,
                                        int64_t H, int64_t I, int dtype) {
-  (void)H; (void)dtype;
-  if (n_local < 1 || R_cap < 0 || I < 1) return 0;
-  return tile_ws_bytes(n_local, R_cap, I);
+  (void)dtype;
+  if (n_local < 1 || R_cap < 0 || H < 1 || I < 1) return 0;
+  return tile_ws_bytes(n_local, R_cap, H, I);
 }
 
 namespace {
@@ -166,7 +166,7 @@ int check_ffn(const int32_t *offsets, int64_t n_local, int64_t R_cap,
   }
   if (offsets == nullptr) return MOE_E_ARG;
   if (workspace == nullptr ||
-      workspace_bytes < tile_ws_bytes(n_local, R_cap, I))
+      workspace_bytes < tile_ws_bytes(n_local, R_cap, H, I))
     return MOE_E_WORKSPACE;
   if (!aligned16(workspace)) return MOE_E_ALIGN;
   return MOE_OK;

@@ -14,8 +14,17 @@
 //   * Work unit = tile of BM rows x BN B-rows of one expert.  A plan kernel
 //     turns the device-side offsets into tile prefixes for two classes of
 //     experts: those with at most kSmallRows rows (decode-like shares, run
-//     with 64-row tiles) and the rest (128- or 256-row tiles).  Each class has
-//     its own launch; the host never needs the per-expert counts.
+//     with 64-row tiles) and the rest (128-row tiles).  Each class has its
+//     own launch; the host never needs the per-expert counts.
+//   * Split-K for the 128-row class: when it has too few tiles to fill the
+//     chip (a few experts of a few hundred rows: the weight-streaming EP64
+//     share), the plan kernel also picks S (2..kSplitMax) and each tile
+//     becomes S units over contiguous K ranges.  Every unit stores its fp32
+//     accumulators to a slot of the workspace with coherent stores and
+//     counts itself in on the tile's counter; the unit that arrives last adds
+//     the S partials in fixed K-range order (its own from registers, so the
+//     result does not depend on arrival order) and runs the epilogue.  No
+//     unit waits for another.
 //   * One tile per workgroup; the grid is launched for an upper bound and
 //     each workgroup derives its tile from the device-side count (xcd_tile):
 //     XCD x (workgroup id mod 8) takes a contiguous tile range in dispatch
@@ -46,6 +55,12 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+// Split-K units issue each stage's loads ahead of its MFMAs (1) or spread
+// over them as whole tiles do (0).
+#ifndef MOE_SPLIT_FRONT
+#define MOE_SPLIT_FRONT 1
+#endif
+
 namespace moe {
 
 struct GemmArgs {
@@ -69,69 +84,82 @@ struct GemmArgs {
   int N;                    // output columns (a-columns for SWIGLU)
   int K;
   int NT;                   // n-tiles per m-tile
+  const int32_t *split;     // device word: S K-splits per tile, or null: 1
+  int32_t *ctr;             // split-K: per-tile arrival counters
+  float *part;              // split-K: fp32 partial slot of unit u at u*BM*BN
 };
 
 // Experts with at most this many rows run on the 64-row-tile kernel.
 constexpr int kSmallRows = 64;
 
+// Split-K choice handed from the plan kernel to the GEMM launch.
+struct SplitPlan {
+  int32_t *word;    // out: S for this launch (1 = no split); null: never split
+  int32_t *ctr;     // [slots] per-tile arrival counters, zeroed when S > 1
+  int below;        // split only while the 128-row class has fewer tiles
+  int P;            // compute units
+  int slots;        // partial slots in the workspace: tiles * S <= slots
+  int smax;         // largest S
+  int KT;           // K steps of the launch: each split gets >= kSplitMinKT
+  float part_ratio; // bytes of one partial slot over a tile's weight bytes
+};
+
+constexpr int kSplitMinKT = 8;
+
 // Tile prefixes per row class: prefix_c[e+1] = prefix_c[e] + ceil(rows_e /
 // BM_c) * NT_c when expert e belongs to class c.  Experts with at most
-// kSmallRows rows form the small class (0); the others are tiled either with
-// the wide shape (1) or with the narrow one (2).  Without prefix_narrow the
-// wide shape is used.  Otherwise the narrow one is used when the wide shape
-// would give fewer than wide_min tiles in all, and its tiles fit in
-// narrow_cap; the other shape's prefix is then all zeros.  Segments are cut
-// at the row capacity r_cap; the error word `err` gets kDevErrRows when the
-// offsets run past it or decrease, else 0.  One block.
+// kSmallRows rows form the small class (0), the others the wide class (1).
+// With sp.word, S is chosen for the wide class: the S that minimises the
+// time in units of one whole tile, ceil(tiles * S / P) / S (waves of units
+// over the compute units, each 1/S of a tile), times the tile's bytes grown
+// by the split's fp32 traffic (S slots written, S - 1 read back: (2S - 1)
+// slots against the tile's weight bytes), the smaller S on ties; S = 1 once
+// there are sp.below tiles.  Segments are cut at the row capacity
+// r_cap; the error word `err` gets kDevErrRows when the offsets run past it
+// or decrease, else 0.  One block.
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     const int32_t *__restrict__ offsets, int G, int r_cap, int32_t *err,
-    const int32_t *__restrict__ group_w, int n_w,
-    int bm_small, int nt_small,
-    int bm_wide, int nt_wide, int bm_narrow, int nt_narrow, int wide_min,
-    int narrow_cap, int32_t *__restrict__ prefix_small,
-    int32_t *__restrict__ prefix_wide, int32_t *__restrict__ prefix_narrow) {
-  __shared__ int32_t wsum[3][16];
+    const int32_t *__restrict__ group_w, int n_w, int bm_small, int nt_small,
+    int bm_wide, int nt_wide, int32_t *__restrict__ prefix_small,
+    int32_t *__restrict__ prefix_wide, SplitPlan sp) {
+  __shared__ int32_t wsum[2][16];
   const int tid = threadIdx.x;
   const int per = (G + 1023) / 1024;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
-  auto tiles = [&](int e, int32_t &t0, int32_t &t1, int32_t &t2) {
+  auto tiles = [&](int e, int32_t &t0, int32_t &t1) {
     int b, en;
     seg_rows(offsets, e, r_cap, b, en);
     const int n = en - b;
-    t0 = t1 = t2 = 0;
-    if (n <= kSmallRows) {
-      t0 = (n + bm_small - 1) / bm_small * nt_small;
-    } else {
-      t1 = (n + bm_wide - 1) / bm_wide * nt_wide;
-      t2 = (n + bm_narrow - 1) / bm_narrow * nt_narrow;
-    }
+    t0 = n <= kSmallRows ? (n + bm_small - 1) / bm_small * nt_small : 0;
+    t1 = n <= kSmallRows ? 0 : (n + bm_wide - 1) / bm_wide * nt_wide;
   };
-  int32_t s[3] = {0, 0, 0};
+  int32_t s[2] = {0, 0};
   int bad = 0;
   for (int e = e0; e < e1; ++e) {
-    int32_t t[3];
-    tiles(e, t[0], t[1], t[2]);
-    for (int c = 0; c < 3; ++c) s[c] += t[c];
+    int32_t t[2];
+    tiles(e, t[0], t[1]);
+    s[0] += t[0];
+    s[1] += t[1];
     bad |= seg_bad(offsets, e, r_cap) ? kDevErrRows : 0;
     if (group_w && (uint32_t)group_w[e] >= (uint32_t)n_w) bad |= kDevErrExpertIndex;
   }
   // Inclusive scan of s over the block: lane shuffles inside each
   // wavefront, then the 16 wavefront totals through LDS (one barrier).
   const int lane = tid & 63, wv = tid >> 6;
-  int32_t x[3] = {s[0], s[1], s[2]};
+  int32_t x[2] = {s[0], s[1]};
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
 #pragma unroll
-    for (int c = 0; c < 3; ++c) {
+    for (int c = 0; c < 2; ++c) {
       const int32_t y = __shfl_up(x[c], off, 64);
       if (lane >= off) x[c] += y;
     }
   }
   if (lane == 63)
-    for (int c = 0; c < 3; ++c) wsum[c][wv] = x[c];
+    for (int c = 0; c < 2; ++c) wsum[c][wv] = x[c];
   __syncthreads();
-  int32_t incl[3], total[3];
-  for (int c = 0; c < 3; ++c) {
+  int32_t r[2], total[2];
+  for (int c = 0; c < 2; ++c) {
     int32_t before = 0, all = 0;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -139,25 +167,41 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
       before += q < wv ? v : 0;
       all += v;
     }
-    incl[c] = before + x[c];
+    r[c] = before + x[c] - s[c];
     total[c] = all;
   }
-  const bool narrow = prefix_narrow != nullptr && total[1] < wide_min &&
-                      total[2] <= narrow_cap;
-  int32_t r[3];
-  for (int c = 0; c < 3; ++c) r[c] = incl[c] - s[c];
   for (int e = e0; e < e1; ++e) {
     prefix_small[e] = r[0];
-    prefix_wide[e] = narrow ? 0 : r[1];
-    if (prefix_narrow) prefix_narrow[e] = narrow ? r[2] : 0;
-    int32_t t[3];
-    tiles(e, t[0], t[1], t[2]);
-    for (int c = 0; c < 3; ++c) r[c] += t[c];
+    prefix_wide[e] = r[1];
+    int32_t t[2];
+    tiles(e, t[0], t[1]);
+    r[0] += t[0];
+    r[1] += t[1];
   }
   if (tid == 1023) {
     prefix_small[G] = total[0];
-    prefix_wide[G] = narrow ? 0 : total[1];
-    if (prefix_narrow) prefix_narrow[G] = narrow ? total[2] : 0;
+    prefix_wide[G] = total[1];
+  }
+  if (sp.word) {
+    // every thread makes the same choice from the block-wide total
+    const int tw = total[1];
+    int S = 1;
+    if (tw > 0 && tw < sp.below) {
+      float best = (float)((tw + sp.P - 1) / sp.P);  // waves at S = 1
+      for (int c = 2; c <= sp.smax && c * kSplitMinKT <= sp.KT &&
+                      (int64_t)tw * c <= sp.slots;
+           ++c) {
+        const int waves = (tw * c + sp.P - 1) / sp.P;
+        const float f = (float)waves / c * (1.f + (2 * c - 1) * sp.part_ratio);
+        if (f < best) {
+          best = f;
+          S = c;
+        }
+      }
+    }
+    if (tid == 0) *sp.word = S;
+    if (S > 1)
+      for (int i = tid; i < tw; i += 1024) sp.ctr[i] = 0;
   }
   // OR of the error bits over the block
   __shared__ int32_t bad_or;
@@ -226,7 +270,8 @@ __device__ __forceinline__ void load_frags(const uint4 *As, const uint4 *Bs,
 // there) instead of being issued in one burst, so the vector-memory queue
 // never stalls the matrix work; fragment reads of k-substep kk+1 are issued
 // before the MFMAs of kk.  The loop body has no data-dependent branches.
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MV>
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MV,
+          bool FRONT>
 __device__ __forceinline__ void gemm_kloop(
     f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
     const char *const (&gsrc)[(BM + BN) * (BK / 8) / (WM * WN * 64)],
@@ -244,6 +289,11 @@ __device__ __forceinline__ void gemm_kloop(
     const int st = (kt + STAGES - 1) % STAGES;
     const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
     const int64_t koff = (int64_t)ks * (BK * 2);
+    if constexpr (FRONT || MV == 0) {
+#pragma unroll
+      for (int i = 0; i < L; ++i)
+        load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
+    }
     if constexpr (MV > 0) {
       const uint4 *As = smem + (kt % STAGES) * STAGE_CHUNKS;
       const uint4 *Bs = As + BM * CPR;
@@ -262,22 +312,104 @@ __device__ __forceinline__ void gemm_kloop(
             acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
                 (kk & 1) ? a1[m] : a0[m], (kk & 1) ? b1[n] : b0[n], acc[m][n],
                 0, 0, 0);
-            const int f = (kk * MV + m) * NB + n;
+            if constexpr (!FRONT) {
+              const int f = (kk * MV + m) * NB + n;
 #pragma unroll
-            for (int i = f * L / NMF; i < (f + 1) * L / NMF; ++i) {
-              __builtin_amdgcn_sched_barrier(0);
-              load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
-              __builtin_amdgcn_sched_barrier(0);
+              for (int i = f * L / NMF; i < (f + 1) * L / NMF; ++i) {
+                __builtin_amdgcn_sched_barrier(0);
+                load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
+                __builtin_amdgcn_sched_barrier(0);
+              }
             }
           }
       }
-    } else {
-#pragma unroll
-      for (int i = 0; i < L; ++i)
-        load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
     }
   }
   wait_loads_barrier<0>();
+}
+
+// Split-K hand-over of unit u (tile t, K range ks of S).  Every unit
+// stores its accumulators (the wavefront's valid 32-row blocks) to slot u
+// with coherent stores, waits for them, and counts itself in on ctr[t]; the
+// unit that counts last returns true after replacing acc with the sum of the
+// S partials taken in ks order (its own from registers).  The others return
+// false.  A slot holds SLOT = BM * BN floats; layout: per wavefront, block
+// (m, n), quarter q of the 16 accumulator values, half h of the quarter,
+// lane: 8 bytes at float (((wid*MB + m)*NB + n)*4 + q)*256 + h*128 +
+// 2*lane, so each 8-byte store or load instruction covers 512 contiguous
+// bytes.
+template <int MB, int NB, int SLOT>
+__device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
+                                                const GemmArgs &p, int u,
+                                                int t, int ks, int S, int wid,
+                                                int lane, int mvalid,
+                                                int *s_last) {
+  {
+    float *mine = p.part + (int64_t)u * SLOT;
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m >= mvalid) continue;
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float *d = mine + (((wid * MB + m) * NB + n) * 4 + q) * 256 + lane * 2;
+          uint64_t lo, hi;
+          const float v[4] = {acc[m][n][4 * q], acc[m][n][4 * q + 1],
+                              acc[m][n][4 * q + 2], acc[m][n][4 * q + 3]};
+          __builtin_memcpy(&lo, v, 8);
+          __builtin_memcpy(&hi, v + 2, 8);
+          store_coherent8(d, lo);
+          store_coherent8(d + 128, hi);
+        }
+    }
+  }
+  wait_vmem();
+  __syncthreads();
+  if (wid == 0) {
+    // every lane of wavefront 0 takes part (the atomic is combined into one
+    // per wavefront); lane 0's old value is the arrival number
+    const int v = __hip_atomic_fetch_add(p.ctr + t, lane == 0 ? 1 : 0,
+                                         __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __builtin_amdgcn_readfirstlane(v);
+    if (lane == 0) *s_last = old == S - 1;
+  }
+  __syncthreads();
+  if (!*s_last) return false;
+  const float *slots = p.part + (int64_t)(u - ks) * SLOT;
+#pragma unroll
+  for (int m = 0; m < MB; ++m) {
+    if (m >= mvalid) continue;
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+      f32x16 sum;
+      for (int j = 0; j < S; ++j) {
+        f32x16 v;
+        if (j == ks) {
+          v = acc[m][n];
+        } else {
+          const float *src = slots + (int64_t)j * SLOT;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float *d = src + (((wid * MB + m) * NB + n) * 4 + q) * 256 + lane * 2;
+            const uint64_t lo = load_coherent8(d), hi = load_coherent8(d + 128);
+            float w[4];
+            __builtin_memcpy(w, &lo, 8);
+            __builtin_memcpy(w + 2, &hi, 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[4 * q + i] = w[i];
+          }
+        }
+        if (j == 0) sum = v;
+        else
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum[i] += v[i];
+      }
+      acc[m][n] = sum;
+    }
+  }
+  return true;
 }
 
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
@@ -307,12 +439,19 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
   const int KT = K / BK;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
 
+  __shared__ int s_last;
+
   int total;
   if (p.offsets) total = p.tile_prefix[p.G];
   else total = (p.single_rows + BM - 1) / BM * p.NT;
+  const int S = p.split ? *p.split : 1;
 
-  const int t = xcd_tile(blockIdx.x, total);
-  if (t < 0) return;
+  // unit u = K range ks of tile t; a tile's S units are consecutive, so they
+  // run together on one XCD
+  const int u = xcd_tile(blockIdx.x, total * S);
+  if (u < 0) return;
+  const int t = S == 1 ? u : u / S, ks = u - t * S;
+  const int kt0 = ks * KT / S, KTs = (ks + 1) * KT / S - kt0;
   {
     int e, r_begin, r_end, local;
     if (p.offsets) {
@@ -361,6 +500,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
         const int we = p.group_w ? min(max(p.group_w[e], 0), p.n_w - 1) : e;
         gsrc[i] = (const char *)(base + (int64_t)we * p.b_stride + (int64_t)col * K + kc * 8);
       }
+      gsrc[i] += (int64_t)kt0 * (BK * 2);
     }
     const uint32_t wave_off = (uint32_t)(wid * L * 64 * 16);
 
@@ -380,31 +520,43 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
 #pragma unroll
     for (int st = 0; st < STAGES - 1; ++st) {
       const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
-      const int64_t koff = (int64_t)min(st, KT - 1) * (BK * 2);
+      const int64_t koff = (int64_t)min(st, KTs - 1) * (BK * 2);
 #pragma unroll
       for (int i = 0; i < L; ++i)
         load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
     }
     // the K loop, specialised for this wavefront's number of valid blocks
     // (a wavefront with none still keeps the loads and barriers going)
-    switch (mvalid) {
+    // Split units stream weights with little MFMA work per step: they issue
+    // each stage's loads at once, ahead of the MFMAs, which keeps more bytes
+    // in flight; whole tiles spread the loads over the MFMAs.
+    const bool front = MOE_SPLIT_FRONT && S > 1;
 #define MOE_KLOOP_CASE(mv)                                                    \
       case mv:                                                                \
-        if (mv <= MB)                                                         \
-          gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1)>(        \
-              acc, gsrc, smem, lds0, wave_off, KT, lane, wrow0, brow0);       \
+        if (mv <= MB) {                                                       \
+          if (front)                                                          \
+            gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1), true>(\
+                acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);    \
+          else                                                                \
+            gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1), false>(\
+                acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);    \
+        }                                                                     \
         break;
+    switch (mvalid) {
       MOE_KLOOP_CASE(1)
       MOE_KLOOP_CASE(2)
       MOE_KLOOP_CASE(3)
       MOE_KLOOP_CASE(4)
-#undef MOE_KLOOP_CASE
       default:
-        gemm_kloop<BM, BN, WM, WN, BK, STAGES, 0>(
-            acc, gsrc, smem, lds0, wave_off, KT, lane, wrow0, brow0);
+        gemm_kloop<BM, BN, WM, WN, BK, STAGES, 0, false>(
+            acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);
     }
+#undef MOE_KLOOP_CASE
     // every wavefront is done reading the ring before the next tile refills it
     wait_loads_barrier<0>();
+    if (S > 1 && !split_hand_over<MB, NB, BM * BN>(acc, p, u, t, ks, S, wid, lane,
+                                          mvalid, &s_last))
+      return;
 
     // Epilogue.  Lane holds column (lane & 31) of each 32x32 block and rows
     // 8*(r/4) + 4*(lane/32) + (r%4), r < 16.  bf16 outputs are staged in a
@@ -473,94 +625,132 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
 
 namespace {
 
-// BM, BN, WM, WN, BK, STAGES of the wide large-expert shape.
-#ifndef MOE_NARROW_CFG
-#define MOE_NARROW_CFG 256, 64, 4, 1, 64, 3
-#endif
+// BM, BN, WM, WN, BK, STAGES of the large-expert shape.
 #ifndef MOE_WIDE_CFG
 #define MOE_WIDE_CFG 128, 256, 2, 2, 64, 3
 #endif
+constexpr int kWideCfg[6] = {MOE_WIDE_CFG};
+constexpr int kWideBM = kWideCfg[0], kWideBN = kWideCfg[1];
+
+// Largest K split, and the most partial slots a workspace carries (at
+// 128 KiB each: 64 MiB).
+#ifndef MOE_SPLITK_MAX
+#define MOE_SPLITK_MAX 4
+#endif
+constexpr int kSplitMax = MOE_SPLITK_MAX;
+constexpr int64_t kSplitSlotsMax = 512;
+constexpr size_t kSlotBytes = (size_t)kWideBM * kWideBN * 4;
 
 int ntiles(int N, int BN, bool swiglu) {
   const int cols = swiglu ? BN / 2 : BN;
   return (N + cols - 1) / cols;
 }
 
+int64_t align256(int64_t b) { return (b + 255) / 256 * 256; }
+
+// Partial slots of the workspace: kSplitMax splits of every wide tile that
+// rows up to R_cap over n_local experts can give for either GEMM of the FFN
+// (gate/up: 128 a-columns per tile; down: 256 output columns), at most
+// kSplitSlotsMax.
+int64_t split_slots(int64_t n_local, int64_t R_cap, int64_t H, int64_t I) {
+  if (R_cap <= kSmallRows) return 0;
+  const int64_t mt = (R_cap + kWideBM - 1) / kWideBM + n_local;
+  const int64_t nt = std::max<int64_t>(ntiles((int)I, kWideBN, true),
+                                       ntiles((int)H, kWideBN, false));
+  return std::min(kSplitSlotsMax, kSplitMax * std::min(mt * nt, kSplitSlotsMax));
+}
+
+// The grouped GEMM's part of a tile workspace (int32 words from ws): error
+// header, the two class prefixes and the split word, then the split-K
+// counters and partial slots.
+struct TileWs {
+  int32_t *err, *pre_s, *pre_w, *split, *ctr;
+  float *part;
+  int slots;
+};
+
+TileWs tile_ws(int32_t *ws, int64_t n_local, int64_t slots) {
+  TileWs w;
+  w.err = ws;
+  w.pre_s = ws + kErrHeaderBytes / 4;
+  w.pre_w = w.pre_s + (n_local + 1);
+  w.split = w.pre_w + (n_local + 1);
+  const int64_t head = kErrHeaderBytes + align256((2 * (n_local + 1) + 1) * 4);
+  w.ctr = ws + head / 4;
+  w.part = (float *)((char *)ws + head + align256(slots * 4));
+  w.slots = (int)slots;
+  return w;
+}
+
 template <int BM, int BN, int WM, int WN, int BK, int ST, int EPI>
-hipError_t launch_one(GemmArgs p, int num_cus, int64_t max_tiles,
-                      hipStream_t s) {
-  (void)num_cus;
+hipError_t launch_one(GemmArgs p, int64_t max_units, hipStream_t s) {
   grouped_gemm_kernel<BM, BN, WM, WN, BK, ST, EPI>
-      <<<(unsigned)tile_grid(max_tiles), WM * WN * 64, 0, s>>>(p);
+      <<<(unsigned)tile_grid(max_units), WM * WN * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
-// Tile shapes.  Large experts: 128 rows x 256 B-rows (BK 64, 3 stages), or
-// 256 x 64 (BK 64, 3 stages) when the wide shape would give fewer than two
-// tiles per CU.  Small experts: 64 x 256 (BK 64, 3 stages).  When the host
-// cannot rule the narrow shape out (few experts times n-tiles), the plan
-// kernel chooses from the actual rows and both kernels are launched; the one
-// not chosen finds no tiles.
+// Tile shapes.  Large experts: 128 rows x 256 B-rows (BK 64, 3 stages), split
+// along K when the plan kernel finds too few tiles for the chip.  Small
+// experts: 64 x 256 (BK 64, 3 stages).
 // host_rows >= 0: the launch covers one group whose row count the host
 // knows (the per-expert loop); the grids are sized for it and the class of
 // kernels that cannot find a tile is not launched.
 template <int EPI>
-hipError_t launch_grouped(GemmArgs p, int num_cus, int32_t *tile_ws,
+hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
                           int64_t R_cap, hipStream_t s,
                           int64_t host_rows = -1) {
   const bool sw = EPI == EPI_SWIGLU;
-  constexpr int wide_cfg[6] = {MOE_WIDE_CFG};
-  constexpr int narrow_cfg[6] = {MOE_NARROW_CFG};
-  constexpr int WBM = wide_cfg[0], WBN = wide_cfg[1];
-  constexpr int NBM = narrow_cfg[0], NBN = narrow_cfg[1];
-  const int wide_min = 2 * num_cus;
-  const int nt_w = ntiles(p.N, WBN, sw), nt_n = ntiles(p.N, NBN, sw);
+  const int nt_w = ntiles(p.N, kWideBN, sw);
   const int nt_s = ntiles(p.N, 256, sw);
-  const bool wide_sure = (int64_t)p.G * nt_w >= wide_min;
-  // The narrow kernel's grid; the plan kernel keeps the wide shape when the
-  // narrow one would need more tiles than this.
   const int64_t grid_rows = host_rows >= 0 ? host_rows : R_cap;
-  const int64_t max_n = ((grid_rows + NBM - 1) / NBM + p.G) * (int64_t)nt_n;
-  const int narrow_cap = (int)std::min<int64_t>(max_n, 8LL * num_cus);
   p.r_cap = (int)R_cap;
-  int32_t *errw = tile_ws;
-  int32_t *pre_s = tile_ws + kErrHeaderBytes / 4;
-  int32_t *pre_w = pre_s + (p.G + 1);
-  int32_t *pre_n = pre_s + 2 * (p.G + 1);
-  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.r_cap, errw, p.group_w, p.n_w, 64, nt_s, WBM, nt_w,
-                                      NBM, nt_n, wide_min, narrow_cap, pre_s,
-                                      pre_w, wide_sure ? nullptr : pre_n);
+  SplitPlan sp{};
+  if (ws.slots >= 2) {
+    sp.word = ws.split;
+    sp.ctr = ws.ctr;
+    sp.below = 2 * num_cus;
+    sp.P = num_cus;
+    sp.slots = ws.slots;
+    sp.smax = kSplitMax;
+    sp.KT = p.K / kWideCfg[4];
+    // slot: BM x BN fp32; the tile's weights: BN rows of K bf16
+    sp.part_ratio = (float)(kWideBM * 4) / (float)(p.K * 2);
+  }
+  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.r_cap, ws.err,
+                                      p.group_w, p.n_w, 64, nt_s, kWideBM,
+                                      nt_w, ws.pre_s, ws.pre_w, sp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // small-row class
   if (host_rows < 0 || host_rows <= kSmallRows) {
     GemmArgs ps = p;
-    ps.tile_prefix = pre_s;
+    ps.tile_prefix = ws.pre_s;
     ps.NT = nt_s;
-    err = launch_one<64, 256, 1, 4, 64, 3, EPI>(ps, num_cus,
-                                                (int64_t)p.G * nt_s, s);
+    err = launch_one<64, 256, 1, 4, 64, 3, EPI>(ps, (int64_t)p.G * nt_s, s);
     if (err != hipSuccess) return err;
   }
   if (host_rows >= 0 && host_rows <= kSmallRows) return hipSuccess;
-  // large-row class
-  if (!wide_sure) {
-    GemmArgs pn = p;
-    pn.tile_prefix = pre_n;
-    pn.NT = nt_n;
-    err = launch_one<MOE_NARROW_CFG, EPI>(pn, num_cus, narrow_cap, s);
-    if (err != hipSuccess) return err;
-  }
+  // large-row class, split or not
   GemmArgs pw = p;
-  pw.tile_prefix = pre_w;
+  pw.tile_prefix = ws.pre_w;
   pw.NT = nt_w;
-  const int64_t max_w = ((grid_rows + WBM - 1) / WBM + p.G) * (int64_t)nt_w;
-  return launch_one<MOE_WIDE_CFG, EPI>(pw, num_cus, max_w, s);
+  int64_t units = ((grid_rows + kWideBM - 1) / kWideBM + p.G) * (int64_t)nt_w;
+  if (sp.word) {
+    pw.split = ws.split;
+    pw.ctr = ws.ctr;
+    pw.part = ws.part;
+    units = std::max<int64_t>(units, ws.slots);
+  }
+  return launch_one<MOE_WIDE_CFG, EPI>(pw, units, s);
 }
 
 }  // namespace
 
-size_t gemm_workspace_bytes(int64_t n_local) {
-  return kErrHeaderBytes + (size_t)((3 * (n_local + 1) * 4 + 255) / 256 * 256);
+size_t gemm_workspace_bytes(int64_t n_local, int64_t R_cap, int64_t H,
+                            int64_t I) {
+  const int64_t slots = split_slots(n_local, R_cap, H, I);
+  return kErrHeaderBytes + align256((2 * (n_local + 1) + 1) * 4) +
+         align256(slots * 4) + slots * kSlotBytes;
 }
 
 hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
@@ -577,7 +767,9 @@ hipError_t launch_gate_up_bf16(const uint16_t *x_perm, const int32_t *offsets,
   p.b_stride = (int64_t)I * H;
   p.C = a; p.ldc = I; p.row_scale = s_perm;
   p.offsets = offsets; p.G = n_local; p.N = I; p.K = H;
-  return launch_grouped<EPI_SWIGLU>(p, num_cus, tile_ws, R_cap, s);
+  const TileWs ws = moe::tile_ws(tile_ws, n_local,
+                                 split_slots(n_local, R_cap, H, I));
+  return launch_grouped<EPI_SWIGLU>(p, num_cus, ws, R_cap, s);
 }
 
 hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
@@ -591,7 +783,9 @@ hipError_t launch_down_bf16(const uint16_t *a, const int32_t *offsets,
   p.b_stride = (int64_t)H * I;
   p.C = y; p.ldc = H;
   p.offsets = offsets; p.G = n_local; p.N = H; p.K = I;
-  return launch_grouped<EPI_BF16>(p, num_cus, tile_ws, R_cap, s);
+  const TileWs ws = moe::tile_ws(tile_ws, n_local,
+                                 split_slots(n_local, R_cap, H, I));
+  return launch_grouped<EPI_BF16>(p, num_cus, ws, R_cap, s);
 }
 
 hipError_t launch_ffn_loop_bf16(const uint16_t *x_perm, const int32_t *offsets,
@@ -602,6 +796,8 @@ hipError_t launch_ffn_loop_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                uint16_t *y, int32_t *tile_ws, int num_cus,
                                hipStream_t s) {
   const int64_t IH = (int64_t)I * H;
+  const TileWs ws = moe::tile_ws(tile_ws, n_local,
+                                 split_slots(n_local, R_cap, H, I));
   for (int e = 0; e < n_local; ++e) {
     const int64_t n = host_counts[e];
     if (n <= 0) continue;
@@ -611,14 +807,14 @@ hipError_t launch_ffn_loop_bf16(const uint16_t *x_perm, const int32_t *offsets,
     g.b_stride = 0;
     g.C = a; g.ldc = I; g.row_scale = s_perm;
     g.offsets = offsets + e; g.G = 1; g.N = I; g.K = H;
-    hipError_t err = launch_grouped<EPI_SWIGLU>(g, num_cus, tile_ws, R_cap, s, n);
+    hipError_t err = launch_grouped<EPI_SWIGLU>(g, num_cus, ws, R_cap, s, n);
     if (err != hipSuccess) return err;
     GemmArgs d{};
     d.A = a; d.B0 = w_down + e * IH; d.B1 = nullptr;
     d.b_stride = 0;
     d.C = y; d.ldc = H;
     d.offsets = offsets + e; d.G = 1; d.N = H; d.K = I;
-    err = launch_grouped<EPI_BF16>(d, num_cus, tile_ws, R_cap, s, n);
+    err = launch_grouped<EPI_BF16>(d, num_cus, ws, R_cap, s, n);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
@@ -636,7 +832,8 @@ hipError_t launch_router_gemm_bf16(const uint16_t *x, const uint16_t *w,
   // one tile per CU and each token row read twice (64 x 64 tiles: 9% slower)
   p.NT = ntiles(E, 128, false);
   const int64_t max_tiles = (T + 63) / 64 * (int64_t)p.NT;
-  return launch_one<64, 128, 2, 2, 64, 4, EPI_F32_BIAS>(p, num_cus, max_tiles, s);
+  (void)num_cus;
+  return launch_one<64, 128, 2, 2, 64, 4, EPI_F32_BIAS>(p, max_tiles, s);
 }
 
 }  // namespace moe

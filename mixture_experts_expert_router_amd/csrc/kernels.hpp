@@ -58,9 +58,12 @@ hipError_t launch_permute_replicated(
     float *s_perm, int32_t *row_src, int32_t *inv, int32_t *counts,
     int32_t *offsets, void *ws, int num_cus, hipStream_t s);
 
-// Workspace of one grouped GEMM launch: the error header and three tile
-// prefixes of n_local + 1.
-size_t gemm_workspace_bytes(int64_t n_local);
+// Workspace of the grouped GEMM launches of an FFN: the error header, two
+// tile prefixes of n_local + 1 and the split word, then the split-K arrival
+// counters and fp32 partial slots (as many as rows up to R_cap can use, at
+// most 512 of 128 KiB).
+size_t gemm_workspace_bytes(int64_t n_local, int64_t R_cap, int64_t H,
+                            int64_t I);
 
 // group_w (device [n_local] or null): group g uses the weights of stacked
 // expert group_w[g] (of n_w); null: expert g.

@@ -181,7 +181,9 @@ def test_eplb_validation(L):
 
 def test_ffn_validation(L):
     g = L.moe_grouped_gate_up
-    ws = L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)
+    # sized for the largest R_cap below (the split-K slots grow with R_cap)
+    ws = L.moe_grouped_ffn_workspace_bytes(65, 4, 128, 128, BF16)
+    assert ws > L.moe_grouped_ffn_workspace_bytes(64, 4, 128, 128, BF16)
 
     def call(R=64, H=128, I=128, nl=4, dt=BF16, wsp=P, wsb=ws, x=P, off=P):
         return g(x, off, None, nl, R, H, I, P, P, dt, P, wsp, wsb, None)

@@ -300,10 +300,12 @@ def test_step_captured_in_a_graph_replays_bit_exactly():
         _ = (d["x"].float() @ d["w_router"].float().T).sum().item()
 
 
-@pytest.mark.parametrize("name", ["small_bf16", "small_ep_bf16", "mid_bf16"])
+@pytest.mark.parametrize("name", ["small_bf16", "small_ep_bf16"])
 def test_ffn_loop_equals_grouped_bit_for_bit(name):
     """The per-expert loop (one set of launches per expert, host-known
-    counts) computes exactly what the grouped call computes."""
+    counts) computes exactly what the grouped call computes.  (Bit equality
+    needs the same K split on both sides; with K below 16 steps of 64 there
+    is none.  Larger shapes are held to the oracle instead, below.)"""
     wl = synth.WORKLOADS[name]
     print_case("loop vs grouped", name)
     inp = synth.make_inputs(wl)
@@ -338,3 +340,60 @@ def test_ffn_loop_edge_segments():
     R = sum(counts)
     assert torch.equal(bits_t(a[:R]), bits_t(a2[:R]))
     assert torch.equal(bits_t(y[:R]), bits_t(y2[:R]))
+
+
+@pytest.mark.parametrize("counts,H,I", [
+    # gate/up: 5 m-tiles x 8 n-tiles, K 2048 -> split 4; down: 40 tiles,
+    # K 1024 -> split 2; one small-class expert and an empty one beside them
+    ([200, 0, 129, 70, 40], 2048, 1024),
+    # one expert of 65 rows (wide class; the second row-half of the tile
+    # holds a single row): 10 gate/up and 4 down tiles, each split 2 ways
+    ([65], 1024, 1280),
+])
+def test_split_k_segments(counts, H, I):
+    """Few wide-class tiles: the plan kernel splits K, the last unit of each
+    tile adds the fp32 partials.  Held to the oracle, deterministic from call
+    to call, and the per-expert loop (other splits) to the oracle too."""
+    print_case("split-K", counts, H, I)
+    n_local, E, k, e_begin = len(counts), 16, 4, 0
+    idx, w, x, wg, wu, wd = _edge_inputs(counts, n_local, e_begin, E, k, H, I,
+                                         seed=9)
+    p_ref = orc.permute(idx, e_begin, n_local)
+    np.testing.assert_array_equal(p_ref["counts"], counts)
+    xp = orc.gather_rows(x, p_ref["row_src"], k)
+    s = w.reshape(-1)[p_ref["row_src"]]
+    ex = np.repeat(np.arange(n_local, dtype=np.int32), p_ref["counts"])
+    a_ref, y_ref = orc.expert_ffn_rows(xp, ex, s, wg, wu, wd)
+
+    wt = to_dev(w.astype(np.float32))
+    p = moe.permute(to_dev(idx), to_dev(x), e_begin, n_local, topk_w=wt, E=E)
+    dwg, dwu, dwd = to_dev(wg), to_dev(wu), to_dev(wd)
+    a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, dwg, dwu, dwd)
+    a2, y2 = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, dwg, dwu, dwd)
+    a3, y3 = moe.grouped_ffn_loop(p.x_perm, p.offsets, counts, p.s_perm,
+                                  dwg, dwu, dwd)
+    moe.debug_sync()
+    R = sum(counts)
+    assert_close(to_f64(a[:R]), a_ref, "bf16", "a")
+    assert_close(to_f64(y[:R]), y_ref, "bf16", "y")
+    assert torch.equal(bits_t(a[:R]), bits_t(a2[:R]))
+    assert torch.equal(bits_t(y[:R]), bits_t(y2[:R]))
+    assert_close(to_f64(a3[:R]), a_ref, "bf16", "loop a")
+    assert_close(to_f64(y3[:R]), y_ref, "bf16", "loop y")
+
+
+def test_ffn_loop_mid_workload_matches_oracle():
+    wl = synth.WORKLOADS["mid_bf16"]
+    print_case("loop vs oracle", wl.name)
+    inp = synth.make_inputs(wl)
+    d = {k: to_dev(v) for k, v in inp.items()}
+    g = gpu_chain(wl, d)
+    p = g["p"]
+    counts = p.counts.cpu().tolist()
+    a2, y2 = moe.grouped_ffn_loop(p.x_perm, p.offsets, counts, p.s_perm,
+                                  d["w_gate"], d["w_up"], d["w_down"])
+    moe.debug_sync()
+    ref = orc.moe_layer(wl, inp)
+    R = int(p.offsets[-1].item())
+    assert_close(to_f64(a2[:R]), ref["a"], "bf16", "loop a")
+    assert_close(to_f64(y2[:R]), ref["y"], "bf16", "loop y")
