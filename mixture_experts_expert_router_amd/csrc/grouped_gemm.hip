@@ -412,6 +412,78 @@ __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
   return true;
 }
 
+// Epilogue of one wavefront's WTM x WTN part of a tile (rows wrow0 ..
+// of the tile, B-rows wn*WTN .. of its BN).  Lane holds column (lane & 31)
+// of each 32x32 block and rows 8*(r/4) + 4*(lane/32) + (r%4), r < 16.  bf16
+// outputs are staged in a per-wavefront LDS region (smem must be free) and
+// leave as 16-byte row pieces.
+template <int EPI, int BN, int MB, int NB, int WTM, int WTN>
+__device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[MB][NB],
+                                              const GemmArgs &p, uint4 *smem,
+                                              int wid, int wn, int lane,
+                                              int mvalid, int nt, int row0,
+                                              int wrow0, int rows) {
+  if (EPI == EPI_SWIGLU) {
+    // B rows alternate 32 gate rows and the 32 matching up rows, so block
+    // 2q holds g and block 2q+1 holds u of the same outputs in every lane.
+    constexpr int W = WTN / 2;
+    uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * W);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m >= mvalid) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rw = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int i = wrow0 + rw;
+        const float s = (i < rows && p.row_scale) ? p.row_scale[row0 + i] : 1.f;
+#pragma unroll
+        for (int q = 0; q < NB / 2; ++q) {
+          const float g = acc[m][2 * q][r], u = acc[m][2 * q + 1][r];
+          lw[rw * W + st_col<W>(rw, q * 32 + (lane & 31))] =
+              (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
+        }
+      }
+    }
+    __syncthreads();
+    store_staged<W, WTM>(lw, (uint16_t *)p.C, p.ldc,
+                         (int64_t)nt * (BN / 2) + wn * W, p.N, row0 + wrow0,
+                         wrow0, rows, lane);
+  } else if (EPI == EPI_BF16) {
+    uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * WTN);
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m >= mvalid) continue;
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rw = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          lw[rw * WTN + st_col<WTN>(rw, n * 32 + (lane & 31))] =
+              (uint16_t)f32_to_bf16_bits(acc[m][n][r]);
+        }
+    }
+    __syncthreads();
+    store_staged<WTN, WTM>(lw, (uint16_t *)p.C, p.ldc,
+                           (int64_t)nt * BN + wn * WTN, p.N, row0 + wrow0,
+                           wrow0, rows, lane);
+  } else {
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+      if (m >= mvalid) continue;
+#pragma unroll
+      for (int n = 0; n < NB; ++n)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int col = nt * BN + wn * WTN + n * 32 + (lane & 31);
+          if (i < rows && col < p.N)
+            ((float *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
+                acc[m][n][r] + (p.bias ? p.bias[col] : 0.f);
+        }
+    }
+  }
+}
+
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) {
   constexpr int NTH = WM * WN * 64;            // 4 or 8 wavefronts
@@ -558,68 +630,8 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
                                           mvalid, &s_last))
       return;
 
-    // Epilogue.  Lane holds column (lane & 31) of each 32x32 block and rows
-    // 8*(r/4) + 4*(lane/32) + (r%4), r < 16.  bf16 outputs are staged in a
-    // per-wavefront LDS region and leave as 16-byte row pieces.
-    if (EPI == EPI_SWIGLU) {
-      // B rows alternate 32 gate rows and the 32 matching up rows, so block
-      // 2q holds g and block 2q+1 holds u of the same outputs in every lane.
-      constexpr int W = WTN / 2;
-      uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * W);
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        if (m >= mvalid) continue;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rw = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          const int i = wrow0 + rw;
-          const float s = (i < rows && p.row_scale) ? p.row_scale[row0 + i] : 1.f;
-#pragma unroll
-          for (int q = 0; q < NB / 2; ++q) {
-            const float g = acc[m][2 * q][r], u = acc[m][2 * q + 1][r];
-            lw[rw * W + st_col<W>(rw, q * 32 + (lane & 31))] =
-                (uint16_t)f32_to_bf16_bits(s * silu_f32(g) * u);
-          }
-        }
-      }
-      __syncthreads();
-      store_staged<W, WTM>(lw, (uint16_t *)p.C, p.ldc,
-                           (int64_t)nt * (BN / 2) + wn * W, p.N, row0 + wrow0,
-                           wrow0, rows, lane);
-    } else if (EPI == EPI_BF16) {
-      uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * WTN);
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        if (m >= mvalid) continue;
-#pragma unroll
-        for (int n = 0; n < NB; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rw = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            lw[rw * WTN + st_col<WTN>(rw, n * 32 + (lane & 31))] =
-                (uint16_t)f32_to_bf16_bits(acc[m][n][r]);
-          }
-      }
-      __syncthreads();
-      store_staged<WTN, WTM>(lw, (uint16_t *)p.C, p.ldc,
-                             (int64_t)nt * BN + wn * WTN, p.N, row0 + wrow0,
-                             wrow0, rows, lane);
-    } else {
-#pragma unroll
-      for (int m = 0; m < MB; ++m) {
-        if (m >= mvalid) continue;
-#pragma unroll
-        for (int n = 0; n < NB; ++n)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-            const int col = nt * BN + wn * WTN + n * 32 + (lane & 31);
-            if (i < rows && col < p.N)
-              ((float *)p.C)[(int64_t)(row0 + i) * p.ldc + col] =
-                  acc[m][n][r] + (p.bias ? p.bias[col] : 0.f);
-          }
-      }
-    }
+    tile_epilogue<EPI, BN, MB, NB, WTM, WTN>(acc, p, smem, wid, wn, lane,
+                                             mvalid, nt, row0, wrow0, rows);
   }
 }
 
