@@ -25,12 +25,13 @@
 //     the S partials in fixed K-range order (its own from registers, so the
 //     result does not depend on arrival order) and runs the epilogue.  No
 //     unit waits for another.
-//   * One tile per workgroup; the grid is launched for an upper bound and
-//     each workgroup derives its tile from the device-side count (xcd_tile):
-//     XCD x (workgroup id mod 8) takes a contiguous tile range in dispatch
-//     order, and inside an expert tiles run in bands of 8 m-tiles with the
-//     m-tile fastest (banded_mn), so workgroups running together on one L2
-//     share the weight strip and the expert's rows.
+//   * Persistent workgroups, one per compute unit (fewer when there are
+//     fewer units of work), read the unit count from the device: XCD x
+//     (workgroup id mod 8) takes a contiguous range of units and its
+//     workgroups walk it in rounds of consecutive units.  Inside an expert
+//     tiles run in bands of 8 m-tiles with the m-tile fastest (banded_mn),
+//     so the workgroups of one round share the weight strip and the
+//     expert's rows in their L2.
 //   * 256 threads = 4 wavefronts in a WM x WN grid; each wavefront owns a
 //     (BM/WM) x (BN/WN) sub-tile of 32x32 blocks, v_mfma_f32_32x32x16_bf16
 //     with fp32 accumulators.
@@ -55,6 +56,11 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+// Workgroups resident and walking the units, one per compute unit (1), or
+// one workgroup per unit (0).
+#ifndef MOE_GEMM_PERSISTENT
+#define MOE_GEMM_PERSISTENT 1
+#endif
 // Split-K units issue each stage's loads ahead of its MFMAs (1) or spread
 // over them as whole tiles do (0).
 #ifndef MOE_SPLIT_FRONT
@@ -376,7 +382,7 @@ __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
     if (lane == 0) *s_last = old == S - 1;
   }
   __syncthreads();
-  if (!*s_last) return false;
+  if (!__builtin_amdgcn_readfirstlane(*s_last)) return false;
   const float *slots = p.part + (int64_t)(u - ks) * SLOT;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
@@ -504,7 +510,7 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
                 "vmcnt range");
   __shared__ uint4 smem[STAGES * STAGE_CHUNKS];
 
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int wm = wid / WN, wn = wid % WN;
   const int K = p.K;
@@ -518,13 +524,28 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
   else total = (p.single_rows + BM - 1) / BM * p.NT;
   const int S = p.split ? *p.split : 1;
 
-  // unit u = K range ks of tile t; a tile's S units are consecutive, so they
-  // run together on one XCD
-  const int u = xcd_tile(blockIdx.x, total * S);
-  if (u < 0) return;
-  const int t = S == 1 ? u : u / S, ks = u - t * S;
-  const int kt0 = ks * KT / S, KTs = (ks + 1) * KT / S - kt0;
-  {
+  // Unit u = K range ks of tile t; a tile's S units are consecutive.  XCD x
+  // (workgroups b with b % 8 == x) takes the units [x*per, (x+1)*per) and
+  // its nx workgroups walk them in rounds of nx consecutive units, so the
+  // units that share an expert's rows or a weight strip run at the same
+  // time behind one L2.  With at least one workgroup per unit each does
+  // one unit.  Every loop condition is uniform over the workgroup.
+  const int units = total * S;
+  const int nx = gridDim.x >> 3, xcd = blockIdx.x & 7;
+  const int per = (units + 7) >> 3;
+#pragma nounroll
+  for (int r = blockIdx.x >> 3; r < per; r += nx) {
+    const int u = xcd * per + r;
+    if (u >= units) break;
+    const int t = S == 1 ? u : u / S, ks = u - t * S;
+    const int kt0 = ks * KT / S, KTs = (ks + 1) * KT / S - kt0;
+    // the previous unit's epilogue is done with the LDS ring
+    __syncthreads();
+    // The lane index, opaque to the compiler inside the loop: otherwise it
+    // hoists every lane-dependent LDS address of the unit out of the loop
+    // and keeps them all live (register spills).
+    int lane;
+    asm volatile("; lane index" : "=v"(lane) : "0"(tid & 63));
     int e, r_begin, r_end, local;
     if (p.offsets) {
       e = upper_bound_minus1(p.tile_prefix, p.G, t);
@@ -626,12 +647,10 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
 #undef MOE_KLOOP_CASE
     // every wavefront is done reading the ring before the next tile refills it
     wait_loads_barrier<0>();
-    if (S > 1 && !split_hand_over<MB, NB, BM * BN>(acc, p, u, t, ks, S, wid, lane,
-                                          mvalid, &s_last))
-      return;
-
-    tile_epilogue<EPI, BN, MB, NB, WTM, WTN>(acc, p, smem, wid, wn, lane,
-                                             mvalid, nt, row0, wrow0, rows);
+    if (S == 1 || split_hand_over<MB, NB, BM * BN>(acc, p, u, t, ks, S, wid,
+                                                  lane, mvalid, &s_last))
+      tile_epilogue<EPI, BN, MB, NB, WTM, WTN>(acc, p, smem, wid, wn, lane,
+                                               mvalid, nt, row0, wrow0, rows);
   }
 }
 
@@ -681,23 +700,33 @@ struct TileWs {
   int slots;
 };
 
+// int32 words after the error header: two prefixes and the split word
+int64_t tile_head_words(int64_t n_local) { return 2 * (n_local + 1) + 1; }
+
 TileWs tile_ws(int32_t *ws, int64_t n_local, int64_t slots) {
   TileWs w;
   w.err = ws;
   w.pre_s = ws + kErrHeaderBytes / 4;
   w.pre_w = w.pre_s + (n_local + 1);
   w.split = w.pre_w + (n_local + 1);
-  const int64_t head = kErrHeaderBytes + align256((2 * (n_local + 1) + 1) * 4);
+  const int64_t head = kErrHeaderBytes + align256(tile_head_words(n_local) * 4);
   w.ctr = ws + head / 4;
   w.part = (float *)((char *)ws + head + align256(slots * 4));
   w.slots = (int)slots;
   return w;
 }
 
+// Grid of a grouped GEMM launch: one workgroup per unit up to one per
+// compute unit (each kernel's LDS ring allows one workgroup per CU); past
+// that the workgroups stay resident and walk the units (persistent).
 template <int BM, int BN, int WM, int WN, int BK, int ST, int EPI>
-hipError_t launch_one(GemmArgs p, int64_t max_units, hipStream_t s) {
+hipError_t launch_one(GemmArgs p, int64_t max_units, int num_cus,
+                      hipStream_t s) {
+  int64_t grid = tile_grid(max_units);
+  if (MOE_GEMM_PERSISTENT)
+    grid = std::min<int64_t>(grid, std::max(8, num_cus / 8 * 8));
   grouped_gemm_kernel<BM, BN, WM, WN, BK, ST, EPI>
-      <<<(unsigned)tile_grid(max_units), WM * WN * 64, 0, s>>>(p);
+      <<<(unsigned)grid, WM * WN * 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
@@ -738,7 +767,8 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
     GemmArgs ps = p;
     ps.tile_prefix = ws.pre_s;
     ps.NT = nt_s;
-    err = launch_one<64, 256, 1, 4, 64, 3, EPI>(ps, (int64_t)p.G * nt_s, s);
+    err = launch_one<64, 256, 1, 4, 64, 3, EPI>(ps, (int64_t)p.G * nt_s,
+                                                num_cus, s);
     if (err != hipSuccess) return err;
   }
   if (host_rows >= 0 && host_rows <= kSmallRows) return hipSuccess;
@@ -753,7 +783,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
     pw.part = ws.part;
     units = std::max<int64_t>(units, ws.slots);
   }
-  return launch_one<MOE_WIDE_CFG, EPI>(pw, units, s);
+  return launch_one<MOE_WIDE_CFG, EPI>(pw, units, num_cus, s);
 }
 
 }  // namespace
@@ -761,7 +791,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
 size_t gemm_workspace_bytes(int64_t n_local, int64_t R_cap, int64_t H,
                             int64_t I) {
   const int64_t slots = split_slots(n_local, R_cap, H, I);
-  return kErrHeaderBytes + align256((2 * (n_local + 1) + 1) * 4) +
+  return kErrHeaderBytes + align256(tile_head_words(n_local) * 4) +
          align256(slots * 4) + slots * kSlotBytes;
 }
 
@@ -844,8 +874,8 @@ hipError_t launch_router_gemm_bf16(const uint16_t *x, const uint16_t *w,
   // one tile per CU and each token row read twice (64 x 64 tiles: 9% slower)
   p.NT = ntiles(E, 128, false);
   const int64_t max_tiles = (T + 63) / 64 * (int64_t)p.NT;
-  (void)num_cus;
-  return launch_one<64, 128, 2, 2, 64, 4, EPI_F32_BIAS>(p, max_tiles, s);
+  return launch_one<64, 128, 2, 2, 64, 4, EPI_F32_BIAS>(p, max_tiles, num_cus,
+                                                        s);
 }
 
 }  // namespace moe
