@@ -42,13 +42,14 @@ TIMING_GRAPH = ("K replays of the step captured in a HIP graph (same kernels, no
 TIMING_EAGER = "K eager steps"
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE passes (profiles/traffic.json), or None
-    when there are none or the kernel's sources changed since they were
-    taken."""
+def measured_profile(workload):
+    """The dominant kernel's figures from the committed rocprofv3 runs
+    (profiles/kernel_profile.json: timed-dispatch average duration, HBM
+    bytes from FETCH_SIZE / WRITE_SIZE, MFMA ops, clock and busy fraction,
+    wait fraction), or None when there are none or the kernel's sources
+    changed since they were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+    path = os.path.join(ROOT, "profiles", "kernel_profile.json")
     try:
         rec = json.load(open(path))[workload]
     except (OSError, KeyError, ValueError):
@@ -59,7 +60,20 @@ def measured_traffic(workload):
             h.update(fh.read())
     if h.hexdigest() != rec["sources_sha256"]:
         return None
-    return int(rec["bytes"])
+    return rec
+
+
+def profile_fields(rec, amount, peak, unit_scale):
+    """The roofline's profile-derived figures: `amount` (algorithmic bytes or
+    FLOPs per launch) over the profiled average duration against `peak` (in
+    units of unit_scale per second), beside the counters."""
+    if rec is None:
+        return None
+    achieved = amount / (rec["avg_ms"] * 1e-3) / unit_scale
+    return {"avg_ms": rec["avg_ms"], "achieved": round(achieved, 1),
+            "frac": round(achieved / peak, 4),
+            "mfma_busy": rec["mfma_busy"], "clock_ghz": rec["clock_ghz"],
+            "wait_frac": rec["wait_frac"], "summary": rec["profile"]}
 
 
 def copy_probe(mb, dev):
@@ -375,6 +389,7 @@ def run_mx(args, wl, dev, cpu=True):
     tflops = flop / (ms_step * 1e-3) / 1e12
     gu_flop = 4.0 * R * H * I
     gu_tflops = gu_flop / (gu_ms * 1e-3) / 1e12
+    prof = measured_profile(wl.name)
     res = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -411,9 +426,10 @@ def run_mx(args, wl, dev, cpu=True):
             "peak": FP8_PEAK_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(gu_tflops / FP8_PEAK_TFLOPS, 4),
-            "traffic": measured_traffic(wl.name),
+            "traffic": (prof or {}).get("bytes"),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "avg_ms": round(gu_ms, 4),
+            "profile": profile_fields(prof, gu_flop, FP8_PEAK_TFLOPS, 1e12),
         },
     }
     if cpu:
@@ -797,6 +813,7 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
         res_fused = fused_vs_grouped(wl, d["x"], topk_idx, topk_w, wcopies,
                                      args.steps, dev)
     alg = algorithmic(wl, R, n_touched, gather)
+    prof = measured_profile(wl.name)
     flop = alg["flop_ffn"] + alg["flop_router"]
     tflops = flop / (ms_step * 1e-3) / 1e12
     gu_gbs = alg["gate_up_bytes"] / (gate_up_ms * 1e-3) / 1e9
@@ -858,8 +875,12 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
         "roofline": dict(**gate_up_bound, **{
             "kernel": ("fused FFN (gate/up + SwiGLU x scale + down) with its plan kernel"
                        if fused else "grouped gate/up GEMM + SwiGLU x scale"),
-            "traffic": measured_traffic(wl.name),
+            "traffic": None if fused else (prof or {}).get("bytes"),
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "profile": None if fused else (
+                profile_fields(prof, alg["gate_up_bytes"], HBM_PEAK_GBS, 1e9)
+                if gate_up_bound["bound"] == "hbm" else
+                profile_fields(prof, alg["gate_up_flop"], BF16_PEAK_TFLOPS, 1e12)),
             "algorithmic_bytes": int(alg["fused_bytes"] if fused else alg["gate_up_bytes"]),
             "avg_ms": round(gate_up_ms, 4),
             "gbs": round(gu_gbs, 1),

@@ -47,9 +47,18 @@ def test_percentiles():
     assert bench.percentiles([2.0] * 7) == {"p10": 2.0, "p50": 2.0, "p90": 2.0}
 
 
-def test_stored_counter_bytes_follow_the_kernel_sources():
-    # the stored bytes are reported while the dominant kernel's sources hash
-    # to the recorded value, and not for workloads without a record
-    v = bench.measured_traffic("c4_full_bf16")
-    assert v is None or (isinstance(v, int) and v > 0)
-    assert bench.measured_traffic("no_such_workload") is None
+def test_stored_profile_follows_the_kernel_sources():
+    # the stored figures are reported while the dominant kernel's sources
+    # hash to the recorded value, and not for workloads without a record
+    rec = bench.measured_profile("c4_full_bf16")
+    assert rec is None or (rec["bytes"] > 0 and rec["avg_ms"] > 0)
+    assert bench.measured_profile("no_such_workload") is None
+
+
+def test_profile_fields():
+    rec = {"avg_ms": 2.0, "mfma_busy": 0.5, "clock_ghz": 1.4, "wait_frac": 0.2,
+           "profile": "profiles/x.md"}
+    f = bench.profile_fields(rec, 8e9, 8000.0, 1e9)  # 8 GB in 2 ms
+    assert f["achieved"] == 4000.0 and f["frac"] == 0.5
+    assert f["summary"] == "profiles/x.md"
+    assert bench.profile_fields(None, 1.0, 1.0, 1.0) is None
