@@ -490,176 +490,221 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[MB][NB],
   }
 }
 
-template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
-__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) {
-  constexpr int NTH = WM * WN * 64;            // 4 or 8 wavefronts
-  constexpr int CPR = BK / 8;                  // 16-byte chunks per row
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int MB = WTM / 32, NB = WTN / 32;
-  constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
-  constexpr int L = STAGE_CHUNKS / NTH;        // loads per thread per stage
+// Static shape facts of one tile configuration.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES>
+struct TileCfg {
+  static constexpr int NTH = WM * WN * 64;           // 4 or 8 wavefronts
+  static constexpr int CPR = BK / 8;                 // 16-byte chunks per row
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int MB = WTM / 32, NB = WTN / 32;
+  static constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
+  static constexpr int L = STAGE_CHUNKS / NTH;       // loads per thread per stage
+  static constexpr int RING = STAGES * STAGE_CHUNKS; // 16-byte LDS chunks
   static_assert(WM * WN == 4 || WM * WN == 8, "four or eight wavefronts");
   static_assert(MB >= 1 && NB >= 1, "wave tile is a multiple of 32x32");
-  static_assert(EPI != EPI_SWIGLU || NB % 2 == 0,
-                "SwiGLU pairs a gate block with the up block next to it");
   static_assert(BM * CPR % NTH == 0 && BN * CPR % NTH == 0, "load split");
   static_assert(STAGES * STAGE_CHUNKS * 16 >= WM * WN * WTM * WTN * 2,
                 "the ring must hold every wavefront's epilogue region");
   static_assert(BK == 32 || BK == 64, "BK");
   static_assert(STAGES >= 2 && STAGES <= 6 && (STAGES - 2) * L <= 63,
                 "vmcnt range");
-  __shared__ uint4 smem[STAGES * STAGE_CHUNKS];
+};
 
+// Unit u of a launch's class: K range ks of tile t (S ranges per tile).
+// smem: the LDS ring (at least the configuration's RING chunks), free on
+// entry; s_last: an LDS word for the split hand-over.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
+__device__ __forceinline__ void gemm_unit(const GemmArgs &p, int u, int S,
+                                          uint4 *smem, int *s_last) {
+  using C = TileCfg<BM, BN, WM, WN, BK, STAGES>;
+  constexpr int CPR = C::CPR, WTM = C::WTM, WTN = C::WTN, MB = C::MB,
+                NB = C::NB, STAGE_CHUNKS = C::STAGE_CHUNKS, L = C::L;
+  static_assert(EPI != EPI_SWIGLU || NB % 2 == 0,
+                "SwiGLU pairs a gate block with the up block next to it");
   const int tid = threadIdx.x;
   const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
   const int wm = wid / WN, wn = wid % WN;
   const int K = p.K;
   const int KT = K / BK;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  const int t = S == 1 ? u : u / S, ks = u - t * S;
+  const int kt0 = ks * KT / S, KTs = (ks + 1) * KT / S - kt0;
+  // The lane index, opaque to the compiler: otherwise, inside the caller's
+  // persistent loop, it hoists every lane-dependent LDS address of the unit
+  // out of the loop and keeps them all live (register spills).
+  int lane;
+  asm volatile("; lane index" : "=v"(lane) : "0"(tid & 63));
+    int e, r_begin, r_end, local;
+  if (p.offsets) {
+    e = upper_bound_minus1(p.tile_prefix, p.G, t);
+    seg_rows(p.offsets, e, p.r_cap, r_begin, r_end);
+    local = t - p.tile_prefix[e];
+  } else {
+    e = 0; r_begin = 0; r_end = p.single_rows; local = t;
+  }
+  const int mtiles = (r_end - r_begin + BM - 1) / BM;
+  int mt, nt;
+  banded_mn(local, mtiles, p.NT, 8, mt, nt);
+  const int row0 = r_begin + mt * BM;
+  const int rows = min(BM, r_end - row0);
 
-  __shared__ int s_last;
+  // Global source of each of this thread's L loads per stage.  The stage
+  // is cut into groups of 64 chunks (one load instruction each); wavefront
+  // w issues groups [w*L, w*L + L), so with BM == BN two wavefronts load
+  // only A rows (mostly L2 hits) and two only B rows (weight stream): a
+  // wavefront's loads return in order, and this keeps the quick hits out
+  // of the queue behind slow misses.  Chunk q = (w*L + i)*64 + lane.
+  const char *gsrc[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) {
+    const int q = (wid * L + i) * 64 + lane;
+    const int row = q / CPR;
+    if (row < BM) {
+      const int kc = swz<CPR>(row, q % CPR);
+      int64_t ar = row0 + min(row, rows - 1);
+      if (p.a_rows) ar = min(p.a_rows[ar] / p.a_div, p.a_rows_max);
+      gsrc[i] = (const char *)(p.A + ar * K + kc * 8);
+    } else {
+      const int j = row - BM;
+      const int kc = swz<CPR>(j, q % CPR);
+      const uint16_t *base;
+      int col;
+      if (EPI == EPI_SWIGLU) {
+        const int w = j & 63;
+        col = nt * (BN / 2) + (j >> 6) * 32 + (w & 31);
+        base = w < 32 ? p.B0 : p.B1;
+      } else {
+        col = nt * BN + j;
+        base = p.B0;
+      }
+      col = min(col, p.N - 1);
+      const int we = p.group_w ? min(max(p.group_w[e], 0), p.n_w - 1) : e;
+      gsrc[i] = (const char *)(base + (int64_t)we * p.b_stride + (int64_t)col * K + kc * 8);
+    }
+    gsrc[i] += (int64_t)kt0 * (BK * 2);
+  }
+  const uint32_t wave_off = (uint32_t)(wid * L * 64 * 16);
 
-  int total;
-  if (p.offsets) total = p.tile_prefix[p.G];
-  else total = (p.single_rows + BM - 1) / BM * p.NT;
-  const int S = p.split ? *p.split : 1;
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
 
-  // Unit u = K range ks of tile t; a tile's S units are consecutive.  XCD x
-  // (workgroups b with b % 8 == x) takes the units [x*per, (x+1)*per) and
-  // its nx workgroups walk them in rounds of nx consecutive units, so the
-  // units that share an expert's rows or a weight strip run at the same
-  // time behind one L2.  With at least one workgroup per unit each does
-  // one unit.  Every loop condition is uniform over the workgroup.
-  const int units = total * S;
+  const int wrow0 = wm * WTM;
+  const int mvalid = rows > wrow0 ? min(MB, (rows - wrow0 + 31) / 32) : 0;
+
+  const int brow0 = wn * WTN;
+  // prologue: stages 0 .. STAGES-2
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st) {
+    const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
+    const int64_t koff = (int64_t)min(st, KTs - 1) * (BK * 2);
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
+  }
+  // the K loop, specialised for this wavefront's number of valid blocks
+  // (a wavefront with none still keeps the loads and barriers going)
+  // Split units stream weights with little MFMA work per step: they issue
+  // each stage's loads at once, ahead of the MFMAs, which keeps more bytes
+  // in flight; whole tiles spread the loads over the MFMAs.
+  const bool front = MOE_SPLIT_FRONT && S > 1;
+#define MOE_KLOOP_CASE(mv)                                                    \
+    case mv:                                                                \
+      if (mv <= MB) {                                                       \
+        if (front)                                                          \
+          gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1), true>(\
+              acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);    \
+        else                                                                \
+          gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1), false>(\
+              acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);    \
+      }                                                                     \
+      break;
+  switch (mvalid) {
+    MOE_KLOOP_CASE(1)
+    MOE_KLOOP_CASE(2)
+    MOE_KLOOP_CASE(3)
+    MOE_KLOOP_CASE(4)
+    default:
+      gemm_kloop<BM, BN, WM, WN, BK, STAGES, 0, false>(
+          acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);
+  }
+#undef MOE_KLOOP_CASE
+  // every wavefront is done reading the ring before the next tile refills it
+  wait_loads_barrier<0>();
+  if (S == 1 || split_hand_over<MB, NB, BM * BN>(acc, p, u, t, ks, S, wid,
+                                                lane, mvalid, s_last))
+    tile_epilogue<EPI, BN, MB, NB, WTM, WTN>(acc, p, smem, wid, wn, lane,
+                                             mvalid, nt, row0, wrow0, rows);
+}
+
+// Walk the units [0, units) of a launch: XCD x (workgroups b with b % 8 ==
+// x) takes the units [x*per, (x+1)*per) and its nx workgroups walk them in
+// rounds of nx consecutive units, so the units that share an expert's rows
+// or a weight strip run at the same time behind one L2.  With at least one
+// workgroup per unit each does one unit.  Every loop condition is uniform
+// over the workgroup.
+template <typename F>
+__device__ __forceinline__ void walk_units(int units, F &&run) {
   const int nx = gridDim.x >> 3, xcd = blockIdx.x & 7;
   const int per = (units + 7) >> 3;
 #pragma nounroll
   for (int r = blockIdx.x >> 3; r < per; r += nx) {
     const int u = xcd * per + r;
     if (u >= units) break;
-    const int t = S == 1 ? u : u / S, ks = u - t * S;
-    const int kt0 = ks * KT / S, KTs = (ks + 1) * KT / S - kt0;
-    // the previous unit's epilogue is done with the LDS ring
-    __syncthreads();
-    // The lane index, opaque to the compiler inside the loop: otherwise it
-    // hoists every lane-dependent LDS address of the unit out of the loop
-    // and keeps them all live (register spills).
-    int lane;
-    asm volatile("; lane index" : "=v"(lane) : "0"(tid & 63));
-    int e, r_begin, r_end, local;
-    if (p.offsets) {
-      e = upper_bound_minus1(p.tile_prefix, p.G, t);
-      seg_rows(p.offsets, e, p.r_cap, r_begin, r_end);
-      local = t - p.tile_prefix[e];
-    } else {
-      e = 0; r_begin = 0; r_end = p.single_rows; local = t;
-    }
-    const int mtiles = (r_end - r_begin + BM - 1) / BM;
-    int mt, nt;
-    banded_mn(local, mtiles, p.NT, 8, mt, nt);
-    const int row0 = r_begin + mt * BM;
-    const int rows = min(BM, r_end - row0);
-
-    // Global source of each of this thread's L loads per stage.  The stage
-    // is cut into groups of 64 chunks (one load instruction each); wavefront
-    // w issues groups [w*L, w*L + L), so with BM == BN two wavefronts load
-    // only A rows (mostly L2 hits) and two only B rows (weight stream): a
-    // wavefront's loads return in order, and this keeps the quick hits out
-    // of the queue behind slow misses.  Chunk q = (w*L + i)*64 + lane.
-    const char *gsrc[L];
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int q = (wid * L + i) * 64 + lane;
-      const int row = q / CPR;
-      if (row < BM) {
-        const int kc = swz<CPR>(row, q % CPR);
-        int64_t ar = row0 + min(row, rows - 1);
-        if (p.a_rows) ar = min(p.a_rows[ar] / p.a_div, p.a_rows_max);
-        gsrc[i] = (const char *)(p.A + ar * K + kc * 8);
-      } else {
-        const int j = row - BM;
-        const int kc = swz<CPR>(j, q % CPR);
-        const uint16_t *base;
-        int col;
-        if (EPI == EPI_SWIGLU) {
-          const int w = j & 63;
-          col = nt * (BN / 2) + (j >> 6) * 32 + (w & 31);
-          base = w < 32 ? p.B0 : p.B1;
-        } else {
-          col = nt * BN + j;
-          base = p.B0;
-        }
-        col = min(col, p.N - 1);
-        const int we = p.group_w ? min(max(p.group_w[e], 0), p.n_w - 1) : e;
-        gsrc[i] = (const char *)(base + (int64_t)we * p.b_stride + (int64_t)col * K + kc * 8);
-      }
-      gsrc[i] += (int64_t)kt0 * (BK * 2);
-    }
-    const uint32_t wave_off = (uint32_t)(wid * L * 64 * 16);
-
-    f32x16 acc[MB][NB];
-#pragma unroll
-    for (int m = 0; m < MB; ++m)
-#pragma unroll
-      for (int n = 0; n < NB; ++n)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[m][n][r] = 0.f;
-
-    const int wrow0 = wm * WTM;
-    const int mvalid = rows > wrow0 ? min(MB, (rows - wrow0 + 31) / 32) : 0;
-
-    const int brow0 = wn * WTN;
-    // prologue: stages 0 .. STAGES-2
-#pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st) {
-      const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
-      const int64_t koff = (int64_t)min(st, KTs - 1) * (BK * 2);
-#pragma unroll
-      for (int i = 0; i < L; ++i)
-        load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
-    }
-    // the K loop, specialised for this wavefront's number of valid blocks
-    // (a wavefront with none still keeps the loads and barriers going)
-    // Split units stream weights with little MFMA work per step: they issue
-    // each stage's loads at once, ahead of the MFMAs, which keeps more bytes
-    // in flight; whole tiles spread the loads over the MFMAs.
-    const bool front = MOE_SPLIT_FRONT && S > 1;
-#define MOE_KLOOP_CASE(mv)                                                    \
-      case mv:                                                                \
-        if (mv <= MB) {                                                       \
-          if (front)                                                          \
-            gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1), true>(\
-                acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);    \
-          else                                                                \
-            gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1), false>(\
-                acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);    \
-        }                                                                     \
-        break;
-    switch (mvalid) {
-      MOE_KLOOP_CASE(1)
-      MOE_KLOOP_CASE(2)
-      MOE_KLOOP_CASE(3)
-      MOE_KLOOP_CASE(4)
-      default:
-        gemm_kloop<BM, BN, WM, WN, BK, STAGES, 0, false>(
-            acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);
-    }
-#undef MOE_KLOOP_CASE
-    // every wavefront is done reading the ring before the next tile refills it
-    wait_loads_barrier<0>();
-    if (S == 1 || split_hand_over<MB, NB, BM * BN>(acc, p, u, t, ks, S, wid,
-                                                  lane, mvalid, &s_last))
-      tile_epilogue<EPI, BN, MB, NB, WTM, WTN>(acc, p, smem, wid, wn, lane,
-                                               mvalid, nt, row0, wrow0, rows);
+    __syncthreads();  // the previous unit's epilogue is done with the LDS ring
+    run(u);
   }
+}
+
+// One class of tiles (the router GEMM: one group, rows p.single_rows).
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
+__global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) {
+  __shared__ uint4 smem[TileCfg<BM, BN, WM, WN, BK, STAGES>::RING];
+  __shared__ int s_last;
+  int total;
+  if (p.offsets) total = p.tile_prefix[p.G];
+  else total = (p.single_rows + BM - 1) / BM * p.NT;
+  const int S = p.split ? *p.split : 1;
+  walk_units(total * S, [&](int u) {
+    gemm_unit<BM, BN, WM, WN, BK, STAGES, EPI>(p, u, S, smem, &s_last);
+  });
+}
+
+// Both row classes of a grouped GEMM in one launch: the small-row class's
+// tiles (ps, 64 x 256, never split) are units [0, us), the large-row
+// class's units (pw, 128 x 256, S K ranges per tile) follow.  One launch
+// instead of two saves the launch of whichever class has no tiles.
+#ifndef MOE_WIDE_CFG
+#define MOE_WIDE_CFG 128, 256, 2, 2, 64, 3
+#endif
+#define MOE_SMALL_CFG 64, 256, 1, 4, 64, 3
+template <int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm2_kernel(GemmArgs ps,
+                                                            GemmArgs pw) {
+  constexpr int RS = TileCfg<MOE_SMALL_CFG>::RING;
+  constexpr int RW = TileCfg<MOE_WIDE_CFG>::RING;
+  static_assert(TileCfg<MOE_SMALL_CFG>::NTH == 256 &&
+                TileCfg<MOE_WIDE_CFG>::NTH == 256, "256 threads");
+  __shared__ uint4 smem[RS > RW ? RS : RW];
+  __shared__ int s_last;
+  const int us = ps.tile_prefix[ps.G];
+  const int S = pw.split ? *pw.split : 1;
+  const int uw = pw.tile_prefix[pw.G] * S;
+  walk_units(us + uw, [&](int u) {
+    if (u < us)
+      gemm_unit<MOE_SMALL_CFG, EPI>(ps, u, 1, smem, &s_last);
+    else
+      gemm_unit<MOE_WIDE_CFG, EPI>(pw, u - us, S, smem, &s_last);
+  });
 }
 
 namespace {
 
-// BM, BN, WM, WN, BK, STAGES of the large-expert shape.
-#ifndef MOE_WIDE_CFG
-#define MOE_WIDE_CFG 128, 256, 2, 2, 64, 3
-#endif
+// BM, BN, WM, WN, BK, STAGES of the large-expert shape: MOE_WIDE_CFG.
 constexpr int kWideCfg[6] = {MOE_WIDE_CFG};
 constexpr int kWideBM = kWideCfg[0], kWideBN = kWideCfg[1];
 
@@ -732,10 +777,10 @@ hipError_t launch_one(GemmArgs p, int64_t max_units, int num_cus,
 
 // Tile shapes.  Large experts: 128 rows x 256 B-rows (BK 64, 3 stages), split
 // along K when the plan kernel finds too few tiles for the chip.  Small
-// experts: 64 x 256 (BK 64, 3 stages).
+// experts: 64 x 256 (BK 64, 3 stages).  One plan kernel, then one launch
+// that runs both classes.
 // host_rows >= 0: the launch covers one group whose row count the host
-// knows (the per-expert loop); the grids are sized for it and the class of
-// kernels that cannot find a tile is not launched.
+// knows (the per-expert loop); the grid is sized for it.
 template <int EPI>
 hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
                           int64_t R_cap, hipStream_t s,
@@ -762,28 +807,32 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
                                       nt_w, ws.pre_s, ws.pre_w, sp);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // small-row class
-  if (host_rows < 0 || host_rows <= kSmallRows) {
-    GemmArgs ps = p;
-    ps.tile_prefix = ws.pre_s;
-    ps.NT = nt_s;
-    err = launch_one<64, 256, 1, 4, 64, 3, EPI>(ps, (int64_t)p.G * nt_s,
-                                                num_cus, s);
-    if (err != hipSuccess) return err;
-  }
-  if (host_rows >= 0 && host_rows <= kSmallRows) return hipSuccess;
-  // large-row class, split or not
+  // both row classes in one launch
+  GemmArgs ps = p;
+  ps.tile_prefix = ws.pre_s;
+  ps.NT = nt_s;
   GemmArgs pw = p;
   pw.tile_prefix = ws.pre_w;
   pw.NT = nt_w;
-  int64_t units = ((grid_rows + kWideBM - 1) / kWideBM + p.G) * (int64_t)nt_w;
+  // units: the small class's tiles (an expert of at most 64 rows has one
+  // m-tile) plus the large class's tiles or split units
+  const int64_t small_units =
+      host_rows >= 0 ? (host_rows <= kSmallRows ? nt_s : 0) : (int64_t)p.G * nt_s;
+  int64_t wide_units =
+      host_rows >= 0 && host_rows <= kSmallRows
+          ? 0
+          : ((grid_rows + kWideBM - 1) / kWideBM + p.G) * (int64_t)nt_w;
   if (sp.word) {
     pw.split = ws.split;
     pw.ctr = ws.ctr;
     pw.part = ws.part;
-    units = std::max<int64_t>(units, ws.slots);
+    if (wide_units > 0) wide_units = std::max<int64_t>(wide_units, ws.slots);
   }
-  return launch_one<MOE_WIDE_CFG, EPI>(pw, units, num_cus, s);
+  int64_t grid = tile_grid(small_units + wide_units);
+  if (MOE_GEMM_PERSISTENT)
+    grid = std::min<int64_t>(grid, std::max(8, num_cus / 8 * 8));
+  grouped_gemm2_kernel<EPI><<<(unsigned)grid, 256, 0, s>>>(ps, pw);
+  return hipGetLastError();
 }
 
 }  // namespace
