@@ -90,9 +90,9 @@ enum moe_device_error {
   MOE_DEVERR_ROWS = 2,          /* grouped GEMMs: offsets decrease or run
                                    past R_cap; rows at or past R_cap were
                                    not computed                          */
-  MOE_DEVERR_WAIT = 4           /* moe_grouped_ffn_fused: a down unit
+  MOE_DEVERR_WAIT = 4           /* moe_grouped_ffn_fused: a down tile
                                    stopped waiting for its expert's a
-                                   (a bound of seconds; not expected)    */
+                                   (a bound of 0.2 s; not expected)      */
 };
 
 /* Human-readable name of a status code (static string, host). */
@@ -240,29 +240,28 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
                     hipStream_t stream);
 
 /*
- * moe_grouped_ffn_fused - the computation of moe_grouped_ffn (bf16) for
- * decode-sized shares, gate/up and down in one persistent kernel (after a
- * one-block plan kernel).  BioNeMo MoE article, "GroupedLinear Optimizes
- * Expert Computation in MoE Models": all experts in one operation and the
- * fused MLP without materialised intermediates.  With few rows per expert
- * the layer streams each weight byte for a handful of rows; one launch
- * saves the second launch, its ramp-up and drain, and the plan in between.
- * Work units are (expert, <= 32 rows, 64 columns of a) for gate/up and
- * (expert, <= 32 rows, 128 columns of y) for down; a down unit starts once
- * all of its expert's gate/up units have written their part of a.  Any row
- * count works (more than 32 rows per expert re-read the weights once per 32
- * rows).  Measured against moe_grouped_ffn on EP shares of 7-34 and of
- * 116-229 rows per expert, it is the slower of the two (the layer is a
- * weight stream either way, and the grouped kernels stream it faster), so
- * moe_grouped_ffn stays the default path.
+ * moe_grouped_ffn_fused - the computation of moe_grouped_ffn (bf16) in one
+ * persistent launch after a one-block plan kernel.  BioNeMo MoE article,
+ * "GroupedLinear Optimizes Expert Computation in MoE Models": all experts
+ * in one operation and the fused MLP without materialised intermediates.
+ * The launch runs the grouped GEMMs' tiles (64 or 128 rows x 256 weight
+ * rows, the same K splits): its workgroups claim every gate/up tile, then
+ * every down tile, from one counter; a down tile starts once all gate/up
+ * tiles of its expert's rows have written their part of a, so one launch
+ * replaces two and the plan in between, and the gate/up tail overlaps the
+ * down start.  Measured against moe_grouped_ffn: about 1% faster on an EP8
+ * share of 7-34 rows per expert, 7% slower on an EP64 share of 116-229 rows
+ * (tiles taken in claim order rather than by XCD share their weight strips
+ * less), so moe_grouped_ffn stays the default path.
  * x: with row_src non-NULL the token rows [T, H] (permuted row r is
  * x[row_src[r] / k], as moe_grouped_gate_up_gather; R_cap <= T * k); with
  * row_src NULL, x_perm [R_cap, H] (T and k unused).
- * a [R_cap, I] and y [R_cap, H] (bf16): outputs, rows < R, the same
- * quantities as moe_grouped_ffn (fp32 accumulation in a different order, so
- * not the same bits).  Deterministic: repeated calls give identical bits.
+ * a [R_cap, I] and y [R_cap, H] (bf16): outputs, rows < R, the same bits as
+ * moe_grouped_ffn when both choose the same K splits (they use the same
+ * rule; the fused call splits only within the workspace both GEMMs share).
+ * Deterministic: repeated calls give identical bits.
  * Offsets, s_perm and the cut at R_cap as moe_grouped_gate_up; the error
- * word gets MOE_DEVERR_ROWS as there, and MOE_DEVERR_WAIT if a down unit
+ * word gets MOE_DEVERR_ROWS as there, and MOE_DEVERR_WAIT if a down tile
  * gave up waiting (its rows of y are then unspecified).
  * workspace: moe_grouped_ffn_workspace_bytes(...) bytes, 16-aligned.
  * Limits: dtype MOE_DT_BF16 (MOE_E_UNSUPPORTED otherwise), others as

@@ -44,7 +44,7 @@ constexpr int64_t kMaxRows = (int64_t)1 << 31;
 // loop, fused).
 size_t tile_ws_bytes(int64_t n_local, int64_t R_cap, int64_t H, int64_t I) {
   return std::max(moe::gemm_workspace_bytes(n_local, R_cap, H, I),
-                  moe::ffn_fused_workspace_bytes(n_local, R_cap, I));
+                  moe::ffn_fused_workspace_bytes(n_local, R_cap, H, I));
 }
 
 }  // namespace

@@ -140,6 +140,29 @@ __device__ __forceinline__ void store_staged(const uint16_t *l, uint16_t *dst,
   }
 }
 
+// store_staged for data that other workgroups of the same launch read:
+// every 16-byte piece leaves through device-coherent stores (see
+// store_coherent16); the caller waits for them (wait_vmem) before it
+// signals.
+template <int W, int NROWS>
+__device__ __forceinline__ void store_staged_coherent(const uint16_t *l,
+                                                      uint16_t *dst, int64_t ld,
+                                                      int64_t col0, int N,
+                                                      int64_t grow0, int arow0,
+                                                      int rows, int lane) {
+  constexpr int LPR = W / 8;                 // lanes per row
+  constexpr int RPI = 64 / LPR;              // rows per instruction
+#pragma unroll
+  for (int it = 0; it < NROWS / RPI; ++it) {
+    const int r = it * RPI + lane / LPR;
+    const int c8 = (lane % LPR) * 8;
+    if (arow0 + r < rows && col0 + c8 < N) {
+      const uint4 v = *(const uint4 *)(l + r * W + st_col<W>(r, c8));
+      store_coherent16(dst + (grow0 + r) * ld + col0 + c8, v.x, v.y, v.z, v.w);
+    }
+  }
+}
+
 // Tile of workgroup `bid` when every tile has its own workgroup and the
 // grid is launched for an upper bound of `total` (the real count lives on
 // the device).  Workgroups are handed to the 8 XCDs round-robin by id and,

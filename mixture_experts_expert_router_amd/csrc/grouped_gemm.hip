@@ -98,6 +98,9 @@ struct GemmArgs {
 // Experts with at most this many rows run on the 64-row-tile kernel.
 constexpr int kSmallRows = 64;
 
+// Floats per split-K partial slot of the workspace: one 128 x 256 tile.
+constexpr int kSlotFloats = 128 * 256;
+
 // Split-K choice handed from the plan kernel to the GEMM launch.
 struct SplitPlan {
   int32_t *word;    // out: S for this launch (1 = no split); null: never split
@@ -111,6 +114,27 @@ struct SplitPlan {
 };
 
 constexpr int kSplitMinKT = 8;
+
+// K ranges per tile for tw tiles of the large-row class with `cap` partial
+// slots free (see gemm_plan_kernel).
+__device__ __forceinline__ int choose_split(const SplitPlan &sp, int tw,
+                                            int64_t cap) {
+  int S = 1;
+  if (tw > 0 && tw < sp.below) {
+    float best = (float)((tw + sp.P - 1) / sp.P);  // waves at S = 1
+    for (int c = 2; c <= sp.smax && c * kSplitMinKT <= sp.KT &&
+                    (int64_t)tw * c <= cap;
+         ++c) {
+      const int waves = (tw * c + sp.P - 1) / sp.P;
+      const float f = (float)waves / c * (1.f + (2 * c - 1) * sp.part_ratio);
+      if (f < best) {
+        best = f;
+        S = c;
+      }
+    }
+  }
+  return S;
+}
 
 // Tile prefixes per row class: prefix_c[e+1] = prefix_c[e] + ceil(rows_e /
 // BM_c) * NT_c when expert e belongs to class c.  Experts with at most
@@ -191,20 +215,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
   if (sp.word) {
     // every thread makes the same choice from the block-wide total
     const int tw = total[1];
-    int S = 1;
-    if (tw > 0 && tw < sp.below) {
-      float best = (float)((tw + sp.P - 1) / sp.P);  // waves at S = 1
-      for (int c = 2; c <= sp.smax && c * kSplitMinKT <= sp.KT &&
-                      (int64_t)tw * c <= sp.slots;
-           ++c) {
-        const int waves = (tw * c + sp.P - 1) / sp.P;
-        const float f = (float)waves / c * (1.f + (2 * c - 1) * sp.part_ratio);
-        if (f < best) {
-          best = f;
-          S = c;
-        }
-      }
-    }
+    const int S = choose_split(sp, tw, sp.slots);
     if (tid == 0) *sp.word = S;
     if (S > 1)
       for (int i = tid; i < tw; i += 1024) sp.ctr[i] = 0;
@@ -334,24 +345,26 @@ __device__ __forceinline__ void gemm_kloop(
   wait_loads_barrier<0>();
 }
 
-// Split-K hand-over of unit u (tile t, K range ks of S).  Every unit
-// stores its accumulators (the wavefront's valid 32-row blocks) to slot u
-// with coherent stores, waits for them, and counts itself in on ctr[t]; the
-// unit that counts last returns true after replacing acc with the sum of the
-// S partials taken in ks order (its own from registers).  The others return
-// false.  A slot holds SLOT = BM * BN floats; layout: per wavefront, block
-// (m, n), quarter q of the 16 accumulator values, half h of the quarter,
-// lane: 8 bytes at float (((wid*MB + m)*NB + n)*4 + q)*256 + h*128 +
-// 2*lane, so each 8-byte store or load instruction covers 512 contiguous
-// bytes.
-template <int MB, int NB, int SLOT>
+// Split-K hand-over of one unit: K range ks of S of a tile whose units own
+// the workspace slots slot0 .. slot0 + S - 1 (kSlotFloats floats apart) and
+// the arrival counter ctr[ci].  Every unit stores its accumulators (the
+// wavefront's valid 32-row blocks) to its slot with coherent stores, waits
+// for them, and counts itself in; the unit that counts last returns true
+// after replacing acc with the sum of the S partials taken in ks order (its
+// own from registers).  The others return false.  Layout inside a slot: per
+// wavefront, block (m, n), quarter q of the 16 accumulator values, half h
+// of the quarter, lane: 8 bytes at float (((wid*MB + m)*NB + n)*4 + q)*256
+// + h*128 + 2*lane, so each 8-byte store or load instruction covers 512
+// contiguous bytes.
+template <int MB, int NB>
 __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
-                                                const GemmArgs &p, int u,
-                                                int t, int ks, int S, int wid,
+                                                const GemmArgs &p, int slot0,
+                                                int ci, int ks, int S, int wid,
                                                 int lane, int mvalid,
                                                 int *s_last) {
+  static_assert(4 * MB * NB * 1024 <= kSlotFloats, "a slot holds the tile");
   {
-    float *mine = p.part + (int64_t)u * SLOT;
+    float *mine = p.part + (int64_t)(slot0 + ks) * kSlotFloats;
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
       if (m >= mvalid) continue;
@@ -375,7 +388,7 @@ __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
   if (wid == 0) {
     // every lane of wavefront 0 takes part (the atomic is combined into one
     // per wavefront); lane 0's old value is the arrival number
-    const int v = __hip_atomic_fetch_add(p.ctr + t, lane == 0 ? 1 : 0,
+    const int v = __hip_atomic_fetch_add(p.ctr + ci, lane == 0 ? 1 : 0,
                                          __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT);
     const int old = __builtin_amdgcn_readfirstlane(v);
@@ -383,7 +396,7 @@ __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*s_last)) return false;
-  const float *slots = p.part + (int64_t)(u - ks) * SLOT;
+  const float *slots = p.part + (int64_t)slot0 * kSlotFloats;
 #pragma unroll
   for (int m = 0; m < MB; ++m) {
     if (m >= mvalid) continue;
@@ -395,7 +408,7 @@ __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
         if (j == ks) {
           v = acc[m][n];
         } else {
-          const float *src = slots + (int64_t)j * SLOT;
+          const float *src = slots + (int64_t)j * kSlotFloats;
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             const float *d = src + (((wid * MB + m) * NB + n) * 4 + q) * 256 + lane * 2;
@@ -428,7 +441,8 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[MB][NB],
                                               const GemmArgs &p, uint4 *smem,
                                               int wid, int wn, int lane,
                                               int mvalid, int nt, int row0,
-                                              int wrow0, int rows) {
+                                              int wrow0, int rows,
+                                              int32_t *dep, int di) {
   if (EPI == EPI_SWIGLU) {
     // B rows alternate 32 gate rows and the 32 matching up rows, so block
     // 2q holds g and block 2q+1 holds u of the same outputs in every lane.
@@ -451,9 +465,22 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[MB][NB],
       }
     }
     __syncthreads();
-    store_staged<W, WTM>(lw, (uint16_t *)p.C, p.ldc,
-                         (int64_t)nt * (BN / 2) + wn * W, p.N, row0 + wrow0,
-                         wrow0, rows, lane);
+    if (dep == nullptr) {
+      store_staged<W, WTM>(lw, (uint16_t *)p.C, p.ldc,
+                           (int64_t)nt * (BN / 2) + wn * W, p.N, row0 + wrow0,
+                           wrow0, rows, lane);
+    } else {
+      // a for other workgroups of this launch: coherent stores, waited for,
+      // then the tile counts in
+      store_staged_coherent<W, WTM>(lw, (uint16_t *)p.C, p.ldc,
+                                    (int64_t)nt * (BN / 2) + wn * W, p.N,
+                                    row0 + wrow0, wrow0, rows, lane);
+      wait_vmem();
+      __syncthreads();
+      if (wid == 0 && lane == 0)
+        __hip_atomic_fetch_add(dep + di, 1, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
   } else if (EPI == EPI_BF16) {
     uint16_t *lw = (uint16_t *)smem + (size_t)wid * (WTM * WTN);
 #pragma unroll
@@ -510,12 +537,37 @@ struct TileCfg {
                 "vmcnt range");
 };
 
-// Unit u of a launch's class: K range ks of tile t (S ranges per tile).
+// Tile t of a launch's class (BM-row tiles): its expert e, m-tile mt,
+// n-tile nt and rows [row0, row0 + rows).
+template <int BM>
+__device__ __forceinline__ void tile_coords(const GemmArgs &p, int t, int &e,
+                                            int &mt, int &nt, int &row0,
+                                            int &rows) {
+  int r_begin, r_end, local;
+  if (p.offsets) {
+    e = upper_bound_minus1(p.tile_prefix, p.G, t);
+    seg_rows(p.offsets, e, p.r_cap, r_begin, r_end);
+    local = t - p.tile_prefix[e];
+  } else {
+    e = 0; r_begin = 0; r_end = p.single_rows; local = t;
+  }
+  const int mtiles = (r_end - r_begin + BM - 1) / BM;
+  banded_mn(local, mtiles, p.NT, 8, mt, nt);
+  row0 = r_begin + mt * BM;
+  rows = min(BM, r_end - row0);
+}
+
+// One unit of a launch's class: K range ks of S of tile t; split units
+// hand over through slots slot0 .. slot0 + S - 1 and counter ctr[ci].  With
+// dep non-null (gate/up inside the fused FFN) the epilogue writes a through
+// device-coherent stores and then counts the tile in on dep[di].
 // smem: the LDS ring (at least the configuration's RING chunks), free on
 // entry; s_last: an LDS word for the split hand-over.
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
-__device__ __forceinline__ void gemm_unit(const GemmArgs &p, int u, int S,
-                                          uint4 *smem, int *s_last) {
+__device__ __forceinline__ void gemm_unit(const GemmArgs &p, int t, int ks,
+                                          int S, int slot0, int ci,
+                                          int32_t *dep, int di, uint4 *smem,
+                                          int *s_last) {
   using C = TileCfg<BM, BN, WM, WN, BK, STAGES>;
   constexpr int CPR = C::CPR, WTM = C::WTM, WTN = C::WTN, MB = C::MB,
                 NB = C::NB, STAGE_CHUNKS = C::STAGE_CHUNKS, L = C::L;
@@ -527,26 +579,14 @@ __device__ __forceinline__ void gemm_unit(const GemmArgs &p, int u, int S,
   const int K = p.K;
   const int KT = K / BK;
   const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-  const int t = S == 1 ? u : u / S, ks = u - t * S;
   const int kt0 = ks * KT / S, KTs = (ks + 1) * KT / S - kt0;
   // The lane index, opaque to the compiler: otherwise, inside the caller's
   // persistent loop, it hoists every lane-dependent LDS address of the unit
   // out of the loop and keeps them all live (register spills).
   int lane;
   asm volatile("; lane index" : "=v"(lane) : "0"(tid & 63));
-    int e, r_begin, r_end, local;
-  if (p.offsets) {
-    e = upper_bound_minus1(p.tile_prefix, p.G, t);
-    seg_rows(p.offsets, e, p.r_cap, r_begin, r_end);
-    local = t - p.tile_prefix[e];
-  } else {
-    e = 0; r_begin = 0; r_end = p.single_rows; local = t;
-  }
-  const int mtiles = (r_end - r_begin + BM - 1) / BM;
-  int mt, nt;
-  banded_mn(local, mtiles, p.NT, 8, mt, nt);
-  const int row0 = r_begin + mt * BM;
-  const int rows = min(BM, r_end - row0);
+  int e, mt, nt, row0, rows;
+  tile_coords<BM>(p, t, e, mt, nt, row0, rows);
 
   // Global source of each of this thread's L loads per stage.  The stage
   // is cut into groups of 64 chunks (one load instruction each); wavefront
@@ -635,10 +675,11 @@ __device__ __forceinline__ void gemm_unit(const GemmArgs &p, int u, int S,
 #undef MOE_KLOOP_CASE
   // every wavefront is done reading the ring before the next tile refills it
   wait_loads_barrier<0>();
-  if (S == 1 || split_hand_over<MB, NB, BM * BN>(acc, p, u, t, ks, S, wid,
-                                                lane, mvalid, s_last))
+  if (S == 1 || split_hand_over<MB, NB>(acc, p, slot0, ci, ks, S, wid, lane,
+                                         mvalid, s_last))
     tile_epilogue<EPI, BN, MB, NB, WTM, WTN>(acc, p, smem, wid, wn, lane,
-                                             mvalid, nt, row0, wrow0, rows);
+                                             mvalid, nt, row0, wrow0, rows,
+                                             dep, di);
 }
 
 // Walk the units [0, units) of a launch: XCD x (workgroups b with b % 8 ==
@@ -670,7 +711,9 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
   else total = (p.single_rows + BM - 1) / BM * p.NT;
   const int S = p.split ? *p.split : 1;
   walk_units(total * S, [&](int u) {
-    gemm_unit<BM, BN, WM, WN, BK, STAGES, EPI>(p, u, S, smem, &s_last);
+    const int t = u / S;
+    gemm_unit<BM, BN, WM, WN, BK, STAGES, EPI>(p, t, u - t * S, S, t * S, t,
+                                               nullptr, 0, smem, &s_last);
   });
 }
 
@@ -695,10 +738,14 @@ __global__ __launch_bounds__(256) void grouped_gemm2_kernel(GemmArgs ps,
   const int S = pw.split ? *pw.split : 1;
   const int uw = pw.tile_prefix[pw.G] * S;
   walk_units(us + uw, [&](int u) {
-    if (u < us)
-      gemm_unit<MOE_SMALL_CFG, EPI>(ps, u, 1, smem, &s_last);
-    else
-      gemm_unit<MOE_WIDE_CFG, EPI>(pw, u - us, S, smem, &s_last);
+    if (u < us) {
+      gemm_unit<MOE_SMALL_CFG, EPI>(ps, u, 0, 1, 0, 0, nullptr, 0, smem,
+                                    &s_last);
+    } else {
+      const int t = (u - us) / S;
+      gemm_unit<MOE_WIDE_CFG, EPI>(pw, t, u - us - t * S, S, t * S, t,
+                                   nullptr, 0, smem, &s_last);
+    }
   });
 }
 
@@ -925,6 +972,315 @@ hipError_t launch_router_gemm_bf16(const uint16_t *x, const uint16_t *w,
   const int64_t max_tiles = (T + 63) / 64 * (int64_t)p.NT;
   return launch_one<64, 128, 2, 2, 64, 4, EPI_F32_BIAS>(p, max_tiles, num_cus,
                                                         s);
+}
+
+// ---- the FFN in one launch (decode fusion) ---------------------------------
+// Gate/up and down of the grouped FFN as one persistent launch, on the same
+// tiles, unit bodies and split-K hand-over as the two grouped launches.
+// Workgroups claim units in order through one atomic counter: every gate/up
+// unit (small-row class, then large-row class), then every down unit.  A
+// gate/up tile writes its columns of a through device-coherent stores and
+// counts in on its (expert, m-tile) counter; a down tile of that expert and
+// m-tile (same row class, so the same rows) waits until all nt_gu gate/up
+// tiles of those rows have counted in, then reads a through its direct-to-LDS
+// loads: its lines of a were never read before in this launch, so no cache
+// holds a stale copy (rows of a are whole cache lines: I % 64 == 0).  Every
+// unit a waiting workgroup depends on was claimed before it by a running
+// workgroup that never waits, so each wait ends; a wall-clock bound on it
+// sets kDevErrWait instead of hanging.  Control flow is uniform per
+// workgroup: the claim goes through all of wavefront 0's lanes and
+// readfirstlane.
+
+// Per (class, GEMM) launch state, then the hand-over state.
+struct FfnArgs {
+  GemmArgs g[4];            // gate/up small, gate/up large, down small, down large
+  const int32_t *mpre_s;    // [G + 1] m-tile prefix of the small-row class
+  const int32_t *mpre_w;    // [G + 1] m-tile prefix of the large-row class
+  int32_t *words;           // [0] claim counter, [1] S gate/up, [2] S down
+  int32_t *dep;             // per m-tile (small class, then large) counters
+  int32_t *err;             // error word (kDevErrWait on a wait that gave up)
+  int nt_gu;                // gate/up tiles per m-tile
+};
+
+// Bound on one wait, in ticks of the 100 MHz constant clock (0.2 s).
+constexpr uint64_t kFfnWaitTicks = 20000000;
+
+// Wavefront 0 polls *cnt until it reaches target (bounded), then the
+// workgroup goes on.
+__device__ __forceinline__ void ffn_wait(const int32_t *cnt, int target,
+                                         int32_t *err, int wid, int lane) {
+  if (wid == 0) {
+    const uint64_t t0 = wall_clock64();
+    for (;;) {
+      const int v = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+          cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (v >= target) break;
+      if (wall_clock64() - t0 > kFfnWaitTicks) {
+        if (lane == 0) atomicOr(err, kDevErrWait);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void grouped_ffn_kernel(FfnArgs f) {
+  constexpr int RS = TileCfg<MOE_SMALL_CFG>::RING;
+  constexpr int RW = TileCfg<MOE_WIDE_CFG>::RING;
+  __shared__ uint4 smem[RS > RW ? RS : RW];
+  __shared__ int s_last, s_unit;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = f.g[0].G;
+  const int Gs = f.g[0].tile_prefix[G], Gw = f.g[1].tile_prefix[G];
+  const int Ds = f.g[2].tile_prefix[G], Dw = f.g[3].tile_prefix[G];
+  const int Sg = f.words[1], Sd = f.words[2];
+  const int Ms = f.mpre_s[G];
+  const int n0 = Gs, n1 = n0 + Gw * Sg, n2 = n1 + Ds, n3 = n2 + Dw * Sd;
+  for (;;) {
+    __syncthreads();  // the previous unit is done with LDS and s_unit
+    if (wid == 0) {
+      // every lane takes part (combined into one atomic); lane 0's old
+      // value is the unit
+      const int v = __hip_atomic_fetch_add(f.words, lane == 0 ? 1 : 0,
+                                           __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+      if (lane == 0) s_unit = v;
+    }
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(s_unit);
+    if (u >= n3) break;
+    int e, mt, nt, row0, rows;
+    if (u < n0) {
+      tile_coords<64>(f.g[0], u, e, mt, nt, row0, rows);
+      gemm_unit<MOE_SMALL_CFG, EPI_SWIGLU>(f.g[0], u, 0, 1, 0, 0, f.dep,
+                                           f.mpre_s[e] + mt, smem, &s_last);
+    } else if (u < n1) {
+      const int t = (u - n0) / Sg;
+      tile_coords<128>(f.g[1], t, e, mt, nt, row0, rows);
+      gemm_unit<MOE_WIDE_CFG, EPI_SWIGLU>(f.g[1], t, u - n0 - t * Sg, Sg,
+                                          t * Sg, t, f.dep,
+                                          Ms + f.mpre_w[e] + mt, smem, &s_last);
+    } else if (u < n2) {
+      const int t = u - n1;
+      tile_coords<64>(f.g[2], t, e, mt, nt, row0, rows);
+      ffn_wait(f.dep + f.mpre_s[e] + mt, f.nt_gu, f.err, wid, lane);
+      gemm_unit<MOE_SMALL_CFG, EPI_BF16>(f.g[2], t, 0, 1, 0, 0, nullptr, 0,
+                                         smem, &s_last);
+    } else {
+      const int t = (u - n2) / Sd;
+      tile_coords<128>(f.g[3], t, e, mt, nt, row0, rows);
+      ffn_wait(f.dep + Ms + f.mpre_w[e] + mt, f.nt_gu, f.err, wid, lane);
+      gemm_unit<MOE_WIDE_CFG, EPI_BF16>(f.g[3], t, u - n2 - t * Sd, Sd,
+                                        Gw * Sg + t * Sd, Gw + t, nullptr, 0,
+                                        smem, &s_last);
+    }
+  }
+}
+
+// Plan of the fused FFN, one block: per expert the tiles of both row
+// classes for both GEMMs and the m-tiles of both classes, as exclusive
+// prefixes (G + 1 entries each); the split of each GEMM's large-row class
+// (gate/up first, down with the slots gate/up leaves); the claim counter,
+// the m-tile counters and the split counters in use cleared; the error word
+// (kDevErrRows for offsets past r_cap or decreasing, else 0).
+struct FfnPlanArgs {
+  const int32_t *offsets;
+  int G, r_cap;
+  int nt[4];                // n-tiles: gate/up small, gate/up large, down small, down large
+  int32_t *pre[4];          // tile prefixes, same order
+  int32_t *mpre[2];         // m-tile prefixes: small, large
+  int32_t *words, *dep, *err;
+  SplitPlan gu, dn;         // split choice of each GEMM (word unused)
+};
+
+__global__ __launch_bounds__(1024) void ffn_plan_kernel(FfnPlanArgs a) {
+  constexpr int NC = 6;     // 4 tile counts, 2 m-tile counts
+  __shared__ int32_t wsum[NC][16];
+  __shared__ int32_t bad_or;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  if (tid == 0) bad_or = 0;
+  const int G = a.G;
+  const int per = (G + 1023) / 1024;
+  const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
+  auto counts = [&](int e, int32_t (&c)[NC]) {
+    int b, en;
+    seg_rows(a.offsets, e, a.r_cap, b, en);
+    const int n = en - b;
+    const int ms = n <= kSmallRows ? (n + 63) / 64 : 0;
+    const int mw = n <= kSmallRows ? 0 : (n + 127) / 128;
+    c[0] = ms * a.nt[0]; c[1] = mw * a.nt[1];
+    c[2] = ms * a.nt[2]; c[3] = mw * a.nt[3];
+    c[4] = ms; c[5] = mw;
+  };
+  int32_t s[NC] = {};
+  int bad = 0;
+  for (int e = e0; e < e1; ++e) {
+    int32_t c[NC];
+    counts(e, c);
+    for (int i = 0; i < NC; ++i) s[i] += c[i];
+    bad |= seg_bad(a.offsets, e, a.r_cap) ? kDevErrRows : 0;
+  }
+  int32_t x[NC];
+  for (int i = 0; i < NC; ++i) x[i] = s[i];
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int32_t y = __shfl_up(x[i], off, 64);
+      if (lane >= off) x[i] += y;
+    }
+  }
+  if (lane == 63)
+    for (int i = 0; i < NC; ++i) wsum[i][wv] = x[i];
+  __syncthreads();
+  int32_t r[NC], total[NC];
+  for (int i = 0; i < NC; ++i) {
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int32_t v = wsum[i][q];
+      before += q < wv ? v : 0;
+      all += v;
+    }
+    r[i] = before + x[i] - s[i];
+    total[i] = all;
+  }
+  for (int e = e0; e < e1; ++e) {
+    for (int i = 0; i < 4; ++i) a.pre[i][e] = r[i];
+    a.mpre[0][e] = r[4];
+    a.mpre[1][e] = r[5];
+    int32_t c[NC];
+    counts(e, c);
+    for (int i = 0; i < NC; ++i) r[i] += c[i];
+  }
+  if (tid == 1023) {
+    for (int i = 0; i < 4; ++i) a.pre[i][G] = total[i];
+    a.mpre[0][G] = total[4];
+    a.mpre[1][G] = total[5];
+  }
+  // splits of the large-row class (every thread chooses the same)
+  const int gw = total[1], dw = total[3];
+  int Sg = 1, Sd = 1;
+  if (a.gu.slots >= 2 && (int64_t)gw + dw <= a.gu.slots) {
+    // gate/up's units take slots [0, gw*Sg), down's the ones after
+    Sg = choose_split(a.gu, gw, a.gu.slots);
+    Sd = choose_split(a.dn, dw, (int64_t)a.dn.slots - (int64_t)gw * Sg);
+  }
+  if (tid == 0) {
+    a.words[0] = 0;
+    a.words[1] = Sg;
+    a.words[2] = Sd;
+  }
+  const int nm = total[4] + total[5];
+  for (int i = tid; i < nm; i += 1024) a.dep[i] = 0;
+  // split counters: gate/up tiles [0, gw), down tiles [gw, gw + dw)
+  const int nc = (Sg > 1 || Sd > 1) ? gw + dw : 0;
+  for (int i = tid; i < nc; i += 1024) a.gu.ctr[i] = 0;
+  if (bad) atomicOr(&bad_or, bad);
+  __syncthreads();
+  if (tid == 0) *a.err = bad_or;
+}
+
+namespace {
+
+// The fused FFN's arrays after the grouped GEMM's part of the workspace.
+struct FfnWs {
+  int32_t *pre_ds, *pre_dw, *mpre_s, *mpre_w, *words, *dep;
+};
+
+int64_t ffn_extra_words(int64_t n_local, int64_t R_cap) {
+  // 4 prefixes, 4 words, m-tile counters: at most n_local small m-tiles
+  // and R_cap / 128 + n_local large ones
+  return 4 * (n_local + 1) + 4 + 2 * n_local + R_cap / 128 + 1;
+}
+
+FfnWs ffn_ws(const TileWs &w, int64_t n_local) {
+  FfnWs f;
+  int32_t *x = (int32_t *)(w.part + (int64_t)w.slots * kSlotFloats);
+  f.pre_ds = x;
+  f.pre_dw = f.pre_ds + (n_local + 1);
+  f.mpre_s = f.pre_dw + (n_local + 1);
+  f.mpre_w = f.mpre_s + (n_local + 1);
+  f.words = f.mpre_w + (n_local + 1);
+  f.dep = f.words + 4;
+  return f;
+}
+
+}  // namespace
+
+size_t ffn_fused_workspace_bytes(int64_t n_local, int64_t R_cap, int64_t H,
+                                 int64_t I) {
+  return gemm_workspace_bytes(n_local, R_cap, H, I) +
+         (size_t)align256(ffn_extra_words(n_local, R_cap) * 4);
+}
+
+hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
+                                 int k, int64_t T, const int32_t *offsets,
+                                 const float *s_perm, int n_local,
+                                 int64_t R_cap, int H, int I,
+                                 const uint16_t *w_gate, const uint16_t *w_up,
+                                 const uint16_t *w_down, uint16_t *a,
+                                 uint16_t *y, int32_t *ws, int num_cus,
+                                 hipStream_t s) {
+  const int64_t slots = split_slots(n_local, R_cap, H, I);
+  const TileWs w = moe::tile_ws(ws, n_local, slots);
+  const FfnWs fw = ffn_ws(w, n_local);
+  FfnArgs f{};
+  // gate/up: x (gathered through row_src, or x_perm) against W_gate / W_up
+  GemmArgs gu{};
+  gu.A = x; gu.B0 = w_gate; gu.B1 = w_up;
+  gu.a_rows = row_src; gu.a_div = row_src ? k : 1;
+  gu.a_rows_max = row_src ? (int)(T - 1) : (int)R_cap - 1;
+  gu.b_stride = (int64_t)I * H;
+  gu.C = a; gu.ldc = I; gu.row_scale = s_perm;
+  gu.offsets = offsets; gu.G = n_local; gu.N = I; gu.K = H;
+  gu.r_cap = (int)R_cap;
+  gu.ctr = w.ctr; gu.part = w.part;
+  GemmArgs dn{};
+  dn.A = a; dn.B0 = w_down;
+  dn.b_stride = (int64_t)H * I;
+  dn.C = y; dn.ldc = H;
+  dn.offsets = offsets; dn.G = n_local; dn.N = H; dn.K = I;
+  dn.r_cap = (int)R_cap;
+  dn.ctr = w.ctr; dn.part = w.part;
+  const int nt[4] = {ntiles(I, 256, true), ntiles(I, kWideBN, true),
+                     ntiles(H, 256, false), ntiles(H, kWideBN, false)};
+  int32_t *pre[4] = {w.pre_s, w.pre_w, fw.pre_ds, fw.pre_dw};
+  for (int i = 0; i < 4; ++i) {
+    f.g[i] = i < 2 ? gu : dn;
+    f.g[i].tile_prefix = pre[i];
+    f.g[i].NT = nt[i];
+  }
+  f.mpre_s = fw.mpre_s; f.mpre_w = fw.mpre_w;
+  f.words = fw.words; f.dep = fw.dep; f.err = w.err;
+  f.nt_gu = nt[0];
+  FfnPlanArgs pa{};
+  pa.offsets = offsets; pa.G = n_local; pa.r_cap = (int)R_cap;
+  for (int i = 0; i < 4; ++i) { pa.nt[i] = nt[i]; pa.pre[i] = pre[i]; }
+  pa.mpre[0] = fw.mpre_s; pa.mpre[1] = fw.mpre_w;
+  pa.words = fw.words; pa.dep = fw.dep; pa.err = w.err;
+  for (int i = 0; i < 2; ++i) {
+    SplitPlan &sp = i == 0 ? pa.gu : pa.dn;
+    const int K = i == 0 ? H : I;
+    if (slots >= 2) {
+      sp.ctr = w.ctr;
+      sp.below = 2 * num_cus;
+      sp.P = num_cus;
+      sp.slots = (int)slots;
+      sp.smax = kSplitMax;
+      sp.KT = K / kWideCfg[4];
+      sp.part_ratio = (float)(kWideBM * 4) / (float)(K * 2);
+    }
+  }
+  ffn_plan_kernel<<<1, 1024, 0, s>>>(pa);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  // one resident workgroup per CU (the LDS ring allows one); a grid larger
+  // than the work only adds workgroups that claim nothing
+  grouped_ffn_kernel<<<(unsigned)std::max(1, num_cus), 256, 0, s>>>(f);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -90,10 +90,11 @@ hipError_t launch_ffn_loop_bf16(const uint16_t *x_perm, const int32_t *offsets,
                                const uint16_t *w_down, uint16_t *a,
                                uint16_t *y, int32_t *tile_ws, int num_cus,
                                hipStream_t s);
-// Decode-sized FFN (gate/up, ScaledSwiGLU, down) in one persistent launch
-// after a plan kernel; x is gathered through row_src (x [T, H]) or, with
-// row_src null, read as x_perm [R_cap, H].
-size_t ffn_fused_workspace_bytes(int64_t n_local, int64_t R_cap, int64_t I);
+// The FFN (gate/up, ScaledSwiGLU, down) in one persistent launch after a
+// plan kernel, on the grouped GEMM's tiles; x is gathered through row_src
+// (x [T, H]) or, with row_src null, read as x_perm [R_cap, H].
+size_t ffn_fused_workspace_bytes(int64_t n_local, int64_t R_cap, int64_t H,
+                                 int64_t I);
 hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
                                  int k, int64_t T, const int32_t *offsets,
                                  const float *s_perm, int n_local,

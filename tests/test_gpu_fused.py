@@ -1,14 +1,18 @@
 """The fused decode FFN (moe_grouped_ffn_fused: gate/up, ScaledSwiGLU and
-down in one persistent launch) through the C ABI, against the oracle.
+down in one persistent launch on the grouped GEMM's tiles) through the C
+ABI, against the oracle.
 
 - Small workloads: a and y per row against the oracle (bf16 rule), with the
   rows read from x_perm and gathered from the token rows (identical bits),
-  and repeated calls bit-identical (no split-K, fixed reduction order).
+  and repeated calls bit-identical (fixed reduction order, split-K
+  included).
 - Edge segments: empty experts, one-row experts, experts with more than 64
   rows (several row groups), H not a multiple of the 128-column down unit,
   I of three 64-column gate/up units.
 - Full-size EP shares (C2: 4 experts of 116-229 rows, C3: 32 experts of 7-34
-  rows, C3 read literally: 32 experts of ~128 rows): every row and token.
+  rows, C3 read literally: 32 experts of ~128 rows): every row and token
+  against the oracle, and a and y bit for bit against the two grouped
+  launches (the same tiles and, at these sizes, the same K splits).
 - Segments past R_cap: cut there, memory past R_cap untouched, error word.
 - Captured in a HIP graph with the permute and the combine: every replay
   equals the eager result bit for bit (the plan kernel resets the unit
@@ -121,6 +125,14 @@ def test_fused_ep_share_full(name):
     assert_close(to_f64(a[:R]), ref["a"], "bf16", f"{name} a")
     assert_close(to_f64(y[:R]), ref["y"], "bf16", f"{name} y")
     assert_close(o[touched], ref["out"][touched], "bf16", f"{name} out")
+    # the grouped launches on the same rows: same tiles, same splits
+    a2 = moe.grouped_gate_up_gather(d["x"], p.row_src, wl.k, p.offsets,
+                                    p.s_perm, d["w_gate"], d["w_up"],
+                                    workspace=ws)
+    y2 = moe.grouped_down(a2, p.offsets, d["w_down"], workspace=ws)
+    moe.debug_sync()
+    np.testing.assert_array_equal(_bits(a[:R]), _bits(a2[:R]))
+    np.testing.assert_array_equal(_bits(y[:R]), _bits(y2[:R]))
 
 
 @pytest.mark.parametrize("offsets,R_cap", [
