@@ -442,6 +442,54 @@ def run_mx(args, wl, dev, cpu=True):
     return res
 
 
+def dense_vs_library(args, dev):
+    """Calibration, not the step: one dense bf16 GEMM, C[M, N] = A[M, K] .
+    W[N, K]^T with M 32768, N 16384, K 4096, by this library's grouped GEMM
+    (one expert, the down projection's call) and by torch.mm (the vendor
+    BLAS), each timed with HIP events over K calls after W warm-up
+    calls.  The rocprofv3 counters of both kernels come from profiling this
+    mode."""
+    M, N, K = 32768, 16384, 4096
+    g = torch.Generator(device="cpu").manual_seed(0)
+    a = (torch.randn(M, K, generator=g) * 0.5).to(torch.bfloat16).to(dev)
+    w = (torch.randn(1, N, K, generator=g) * 0.02).to(torch.bfloat16).to(dev)
+    offsets = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = moe.ffn_workspace(M, 1, N, K, torch.bfloat16, dev)
+    lib_out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+
+    def ours():
+        moe.grouped_down(a, offsets, w, y=y, workspace=ws)
+
+    wt = w[0].t()  # a transposed view: the BLAS reads W K-contiguous as it is
+
+    def library():
+        torch.mm(a, wt, out=lib_out)
+
+    res = {}
+    for name, fn in (("grouped_gemm", ours), ("library_linear", library)):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        res[name] = {"ms": round(ms, 4),
+                     "tflops": round(2.0 * M * N * K / (ms * 1e-3) / 1e12, 1)}
+    err = (y.float() - lib_out.float()).abs().max().item()
+    ref = lib_out.float().pow(2).mean().sqrt().item()
+    return {"mode": "dense_vs_library", "M": M, "N": N, "K": K,
+            "dtype": "bf16", **res,
+            "max_abs_diff_over_rms": round(err / ref, 5),
+            "what": "calibration of the bf16 GEMM mainloop against the vendor "
+                    "library on one dense GEMM; not a step of the path"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -477,6 +525,9 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after timing, run one elementwise copy of this many "
                          "MiB (read + write) to calibrate HBM byte counters")
+    ap.add_argument("--dense-vs-library", action="store_true",
+                    help="calibration instead of the benchmark: one dense bf16 "
+                         "GEMM by this library and by the vendor BLAS")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -488,6 +539,9 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.dense_vs_library:
+        print(json.dumps(dense_vs_library(args, dev)), flush=True)
+        return
     cpu = not args.no_cpu_baseline
     if wl.dtype == "mxfp8":
         res = run_mx(args, wl, dev, cpu=cpu)
