@@ -8,14 +8,16 @@
 // Wide-EP explainer (効果2:演算強度が上がる) gives why: gathering all of an
 // expert's tokens into one GEMM reuses each weight byte read from HBM.
 //
-// Design (one launch per expert-size class, all experts of that class):
+// Design (a plan kernel, then one launch for all experts):
 //   * C[r, n] = sum_k A[r, k] * B_e[n, k] for the rows r of expert e's
 //     segment [offsets[e], offsets[e+1]); A and B are K-contiguous bf16.
 //   * Work unit = tile of BM rows x BN B-rows of one expert.  A plan kernel
 //     turns the device-side offsets into tile prefixes for two classes of
 //     experts: those with at most kSmallRows rows (decode-like shares, run
-//     with 64-row tiles) and the rest (128-row tiles).  Each class has its
-//     own launch; the host never needs the per-expert counts.
+//     with 64-row tiles) and the rest (128-row tiles).  One launch runs both
+//     classes' tiles; the host never needs the per-expert counts.  (The FFN
+//     can also run as a single launch for both GEMMs: grouped_ffn_kernel at
+//     the end of this file.)
 //   * Split-K for the 128-row class: when it has too few tiles to fill the
 //     chip (a few experts of a few hundred rows: the weight-streaming EP64
 //     share), the plan kernel also picks S (2..kSplitMax) and each tile
@@ -385,14 +387,11 @@ __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
   }
   wait_vmem();
   __syncthreads();
-  if (wid == 0) {
-    // every lane of wavefront 0 takes part (the atomic is combined into one
-    // per wavefront); lane 0's old value is the arrival number
-    const int v = __hip_atomic_fetch_add(p.ctr + ci, lane == 0 ? 1 : 0,
-                                         __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-    const int old = __builtin_amdgcn_readfirstlane(v);
-    if (lane == 0) *s_last = old == S - 1;
+  if (wid == 0 && lane == 0) {
+    // one atomic; its old value is the arrival number
+    const int old = __hip_atomic_fetch_add(p.ctr + ci, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    *s_last = old == S - 1;
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*s_last)) return false;
@@ -977,8 +976,11 @@ hipError_t launch_router_gemm_bf16(const uint16_t *x, const uint16_t *w,
 // ---- the FFN in one launch (decode fusion) ---------------------------------
 // Gate/up and down of the grouped FFN as one persistent launch, on the same
 // tiles, unit bodies and split-K hand-over as the two grouped launches.
-// Workgroups claim units in order through one atomic counter: every gate/up
-// unit (small-row class, then large-row class), then every down unit.  A
+// The units of each phase (every gate/up unit: small-row class, then
+// large-row class; then every down unit) are cut into 8 contiguous shares,
+// one per XCD, each with a claim counter; a workgroup claims from its XCD's
+// share and, when that is used up, from the others'.  It moves on to the
+// down phase only after finding every gate/up share used up.  A
 // gate/up tile writes its columns of a through device-coherent stores and
 // counts in on its (expert, m-tile) counter; a down tile of that expert and
 // m-tile (same row class, so the same rows) waits until all nt_gu gate/up
@@ -987,16 +989,18 @@ hipError_t launch_router_gemm_bf16(const uint16_t *x, const uint16_t *w,
 // holds a stale copy (rows of a are whole cache lines: I % 64 == 0).  Every
 // unit a waiting workgroup depends on was claimed before it by a running
 // workgroup that never waits, so each wait ends; a wall-clock bound on it
-// sets kDevErrWait instead of hanging.  Control flow is uniform per
-// workgroup: the claim goes through all of wavefront 0's lanes and
-// readfirstlane.
+// sets kDevErrWait instead of hanging.  Shares by XCD keep the tiles that
+// share a weight strip or an expert's rows behind one L2, as in the grouped
+// launches.  Control flow is uniform per workgroup: the claims go through
+// all of wavefront 0's lanes and readfirstlane.
 
 // Per (class, GEMM) launch state, then the hand-over state.
 struct FfnArgs {
   GemmArgs g[4];            // gate/up small, gate/up large, down small, down large
   const int32_t *mpre_s;    // [G + 1] m-tile prefix of the small-row class
   const int32_t *mpre_w;    // [G + 1] m-tile prefix of the large-row class
-  int32_t *words;           // [0] claim counter, [1] S gate/up, [2] S down
+  int32_t *words;           // [0..15] claim counters (gate/up, then down,
+                            //   per XCD share); [16] S gate/up, [17] S down
   int32_t *dep;             // per m-tile (small class, then large) counters
   int32_t *err;             // error word (kDevErrWait on a wait that gave up)
   int nt_gu;                // gate/up tiles per m-tile
@@ -1019,7 +1023,10 @@ __device__ __forceinline__ void ffn_wait(const int32_t *cnt, int target,
         if (lane == 0) atomicOr(err, kDevErrWait);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      // about a microsecond between polls: waits last up to a gate/up
+      // tile's time, and denser polling of one address slows the weight
+      // stream of the tiles being waited for
+      __builtin_amdgcn_s_sleep(32);
     }
   }
   __syncthreads();
@@ -1035,18 +1042,36 @@ __global__ __launch_bounds__(256) void grouped_ffn_kernel(FfnArgs f) {
   const int G = f.g[0].G;
   const int Gs = f.g[0].tile_prefix[G], Gw = f.g[1].tile_prefix[G];
   const int Ds = f.g[2].tile_prefix[G], Dw = f.g[3].tile_prefix[G];
-  const int Sg = f.words[1], Sd = f.words[2];
+  const int Sg = f.words[16], Sd = f.words[17];
   const int Ms = f.mpre_s[G];
   const int n0 = Gs, n1 = n0 + Gw * Sg, n2 = n1 + Ds, n3 = n2 + Dw * Sd;
+  const int xcd = blockIdx.x & 7;
+  int phase = 0;  // wavefront 0's: 0 gate/up, 1 down, 2 done
   for (;;) {
     __syncthreads();  // the previous unit is done with LDS and s_unit
     if (wid == 0) {
-      // every lane takes part (combined into one atomic); lane 0's old
-      // value is the unit
-      const int v = __hip_atomic_fetch_add(f.words, lane == 0 ? 1 : 0,
-                                           __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT);
-      if (lane == 0) s_unit = v;
+      int unit = -1;
+      while (phase < 2 && unit < 0) {
+        const int base = phase == 0 ? 0 : n1;
+        const int n = phase == 0 ? n1 : n3 - n1;
+        const int per = (n + 7) >> 3;
+        for (int y = 0; y < 8 && unit < 0; ++y) {
+          const int z = (xcd + y) & 7;
+          const int lo = min(n, z * per), size = min(n, lo + per) - lo;
+          if (size == 0) continue;
+          // one atomic, from lane 0 (a branch without barriers or loops
+          // inside); its old value is the claim
+          int v = 0;
+          if (lane == 0)
+            v = __hip_atomic_fetch_add(f.words + phase * 8 + z, 1,
+                                       __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+          v = __builtin_amdgcn_readfirstlane(v);
+          if (v < size) unit = base + lo + v;
+        }
+        if (unit < 0) ++phase;  // every share of this phase is used up
+      }
+      if (lane == 0) s_unit = unit < 0 ? n3 : unit;
     }
     __syncthreads();
     const int u = __builtin_amdgcn_readfirstlane(s_unit);
@@ -1168,10 +1193,10 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(FfnPlanArgs a) {
     Sg = choose_split(a.gu, gw, a.gu.slots);
     Sd = choose_split(a.dn, dw, (int64_t)a.dn.slots - (int64_t)gw * Sg);
   }
+  if (tid < 16) a.words[tid] = 0;
   if (tid == 0) {
-    a.words[0] = 0;
-    a.words[1] = Sg;
-    a.words[2] = Sd;
+    a.words[16] = Sg;
+    a.words[17] = Sd;
   }
   const int nm = total[4] + total[5];
   for (int i = tid; i < nm; i += 1024) a.dep[i] = 0;
@@ -1191,9 +1216,9 @@ struct FfnWs {
 };
 
 int64_t ffn_extra_words(int64_t n_local, int64_t R_cap) {
-  // 4 prefixes, 4 words, m-tile counters: at most n_local small m-tiles
+  // 4 prefixes, 20 words, m-tile counters: at most n_local small m-tiles
   // and R_cap / 128 + n_local large ones
-  return 4 * (n_local + 1) + 4 + 2 * n_local + R_cap / 128 + 1;
+  return 4 * (n_local + 1) + 20 + 2 * n_local + R_cap / 128 + 1;
 }
 
 FfnWs ffn_ws(const TileWs &w, int64_t n_local) {
@@ -1204,7 +1229,7 @@ FfnWs ffn_ws(const TileWs &w, int64_t n_local) {
   f.mpre_s = f.pre_dw + (n_local + 1);
   f.mpre_w = f.mpre_s + (n_local + 1);
   f.words = f.mpre_w + (n_local + 1);
-  f.dep = f.words + 4;
+  f.dep = f.words + 20;
   return f;
 }
 
@@ -1277,9 +1302,10 @@ hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
   ffn_plan_kernel<<<1, 1024, 0, s>>>(pa);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  // one resident workgroup per CU (the LDS ring allows one); a grid larger
-  // than the work only adds workgroups that claim nothing
-  grouped_ffn_kernel<<<(unsigned)std::max(1, num_cus), 256, 0, s>>>(f);
+  // one resident workgroup per CU (the LDS ring allows one), a multiple of
+  // 8 so that every XCD has as many; a grid larger than the work only adds
+  // workgroups that claim nothing
+  grouped_ffn_kernel<<<(unsigned)std::max(8, num_cus / 8 * 8), 256, 0, s>>>(f);
   return hipGetLastError();
 }
 
