@@ -246,10 +246,10 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
  * in one operation and the fused MLP without materialised intermediates.
  * The launch runs the grouped GEMMs' tiles (64 or 128 rows x 256 weight
  * rows, the same K splits): its workgroups claim every gate/up tile, then
- * every down tile, by XCD shares of each phase; a down tile starts once all gate/up
- * tiles of its expert's rows have written their part of a, so one launch
- * replaces two and the plan in between, and the gate/up tail overlaps the
- * down start.  Measured against moe_grouped_ffn: about 3% faster on an EP8
+ * every down tile, by XCD shares of each phase; a down tile starts once
+ * all gate/up tiles of its expert's rows have written their part of a, so
+ * one launch replaces two and the plan in between, and the gate/up tail
+ * overlaps the down start.  Measured against moe_grouped_ffn: about 3% faster on an EP8
  * share of 7-34 rows per expert, 6% slower on an EP64 share of 116-229 rows
  * (one round of gate/up tiles: nothing to overlap, and the early down tiles
  * wait it out), so moe_grouped_ffn stays the default path.
