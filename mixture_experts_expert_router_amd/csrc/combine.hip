@@ -8,45 +8,62 @@
 
 namespace moe {
 
-// bf16 rows as 16-byte vectors of 8 values.
+// bf16 rows as 16-byte vectors of 8 values.  Lane j < k of every wavefront
+// loads the token's slot j (row and weight) with one load each; a ballot
+// then names the local slots, and the row loop visits only those, four rows
+// in flight at a time, summing in slot order.  The slot list is the same in
+// every wavefront, so the loops are uniform.
 __global__ __launch_bounds__(256) void combine_bf16_kernel(
     const uint4 *__restrict__ y, const int32_t *__restrict__ inv,
     const float *__restrict__ w, int64_t T, int k, int64_t vecs,
     uint4 *__restrict__ out) {
+  const int lane = threadIdx.x & 63;
   for (int64_t t = blockIdx.x; t < T; t += gridDim.x) {
-    // First local slot of the token (uniform); none -> a zero row.
-    int rdef = -1;
-    for (int j = 0; j < k && rdef < 0; ++j) rdef = inv[t * k + j];
-    rdef = __builtin_amdgcn_readfirstlane(rdef);
-    if (rdef < 0) {
+    int32_t rj = -1;
+    float wj = 1.f;
+    if (lane < k) {
+      rj = inv[t * k + lane];
+      if (w) wj = w[t * k + lane];
+    }
+    const uint64_t local = __ballot(rj >= 0);
+    if (local == 0) {  // no local slot: a zero row
       for (int64_t c = threadIdx.x; c < vecs; c += blockDim.x)
         out[t * vecs + c] = make_uint4(0u, 0u, 0u, 0u);
       continue;
     }
     for (int64_t c = threadIdx.x; c < vecs; c += blockDim.x) {
       float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      // Slots in groups of four, without branches: a non-local slot loads
-      // the token's first local row and its sum is dropped by a select, so
-      // the four row loads are in flight together.  Sums run in slot order.
-      for (int j0 = 0; j0 < k; j0 += 4) {
-        int r[4];
+      uint64_t rest = local;
+      while (rest) {
+        // the next (up to) four local slots, in slot order; missing ones
+        // repeat the first row and are left out of the sum
+        int32_t r[4];
+        float cw[4];
+        const int n = min(4, __popcll(rest));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (q < n) {
+            const int j = __builtin_ctzll(rest);
+            rest &= rest - 1;
+            r[q] = __builtin_amdgcn_readlane(rj, j);
+            cw[q] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wj), j));
+          } else {
+            r[q] = r[0];
+            cw[q] = 0.f;
+          }
+        }
         uint4 v[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          r[q] = j0 + q < k ? inv[t * k + j0 + q] : -1;
-          v[q] = y[(int64_t)(r[q] >= 0 ? r[q] : rdef) * vecs + c];
-        }
+        for (int q = 0; q < 4; ++q) v[q] = y[(int64_t)r[q] * vecs + c];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const bool ok = r[q] >= 0;
-          const float cj = (ok && w) ? w[t * k + j0 + q] : 1.f;
-          const uint32_t u[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+          if (q < n) {
+            const uint32_t u[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float lo = fmaf(cj, bf16_bits_to_f32(u[e] & 0xffffu), acc[2 * e]);
-            const float hi = fmaf(cj, bf16_bits_to_f32(u[e] >> 16), acc[2 * e + 1]);
-            acc[2 * e] = ok ? lo : acc[2 * e];
-            acc[2 * e + 1] = ok ? hi : acc[2 * e + 1];
+            for (int e = 0; e < 4; ++e) {
+              acc[2 * e] = fmaf(cw[q], bf16_bits_to_f32(u[e] & 0xffffu), acc[2 * e]);
+              acc[2 * e + 1] = fmaf(cw[q], bf16_bits_to_f32(u[e] >> 16), acc[2 * e + 1]);
+            }
           }
         }
       }

@@ -4,7 +4,8 @@
 // MoEの課題 (counts are only known once the router has run).
 //
 // Four launches, all on the caller's stream, none needing the host to know a
-// count:
+// count (small batches take one launch for steps 1-3, then step 4; see
+// permute_small_kernel):
 //   1. hist:    each block counts its chunk of flat slots per local expert
 //               (LDS histogram) -> hist[e][blk], and flags the chunk when
 //               one of its indices lies outside [0, E)
@@ -119,6 +120,32 @@ __global__ __launch_bounds__(1024) void permute_scan_kernel(
   }
 }
 
+// Stable rows of one wavefront's 64 consecutive slots: a slot's rank among
+// the equal local experts before it in the 64 comes from ballots over the
+// expert id bits (a wave-level match); running[e] (LDS, this wavefront's
+// alone) holds the next row of expert e and is advanced by the leader of
+// each expert group.  Returns the slot's row, or -1 for a non-local slot.
+__device__ __forceinline__ int32_t rank_step(uint32_t e, bool local,
+                                             int n_local, int nbits,
+                                             uint64_t lt_mask,
+                                             int32_t *running) {
+  uint64_t match = __ballot(local);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (e >> b) & 1u;
+    const uint64_t bb = __ballot(local && bit);
+    match &= bit ? bb : ~bb;
+  }
+  int32_t r = -1;
+  if (local) r = running[e] + __popcll(match & lt_mask);
+  // every lane has read running[] above before any leader updates it
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  if (local && (match & lt_mask) == 0) running[e] += __popcll(match);
+  __builtin_amdgcn_s_waitcnt(0xc07f);
+  __builtin_amdgcn_wave_barrier();
+  return r;
+}
+
 // One wavefront per chunk of CHUNK flat slots.  The chunk's expert ids and
 // weights, and the chunk's base row of every local expert, are loaded up
 // front with independent loads; the ranking then runs on ballots and LDS
@@ -150,24 +177,128 @@ __global__ __launch_bounds__(64) void permute_scatter_kernel(
     const int64_t f = f0 + st * 64 + lane;
     const uint32_t e = ev[st];
     const bool local = e < (uint32_t)n_local;
-    uint64_t match = __ballot(local);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (e >> b) & 1u;
-      const uint64_t bb = __ballot(local && bit);
-      match &= bit ? bb : ~bb;
-    }
-    int32_t r = -1;
-    if (local) r = running[e] + __popcll(match & lt_mask);
-    // every lane has read running[] above before any leader updates it
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-    __builtin_amdgcn_wave_barrier();
-    if (local && (match & lt_mask) == 0) running[e] += __popcll(match);
-    __builtin_amdgcn_s_waitcnt(0xc07f);
-    __builtin_amdgcn_wave_barrier();
+    const int32_t r = rank_step(e, local, n_local, nbits, lt_mask, running);
     if (f < F) inv[f] = r;
     if (local) {
       row_src[r] = (int32_t)f;
       if (s_perm) s_perm[r] = wv[st];
+    }
+  }
+}
+
+// Steps 1-3 in one workgroup of 1024 threads, for F <= kSmallPermuteF and
+// n_local <= kSmallPermuteExperts.  Wavefront w owns the flat slots
+// [w*per, (w+1)*per) (per a multiple of 64), in groups of 8 x 64:
+//   1. it counts them per local expert into its own LDS row bins[w][.] and
+//      keeps their local expert ids in LDS (16 bits each);
+//   2. thread e turns column e into prefixes: counts[e] is the column's sum,
+//      offsets[e] an exclusive scan of the counts over the block (wavefront
+//      shuffles, then the 16 wavefront totals), and bins[w][e] becomes
+//      offsets[e] + the slots of e owned by wavefronts before w;
+//   3. each wavefront ranks its slots in order against its own row.
+// The rows are the same as the four-launch path's: both place every expert's
+// slots in flat-slot order.
+constexpr int64_t kSmallPermuteF = 8192;
+constexpr int kSmallPermuteExperts = 1024;
+constexpr int kSmallPermuteWaves = 16;
+
+__global__ __launch_bounds__(1024) void permute_small_kernel(
+    const int32_t *__restrict__ idx, const float *__restrict__ w, int64_t F,
+    int E, int e_begin, int n_local, int nbits, int32_t *__restrict__ row_src,
+    int32_t *__restrict__ inv, float *__restrict__ s_perm,
+    int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ err) {
+  constexpr int NW = kSmallPermuteWaves, G = 8;
+  constexpr uint16_t kNone = 0xffff;  // a slot of no local expert
+  __shared__ int32_t bins[NW * kSmallPermuteExperts];
+  __shared__ uint16_t ev[kSmallPermuteF];
+  __shared__ int32_t wtot[NW];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int per = (int)((F + NW * 64 - 1) / (NW * 64)) * 64;
+  const int ngroups = (per / 64 + G - 1) / G;
+  const int64_t f0 = (int64_t)wid * per;
+  for (int i = tid; i < NW * n_local; i += 1024) bins[i] = 0;
+  __syncthreads();
+  // 1. this wavefront's slots: local ids into LDS, counts into its row
+  int32_t *const mine = bins + wid * n_local;
+  int bad = 0;
+  for (int g = 0; g < ngroups; ++g) {
+    int32_t gi[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int64_t f = f0 + (g * G + i) * 64 + lane;
+      gi[i] = (f < f0 + per && f < F) ? idx[f] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int64_t f = f0 + (g * G + i) * 64 + lane;
+      if (!(f < f0 + per && f < F)) continue;  // past this wavefront's slots
+      bad |= (uint32_t)gi[i] >= (uint32_t)E;
+      const uint32_t e = (uint32_t)(gi[i] - e_begin);
+      const bool local = e < (uint32_t)n_local;
+      ev[f] = local ? (uint16_t)e : kNone;
+      if (local) atomicAdd(&mine[e], 1);
+    }
+  }
+  bad = __syncthreads_or(bad);
+  // 2. column sums, their exclusive scan over the experts, per-wave bases
+  int32_t s = 0;
+  if (tid < n_local)
+    for (int q = 0; q < NW; ++q) s += bins[q * n_local + tid];
+  int32_t x = s;  // inclusive prefix over the wavefront
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t yv = __shfl_up(x, off, 64);
+    if (lane >= off) x += yv;
+  }
+  if (lane == 63) wtot[wid] = x;
+  __syncthreads();
+  int32_t before = 0, total = 0;
+#pragma unroll
+  for (int q = 0; q < NW; ++q) {
+    const int32_t tq = wtot[q];
+    before += q < wid ? tq : 0;
+    total += tq;
+  }
+  if (tid < n_local) {
+    int32_t run = before + x - s;  // offsets[tid]
+    offsets[tid] = run;
+    counts[tid] = s;
+    for (int q = 0; q < NW; ++q) {
+      const int32_t c = bins[q * n_local + tid];
+      bins[q * n_local + tid] = run;
+      run += c;
+    }
+  }
+  if (tid == 0) {
+    offsets[n_local] = total;
+    *err = bad ? kDevErrExpertIndex : 0;
+  }
+  __syncthreads();
+  // 3. stable rows of this wavefront's slots, in order
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int g = 0; g < ngroups; ++g) {
+    uint32_t e[G];
+    float wv[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      const int64_t f = f0 + (g * G + i) * 64 + lane;
+      const bool in = f < f0 + per && f < F;
+      e[i] = in ? (uint32_t)ev[f] : 0xffffffffu;
+      wv[i] = (s_perm && e[i] < (uint32_t)n_local) ? w[f] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+      if ((g * G + i) * 64 >= per) break;  // uniform
+      const int64_t f = f0 + (g * G + i) * 64 + lane;
+      const bool local = e[i] < (uint32_t)n_local;
+      const int32_t r = rank_step(e[i], local, n_local, nbits, lt_mask, mine);
+      if (f < F) inv[f] = r;
+      if (local) {
+        row_src[r] = (int32_t)f;
+        if (s_perm) s_perm[r] = wv[i];
+      }
     }
   }
 }
@@ -249,6 +380,15 @@ hipError_t launch_permute(const int32_t *idx, const float *w, const void *x,
   int32_t *bad_blk = hist + (int64_t)n_local * nblk;
   int nbits = 0;
   while ((1ll << nbits) < n_local) ++nbits;
+  if (F <= kSmallPermuteF && n_local <= kSmallPermuteExperts) {
+    permute_small_kernel<<<1, 1024, 0, s>>>(
+        idx, w, F, (int)E, (int)e_begin, (int)n_local, nbits, row_src, inv,
+        (w ? s_perm : nullptr), counts, offsets, err);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !(x && x_perm)) return e;
+    return launch_permute_gather(x, row_bytes, k, row_src, offsets + n_local,
+                                 x_perm, F, num_cus, s);
+  }
   const size_t lds = (size_t)n_local * 4;
   permute_hist_kernel<<<nblk, 256, lds, s>>>(idx, F, (int)E, (int)e_begin,
                                               (int)n_local, chunk, nblk, hist,

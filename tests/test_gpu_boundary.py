@@ -5,7 +5,8 @@
 - moe_permute with expert indices outside [0, E): the slots are dropped like
   non-local ones (bit-exact against the oracle, which drops them the same
   way) and the workspace's error word reports MOE_DEVERR_EXPERT_INDEX; a
-  clean call on the same workspace clears it.
+  clean call on the same workspace clears it.  Both dispatch paths: one
+  workgroup (up to 8192 slots and 1024 local experts) and four launches.
 - Grouped FFN with offsets past R_cap (or decreasing): segments are cut at
   R_cap, rows below it match the oracle, memory past the R_cap rows of a and
   y stays untouched, and the error word reports MOE_DEVERR_ROWS.
@@ -50,10 +51,16 @@ def _perm_inputs(T, k, E, rng):
     return idx
 
 
-def test_permute_out_of_range_index_sets_error_word():
-    print_case("permute, indices outside [0, E)")
+@pytest.mark.parametrize("T,k,E,e_begin,n_local", [
+    (700, 4, 16, 4, 8),          # one workgroup (F <= 8192 slots)
+    (2048, 4, 16, 4, 8),         # F = 8192, the one-workgroup limit
+    (2049, 4, 16, 4, 8),         # F > 8192: four launches
+    (40, 4, 2048, 100, 1100),    # more than 1024 local experts: four launches
+])
+def test_permute_out_of_range_index_sets_error_word(T, k, E, e_begin, n_local):
+    print_case(f"permute, indices outside [0, E), T={T} k={k} E={E} n_local={n_local}")
     rng = np.random.default_rng(22)
-    T, k, E, e_begin, n_local, H = 700, 4, 16, 4, 8, 64
+    H = 64
     idx = _perm_inputs(T, k, E, rng)
     bad = idx.copy()
     pos = rng.choice(T * k, 37, replace=False)
