@@ -94,6 +94,7 @@ struct GemmArgs {
   int NT;                   // n-tiles per m-tile
   const int32_t *split;     // device word: S K-splits per tile, or null: 1
   int32_t *ctr;             // split-K: per-tile arrival counters
+  int32_t *claims;          // claim counters of the 8 XCD shares, or null
   float *part;              // split-K: fp32 partial slot of unit u at u*BM*BN
 };
 
@@ -148,14 +149,16 @@ __device__ __forceinline__ int choose_split(const SplitPlan &sp, int tw,
 // slots against the tile's weight bytes), the smaller S on ties; S = 1 once
 // there are sp.below tiles.  Segments are cut at the row capacity
 // r_cap; the error word `err` gets kDevErrRows when the offsets run past it
-// or decrease, else 0.  One block.
+// or decrease, else 0.  The 8 claim counters (when given) are cleared.  One
+// block.
 __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     const int32_t *__restrict__ offsets, int G, int r_cap, int32_t *err,
     const int32_t *__restrict__ group_w, int n_w, int bm_small, int nt_small,
     int bm_wide, int nt_wide, int32_t *__restrict__ prefix_small,
-    int32_t *__restrict__ prefix_wide, SplitPlan sp) {
+    int32_t *__restrict__ prefix_wide, SplitPlan sp, int32_t *claims) {
   __shared__ int32_t wsum[2][16];
   const int tid = threadIdx.x;
+  if (claims && tid < 8) claims[tid] = 0;
   const int per = (G + 1023) / 1024;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
   auto tiles = [&](int e, int32_t &t0, int32_t &t1) {
@@ -700,6 +703,84 @@ __device__ __forceinline__ void walk_units(int units, F &&run) {
   }
 }
 
+// Claim the units [0, units) of a launch.  The units are cut into 8 shares
+// ([z*per, (z+1)*per)), one per XCD.  On XCD x, workgroup j (of nx) starts
+// with unit j of share x; after that its workgroups claim the share's
+// remaining units in order through the counter claims[x], each claim made
+// when the previous unit is done.  Units claimed one after the other
+// start at about the same time, so tiles that share a weight strip or an
+// expert's rows (consecutive units) stream them behind one L2 together.
+// When its share is used up a workgroup reads all 8 counters at once and
+// claims from a share that still has units.  Control flow is uniform:
+// wavefront 0 claims with one lane's atomic and broadcasts the unit through
+// LDS.
+#ifndef MOE_CLAIMS
+#define MOE_CLAIMS 1
+#endif
+// Units per workgroup from which a launch claims its units.
+constexpr int kClaimRounds = 8;
+template <typename F>
+__device__ __forceinline__ void claim_units(int units, int32_t *claims,
+                                            int *s_unit, F &&run) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int nx = gridDim.x >> 3, xcd = blockIdx.x & 7, j = blockIdx.x >> 3;
+  const int per = (units + 7) >> 3;
+  auto share = [&](int z, int &lo, int &rest) {  // units past the first nx
+    lo = min(units, z * per);
+    rest = max(0, min(units, lo + per) - lo - nx);
+  };
+  int own_lo, own_rest;
+  share(xcd, own_lo, own_rest);
+  const int own_size = min(units, own_lo + per) - own_lo;
+  int next = j < own_size ? own_lo + j : -1;
+  bool own_done = false;
+#pragma nounroll
+  for (;;) {
+    __syncthreads();  // the previous unit is done with LDS and s_unit
+    if (wid == 0) {
+      int unit = next;
+      next = -1;
+      if (unit < 0 && !own_done) {
+        int v = 0;
+        if (lane == 0)
+          v = __hip_atomic_fetch_add(claims + xcd, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        v = __builtin_amdgcn_readfirstlane(v);
+        if (v < own_rest) unit = own_lo + nx + v;
+        else own_done = true;
+      }
+      // the own share is used up: claim from another that has units left
+      while (unit < 0) {
+        int lo = 0, rest = 0, c = 0;
+        if (lane < 8) {
+          share(lane, lo, rest);
+          c = __hip_atomic_load(claims + lane, __ATOMIC_RELAXED,
+                                __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const uint64_t open = __ballot(lane < 8 && c < rest) & 0xffull;
+        if (open == 0) break;
+        // the first open share after this XCD's, in ring order
+        const uint64_t rot = ((open >> xcd) | (open << (8 - xcd))) & 0xffull;
+        const int z = (xcd + __builtin_ctzll(rot)) & 7;
+        int zlo, zrest;
+        share(z, zlo, zrest);
+        int v = 0;
+        if (lane == 0)
+          v = __hip_atomic_fetch_add(claims + z, 1, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+        v = __builtin_amdgcn_readfirstlane(v);
+        if (v < zrest) unit = zlo + nx + v;
+      }
+      if (lane == 0) *s_unit = unit < 0 ? units : unit;
+    }
+    __syncthreads();
+    const int u = __builtin_amdgcn_readfirstlane(*s_unit);
+    if (u >= units) break;
+    run(u);
+  }
+}
+
 // One class of tiles (the router GEMM: one group, rows p.single_rows).
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
 __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) {
@@ -732,11 +813,11 @@ __global__ __launch_bounds__(256) void grouped_gemm2_kernel(GemmArgs ps,
   static_assert(TileCfg<MOE_SMALL_CFG>::NTH == 256 &&
                 TileCfg<MOE_WIDE_CFG>::NTH == 256, "256 threads");
   __shared__ uint4 smem[RS > RW ? RS : RW];
-  __shared__ int s_last;
+  __shared__ int s_last, s_unit;
   const int us = ps.tile_prefix[ps.G];
   const int S = pw.split ? *pw.split : 1;
   const int uw = pw.tile_prefix[pw.G] * S;
-  walk_units(us + uw, [&](int u) {
+  auto run = [&](int u) {
     if (u < us) {
       gemm_unit<MOE_SMALL_CFG, EPI>(ps, u, 0, 1, 0, 0, nullptr, 0, smem,
                                     &s_last);
@@ -745,7 +826,13 @@ __global__ __launch_bounds__(256) void grouped_gemm2_kernel(GemmArgs ps,
       gemm_unit<MOE_WIDE_CFG, EPI>(pw, t, u - us - t * S, S, t * S, t,
                                    nullptr, 0, smem, &s_last);
     }
-  });
+  };
+  // Many rounds of units per workgroup: claims (partners stay in step over
+  // the rounds); a few: the static walk, which costs no atomics.
+  if (MOE_CLAIMS && pw.claims && us + uw >= kClaimRounds * (int)gridDim.x)
+    claim_units(us + uw, pw.claims, &s_unit, run);
+  else
+    walk_units(us + uw, run);
 }
 
 namespace {
@@ -786,13 +873,14 @@ int64_t split_slots(int64_t n_local, int64_t R_cap, int64_t H, int64_t I) {
 // header, the two class prefixes and the split word, then the split-K
 // counters and partial slots.
 struct TileWs {
-  int32_t *err, *pre_s, *pre_w, *split, *ctr;
+  int32_t *err, *pre_s, *pre_w, *split, *claims, *ctr;
   float *part;
   int slots;
 };
 
-// int32 words after the error header: two prefixes and the split word
-int64_t tile_head_words(int64_t n_local) { return 2 * (n_local + 1) + 1; }
+// int32 words after the error header: two prefixes, the split word and the
+// eight claim counters
+int64_t tile_head_words(int64_t n_local) { return 2 * (n_local + 1) + 1 + 8; }
 
 TileWs tile_ws(int32_t *ws, int64_t n_local, int64_t slots) {
   TileWs w;
@@ -800,6 +888,7 @@ TileWs tile_ws(int32_t *ws, int64_t n_local, int64_t slots) {
   w.pre_s = ws + kErrHeaderBytes / 4;
   w.pre_w = w.pre_s + (n_local + 1);
   w.split = w.pre_w + (n_local + 1);
+  w.claims = w.split + 1;
   const int64_t head = kErrHeaderBytes + align256(tile_head_words(n_local) * 4);
   w.ctr = ws + head / 4;
   w.part = (float *)((char *)ws + head + align256(slots * 4));
@@ -850,7 +939,8 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
   }
   gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.r_cap, ws.err,
                                       p.group_w, p.n_w, 64, nt_s, kWideBM,
-                                      nt_w, ws.pre_s, ws.pre_w, sp);
+                                      nt_w, ws.pre_s, ws.pre_w, sp,
+                                      ws.claims);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // both row classes in one launch
@@ -860,6 +950,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
   GemmArgs pw = p;
   pw.tile_prefix = ws.pre_w;
   pw.NT = nt_w;
+  pw.claims = ws.claims;
   // units: the small class's tiles (an expert of at most 64 rows has one
   // m-tile) plus the large class's tiles or split units
   const int64_t small_units =
