@@ -186,9 +186,13 @@ int moe_permute(const int32_t *topk_idx, const float *topk_w, const void *x,
  * splits K into 2-4 ranges per tile and adds the fp32 partials (in a fixed
  * order: repeated calls give identical bits; a different split, as the per
  * expert loop may choose, rounds differently).
+ * The order in which tiles run never changes a tile's result; launches with
+ * many tiles per compute unit hand them out through per-XCD claim counters
+ * held in the workspace, so calls that share a workspace must not overlap.
  * workspace: moe_grouped_ffn_workspace_bytes(...) bytes, 16-aligned: the
- * tile plan plus, for R_cap > 64, the split-K partial sums (up to 512 slots
- * of 128 KiB: 64 MiB, fewer when R_cap, H and I allow fewer tiles).
+ * tile plan and claim counters plus, for R_cap > 64, the split-K partial
+ * sums (up to 512 slots of 128 KiB: 64 MiB, fewer when R_cap, H and I allow
+ * fewer tiles).
  * Limits (bf16): H % 64 == 0, I % 64 == 0, 1 <= n_local <= 4096,
  * R_cap < 2^31.  (fp32): H % 4 == 0, I % 4 == 0.
  */
