@@ -568,6 +568,7 @@ def compact(r):
     keep = ("value", "unit", "ms_per_step", "ms_per_step_eager", "dtype",
             "rows_per_s", "step_hbm_gbs", "step_hbm_frac", "step_mfma_frac",
             "step_mfma_frac_fp8", "step_mfma_frac_bf16", "ffn_ms_events",
+            "ffn_hbm_frac_p50",
             "step_ms_events", "loop_vs_grouped", "fused_vs_grouped",
             "master_quant_ms", "backward_ms_by_grad_format")
     out = {k: r[k] for k in keep if k in r}
@@ -927,6 +928,10 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
         "step_ms_events": step_pct,
         "ffn_ms_events": ffn_pct,
         "ffn_tflops_p50": round(alg["flop_ffn"] / (ffn_pct["p50"] * 1e-3) / 1e12, 2),
+        # the FFN's own bytes (every touched expert's weights once, the rows
+        # of x read, a written and read back, y written) over its p50 time
+        "ffn_hbm_frac_p50": round(alg["fused_bytes"] / (ffn_pct["p50"] * 1e-3) / 1e9
+                                  / HBM_PEAK_GBS, 4),
         "roofline": dict(**gate_up_bound, **{
             "kernel": ("fused FFN (gate/up + SwiGLU x scale + down) with its plan kernel"
                        if fused else "grouped gate/up GEMM + SwiGLU x scale"),
