@@ -438,6 +438,24 @@ __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
 // of each 32x32 block and rows 8*(r/4) + 4*(lane/32) + (r%4), r < 16.  bf16
 // outputs are staged in a per-wavefront LDS region (smem must be free) and
 // leave as 16-byte row pieces.
+// The routing-weight scale of each accumulator row of this lane (the
+// SwiGLU epilogue's s), 1 where there is none: all of them loaded at once,
+// ahead of the epilogue's arithmetic, instead of one load and one wait per
+// row inside it.
+template <int MB>
+__device__ __forceinline__ void load_row_scales(const GemmArgs &p, int row0,
+                                                int wrow0, int rows, int lane,
+                                                int mvalid,
+                                                float (&sc)[MB][16]) {
+#pragma unroll
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = wrow0 + m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      sc[m][r] = (m < mvalid && i < rows && p.row_scale) ? p.row_scale[row0 + i] : 1.f;
+    }
+}
+
 template <int EPI, int BN, int MB, int NB, int WTM, int WTN>
 __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[MB][NB],
                                               const GemmArgs &p, uint4 *smem,
@@ -446,6 +464,8 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[MB][NB],
                                               int wrow0, int rows,
                                               int32_t *dep, int di) {
   if (EPI == EPI_SWIGLU) {
+    float sc[MB][16];
+    load_row_scales<MB>(p, row0, wrow0, rows, lane, mvalid, sc);
     // B rows alternate 32 gate rows and the 32 matching up rows, so block
     // 2q holds g and block 2q+1 holds u of the same outputs in every lane.
     constexpr int W = WTN / 2;
@@ -456,8 +476,7 @@ __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[MB][NB],
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rw = m * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int i = wrow0 + rw;
-        const float s = (i < rows && p.row_scale) ? p.row_scale[row0 + i] : 1.f;
+        const float s = sc[m][r];
 #pragma unroll
         for (int q = 0; q < NB / 2; ++q) {
           const float g = acc[m][2 * q][r], u = acc[m][2 * q + 1][r];
