@@ -36,9 +36,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA
 FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 (MX-scaled) MFMA
 METRIC = "grouped MoE FFN TFLOP/s + rows/s per layer; % MFMA peak or % HBM BW"
-TIMING_GRAPH = ("K replays of the step captured in a HIP graph (same kernels, no host "
-                "launch overhead), after W eager warmup steps and K eager steps timed "
-                "with HIP events")
+TIMING_GRAPH = ("K steps replayed from HIP graphs that each hold up to 8 consecutive "
+                "steps (same kernels, no host launch between them), after W eager "
+                "warmup steps and K eager steps timed with HIP events")
 TIMING_EAGER = "K eager steps"
 
 
@@ -150,39 +150,61 @@ def algorithmic(wl, R, n_touched, gather=True):
                 fused_bytes=fused_bytes, step_bytes=step_bytes)
 
 
-def capture_steps(step_fns):
-    """One HIP graph per callable (each runs one step with preallocated
-    buffers), or None when capture is not possible here."""
+# Consecutive steps captured in one HIP graph: a model replays many MoE
+# layers inside one graph, so the step's kernels follow each other without a
+# host launch between steps.
+GRAPH_STEPS = 8
+
+
+def capture_steps(step_fn, n_steps, period=1):
+    """HIP graphs that hold consecutive steps: step_fn(j) runs step j (with
+    preallocated buffers; j % period selects the rotated weight copy).
+    Returns (graph of GRAPH_STEPS steps or fewer, steps in it, graph of the
+    remaining n_steps % that many steps or None), or None when capture is
+    not possible here."""
+    per = max(1, min(GRAPH_STEPS, n_steps))
+    per -= per % period if per >= period else 0
+    per = max(per, 1)
+    rest = n_steps % per
     try:
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            for fn in step_fns:
-                fn()
+            for j in range(per):
+                step_fn(j)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
-        graphs = []
-        for fn in step_fns:
+
+        def capture(n):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                fn()
-            graphs.append(g)
-        for g in graphs:
-            g.replay()
+                for j in range(n):
+                    step_fn(j)
+            return g
+
+        full = capture(per)
+        tail = capture(rest) if rest else None
+        full.replay()
+        if tail is not None:
+            tail.replay()
         torch.cuda.synchronize()
-        return graphs
+        return full, per, tail
     except RuntimeError as exc:           # capture not possible here
         log(f"graph capture failed, timing eager launches: {exc}")
         return None
 
 
 def time_graph_steps(graphs, steps):
-    """Milliseconds per step over exactly `steps` replays (graph j % n for
-    step j), bracketed by device synchronisation."""
+    """Milliseconds per step over exactly `steps` steps replayed from the
+    captured graphs, bracketed by device synchronisation."""
+    full, per, tail = graphs
+    n_full = steps // per
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for j in range(steps):
-        graphs[j % len(graphs)].replay()
+    for _ in range(n_full):
+        full.replay()
+    if tail is not None:
+        tail.replay()
     torch.cuda.synchronize()
     return (time.perf_counter() - t0) * 1e3 / steps
 
@@ -360,7 +382,7 @@ def run_mx(args, wl, dev, cpu=True):
     ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     gu_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
     step_pct = percentiles([e[0].elapsed_time(e[3]) for e in ev])
-    graphs = None if args.no_graph else capture_steps([step])
+    graphs = None if args.no_graph else capture_steps(lambda j: step(), args.steps)
     ms_step = time_graph_steps(graphs, args.steps) if graphs else ms_eager
     timing = TIMING_GRAPH if graphs else TIMING_EAGER
     if args.copy_probe_mb > 0:
@@ -502,9 +524,9 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=1536)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gather", action="store_true",
-                    help="full layer: permute writes x_perm and the gate/up "
-                         "GEMM reads it, instead of reading token rows of x "
-                         "through row_src (EP shares always read x_perm)")
+                    help="permute writes x_perm and the gate/up GEMM reads "
+                         "it, instead of reading token rows of x through "
+                         "row_src")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches instead of replays of the step "
                          "captured in a HIP graph")
@@ -768,9 +790,9 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
     logits = torch.empty((T, wl.E), dtype=torch.float32, device=dev)
     topk_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev)
-    # The full layer on one GPU reads token rows through row_src; an EP share
-    # gets its rows already permuted by the dispatch, so it reads x_perm.
-    gather = not args.no_gather and wl.n_local == wl.E
+    # The gate/up GEMM reads the token rows through row_src (the permute
+    # writes no x_perm), on the full layer and on the EP shares alike.
+    gather = not args.no_gather
     fused = args.ffn == "fused"
     pout = moe.PermuteOut(T, k, H, wl.n_local, torch.bfloat16, dev,
                           with_x=not gather)
@@ -811,7 +833,19 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
             if timed_ev is not None:
                 timed_ev[2].record(stream)
                 timed_ev[3].record(stream)
+        elif timed_ev is None:
+            # warm-up and captured steps: one call, one plan kernel for both
+            # GEMMs
+            if gather:
+                moe.grouped_ffn_gather(d["x"], pout.row_src, k, pout.offsets,
+                                       pout.s_perm, wg, wu, wd, a=a, y=y,
+                                       workspace=ws)
+            else:
+                moe.grouped_ffn(pout.x_perm, pout.offsets, pout.s_perm, wg, wu,
+                                wd, a=a, y=y, workspace=ws)
         else:
+            # event-timed eager steps: gate/up and down as separate calls
+            # (each with its plan kernel) so that an event sits between them
             if gather:
                 moe.grouped_gate_up_gather(d["x"], pout.row_src, k, pout.offsets,
                                            pout.s_perm, wg, wu, a=a, workspace=ws)
@@ -847,7 +881,7 @@ def run_bf16(args, wl, dev, cpu=True, loop=True):
 
     # the same steps replayed from captured graphs, one per weight copy
     graphs = (None if args.no_graph else
-              capture_steps([lambda i=i: step(i) for i in range(len(wcopies))]))
+              capture_steps(step, args.steps, len(wcopies)))
     ms_step = time_graph_steps(graphs, args.steps) if graphs else ms_eager
     timing = TIMING_GRAPH if graphs else TIMING_EAGER
 

@@ -234,7 +234,10 @@ int moe_grouped_down(const void *a, const int32_t *offsets, int64_t n_local,
 
 /*
  * moe_grouped_ffn - moe_grouped_gate_up followed by moe_grouped_down; `a`
- * [R_cap, I] (dtype) is the one intermediate handed between them.
+ * [R_cap, I] (dtype) is the one intermediate handed between them.  For bf16
+ * one plan kernel sizes both GEMMs' tile lists from the offsets (instead of
+ * one per call); the two grouped launches, their K splits and their output
+ * bits are those of the two calls.
  */
 int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
                     const float *s_perm, int64_t n_local, int64_t R_cap,
@@ -242,6 +245,26 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
                     const void *w_up, const void *w_down, int dtype, void *a,
                     void *y, void *workspace, size_t workspace_bytes,
                     hipStream_t stream);
+
+/*
+ * moe_grouped_ffn_gather - moe_grouped_ffn with the gate/up GEMM reading
+ * the token rows x [T, H] through row_src (permuted row r is
+ * x[row_src[r] / k]), as moe_grouped_gate_up_gather does: the permuted copy
+ * x_perm is never written.  Wide-EP explainer, 前提条件 (dispatch sends each
+ * token row to the experts it chose); the gather is folded into the GEMM's
+ * loads.  Outputs a, y, the error word, workspace and limits as
+ * moe_grouped_ffn, with T, k and R_cap <= T * k as for
+ * moe_grouped_gate_up_gather.  bf16 only (MOE_E_UNSUPPORTED otherwise).
+ * Same bits as moe_grouped_gate_up_gather followed by moe_grouped_down.
+ */
+int moe_grouped_ffn_gather(const void *x, const int32_t *row_src, int64_t T,
+                           int64_t k, const int32_t *offsets,
+                           const float *s_perm, int64_t n_local,
+                           int64_t R_cap, int64_t H, int64_t I,
+                           const void *w_gate, const void *w_up,
+                           const void *w_down, int dtype, void *a, void *y,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /*
  * moe_grouped_ffn_fused - the computation of moe_grouped_ffn (bf16) in one

@@ -67,6 +67,9 @@ def lib():
                                             vp, vp]
         L.moe_grouped_ffn_loop.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64,
                                            vp, vp, vp, i32, vp, vp, vp, sz, vp]
+        L.moe_grouped_ffn_gather.argtypes = [vp, vp, i64, i64, vp, vp, i64,
+                                             i64, i64, i64, vp, vp, vp, i32,
+                                             vp, vp, vp, sz, vp]
         L.moe_grouped_ffn_fused.argtypes = [vp, vp, i64, i64, vp, vp, i64, i64,
                                             i64, i64, vp, vp, vp, i32, vp, vp,
                                             vp, sz, vp]
@@ -303,6 +306,26 @@ def grouped_ffn(x_perm, offsets, s_perm, w_gate, w_up, w_down, a=None,
     _call("moe_grouped_ffn", _p(x_perm), _p(offsets), _p(s_perm), n_local,
           R_cap, H, I, _p(w_gate), _p(w_up), _p(w_down), _dt(x_perm), _p(a),
           _p(y), _p(workspace), workspace.numel(), _stream(stream))
+    return a, y
+
+
+def grouped_ffn_gather(x, row_src, k, offsets, s_perm, w_gate, w_up, w_down,
+                       a=None, y=None, workspace=None, stream=None):
+    """grouped_ffn with permuted row r of the gate/up input read as
+    x[row_src[r] // k] (R_cap = row_src.shape[0])."""
+    T, H = x.shape
+    R_cap = row_src.shape[0]
+    n_local, I, _ = w_gate.shape
+    if a is None:
+        a = torch.empty((R_cap, I), dtype=x.dtype, device=x.device)
+    if y is None:
+        y = torch.empty((R_cap, H), dtype=x.dtype, device=x.device)
+    if workspace is None:
+        workspace = ffn_workspace(R_cap, n_local, H, I, x.dtype, x.device)
+    _call("moe_grouped_ffn_gather", _p(x), _p(row_src), T, k, _p(offsets),
+          _p(s_perm), n_local, R_cap, H, I, _p(w_gate), _p(w_up), _p(w_down),
+          _dt(x), _p(a), _p(y), _p(workspace), workspace.numel(),
+          _stream(stream))
     return a, y
 
 

@@ -269,12 +269,47 @@ int moe_grouped_ffn(const void *x_perm, const int32_t *offsets,
   if (R_cap == 0) return MOE_OK;
   if (!w_down || !y) return MOE_E_ARG;
   if (!aligned16(w_down) || !aligned16(y)) return MOE_E_ALIGN;
+  if (dtype == MOE_DT_BF16) {
+    // one plan kernel for both GEMMs
+    if (!x_perm || !w_gate || !w_up || !a) return MOE_E_ARG;
+    if (!all_aligned16({x_perm, w_gate, w_up, a})) return MOE_E_ALIGN;
+    return status_of(moe::launch_ffn_grouped_bf16(
+        (const uint16_t *)x_perm, nullptr, 1, 1, offsets, s_perm,
+        (int)n_local, R_cap, (int)H, (int)I, (const uint16_t *)w_gate,
+        (const uint16_t *)w_up, (const uint16_t *)w_down, (uint16_t *)a,
+        (uint16_t *)y, (int32_t *)workspace, num_cus(), stream));
+  }
   st = moe_grouped_gate_up(x_perm, offsets, s_perm, n_local, R_cap, H, I,
                            w_gate, w_up, dtype, a, workspace, workspace_bytes,
                            stream);
   if (st != MOE_OK) return st;
   return moe_grouped_down(a, offsets, n_local, R_cap, H, I, w_down, dtype, y,
                           workspace, workspace_bytes, stream);
+}
+
+int moe_grouped_ffn_gather(const void *x, const int32_t *row_src, int64_t T,
+                           int64_t k, const int32_t *offsets,
+                           const float *s_perm, int64_t n_local,
+                           int64_t R_cap, int64_t H, int64_t I,
+                           const void *w_gate, const void *w_up,
+                           const void *w_down, int dtype, void *a, void *y,
+                           void *workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  int st = check_ffn(offsets, n_local, R_cap, H, I, dtype, workspace,
+                     workspace_bytes);
+  if (st != MOE_OK) return st;
+  if (dtype != MOE_DT_BF16) return MOE_E_UNSUPPORTED;
+  if (T < 1 || k < 1 || k > 32 || T * k >= kMaxRows || R_cap > T * k)
+    return MOE_E_SHAPE;
+  if (R_cap == 0) return MOE_OK;
+  if (!x || !row_src || !w_gate || !w_up || !w_down || !a || !y)
+    return MOE_E_ARG;
+  if (!all_aligned16({x, w_gate, w_up, w_down, a, y})) return MOE_E_ALIGN;
+  return status_of(moe::launch_ffn_grouped_bf16(
+      (const uint16_t *)x, row_src, (int)k, T, offsets, s_perm, (int)n_local,
+      R_cap, (int)H, (int)I, (const uint16_t *)w_gate, (const uint16_t *)w_up,
+      (const uint16_t *)w_down, (uint16_t *)a, (uint16_t *)y,
+      (int32_t *)workspace, num_cus(), stream));
 }
 
 int moe_grouped_ffn_fused(const void *x, const int32_t *row_src, int64_t T,

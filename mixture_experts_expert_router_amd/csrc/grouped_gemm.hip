@@ -47,6 +47,9 @@
 //     fragment reads) while every 8 lanes still read one contiguous row piece.
 //   * 32-row sub-tiles past the end of an expert's segment are skipped
 //     (uniform per wavefront).
+//   * A whole tile starts its K loop at a step rotated by its n-tile index
+//     (tile_rot), so that concurrent tiles read different columns of their
+//     weight rows.
 //   * Gather on load (gate/up): A rows may be read straight from the token
 //     rows x[row_src[r] / k] instead of a permuted copy.
 //   * Epilogues: SWIGLU (B rows alternate 32 gate and the 32 matching up
@@ -157,9 +160,9 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     int bm_wide, int nt_wide, int32_t *__restrict__ prefix_small,
     int32_t *__restrict__ prefix_wide, SplitPlan sp, int32_t *claims) {
   __shared__ int32_t wsum[2][16];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, nth = blockDim.x, nw = nth >> 6;
   if (claims && tid < 8) claims[tid] = 0;
-  const int per = (G + 1023) / 1024;
+  const int per = (G + nth - 1) / nth;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
   auto tiles = [&](int e, int32_t &t0, int32_t &t1) {
     int b, en;
@@ -196,8 +199,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
   int32_t r[2], total[2];
   for (int c = 0; c < 2; ++c) {
     int32_t before = 0, all = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < nw; ++q) {
       const int32_t v = wsum[c][q];
       before += q < wv ? v : 0;
       all += v;
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     r[0] += t[0];
     r[1] += t[1];
   }
-  if (tid == 1023) {
+  if (tid == nth - 1) {
     prefix_small[G] = total[0];
     prefix_wide[G] = total[1];
   }
@@ -223,7 +225,7 @@ __global__ __launch_bounds__(1024) void gemm_plan_kernel(
     const int S = choose_split(sp, tw, sp.slots);
     if (tid == 0) *sp.word = S;
     if (S > 1)
-      for (int i = tid; i < tw; i += 1024) sp.ctr[i] = 0;
+      for (int i = tid; i < tw; i += nth) sp.ctr[i] = 0;
   }
   // OR of the error bits over the block
   __shared__ int32_t bad_or;
@@ -261,6 +263,28 @@ __device__ __forceinline__ int swz(int row, int c) {
   return CPR == 8 ? (c ^ ((row >> 1) & 7)) : (c ^ ((row >> 2) & 3));
 }
 
+// K steps of a whole tile may start at step rot (then wrap): K step ks of
+// the loop reads step (ks + rot) mod KT, with rot = 5 * n-tile mod KT.
+// Workgroups that start together and stream weights at the same rate would
+// otherwise read the same 128-byte column of every weight row at the same
+// time; with rows a power of two bytes apart (4 KiB at K = 2048, the down
+// projection) those reads fall on the same few HBM channels.  Measured on
+// the EP8 share (32 experts of 7-34 rows, weight-streaming): the down
+// projection replayed in a graph 196 -> 172 us.  The rotation depends only
+// on the tile's n-tile and K, so every path that runs a tile whole sums in
+// the same order (bit-equal results across the grouped, per-expert-loop and
+// one-launch paths); split-K units are not rotated.
+#ifndef MOE_KROT
+#define MOE_KROT 1
+#endif
+__device__ __forceinline__ int rot_step(int ks, int rot, int KT) {
+  const int r = ks + rot;
+  return r >= KT ? r - KT : r;
+}
+__device__ __forceinline__ int tile_rot(int nt, int KT) {
+  return MOE_KROT ? (nt * 5) % KT : 0;
+}
+
 // Load the A and B fragments of k-substep kk (16 values of K) from one LDS
 // stage: lane holds row (lane & 31) of each 32-row block, K chunk
 // 2*kk + lane/32.
@@ -292,13 +316,14 @@ __device__ __forceinline__ void load_frags(const uint4 *As, const uint4 *Bs,
 // there) instead of being issued in one burst, so the vector-memory queue
 // never stalls the matrix work; fragment reads of k-substep kk+1 are issued
 // before the MFMAs of kk.  The loop body has no data-dependent branches.
+// Loop step ks reads K step rot_step(ks, rot, KT) (see tile_rot).
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int MV,
           bool FRONT>
 __device__ __forceinline__ void gemm_kloop(
     f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
     const char *const (&gsrc)[(BM + BN) * (BK / 8) / (WM * WN * 64)],
     const uint4 *smem, uint32_t lds0, uint32_t wave_off, int KT, int lane,
-    int arow0, int brow0) {
+    int arow0, int brow0, int rot = 0) {
   constexpr int CPR = BK / 8, NB = BN / WN / 32, KK = BK / 16;
   constexpr int STAGE_CHUNKS = (BM + BN) * CPR;
   constexpr int L = STAGE_CHUNKS / (WM * WN * 64);
@@ -310,7 +335,7 @@ __device__ __forceinline__ void gemm_kloop(
     const int ks = min(kt + STAGES - 1, KT - 1);
     const int st = (kt + STAGES - 1) % STAGES;
     const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
-    const int64_t koff = (int64_t)ks * (BK * 2);
+    const int64_t koff = (int64_t)rot_step(ks, rot, KT) * (BK * 2);
     if constexpr (FRONT || MV == 0) {
 #pragma unroll
       for (int i = 0; i < L; ++i)
@@ -395,6 +420,11 @@ __device__ __forceinline__ bool split_hand_over(f32x16 (&acc)[MB][NB],
     const int old = __hip_atomic_fetch_add(p.ctr + ci, 1, __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT);
     *s_last = old == S - 1;
+    // every unit of the tile has counted in: the counter goes back to zero
+    // for a later launch that reuses it (the two launches of the grouped FFN)
+    if (old == S - 1)
+      __hip_atomic_store(p.ctr + ci, 0, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
   if (!__builtin_amdgcn_readfirstlane(*s_last)) return false;
@@ -456,16 +486,16 @@ __device__ __forceinline__ void load_row_scales(const GemmArgs &p, int row0,
     }
 }
 
+// sc: the rows' routing scales (SWIGLU; load_row_scales), unused otherwise.
 template <int EPI, int BN, int MB, int NB, int WTM, int WTN>
 __device__ __forceinline__ void tile_epilogue(f32x16 (&acc)[MB][NB],
                                               const GemmArgs &p, uint4 *smem,
                                               int wid, int wn, int lane,
                                               int mvalid, int nt, int row0,
                                               int wrow0, int rows,
-                                              int32_t *dep, int di) {
+                                              int32_t *dep, int di,
+                                              const float (&sc)[MB][16]) {
   if (EPI == EPI_SWIGLU) {
-    float sc[MB][16];
-    load_row_scales<MB>(p, row0, wrow0, rows, lane, mvalid, sc);
     // B rows alternate 32 gate rows and the 32 matching up rows, so block
     // 2q holds g and block 2q+1 holds u of the same outputs in every lane.
     constexpr int W = WTN / 2;
@@ -578,44 +608,22 @@ __device__ __forceinline__ void tile_coords(const GemmArgs &p, int t, int &e,
   rows = min(BM, r_end - row0);
 }
 
-// One unit of a launch's class: K range ks of S of tile t; split units
-// hand over through slots slot0 .. slot0 + S - 1 and counter ctr[ci].  With
-// dep non-null (gate/up inside the fused FFN) the epilogue writes a through
-// device-coherent stores and then counts the tile in on dep[di].
-// smem: the LDS ring (at least the configuration's RING chunks), free on
-// entry; s_last: an LDS word for the split hand-over.
+// Global source of each of this thread's L loads per stage of tile t (K
+// range starting at step kt0), and the tile's coordinates.  The stage is
+// cut into groups of 64 chunks (one load instruction each); wavefront w
+// issues groups [w*L, w*L + L), so with BM == BN two wavefronts load only A
+// rows (mostly L2 hits) and two only B rows (weight stream): a wavefront's
+// loads return in order, and this keeps the quick hits out of the queue
+// behind slow misses.  Chunk q = (w*L + i)*64 + lane.
 template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
-__device__ __forceinline__ void gemm_unit(const GemmArgs &p, int t, int ks,
-                                          int S, int slot0, int ci,
-                                          int32_t *dep, int di, uint4 *smem,
-                                          int *s_last) {
+__device__ __forceinline__ void tile_sources(
+    const GemmArgs &p, int t, int kt0, int wid, int lane,
+    const char *(&gsrc)[TileCfg<BM, BN, WM, WN, BK, STAGES>::L], int &e,
+    int &mt, int &nt, int &row0, int &rows) {
   using C = TileCfg<BM, BN, WM, WN, BK, STAGES>;
-  constexpr int CPR = C::CPR, WTM = C::WTM, WTN = C::WTN, MB = C::MB,
-                NB = C::NB, STAGE_CHUNKS = C::STAGE_CHUNKS, L = C::L;
-  static_assert(EPI != EPI_SWIGLU || NB % 2 == 0,
-                "SwiGLU pairs a gate block with the up block next to it");
-  const int tid = threadIdx.x;
-  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
-  const int wm = wid / WN, wn = wid % WN;
+  constexpr int CPR = C::CPR, L = C::L;
   const int K = p.K;
-  const int KT = K / BK;
-  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
-  const int kt0 = ks * KT / S, KTs = (ks + 1) * KT / S - kt0;
-  // The lane index, opaque to the compiler: otherwise, inside the caller's
-  // persistent loop, it hoists every lane-dependent LDS address of the unit
-  // out of the loop and keeps them all live (register spills).
-  int lane;
-  asm volatile("; lane index" : "=v"(lane) : "0"(tid & 63));
-  int e, mt, nt, row0, rows;
   tile_coords<BM>(p, t, e, mt, nt, row0, rows);
-
-  // Global source of each of this thread's L loads per stage.  The stage
-  // is cut into groups of 64 chunks (one load instruction each); wavefront
-  // w issues groups [w*L, w*L + L), so with BM == BN two wavefronts load
-  // only A rows (mostly L2 hits) and two only B rows (weight stream): a
-  // wavefront's loads return in order, and this keeps the quick hits out
-  // of the queue behind slow misses.  Chunk q = (w*L + i)*64 + lane.
-  const char *gsrc[L];
 #pragma unroll
   for (int i = 0; i < L; ++i) {
     const int q = (wid * L + i) * 64 + lane;
@@ -644,7 +652,41 @@ __device__ __forceinline__ void gemm_unit(const GemmArgs &p, int t, int ks,
     }
     gsrc[i] += (int64_t)kt0 * (BK * 2);
   }
+}
+
+// One unit of a launch's class: K range ks of S of tile t; split units
+// hand over through slots slot0 .. slot0 + S - 1 and counter ctr[ci].  With
+// dep non-null (gate/up inside the fused FFN) the epilogue writes a through
+// device-coherent stores and then counts the tile in on dep[di].
+// smem: the LDS ring (at least the configuration's RING chunks), free on
+// entry; s_last: an LDS word for the split hand-over.
+template <int BM, int BN, int WM, int WN, int BK, int STAGES, int EPI>
+__device__ __forceinline__ void gemm_unit(const GemmArgs &p, int t, int ks,
+                                          int S, int slot0, int ci,
+                                          int32_t *dep, int di, uint4 *smem,
+                                          int *s_last) {
+  using C = TileCfg<BM, BN, WM, WN, BK, STAGES>;
+  constexpr int WTM = C::WTM, WTN = C::WTN, MB = C::MB, NB = C::NB,
+                STAGE_CHUNKS = C::STAGE_CHUNKS, L = C::L;
+  static_assert(EPI != EPI_SWIGLU || NB % 2 == 0,
+                "SwiGLU pairs a gate block with the up block next to it");
+  const int tid = threadIdx.x;
+  const int wid = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform
+  const int wm = wid / WN, wn = wid % WN;
+  const int KT = p.K / BK;
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)smem);
+  const int kt0 = ks * KT / S, KTs = (ks + 1) * KT / S - kt0;
+  // The lane index, opaque to the compiler: otherwise, inside the caller's
+  // persistent loop, it hoists every lane-dependent LDS address of the unit
+  // out of the loop and keeps them all live (register spills).
+  int lane;
+  asm volatile("; lane index" : "=v"(lane) : "0"(tid & 63));
+  int e, mt, nt, row0, rows;
+  const char *gsrc[L];
+  tile_sources<BM, BN, WM, WN, BK, STAGES, EPI>(p, t, kt0, wid, lane, gsrc, e,
+                                                mt, nt, row0, rows);
   const uint32_t wave_off = (uint32_t)(wid * L * 64 * 16);
+  const int rot = S == 1 ? tile_rot(nt, KTs) : 0;
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -662,7 +704,7 @@ __device__ __forceinline__ void gemm_unit(const GemmArgs &p, int t, int ks,
 #pragma unroll
   for (int st = 0; st < STAGES - 1; ++st) {
     const uint32_t sb = lds0 + (uint32_t)(st * STAGE_CHUNKS * 16) + wave_off;
-    const int64_t koff = (int64_t)min(st, KTs - 1) * (BK * 2);
+    const int64_t koff = (int64_t)rot_step(min(st, KTs - 1), rot, KTs) * (BK * 2);
 #pragma unroll
     for (int i = 0; i < L; ++i)
       load_lds16(sb + (uint32_t)(i * 64 * 16), gsrc[i] + koff);
@@ -681,7 +723,7 @@ __device__ __forceinline__ void gemm_unit(const GemmArgs &p, int t, int ks,
               acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);    \
         else                                                                \
           gemm_kloop<BM, BN, WM, WN, BK, STAGES, (mv <= MB ? mv : 1), false>(\
-              acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);    \
+              acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0, rot);\
       }                                                                     \
       break;
   switch (mvalid) {
@@ -691,16 +733,20 @@ __device__ __forceinline__ void gemm_unit(const GemmArgs &p, int t, int ks,
     MOE_KLOOP_CASE(4)
     default:
       gemm_kloop<BM, BN, WM, WN, BK, STAGES, 0, false>(
-          acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0);
+          acc, gsrc, smem, lds0, wave_off, KTs, lane, wrow0, brow0, rot);
   }
 #undef MOE_KLOOP_CASE
   // every wavefront is done reading the ring before the next tile refills it
   wait_loads_barrier<0>();
   if (S == 1 || split_hand_over<MB, NB>(acc, p, slot0, ci, ks, S, wid, lane,
-                                         mvalid, s_last))
+                                         mvalid, s_last)) {
+    float sc[MB][16];
+    if constexpr (EPI == EPI_SWIGLU)
+      load_row_scales<MB>(p, row0, wrow0, rows, lane, mvalid, sc);
     tile_epilogue<EPI, BN, MB, NB, WTM, WTN>(acc, p, smem, wid, wn, lane,
                                              mvalid, nt, row0, wrow0, rows,
-                                             dep, di);
+                                             dep, di, sc);
+  }
 }
 
 // Walk the units [0, units) of a launch: XCD x (workgroups b with b % 8 ==
@@ -823,7 +869,9 @@ __global__ __launch_bounds__(WM * WN * 64) void grouped_gemm_kernel(GemmArgs p) 
 #ifndef MOE_WIDE_CFG
 #define MOE_WIDE_CFG 128, 256, 2, 2, 64, 3
 #endif
+#ifndef MOE_SMALL_CFG
 #define MOE_SMALL_CFG 64, 256, 1, 4, 64, 3
+#endif
 template <int EPI>
 __global__ __launch_bounds__(256) void grouped_gemm2_kernel(GemmArgs ps,
                                                             GemmArgs pw) {
@@ -859,6 +907,9 @@ namespace {
 // BM, BN, WM, WN, BK, STAGES of the large-expert shape: MOE_WIDE_CFG.
 constexpr int kWideCfg[6] = {MOE_WIDE_CFG};
 constexpr int kWideBM = kWideCfg[0], kWideBN = kWideCfg[1];
+constexpr int kSmallCfg[6] = {MOE_SMALL_CFG};
+constexpr int kSmallBN = kSmallCfg[1];
+static_assert(kSmallCfg[0] == kSmallRows, "the small class is one m-tile");
 
 // Largest K split, and the most partial slots a workspace carries (at
 // 128 KiB each: 64 MiB).
@@ -868,6 +919,12 @@ constexpr int kWideBM = kWideCfg[0], kWideBN = kWideCfg[1];
 constexpr int kSplitMax = MOE_SPLITK_MAX;
 constexpr int64_t kSplitSlotsMax = 512;
 constexpr size_t kSlotBytes = (size_t)kWideBM * kWideBN * 4;
+
+// Threads of a one-block plan kernel over G experts: one per expert, in
+// whole wavefronts, at most 1024 (a small launch starts and ends sooner).
+unsigned plan_threads(int G) {
+  return (unsigned)std::min(1024, std::max(64, (G + 63) / 64 * 64));
+}
 
 int ntiles(int N, int BN, bool swiglu) {
   const int cols = swiglu ? BN / 2 : BN;
@@ -941,7 +998,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
                           int64_t host_rows = -1) {
   const bool sw = EPI == EPI_SWIGLU;
   const int nt_w = ntiles(p.N, kWideBN, sw);
-  const int nt_s = ntiles(p.N, 256, sw);
+  const int nt_s = ntiles(p.N, kSmallBN, sw);
   const int64_t grid_rows = host_rows >= 0 ? host_rows : R_cap;
   p.r_cap = (int)R_cap;
   SplitPlan sp{};
@@ -956,7 +1013,7 @@ hipError_t launch_grouped(GemmArgs p, int num_cus, const TileWs &ws,
     // slot: BM x BN fp32; the tile's weights: BN rows of K bf16
     sp.part_ratio = (float)(kWideBM * 4) / (float)(p.K * 2);
   }
-  gemm_plan_kernel<<<1, 1024, 0, s>>>(p.offsets, p.G, p.r_cap, ws.err,
+  gemm_plan_kernel<<<1, plan_threads(p.G), 0, s>>>(p.offsets, p.G, p.r_cap, ws.err,
                                       p.group_w, p.n_w, 64, nt_s, kWideBM,
                                       nt_w, ws.pre_s, ws.pre_w, sp,
                                       ws.claims);
@@ -1214,12 +1271,18 @@ __global__ __launch_bounds__(256) void grouped_ffn_kernel(FfnArgs f) {
   }
 }
 
-// Plan of the fused FFN, one block: per expert the tiles of both row
+// Plan of the FFN's two GEMMs, one block: per expert the tiles of both row
 // classes for both GEMMs and the m-tiles of both classes, as exclusive
-// prefixes (G + 1 entries each); the split of each GEMM's large-row class
-// (gate/up first, down with the slots gate/up leaves); the claim counter,
-// the m-tile counters and the split counters in use cleared; the error word
-// (kDevErrRows for offsets past r_cap or decreasing, else 0).
+// prefixes (G + 1 entries each); the split of each GEMM's large-row class;
+// the claim counters, the m-tile counters and the split counters in use
+// cleared; the error word (kDevErrRows for offsets past r_cap or
+// decreasing, else 0).  For the one-launch FFN (independent == 0) both
+// GEMMs' units share the partial slots (gate/up first, down with the slots
+// gate/up leaves) and down's tiles count in on the counters after gate/up's.
+// For the grouped FFN's two launches (independent == 1) each GEMM chooses
+// its split as its own launch would and both start at slot and counter 0:
+// the gate/up launch has handed over (and reset its counters) before the
+// down launch starts.
 struct FfnPlanArgs {
   const int32_t *offsets;
   int G, r_cap;
@@ -1228,6 +1291,7 @@ struct FfnPlanArgs {
   int32_t *mpre[2];         // m-tile prefixes: small, large
   int32_t *words, *dep, *err;
   SplitPlan gu, dn;         // split choice of each GEMM (word unused)
+  int independent;          // 1: the two GEMMs run as separate launches
 };
 
 __global__ __launch_bounds__(1024) void ffn_plan_kernel(FfnPlanArgs a) {
@@ -1235,9 +1299,10 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(FfnPlanArgs a) {
   __shared__ int32_t wsum[NC][16];
   __shared__ int32_t bad_or;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int nth = blockDim.x, nw = nth >> 6;
   if (tid == 0) bad_or = 0;
   const int G = a.G;
-  const int per = (G + 1023) / 1024;
+  const int per = (G + nth - 1) / nth;
   const int e0 = min(G, tid * per), e1 = min(G, e0 + per);
   auto counts = [&](int e, int32_t (&c)[NC]) {
     int b, en;
@@ -1273,8 +1338,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(FfnPlanArgs a) {
   int32_t r[NC], total[NC];
   for (int i = 0; i < NC; ++i) {
     int32_t before = 0, all = 0;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
+    for (int q = 0; q < nw; ++q) {
       const int32_t v = wsum[i][q];
       before += q < wv ? v : 0;
       all += v;
@@ -1290,7 +1354,7 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(FfnPlanArgs a) {
     counts(e, c);
     for (int i = 0; i < NC; ++i) r[i] += c[i];
   }
-  if (tid == 1023) {
+  if (tid == nth - 1) {
     for (int i = 0; i < 4; ++i) a.pre[i][G] = total[i];
     a.mpre[0][G] = total[4];
     a.mpre[1][G] = total[5];
@@ -1298,7 +1362,12 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(FfnPlanArgs a) {
   // splits of the large-row class (every thread chooses the same)
   const int gw = total[1], dw = total[3];
   int Sg = 1, Sd = 1;
-  if (a.gu.slots >= 2 && (int64_t)gw + dw <= a.gu.slots) {
+  if (a.independent) {
+    if (a.gu.slots >= 2) {
+      Sg = choose_split(a.gu, gw, a.gu.slots);
+      Sd = choose_split(a.dn, dw, a.dn.slots);
+    }
+  } else if (a.gu.slots >= 2 && (int64_t)gw + dw <= a.gu.slots) {
     // gate/up's units take slots [0, gw*Sg), down's the ones after
     Sg = choose_split(a.gu, gw, a.gu.slots);
     Sd = choose_split(a.dn, dw, (int64_t)a.dn.slots - (int64_t)gw * Sg);
@@ -1309,10 +1378,12 @@ __global__ __launch_bounds__(1024) void ffn_plan_kernel(FfnPlanArgs a) {
     a.words[17] = Sd;
   }
   const int nm = total[4] + total[5];
-  for (int i = tid; i < nm; i += 1024) a.dep[i] = 0;
-  // split counters: gate/up tiles [0, gw), down tiles [gw, gw + dw)
-  const int nc = (Sg > 1 || Sd > 1) ? gw + dw : 0;
-  for (int i = tid; i < nc; i += 1024) a.gu.ctr[i] = 0;
+  for (int i = tid; i < nm; i += nth) a.dep[i] = 0;
+  // split counters: gate/up tiles [0, gw), down tiles [gw, gw + dw) (one
+  // launch) or [0, dw) (two launches)
+  const int nc = a.independent ? max(Sg > 1 ? gw : 0, Sd > 1 ? dw : 0)
+                               : ((Sg > 1 || Sd > 1) ? gw + dw : 0);
+  for (int i = tid; i < nc; i += nth) a.gu.ctr[i] = 0;
   if (bad) atomicOr(&bad_or, bad);
   __syncthreads();
   if (tid == 0) *a.err = bad_or;
@@ -1351,18 +1422,31 @@ size_t ffn_fused_workspace_bytes(int64_t n_local, int64_t R_cap, int64_t H,
          (size_t)align256(ffn_extra_words(n_local, R_cap) * 4);
 }
 
-hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
-                                 int k, int64_t T, const int32_t *offsets,
-                                 const float *s_perm, int n_local,
-                                 int64_t R_cap, int H, int I,
-                                 const uint16_t *w_gate, const uint16_t *w_up,
-                                 const uint16_t *w_down, uint16_t *a,
-                                 uint16_t *y, int32_t *ws, int num_cus,
-                                 hipStream_t s) {
+namespace {
+
+// Arguments of both GEMMs of the FFN and of their plan kernel, over the
+// workspace laid out as the one-launch FFN's (the grouped FFN's two launches
+// use the same layout).
+struct FfnSetup {
+  FfnArgs f;
+  FfnPlanArgs pa;
+  TileWs w;
+  FfnWs fw;
+};
+
+FfnSetup ffn_setup(const uint16_t *x, const int32_t *row_src, int k,
+                   int64_t T, const int32_t *offsets, const float *s_perm,
+                   int n_local, int64_t R_cap, int H, int I,
+                   const uint16_t *w_gate, const uint16_t *w_up,
+                   const uint16_t *w_down, uint16_t *a, uint16_t *y,
+                   int32_t *ws, int num_cus, int independent) {
+  FfnSetup st{};
   const int64_t slots = split_slots(n_local, R_cap, H, I);
-  const TileWs w = moe::tile_ws(ws, n_local, slots);
-  const FfnWs fw = ffn_ws(w, n_local);
-  FfnArgs f{};
+  st.w = moe::tile_ws(ws, n_local, slots);
+  st.fw = ffn_ws(st.w, n_local);
+  const TileWs &w = st.w;
+  const FfnWs &fw = st.fw;
+  FfnArgs &f = st.f;
   // gate/up: x (gathered through row_src, or x_perm) against W_gate / W_up
   GemmArgs gu{};
   gu.A = x; gu.B0 = w_gate; gu.B1 = w_up;
@@ -1380,8 +1464,8 @@ hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
   dn.offsets = offsets; dn.G = n_local; dn.N = H; dn.K = I;
   dn.r_cap = (int)R_cap;
   dn.ctr = w.ctr; dn.part = w.part;
-  const int nt[4] = {ntiles(I, 256, true), ntiles(I, kWideBN, true),
-                     ntiles(H, 256, false), ntiles(H, kWideBN, false)};
+  const int nt[4] = {ntiles(I, kSmallBN, true), ntiles(I, kWideBN, true),
+                     ntiles(H, kSmallBN, false), ntiles(H, kWideBN, false)};
   int32_t *pre[4] = {w.pre_s, w.pre_w, fw.pre_ds, fw.pre_dw};
   for (int i = 0; i < 4; ++i) {
     f.g[i] = i < 2 ? gu : dn;
@@ -1391,11 +1475,12 @@ hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
   f.mpre_s = fw.mpre_s; f.mpre_w = fw.mpre_w;
   f.words = fw.words; f.dep = fw.dep; f.err = w.err;
   f.nt_gu = nt[0];
-  FfnPlanArgs pa{};
+  FfnPlanArgs &pa = st.pa;
   pa.offsets = offsets; pa.G = n_local; pa.r_cap = (int)R_cap;
   for (int i = 0; i < 4; ++i) { pa.nt[i] = nt[i]; pa.pre[i] = pre[i]; }
   pa.mpre[0] = fw.mpre_s; pa.mpre[1] = fw.mpre_w;
   pa.words = fw.words; pa.dep = fw.dep; pa.err = w.err;
+  pa.independent = independent;
   for (int i = 0; i < 2; ++i) {
     SplitPlan &sp = i == 0 ? pa.gu : pa.dn;
     const int K = i == 0 ? H : I;
@@ -1409,14 +1494,79 @@ hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
       sp.part_ratio = (float)(kWideBM * 4) / (float)(K * 2);
     }
   }
-  ffn_plan_kernel<<<1, 1024, 0, s>>>(pa);
+  return st;
+}
+
+// Workgroups of a grouped GEMM launch over n_local experts and rows up to
+// R_cap (units of both classes; the wide class at least as many as the
+// partial slots when it may split), one per compute unit at most.
+int64_t gemm2_grid(int N, bool swiglu, int n_local, int64_t R_cap,
+                   int slots, int num_cus) {
+  const int64_t small_units = (int64_t)n_local * ntiles(N, kSmallBN, swiglu);
+  int64_t wide_units = ((R_cap + kWideBM - 1) / kWideBM + n_local) *
+                       (int64_t)ntiles(N, kWideBN, swiglu);
+  if (slots >= 2) wide_units = std::max<int64_t>(wide_units, slots);
+  int64_t grid = tile_grid(small_units + wide_units);
+  if (MOE_GEMM_PERSISTENT)
+    grid = std::min<int64_t>(grid, std::max(8, num_cus / 8 * 8));
+  return grid;
+}
+
+}  // namespace
+
+hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
+                                 int k, int64_t T, const int32_t *offsets,
+                                 const float *s_perm, int n_local,
+                                 int64_t R_cap, int H, int I,
+                                 const uint16_t *w_gate, const uint16_t *w_up,
+                                 const uint16_t *w_down, uint16_t *a,
+                                 uint16_t *y, int32_t *ws, int num_cus,
+                                 hipStream_t s) {
+  const FfnSetup st = ffn_setup(x, row_src, k, T, offsets, s_perm, n_local,
+                                R_cap, H, I, w_gate, w_up, w_down, a, y, ws,
+                                num_cus, 0);
+  ffn_plan_kernel<<<1, plan_threads(n_local), 0, s>>>(st.pa);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   // one resident workgroup per CU (the LDS ring allows one), a multiple of
   // 8 so that every XCD has as many; a grid larger than the work only adds
   // workgroups that claim nothing
-  grouped_ffn_kernel<<<(unsigned)std::max(8, num_cus / 8 * 8), 256, 0, s>>>(f);
+  grouped_ffn_kernel<<<(unsigned)std::max(8, num_cus / 8 * 8), 256, 0, s>>>(
+      st.f);
   return hipGetLastError();
+}
+
+hipError_t launch_ffn_grouped_bf16(const uint16_t *x, const int32_t *row_src,
+                                   int k, int64_t T, const int32_t *offsets,
+                                   const float *s_perm, int n_local,
+                                   int64_t R_cap, int H, int I,
+                                   const uint16_t *w_gate,
+                                   const uint16_t *w_up,
+                                   const uint16_t *w_down, uint16_t *a,
+                                   uint16_t *y, int32_t *ws, int num_cus,
+                                   hipStream_t s) {
+  const FfnSetup st = ffn_setup(x, row_src, k, T, offsets, s_perm, n_local,
+                                R_cap, H, I, w_gate, w_up, w_down, a, y, ws,
+                                num_cus, 1);
+  ffn_plan_kernel<<<1, plan_threads(n_local), 0, s>>>(st.pa);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const bool split = st.w.slots >= 2;
+  for (int d = 0; d < 2; ++d) {
+    GemmArgs ps = st.f.g[2 * d], pw = st.f.g[2 * d + 1];
+    pw.claims = st.fw.words + 8 * d;
+    if (split) pw.split = st.fw.words + 16 + d;
+    else { pw.ctr = nullptr; pw.part = nullptr; }
+    const int64_t grid = gemm2_grid(d == 0 ? I : H, d == 0, n_local, R_cap,
+                                    st.w.slots, num_cus);
+    if (d == 0)
+      grouped_gemm2_kernel<EPI_SWIGLU><<<(unsigned)grid, 256, 0, s>>>(ps, pw);
+    else
+      grouped_gemm2_kernel<EPI_BF16><<<(unsigned)grid, 256, 0, s>>>(ps, pw);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
 }
 
 }  // namespace moe

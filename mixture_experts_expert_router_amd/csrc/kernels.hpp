@@ -103,6 +103,19 @@ hipError_t launch_ffn_fused_bf16(const uint16_t *x, const int32_t *row_src,
                                  const uint16_t *w_down, uint16_t *a,
                                  uint16_t *y, int32_t *ws, int num_cus,
                                  hipStream_t s);
+// The grouped FFN: one plan kernel for both GEMMs, then the gate/up and the
+// down launches of the grouped GEMM (the same kernels, tiles and results as
+// launch_gate_up_bf16 followed by launch_down_bf16); x as for the one-launch
+// FFN; the workspace as the one-launch FFN's.
+hipError_t launch_ffn_grouped_bf16(const uint16_t *x, const int32_t *row_src,
+                                   int k, int64_t T, const int32_t *offsets,
+                                   const float *s_perm, int n_local,
+                                   int64_t R_cap, int H, int I,
+                                   const uint16_t *w_gate,
+                                   const uint16_t *w_up,
+                                   const uint16_t *w_down, uint16_t *a,
+                                   uint16_t *y, int32_t *ws, int num_cus,
+                                   hipStream_t s);
 hipError_t launch_gate_up_f32(const float *x_perm, const int32_t *offsets,
                               const float *s_perm, int n_local, int64_t R_cap,
                               int64_t H, int64_t I, const float *w_gate,

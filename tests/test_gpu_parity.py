@@ -397,3 +397,91 @@ def test_ffn_loop_mid_workload_matches_oracle():
     R = int(p.offsets[-1].item())
     assert_close(to_f64(a2[:R]), ref["a"], "bf16", "loop a")
     assert_close(to_f64(y2[:R]), ref["y"], "bf16", "loop y")
+
+
+@pytest.mark.parametrize("counts,H,I", [
+    # split K in both GEMMs (gate/up 4 ways, down 2) beside a small-class
+    # expert and an empty one
+    ([200, 0, 129, 70, 40], 2048, 1024),
+    # gate/up split, down (K 512: too short to split) not
+    ([300, 17], 1024, 512),
+    # small class only: no split, no claim
+    ([1, 64, 33, 0, 7], 512, 384),
+])
+def test_ffn_one_plan_equals_separate_calls(counts, H, I):
+    """moe_grouped_ffn plans both GEMMs in one kernel; its a and y are the
+    bits of moe_grouped_gate_up followed by moe_grouped_down (same splits,
+    the split counters reset by the gate/up launch for the down launch), and
+    moe_grouped_ffn_gather's are those of the gathering gate/up call followed
+    by the down call.  Two calls in a row, on one workspace."""
+    print_case("one-plan FFN", counts, H, I)
+    n_local, E, k, e_begin = len(counts), 16, 4, 0
+    idx, w, x, wg, wu, wd = _edge_inputs(counts, n_local, e_begin, E, k, H, I,
+                                         seed=11)
+    wt = to_dev(w.astype(np.float32))
+    dx = to_dev(x)
+    p = moe.permute(to_dev(idx), dx, e_begin, n_local, topk_w=wt, E=E)
+    dwg, dwu, dwd = to_dev(wg), to_dev(wu), to_dev(wd)
+    R_cap, I_ = p.x_perm.shape[0], wg.shape[1]
+    ws = moe.ffn_workspace(R_cap, n_local, H, I_, torch.bfloat16, "cuda")
+    a1 = moe.grouped_gate_up(p.x_perm, p.offsets, p.s_perm, dwg, dwu,
+                             workspace=ws)
+    y1 = moe.grouped_down(a1, p.offsets, dwd, workspace=ws)
+    a1g = moe.grouped_gate_up_gather(dx, p.row_src, k, p.offsets, p.s_perm,
+                                     dwg, dwu, workspace=ws)
+    y1g = moe.grouped_down(a1g, p.offsets, dwd, workspace=ws)
+    outs = []
+    for _ in range(2):
+        a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, dwg, dwu, dwd,
+                               workspace=ws)
+        ag, yg = moe.grouped_ffn_gather(dx, p.row_src, k, p.offsets, p.s_perm,
+                                        dwg, dwu, dwd, workspace=ws)
+        outs.append((a, y, ag, yg))
+    moe.debug_sync()
+    assert moe.read_device_error(ws) == 0
+    R = sum(counts)
+    for a, y, ag, yg in outs:
+        assert torch.equal(bits_t(a[:R]), bits_t(a1[:R]))
+        assert torch.equal(bits_t(y[:R]), bits_t(y1[:R]))
+        assert torch.equal(bits_t(ag[:R]), bits_t(a1g[:R]))
+        assert torch.equal(bits_t(yg[:R]), bits_t(y1g[:R]))
+
+
+def test_many_small_tiles_per_workgroup_equal_loop():
+    """Experts of at most 64 rows and more small-class tiles than
+    workgroups: each persistent workgroup walks 2-3 tiles of different
+    experts.  The per-expert loop runs every tile on a workgroup of its own;
+    each tile's K order (its start rotated by its n-tile) is the same in
+    both, so a and y must be the same bits, with x_perm and with rows
+    gathered on load.  One expert checked against the oracle too."""
+    rng = np.random.default_rng(21)
+    counts = [int(c) for c in rng.integers(1, 65, size=80)]
+    counts[3], counts[7], counts[11] = 64, 1, 0
+    H, I = 2048, 1024
+    print_case("small tiles per workgroup", len(counts), "experts", sum(counts), "rows")
+    n_local, E, k, e_begin = len(counts), 96, 4, 0
+    idx, w, x, wg, wu, wd = _edge_inputs(counts, n_local, e_begin, E, k, H, I,
+                                         seed=13)
+    wt = to_dev(w.astype(np.float32))
+    dx = to_dev(x)
+    p = moe.permute(to_dev(idx), dx, e_begin, n_local, topk_w=wt, E=E)
+    dwg, dwu, dwd = to_dev(wg), to_dev(wu), to_dev(wd)
+    a, y = moe.grouped_ffn(p.x_perm, p.offsets, p.s_perm, dwg, dwu, dwd)
+    ag, yg = moe.grouped_ffn_gather(dx, p.row_src, k, p.offsets, p.s_perm,
+                                    dwg, dwu, dwd)
+    a2, y2 = moe.grouped_ffn_loop(p.x_perm, p.offsets, counts, p.s_perm,
+                                  dwg, dwu, dwd)
+    moe.debug_sync()
+    R = sum(counts)
+    for got_a, got_y in ((a, y), (ag, yg)):
+        assert torch.equal(bits_t(got_a[:R]), bits_t(a2[:R]))
+        assert torch.equal(bits_t(got_y[:R]), bits_t(y2[:R]))
+    # expert 3 (64 rows) against the oracle
+    p_ref = orc.permute(idx, e_begin, n_local)
+    b0, b1 = int(p_ref["offsets"][3]), int(p_ref["offsets"][4])
+    xp = orc.gather_rows(x, p_ref["row_src"][b0:b1], k)
+    s = w.reshape(-1)[p_ref["row_src"][b0:b1]]
+    ex = np.zeros(b1 - b0, dtype=np.int32)
+    a_ref, y_ref = orc.expert_ffn_rows(xp, ex, s, wg[3:4], wu[3:4], wd[3:4])
+    assert_close(to_f64(a[b0:b1]), a_ref, "bf16", "a expert 3")
+    assert_close(to_f64(y[b0:b1]), y_ref, "bf16", "y expert 3")
