@@ -540,8 +540,8 @@ def main():
                          "gradient operands (dY, dg, du)")
     ap.add_argument("--ffn", choices=("grouped", "fused"), default="grouped",
                     help="bf16 FFN path: the grouped GEMMs (default) or the "
-                         "one-launch FFN on the same tiles (about 3%% faster on "
-                         "the EP8 share, 6%% slower on the EP64 share)")
+                         "one-launch FFN on the same tiles (about 2%% slower on "
+                         "the EP8 share, 9%% slower on the EP64 share)")
     ap.add_argument("--no-loop", action="store_true",
                     help="skip the per-expert-loop comparison of the grouped FFN")
     ap.add_argument("--copy-probe-mb", type=int, default=0,

@@ -275,11 +275,12 @@ int moe_grouped_ffn_gather(const void *x, const int32_t *row_src, int64_t T,
  * rows, the same K splits): its workgroups claim every gate/up tile, then
  * every down tile, by XCD shares of each phase; a down tile starts once
  * all gate/up tiles of its expert's rows have written their part of a, so
- * one launch replaces two and the plan in between, and the gate/up tail
- * overlaps the down start.  Measured against moe_grouped_ffn: about 3% faster on an EP8
- * share of 7-34 rows per expert, 6% slower on an EP64 share of 116-229 rows
- * (one round of gate/up tiles: nothing to overlap, and the early down tiles
- * wait it out), so moe_grouped_ffn stays the default path.
+ * one launch replaces the two grouped launches, and the gate/up tail
+ * overlaps the down start.  Measured against moe_grouped_ffn (one plan
+ * kernel for both GEMMs, rotated K loops): 2% slower on an EP8 share of 7-34
+ * rows per expert (0.497 against 0.487 ms), 9% slower on an EP64 share of
+ * 116-229 rows (one round of gate/up tiles: nothing to overlap, and the
+ * early down tiles wait it out), so moe_grouped_ffn is the default path.
  * x: with row_src non-NULL the token rows [T, H] (permuted row r is
  * x[row_src[r] / k], as moe_grouped_gate_up_gather; R_cap <= T * k); with
  * row_src NULL, x_perm [R_cap, H] (T and k unused).
