@@ -223,12 +223,19 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
   // 1. this wavefront's slots: local ids into LDS, counts into its row
   int32_t *const mine = bins + wid * n_local;
   int bad = 0;
+  // A wavefront owns at most G * 64 slots (one group), so the routing
+  // weights are loaded here with the expert ids and kept in registers for
+  // step 3: one memory round trip instead of two.
+  static_assert(kSmallPermuteF <= (int64_t)NW * 64 * G, "one group per wavefront");
+  float wpre[G];
   for (int g = 0; g < ngroups; ++g) {
     int32_t gi[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const int64_t f = f0 + (g * G + i) * 64 + lane;
-      gi[i] = (f < f0 + per && f < F) ? idx[f] : 0;
+      const bool in = f < f0 + per && f < F;
+      gi[i] = in ? idx[f] : 0;
+      wpre[i] = (in && s_perm) ? w[f] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < G; ++i) {
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(1024) void permute_small_kernel(
       const int64_t f = f0 + (g * G + i) * 64 + lane;
       const bool in = f < f0 + per && f < F;
       e[i] = in ? (uint32_t)ev[f] : 0xffffffffu;
-      wv[i] = (s_perm && e[i] < (uint32_t)n_local) ? w[f] : 0.f;
+      wv[i] = (s_perm && e[i] < (uint32_t)n_local) ? wpre[i] : 0.f;
     }
 #pragma unroll
     for (int i = 0; i < G; ++i) {
