@@ -210,6 +210,32 @@ def test_ffn_validation(L):
     d = L.moe_grouped_down
     assert d(P, P, 4, 64, 100, 128, P, BF16, P, P, ws, None) == E_SHAPE
     assert d(P, P, 4, 64, 128, 128, None, BF16, P, P, ws, None) == E_ARG
+    # the grouped FFN as one call (bf16: one plan kernel), and its gather
+    # variant
+    ff = L.moe_grouped_ffn
+
+    def ffn(x=P, wd=P, y=P, dt=BF16, R=64, wsb=ws):
+        return ff(x, P, None, 4, R, 128, 128, P, P, wd, dt, P, y, P, wsb, None)
+
+    assert ffn(wd=None) == E_ARG and ffn(y=None) == E_ARG
+    assert ffn(x=None) == E_ARG
+    assert ffn(x=P_ODD) == E_ALIGN and ffn(y=P_ODD) == E_ALIGN
+    assert ffn(wsb=16) == E_WS
+    assert ffn(R=0) == 0
+    fg = L.moe_grouped_ffn_gather
+
+    def fga(x=P, rs=P, T=32, k=2, R=64, dt=BF16, wd=P, y=P, wsb=ws):
+        return fg(x, rs, T, k, P, None, 4, R, 128, 128, P, P, wd, dt, P, y, P,
+                  wsb, None)
+
+    assert fga(dt=F32) == 5                      # MOE_E_UNSUPPORTED
+    assert fga(k=0) == E_SHAPE and fga(T=0) == E_SHAPE and fga(k=33) == E_SHAPE
+    assert fga(R=65) == E_SHAPE                  # R_cap > T * k
+    assert fga(rs=None) == E_ARG and fga(wd=None) == E_ARG
+    assert fga(y=None) == E_ARG and fga(x=None) == E_ARG
+    assert fga(x=P_ODD) == E_ALIGN and fga(y=P_ODD) == E_ALIGN
+    assert fga(wsb=16) == E_WS
+    assert fga(R=0) == 0
 
 
 def test_combine_validation(L):
