@@ -264,13 +264,17 @@ __device__ __forceinline__ int swz(int row, int c) {
 }
 
 // K steps of a whole tile may start at step rot (then wrap): K step ks of
-// the loop reads step (ks + rot) mod KT, with rot = 5 * n-tile mod KT.
+// the loop reads step (ks + rot) mod KT, with rot = n-tile mod KT.
 // Workgroups that start together and stream weights at the same rate would
 // otherwise read the same 128-byte column of every weight row at the same
 // time; with rows a power of two bytes apart (4 KiB at K = 2048, the down
 // projection) those reads fall on the same few HBM channels.  Measured on
 // the EP8 share (32 experts of 7-34 rows, weight-streaming): the down
-// projection replayed in a graph 196 -> 172 us.  The rotation depends only
+// projection replayed in a graph 196 -> 172 us with a stride of 5 steps per
+// n-tile; a stride of 1 (neighbouring n-tiles one step apart) took the step
+// another 0.9% lower (strides 3, 7, 11, 13 and ones that add the expert
+// index measured like 5; the full layer and the EP64 share did not move).
+// The rotation depends only
 // on the tile's n-tile and K, so every path that runs a tile whole sums in
 // the same order (bit-equal results across the grouped, per-expert-loop and
 // one-launch paths); split-K units are not rotated.
@@ -282,7 +286,7 @@ __device__ __forceinline__ int rot_step(int ks, int rot, int KT) {
   return r >= KT ? r - KT : r;
 }
 __device__ __forceinline__ int tile_rot(int nt, int KT) {
-  return MOE_KROT ? (nt * 5) % KT : 0;
+  return MOE_KROT ? nt % KT : 0;
 }
 
 // Load the A and B fragments of k-substep kk (16 values of K) from one LDS
