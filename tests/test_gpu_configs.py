@@ -80,7 +80,7 @@ def c4():
     dev.update(w_gate=wg, w_up=wu, w_down=wd)
     print_case("c4 oracle routing")
     ridx, rw, l32, l64 = orc.routing_of(wl, inp)
-    return wl, inp, dev, dict(idx=ridx, w=rw, l64=l64)
+    return wl, inp, dev, dict(idx=ridx, w=rw, l32=l32, l64=l64)
 
 
 @pytest.mark.timeout(300)
@@ -104,6 +104,19 @@ def test_c4_router_and_topk(c4):
         got_min = l[gi[t]].min()
         other = np.setdiff1d(np.arange(wl.E), gi[t])
         assert l[other].max() - got_min <= tol, t
+
+
+@pytest.mark.timeout(300)
+def test_c4_topk_on_oracle_logits_bit_exact(c4):
+    """Softmax -> top-8 -> renormalise at the full layer's size (8192 tokens
+    over 256 experts) on the oracle's logits rounded to fp32: both sides take
+    the choice on the same fp32 values, so the indices match bit for bit."""
+    wl, inp, d, r = c4
+    print_case("c4 top-k on oracle logits")
+    idx, w, _ = moe.route_topk(wl.k, logits=to_dev(r["l32"]))
+    moe.debug_sync()
+    np.testing.assert_array_equal(idx.cpu().numpy(), r["idx"])
+    np.testing.assert_allclose(w.cpu().numpy(), r["w"], atol=2e-6)
 
 
 @pytest.mark.timeout(300)
